@@ -1,0 +1,246 @@
+"""Pin checks of the CPU oracle against things other than itself.
+
+Each check returns None on success and raises AssertionError otherwise. They
+are collected by ``test_oracle_pins.py`` and re-run against deliberately
+broken copies of the oracle by ``test_oracle_mutations.py`` (which expects at
+least one of them to fail for every planted mistake).
+
+What pins what:
+* bf16 rounding            -- torch's float64 -> bfloat16 conversion (library).
+* RMSNorm                  -- closed form on constant vectors; scale invariance.
+* RoPE                     -- identity at p = 0; complex rotation e^{i p theta_i}
+                              (the standard rotary convention); relative-position
+                              invariance of q.k.
+* one attention head       -- torch's scaled_dot_product_attention (library);
+                              single key gives v; equal keys give mean(v).
+* SiLU / argmax            -- torch.nn.functional.silu; numpy argmax (first max);
+                              constructed ties.
+* embedding                -- one-hot tables (zero layers): hidden = norm(row).
+* ring + window + positions-- full-history recompute with a window mask
+                              (fullseq_ref.temporal_fullseq), W in {1,2,4,7,64},
+                              T up to 3W, wrap-around, prefill + decode, and the
+                              mask-oldest reading.
+* depformer                -- all-substeps-at-once recompute with a causal mask
+                              (fullseq_ref.depformer_fullseq), teacher-forced.
+* sizes                    -- K/V bytes per frame printed on the pages.
+"""
+import numpy as np
+import torch
+
+import oracle
+from synth import spec, workloads as wl, rng
+import fullseq_ref as ref
+
+TOL = 1e-10
+
+
+def mini(dtype="f32", window=8, mask_oldest=False, n_layers=2):
+    return spec.ModelShape(dim=64, n_layers=n_layers, n_heads=2, ffn=96, window=window,
+                           dep_dim=32, dep_layers=2, dep_heads=2, dep_ffn=48, n_substeps=16,
+                           text_vocab=50, audio_card=40, dtype=dtype, mask_oldest=mask_oldest)
+
+
+def _model(shape, seed=7, std=0.25):
+    w = wl.make_weights(shape, seed, gains="random", std=std)
+    return w, oracle.Model(shape, w)
+
+
+# ------------------------------------------------------------ primitives
+
+def check_bf16_round():
+    g = np.random.default_rng(1)
+    x = np.concatenate([g.normal(0, 1, 2000), g.normal(0, 1e-3, 500), g.normal(0, 50, 500),
+                        [0.0, 1.0, -1.0, 1.00390625, 1.01171875, 1.005859375, 3.0e-39, -2.5]])
+    want = torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.bf16_round(v) for v in x])
+    assert np.array_equal(got, want), "bf16 rounding differs from torch"
+
+
+def check_rmsnorm():
+    eps = 1e-8
+    for c in (0.5, -3.0, 1e-3):
+        g = np.linspace(0.5, 2.0, 16)
+        got = oracle.rmsnorm(np.full(16, c), g, eps)
+        want = np.sign(c) * g * abs(c) / np.sqrt(c * c + eps)
+        assert np.allclose(got, want, rtol=1e-13, atol=0), "rmsnorm closed form"
+    x = np.random.default_rng(2).normal(size=33)
+    g = np.random.default_rng(3).normal(size=33)
+    a = oracle.rmsnorm(x, g, 0.0)
+    b = oracle.rmsnorm(7.5 * x, g, 0.0)
+    assert np.allclose(a, b, rtol=1e-12), "rmsnorm scale invariance"
+
+
+def check_rope():
+    hd, H = 16, 3
+    v = np.random.default_rng(4).normal(size=H * hd)
+    assert np.array_equal(oracle.rope(v, H, hd, 0), v), "rope at p=0 must be the identity"
+    for p in (1, 5, 123, 3000):
+        got = oracle.rope(v, H, hd, p).reshape(H, hd // 2, 2)
+        z = v.reshape(H, hd // 2, 2)
+        zc = (z[..., 0] + 1j * z[..., 1]) * np.exp(1j * p * 1e4 ** (-2.0 * np.arange(hd // 2) / hd))
+        assert np.allclose(got[..., 0], zc.real, atol=1e-12) and \
+            np.allclose(got[..., 1], zc.imag, atol=1e-12), "rope != complex rotation"
+    q = np.random.default_rng(5).normal(size=hd)
+    k = np.random.default_rng(6).normal(size=hd)
+    base = oracle.rope(q, 1, hd, 10) @ oracle.rope(k, 1, hd, 3)
+    for d in (1, 17, 400):
+        sh = oracle.rope(q, 1, hd, 10 + d) @ oracle.rope(k, 1, hd, 3 + d)
+        assert abs(sh - base) < 1e-10, "rope relative-position invariance"
+
+
+def check_attend():
+    g = np.random.default_rng(8)
+    hd = 24
+    for n in (1, 2, 9, 40):
+        q = g.normal(size=hd)
+        K = g.normal(size=(n, hd))
+        V = g.normal(size=(n, hd))
+        got = oracle.attend(q, K, V)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q)[None, None, None, :], torch.tensor(K)[None, None],
+            torch.tensor(V)[None, None]).numpy().reshape(-1)
+        assert np.allclose(got, want, atol=1e-12), "attention != torch sdpa"
+    V = g.normal(size=(1, hd))
+    assert np.allclose(oracle.attend(g.normal(size=hd), g.normal(size=(1, hd)), V), V[0]), \
+        "single key must return its value"
+    K = np.tile(g.normal(size=(1, hd)), (6, 1))
+    V = g.normal(size=(6, hd))
+    assert np.allclose(oracle.attend(g.normal(size=hd), K, V), V.mean(0), atol=1e-13), \
+        "equal keys must average the values"
+
+
+def check_silu_argmax():
+    z = np.linspace(-30, 30, 121)
+    got = np.array([oracle.silu(v) for v in z])
+    want = torch.nn.functional.silu(torch.tensor(z)).numpy()
+    assert np.allclose(got, want, rtol=1e-14, atol=1e-300) and oracle.silu(0.0) == 0.0
+    v = np.random.default_rng(9).normal(size=1000)
+    i, m = oracle.argmax(v)
+    srt = np.sort(v)
+    assert i == int(np.argmax(v)) and abs(m - (srt[-1] - srt[-2])) < 1e-15
+    t = np.zeros(10)
+    t[[3, 7]] = 2.0
+    assert oracle.argmax(t) == (3, 0.0), "ties go to the lowest index"
+
+
+# ------------------------------------------------------------ model pins
+
+def check_embedding_onehot():
+    s = mini(n_layers=0)
+    w = [np.zeros_like(a) if nm.startswith("emb.") else a
+         for a, (nm, _, _) in zip(wl.make_weights(s, 11, gains="random", std=0.25),
+                                  spec.tensor_list(s))]
+    names = [t[0] for t in spec.tensor_list(s)]
+    row = np.random.default_rng(12).normal(size=s.dim).astype(np.float32)
+    frame = np.array([4] + [1] * s.n_substeps, np.int32)
+    w[names.index("emb.audio.5")].reshape(s.audio_card + 1, s.dim)[1] = row
+    M = oracle.Model(s, w)
+    out = oracle.Session(M).temporal(frame)
+    g = w[names.index("out_norm")].astype(np.float64)
+    want = oracle.rmsnorm(row.astype(np.float64), g, s.norm_eps)
+    assert np.allclose(out["hidden"], want, atol=1e-12), "one-hot embedding"
+    # linearity: a second channel adds its own row
+    row2 = np.random.default_rng(13).normal(size=s.dim).astype(np.float32)
+    w[names.index("emb.text")].reshape(s.text_vocab + 1, s.dim)[4] = row2
+    M = oracle.Model(s, w)
+    out = oracle.Session(M).temporal(frame)
+    want = oracle.rmsnorm(row.astype(np.float64) + row2, g, s.norm_eps)
+    assert np.allclose(out["hidden"], want, atol=1e-12), "embedding sum"
+
+
+def _ring_case(shape, T, n_prefill, seed=21):
+    w, M = _model(shape, seed)
+    W64 = ref.Weights(shape, w)
+    fr = wl.frames(shape, 99, 0, 0, T)
+    sess = oracle.Session(M)
+    pre = None
+    if n_prefill:
+        k, v = wl.prefill_kv(shape, 98, 0, n_prefill)
+        sess.prefill(k, v)
+        pre = (ref.to_f64(k, shape.dtype), ref.to_f64(v, shape.dtype))
+    hid_ref, log_ref = ref.temporal_fullseq(W64, fr, pre)
+    for t in range(T):
+        o = sess.temporal(fr[t])
+        assert np.max(np.abs(o["hidden"] - hid_ref[t])) < TOL, \
+            f"hidden mismatch at t={t} (W={shape.window}, prefill={n_prefill})"
+        assert np.max(np.abs(o["text_logits"] - log_ref[t])) < TOL, f"logits mismatch t={t}"
+        assert o["text_token"] == int(np.argmax(log_ref[t]))
+        pos, fill, wi = sess.info()
+        assert pos == n_prefill + t + 1 and wi == pos % shape.window
+        assert fill == min(pos, shape.window)
+
+
+def check_ring_window_fp32():
+    for W in (1, 2, 4, 7):
+        _ring_case(mini("f32", window=W), T=3 * W + 2, n_prefill=0)
+    _ring_case(mini("f32", window=7), T=12, n_prefill=5)
+    _ring_case(mini("f32", window=7), T=9, n_prefill=7)
+
+
+def check_ring_window_mask_oldest():
+    for W in (2, 5):
+        _ring_case(mini("f32", window=W, mask_oldest=True), T=3 * W, n_prefill=0)
+    _ring_case(mini("f32", window=6, mask_oldest=True), T=8, n_prefill=6)
+
+
+def check_incremental_equals_fullseq_bf16():
+    _ring_case(mini("bf16", window=64), T=20, n_prefill=0)
+    _ring_case(mini("bf16", window=4), T=11, n_prefill=3)
+
+
+def check_depformer_fullseq():
+    for dt in ("f32", "bf16"):
+        s = mini(dt)
+        w, M = _model(s, 31)
+        W64 = ref.Weights(s, w)
+        g = np.random.default_rng(32)
+        hid = g.normal(size=s.dim)
+        if dt == "bf16":
+            hid = ref.bf_round(hid)
+        text_in = 17
+        out = M.depformer(hid, text_in)
+        want = ref.depformer_fullseq(W64, hid, text_in, out["codes"])
+        assert np.max(np.abs(out["audio_logits"] - want)) < TOL, f"depformer ({dt})"
+        forced = g.integers(0, s.audio_card, size=s.n_substeps).astype(np.int32)
+        out = M.depformer(hid, text_in, forced=forced)
+        want = ref.depformer_fullseq(W64, hid, text_in, forced)
+        assert np.max(np.abs(out["audio_logits"] - want)) < TOL, f"forced depformer ({dt})"
+        assert np.array_equal(out["codes"], np.argmax(want, axis=1))
+
+
+def check_step_composition():
+    """orc_step = temporal then depformer on the temporal hidden and token."""
+    s = mini("bf16", window=5)
+    w, M = _model(s, 41)
+    fr = wl.frames(s, 42, 0, 0, 3)
+    a, b = oracle.Session(M), oracle.Session(M)
+    for t in range(3):
+        full = a.step(fr[t])
+        tp = b.temporal(fr[t])
+        dp = M.depformer(tp["hidden"], tp["text_token"])
+        assert full["text_token"] == tp["text_token"]
+        assert np.array_equal(full["codes"], dp["codes"])
+        assert np.array_equal(full["audio_logits"], dp["audio_logits"])
+        # teacher forcing with the oracle's own choices changes nothing
+        c = oracle.Session(M)
+        for u in range(t):
+            c.temporal(fr[u])
+        forced = c.step(fr[t], forced_text=full["text_token"], forced_codes=full["codes"])
+        assert np.array_equal(forced["audio_logits"], full["audio_logits"])
+
+
+def check_sizes():
+    """K/V per frame and per 3.1k positions, as printed on the pages."""
+    import json, os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_sizes.json")))
+    m = spec.PERSONAPLEX
+    assert spec.kv_bytes_per_frame(m) == gold["kv_bytes_per_frame_bf16"]["value"]
+    gib = 3100 * spec.kv_bytes_per_frame(m) / 2 ** 30
+    assert abs(gib - gold["kv_gib_at_3100_positions"]["value"]) < 0.05
+    assert m.window * gold["frame_ms"]["value"] / 1000 / 60 == gold["window_minutes"]["value"]
+
+
+ALL = [check_bf16_round, check_rmsnorm, check_rope, check_attend, check_silu_argmax,
+       check_embedding_onehot, check_ring_window_fp32, check_ring_window_mask_oldest,
+       check_incremental_equals_fullseq_bf16, check_depformer_fullseq, check_step_composition,
+       check_sizes]
