@@ -1,0 +1,939 @@
+// engine.cpp -- host side of libmoshi.so: the C ABI of include/moshi.h, the
+// session slot table, device buffers, and the two captured HIP graphs (the
+// temporal step and the 16 depformer substeps) that run a frame.
+//
+// One user frame in, one text token and one set of codes out per live slot
+// per call ("vLLM-Omni recipe: PersonaPlex", "Why it is different"); sessions
+// join and leave between calls, a full engine refuses joins, and a recycled
+// slot starts exactly like a fresh one ("Notes"). Per-slot state that changes
+// between calls (liveness, position, the frame) lives in device buffers the
+// graphs read, so joins and leaves never re-capture a graph.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/moshi.h"
+#include "kernels.h"
+
+using namespace moshi;
+
+namespace {
+
+// Kernel classes reported by moshi_time_kernels.
+enum KClass {
+  KC_EMBED = 0,
+  KC_T_QKV,
+  KC_T_ATTN,
+  KC_T_O,
+  KC_T_GATEUP,
+  KC_T_DOWN,
+  KC_T_HEAD,
+  KC_D_INPROJ,
+  KC_D_ENTRY,
+  KC_D_QKV,
+  KC_D_ATTN,
+  KC_D_O,
+  KC_D_GATEUP,
+  KC_D_DOWN,
+  KC_D_HEAD,
+  KC_COUNT
+};
+const char* kClassNames[KC_COUNT] = {
+    "embed",      "temporal_qkv",  "temporal_attn", "temporal_o",    "temporal_gateup",
+    "temporal_down", "text_head",  "dep_inproj",    "dep_entry",     "dep_qkv",
+    "dep_attn",   "dep_o",         "dep_gateup",    "dep_down",      "dep_head"};
+
+// Waves per workgroup of the projections: the temporal ones have K = 4096 or
+// 11264 and many rows; the depformer ones K = 1024 / 2816 and few rows.
+constexpr int KW_TEMPORAL = 8;
+constexpr int KW_DEP = 4;
+
+bool valid_head_dim(int hd) { return hd == 32 || hd == 64 || hd == 128; }
+
+int32_t tensor_count(const moshi_config* c) {
+  const int S = c->n_substeps, L = c->n_layers, Ld = c->dep_layers;
+  return 1 + S + 6 * L + 2 + S + S + 2 * Ld + 4 * S * Ld + S;
+}
+
+const char* config_error(const moshi_config* c) {
+  if (!c) return "config is NULL";
+  if (c->dtype != MOSHI_F32 && c->dtype != MOSHI_BF16) return "dtype must be MOSHI_F32 or MOSHI_BF16";
+  const int vec = c->dtype == MOSHI_BF16 ? 8 : 4;
+  if (c->dim <= 0 || c->n_heads <= 0 || c->dim % c->n_heads) return "dim must be a positive multiple of n_heads";
+  if (!valid_head_dim(c->dim / c->n_heads)) return "temporal head_dim must be 32, 64 or 128";
+  if (c->dep_dim <= 0 || c->dep_heads <= 0 || c->dep_dim % c->dep_heads) return "dep_dim must be a positive multiple of dep_heads";
+  if (!valid_head_dim(c->dep_dim / c->dep_heads)) return "depformer head_dim must be 32, 64 or 128";
+  if (c->n_layers < 1 || c->dep_layers < 1) return "n_layers and dep_layers must be >= 1";
+  if (c->n_substeps < 1 || c->n_substeps > 64) return "n_substeps must be in [1, 64]";
+  if (c->ffn_hidden <= 0 || c->dep_ffn_hidden <= 0) return "ffn widths must be positive";
+  if (c->dim % vec || c->ffn_hidden % vec || c->dep_dim % vec || c->dep_ffn_hidden % vec)
+    return "widths must be multiples of 8 (bf16) / 4 (fp32)";
+  if (c->window < 1) return "window must be >= 1";
+  if ((c->flags & MOSHI_FLAG_MASK_OLDEST) && c->window < 2) return "mask-oldest needs window >= 2";
+  if (c->flags & ~MOSHI_FLAG_MASK_OLDEST) return "unknown flag bits";
+  if (c->text_vocab < 2 || c->audio_card < 2) return "vocabularies must have >= 2 entries";
+  if (c->max_sessions < 1 || c->max_sessions > 64) return "max_sessions must be in [1, 64]";
+  if (!(c->rope_theta > 0.f) || !(c->norm_eps >= 0.f)) return "rope_theta must be > 0 and norm_eps >= 0";
+  return nullptr;
+}
+
+}  // namespace
+
+struct moshi_ctx {
+  moshi_config c{};
+  int B = 0, dtype = 0, esz = 0, device = 0;
+  int D = 0, H = 0, hd = 0, F = 0, W = 0, L = 0;
+  int Dd = 0, Hd = 0, hdd = 0, Fd = 0, Ld = 0, S = 0, Vt = 0, Va = 0, NCH = 0;
+  hipStream_t stream = nullptr;
+  bool own_stream = false;
+  bool failed = false;
+  std::string err;
+
+  // weights (device)
+  std::vector<void*> dev_alloc;  // every hipMalloc, freed at destroy
+  const void* emb_text = nullptr;
+  std::vector<const void*> emb_audio, attn_norm, qkv, wo, mlp_norm, gate_up, down;
+  const void* out_norm = nullptr;
+  const void* text_head = nullptr;
+  const void* dep_in = nullptr;  // [S*Dd][D], contiguous
+  std::vector<const void*> dep_emb, dep_attn_norm, dep_mlp_norm, dep_qkv, dep_o, dep_gate_up,
+      dep_down, dep_head;
+  const void** d_tables = nullptr;  // [NCH] device copy of the embedding table pointers
+
+  // state and activations (device)
+  void *ring_k = nullptr, *ring_v = nullptr;  // [B][L][H][W][hd]
+  void *dkv_k = nullptr, *dkv_v = nullptr;    // [B][Ld][Hd][S][hdd]
+  float *x = nullptr, *ssq = nullptr, *q = nullptr;
+  void *o = nullptr, *act = nullptr, *hid = nullptr;
+  float *pre = nullptr, *y = nullptr, *ssq_d = nullptr, *qd = nullptr;
+  void *od = nullptr, *actd = nullptr;
+  float *text_logits = nullptr, *audio_logits = nullptr;
+  int *tokens = nullptr, *codes = nullptr;
+  ArgPart* apart = nullptr;
+  unsigned* tickets = nullptr;  // [1 + S] argmax tickets
+  float* attn_part = nullptr;
+  unsigned* attn_ticket = nullptr;  // [B][max(H, Hd)]
+  int *d_frames = nullptr, *d_live = nullptr;
+  int64_t* d_pos = nullptr;
+  int* d_err = nullptr;  // set by the embedding when a live code was out of range
+  double *d_inv_freq = nullptr;
+  void* staging = nullptr;  // one layer of prefill K or V
+  int max_chunks = 0;
+
+  // host state (the device copies of live / pos are refreshed only when
+  // `meta_dirty`; the step itself advances the device positions)
+  std::vector<int> live;
+  std::vector<int64_t> pos;
+  bool meta_dirty = true;
+  int* h_frames = nullptr;  // pinned
+  int* h_live = nullptr;
+  int64_t* h_pos = nullptr;
+  int* h_tokens = nullptr;
+  int* h_codes = nullptr;
+
+  // graphs
+  hipGraphExec_t g_temporal = nullptr, g_dep = nullptr;
+  bool use_graphs = true;
+
+  // kernel timing (eager launches bracketed by events)
+  bool timing = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ev_class;
+  std::vector<double> ev_bytes;
+  size_t ev_used = 0;
+};
+
+namespace {
+
+int fail(moshi_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+int device_fail(moshi_ctx* c, hipError_t e, const char* where) {
+  if (c) {
+    c->failed = true;
+    c->err = std::string(where) + ": " + hipGetErrorString(e);
+  }
+  return MOSHI_E_DEVICE;
+}
+
+#define CKD(ctx, expr)                                        \
+  do {                                                        \
+    hipError_t e_ = (expr);                                   \
+    if (e_ != hipSuccess) return device_fail(ctx, e_, #expr); \
+  } while (0)
+
+hipError_t dalloc(moshi_ctx* c, void** p, size_t bytes) {
+  *p = nullptr;
+  if (bytes == 0) bytes = 256;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e == hipSuccess) c->dev_alloc.push_back(*p);
+  return e;
+}
+
+// ---- launch helpers (each kernel launch goes through `run`) ----
+
+template <typename F>
+hipError_t run(moshi_ctx* c, int kclass, double bytes, F&& launch) {
+  if (!c->timing) return launch();
+  if (c->ev_used + 2 > c->ev.size()) {
+    for (int i = 0; i < 64; ++i) {
+      hipEvent_t e;
+      hipError_t r = hipEventCreate(&e);
+      if (r != hipSuccess) return r;
+      c->ev.push_back(e);
+    }
+  }
+  hipError_t r = hipEventRecord(c->ev[c->ev_used], c->stream);
+  if (r != hipSuccess) return r;
+  r = launch();
+  if (r != hipSuccess) return r;
+  r = hipEventRecord(c->ev[c->ev_used + 1], c->stream);
+  if (r != hipSuccess) return r;
+  c->ev_class.push_back(kclass);
+  c->ev_bytes.push_back(bytes);
+  c->ev_used += 2;
+  return hipSuccess;
+}
+
+int live_count(const moshi_ctx* c) {
+  int n = 0;
+  for (int v : c->live) n += v;
+  return n;
+}
+
+GemmArgs gemm_base(const moshi_ctx* c) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.B = c->B;
+  a.eps = c->c.norm_eps;
+  a.live = c->d_live;
+  return a;
+}
+
+// ---- the temporal step: embed, L layers, final norm + text head ----
+
+hipError_t enqueue_temporal(moshi_ctx* c) {
+  const int dt = c->dtype, B = c->B, D = c->D, F = c->F, es = c->esz;
+  const double nlive = live_count(c);
+  hipError_t e;
+  {
+    EmbedArgs a{c->d_tables, c->d_frames, c->d_live, c->NCH, D, B, c->Vt + 1, c->Va + 1,
+                c->d_err, c->x, c->ssq};
+    e = run(c, KC_EMBED, nlive * c->NCH * D * es, [&] { return launch_embed(dt, a, c->stream); });
+    if (e != hipSuccess) return e;
+  }
+  const int nt_d = (D + 15) / 16;
+  const int64_t slot_stride = (int64_t)c->L * c->H * c->W * c->hd;
+  for (int l = 0; l < c->L; ++l) {
+    {  // RMSNorm -> q|k|v -> RoPE -> ring write
+      GemmArgs a = gemm_base(c);
+      a.W = c->qkv[l]; a.N = 3 * D; a.K = D;
+      a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->attn_norm[l];
+      a.q_out = c->q; a.dq = D; a.hd = c->hd; a.inv_freq = c->d_inv_freq; a.pos = c->d_pos;
+      a.ring_k = c->ring_k; a.ring_v = c->ring_v; a.slot_stride = slot_stride;
+      a.layer_off = (int64_t)l * c->H * c->W * c->hd; a.head_stride = (int64_t)c->W * c->hd;
+      a.cap = c->W;
+      double bytes = 3.0 * D * D * es + D * es + nlive * 2.0 * D * es;
+      e = run(c, KC_T_QKV, bytes,
+              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_NORM, EPI_QKV, a, c->stream); });
+      if (e != hipSuccess) return e;
+    }
+    {  // window attention over the ring
+      AttnArgs a;
+      memset(&a, 0, sizeof(a));
+      a.q = c->q; a.ldq = D; a.ring_k = c->ring_k; a.ring_v = c->ring_v;
+      a.slot_stride = slot_stride; a.layer_off = (int64_t)l * c->H * c->W * c->hd;
+      a.head_stride = (int64_t)c->W * c->hd; a.cap = c->W; a.pos = c->d_pos; a.live = c->d_live;
+      a.mask_oldest = (c->c.flags & MOSHI_FLAG_MASK_OLDEST) ? 1 : 0;
+      a.n_heads = c->H; a.max_chunks = c->max_chunks; a.part = c->attn_part;
+      a.ticket = c->attn_ticket; a.o_out = c->o; a.ldo = D;
+      double keys = 0;
+      for (int b = 0; b < B; ++b)
+        if (c->live[b]) {
+          int64_t p = c->pos[b];
+          int64_t n = p + 1 < c->W ? p + 1 : c->W;
+          if (a.mask_oldest && p >= c->W - 1) n -= 1;
+          keys += (double)n;
+        }
+      e = run(c, KC_T_ATTN, keys * 2.0 * D * es,
+              [&] { return launch_attn(dt, c->hd, a, B, c->stream); });
+      if (e != hipSuccess) return e;
+    }
+    {  // o-projection + residual
+      GemmArgs a = gemm_base(c);
+      a.W = c->wo[l]; a.N = D; a.K = D; a.X = c->o; a.ldx = D;
+      a.resid = c->x; a.ldr = D; a.ssq_out = c->ssq;
+      e = run(c, KC_T_O, (double)D * D * es,
+              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_DIRECT, EPI_RESID, a, c->stream); });
+      if (e != hipSuccess) return e;
+    }
+    {  // RMSNorm -> gate|up -> SiLU(gate)*up
+      GemmArgs a = gemm_base(c);
+      a.W = c->gate_up[l]; a.N = F; a.K = D;
+      a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->mlp_norm[l];
+      a.act = c->act; a.lda = F;
+      e = run(c, KC_T_GATEUP, 2.0 * F * D * es + D * es,
+              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_NORM, EPI_SWIGLU, a, c->stream); });
+      if (e != hipSuccess) return e;
+    }
+    {  // down + residual
+      GemmArgs a = gemm_base(c);
+      a.W = c->down[l]; a.N = D; a.K = F; a.X = c->act; a.ldx = F;
+      a.resid = c->x; a.ldr = D; a.ssq_out = c->ssq;
+      e = run(c, KC_T_DOWN, (double)D * F * es,
+              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_DIRECT, EPI_RESID, a, c->stream); });
+      if (e != hipSuccess) return e;
+    }
+  }
+  {  // final norm -> hidden (kept for the depformer) -> text head -> greedy token
+    GemmArgs a = gemm_base(c);
+    a.W = c->text_head; a.N = c->Vt; a.K = D;
+    a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->out_norm;
+    a.xn_out = c->hid;
+    a.out = c->text_logits; a.ldo = c->Vt; a.apart = c->apart; a.ticket = c->tickets;
+    a.tok_out = c->tokens; a.tok_stride = 1;
+    e = run(c, KC_T_HEAD, (double)c->Vt * D * es + D * es,
+            [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_NORM, EPI_ARGMAX, a, c->stream); });
+    if (e != hipSuccess) return e;
+  }
+  return launch_advance(c->d_pos, c->d_live, B, c->stream);
+}
+
+// ---- the depformer: all substep input projections, then 16 substeps ----
+
+hipError_t enqueue_depformer(moshi_ctx* c) {
+  const int dt = c->dtype, B = c->B, D = c->D, Dd = c->Dd, Fd = c->Fd, S = c->S, es = c->esz;
+  const double nlive = live_count(c);
+  hipError_t e;
+  {  // y_pre[s] = W_in[s] . hidden for every substep at once
+    GemmArgs a = gemm_base(c);
+    a.W = c->dep_in; a.N = S * Dd; a.K = D; a.X = c->hid; a.ldx = D;
+    a.out = c->pre; a.ldo = S * Dd;
+    e = run(c, KC_D_INPROJ, (double)S * Dd * D * es,
+            [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_DIRECT, EPI_STORE, a, c->stream); });
+    if (e != hipSuccess) return e;
+  }
+  const int nt_dd = (Dd + 15) / 16;
+  const int64_t slot_stride = (int64_t)c->Ld * c->Hd * S * c->hdd;
+  for (int s = 0; s < S; ++s) {
+    {  // entry: y = pre[s] + E_s[previous token]
+      EntryArgs a{c->pre, S * Dd, s, c->dep_emb[s], s == 0 ? c->tokens : c->codes + (s - 1),
+                  s == 0 ? 1 : S, Dd, B, c->y, c->ssq_d};
+      e = run(c, KC_D_ENTRY, nlive * Dd * es, [&] { return launch_entry(dt, a, c->stream); });
+      if (e != hipSuccess) return e;
+    }
+    for (int l = 0; l < c->Ld; ++l) {
+      const int wi = s * c->Ld + l;
+      const int64_t layer_off = (int64_t)l * c->Hd * S * c->hdd;
+      {
+        GemmArgs a = gemm_base(c);
+        a.W = c->dep_qkv[wi]; a.N = 3 * Dd; a.K = Dd;
+        a.X = c->y; a.ldx = Dd; a.ssq = c->ssq_d; a.n_ssq = nt_dd; a.gain = c->dep_attn_norm[l];
+        a.q_out = c->qd; a.dq = Dd; a.hd = c->hdd; a.inv_freq = nullptr; a.pos = nullptr;
+        a.scalar_widx = s; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v; a.slot_stride = slot_stride;
+        a.layer_off = layer_off; a.head_stride = (int64_t)S * c->hdd; a.cap = S;
+        e = run(c, KC_D_QKV, 3.0 * Dd * Dd * es + Dd * es + nlive * 2.0 * Dd * es,
+                [&] { return launch_gemm(dt, KW_DEP, PRO_NORM, EPI_QKV, a, c->stream); });
+        if (e != hipSuccess) return e;
+      }
+      {
+        AttnArgs a;
+        memset(&a, 0, sizeof(a));
+        a.q = c->qd; a.ldq = Dd; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v;
+        a.slot_stride = slot_stride; a.layer_off = layer_off; a.head_stride = (int64_t)S * c->hdd;
+        a.cap = S; a.pos = nullptr; a.scalar_nvalid = s + 1; a.live = c->d_live;
+        a.n_heads = c->Hd; a.max_chunks = (S + ATTN_CHUNK - 1) / ATTN_CHUNK; a.part = c->attn_part;
+        a.ticket = c->attn_ticket; a.o_out = c->od; a.ldo = Dd;
+        e = run(c, KC_D_ATTN, nlive * (s + 1) * 2.0 * Dd * es,
+                [&] { return launch_attn(dt, c->hdd, a, B, c->stream); });
+        if (e != hipSuccess) return e;
+      }
+      {
+        GemmArgs a = gemm_base(c);
+        a.W = c->dep_o[wi]; a.N = Dd; a.K = Dd; a.X = c->od; a.ldx = Dd;
+        a.resid = c->y; a.ldr = Dd; a.ssq_out = c->ssq_d;
+        e = run(c, KC_D_O, (double)Dd * Dd * es,
+                [&] { return launch_gemm(dt, KW_DEP, PRO_DIRECT, EPI_RESID, a, c->stream); });
+        if (e != hipSuccess) return e;
+      }
+      {
+        GemmArgs a = gemm_base(c);
+        a.W = c->dep_gate_up[wi]; a.N = Fd; a.K = Dd;
+        a.X = c->y; a.ldx = Dd; a.ssq = c->ssq_d; a.n_ssq = nt_dd; a.gain = c->dep_mlp_norm[l];
+        a.act = c->actd; a.lda = Fd;
+        e = run(c, KC_D_GATEUP, 2.0 * Fd * Dd * es + Dd * es,
+                [&] { return launch_gemm(dt, KW_DEP, PRO_NORM, EPI_SWIGLU, a, c->stream); });
+        if (e != hipSuccess) return e;
+      }
+      {
+        GemmArgs a = gemm_base(c);
+        a.W = c->dep_down[wi]; a.N = Dd; a.K = Fd; a.X = c->actd; a.ldx = Fd;
+        a.resid = c->y; a.ldr = Dd; a.ssq_out = c->ssq_d;
+        e = run(c, KC_D_DOWN, (double)Dd * Fd * es,
+                [&] { return launch_gemm(dt, KW_DEP, PRO_DIRECT, EPI_RESID, a, c->stream); });
+        if (e != hipSuccess) return e;
+      }
+    }
+    {  // head s on the rounded residual -> code s
+      GemmArgs a = gemm_base(c);
+      a.W = c->dep_head[s]; a.N = c->Va; a.K = Dd; a.X = c->y; a.ldx = Dd;
+      a.out = c->audio_logits + (size_t)s * c->Va; a.ldo = S * c->Va;
+      a.apart = c->apart; a.ticket = c->tickets + 1 + s; a.tok_out = c->codes + s; a.tok_stride = S;
+      e = run(c, KC_D_HEAD, (double)c->Va * Dd * es,
+              [&] { return launch_gemm(dt, KW_DEP, PRO_CAST, EPI_ARGMAX, a, c->stream); });
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+hipError_t capture(moshi_ctx* c, hipError_t (*fn)(moshi_ctx*), hipGraphExec_t* out) {
+  hipGraph_t g = nullptr;
+  hipError_t e = hipStreamBeginCapture(c->stream, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) return e;
+  hipError_t e2 = fn(c);
+  e = hipStreamEndCapture(c->stream, &g);
+  if (e2 != hipSuccess) {
+    if (g) (void)hipGraphDestroy(g);
+    return e2;
+  }
+  if (e != hipSuccess) return e;
+  e = hipGraphInstantiate(out, g, nullptr, nullptr, 0);
+  (void)hipGraphDestroy(g);
+  return e;
+}
+
+int ensure_graphs(moshi_ctx* c) {
+  if (!c->use_graphs || c->timing) return MOSHI_OK;
+  if (!c->g_temporal) CKD(c, capture(c, enqueue_temporal, &c->g_temporal));
+  if (!c->g_dep) CKD(c, capture(c, enqueue_depformer, &c->g_dep));
+  return MOSHI_OK;
+}
+
+int launch_part(moshi_ctx* c, bool temporal) {
+  if (c->use_graphs && !c->timing) {
+    CKD(c, hipGraphLaunch(temporal ? c->g_temporal : c->g_dep, c->stream));
+  } else {
+    CKD(c, temporal ? enqueue_temporal(c) : enqueue_depformer(c));
+  }
+  return MOSHI_OK;
+}
+
+int check_ctx(moshi_ctx* c) {
+  if (!c) return MOSHI_E_INVALID;
+  if (c->failed) return MOSHI_E_DEVICE;
+  hipError_t e = hipSetDevice(c->device);
+  if (e != hipSuccess) return device_fail(c, e, "hipSetDevice");
+  return MOSHI_OK;
+}
+
+int validate_frames(moshi_ctx* c, const int32_t* frames) {
+  if (!frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
+  for (int b = 0; b < c->B; ++b) {
+    if (!c->live[b]) continue;
+    const int32_t* f = frames + (size_t)b * c->NCH;
+    if (f[0] < 0 || f[0] > c->Vt) return fail(c, MOSHI_E_INVALID, "text code out of range");
+    for (int k = 1; k < c->NCH; ++k)
+      if (f[k] < 0 || f[k] > c->Va) return fail(c, MOSHI_E_INVALID, "audio code out of range");
+  }
+  return MOSHI_OK;
+}
+
+// Refresh the device copies of liveness and positions after a join, leave or
+// prefill (the step advances the device positions itself).
+int upload_meta(moshi_ctx* c) {
+  if (!c->meta_dirty) return MOSHI_OK;
+  for (int b = 0; b < c->B; ++b) {
+    c->h_live[b] = c->live[b];
+    c->h_pos[b] = c->pos[b];
+  }
+  CKD(c, hipMemcpyAsync(c->d_live, c->h_live, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
+  CKD(c, hipMemcpyAsync(c->d_pos, c->h_pos, sizeof(int64_t) * c->B, hipMemcpyHostToDevice, c->stream));
+  c->meta_dirty = false;
+  return MOSHI_OK;
+}
+
+// Stage the host frames (zeros for free slots) and the slot metadata.
+int upload_step_inputs(moshi_ctx* c, const int32_t* frames) {
+  int rc = upload_meta(c);
+  if (rc) return rc;
+  if (!frames) return MOSHI_OK;
+  for (int b = 0; b < c->B; ++b)
+    for (int k = 0; k < c->NCH; ++k)
+      c->h_frames[(size_t)b * c->NCH + k] = c->live[b] ? frames[(size_t)b * c->NCH + k] : 0;
+  CKD(c, hipMemcpyAsync(c->d_frames, c->h_frames, sizeof(int) * c->B * c->NCH,
+                        hipMemcpyHostToDevice, c->stream));
+  return MOSHI_OK;
+}
+
+int run_step(moshi_ctx* c, const int32_t* frames, int32_t* text_token, int32_t* audio_codes,
+             bool with_dep) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if ((rc = validate_frames(c, frames))) return rc;
+  if ((rc = ensure_graphs(c))) return rc;
+  if ((rc = upload_step_inputs(c, frames))) return rc;
+  if ((rc = launch_part(c, true))) return rc;
+  if (with_dep && (rc = launch_part(c, false))) return rc;
+  CKD(c, hipMemcpyAsync(c->h_tokens, c->tokens, sizeof(int) * c->B, hipMemcpyDeviceToHost, c->stream));
+  if (with_dep)
+    CKD(c, hipMemcpyAsync(c->h_codes, c->codes, sizeof(int) * c->B * c->S, hipMemcpyDeviceToHost,
+                          c->stream));
+  CKD(c, hipStreamSynchronize(c->stream));
+  for (int b = 0; b < c->B; ++b) {
+    if (c->live[b]) c->pos[b] += 1;
+    if (text_token) text_token[b] = c->live[b] ? c->h_tokens[b] : -1;
+    if (with_dep && audio_codes)
+      for (int s = 0; s < c->S; ++s)
+        audio_codes[(size_t)b * c->S + s] = c->live[b] ? c->h_codes[(size_t)b * c->S + s] : -1;
+  }
+  return MOSHI_OK;
+}
+
+int upload_weights(moshi_ctx* c, const void* const* t) {
+  const moshi_config& k = c->c;
+  const size_t es = c->esz;
+  const int D = c->D, F = c->F, Dd = c->Dd, Fd = c->Fd, S = c->S, Vt = c->Vt, Va = c->Va;
+  int i = 0;
+  auto put = [&](const void* src, size_t elems, const void** dst) -> int {
+    void* p;
+    hipError_t e = dalloc(c, &p, elems * es);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return fail(c, MOSHI_E_OOM, "weights: out of device memory");
+    if (e != hipSuccess) return device_fail(c, e, "hipMalloc(weights)");
+    if (!src) return fail(c, MOSHI_E_INVALID, "NULL weight tensor");
+    e = hipMemcpy(p, src, elems * es, hipMemcpyHostToDevice);
+    if (e != hipSuccess) return device_fail(c, e, "hipMemcpy(weights)");
+    *dst = p;
+    return MOSHI_OK;
+  };
+  int rc;
+  (void)k;
+  if ((rc = put(t[i++], (size_t)(Vt + 1) * D, &c->emb_text))) return rc;
+  c->emb_audio.resize(S);
+  for (int s = 0; s < S; ++s)
+    if ((rc = put(t[i++], (size_t)(Va + 1) * D, &c->emb_audio[s]))) return rc;
+  c->attn_norm.resize(c->L); c->qkv.resize(c->L); c->wo.resize(c->L);
+  c->mlp_norm.resize(c->L); c->gate_up.resize(c->L); c->down.resize(c->L);
+  for (int l = 0; l < c->L; ++l) {
+    if ((rc = put(t[i++], D, &c->attn_norm[l]))) return rc;
+    if ((rc = put(t[i++], (size_t)3 * D * D, &c->qkv[l]))) return rc;
+    if ((rc = put(t[i++], (size_t)D * D, &c->wo[l]))) return rc;
+    if ((rc = put(t[i++], D, &c->mlp_norm[l]))) return rc;
+    if ((rc = put(t[i++], (size_t)2 * F * D, &c->gate_up[l]))) return rc;
+    if ((rc = put(t[i++], (size_t)D * F, &c->down[l]))) return rc;
+  }
+  if ((rc = put(t[i++], D, &c->out_norm))) return rc;
+  if ((rc = put(t[i++], (size_t)Vt * D, &c->text_head))) return rc;
+  {  // the S input projections, contiguous: one [S*Dd, D] matrix
+    void* p;
+    const size_t one = (size_t)Dd * D;
+    hipError_t e = dalloc(c, &p, one * S * es);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return fail(c, MOSHI_E_OOM, "weights: out of device memory");
+    if (e != hipSuccess) return device_fail(c, e, "hipMalloc(dep_in)");
+    for (int s = 0; s < S; ++s) {
+      const void* src = t[i++];
+      if (!src) return fail(c, MOSHI_E_INVALID, "NULL weight tensor");
+      CKD(c, hipMemcpy((char*)p + one * s * es, src, one * es, hipMemcpyHostToDevice));
+    }
+    c->dep_in = p;
+  }
+  c->dep_emb.resize(S);
+  for (int s = 0; s < S; ++s)
+    if ((rc = put(t[i++], (size_t)((s == 0 ? Vt : Va) + 1) * Dd, &c->dep_emb[s]))) return rc;
+  c->dep_attn_norm.resize(c->Ld); c->dep_mlp_norm.resize(c->Ld);
+  for (int l = 0; l < c->Ld; ++l) {
+    if ((rc = put(t[i++], Dd, &c->dep_attn_norm[l]))) return rc;
+    if ((rc = put(t[i++], Dd, &c->dep_mlp_norm[l]))) return rc;
+  }
+  const int n = S * c->Ld;
+  c->dep_qkv.resize(n); c->dep_o.resize(n); c->dep_gate_up.resize(n); c->dep_down.resize(n);
+  for (int s = 0; s < S; ++s)
+    for (int l = 0; l < c->Ld; ++l) {
+      const int wi = s * c->Ld + l;
+      if ((rc = put(t[i++], (size_t)3 * Dd * Dd, &c->dep_qkv[wi]))) return rc;
+      if ((rc = put(t[i++], (size_t)Dd * Dd, &c->dep_o[wi]))) return rc;
+      if ((rc = put(t[i++], (size_t)2 * Fd * Dd, &c->dep_gate_up[wi]))) return rc;
+      if ((rc = put(t[i++], (size_t)Dd * Fd, &c->dep_down[wi]))) return rc;
+    }
+  c->dep_head.resize(S);
+  for (int s = 0; s < S; ++s)
+    if ((rc = put(t[i++], (size_t)Va * Dd, &c->dep_head[s]))) return rc;
+  // device copy of the channel table pointers (text, then the S audio tables)
+  std::vector<const void*> tabs;
+  tabs.push_back(c->emb_text);
+  for (int s = 0; s < S; ++s) tabs.push_back(c->emb_audio[s]);
+  void* p;
+  CKD(c, dalloc(c, &p, sizeof(void*) * tabs.size()));
+  CKD(c, hipMemcpy(p, tabs.data(), sizeof(void*) * tabs.size(), hipMemcpyHostToDevice));
+  c->d_tables = (const void**)p;
+  return MOSHI_OK;
+}
+
+int alloc_buffers(moshi_ctx* c) {
+  const size_t B = c->B, es = c->esz;
+  const size_t D = c->D, F = c->F, Dd = c->Dd, Fd = c->Fd, S = c->S;
+  struct Req {
+    void** p;
+    size_t bytes;
+  };
+  c->max_chunks = (c->W + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  const size_t hmax = c->H > c->Hd ? c->H : c->Hd;
+  const size_t hdmax = c->hd > c->hdd ? c->hd : c->hdd;
+  const size_t ntile_max = ((size_t)(c->Vt > c->Va ? c->Vt : c->Va) + 15) / 16;  // argmax tiles
+  Req reqs[] = {
+      {&c->ring_k, B * c->L * c->H * c->W * c->hd * es},
+      {&c->ring_v, B * c->L * c->H * c->W * c->hd * es},
+      {&c->dkv_k, B * c->Ld * c->Hd * S * c->hdd * es},
+      {&c->dkv_v, B * c->Ld * c->Hd * S * c->hdd * es},
+      {(void**)&c->x, B * D * 4},
+      {(void**)&c->ssq, ((D + 15) / 16) * B * 4},
+      {(void**)&c->q, B * D * 4},
+      {&c->o, B * D * es},
+      {&c->act, B * F * es},
+      {&c->hid, B * D * es},
+      {(void**)&c->pre, B * S * Dd * 4},
+      {(void**)&c->y, B * Dd * 4},
+      {(void**)&c->ssq_d, ((Dd + 15) / 16) * B * 4},
+      {(void**)&c->qd, B * Dd * 4},
+      {&c->od, B * Dd * es},
+      {&c->actd, B * Fd * es},
+      {(void**)&c->text_logits, B * c->Vt * 4},
+      {(void**)&c->audio_logits, B * S * c->Va * 4},
+      {(void**)&c->tokens, B * 4},
+      {(void**)&c->codes, B * S * 4},
+      {(void**)&c->apart, ntile_max * B * sizeof(ArgPart)},
+      {(void**)&c->tickets, (1 + S) * 4},
+      {(void**)&c->attn_part, B * hmax * c->max_chunks * (hdmax + 2) * 4},
+      {(void**)&c->attn_ticket, B * hmax * 4},
+      {(void**)&c->d_frames, B * c->NCH * 4},
+      {(void**)&c->d_live, B * 4},
+      {(void**)&c->d_pos, B * 8},
+      {(void**)&c->d_err, 4},
+      {(void**)&c->d_inv_freq, (size_t)(c->hd / 2) * 8},
+      {&c->staging, (size_t)c->W * D * es},
+  };
+  for (auto& r : reqs) {
+    hipError_t e = dalloc(c, r.p, r.bytes);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return fail(c, MOSHI_E_OOM, "buffers: out of device memory");
+    if (e != hipSuccess) return device_fail(c, e, "hipMalloc(buffers)");
+  }
+  // Zero everything small (tickets must start at zero; activations of free
+  // slots then hold finite values). The rings need no clearing: only positions
+  // a session has written are ever attended.
+  for (size_t i = 4; i < sizeof(reqs) / sizeof(reqs[0]); ++i)
+    CKD(c, hipMemsetAsync(*reqs[i].p, 0, reqs[i].bytes, c->stream));
+  std::vector<double> inv(c->hd / 2);
+  for (int i = 0; i < c->hd / 2; ++i) inv[i] = pow((double)c->c.rope_theta, -2.0 * i / c->hd);
+  CKD(c, hipMemcpyAsync(c->d_inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice,
+                        c->stream));
+  CKD(c, hipStreamSynchronize(c->stream));
+  // pinned host staging
+  CKD(c, hipHostMalloc((void**)&c->h_frames, sizeof(int) * B * c->NCH, hipHostMallocDefault));
+  CKD(c, hipHostMalloc((void**)&c->h_live, sizeof(int) * B, hipHostMallocDefault));
+  CKD(c, hipHostMalloc((void**)&c->h_pos, sizeof(int64_t) * B, hipHostMallocDefault));
+  CKD(c, hipHostMalloc((void**)&c->h_tokens, sizeof(int) * B, hipHostMallocDefault));
+  CKD(c, hipHostMalloc((void**)&c->h_codes, sizeof(int) * B * S, hipHostMallocDefault));
+  return MOSHI_OK;
+}
+
+void release(moshi_ctx* c) {
+  if (!c) return;
+  (void)hipSetDevice(c->device);
+  if (c->stream) (void)hipStreamSynchronize(c->stream);
+  if (c->g_temporal) (void)hipGraphExecDestroy(c->g_temporal);
+  if (c->g_dep) (void)hipGraphExecDestroy(c->g_dep);
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  for (void* p : c->dev_alloc) (void)hipFree(p);
+  if (c->h_frames) (void)hipHostFree(c->h_frames);
+  if (c->h_live) (void)hipHostFree(c->h_live);
+  if (c->h_pos) (void)hipHostFree(c->h_pos);
+  if (c->h_tokens) (void)hipHostFree(c->h_tokens);
+  if (c->h_codes) (void)hipHostFree(c->h_codes);
+  if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
+  delete c;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+
+extern "C" {
+
+int32_t moshi_n_tensors(const moshi_config* cfg) {
+  if (config_error(cfg)) return MOSHI_E_INVALID;
+  return tensor_count(cfg);
+}
+
+const char* moshi_strerror(int status) {
+  switch (status) {
+    case MOSHI_OK: return "ok";
+    case MOSHI_E_INVALID: return "invalid argument";
+    case MOSHI_E_FULL: return "all session slots are taken";
+    case MOSHI_E_NOSESSION: return "no live session in that slot";
+    case MOSHI_E_DEVICE: return "device error";
+    case MOSHI_E_OOM: return "out of device memory";
+  }
+  return "unknown status";
+}
+
+const char* moshi_last_error(const moshi_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+const char* moshi_kernel_class_name(int32_t c) {
+  return (c >= 0 && c < KC_COUNT) ? kClassNames[c] : "";
+}
+
+int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_tensors,
+                 void* hip_stream, moshi_ctx** out) {
+  if (!out) return MOSHI_E_INVALID;
+  *out = nullptr;
+  if (config_error(cfg) || !tensors) return MOSHI_E_INVALID;
+  if (n_tensors != tensor_count(cfg)) return MOSHI_E_INVALID;
+  for (int i = 0; i < n_tensors; ++i)
+    if (!tensors[i]) return MOSHI_E_INVALID;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return MOSHI_E_DEVICE;
+
+  moshi_ctx* c = new moshi_ctx();
+  c->c = *cfg;
+  c->B = cfg->max_sessions;
+  c->dtype = cfg->dtype == MOSHI_BF16 ? DT_BF16 : DT_F32;
+  c->esz = cfg->dtype == MOSHI_BF16 ? 2 : 4;
+  c->D = cfg->dim; c->H = cfg->n_heads; c->hd = cfg->dim / cfg->n_heads; c->F = cfg->ffn_hidden;
+  c->W = cfg->window; c->L = cfg->n_layers;
+  c->Dd = cfg->dep_dim; c->Hd = cfg->dep_heads; c->hdd = cfg->dep_dim / cfg->dep_heads;
+  c->Fd = cfg->dep_ffn_hidden; c->Ld = cfg->dep_layers; c->S = cfg->n_substeps;
+  c->Vt = cfg->text_vocab; c->Va = cfg->audio_card; c->NCH = 1 + cfg->n_substeps;
+  c->live.assign(c->B, 0);
+  c->pos.assign(c->B, 0);
+  const char* ng = getenv("MOSHI_NO_GRAPH");
+  c->use_graphs = !(ng && ng[0] == '1');
+  if (hipGetDevice(&c->device) != hipSuccess) {
+    release(c);
+    return MOSHI_E_DEVICE;
+  }
+  int rc = MOSHI_OK;
+  if (hip_stream) {
+    c->stream = (hipStream_t)hip_stream;
+  } else {
+    if (hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking) != hipSuccess) {
+      release(c);
+      return MOSHI_E_DEVICE;
+    }
+    c->own_stream = true;
+  }
+  if ((rc = alloc_buffers(c)) || (rc = upload_weights(c, tensors))) {
+    release(c);
+    return rc;
+  }
+  *out = c;
+  return MOSHI_OK;
+}
+
+int moshi_destroy(moshi_ctx* ctx) {
+  release(ctx);
+  return MOSHI_OK;
+}
+
+int moshi_session_join(moshi_ctx* ctx, int32_t* slot_out) {
+  if (!ctx || !slot_out) return MOSHI_E_INVALID;
+  if (ctx->failed) return MOSHI_E_DEVICE;
+  for (int b = 0; b < ctx->B; ++b)
+    if (!ctx->live[b]) {
+      ctx->live[b] = 1;
+      ctx->pos[b] = 0;
+      ctx->meta_dirty = true;
+      *slot_out = b;
+      return MOSHI_OK;
+    }
+  return fail(ctx, MOSHI_E_FULL, "every slot is live");
+}
+
+int moshi_session_leave(moshi_ctx* ctx, int32_t slot) {
+  if (!ctx) return MOSHI_E_INVALID;
+  if (ctx->failed) return MOSHI_E_DEVICE;
+  if (slot < 0 || slot >= ctx->B || !ctx->live[slot]) return fail(ctx, MOSHI_E_NOSESSION, "slot not live");
+  ctx->live[slot] = 0;
+  ctx->pos[slot] = 0;
+  ctx->meta_dirty = true;
+  return MOSHI_OK;
+}
+
+int moshi_step(moshi_ctx* ctx, const int32_t* frames, int32_t* text_token, int32_t* audio_codes) {
+  return run_step(ctx, frames, text_token, audio_codes, true);
+}
+
+int moshi_step_enqueue(moshi_ctx* c, const int32_t* d_frames, int32_t* d_text_token,
+                       int32_t* d_audio_codes) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!d_frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
+  if ((rc = ensure_graphs(c))) return rc;
+  if ((rc = upload_meta(c))) return rc;
+  CKD(c, hipMemcpyAsync(c->d_frames, d_frames, sizeof(int) * c->B * c->NCH,
+                        hipMemcpyDeviceToDevice, c->stream));
+  if ((rc = launch_part(c, true))) return rc;
+  if ((rc = launch_part(c, false))) return rc;
+  if (d_text_token)
+    CKD(c, hipMemcpyAsync(d_text_token, c->tokens, sizeof(int) * c->B, hipMemcpyDeviceToDevice,
+                          c->stream));
+  if (d_audio_codes)
+    CKD(c, hipMemcpyAsync(d_audio_codes, c->codes, sizeof(int) * c->B * c->S,
+                          hipMemcpyDeviceToDevice, c->stream));
+  for (int b = 0; b < c->B; ++b)
+    if (c->live[b]) c->pos[b] += 1;
+  return MOSHI_OK;
+}
+
+int moshi_sync(moshi_ctx* c) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  int bad = 0;
+  CKD(c, hipMemcpyAsync(&bad, c->d_err, sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  CKD(c, hipStreamSynchronize(c->stream));
+  if (bad) {
+    CKD(c, hipMemsetAsync(c->d_err, 0, sizeof(int), c->stream));
+    CKD(c, hipStreamSynchronize(c->stream));
+    return fail(c, MOSHI_E_INVALID, "a live frame code was out of range (clamped)");
+  }
+  return MOSHI_OK;
+}
+
+int moshi_temporal_step(moshi_ctx* ctx, const int32_t* frames, int32_t* text_token) {
+  return run_step(ctx, frames, text_token, nullptr, false);
+}
+
+int moshi_depformer_step(moshi_ctx* c, const void* hidden, const int32_t* text_in,
+                         int32_t* audio_codes) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!hidden || !text_in) return fail(c, MOSHI_E_INVALID, "NULL argument");
+  for (int b = 0; b < c->B; ++b)
+    if (c->live[b] && (text_in[b] < 0 || text_in[b] > c->Vt))
+      return fail(c, MOSHI_E_INVALID, "text token out of range");
+  if ((rc = ensure_graphs(c))) return rc;
+  if ((rc = upload_step_inputs(c, nullptr))) return rc;
+  for (int b = 0; b < c->B; ++b) c->h_tokens[b] = c->live[b] ? text_in[b] : 0;
+  CKD(c, hipMemcpyAsync(c->tokens, c->h_tokens, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
+  CKD(c, hipMemcpyAsync(c->hid, hidden, (size_t)c->B * c->D * c->esz, hipMemcpyHostToDevice, c->stream));
+  if ((rc = launch_part(c, false))) return rc;
+  CKD(c, hipMemcpyAsync(c->h_codes, c->codes, sizeof(int) * c->B * c->S, hipMemcpyDeviceToHost, c->stream));
+  CKD(c, hipStreamSynchronize(c->stream));
+  if (audio_codes)
+    for (int b = 0; b < c->B; ++b)
+      for (int s = 0; s < c->S; ++s)
+        audio_codes[(size_t)b * c->S + s] = c->live[b] ? c->h_codes[(size_t)b * c->S + s] : -1;
+  return MOSHI_OK;
+}
+
+int moshi_session_prefill_kv(moshi_ctx* c, int32_t slot, int32_t n, const void* k, const void* v) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (slot < 0 || slot >= c->B || !c->live[slot]) return fail(c, MOSHI_E_NOSESSION, "slot not live");
+  if (n < 0 || n > c->W) return fail(c, MOSHI_E_INVALID, "prefill length outside [0, window]");
+  if (n > 0 && (!k || !v)) return fail(c, MOSHI_E_INVALID, "NULL prefill data");
+  const size_t layer_elems = (size_t)n * c->D;
+  const int64_t slot_stride = (int64_t)c->L * c->H * c->W * c->hd;
+  for (int l = 0; l < c->L && n > 0; ++l) {
+    for (int kv = 0; kv < 2; ++kv) {
+      const char* src = (const char*)(kv == 0 ? k : v) + (size_t)l * layer_elems * c->esz;
+      char* ring = (char*)(kv == 0 ? c->ring_k : c->ring_v) +
+                   ((size_t)slot * slot_stride + (size_t)l * c->H * c->W * c->hd) * c->esz;
+      CKD(c, hipMemcpyAsync(c->staging, src, layer_elems * c->esz, hipMemcpyHostToDevice, c->stream));
+      CKD(c, launch_scatter_prefill(c->dtype, c->staging, ring, n, c->H, c->hd,
+                                    (int64_t)c->W * c->hd, c->stream));
+    }
+  }
+  CKD(c, hipStreamSynchronize(c->stream));
+  c->pos[slot] = n;
+  c->meta_dirty = true;
+  return MOSHI_OK;
+}
+
+int moshi_session_info(moshi_ctx* c, int32_t slot, int64_t* pos, int32_t* fill, int32_t* write_idx) {
+  if (!c) return MOSHI_E_INVALID;
+  if (slot < 0 || slot >= c->B || !c->live[slot]) return fail(c, MOSHI_E_NOSESSION, "slot not live");
+  const int64_t p = c->pos[slot];
+  if (pos) *pos = p;
+  if (fill) *fill = (int32_t)(p < c->W ? p : c->W);
+  if (write_idx) *write_idx = (int32_t)(p % c->W);
+  return MOSHI_OK;
+}
+
+int moshi_read_logits(moshi_ctx* c, float* text, float* audio) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (text)
+    CKD(c, hipMemcpy(text, c->text_logits, sizeof(float) * c->B * c->Vt, hipMemcpyDeviceToHost));
+  if (audio)
+    CKD(c, hipMemcpy(audio, c->audio_logits, sizeof(float) * c->B * c->S * c->Va,
+                     hipMemcpyDeviceToHost));
+  return MOSHI_OK;
+}
+
+int moshi_read_hidden(moshi_ctx* c, float* hidden) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!hidden) return fail(c, MOSHI_E_INVALID, "NULL argument");
+  const size_t n = (size_t)c->B * c->D;
+  if (c->dtype == DT_F32) {
+    CKD(c, hipMemcpy(hidden, c->hid, n * 4, hipMemcpyDeviceToHost));
+  } else {
+    std::vector<uint16_t> tmp(n);
+    CKD(c, hipMemcpy(tmp.data(), c->hid, n * 2, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < n; ++i) {
+      uint32_t u = (uint32_t)tmp[i] << 16;
+      memcpy(&hidden[i], &u, 4);
+    }
+  }
+  return MOSHI_OK;
+}
+
+int moshi_time_kernels(moshi_ctx* c, const int32_t* frames, int32_t n_steps, double* ms,
+                       int64_t* launches, double* bytes, int32_t n_classes) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (n_steps < 0 || n_classes < 0) return fail(c, MOSHI_E_INVALID, "negative count");
+  if ((rc = validate_frames(c, frames))) return rc;
+  std::vector<double> acc_ms(KC_COUNT, 0.0), acc_b(KC_COUNT, 0.0);
+  std::vector<int64_t> acc_n(KC_COUNT, 0);
+  c->timing = true;
+  for (int it = 0; it < n_steps; ++it) {
+    c->ev_used = 0;
+    c->ev_class.clear();
+    c->ev_bytes.clear();
+    rc = run_step(c, frames, nullptr, nullptr, true);
+    if (rc) break;
+    for (size_t i = 0; i < c->ev_class.size(); ++i) {
+      float t = 0.f;
+      hipError_t e = hipEventElapsedTime(&t, c->ev[2 * i], c->ev[2 * i + 1]);
+      if (e != hipSuccess) {
+        rc = device_fail(c, e, "hipEventElapsedTime");
+        break;
+      }
+      acc_ms[c->ev_class[i]] += t;
+      acc_b[c->ev_class[i]] += c->ev_bytes[i];
+      acc_n[c->ev_class[i]] += 1;
+    }
+    if (rc) break;
+  }
+  c->timing = false;
+  if (rc) return rc;
+  for (int k = 0; k < n_classes && k < KC_COUNT; ++k) {
+    if (ms) ms[k] = acc_ms[k];
+    if (launches) launches[k] = acc_n[k];
+    if (bytes) bytes[k] = acc_b[k];
+  }
+  return KC_COUNT;
+}
+
+}  // extern "C"

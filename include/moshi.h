@@ -1,0 +1,191 @@
+/*
+ * moshi.h -- C ABI of the MI355X Moshi/PersonaPlex frame-step library
+ * (libmoshi.so).
+ *
+ * One call of moshi_step() advances every live session slot by one 80 ms
+ * frame: one 17-row token column in (text, 8 agent codes, 8 user codes), one
+ * text token and 16 audio codes out ("vLLM-Omni recipe: PersonaPlex", sections
+ * "Why it is different" and "Architecture"). Sessions join and leave between
+ * steps without disturbing the others ("When to use this recipe"; "Notes":
+ * joins beyond the capacity are refused, a recycled slot behaves like a fresh
+ * engine).
+ *
+ * Conventions shared by every entry point:
+ *  - Every call returns an int status: MOSHI_OK (0) or a negative MOSHI_E_*.
+ *    On any error nothing observable changes (no session state moves), except
+ *    that a device failure makes the context sticky-failed (every later call
+ *    returns MOSHI_E_DEVICE).
+ *  - All pointers in the signatures are HOST pointers owned by the caller; the
+ *    library copies what it needs before returning. The library owns all
+ *    device memory and the context.
+ *  - A context is not thread-safe: use one thread per context.
+ *  - B below is the capacity `max_sessions` fixed at creation; per-slot arrays
+ *    have B rows indexed by slot. Rows of slots that are not live are ignored
+ *    on input and written as -1 on output.
+ */
+#ifndef MOSHI_H
+#define MOSHI_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moshi_ctx moshi_ctx;
+
+enum {
+  MOSHI_OK = 0,
+  MOSHI_E_INVALID = -1,   /* bad argument, config or code; nothing changed */
+  MOSHI_E_FULL = -2,      /* join with every slot taken */
+  MOSHI_E_NOSESSION = -3, /* slot out of range or not live */
+  MOSHI_E_DEVICE = -4,    /* HIP error; the context is now unusable */
+  MOSHI_E_OOM = -5        /* device allocation failed at creation */
+};
+
+enum { MOSHI_F32 = 0, MOSHI_BF16 = 1 };
+
+/* Window reading flag: once a session's ring is full, also mask the oldest
+ * key (W-1 keys attended instead of W) -- the SGLang-Omni cookbook's
+ * "Known limitations" mentions such a masked oldest slot. Default off. */
+#define MOSHI_FLAG_MASK_OLDEST 1u
+
+/* Model shape and engine capacity.
+ * Temporal transformer: `dim`, `n_layers`, `n_heads` (head_dim = dim/n_heads
+ * must be 32, 64 or 128; the same holds for the depformer), SwiGLU width
+ * `ffn_hidden`, ring window `window` frames (mobius PR #368, "P2 - Moshi LM";
+ * recipe "Architecture": 4096-d, 32 layers, 32 heads, window 3000).
+ * Depformer: `dep_dim`, `dep_layers`, `dep_heads`, `dep_ffn_hidden`,
+ * `n_substeps` substeps (1024-d, 6 layers, 16 heads, 16 substeps).
+ * Vocabularies: `text_vocab` (32000), `audio_card` (2048); the token column
+ * has 1 + n_substeps rows and every embedding table has card+1 rows.
+ * `dtype` MOSHI_BF16 or MOSHI_F32 (weights, K/V and linear inputs);
+ * `max_sessions` = capacity B (1..64), fixed for the life of the context.
+ * Every width (dim, ffn_hidden, dep_dim, dep_ffn_hidden) must be a multiple of
+ * 8 (bf16) or 4 (fp32). */
+typedef struct {
+  int32_t dim, n_layers, n_heads, ffn_hidden, window;
+  int32_t dep_dim, dep_layers, dep_heads, dep_ffn_hidden, n_substeps;
+  int32_t text_vocab, audio_card;
+  float rope_theta, norm_eps;
+  int32_t dtype, max_sessions;
+  uint32_t flags;
+} moshi_config;
+
+/* Number of weight tensors moshi_create expects for this config (< 0 on a bad
+ * config). */
+int32_t moshi_n_tensors(const moshi_config* cfg);
+
+/* Creates a context and uploads the weights.
+ * tensors: n_tensors host pointers in the order below, each row-major in the
+ * config's dtype (uint16 bf16 bit patterns or float32); copied, so the caller
+ * may free them afterwards. A matrix [N, K] maps a K-vector to N outputs.
+ *   emb.text [Vt+1, D]; emb.audio.k [Va+1, D] for k < S;
+ *   per temporal layer l: attn_norm [D], qkv [3D, D] (rows q|k|v),
+ *     o [D, D], mlp_norm [D], gate_up [2F, D] (rows gate|up), down [D, F];
+ *   out_norm [D]; text_head [Vt, D];
+ *   dep.in.s [Dd, D] for s < S; dep.emb.0 [Vt+1, Dd]; dep.emb.s [Va+1, Dd];
+ *   per depformer layer l: attn_norm [Dd], mlp_norm [Dd] (shared by substeps);
+ *   per substep s, per layer l: qkv [3Dd, Dd], o [Dd, Dd],
+ *     gate_up [2Fd, Dd], down [Dd, Fd];
+ *   dep.head.s [Va, Dd] for s < S.
+ * hip_stream: a hipStream_t created by the caller (not the legacy default
+ * stream) that every launch and copy uses, or NULL for a library-owned
+ * stream. A borrowed stream is never destroyed.
+ * Errors: MOSHI_E_INVALID (bad config / count / NULL), MOSHI_E_OOM,
+ * MOSHI_E_DEVICE (no GPU or a HIP failure). *out is NULL on error. */
+int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_tensors,
+                 void* hip_stream, moshi_ctx** out);
+
+/* Frees the context and its device memory. NULL is accepted. */
+int moshi_destroy(moshi_ctx* ctx);
+
+/* Opens a session in the lowest free slot: position 0, empty window.
+ * MOSHI_E_FULL when all B slots are live. */
+int moshi_session_join(moshi_ctx* ctx, int32_t* slot_out);
+
+/* Closes a live session; its slot becomes free for the next join.
+ * MOSHI_E_NOSESSION if the slot is out of range or not live. */
+int moshi_session_leave(moshi_ctx* ctx, int32_t slot);
+
+/* One frame for every live slot (synchronous: returns when the outputs are on
+ * the host).
+ * frames [B, 1+S] int32: row = slot; text code in [0, Vt], audio codes in
+ *   [0, Va] (the last row of each table is the initial token). Any live row
+ *   out of range -> MOSHI_E_INVALID before any device work, state unchanged.
+ * text_token [B]: greedy text token (lowest index on ties).
+ * audio_codes [B, S]: greedy code of each depformer substep; substep s
+ *   consumes code s-1 (the text token at s = 0).
+ * Each live slot's position advances by one; the frame's K/V are written into
+ * the slot's ring at position mod W. */
+int moshi_step(moshi_ctx* ctx, const int32_t* frames, int32_t* text_token, int32_t* audio_codes);
+
+/* Device-resident step, for callers whose codes already live in HBM (a codec
+ * on the same GPU): enqueues one moshi_step on the context's stream and
+ * returns without waiting.
+ * d_frames: DEVICE pointer to [B, 1+S] int32 codes, read when the step runs.
+ *   Codes are not checked on the host; a live code outside its table is
+ *   clamped to the nearest valid row and reported by the next moshi_sync.
+ * d_text_token [B], d_audio_codes [B, S]: DEVICE pointers that receive the
+ *   outputs (either may be NULL; the last outputs also stay readable through
+ *   moshi_read_logits). Live slots' positions advance by one per call. */
+int moshi_step_enqueue(moshi_ctx* ctx, const int32_t* d_frames, int32_t* d_text_token,
+                       int32_t* d_audio_codes);
+
+/* Waits for every enqueued step. MOSHI_E_INVALID if a clamped code was seen
+ * since the last call (the flag is then cleared). */
+int moshi_sync(moshi_ctx* ctx);
+
+/* ---- test and benchmark hooks (same kernels as moshi_step) ---- */
+
+/* Temporal transformer and text head only (the depformer is not run); the
+ * positions advance as in moshi_step. text_token [B]. */
+int moshi_temporal_step(moshi_ctx* ctx, const int32_t* frames, int32_t* text_token);
+
+/* Depformer only, from a given hidden state: hidden [B, D] in the config's
+ * dtype (the temporal output after its final norm), text_in [B] in [0, Vt].
+ * audio_codes [B, S]. Positions do not move. Rows of non-live slots ignored. */
+int moshi_depformer_step(moshi_ctx* ctx, const void* hidden, const int32_t* text_in,
+                         int32_t* audio_codes);
+
+/* Loads K and V of positions 0..n-1 of a live slot (n in [0, W]) and sets its
+ * position to n. k, v: [L][n][D] in the config's dtype, already rotated
+ * (post-RoPE), head h at columns h*head_dim.. of each row. */
+int moshi_session_prefill_kv(moshi_ctx* ctx, int32_t slot, int32_t n, const void* k,
+                             const void* v);
+
+/* Bookkeeping of a live slot's next step: absolute position (frames consumed),
+ * fill = min(pos, W), ring write index = pos mod W. */
+int moshi_session_info(moshi_ctx* ctx, int32_t slot, int64_t* pos, int32_t* fill,
+                       int32_t* write_idx);
+
+/* Logits of the last step: text [B, Vt] and/or audio [B, S, Va] (float32;
+ * either may be NULL). Rows of non-live slots are unspecified. */
+int moshi_read_logits(moshi_ctx* ctx, float* text, float* audio);
+
+/* Temporal hidden state of the last step (after the final norm and rounding),
+ * [B, D] float32. */
+int moshi_read_hidden(moshi_ctx* ctx, float* hidden);
+
+/* Kernel timing. Runs `n_steps` full steps (frames as in moshi_step, outputs
+ * discarded; positions advance) launching every kernel eagerly with a HIP
+ * event pair around it on the library's stream, and returns per kernel class
+ * c < n_classes: the summed device time in ms (ms[c]), the launch count
+ * (launches[c]) and the algorithmic bytes moved (bytes[c]: weights read once,
+ * K/V attended and written). Class names: moshi_kernel_class_name(c).
+ * Returns the number of classes (>= 0) or an error. */
+int moshi_time_kernels(moshi_ctx* ctx, const int32_t* frames, int32_t n_steps, double* ms,
+                       int64_t* launches, double* bytes, int32_t n_classes);
+const char* moshi_kernel_class_name(int32_t c);
+
+/* Static text of a status code. */
+const char* moshi_strerror(int status);
+
+/* Detail of the last error on this context (never NULL). */
+const char* moshi_last_error(const moshi_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOSHI_H */

@@ -61,12 +61,39 @@ static inline uint16_t f32_to_bf16_rne(float f) {
 
 /* ---- single-threaded kernels over [offset, offset+count) ---- */
 
+/* Both draws of Box-Muller pair j (elements 2j and 2j+1). */
+static inline void normal_pair(uint64_t key, uint64_t j, double* z0, double* z1) {
+  double u1 = unit(draw(key, 2 * j));
+  double u2 = unit(draw(key, 2 * j + 1));
+  double r = sqrt(-2.0 * log(u1));
+  double t = 6.283185307179586476925286766559 * u2;
+  *z0 = r * cos(t);
+  *z1 = r * sin(t);
+}
+
+static void fill_normal_any(uint64_t key, uint64_t off, uint64_t cnt, double stdv, void* out,
+                            int bf16) {
+  uint64_t i = 0;
+  while (i < cnt) {
+    uint64_t e = off + i;
+    double z[2];
+    normal_pair(key, e >> 1, &z[0], &z[1]);
+    for (int h = (int)(e & 1); h < 2 && i < cnt; ++h, ++i) {
+      float f = (float)(stdv * z[h]);
+      if (bf16)
+        ((uint16_t*)out)[i] = f32_to_bf16_rne(f);
+      else
+        ((float*)out)[i] = f;
+    }
+  }
+}
+
 static void fill_normal_f32(uint64_t key, uint64_t off, uint64_t cnt, double stdv, float* out) {
-  for (uint64_t i = 0; i < cnt; ++i) out[i] = (float)(stdv * normal_at(key, off + i));
+  fill_normal_any(key, off, cnt, stdv, out, 0);
 }
 
 static void fill_normal_bf16(uint64_t key, uint64_t off, uint64_t cnt, double stdv, uint16_t* out) {
-  for (uint64_t i = 0; i < cnt; ++i) out[i] = f32_to_bf16_rne((float)(stdv * normal_at(key, off + i)));
+  fill_normal_any(key, off, cnt, stdv, out, 1);
 }
 
 /* ---- threaded front ends ---- */

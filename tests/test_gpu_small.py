@@ -1,0 +1,205 @@
+"""GPU parity of the HIP path against the fp64 oracle, at sizes the oracle
+finishes in seconds (several tiles, ragged tails, ring wrap-around), plus the
+slot-isolation, recycle, determinism and error-path properties."""
+import numpy as np
+import pytest
+
+import full_duplex_speech_amd as M
+import oracle
+from synth import spec, workloads as wl
+from gpu_util import Stats, cfg_of, compare_frame, frames_matrix, log, new_engine
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_sessions(shape, weights, B, plan, T, seed=77, check=True):
+    """Run T ticks. plan: {tick: [("join", sid, fill) | ("leave", sid)]} applied
+    before the tick. Every live session is checked against its own oracle."""
+    ctx = new_engine(shape, weights, B)
+    om = oracle.Model(shape, weights)
+    slot_of, orc, t_of = {}, {}, {}
+    stats = Stats()
+    outs = {}
+    for t in range(T):
+        for act in plan.get(t, []):
+            if act[0] == "leave":
+                M.moshi_session_leave(ctx, slot_of.pop(act[1]))
+            else:
+                sid, fill = act[1], act[2]
+                slot = M.moshi_session_join(ctx)
+                slot_of[sid] = slot
+                k, v = wl.prefill_kv(shape, seed + 1, sid, fill)
+                M.moshi_session_prefill_kv(ctx, slot, k, v)
+                o = oracle.Session(om)
+                o.prefill(k, v)
+                orc[sid] = o
+                t_of[sid] = 0
+        rows = {slot_of[sid]: wl.frames(shape, seed, sid, t_of[sid], 1)[0] for sid in slot_of}
+        f = frames_matrix(shape, B, rows)
+        tok, codes = M.moshi_step(ctx, f)
+        tl, al = M.moshi_read_logits(ctx)
+        for b in range(B):
+            if b not in rows:
+                assert tok[b] == -1 and (codes[b] == -1).all()
+        for sid, slot in slot_of.items():
+            outs.setdefault(sid, []).append((tok[slot], codes[slot].copy(), tl[slot].copy(),
+                                             al[slot].copy()))
+            if check:
+                pre = orc[sid].info()
+                assert M.moshi_session_info(ctx, slot)[0] == pre[0] + 1
+                r = orc[sid].step(rows[slot], forced_text=int(tok[slot]), forced_codes=codes[slot])
+                compare_frame(shape, stats, f"t={t} sid={sid} slot={slot}", int(tok[slot]),
+                              codes[slot], tl[slot], al[slot], r)
+                assert M.moshi_session_info(ctx, slot) == orc[sid].info()
+            t_of[sid] += 1
+    M.moshi_destroy(ctx)
+    return outs, stats
+
+
+def test_tiny_fp32_workload_parity():
+    """Workload 1: tiny fp32 model, B=1, 100 frames, the 64-frame ring wraps."""
+    w = wl.WORKLOADS[1]
+    shape = w.shape()
+    weights = wl.make_weights(shape, wl.MODEL_SEEDS["tiny"])
+    log("tiny: weights ready")
+    _, stats = _run_sessions(shape, weights, 1, {0: [("join", 0, 0)]}, w.frames,
+                             seed=w.seed("frames"))
+    log("tiny:", stats)
+
+
+def test_ragged_bf16_elastic_parity():
+    """Ragged bf16 model (no dimension a multiple of the tiles), 3 slots with
+    different prefills, wrap-around, a leave and a recycled slot."""
+    shape = spec.RAGGED
+    weights = wl.make_weights(shape, wl.MODEL_SEEDS["ragged"], gains="random")
+    plan = {0: [("join", 0, 0), ("join", 1, 20), ("join", 2, 37)],
+            30: [("leave", 1), ("join", 3, 5)],
+            55: [("leave", 0)],
+            60: [("join", 4, 0)]}
+    _, stats = _run_sessions(shape, weights, 3, plan, 90)
+    log("ragged:", stats)
+
+
+def test_mask_oldest_parity():
+    shape = spec.RAGGED.replace(mask_oldest=True, window=9)
+    weights = wl.make_weights(shape, 5, gains="random")
+    plan = {0: [("join", 0, 0), ("join", 1, 9)]}
+    _, stats = _run_sessions(shape, weights, 2, plan, 25)
+    log("mask_oldest:", stats)
+
+
+def test_tiny_fp32_batched_ragged_capacity():
+    """fp32 model with capacity 5 (ragged column tile), window 7."""
+    shape = spec.TINY.replace(window=7)
+    weights = wl.make_weights(shape, 9, gains="random")
+    plan = {0: [("join", i, [0, 3, 7, 1, 5][i]) for i in range(5)]}
+    _, stats = _run_sessions(shape, weights, 5, plan, 20)
+    log("tiny B=5:", stats)
+
+
+def test_isolation_and_recycle_bit_exact():
+    """A session's outputs are bit-identical alone in slot 0 of a fresh engine
+    and batched in slot 2 among others; a recycled slot equals a fresh one."""
+    shape = spec.RAGGED
+    weights = wl.make_weights(shape, 13, gains="random")
+    B = 4
+    batched, _ = _run_sessions(shape, weights, B, {0: [("join", 10, 4), ("join", 11, 0),
+                                                        ("join", 12, 11), ("join", 13, 30)]},
+                               20, check=False)
+    alone, _ = _run_sessions(shape, weights, B, {0: [("join", 12, 11)]}, 20, check=False)
+    # recycle: slot 2 first hosts another session that leaves, then session 12 joins there
+    recyc, _ = _run_sessions(shape, weights, B, {0: [("join", 20, 3), ("join", 21, 3),
+                                                     ("join", 22, 30)],
+                                                 7: [("leave", 22)],
+                                                 8: [("join", 12, 11)]}, 28, check=False)
+    for t in range(20):
+        a, b, r = alone[12][t], batched[12][t], recyc[12][t]
+        for x, y, z in zip(a, b, r):
+            assert np.array_equal(np.asarray(x), np.asarray(y)), f"isolation broken at t={t}"
+            assert np.array_equal(np.asarray(x), np.asarray(z)), f"recycle broken at t={t}"
+
+
+def test_run_twice_deterministic():
+    shape = spec.RAGGED
+    weights = wl.make_weights(shape, 17, gains="random")
+    plan = {0: [("join", 0, 37), ("join", 1, 2)]}
+    a, _ = _run_sessions(shape, weights, 2, plan, 10, check=False)
+    b, _ = _run_sessions(shape, weights, 2, plan, 10, check=False)
+    for sid in a:
+        for x, y in zip(a[sid], b[sid]):
+            for u, v in zip(x, y):
+                assert np.array_equal(np.asarray(u), np.asarray(v))
+
+
+def test_temporal_and_depformer_hooks():
+    """The temporal-only and depformer-only entry points agree with the oracle
+    and with the full step."""
+    shape = spec.RAGGED
+    weights = wl.make_weights(shape, 19, gains="random")
+    om = oracle.Model(shape, weights)
+    ctx = new_engine(shape, weights, 2)
+    s0 = M.moshi_session_join(ctx)
+    s1 = M.moshi_session_join(ctx)
+    o0, o1 = oracle.Session(om), oracle.Session(om)
+    stats = Stats()
+    for t in range(6):
+        f = np.stack([wl.frames(shape, 3, 0, t, 1)[0], wl.frames(shape, 3, 1, t, 1)[0]])
+        tok = M.moshi_temporal_step(ctx, f)
+        tl, _ = M.moshi_read_logits(ctx, audio=False)
+        hid = M.moshi_read_hidden(ctx)
+        for slot, o in ((s0, o0), (s1, o1)):
+            r = o.temporal(f[slot])
+            compare_frame(shape, stats, f"temporal t={t}", int(tok[slot]), None, tl[slot], None, r)
+            assert np.max(np.abs(hid[slot] - r["hidden"])) < 0.05
+    # depformer alone from a given hidden state
+    g = np.random.default_rng(5)
+    hid = g.normal(size=(2, shape.dim)).astype(np.float32)
+    hb = (hid.view(np.uint32) >> 16).astype(np.uint16)  # truncated to bf16 bits: any bf16 input
+    text_in = np.array([7, shape.text_vocab], np.int32)
+    codes = M.moshi_depformer_step(ctx, hb, text_in)
+    _, al = M.moshi_read_logits(ctx, text=False)
+    from synth.rng import bf16_to_f32
+    for slot in (0, 1):
+        r = om.depformer(bf16_to_f32(hb[slot]).astype(np.float64), int(text_in[slot]),
+                         forced=codes[slot])
+        r["text_margin"] = np.inf
+        r["text_token"] = 0
+        compare_frame(shape, stats, f"depformer slot={slot}", 0, codes[slot], None, al[slot], r)
+    log("hooks:", stats)
+    M.moshi_destroy(ctx)
+
+
+def test_error_paths_leave_state_unchanged():
+    shape = spec.RAGGED
+    weights = wl.make_weights(shape, 23)
+    ctx = new_engine(shape, weights, 2)
+    a = M.moshi_session_join(ctx)
+    b = M.moshi_session_join(ctx)
+    with pytest.raises(M.MoshiError) as e:
+        M.moshi_session_join(ctx)
+    assert e.value.status == M.MOSHI_E_FULL
+    with pytest.raises(M.MoshiError) as e:
+        M.moshi_session_leave(ctx, 5)
+    assert e.value.status == M.MOSHI_E_NOSESSION
+    f = np.stack([wl.frames(shape, 1, 0, 0, 1)[0]] * 2)
+    M.moshi_step(ctx, f)
+    bad = f.copy()
+    bad[b, 3] = shape.audio_card + 1
+    with pytest.raises(M.MoshiError) as e:
+        M.moshi_step(ctx, bad)
+    assert e.value.status == M.MOSHI_E_INVALID
+    assert M.moshi_session_info(ctx, a)[0] == 1 and M.moshi_session_info(ctx, b)[0] == 1
+    k, v = wl.prefill_kv(shape.replace(window=shape.window + 1), 1, 0, shape.window + 1)
+    with pytest.raises(M.MoshiError) as e:
+        M.moshi_session_prefill_kv(ctx, a, k, v)
+    assert e.value.status == M.MOSHI_E_INVALID
+    M.moshi_session_leave(ctx, a)
+    with pytest.raises(M.MoshiError) as e:
+        M.moshi_session_info(ctx, a)
+    assert e.value.status == M.MOSHI_E_NOSESSION
+    # a free row with garbage codes is ignored
+    f2 = f.copy()
+    f2[a] = -5
+    tok, codes = M.moshi_step(ctx, f2)
+    assert tok[a] == -1 and tok[b] >= 0
+    M.moshi_destroy(ctx)
