@@ -18,7 +18,6 @@ import argparse
 import json
 import os
 import sys
-import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -187,7 +186,8 @@ def main():
         b16 = {"frames_per_s": round(16 * 1000.0 / ms16, 1), "ms_per_step": round(ms16, 4),
                "rtf": round(ms16 / FRAME_MS, 5), "bytes_per_step": by16,
                "hbm_frac_step": round(by16 / (ms16 * 1e6) / HBM_PEAK_GBS, 4),
-               "fills": "U{0..3000} per slot (workload 4 at t=0)", "steps": n16}
+               "fills": "U{0..3000} per slot (workload 4 at t=0)", "steps": n16,
+               "kernels": kt16}
         log(f"B=16: {ms16:.3f} ms/step, {b16['frames_per_s']} frames/s")
         M.moshi_destroy(ctx)
         del ctx

@@ -63,7 +63,7 @@ class moshi_config(ctypes.Structure):
         "dim", "n_layers", "n_heads", "ffn_hidden", "window",
         "dep_dim", "dep_layers", "dep_heads", "dep_ffn_hidden", "n_substeps",
         "text_vocab", "audio_card")] + [
-        ("rope_theta", ctypes.c_float), ("norm_eps", ctypes.c_float),
+        ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_double),
         ("dtype", ctypes.c_int32), ("max_sessions", ctypes.c_int32), ("flags", ctypes.c_uint32)]
 
 
@@ -89,6 +89,7 @@ def lib():
             "moshi_depformer_step": ([vp, vp, vp, vp], ctypes.c_int),
             "moshi_session_prefill_kv": ([vp, i32, i32, vp, vp], ctypes.c_int),
             "moshi_session_info": ([vp, i32, vp, vp, vp], ctypes.c_int),
+            "moshi_session_read_kv": ([vp, i32, vp, vp], ctypes.c_int),
             "moshi_read_logits": ([vp, vp, vp], ctypes.c_int),
             "moshi_read_hidden": ([vp, vp], ctypes.c_int),
             "moshi_time_kernels": ([vp, vp, i32, vp, vp, vp, i32], ctypes.c_int),
@@ -229,6 +230,16 @@ def moshi_session_prefill_kv(ctx: Ctx, slot: int, k, v):
     k = None if n == 0 else np.ascontiguousarray(k)
     v = None if n == 0 else np.ascontiguousarray(v)
     _check(lib().moshi_session_prefill_kv(ctx.h, int(slot), n, _p(k), _p(v)), ctx)
+
+
+def moshi_session_read_kv(ctx: Ctx, slot: int):
+    """The slot's ring: (k, v) [L][W][D] in the model dtype (ring-slot order)."""
+    c = ctx.cfg
+    dt = np.uint16 if ctx.esz == 2 else np.float32
+    k = np.empty((c.n_layers, c.window, c.dim), dt)
+    v = np.empty_like(k)
+    _check(lib().moshi_session_read_kv(ctx.h, int(slot), _p(k), _p(v)), ctx)
+    return k, v
 
 
 def moshi_session_info(ctx: Ctx, slot: int):

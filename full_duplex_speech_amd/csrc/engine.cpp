@@ -42,17 +42,15 @@ enum KClass {
   KC_D_GATEUP,
   KC_D_DOWN,
   KC_D_HEAD,
+  KC_T_COMBINE,
+  KC_ARGMAX,
   KC_COUNT
 };
 const char* kClassNames[KC_COUNT] = {
     "embed",      "temporal_qkv",  "temporal_attn", "temporal_o",    "temporal_gateup",
     "temporal_down", "text_head",  "dep_inproj",    "dep_entry",     "dep_qkv",
-    "dep_attn",   "dep_o",         "dep_gateup",    "dep_down",      "dep_head"};
-
-// Waves per workgroup of the projections: the temporal ones have K = 4096 or
-// 11264 and many rows; the depformer ones K = 1024 / 2816 and few rows.
-constexpr int KW_TEMPORAL = 8;
-constexpr int KW_DEP = 4;
+    "dep_attn",   "dep_o",         "dep_gateup",    "dep_down",      "dep_head",
+    "temporal_attn_combine", "argmax_reduce"};
 
 bool valid_head_dim(int hd) { return hd == 32 || hd == 64 || hd == 128; }
 
@@ -79,7 +77,7 @@ const char* config_error(const moshi_config* c) {
   if (c->flags & ~MOSHI_FLAG_MASK_OLDEST) return "unknown flag bits";
   if (c->text_vocab < 2 || c->audio_card < 2) return "vocabularies must have >= 2 entries";
   if (c->max_sessions < 1 || c->max_sessions > 64) return "max_sessions must be in [1, 64]";
-  if (!(c->rope_theta > 0.f) || !(c->norm_eps >= 0.f)) return "rope_theta must be > 0 and norm_eps >= 0";
+  if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0)) return "rope_theta must be > 0 and norm_eps >= 0";
   return nullptr;
 }
 
@@ -104,21 +102,19 @@ struct moshi_ctx {
   const void* dep_in = nullptr;  // [S*Dd][D], contiguous
   std::vector<const void*> dep_emb, dep_attn_norm, dep_mlp_norm, dep_qkv, dep_o, dep_gate_up,
       dep_down, dep_head;
-  const void** d_tables = nullptr;  // [NCH] device copy of the embedding table pointers
 
   // state and activations (device)
   void *ring_k = nullptr, *ring_v = nullptr;  // [B][L][H][W][hd]
   void *dkv_k = nullptr, *dkv_v = nullptr;    // [B][Ld][Hd][S][hdd]
-  float *x = nullptr, *ssq = nullptr, *q = nullptr;
-  void *o = nullptr, *act = nullptr, *hid = nullptr;
-  float *pre = nullptr, *y = nullptr, *ssq_d = nullptr, *qd = nullptr;
+  double *x = nullptr, *ssq = nullptr, *q = nullptr;     // fp64 arithmetic state
+  void *o = nullptr, *act = nullptr, *hid = nullptr;      // model dtype
+  double *pre = nullptr, *y = nullptr, *ssq_d = nullptr, *qd = nullptr;
   void *od = nullptr, *actd = nullptr;
+  void *hn = nullptr, *hnd = nullptr;  // rounded norm outputs (two or more sessions)
   float *text_logits = nullptr, *audio_logits = nullptr;
   int *tokens = nullptr, *codes = nullptr;
-  ArgPart* apart = nullptr;
-  unsigned* tickets = nullptr;  // [1 + S] argmax tickets
-  float* attn_part = nullptr;
-  unsigned* attn_ticket = nullptr;  // [B][max(H, Hd)]
+  ArgPart* apart = nullptr;  // per-tile argmax partials of the last head
+  double* attn_part = nullptr;
   int *d_frames = nullptr, *d_live = nullptr;
   int64_t* d_pos = nullptr;
   int* d_err = nullptr;  // set by the embedding when a live code was out of range
@@ -218,6 +214,10 @@ GemmArgs gemm_base(const moshi_ctx* c) {
   return a;
 }
 
+hipError_t gemm(moshi_ctx* c, int pro, int epi, const GemmArgs& a) {
+  return launch_gemm(c->dtype, gemm_kw(c->dtype, a.B, a.K), pro, epi, a, c->stream);
+}
+
 // ---- the temporal step: embed, L layers, final norm + text head ----
 
 hipError_t enqueue_temporal(moshi_ctx* c) {
@@ -225,8 +225,13 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
   const double nlive = live_count(c);
   hipError_t e;
   {
-    EmbedArgs a{c->d_tables, c->d_frames, c->d_live, c->NCH, D, B, c->Vt + 1, c->Va + 1,
-                c->d_err, c->x, c->ssq};
+    EmbedArgs a;
+    memset(&a, 0, sizeof(a));
+    a.tables[0] = c->emb_text;
+    for (int k = 0; k < c->S; ++k) a.tables[1 + k] = c->emb_audio[k];
+    a.frames = c->d_frames; a.live = c->d_live; a.n_ch = c->NCH; a.D = D; a.B = B;
+    a.rows_text = c->Vt + 1; a.rows_audio = c->Va + 1; a.bad_code = c->d_err;
+    a.x = c->x; a.ssq_out = c->ssq;
     e = run(c, KC_EMBED, nlive * c->NCH * D * es, [&] { return launch_embed(dt, a, c->stream); });
     if (e != hipSuccess) return e;
   }
@@ -237,13 +242,14 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
       GemmArgs a = gemm_base(c);
       a.W = c->qkv[l]; a.N = 3 * D; a.K = D;
       a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->attn_norm[l];
+      a.xn_out = B > 1 ? c->hn : nullptr;
       a.q_out = c->q; a.dq = D; a.hd = c->hd; a.inv_freq = c->d_inv_freq; a.pos = c->d_pos;
       a.ring_k = c->ring_k; a.ring_v = c->ring_v; a.slot_stride = slot_stride;
       a.layer_off = (int64_t)l * c->H * c->W * c->hd; a.head_stride = (int64_t)c->W * c->hd;
       a.cap = c->W;
       double bytes = 3.0 * D * D * es + D * es + nlive * 2.0 * D * es;
       e = run(c, KC_T_QKV, bytes,
-              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_NORM, EPI_QKV, a, c->stream); });
+              [&] { return gemm(c, PRO_NORM, EPI_QKV, a); });
       if (e != hipSuccess) return e;
     }
     {  // window attention over the ring
@@ -254,7 +260,7 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
       a.head_stride = (int64_t)c->W * c->hd; a.cap = c->W; a.pos = c->d_pos; a.live = c->d_live;
       a.mask_oldest = (c->c.flags & MOSHI_FLAG_MASK_OLDEST) ? 1 : 0;
       a.n_heads = c->H; a.max_chunks = c->max_chunks; a.part = c->attn_part;
-      a.ticket = c->attn_ticket; a.o_out = c->o; a.ldo = D;
+      a.o_out = c->o; a.ldo = D;
       double keys = 0;
       for (int b = 0; b < B; ++b)
         if (c->live[b]) {
@@ -266,22 +272,27 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
       e = run(c, KC_T_ATTN, keys * 2.0 * D * es,
               [&] { return launch_attn(dt, c->hd, a, B, c->stream); });
       if (e != hipSuccess) return e;
+      if (c->max_chunks > 1) {
+        e = run(c, KC_T_COMBINE, 0.0, [&] { return launch_attn_combine(dt, c->hd, a, B, c->stream); });
+        if (e != hipSuccess) return e;
+      }
     }
     {  // o-projection + residual
       GemmArgs a = gemm_base(c);
       a.W = c->wo[l]; a.N = D; a.K = D; a.X = c->o; a.ldx = D;
       a.resid = c->x; a.ldr = D; a.ssq_out = c->ssq;
       e = run(c, KC_T_O, (double)D * D * es,
-              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_DIRECT, EPI_RESID, a, c->stream); });
+              [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
       if (e != hipSuccess) return e;
     }
     {  // RMSNorm -> gate|up -> SiLU(gate)*up
       GemmArgs a = gemm_base(c);
       a.W = c->gate_up[l]; a.N = F; a.K = D;
       a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->mlp_norm[l];
+      a.xn_out = B > 1 ? c->hn : nullptr;
       a.act = c->act; a.lda = F;
       e = run(c, KC_T_GATEUP, 2.0 * F * D * es + D * es,
-              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_NORM, EPI_SWIGLU, a, c->stream); });
+              [&] { return gemm(c, PRO_NORM, EPI_SWIGLU, a); });
       if (e != hipSuccess) return e;
     }
     {  // down + residual
@@ -289,7 +300,7 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
       a.W = c->down[l]; a.N = D; a.K = F; a.X = c->act; a.ldx = F;
       a.resid = c->x; a.ldr = D; a.ssq_out = c->ssq;
       e = run(c, KC_T_DOWN, (double)D * F * es,
-              [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_DIRECT, EPI_RESID, a, c->stream); });
+              [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
       if (e != hipSuccess) return e;
     }
   }
@@ -298,10 +309,13 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
     a.W = c->text_head; a.N = c->Vt; a.K = D;
     a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->out_norm;
     a.xn_out = c->hid;
-    a.out = c->text_logits; a.ldo = c->Vt; a.apart = c->apart; a.ticket = c->tickets;
-    a.tok_out = c->tokens; a.tok_stride = 1;
+    a.logits = c->text_logits; a.ldo = c->Vt; a.apart = c->apart;
     e = run(c, KC_T_HEAD, (double)c->Vt * D * es + D * es,
-            [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_NORM, EPI_ARGMAX, a, c->stream); });
+            [&] { return gemm(c, PRO_NORM, EPI_ARGMAX, a); });
+    if (e != hipSuccess) return e;
+    e = run(c, KC_ARGMAX, 0.0, [&] {
+      return launch_argmax_reduce(c->apart, (c->Vt + 15) / 16, c->Vt, B, c->tokens, 1, c->stream);
+    });
     if (e != hipSuccess) return e;
   }
   return launch_advance(c->d_pos, c->d_live, B, c->stream);
@@ -316,17 +330,22 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
   {  // y_pre[s] = W_in[s] . hidden for every substep at once
     GemmArgs a = gemm_base(c);
     a.W = c->dep_in; a.N = S * Dd; a.K = D; a.X = c->hid; a.ldx = D;
-    a.out = c->pre; a.ldo = S * Dd;
+    a.out64 = c->pre; a.ldo = S * Dd;
     e = run(c, KC_D_INPROJ, (double)S * Dd * D * es,
-            [&] { return launch_gemm(dt, KW_TEMPORAL, PRO_DIRECT, EPI_STORE, a, c->stream); });
+            [&] { return gemm(c, PRO_DIRECT, EPI_STORE, a); });
     if (e != hipSuccess) return e;
   }
   const int nt_dd = (Dd + 15) / 16;
   const int64_t slot_stride = (int64_t)c->Ld * c->Hd * S * c->hdd;
   for (int s = 0; s < S; ++s) {
-    {  // entry: y = pre[s] + E_s[previous token]
-      EntryArgs a{c->pre, S * Dd, s, c->dep_emb[s], s == 0 ? c->tokens : c->codes + (s - 1),
-                  s == 0 ? 1 : S, Dd, B, c->y, c->ssq_d};
+    {  // entry: y = pre[s] + E_s[previous token]; for s >= 1 the previous
+       // head's partials are reduced here and code s-1 is stored
+      EntryArgs a;
+      memset(&a, 0, sizeof(a));
+      a.pre = c->pre; a.ldpre = S * Dd; a.s = s; a.table = c->dep_emb[s];
+      a.prev = s == 0 ? c->tokens : c->codes + (s - 1); a.prev_stride = s == 0 ? 1 : S;
+      a.prev_part = s == 0 ? nullptr : c->apart; a.prev_tiles = (c->Va + 15) / 16;
+      a.prev_n = c->Va; a.D = Dd; a.B = B; a.y = c->y; a.ssq_out = c->ssq_d;
       e = run(c, KC_D_ENTRY, nlive * Dd * es, [&] { return launch_entry(dt, a, c->stream); });
       if (e != hipSuccess) return e;
     }
@@ -337,11 +356,12 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
         GemmArgs a = gemm_base(c);
         a.W = c->dep_qkv[wi]; a.N = 3 * Dd; a.K = Dd;
         a.X = c->y; a.ldx = Dd; a.ssq = c->ssq_d; a.n_ssq = nt_dd; a.gain = c->dep_attn_norm[l];
+        a.xn_out = B > 1 ? c->hnd : nullptr;
         a.q_out = c->qd; a.dq = Dd; a.hd = c->hdd; a.inv_freq = nullptr; a.pos = nullptr;
         a.scalar_widx = s; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v; a.slot_stride = slot_stride;
         a.layer_off = layer_off; a.head_stride = (int64_t)S * c->hdd; a.cap = S;
         e = run(c, KC_D_QKV, 3.0 * Dd * Dd * es + Dd * es + nlive * 2.0 * Dd * es,
-                [&] { return launch_gemm(dt, KW_DEP, PRO_NORM, EPI_QKV, a, c->stream); });
+                [&] { return gemm(c, PRO_NORM, EPI_QKV, a); });
         if (e != hipSuccess) return e;
       }
       {
@@ -350,8 +370,8 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
         a.q = c->qd; a.ldq = Dd; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v;
         a.slot_stride = slot_stride; a.layer_off = layer_off; a.head_stride = (int64_t)S * c->hdd;
         a.cap = S; a.pos = nullptr; a.scalar_nvalid = s + 1; a.live = c->d_live;
-        a.n_heads = c->Hd; a.max_chunks = (S + ATTN_CHUNK - 1) / ATTN_CHUNK; a.part = c->attn_part;
-        a.ticket = c->attn_ticket; a.o_out = c->od; a.ldo = Dd;
+        a.n_heads = c->Hd; a.max_chunks = 1; a.part = c->attn_part;  // S <= 64: one chunk
+        a.o_out = c->od; a.ldo = Dd;
         e = run(c, KC_D_ATTN, nlive * (s + 1) * 2.0 * Dd * es,
                 [&] { return launch_attn(dt, c->hdd, a, B, c->stream); });
         if (e != hipSuccess) return e;
@@ -361,16 +381,17 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
         a.W = c->dep_o[wi]; a.N = Dd; a.K = Dd; a.X = c->od; a.ldx = Dd;
         a.resid = c->y; a.ldr = Dd; a.ssq_out = c->ssq_d;
         e = run(c, KC_D_O, (double)Dd * Dd * es,
-                [&] { return launch_gemm(dt, KW_DEP, PRO_DIRECT, EPI_RESID, a, c->stream); });
+                [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
         if (e != hipSuccess) return e;
       }
       {
         GemmArgs a = gemm_base(c);
         a.W = c->dep_gate_up[wi]; a.N = Fd; a.K = Dd;
         a.X = c->y; a.ldx = Dd; a.ssq = c->ssq_d; a.n_ssq = nt_dd; a.gain = c->dep_mlp_norm[l];
+        a.xn_out = B > 1 ? c->hnd : nullptr;
         a.act = c->actd; a.lda = Fd;
         e = run(c, KC_D_GATEUP, 2.0 * Fd * Dd * es + Dd * es,
-                [&] { return launch_gemm(dt, KW_DEP, PRO_NORM, EPI_SWIGLU, a, c->stream); });
+                [&] { return gemm(c, PRO_NORM, EPI_SWIGLU, a); });
         if (e != hipSuccess) return e;
       }
       {
@@ -378,21 +399,26 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
         a.W = c->dep_down[wi]; a.N = Dd; a.K = Fd; a.X = c->actd; a.ldx = Fd;
         a.resid = c->y; a.ldr = Dd; a.ssq_out = c->ssq_d;
         e = run(c, KC_D_DOWN, (double)Dd * Fd * es,
-                [&] { return launch_gemm(dt, KW_DEP, PRO_DIRECT, EPI_RESID, a, c->stream); });
+                [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
         if (e != hipSuccess) return e;
       }
     }
     {  // head s on the rounded residual -> code s
       GemmArgs a = gemm_base(c);
       a.W = c->dep_head[s]; a.N = c->Va; a.K = Dd; a.X = c->y; a.ldx = Dd;
-      a.out = c->audio_logits + (size_t)s * c->Va; a.ldo = S * c->Va;
-      a.apart = c->apart; a.ticket = c->tickets + 1 + s; a.tok_out = c->codes + s; a.tok_stride = S;
+      a.xn_out = B > 1 ? c->hnd : nullptr;
+      a.logits = c->audio_logits + (size_t)s * c->Va; a.ldo = S * c->Va;
+      a.apart = c->apart;
       e = run(c, KC_D_HEAD, (double)c->Va * Dd * es,
-              [&] { return launch_gemm(dt, KW_DEP, PRO_CAST, EPI_ARGMAX, a, c->stream); });
+              [&] { return gemm(c, PRO_CAST, EPI_ARGMAX, a); });
       if (e != hipSuccess) return e;
     }
   }
-  return hipSuccess;
+  // the last substep's code (earlier ones are stored by the next entry)
+  return run(c, KC_ARGMAX, 0.0, [&] {
+    return launch_argmax_reduce(c->apart, (c->Va + 15) / 16, c->Va, B, c->codes + (S - 1), S,
+                                c->stream);
+  });
 }
 
 hipError_t capture(moshi_ctx* c, hipError_t (*fn)(moshi_ctx*), hipGraphExec_t* out) {
@@ -566,14 +592,6 @@ int upload_weights(moshi_ctx* c, const void* const* t) {
   c->dep_head.resize(S);
   for (int s = 0; s < S; ++s)
     if ((rc = put(t[i++], (size_t)Va * Dd, &c->dep_head[s]))) return rc;
-  // device copy of the channel table pointers (text, then the S audio tables)
-  std::vector<const void*> tabs;
-  tabs.push_back(c->emb_text);
-  for (int s = 0; s < S; ++s) tabs.push_back(c->emb_audio[s]);
-  void* p;
-  CKD(c, dalloc(c, &p, sizeof(void*) * tabs.size()));
-  CKD(c, hipMemcpy(p, tabs.data(), sizeof(void*) * tabs.size(), hipMemcpyHostToDevice));
-  c->d_tables = (const void**)p;
   return MOSHI_OK;
 }
 
@@ -593,26 +611,26 @@ int alloc_buffers(moshi_ctx* c) {
       {&c->ring_v, B * c->L * c->H * c->W * c->hd * es},
       {&c->dkv_k, B * c->Ld * c->Hd * S * c->hdd * es},
       {&c->dkv_v, B * c->Ld * c->Hd * S * c->hdd * es},
-      {(void**)&c->x, B * D * 4},
-      {(void**)&c->ssq, ((D + 15) / 16) * B * 4},
-      {(void**)&c->q, B * D * 4},
+      {(void**)&c->x, B * D * 8},
+      {(void**)&c->ssq, ((D + 15) / 16) * B * 8},
+      {(void**)&c->q, B * D * 8},
       {&c->o, B * D * es},
       {&c->act, B * F * es},
       {&c->hid, B * D * es},
-      {(void**)&c->pre, B * S * Dd * 4},
-      {(void**)&c->y, B * Dd * 4},
-      {(void**)&c->ssq_d, ((Dd + 15) / 16) * B * 4},
-      {(void**)&c->qd, B * Dd * 4},
+      {&c->hn, B * D * es},
+      {(void**)&c->pre, B * S * Dd * 8},
+      {(void**)&c->y, B * Dd * 8},
+      {(void**)&c->ssq_d, ((Dd + 15) / 16) * B * 8},
+      {(void**)&c->qd, B * Dd * 8},
       {&c->od, B * Dd * es},
       {&c->actd, B * Fd * es},
+      {&c->hnd, B * Dd * es},
       {(void**)&c->text_logits, B * c->Vt * 4},
       {(void**)&c->audio_logits, B * S * c->Va * 4},
       {(void**)&c->tokens, B * 4},
       {(void**)&c->codes, B * S * 4},
       {(void**)&c->apart, ntile_max * B * sizeof(ArgPart)},
-      {(void**)&c->tickets, (1 + S) * 4},
-      {(void**)&c->attn_part, B * hmax * c->max_chunks * (hdmax + 2) * 4},
-      {(void**)&c->attn_ticket, B * hmax * 4},
+      {(void**)&c->attn_part, B * hmax * c->max_chunks * (hdmax + 2) * 8},
       {(void**)&c->d_frames, B * c->NCH * 4},
       {(void**)&c->d_live, B * 4},
       {(void**)&c->d_pos, B * 8},
@@ -625,9 +643,9 @@ int alloc_buffers(moshi_ctx* c) {
     if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation) return fail(c, MOSHI_E_OOM, "buffers: out of device memory");
     if (e != hipSuccess) return device_fail(c, e, "hipMalloc(buffers)");
   }
-  // Zero everything small (tickets must start at zero; activations of free
-  // slots then hold finite values). The rings need no clearing: only positions
-  // a session has written are ever attended.
+  // Zero everything but the rings (activations of free slots then hold finite
+  // values). The rings need no clearing: only positions a session has written
+  // are ever attended.
   for (size_t i = 4; i < sizeof(reqs) / sizeof(reqs[0]); ++i)
     CKD(c, hipMemsetAsync(*reqs[i].p, 0, reqs[i].bytes, c->stream));
   std::vector<double> inv(c->hd / 2);
@@ -856,6 +874,27 @@ int moshi_session_prefill_kv(moshi_ctx* c, int32_t slot, int32_t n, const void* 
   CKD(c, hipStreamSynchronize(c->stream));
   c->pos[slot] = n;
   c->meta_dirty = true;
+  return MOSHI_OK;
+}
+
+int moshi_session_read_kv(moshi_ctx* c, int32_t slot, void* k, void* v) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (slot < 0 || slot >= c->B || !c->live[slot]) return fail(c, MOSHI_E_NOSESSION, "slot not live");
+  if (!k || !v) return fail(c, MOSHI_E_INVALID, "NULL output");
+  const size_t layer_elems = (size_t)c->W * c->D;
+  const int64_t slot_stride = (int64_t)c->L * c->H * c->W * c->hd;
+  for (int l = 0; l < c->L; ++l) {
+    for (int kv = 0; kv < 2; ++kv) {
+      char* dst = (char*)(kv == 0 ? k : v) + (size_t)l * layer_elems * c->esz;
+      const char* ring = (const char*)(kv == 0 ? c->ring_k : c->ring_v) +
+                         ((size_t)slot * slot_stride + (size_t)l * c->H * c->W * c->hd) * c->esz;
+      CKD(c, launch_gather_ring(c->dtype, ring, c->staging, c->W, c->H, c->hd,
+                                (int64_t)c->W * c->hd, c->stream));
+      CKD(c, hipMemcpyAsync(dst, c->staging, layer_elems * c->esz, hipMemcpyDeviceToHost, c->stream));
+      CKD(c, hipStreamSynchronize(c->stream));
+    }
+  }
   return MOSHI_OK;
 }
 

@@ -1,5 +1,10 @@
 // kernels.h -- argument blocks and launchers of the gfx950 kernels of the
 // Moshi frame step (internal to libmoshi.so).
+//
+// Storage is the model dtype (bf16 or fp32) for weights, embeddings, the K/V
+// rings and every vector that feeds a projection; all arithmetic is fp64
+// (residual stream, norms, projections, RoPE, attention, SiLU, logits), so the
+// rounding of each stored bf16 value is decided from an fp64 result.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -9,25 +14,26 @@ namespace moshi {
 
 enum Dtype { DT_F32 = 0, DT_BF16 = 1 };
 
-// How a projection kernel builds its input vector (the MFMA B operand).
+// How a projection kernel builds its input vector.
 enum Prologue {
-  PRO_DIRECT = 0,  // X already in the model dtype [B][ldx]
-  PRO_NORM = 1,    // X = round(x * rms_scale * gain): x fp32 [B][ldx] + per-tile sums of squares
-  PRO_CAST = 2,    // X = round(x): x fp32 [B][ldx], no scaling
+  PRO_DIRECT = 0,  // X already stored in the model dtype [B][ldx]
+  PRO_NORM = 1,    // X = round(x * rms_scale * gain): x fp64 [B][ldx] + per-tile sums of squares
+  PRO_CAST = 2,    // X = round(x): x fp64 [B][ldx], no scaling
 };
 
 // What a projection kernel does with its 16-row output tile.
 enum Epilogue {
-  EPI_STORE = 0,   // out[b][row] = y (fp32)
+  EPI_STORE = 0,   // out64[b][row] = y
   EPI_RESID = 1,   // resid[b][row] += y; per-tile sums of squares of the new residual
   EPI_QKV = 2,     // q rows -> RoPE -> q buffer; k,v rows -> (RoPE on k) -> ring cache
   EPI_SWIGLU = 3,  // tile rows interleave gate/up units: act[b][u] = round(silu(g) * u)
-  EPI_ARGMAX = 4,  // logits out + per-tile (max, index); the last workgroup picks the token
+  EPI_ARGMAX = 4,  // logits (fp32 copy) + per-tile (max, index) partials of the fp64 values
 };
 
 struct ArgPart {
-  float v;
+  double v;
   int i;
+  int pad;
 };
 
 struct GemmArgs {
@@ -36,25 +42,28 @@ struct GemmArgs {
   int K;
   int B;          // columns = slot capacity
   // prologue
-  const void* X;  // PRO_DIRECT: model dtype; PRO_NORM / PRO_CAST: fp32
+  const void* X;  // PRO_DIRECT: model dtype; PRO_NORM / PRO_CAST: fp64
   int ldx;
-  const float* ssq;  // PRO_NORM: [n_ssq][B] partial sums of squares of x
+  const double* ssq;  // PRO_NORM: [n_ssq][B] partial sums of squares of x
   int n_ssq;
   const void* gain;  // PRO_NORM: [K] model dtype
-  float eps;
+  double eps;
   void* xn_out;      // PRO_NORM / PRO_CAST: if set, workgroup 0 stores the rounded input [B][K]
-  // EPI_STORE / EPI_ARGMAX
-  float* out;
+  // EPI_STORE
+  double* out64;
   int ldo;
+  // EPI_ARGMAX
+  float* logits;     // [B][ldo]
+  ArgPart* apart;    // [n_tiles][B]
   // EPI_RESID
-  float* resid;
+  double* resid;
   int ldr;
-  float* ssq_out;  // [n_tiles][B]
+  double* ssq_out;   // [n_tiles][B]
   // EPI_SWIGLU
   void* act;
   int lda;
   // EPI_QKV
-  float* q_out;
+  double* q_out;
   int dq;                  // rows per part (q | k | v), = n_heads * head_dim
   int hd;                  // head dim
   const double* inv_freq;  // RoPE inverse frequencies [hd/2]; null = no RoPE
@@ -65,15 +74,10 @@ struct GemmArgs {
   void* ring_v;
   int64_t slot_stride, layer_off, head_stride;  // ring strides, elements
   int cap;                                      // ring capacity
-  // EPI_ARGMAX
-  ArgPart* apart;      // [n_tiles][B]
-  unsigned* ticket;    // zero on entry, reset to zero by the last workgroup
-  int* tok_out;
-  int tok_stride;
 };
 
 struct AttnArgs {
-  const float* q;   // [B][ldq], head h at h*HD
+  const double* q;  // [B][ldq], head h at h*HD
   int ldq;
   const void* ring_k;
   const void* ring_v;
@@ -85,49 +89,65 @@ struct AttnArgs {
   int mask_oldest;
   int n_heads;
   int max_chunks;
-  float* part;        // [B][H][max_chunks][HD + 2]
-  unsigned* ticket;   // [B][H]
-  void* o_out;        // [B][ldo] model dtype
+  double* part;  // [B][H][max_chunks][HD + 2]: (max, sum, p.V) of each key chunk
+  void* o_out;   // [B][ldo] model dtype
   int ldo;
 };
 
+constexpr int MAX_CHANNELS = 65;
+
 struct EmbedArgs {
-  const void* const* tables;  // device array of n_ch table pointers, each [rows][D]
-  const int* frames;          // [B][n_ch]
-  const int* live;            // [B]
+  const void* tables[MAX_CHANNELS];  // n_ch table pointers, each [rows][D]
+  const int* frames;                 // [B][n_ch]
+  const int* live;                   // [B]
   int n_ch;
   int D;
   int B;
   int rows_text, rows_audio;  // table rows (codes are clamped into range)
   int* bad_code;              // set to 1 when a live code was out of range
-  float* x;        // [B][D]
-  float* ssq_out;  // [ceil(D/16)][B]
+  double* x;                  // [B][D]
+  double* ssq_out;            // [ceil(D/16)][B]
 };
 
 struct EntryArgs {
-  const float* pre;  // [B][ldpre]; substep s block at s*D
+  const double* pre;  // [B][ldpre]; substep s block at s*D
   int ldpre;
   int s;
   const void* table;  // [rows][D]
-  const int* prev;    // token of column b at prev[b*prev_stride]
+  // previous token: either read (prev[b*prev_stride]) or, when prev_part is
+  // set, reduced from the previous head's per-tile argmax partials and stored
+  // to prev[b*prev_stride] by the workgroups of the first row tile
+  int* prev;
   int prev_stride;
+  const ArgPart* prev_part;  // [prev_tiles][B] or null
+  int prev_tiles;
+  int prev_n;  // rows of the previous head (index bound)
   int D;
   int B;
-  float* y;        // [B][D]
-  float* ssq_out;  // [ceil(D/16)][B]
+  double* y;        // [B][D]
+  double* ssq_out;  // [ceil(D/16)][B]
 };
 
 // Keys per attention workgroup.
 constexpr int ATTN_CHUNK = 64;
 
-int gemm_nb(int B);            // 16-column tiles for capacity B (1, 2 or 4)
 int gemm_tiles(int epi, int N);  // grid size of a projection
-// kw = waves per workgroup (K split), 4 or 8.
+// Waves per workgroup for a projection with K inputs and B sessions.
+int gemm_kw(int dtype, int B, int K);
+// kw from gemm_kw. With B > 1 and PRO_NORM / PRO_CAST, xn_out must be a
+// [B][K] buffer: the rounded input vectors are written there first.
 hipError_t launch_gemm(int dtype, int kw, int pro, int epi, const GemmArgs& a, hipStream_t st);
 hipError_t launch_attn(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st);
+// Merges the per-chunk partials of every (slot, head) with more than one chunk.
+hipError_t launch_attn_combine(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st);
+// tok[b*stride] = argmax over the per-tile partials of column b (lowest index on ties).
+hipError_t launch_argmax_reduce(const ArgPart* part, int n_tiles, int n_rows, int B, int* tok,
+                                int stride, hipStream_t st);
 hipError_t launch_embed(int dtype, const EmbedArgs& a, hipStream_t st);
 hipError_t launch_entry(int dtype, const EntryArgs& a, hipStream_t st);
 hipError_t launch_advance(int64_t* pos, const int* live, int B, hipStream_t st);
+hipError_t launch_gather_ring(int dtype, const void* ring, void* dst, int n, int n_heads, int hd,
+                              int64_t head_stride, hipStream_t st);
 hipError_t launch_scatter_prefill(int dtype, const void* src, void* ring, int n, int n_heads,
                                   int hd, int64_t head_stride, hipStream_t st);
 

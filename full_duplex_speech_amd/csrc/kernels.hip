@@ -1,28 +1,35 @@
 // kernels.hip -- gfx950 kernels of the Moshi/PersonaPlex frame step.
 //
-// Everything on the step's path runs here:
-//  * gemm_kernel: every projection (q|k|v, o, gate|up, down, text head,
-//    depformer input projections and heads). Weights stream from HBM once per
-//    step in 16-byte loads; each 64-lane wave owns 16 weight rows and a slice
-//    of K; the batch of session columns is the N side of a bf16 (or fp32)
-//    MFMA 16x16 tile, so the same kernel serves one session (15 idle columns,
-//    HBM-bound) and 64 sessions (weights read once for all).
-//    Prologues fuse the RMSNorm (from per-tile sums of squares written by the
-//    producer of the residual) and the bf16 rounding of the input vector;
-//    epilogues fuse RoPE + ring-cache write, the residual add, SiLU(gate)*up,
-//    and the greedy argmax (per-tile maxima, the last workgroup reduces).
-//  * attn_kernel: sliding-window decode attention over the per-slot ring of
-//    K/V; one workgroup per (64-key chunk, head, slot); partial softmax
-//    statistics are combined in a fixed chunk order by the last workgroup of
-//    each (slot, head).
-//  * embed_kernel / entry_kernel: the summed 17-channel embedding and the
-//    depformer substep entry (projection of the hidden state + embedding of
-//    the previous token), both writing sums of squares for the next norm.
-//
 // Model (pages): mobius PR #368 "P2 - Moshi LM" (RMSNorm eps 1e-8, RoPE theta
 // 1e4, sliding-window causal attention, fused gate/up SwiGLU, depformer with
 // per-substep linears, no RoPE, causal over substeps); vLLM-Omni recipe
 // "PersonaPlex", "Architecture" (3000-frame ring window, 17-row token column).
+//
+// Numerics: weights, embeddings, K/V and every vector that feeds a projection
+// are stored in the model dtype (bf16 or fp32); all arithmetic is fp64, and a
+// stored bf16 value is the nearest-even rounding of the fp64 result. This is
+// what keeps every rounding decision equal to an fp64 evaluation of the
+// model: with fp32 accumulation a single flipped bf16 rounding spreads through
+// the next dense projection into many more flips, and after 32 layers the
+// logits drift by several 1e-2.
+//
+// Kernels:
+//  * gemv_kernel (one session): every projection. Weights stream from HBM
+//    once in 16-byte loads; a workgroup owns 16 output rows, its waves split K,
+//    each lane keeps its slice of the input vector in registers and
+//    accumulates in fp64; lanes and waves reduce in a fixed order. The
+//    prologue fuses the RMSNorm (from per-tile sums of squares written by the
+//    producer of the residual) and the bf16 rounding of the input.
+//  * gemm_kernel (two or more sessions): the same projections as fp64 MFMA
+//    16x16x4 tiles (16 weight rows x 16 session columns), input vectors
+//    pre-normalised by norm_kernel.
+//  * epilogues shared by both: RoPE + ring write, residual add + sums of
+//    squares, SiLU(gate)*up, argmax partials.
+//  * attn_kernel / attn_combine_kernel: sliding-window decode attention over
+//    the per-slot ring, one workgroup per (64-key chunk, head, slot), chunks
+//    merged in a fixed order.
+//  * embed_kernel / entry_kernel: summed channel embedding and depformer
+//    substep entry.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -31,33 +38,19 @@
 
 namespace moshi {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte group
 
 template <typename T>
 struct VecOf;
 template <>
 struct VecOf<__bf16> {
-  static constexpr int N = 8;  // elements per 16-byte load
+  static constexpr int N = 8;  // elements per 16-byte group
 };
 template <>
 struct VecOf<float> {
   static constexpr int N = 4;
 };
-
-__device__ __forceinline__ float to_f(__bf16 v) { return (float)v; }
-__device__ __forceinline__ float to_f(float v) { return v; }
-template <typename T>
-__device__ __forceinline__ T from_f(float v);
-template <>
-__device__ __forceinline__ __bf16 from_f<__bf16>(float v) {
-  return (__bf16)v;  // round to nearest even
-}
-template <>
-__device__ __forceinline__ float from_f<float>(float v) {
-  return v;
-}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const u32x4*)p; }
 // Weights are read once per step: stream them past the caches.
@@ -65,61 +58,78 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load((const u32x4*)p);
 }
 
-// ---------------------------------------------------------------------------
-// Input-vector construction (MFMA B operand, one 16-byte group per lane)
-// ---------------------------------------------------------------------------
+// ---- conversions -----------------------------------------------------------
 
-// 8 (bf16) or 4 (fp32) consecutive input elements k0.. of column col, in the
-// model dtype, packed as 16 bytes.
-template <typename T, int PRO>
-__device__ __forceinline__ u32x4 load_x(const GemmArgs& a, int col, int k0, float rs) {
-  constexpr int VEC = VecOf<T>::N;
-  if constexpr (PRO == PRO_DIRECT) {
-    return ld16((const T*)a.X + (size_t)col * a.ldx + k0);
-  } else {
-    const float* xp = (const float*)a.X + (size_t)col * a.ldx + k0;
-    float xv[VEC];
+template <typename T>
+__device__ __forceinline__ void widen(u32x4 w, double* out);
+template <>
+__device__ __forceinline__ void widen<__bf16>(u32x4 w, double* out) {
 #pragma unroll
-    for (int e = 0; e < VEC; e += 4) {
-      const f32x4 f = *(const f32x4*)(xp + e);
-      xv[e] = f[0];
-      xv[e + 1] = f[1];
-      xv[e + 2] = f[2];
-      xv[e + 3] = f[3];
-    }
-    if constexpr (PRO == PRO_NORM) {
-      u32x4 gw = ld16((const T*)a.gain + k0);
-      const T* gv = (const T*)&gw;
-#pragma unroll
-      for (int e = 0; e < VEC; ++e) xv[e] = xv[e] * rs * to_f(gv[e]);
-    }
-    u32x4 r;
-    T* rv = (T*)&r;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) rv[e] = from_f<T>(xv[e]);
-    return r;
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = (double)__uint_as_float(w[i] << 16);
+    out[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
   }
+}
+template <>
+__device__ __forceinline__ void widen<float>(u32x4 w, double* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = (double)__uint_as_float(w[i]);
+}
+
+__device__ __forceinline__ double to_d(__bf16 v) { return (double)(float)v; }
+__device__ __forceinline__ double to_d(float v) { return (double)v; }
+
+// bf16 bits of the value nearest to d (ties to even). Rounding d to fp32 first
+// is exact enough except when that lands exactly on a bf16 midpoint while d
+// itself is not on it; then d decides the direction.
+__device__ __forceinline__ unsigned short bf16_bits_rne(double d) {
+  const float f = (float)d;
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u)
+    return (unsigned short)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  if ((u & 0xffffu) == 0x8000u && (double)f != d) {
+    const bool up = fabs(d) > fabs((double)f);
+    return (unsigned short)((u >> 16) + (up ? 1u : 0u));
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
 }
 
 template <typename T>
-__device__ __forceinline__ f32x4 mma(u32x4 w, u32x4 x, f32x4 acc);
+__device__ __forceinline__ T round_to(double d);
 template <>
-__device__ __forceinline__ f32x4 mma<__bf16>(u32x4 w, u32x4 x, f32x4 acc) {
-  // A = 16 weight rows x 32 k (lane: row lane%16, k 8*(lane/16)..+7);
-  // B = 32 k x 16 columns (lane: column lane%16, same k).
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w),
-                                                  __builtin_bit_cast(bf16x8, x), acc, 0, 0, 0);
+__device__ __forceinline__ __bf16 round_to<__bf16>(double d) {
+  return __builtin_bit_cast(__bf16, bf16_bits_rne(d));
 }
 template <>
-__device__ __forceinline__ f32x4 mma<float>(u32x4 w, u32x4 x, f32x4 acc) {
-  // Four 16x16x4 steps; step c pairs element c of every lane (k-slot lane/16).
-  const f32x4 wf = __builtin_bit_cast(f32x4, w);
-  const f32x4 xf = __builtin_bit_cast(f32x4, x);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[0], xf[0], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[1], xf[1], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[2], xf[2], acc, 0, 0, 0);
-  acc = __builtin_amdgcn_mfma_f32_16x16x4f32(wf[3], xf[3], acc, 0, 0, 0);
-  return acc;
+__device__ __forceinline__ float round_to<float>(double d) {
+  return (float)d;
+}
+
+// The rounded input vector: VEC values k0.. of column col as doubles (the
+// values the stored dtype holds), and the same values packed for storing.
+template <typename T, int PRO>
+__device__ __forceinline__ void load_x(const GemmArgs& a, int col, int k0, double rs, double* xv,
+                                       u32x4* packed) {
+  constexpr int VEC = VecOf<T>::N;
+  if constexpr (PRO == PRO_DIRECT) {
+    const u32x4 w = ld16((const T*)a.X + (size_t)col * a.ldx + k0);
+    widen<T>(w, xv);
+    *packed = w;
+  } else {
+    const double* xp = (const double*)a.X + (size_t)col * a.ldx + k0;
+    double gv[VEC];
+    if constexpr (PRO == PRO_NORM) widen<T>(ld16((const T*)a.gain + k0), gv);
+    u32x4 r;
+    T* rv = (T*)&r;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const double v = (PRO == PRO_NORM) ? xp[e] * rs * gv[e] : xp[e];
+      rv[e] = round_to<T>(v);
+      xv[e] = to_d(rv[e]);
+    }
+    *packed = r;
+  }
 }
 
 // Weight row read by tile row t of tile `tile`. EPI_SWIGLU interleaves units:
@@ -127,244 +137,378 @@ __device__ __forceinline__ f32x4 mma<float>(u32x4 w, u32x4 x, f32x4 acc) {
 template <int EPI>
 __device__ __forceinline__ int tile_row(int tile, int t, int N, bool& ok) {
   if constexpr (EPI == EPI_SWIGLU) {
-    int u = tile * 8 + (t >> 1);
+    const int u = tile * 8 + (t >> 1);
     ok = u < N;
     return (t & 1) ? N + u : u;
   } else {
-    int r = tile * 16 + t;
+    const int r = tile * 16 + t;
     ok = r < N;
     return r;
   }
 }
 
-__device__ __forceinline__ bool arg_better(float v, int i, float bv, int bi) {
+__device__ __forceinline__ bool arg_better(double v, int i, double bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
+__device__ __forceinline__ double shfl_xor_d(double v, int m) {
+  return __hiloint2double(__shfl_xor(__double2hiint(v), m), __shfl_xor(__double2loint(v), m));
+}
+
+// RMSNorm scale 1/sqrt(mean(x^2) + eps) of column col from the producer's
+// per-tile sums of squares; every thread of the workgroup gets the same value.
+// Threads [0, nthr) split the tiles; fixed-order reduction through `red`.
+__device__ __forceinline__ double rms_scale(const GemmArgs& a, int col, double* red, int nthr) {
+  const int t = threadIdx.x;
+  double s = 0.0;
+  for (int i = t; i < a.n_ssq; i += nthr) s += a.ssq[(size_t)i * a.B + col];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += shfl_xor_d(s, off);
+  if ((t & 63) == 0) red[t >> 6] = s;
+  __syncthreads();
+  double tot = 0.0;
+  for (int w = 0; w < nthr / 64; ++w) tot += red[w];
+  return 1.0 / sqrt(tot / (double)a.K + a.eps);
+}
+
+// ---- epilogue: tile rows 4g..4g+3 of column col, values v -----------------
+
+template <typename T, int EPI>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int g, int col,
+                                         const double* v) {
+  const bool cok = col < a.B;
+  if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile * 16 + 4 * g + i;
+      if (cok && row < a.N) a.out64[(size_t)col * a.ldo + row] = v[i];
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile * 16 + 4 * g + i;
+      if (cok && row < a.N) {
+        double* p = a.resid + (size_t)col * a.ldr + row;
+        const double xn = *p + v[i];
+        *p = xn;
+        ss += xn * xn;
+      }
+    }
+    // the 4 lanes of this column (g = 0..3) combine in a fixed order
+    ss += shfl_xor_d(ss, 16);
+    ss += shfl_xor_d(ss, 32);
+    if (g == 0 && cok) a.ssq_out[(size_t)tile * a.B + col] = ss;
+  } else if constexpr (EPI == EPI_QKV) {
+    const int row0 = tile * 16 + 4 * g;  // 16-row tiles never straddle a part or a head
+    const int part = row0 / a.dq;
+    const int din = row0 - part * a.dq;
+    const int head = din / a.hd;
+    const int d0 = din - head * a.hd;
+    double vals[4] = {v[0], v[1], v[2], v[3]};
+    if (!cok || row0 >= a.N) return;
+    if (a.inv_freq != nullptr && part < 2) {
+      const double p = (double)a.pos[col];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const double ang = p * a.inv_freq[(d0 >> 1) + j];
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const double x0 = vals[2 * j], x1 = vals[2 * j + 1];
+        vals[2 * j] = x0 * cs - x1 * sn;
+        vals[2 * j + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    if (part == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a.q_out[(size_t)col * a.dq + din + i] = vals[i];
+    } else if (a.live[col]) {
+      const int widx = a.pos ? (int)(a.pos[col] % a.cap) : a.scalar_widx;
+      T* dst = (T*)(part == 1 ? a.ring_k : a.ring_v) + (size_t)col * a.slot_stride + a.layer_off +
+               (size_t)head * a.head_stride + (size_t)widx * a.hd + d0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = round_to<T>(vals[i]);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = tile * 8 + 2 * g + j;
+      if (cok && u < a.N) {
+        const double gt = v[2 * j], up = v[2 * j + 1];
+        ((T*)a.act)[(size_t)col * a.lda + u] = round_to<T>(gt / (1.0 + exp(-gt)) * up);
+      }
+    }
+  } else if constexpr (EPI == EPI_ARGMAX) {
+    // NaN never wins: it compares as -inf; rows past N carry index INT_MAX.
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile * 16 + 4 * g + i;
+      if (row < a.N) {
+        if (cok) a.logits[(size_t)col * a.ldo + row] = (float)v[i];
+        const double val = (v[i] != v[i]) ? -INFINITY : v[i];
+        if (bi == 0x7fffffff || val > bv) {
+          bv = val;
+          bi = row;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const double ov = shfl_xor_d(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (arg_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (g == 0 && cok) a.apart[(size_t)tile * a.B + col] = ArgPart{bv, bi, 0};
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Projection kernel
+// One session: fp64 VALU GEMV
 // ---------------------------------------------------------------------------
 
-template <typename T, int NB, int KSPLIT, int PRO, int EPI>
-__global__ __launch_bounds__(64 * KSPLIT) void gemm_kernel(GemmArgs a) {
+// Workgroup = KW waves and 16 output rows. Wave w takes K steps [s0, s1) of
+// 64*VEC elements; lane l covers elements step*64*VEC + l*VEC .. +VEC of every
+// row, so its slice of the input vector is the same for all 16 rows.
+template <typename T, int KW, int PRO, int EPI>
+__global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
   constexpr int VEC = VecOf<T>::N;
-  constexpr int KSTEP = 4 * VEC;  // k covered by one 16-byte load per lane
-  constexpr int U = 4;            // loads in flight per lane per operand
-  constexpr int NCOL = 16 * NB;
+  constexpr int KSTEP = 64 * VEC;
+  constexpr int SMAX = 2;  // K steps per batch of weight loads (16 rows each)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tile = blockIdx.x;
+  __shared__ double s_red[KW][16];
+  __shared__ double s_tmp[KW];
+
+  const T* wrow[16];
+  bool rok[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+    const int r = tile_row<EPI>(tile, t, a.N, rok[t]);
+    wrow[t] = (const T*)a.W + (size_t)(rok[t] ? r : 0) * a.K;
+  }
+  const int nsteps = (a.K + KSTEP - 1) / KSTEP;
+  const int s0 = (wave * nsteps) / KW;
+  const int s1 = ((wave + 1) * nsteps) / KW;
+
+  u32x4 wv[SMAX][16];
+  auto load_w = [&](int st) {
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u) {
+      const int k0 = (st + u) * KSTEP + lane * VEC;
+      const bool kok = (st + u < s1) && (k0 < a.K);
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        wv[u][t] = (kok && rok[t]) ? ld16_stream(wrow[t] + k0) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  load_w(s0);  // first batch in flight across the norm prologue
+
+  double rs = 1.0;
+  if constexpr (PRO == PRO_NORM) rs = rms_scale(a, 0, s_tmp, 64 * KW);
+  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && tile == 0;
+
+  double acc[16];
+#pragma unroll
+  for (int t = 0; t < 16; ++t) acc[t] = 0.0;
+  for (int st = s0; st < s1; st += SMAX) {
+    if (st != s0) load_w(st);
+#pragma unroll
+    for (int u = 0; u < SMAX; ++u) {
+      const int k0 = (st + u) * KSTEP + lane * VEC;
+      if (st + u < s1 && k0 < a.K) {
+        double xv[VEC];
+        u32x4 packed;
+        load_x<T, PRO>(a, 0, k0, rs, xv, &packed);
+        if (write_xn) *(u32x4*)((T*)a.xn_out + k0) = packed;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          double wd[VEC];
+          widen<T>(wv[u][t], wd);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[t] = fma(wd[e], xv[e], acc[t]);
+        }
+      }
+    }
+  }
+  // per-row sums over the 64 lanes (butterfly), then over the waves in order
+#pragma unroll
+  for (int t = 0; t < 16; ++t) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc[t] += shfl_xor_d(acc[t], off);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) s_red[wave][t] = acc[t];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  // epilogue lanes: g = lane / 16 holds rows 4g..4g+3 of column lane % 16 (= 0)
+  const int g = lane >> 4;
+  if ((lane & 15) != 0) return;
+  double v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    double s = s_red[0][4 * g + i];
+    for (int w = 1; w < KW; ++w) s += s_red[w][4 * g + i];
+    v[i] = s;
+  }
+  epilogue<T, EPI>(a, tile, g, 0, v);
+}
+
+// ---------------------------------------------------------------------------
+// Two or more sessions: fp64 MFMA 16x16x4 tiles
+// ---------------------------------------------------------------------------
+
+// A = 16 weight rows x 4 k (lane: row lane%16, k-slot lane/16), B = 4 k x 16
+// session columns (lane: column lane%16, same k-slot). A lane loads 16 bytes of
+// its row (VEC consecutive k) and of its column's input; element e of every
+// lane feeds MFMA e, so both operands map k-slot g to k0 + VEC*g + e.
+// The fp64 16x16 result puts row (lane/16) + 4i in element i of a lane, so A
+// row m carries tile row 4*(m%4) + m/4: element i of lane group g is then tile
+// row 4g + i, the layout the epilogues use.
+template <typename T, int NB, int KW, int EPI>
+__global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int KSTEP = 4 * VEC;
+  constexpr int U = 4;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int tile = blockIdx.x;
-
-  __shared__ float s_r[NCOL];
-  __shared__ f32x4 s_acc[KSPLIT][NB][64];
-  __shared__ int s_last;
-
-  // RMSNorm scale of every column from the producer's per-tile sums of squares.
-  if constexpr (PRO == PRO_NORM) {
-    constexpr int TPC = 64 * KSPLIT / NCOL;  // threads per column (power of two <= 64)
-    const int col = threadIdx.x / TPC;
-    const int part = threadIdx.x % TPC;
-    float s = 0.f;
-    if (col < a.B)
-      for (int t = part; t < a.n_ssq; t += TPC) s += a.ssq[(size_t)t * a.B + col];
-#pragma unroll
-    for (int off = TPC / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
-    if (part == 0) s_r[col] = (col < a.B) ? 1.0f / sqrtf(s / (float)a.K + a.eps) : 0.f;
-    __syncthreads();
-  }
+  __shared__ f64x4 s_acc[KW][NB][64];
 
   bool rok;
-  const int wrow = tile_row<EPI>(tile, r16, a.N, rok);
+  const int wrow = tile_row<EPI>(tile, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
   const T* wbase = (const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + g * VEC;
   const int nsteps = (a.K + KSTEP - 1) / KSTEP;
-  const int s0 = (wave * nsteps) / KSPLIT;
-  const int s1 = ((wave + 1) * nsteps) / KSPLIT;
-  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && tile == 0;
+  const int s0 = (wave * nsteps) / KW;
+  const int s1 = ((wave + 1) * nsteps) / KW;
 
-  float rs[NB];
+  f64x4 acc[NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) rs[nb] = (PRO == PRO_NORM) ? s_r[nb * 16 + r16] : 1.f;
-
-  f32x4 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f64x4{0.0, 0.0, 0.0, 0.0};
   for (int st = s0; st < s1; st += U) {
     u32x4 wv[U];
-    u32x4 xv[U][NB];
+    u32x4 xw[U][NB];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k0 = (st + u) * KSTEP + g * VEC;
       const bool kok = (st + u < s1) && (k0 < a.K);
       wv[u] = (kok && rok) ? ld16_stream(wbase + (size_t)(st + u) * KSTEP) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k0 = (st + u) * KSTEP + g * VEC;
-      const bool kok = (st + u < s1) && (k0 < a.K);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = nb * 16 + r16;
-        xv[u][nb] = (kok && col < a.B) ? load_x<T, PRO>(a, col, k0, rs[nb]) : u32x4{0u, 0u, 0u, 0u};
-        if (write_xn && kok && col < a.B)
-          *(u32x4*)((T*)a.xn_out + (size_t)col * a.K + k0) = xv[u][nb];
+        xw[u][nb] = (kok && col < a.B) ? ld16((const T*)a.X + (size_t)col * a.ldx + k0)
+                                       : u32x4{0u, 0u, 0u, 0u};
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
+      double wd[VEC];
+      widen<T>(wv[u], wd);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) acc[nb] = mma<T>(wv[u], xv[u][nb], acc[nb]);
+      for (int nb = 0; nb < NB; ++nb) {
+        double xd[VEC];
+        widen<T>(xw[u][nb], xd);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(wd[e], xd[e], acc[nb], 0, 0, 0);
+      }
+    }
   }
-
-  // Split-K reduction over the waves, fixed order.
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) s_acc[wave][nb][lane] = acc[nb];
   __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    f64x4 s = s_acc[0][nb][lane];
+    for (int w = 1; w < KW; ++w) s += s_acc[w][nb][lane];
+    const double v[4] = {s[0], s[1], s[2], s[3]};
+    epilogue<T, EPI>(a, tile, g, nb * 16 + r16, v);
+  }
+}
 
-  if (wave == 0) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      f32x4 v = s_acc[0][nb][lane];
-#pragma unroll
-      for (int w = 1; w < KSPLIT; ++w) v += s_acc[w][nb][lane];
-      const int col = nb * 16 + r16;
-      const bool cok = col < a.B;
-      // lane holds tile rows 4g..4g+3 of column col
-      if constexpr (EPI == EPI_STORE) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = tile * 16 + 4 * g + i;
-          if (cok && row < a.N) a.out[(size_t)col * a.ldo + row] = v[i];
-        }
-      } else if constexpr (EPI == EPI_RESID) {
-        float ss = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = tile * 16 + 4 * g + i;
-          if (cok && row < a.N) {
-            float* p = a.resid + (size_t)col * a.ldr + row;
-            const float xn = *p + v[i];
-            *p = xn;
-            ss += xn * xn;
-          }
-        }
-        ss += __shfl_xor(ss, 16);
-        ss += __shfl_xor(ss, 32);
-        if (g == 0 && cok) a.ssq_out[(size_t)tile * a.B + col] = ss;
-      } else if constexpr (EPI == EPI_QKV) {
-        const int row0 = tile * 16 + 4 * g;  // 16-row tiles never straddle a part or a head
-        const int part = row0 / a.dq;
-        const int din = row0 - part * a.dq;
-        const int head = din / a.hd;
-        const int d0 = din - head * a.hd;
-        float vals[4] = {v[0], v[1], v[2], v[3]};
-        if (cok && row0 < a.N) {
-          if (a.inv_freq != nullptr && part < 2) {
-            const double p = (double)a.pos[col];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-              const double ang = p * a.inv_freq[(d0 >> 1) + j];
-              double sn, cs;
-              sincos(ang, &sn, &cs);
-              const float c = (float)cs, s = (float)sn;
-              const float x0 = vals[2 * j], x1 = vals[2 * j + 1];
-              vals[2 * j] = x0 * c - x1 * s;
-              vals[2 * j + 1] = x0 * s + x1 * c;
-            }
-          }
-          if (part == 0) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) a.q_out[(size_t)col * a.dq + din + i] = vals[i];
-          } else if (a.live[col]) {
-            const int widx = a.pos ? (int)(a.pos[col] % a.cap) : a.scalar_widx;
-            T* dst = (T*)(part == 1 ? a.ring_k : a.ring_v) + (size_t)col * a.slot_stride +
-                     a.layer_off + (size_t)head * a.head_stride + (size_t)widx * a.hd + d0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[i] = from_f<T>(vals[i]);
-          }
-        }
-      } else if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int u = tile * 8 + 2 * g + j;
-          if (cok && u < a.N) {
-            const float gt = v[2 * j], up = v[2 * j + 1];
-            const float act = gt / (1.0f + expf(-gt)) * up;
-            ((T*)a.act)[(size_t)col * a.lda + u] = from_f<T>(act);
-          }
-        }
-      } else if constexpr (EPI == EPI_ARGMAX) {
-        // NaN never wins: it compares as -inf; rows past N carry index INT_MAX.
-        float bv = -INFINITY;
-        int bi = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = tile * 16 + 4 * g + i;
-          if (row < a.N) {
-            if (cok) a.out[(size_t)col * a.ldo + row] = v[i];
-            const float val = (v[i] != v[i]) ? -INFINITY : v[i];
-            if (bi == 0x7fffffff || val > bv) {
-              bv = val;
-              bi = row;
-            }
-          }
-        }
-#pragma unroll
-        for (int off = 16; off <= 32; off <<= 1) {
-          const float ov = __shfl_xor(bv, off);
-          const int oi = __shfl_xor(bi, off);
-          if (arg_better(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-          }
-        }
-        if (g == 0 && cok) a.apart[(size_t)tile * a.B + col] = ArgPart{bv, bi};
-      }
+// Input vectors for the MFMA path: xn[b][k] = round(x[b][k] * scale_b * g[k])
+// (PRO_NORM) or round(x[b][k]) (PRO_CAST); one workgroup per column.
+template <typename T, int PRO>
+__global__ __launch_bounds__(256) void norm_kernel(GemmArgs a) {
+  const int b = blockIdx.x;
+  __shared__ double s_tmp[4];
+  double rs = 1.0;
+  if constexpr (PRO == PRO_NORM) rs = rms_scale(a, b, s_tmp, 256);
+  const double* x = (const double*)a.X + (size_t)b * a.ldx;
+  T* out = (T*)a.xn_out + (size_t)b * a.K;
+  for (int k = threadIdx.x; k < a.K; k += 256) {
+    const double v = (PRO == PRO_NORM) ? x[k] * rs * to_d(((const T*)a.gain)[k]) : x[k];
+    out[k] = round_to<T>(v);
+  }
+}
+
+// Greedy token of column blockIdx.x from per-tile (max, index) partials.
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const ArgPart* part, int n_tiles,
+                                                            int n_rows, int B, int* tok,
+                                                            int stride) {
+  const int b = blockIdx.x;
+  const int t = threadIdx.x;
+  __shared__ double s_v[4];
+  __shared__ int s_i[4];
+  double bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = t; i < n_tiles; i += 256) {
+    const ArgPart p = part[(size_t)i * B + b];
+    if (arg_better(p.v, p.i, bv, bi)) {
+      bv = p.v;
+      bi = p.i;
     }
   }
-
-  if constexpr (EPI == EPI_ARGMAX) {
-    // The last workgroup to finish reduces the per-tile maxima of every column.
-    __threadfence();
-    __syncthreads();
-    if (threadIdx.x == 0) s_last = (atomicAdd(a.ticket, 1u) == gridDim.x - 1) ? 1 : 0;
-    __syncthreads();
-    if (s_last) {
-      __threadfence();
-      constexpr int TPC = 64 * KSPLIT / NCOL;
-      const int col = threadIdx.x / TPC;
-      const int part = threadIdx.x % TPC;
-      float bv = -INFINITY;
-      int bi = 0x7fffffff;
-      if (col < a.B) {
-        for (int t = part; t < (int)gridDim.x; t += TPC) {
-          const ArgPart p = a.apart[(size_t)t * a.B + col];
-          if (arg_better(p.v, p.i, bv, bi)) {
-            bv = p.v;
-            bi = p.i;
-          }
-        }
-      }
 #pragma unroll
-      for (int off = TPC / 2; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int oi = __shfl_xor(bi, off);
-        if (arg_better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
-      }
-      if (part == 0 && col < a.B) a.tok_out[(size_t)col * a.tok_stride] = (bi < a.N) ? bi : 0;
-      if (threadIdx.x == 0) atomicExch(a.ticket, 0u);
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ov = shfl_xor_d(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (arg_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
     }
+  }
+  if ((t & 63) == 0) {
+    s_v[t >> 6] = bv;
+    s_i[t >> 6] = bi;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int w = 1; w < 4; ++w)
+      if (arg_better(s_v[w], s_i[w], bv, bi)) {
+        bv = s_v[w];
+        bi = s_i[w];
+      }
+    tok[(size_t)b * stride] = (bi < n_rows) ? bi : 0;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Sliding-window decode attention over a ring of K/V
 // ---------------------------------------------------------------------------
+
+// Keys of slot b visible at its current position: ring slots [0, nvalid),
+// minus `excl` (the oldest key, under the mask-oldest reading).
+__device__ __forceinline__ void window_of(const AttnArgs& a, int b, int& nvalid, int& excl) {
+  excl = -1;
+  if (a.pos != nullptr) {
+    const int64_t p = a.pos[b];
+    nvalid = (int)(p + 1 < (int64_t)a.cap ? p + 1 : (int64_t)a.cap);
+    if (a.mask_oldest && p >= (int64_t)a.cap - 1) excl = (int)((p + 1) % a.cap);
+  } else {
+    nvalid = a.scalar_nvalid;
+  }
+}
 
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
@@ -380,60 +524,60 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   const int b = blockIdx.z;
   const int t = threadIdx.x;
   if (!a.live[b]) return;
-  int nvalid, excl = -1;
-  if (a.pos != nullptr) {
-    const int64_t p = a.pos[b];
-    nvalid = (int)(p + 1 < (int64_t)a.cap ? p + 1 : (int64_t)a.cap);
-    if (a.mask_oldest && p >= (int64_t)a.cap - 1) excl = (int)((p + 1) % a.cap);
-  } else {
-    nvalid = a.scalar_nvalid;
-  }
+  int nvalid, excl;
+  window_of(a, b, nvalid, excl);
   const int nchunks = (nvalid + C - 1) / C;
   if (chunk >= nchunks) return;
 
-  __shared__ float s_p[C];
-  __shared__ float s_o[KP][HD + 1];
-  __shared__ float s_ml[2];
-  __shared__ int s_last;
+  __shared__ double s_p[C];
+  __shared__ double s_o[KP][HD + 1];
+  __shared__ double s_ml[2];
 
   const int kd = t % TK;
   const int kk = t / TK;
-  const float scale = 1.0f / sqrtf((float)HD);
-  float qv[VEC];
-  const float* qp = a.q + (size_t)b * a.ldq + h * HD + kd * VEC;
-#pragma unroll
-  for (int e = 0; e < VEC; ++e) qv[e] = qp[e] * scale;
-
   const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
   const T* kbase = (const T*)a.ring_k + base;
   const T* vbase = (const T*)a.ring_v + base;
 
-  // scores
+  // every K and V group of this chunk is requested up front
+  u32x4 kw[PASSES], vw[PASSES];
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int j = chunk * C + ps * KP + kk;
+    const bool ok = j < nvalid;
+    kw[ps] = ok ? ld16(kbase + (size_t)j * HD + kd * VEC) : u32x4{0u, 0u, 0u, 0u};
+    vw[ps] = ok ? ld16(vbase + (size_t)j * HD + kd * VEC) : u32x4{0u, 0u, 0u, 0u};
+  }
+  const double scale = 1.0 / sqrt((double)HD);
+  double qv[VEC];
+  const double* qp = a.q + (size_t)b * a.ldq + h * HD + kd * VEC;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) qv[e] = qp[e];
+
+  // scores s_j = q.k_j / sqrt(HD)
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
     const int j = chunk * C + ps * KP + kk;
     const bool ok = j < nvalid && j != excl;
-    float d = 0.f;
-    if (ok) {
-      u32x4 kw = ld16(kbase + (size_t)j * HD + kd * VEC);
-      const T* kvp = (const T*)&kw;
+    double kd_[VEC];
+    widen<T>(kw[ps], kd_);
+    double d = 0.0;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) d += qv[e] * to_f(kvp[e]);
-    }
+    for (int e = 0; e < VEC; ++e) d = fma(qv[e], kd_[e], d);
 #pragma unroll
-    for (int off = TK / 2; off > 0; off >>= 1) d += __shfl_xor(d, off);
-    if (kd == 0) s_p[ps * KP + kk] = ok ? d : -INFINITY;
+    for (int off = TK / 2; off > 0; off >>= 1) d += shfl_xor_d(d, off);
+    if (kd == 0) s_p[ps * KP + kk] = ok ? d * scale : -INFINITY;
   }
   __syncthreads();
   if (t < 64) {
-    float sv = (t < C) ? s_p[t] : -INFINITY;
-    float m = sv;
+    const double sv = (t < C) ? s_p[t] : -INFINITY;
+    double m = sv;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    float pj = (m == -INFINITY || sv == -INFINITY) ? 0.f : expf(sv - m);
-    float l = pj;
+    for (int off = 32; off > 0; off >>= 1) m = fmax(m, shfl_xor_d(m, off));
+    const double pj = (m == -INFINITY || sv == -INFINITY) ? 0.0 : exp(sv - m);
+    double l = pj;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
+    for (int off = 32; off > 0; off >>= 1) l += shfl_xor_d(l, off);
     if (t < C) s_p[t] = pj;
     if (t == 0) {
       s_ml[0] = m;
@@ -443,66 +587,71 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   __syncthreads();
 
   // p . V
-  float acc[VEC];
+  double acc[VEC];
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
 #pragma unroll
   for (int ps = 0; ps < PASSES; ++ps) {
-    const int j = chunk * C + ps * KP + kk;
-    const float pj = s_p[ps * KP + kk];
-    if (j < nvalid && pj != 0.f) {
-      u32x4 vw = ld16(vbase + (size_t)j * HD + kd * VEC);
-      const T* vvp = (const T*)&vw;
+    const double pj = s_p[ps * KP + kk];
+    double vd[VEC];
+    widen<T>(vw[ps], vd);
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) acc[e] += pj * to_f(vvp[e]);
-    }
+    for (int e = 0; e < VEC; ++e) acc[e] = fma(pj, vd[e], acc[e]);
   }
 #pragma unroll
   for (int e = 0; e < VEC; ++e) s_o[kk][kd * VEC + e] = acc[e];
   __syncthreads();
-  float od = 0.f;
-  if (t < HD) {
-    for (int r = 0; r < KP; ++r) od += s_o[r][t];
-  }
+  if (t >= HD) return;
+  double od = 0.0;
+  for (int r = 0; r < KP; ++r) od += s_o[r][t];
 
-  T* optr = (T*)a.o_out + (size_t)b * a.ldo + h * HD;
   if (nchunks == 1) {
-    if (t < HD) {
-      const float l = s_ml[1];
-      optr[t] = from_f<T>(l > 0.f ? od / l : 0.f);
-    }
+    const double l = s_ml[1];
+    ((T*)a.o_out)[(size_t)b * a.ldo + h * HD + t] = round_to<T>(l > 0.0 ? od / l : 0.0);
     return;
   }
-  float* mypart = a.part + (((size_t)b * a.n_heads + h) * a.max_chunks + chunk) * (HD + 2);
-  if (t < HD) mypart[2 + t] = od;
+  double* mypart = a.part + (((size_t)b * a.n_heads + h) * a.max_chunks + chunk) * (HD + 2);
+  mypart[2 + t] = od;
   if (t == 0) {
     mypart[0] = s_ml[0];
     mypart[1] = s_ml[1];
   }
-  __threadfence();
+}
+
+// Merge the chunk partials of (slot blockIdx.y, head blockIdx.x) in chunk
+// order: o = sum_c e^{m_c - M} (p.V)_c / sum_c e^{m_c - M} l_c.
+template <typename T, int HD>
+__global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int t = threadIdx.x;
+  if (!a.live[b]) return;
+  int nvalid, excl;
+  window_of(a, b, nvalid, excl);
+  const int nchunks = (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  if (nchunks <= 1) return;  // written directly by attn_kernel
+  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
+  __shared__ double s_m[HD / 64 > 0 ? HD / 64 : 1];
+  // M = max over the chunk maxima (exact, so any reduction order gives the same M)
+  double mloc = -INFINITY;
+  for (int c = t; c < nchunks; c += HD) mloc = fmax(mloc, parts[(size_t)c * (HD + 2)]);
+#pragma unroll
+  for (int off = (HD < 64 ? HD : 64) / 2; off > 0; off >>= 1)
+    mloc = fmax(mloc, shfl_xor_d(mloc, off));
+  if ((t & 63) == 0) s_m[t >> 6] = mloc;
   __syncthreads();
-  unsigned* tk = a.ticket + (size_t)b * a.n_heads + h;
-  if (t == 0) s_last = (atomicAdd(tk, 1u) == (unsigned)(nchunks - 1)) ? 1 : 0;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  // combine the chunks in order 0..nchunks-1
-  const float* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < nchunks; ++c) M = fmaxf(M, parts[(size_t)c * (HD + 2)]);
-  if (t < HD) {
-    float L = 0.f, O = 0.f;
-    for (int c = 0; c < nchunks; ++c) {
-      const float* pc = parts + (size_t)c * (HD + 2);
-      const float mc = pc[0];
-      if (mc == -INFINITY) continue;
-      const float w = expf(mc - M);
-      L += pc[1] * w;
-      O += pc[2 + t] * w;
-    }
-    optr[t] = from_f<T>(L > 0.f ? O / L : 0.f);
+  double M = s_m[0];
+  for (int w = 1; w < HD / 64; ++w) M = fmax(M, s_m[w]);
+  double L = 0.0, O = 0.0;
+#pragma unroll 8
+  for (int c = 0; c < nchunks; ++c) {
+    const double* pc = parts + (size_t)c * (HD + 2);
+    const double mc = pc[0];
+    const double w = (mc == -INFINITY) ? 0.0 : exp(mc - M);
+    L += pc[1] * w;
+    O += pc[2 + t] * w;
   }
-  if (t == 0) atomicExch(tk, 0u);
+  ((T*)a.o_out)[(size_t)b * a.ldo + h * HD + t] = round_to<T>(L > 0.0 ? O / L : 0.0);
 }
 
 // ---------------------------------------------------------------------------
@@ -514,43 +663,82 @@ __global__ __launch_bounds__(64) void embed_kernel(EmbedArgs a) {
   const int r = threadIdx.x & 15;
   const int b = blockIdx.y * 4 + (threadIdx.x >> 4);
   const int row = blockIdx.x * 16 + r;
-  float acc = 0.f;
+  double acc = 0.0;
   if (b < a.B && row < a.D) {
     const bool live = a.live[b] != 0;
-    for (int c = 0; c < a.n_ch; ++c) {
-      // Free slots embed code 0. A live code outside the table is clamped to
-      // a valid row (never read out of bounds) and flagged for the host.
-      int code = live ? a.frames[(size_t)b * a.n_ch + c] : 0;
-      const int rows = (c == 0) ? a.rows_text : a.rows_audio;
-      if (code < 0 || code >= rows) {
-        if (row == 0) atomicOr(a.bad_code, 1);
-        code = code < 0 ? 0 : rows - 1;
+    // rows requested 8 channels at a time; the sum runs in channel order
+    for (int c0 = 0; c0 < a.n_ch; c0 += 8) {
+      double v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = c0 + j;
+        v[j] = 0.0;
+        if (c < a.n_ch) {
+          // Free slots embed code 0. A live code outside the table is clamped
+          // to a valid row (never read out of bounds) and flagged for the host.
+          int code = live ? a.frames[(size_t)b * a.n_ch + c] : 0;
+          const int rows = (c == 0) ? a.rows_text : a.rows_audio;
+          if (code < 0 || code >= rows) {
+            if (row == 0) atomicOr(a.bad_code, 1);
+            code = code < 0 ? 0 : rows - 1;
+          }
+          v[j] = to_d(((const T*)a.tables[c])[(size_t)code * a.D + row]);
+        }
       }
-      acc += to_f(((const T*)a.tables[c])[(size_t)code * a.D + row]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (c0 + j < a.n_ch) acc += v[j];
     }
     a.x[(size_t)b * a.D + row] = acc;
   }
-  float ss = acc * acc;
+  double ss = acc * acc;
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  for (int off = 8; off > 0; off >>= 1) ss += shfl_xor_d(ss, off);
   if (r == 0 && b < a.B) a.ssq_out[(size_t)blockIdx.x * a.B + b] = ss;
 }
 
+// Depformer substep entry: y = (W_in[s] hidden) + E_s[previous token].
 template <typename T>
 __global__ __launch_bounds__(64) void entry_kernel(EntryArgs a) {
   const int r = threadIdx.x & 15;
   const int b = blockIdx.y * 4 + (threadIdx.x >> 4);
   const int row = blockIdx.x * 16 + r;
-  float acc = 0.f;
+  int tok = 0;
+  if (a.prev_part != nullptr) {
+    // reduce the previous head's partials of column b over the 16 lanes of this column
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (b < a.B)
+      for (int i = r; i < a.prev_tiles; i += 16) {
+        const ArgPart p = a.prev_part[(size_t)i * a.B + b];
+        if (arg_better(p.v, p.i, bv, bi)) {
+          bv = p.v;
+          bi = p.i;
+        }
+      }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      const double ov = shfl_xor_d(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (arg_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    tok = (bi < a.prev_n) ? bi : 0;
+    if (blockIdx.x == 0 && r == 0 && b < a.B) a.prev[(size_t)b * a.prev_stride] = tok;
+  } else if (b < a.B) {
+    tok = a.prev[(size_t)b * a.prev_stride];
+  }
+  double acc = 0.0;
   if (b < a.B && row < a.D) {
-    const int tok = a.prev[(size_t)b * a.prev_stride];
     acc = a.pre[(size_t)b * a.ldpre + (size_t)a.s * a.D + row] +
-          to_f(((const T*)a.table)[(size_t)tok * a.D + row]);
+          to_d(((const T*)a.table)[(size_t)tok * a.D + row]);
     a.y[(size_t)b * a.D + row] = acc;
   }
-  float ss = acc * acc;
+  double ss = acc * acc;
 #pragma unroll
-  for (int off = 8; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  for (int off = 8; off > 0; off >>= 1) ss += shfl_xor_d(ss, off);
   if (r == 0 && b < a.B) a.ssq_out[(size_t)blockIdx.x * a.B + b] = ss;
 }
 
@@ -574,47 +762,105 @@ __global__ __launch_bounds__(256) void scatter_kernel(const T* src, T* ring, int
   ring[h * head_stride + j * hd + d] = src[e];
 }
 
+// Ring read-back: ring [H][cap][hd] of one slot and layer -> dst [n][H*hd].
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(const T* ring, T* dst, int n, int H, int hd,
+                                                     int64_t head_stride) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t D = (int64_t)H * hd;
+  if (e >= (int64_t)n * D) return;
+  const int64_t j = e / D;
+  const int64_t c = e - j * D;
+  const int64_t h = c / hd;
+  const int64_t d = c - h * hd;
+  dst[e] = ring[h * head_stride + j * hd + d];
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
-int gemm_nb(int B) { return B <= 16 ? 1 : (B <= 32 ? 2 : 4); }
-
 int gemm_tiles(int epi, int N) { return epi == EPI_SWIGLU ? (N + 7) / 8 : (N + 15) / 16; }
 
-template <typename T, int NB, int KW>
-static hipError_t launch_gemm_kw(int pro, int epi, const GemmArgs& a, hipStream_t st) {
-  dim3 grid(gemm_tiles(epi, a.N)), block(64 * KW);
-#define MOSHI_GEMM_CASE(P, E)                                                    \
-  if (pro == P && epi == E) {                                                   \
-    hipLaunchKernelGGL((gemm_kernel<T, NB, KW, P, E>), grid, block, 0, st, a); \
-    return hipGetLastError();                                                   \
+int gemm_kw(int dtype, int B, int K) {
+  if (B == 1) {
+    const int kstep = 64 * (dtype == DT_BF16 ? 8 : 4);
+    const int nsteps = (K + kstep - 1) / kstep;
+    return nsteps >= 8 ? 8 : (nsteps >= 4 ? 4 : 2);
   }
-  MOSHI_GEMM_CASE(PRO_NORM, EPI_QKV)
-  MOSHI_GEMM_CASE(PRO_DIRECT, EPI_RESID)
-  MOSHI_GEMM_CASE(PRO_NORM, EPI_SWIGLU)
-  MOSHI_GEMM_CASE(PRO_NORM, EPI_ARGMAX)
-  MOSHI_GEMM_CASE(PRO_DIRECT, EPI_STORE)
-  MOSHI_GEMM_CASE(PRO_CAST, EPI_ARGMAX)
-#undef MOSHI_GEMM_CASE
+  return K >= 4096 ? 8 : 4;
+}
+
+template <typename T, int KW>
+static hipError_t launch_gemv_kw(int pro, int epi, const GemmArgs& a, hipStream_t st) {
+  dim3 grid(gemm_tiles(epi, a.N)), block(64 * KW);
+#define MOSHI_GEMV_CASE(P, E)                                                \
+  if (pro == P && epi == E) {                                               \
+    hipLaunchKernelGGL((gemv_kernel<T, KW, P, E>), grid, block, 0, st, a); \
+    return hipGetLastError();                                               \
+  }
+  MOSHI_GEMV_CASE(PRO_NORM, EPI_QKV)
+  MOSHI_GEMV_CASE(PRO_DIRECT, EPI_RESID)
+  MOSHI_GEMV_CASE(PRO_NORM, EPI_SWIGLU)
+  MOSHI_GEMV_CASE(PRO_NORM, EPI_ARGMAX)
+  MOSHI_GEMV_CASE(PRO_DIRECT, EPI_STORE)
+  MOSHI_GEMV_CASE(PRO_CAST, EPI_ARGMAX)
+#undef MOSHI_GEMV_CASE
   return hipErrorInvalidValue;
 }
 
-template <typename T, int NB>
-static hipError_t launch_gemm_nb(int kw, int pro, int epi, const GemmArgs& a, hipStream_t st) {
-  if (kw == 8) return launch_gemm_kw<T, NB, 8>(pro, epi, a, st);
-  if (kw == 4) return launch_gemm_kw<T, NB, 4>(pro, epi, a, st);
-  return hipErrorInvalidValue;
+template <typename T, int NB, int KW>
+static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
+  dim3 grid(gemm_tiles(epi, a.N)), block(64 * KW);
+  switch (epi) {
+    case EPI_STORE:
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE>), grid, block, 0, st, a);
+      break;
+    case EPI_RESID:
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_RESID>), grid, block, 0, st, a);
+      break;
+    case EPI_QKV:
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_QKV>), grid, block, 0, st, a);
+      break;
+    case EPI_SWIGLU:
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_SWIGLU>), grid, block, 0, st, a);
+      break;
+    case EPI_ARGMAX:
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_ARGMAX>), grid, block, 0, st, a);
+      break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_gemm_t(int kw, int pro, int epi, const GemmArgs& a, hipStream_t st) {
-  switch (gemm_nb(a.B)) {
-    case 1: return launch_gemm_nb<T, 1>(kw, pro, epi, a, st);
-    case 2: return launch_gemm_nb<T, 2>(kw, pro, epi, a, st);
-    case 4: return launch_gemm_nb<T, 4>(kw, pro, epi, a, st);
+  if (a.B == 1) {
+    if (kw == 8) return launch_gemv_kw<T, 8>(pro, epi, a, st);
+    if (kw == 4) return launch_gemv_kw<T, 4>(pro, epi, a, st);
+    if (kw == 2) return launch_gemv_kw<T, 2>(pro, epi, a, st);
+    return hipErrorInvalidValue;
   }
-  return hipErrorInvalidValue;
+  // more than one session: input vectors rounded first, then MFMA tiles
+  GemmArgs b = a;
+  if (pro != PRO_DIRECT) {
+    if (a.xn_out == nullptr) return hipErrorInvalidValue;  // the caller provides the buffer
+    if (pro == PRO_NORM)
+      hipLaunchKernelGGL((norm_kernel<T, PRO_NORM>), dim3(a.B), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((norm_kernel<T, PRO_CAST>), dim3(a.B), dim3(256), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    b.X = a.xn_out;
+    b.ldx = a.K;
+  }
+  const int nb = a.B <= 16 ? 1 : (a.B <= 32 ? 2 : 4);
+  const int kwm = kw >= 8 ? 8 : 4;
+  if (nb == 1)
+    return kwm == 8 ? launch_gemm_kw<T, 1, 8>(epi, b, st) : launch_gemm_kw<T, 1, 4>(epi, b, st);
+  if (nb == 2)
+    return kwm == 8 ? launch_gemm_kw<T, 2, 8>(epi, b, st) : launch_gemm_kw<T, 2, 4>(epi, b, st);
+  return launch_gemm_kw<T, 4, 4>(epi, b, st);
 }
 
 hipError_t launch_gemm(int dtype, int kw, int pro, int epi, const GemmArgs& a, hipStream_t st) {
@@ -639,6 +885,30 @@ hipError_t launch_attn(int dtype, int hd, const AttnArgs& a, int B, hipStream_t 
   return dtype == DT_BF16 ? launch_attn_t<__bf16>(hd, a, B, st) : launch_attn_t<float>(hd, a, B, st);
 }
 
+template <typename T>
+static hipError_t launch_combine_t(int hd, const AttnArgs& a, int B, hipStream_t st) {
+  dim3 grid(a.n_heads, B);
+  switch (hd) {
+    case 32: hipLaunchKernelGGL((attn_combine_kernel<T, 32>), grid, dim3(32), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((attn_combine_kernel<T, 64>), grid, dim3(64), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((attn_combine_kernel<T, 128>), grid, dim3(128), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_combine(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st) {
+  return dtype == DT_BF16 ? launch_combine_t<__bf16>(hd, a, B, st)
+                          : launch_combine_t<float>(hd, a, B, st);
+}
+
+hipError_t launch_argmax_reduce(const ArgPart* part, int n_tiles, int n_rows, int B, int* tok,
+                                int stride, hipStream_t st) {
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(B), dim3(256), 0, st, part, n_tiles, n_rows, B,
+                     tok, stride);
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(int dtype, const EmbedArgs& a, hipStream_t st) {
   dim3 grid((a.D + 15) / 16, (a.B + 3) / 4), block(64);
   if (dtype == DT_BF16)
@@ -648,17 +918,17 @@ hipError_t launch_embed(int dtype, const EmbedArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_advance(int64_t* pos, const int* live, int B, hipStream_t st) {
-  hipLaunchKernelGGL(advance_kernel, dim3((B + 63) / 64), dim3(64), 0, st, pos, live, B);
-  return hipGetLastError();
-}
-
 hipError_t launch_entry(int dtype, const EntryArgs& a, hipStream_t st) {
   dim3 grid((a.D + 15) / 16, (a.B + 3) / 4), block(64);
   if (dtype == DT_BF16)
     hipLaunchKernelGGL(entry_kernel<__bf16>, grid, block, 0, st, a);
   else
     hipLaunchKernelGGL(entry_kernel<float>, grid, block, 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_advance(int64_t* pos, const int* live, int B, hipStream_t st) {
+  hipLaunchKernelGGL(advance_kernel, dim3((B + 63) / 64), dim3(64), 0, st, pos, live, B);
   return hipGetLastError();
 }
 
@@ -672,6 +942,20 @@ hipError_t launch_scatter_prefill(int dtype, const void* src, void* ring, int n,
                        (__bf16*)ring, n, n_heads, hd, head_stride);
   else
     hipLaunchKernelGGL(scatter_kernel<float>, grid, block, 0, st, (const float*)src, (float*)ring,
+                       n, n_heads, hd, head_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_ring(int dtype, const void* ring, void* dst, int n, int n_heads, int hd,
+                              int64_t head_stride, hipStream_t st) {
+  const int64_t total = (int64_t)n * n_heads * hd;
+  if (total == 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(gather_kernel<__bf16>, grid, block, 0, st, (const __bf16*)ring,
+                       (__bf16*)dst, n, n_heads, hd, head_stride);
+  else
+    hipLaunchKernelGGL(gather_kernel<float>, grid, block, 0, st, (const float*)ring, (float*)dst,
                        n, n_heads, hd, head_stride);
   return hipGetLastError();
 }

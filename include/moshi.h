@@ -67,7 +67,7 @@ typedef struct {
   int32_t dim, n_layers, n_heads, ffn_hidden, window;
   int32_t dep_dim, dep_layers, dep_heads, dep_ffn_hidden, n_substeps;
   int32_t text_vocab, audio_card;
-  float rope_theta, norm_eps;
+  double rope_theta, norm_eps;
   int32_t dtype, max_sessions;
   uint32_t flags;
 } moshi_config;
@@ -153,6 +153,11 @@ int moshi_depformer_step(moshi_ctx* ctx, const void* hidden, const int32_t* text
  * (post-RoPE), head h at columns h*head_dim.. of each row. */
 int moshi_session_prefill_kv(moshi_ctx* ctx, int32_t slot, int32_t n, const void* k,
                              const void* v);
+
+/* Copies a live slot's whole ring out: k, v [L][W][D] in the config's dtype,
+ * ring slot j (row j) holding the position congruent to j mod W; rows the
+ * session has not written yet are unspecified. */
+int moshi_session_read_kv(moshi_ctx* ctx, int32_t slot, void* k, void* v);
 
 /* Bookkeeping of a live slot's next step: absolute position (frames consumed),
  * fill = min(pos, W), ring write index = pos mod W. */

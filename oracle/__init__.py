@@ -100,6 +100,10 @@ def _bind(L):
     L.orc_session_reset.restype = None
     L.orc_session_prefill.argtypes = [vp, i32, vp, vp]
     L.orc_session_prefill.restype = ctypes.c_int
+    L.orc_session_load_ring.argtypes = [vp, i64, vp, vp]
+    L.orc_session_load_ring.restype = ctypes.c_int
+    L.orc_session_read_ring.argtypes = [vp, vp, vp]
+    L.orc_session_read_ring.restype = None
     L.orc_session_info.argtypes = [vp, vp, vp, vp]
     L.orc_session_info.restype = None
     L.orc_temporal.argtypes = [vp, vp, vp, vp, vp, vp]
@@ -222,6 +226,23 @@ class Session:
         v = np.ascontiguousarray(v)
         if self._L.orc_session_prefill(self.h, n, _p(k), _p(v)):
             raise ValueError("prefill length outside [0, window]")
+
+    def load_ring(self, pos, k, v):
+        """Replace the ring (k, v [L][W][D], model storage type, row j = ring
+        slot j) and set the position (state transfer for tests)."""
+        k = np.ascontiguousarray(k)
+        v = np.ascontiguousarray(v)
+        if self._L.orc_session_load_ring(self.h, int(pos), _p(k), _p(v)):
+            raise ValueError("negative position")
+
+    def read_ring(self):
+        """The ring (k, v [L][W][D], model storage type, row j = ring slot j)."""
+        s = self.model.shape
+        dt = np.uint16 if s.dtype == "bf16" else np.float32
+        k = np.empty((s.n_layers, s.window, s.dim), dt)
+        v = np.empty_like(k)
+        self._L.orc_session_read_ring(self.h, _p(k), _p(v))
+        return k, v
 
     def info(self):
         pos = np.zeros(1, np.int64)

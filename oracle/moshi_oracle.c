@@ -351,6 +351,52 @@ int orc_session_prefill(orc_session* s, int32_t n, const void* k, const void* v)
   return 0;
 }
 
+/* Test-only state transfer (no model arithmetic): replaces the whole ring,
+ * k, v [L][W][D] in the model storage type with row j = ring slot j, and sets
+ * the position. Lets a test check one step at any position starting from
+ * another implementation's cache. Returns -1 on a negative position. */
+int orc_session_load_ring(orc_session* s, int64_t pos, const void* k, const void* v) {
+  const orc_model* m = s->m;
+  if (pos < 0) return -1;
+  int D = m->c.dim, W = m->c.window;
+  double* kv = (double*)malloc(sizeof(double) * D);
+  double* vv = (double*)malloc(sizeof(double) * D);
+  for (int l = 0; l < m->c.n_layers; ++l)
+    for (int j = 0; j < W; ++j) {
+      size_t base = ((size_t)l * W + j) * D;
+      for (int i = 0; i < D; ++i) {
+        kv[i] = wget(m, k, base + i);
+        vv[i] = wget(m, v, base + i);
+      }
+      ring_put(s, s->k_ring, l, j, kv);
+      ring_put(s, s->v_ring, l, j, vv);
+    }
+  free(kv);
+  free(vv);
+  s->pos = pos;
+  return 0;
+}
+
+/* Test-only: copies the ring out (k, v [L][W][D], model storage type, row j =
+ * ring slot j). */
+void orc_session_read_ring(const orc_session* s, void* k, void* v) {
+  const orc_model* m = s->m;
+  int D = m->c.dim, W = m->c.window;
+  for (int l = 0; l < m->c.n_layers; ++l)
+    for (int j = 0; j < W; ++j)
+      for (int i = 0; i < D; ++i) {
+        size_t at = ((size_t)l * W + j) * D + i;
+        double kv = ring_get(s, s->k_ring, l, j, i), vv = ring_get(s, s->v_ring, l, j, i);
+        if (m->c.bf16) {
+          ((uint16_t*)k)[at] = double_to_bf16_bits(kv);
+          ((uint16_t*)v)[at] = double_to_bf16_bits(vv);
+        } else {
+          ((float*)k)[at] = (float)kv;
+          ((float*)v)[at] = (float)vv;
+        }
+      }
+}
+
 /* Ring bookkeeping of the next step: its write index and how many keys it
  * will attend (window reading in the header). */
 void orc_session_info(const orc_session* s, int64_t* pos, int32_t* fill, int32_t* write_idx) {

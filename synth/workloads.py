@@ -8,7 +8,9 @@ Seeds: the tiny model's weights use seed 1001, the PersonaPlex-shape model's
 weights seed 1002 (shared by the four full-size workloads), the ragged test
 model seed 1003. Workload w (1..5) draws frames from seed 2000+10w+1, prefill
 K/V from 2000+10w+2, churn from 2000+10w+3, depformer-only inputs from
-2000+10w+4.
+2000+10w+4. The multi-session full-size workloads (4, 5) build every session's
+prefill from one shared bank of W positions, rotated per session
+(prefill_from_bank), so that 64 sessions do not need 100 GB of fresh draws.
 """
 from dataclasses import dataclass, field
 
@@ -79,6 +81,22 @@ def prefill_kv(m: spec.ModelShape, seed: int, session: int, n: int, threads=None
         rng.normal(seed, 2 * session + 1, n * D, 1.0, offset=off, dtype=dt, threads=threads,
                    out=v[l].reshape(-1))
     return k, v
+
+
+def prefill_bank(m: spec.ModelShape, seed: int, threads=None):
+    """A shared bank of N(0, 1) K and V for all W positions ([L][W][D], bank
+    session id 0). Large workloads build each session's prefill from it."""
+    return prefill_kv(m, seed, 0, m.window, threads=threads)
+
+
+def prefill_from_bank(bank, session: int, n: int, stride: int = 47):
+    """Session `session`'s prefill of n positions: the bank rotated by
+    stride*session positions, then cut to n (distinct content per session
+    without drawing W*D*2*L fresh values for every one of them)."""
+    k, v = bank
+    W = k.shape[1]
+    idx = (np.arange(n) + stride * session) % W
+    return np.ascontiguousarray(k[:, idx]), np.ascontiguousarray(v[:, idx])
 
 
 def dep_inputs(m: spec.ModelShape, seed: int, t0: int, count: int):

@@ -80,6 +80,24 @@ def test_ragged_bf16_elastic_parity():
     log("ragged:", stats)
 
 
+def test_multichunk_window_parity():
+    """Window of 150 keys = 3 attention chunks with a ragged last one; a full
+    ring, a partial one and an empty one, all wrapping."""
+    shape = spec.RAGGED.replace(window=150)
+    weights = wl.make_weights(shape, 29, gains="random")
+    plan = {0: [("join", 0, 150), ("join", 1, 70), ("join", 2, 0)]}
+    _, stats = _run_sessions(shape, weights, 3, plan, 40)
+    log("multichunk:", stats)
+
+
+def test_multichunk_single_session():
+    """The one-session projection path with a multi-chunk window."""
+    shape = spec.RAGGED.replace(window=200)
+    weights = wl.make_weights(shape, 31, gains="random")
+    _, stats = _run_sessions(shape, weights, 1, {0: [("join", 0, 190)]}, 20)
+    log("multichunk B=1:", stats)
+
+
 def test_mask_oldest_parity():
     shape = spec.RAGGED.replace(mask_oldest=True, window=9)
     weights = wl.make_weights(shape, 5, gains="random")
