@@ -72,7 +72,13 @@ const char* config_error(const moshi_config* c) {
   if (c->ffn_hidden <= 0 || c->dep_ffn_hidden <= 0) return "ffn widths must be positive";
   if (c->dim % vec || c->ffn_hidden % vec || c->dep_dim % vec || c->dep_ffn_hidden % vec)
     return "widths must be multiples of 8 (bf16) / 4 (fp32)";
-  if (c->window < 1) return "window must be >= 1";
+  if (c->window < 1 || c->window > ATTN_CHUNK * ATTN_MAX_CHUNKS) return "window must be in [1, 32768]";
+  {
+    const int esz = c->dtype == MOSHI_BF16 ? 2 : 4;
+    const int kmax = c->ffn_hidden > c->dim ? c->ffn_hidden : c->dim;
+    if ((long)kmax * esz > 49152 || (long)c->dep_ffn_hidden * esz > 49152)
+      return "projection inputs must fit 48 KB of LDS (ffn_hidden * element size)";
+  }
   if ((c->flags & MOSHI_FLAG_MASK_OLDEST) && c->window < 2) return "mask-oldest needs window >= 2";
   if (c->flags & ~MOSHI_FLAG_MASK_OLDEST) return "unknown flag bits";
   if (c->text_vocab < 2 || c->audio_card < 2) return "vocabularies must have >= 2 entries";

@@ -128,8 +128,9 @@ struct EntryArgs {
   double* ssq_out;  // [ceil(D/16)][B]
 };
 
-// Keys per attention workgroup.
+// Keys per attention workgroup; the window is at most ATTN_CHUNK * ATTN_MAX_CHUNKS.
 constexpr int ATTN_CHUNK = 64;
+constexpr int ATTN_MAX_CHUNKS = 512;
 
 int gemm_tiles(int epi, int N);  // grid size of a projection
 // Waves per workgroup for a projection with K inputs and B sessions.

@@ -271,93 +271,97 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int g, int
 // One session: fp64 VALU GEMV
 // ---------------------------------------------------------------------------
 
-// Workgroup = KW waves and 16 output rows. Wave w takes K steps [s0, s1) of
-// 64*VEC elements; lane l covers elements step*64*VEC + l*VEC .. +VEC of every
-// row, so its slice of the input vector is the same for all 16 rows.
+// Workgroup = KW waves and 16 output rows; wave w owns rows w*R .. w*R+R-1
+// (R = 16/KW) over the whole of K. The rounded input vector is built once per
+// workgroup in LDS (in the model dtype); lane l covers the 16-byte groups
+// l, l+64, ... of every row, so a wave reads each of its rows in contiguous
+// 1 KB pieces. Each row is reduced over the 64 lanes by a butterfly, then
+// wave 0 applies the epilogue to the 16 rows.
 template <typename T, int KW, int PRO, int EPI>
 __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
+  extern __shared__ __align__(16) unsigned char s_dyn[];  // rounded input, K elements
   constexpr int VEC = VecOf<T>::N;
-  constexpr int KSTEP = 64 * VEC;
-  constexpr int SMAX = 2;  // K steps per batch of weight loads (16 rows each)
+  constexpr int R = 16 / KW;        // rows per wave
+  constexpr int U = (R <= 2) ? 8 : 4;  // 16-byte groups in flight per row per batch
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tile = blockIdx.x;
-  __shared__ double s_red[KW][16];
+  T* xs = (T*)s_dyn;
+  __shared__ double s_red[16];
   __shared__ double s_tmp[KW];
 
-  const T* wrow[16];
-  bool rok[16];
+  const T* wrow[R];
+  bool rok[R];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
-    const int r = tile_row<EPI>(tile, t, a.N, rok[t]);
-    wrow[t] = (const T*)a.W + (size_t)(rok[t] ? r : 0) * a.K;
+  for (int r = 0; r < R; ++r) {
+    const int rr = tile_row<EPI>(tile, wave * R + r, a.N, rok[r]);
+    wrow[r] = (const T*)a.W + (size_t)(rok[r] ? rr : 0) * a.K;
   }
-  const int nsteps = (a.K + KSTEP - 1) / KSTEP;
-  const int s0 = (wave * nsteps) / KW;
-  const int s1 = ((wave + 1) * nsteps) / KW;
+  const int ngroups = a.K / VEC;  // K is a multiple of VEC
 
-  u32x4 wv[SMAX][16];
-  auto load_w = [&](int st) {
+  u32x4 wv[U][R];
+  auto load_w = [&](int g0) {
 #pragma unroll
-    for (int u = 0; u < SMAX; ++u) {
-      const int k0 = (st + u) * KSTEP + lane * VEC;
-      const bool kok = (st + u < s1) && (k0 < a.K);
+    for (int u = 0; u < U; ++u) {
+      const int gi = g0 + u * 64 + lane;
 #pragma unroll
-      for (int t = 0; t < 16; ++t)
-        wv[u][t] = (kok && rok[t]) ? ld16_stream(wrow[t] + k0) : u32x4{0u, 0u, 0u, 0u};
+      for (int r = 0; r < R; ++r)
+        wv[u][r] = (gi < ngroups && rok[r]) ? ld16_stream(wrow[r] + (size_t)gi * VEC)
+                                            : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  load_w(s0);  // first batch in flight across the norm prologue
+  load_w(0);  // first batch in flight while the input vector is built
 
+  // input vector -> LDS (rounded to the model dtype)
   double rs = 1.0;
   if constexpr (PRO == PRO_NORM) rs = rms_scale(a, 0, s_tmp, 64 * KW);
   const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && tile == 0;
+  for (int gi = threadIdx.x; gi < ngroups; gi += 64 * KW) {
+    double xv[VEC];
+    u32x4 packed;
+    load_x<T, PRO>(a, 0, gi * VEC, rs, xv, &packed);
+    *(u32x4*)(xs + (size_t)gi * VEC) = packed;
+    if (write_xn) *(u32x4*)((T*)a.xn_out + (size_t)gi * VEC) = packed;
+  }
+  __syncthreads();
 
-  double acc[16];
+  double acc[R];
 #pragma unroll
-  for (int t = 0; t < 16; ++t) acc[t] = 0.0;
-  for (int st = s0; st < s1; st += SMAX) {
-    if (st != s0) load_w(st);
+  for (int r = 0; r < R; ++r) acc[r] = 0.0;
+  for (int g0 = 0; g0 < ngroups; g0 += U * 64) {
+    if (g0 != 0) load_w(g0);
 #pragma unroll
-    for (int u = 0; u < SMAX; ++u) {
-      const int k0 = (st + u) * KSTEP + lane * VEC;
-      if (st + u < s1 && k0 < a.K) {
+    for (int u = 0; u < U; ++u) {
+      const int gi = g0 + u * 64 + lane;
+      if (gi < ngroups) {
         double xv[VEC];
-        u32x4 packed;
-        load_x<T, PRO>(a, 0, k0, rs, xv, &packed);
-        if (write_xn) *(u32x4*)((T*)a.xn_out + k0) = packed;
+        widen<T>(*(const u32x4*)(xs + (size_t)gi * VEC), xv);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
+        for (int r = 0; r < R; ++r) {
           double wd[VEC];
-          widen<T>(wv[u][t], wd);
+          widen<T>(wv[u][r], wd);
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[t] = fma(wd[e], xv[e], acc[t]);
+          for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
         }
       }
     }
   }
-  // per-row sums over the 64 lanes (butterfly), then over the waves in order
+  // row sums over the 64 lanes (same butterfly for every row and launch)
 #pragma unroll
-  for (int t = 0; t < 16; ++t) {
+  for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc[t] += shfl_xor_d(acc[t], off);
+    for (int off = 32; off > 0; off >>= 1) acc[r] += shfl_xor_d(acc[r], off);
   }
   if (lane == 0) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) s_red[wave][t] = acc[t];
+    for (int r = 0; r < R; ++r) s_red[wave * R + r] = acc[r];
   }
   __syncthreads();
   if (wave != 0) return;
   // epilogue lanes: g = lane / 16 holds rows 4g..4g+3 of column lane % 16 (= 0)
   const int g = lane >> 4;
   if ((lane & 15) != 0) return;
-  double v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    double s = s_red[0][4 * g + i];
-    for (int w = 1; w < KW; ++w) s += s_red[w][4 * g + i];
-    v[i] = s;
-  }
+  const double v[4] = {s_red[4 * g], s_red[4 * g + 1], s_red[4 * g + 2], s_red[4 * g + 3]};
   epilogue<T, EPI>(a, tile, g, 0, v);
 }
 
@@ -632,6 +636,7 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
   if (nchunks <= 1) return;  // written directly by attn_kernel
   const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
   __shared__ double s_m[HD / 64 > 0 ? HD / 64 : 1];
+  __shared__ double s_w[ATTN_MAX_CHUNKS];
   // M = max over the chunk maxima (exact, so any reduction order gives the same M)
   double mloc = -INFINITY;
   for (int c = t; c < nchunks; c += HD) mloc = fmax(mloc, parts[(size_t)c * (HD + 2)]);
@@ -642,14 +647,19 @@ __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
   __syncthreads();
   double M = s_m[0];
   for (int w = 1; w < HD / 64; ++w) M = fmax(M, s_m[w]);
+  // chunk weights e^{m_c - M}, one exp per chunk
+  for (int c = t; c < nchunks; c += HD) {
+    const double mc = parts[(size_t)c * (HD + 2)];
+    s_w[c] = (mc == -INFINITY) ? 0.0 : exp(mc - M);
+  }
+  __syncthreads();
   double L = 0.0, O = 0.0;
 #pragma unroll 8
   for (int c = 0; c < nchunks; ++c) {
     const double* pc = parts + (size_t)c * (HD + 2);
-    const double mc = pc[0];
-    const double w = (mc == -INFINITY) ? 0.0 : exp(mc - M);
-    L += pc[1] * w;
-    O += pc[2 + t] * w;
+    const double w = s_w[c];
+    L = fma(pc[1], w, L);
+    O = fma(pc[2 + t], w, O);
   }
   ((T*)a.o_out)[(size_t)b * a.ldo + h * HD + t] = round_to<T>(L > 0.0 ? O / L : 0.0);
 }
@@ -783,21 +793,19 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* ring, T* dst, int 
 int gemm_tiles(int epi, int N) { return epi == EPI_SWIGLU ? (N + 7) / 8 : (N + 15) / 16; }
 
 int gemm_kw(int dtype, int B, int K) {
-  if (B == 1) {
-    const int kstep = 64 * (dtype == DT_BF16 ? 8 : 4);
-    const int nsteps = (K + kstep - 1) / kstep;
-    return nsteps >= 8 ? 8 : (nsteps >= 4 ? 4 : 2);
-  }
+  (void)dtype;
+  if (B == 1) return 8;  // 2 rows per wave
   return K >= 4096 ? 8 : 4;
 }
 
 template <typename T, int KW>
 static hipError_t launch_gemv_kw(int pro, int epi, const GemmArgs& a, hipStream_t st) {
   dim3 grid(gemm_tiles(epi, a.N)), block(64 * KW);
-#define MOSHI_GEMV_CASE(P, E)                                                \
-  if (pro == P && epi == E) {                                               \
-    hipLaunchKernelGGL((gemv_kernel<T, KW, P, E>), grid, block, 0, st, a); \
-    return hipGetLastError();                                               \
+  const size_t lds = (size_t)a.K * sizeof(T);
+#define MOSHI_GEMV_CASE(P, E)                                                  \
+  if (pro == P && epi == E) {                                                 \
+    hipLaunchKernelGGL((gemv_kernel<T, KW, P, E>), grid, block, lds, st, a); \
+    return hipGetLastError();                                                 \
   }
   MOSHI_GEMV_CASE(PRO_NORM, EPI_QKV)
   MOSHI_GEMV_CASE(PRO_DIRECT, EPI_RESID)
