@@ -745,6 +745,11 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
     release(c);
     return MOSHI_E_DEVICE;
   }
+  {
+    int ncu = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess)
+      set_gemv_grid(ncu);
+  }
   int rc = MOSHI_OK;
   if (hip_stream) {
     c->stream = (hipStream_t)hip_stream;

@@ -132,8 +132,11 @@ struct EntryArgs {
 constexpr int ATTN_CHUNK = 64;
 constexpr int ATTN_MAX_CHUNKS = 512;
 
-int gemm_tiles(int epi, int N);  // grid size of a projection
-// Waves per workgroup for a projection with K inputs and B sessions.
+int gemm_tiles(int epi, int N);  // row tiles of a projection
+// Workgroups launched for a one-session projection (the number of CUs).
+void set_gemv_grid(int n);
+// Waves per workgroup for a projection with K inputs and B sessions (8 for
+// the 4096-wide temporal inputs, 4 for the depformer's).
 int gemm_kw(int dtype, int B, int K);
 // kw from gemm_kw. With B > 1 and PRO_NORM / PRO_CAST, xn_out must be a
 // [B][K] buffer: the rounded input vectors are written there first.

@@ -271,51 +271,53 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int g, int
 // One session: fp64 VALU GEMV
 // ---------------------------------------------------------------------------
 
-// Workgroup = KW waves and 16 output rows; wave w owns rows w*R .. w*R+R-1
-// (R = 16/KW) over the whole of K. The rounded input vector is built once per
-// workgroup in LDS (in the model dtype); lane l covers the 16-byte groups
-// l, l+64, ... of every row, so a wave reads each of its rows in contiguous
-// 1 KB pieces. Each row is reduced over the 64 lanes by a butterfly, then
-// wave 0 applies the epilogue to the 16 rows.
+// A workgroup of KW waves walks row tiles blockIdx.x, +gridDim.x, ... (16
+// output rows each); wave w owns rows w*R .. w*R+R-1 (R = 16/KW) of a tile
+// over the whole of K. The rounded input vector is built once per workgroup in
+// LDS (model dtype). Lane l covers the 16-byte groups l, l+64, ... of a row, so
+// a wave reads each row in contiguous 1 KB pieces. Weights stream in batches
+// of U groups per lane and row, double-buffered: the next batch (possibly of
+// the next tile) is requested before the current one is used. Each finished
+// row is reduced over the 64 lanes by a butterfly; wave 0 applies the
+// epilogue to the tile's 16 rows.
 template <typename T, int KW, int PRO, int EPI>
 __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char s_dyn[];  // rounded input, K elements
   constexpr int VEC = VecOf<T>::N;
-  constexpr int R = 16 / KW;        // rows per wave
-  constexpr int U = (R <= 2) ? 8 : 4;  // 16-byte groups in flight per row per batch
+  constexpr int R = 16 / KW;                 // rows per wave
+  constexpr int U = (R <= 2) ? 8 : 4;        // groups per lane and row per batch
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int tile = blockIdx.x;
   T* xs = (T*)s_dyn;
-  __shared__ double s_red[16];
+  __shared__ double s_red[2][16];
   __shared__ double s_tmp[KW];
 
-  const T* wrow[R];
-  bool rok[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int rr = tile_row<EPI>(tile, wave * R + r, a.N, rok[r]);
-    wrow[r] = (const T*)a.W + (size_t)(rok[r] ? rr : 0) * a.K;
-  }
+  const int ntiles = (EPI == EPI_SWIGLU) ? (a.N + 7) / 8 : (a.N + 15) / 16;
   const int ngroups = a.K / VEC;  // K is a multiple of VEC
+  const int nbatch = (ngroups + U * 64 - 1) / (U * 64);
 
-  u32x4 wv[U][R];
-  auto load_w = [&](int g0) {
+  auto load_batch = [&](u32x4 (&w)[U][R], int tile, int bt) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int gi = g0 + u * 64 + lane;
+    for (int r = 0; r < R; ++r) {
+      bool ok;
+      const int rr = tile_row<EPI>(tile, wave * R + r, a.N, ok);
+      const T* wr = (const T*)a.W + (size_t)(ok ? rr : 0) * a.K;
 #pragma unroll
-      for (int r = 0; r < R; ++r)
-        wv[u][r] = (gi < ngroups && rok[r]) ? ld16_stream(wrow[r] + (size_t)gi * VEC)
-                                            : u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < U; ++u) {
+        const int gi = bt * U * 64 + u * 64 + lane;
+        w[u][r] = (ok && gi < ngroups) ? ld16_stream(wr + (size_t)gi * VEC) : u32x4{0u, 0u, 0u, 0u};
+      }
     }
   };
-  load_w(0);  // first batch in flight while the input vector is built
+
+  int tile = blockIdx.x;
+  u32x4 wa[U][R], wb[U][R];
+  if (tile < ntiles) load_batch(wa, tile, 0);  // in flight while the input is built
 
   // input vector -> LDS (rounded to the model dtype)
   double rs = 1.0;
   if constexpr (PRO == PRO_NORM) rs = rms_scale(a, 0, s_tmp, 64 * KW);
-  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && tile == 0;
+  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && blockIdx.x == 0;
   for (int gi = threadIdx.x; gi < ngroups; gi += 64 * KW) {
     double xv[VEC];
     u32x4 packed;
@@ -324,45 +326,76 @@ __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
     if (write_xn) *(u32x4*)((T*)a.xn_out + (size_t)gi * VEC) = packed;
   }
   __syncthreads();
+  if (tile >= ntiles) return;
 
   double acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = 0.0;
-  for (int g0 = 0; g0 < ngroups; g0 += U * 64) {
-    if (g0 != 0) load_w(g0);
+  int bt = 0, parity = 0;
+
+  // consume batch (tile, bt) held in w; finish the tile after its last batch
+  auto consume = [&](const u32x4 (&w)[U][R]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int gi = g0 + u * 64 + lane;
+      const int gi = bt * U * 64 + u * 64 + lane;
       if (gi < ngroups) {
         double xv[VEC];
         widen<T>(*(const u32x4*)(xs + (size_t)gi * VEC), xv);
 #pragma unroll
         for (int r = 0; r < R; ++r) {
           double wd[VEC];
-          widen<T>(wv[u][r], wd);
+          widen<T>(w[u][r], wd);
 #pragma unroll
           for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
         }
       }
     }
-  }
-  // row sums over the 64 lanes (same butterfly for every row and launch)
+    if (bt == nbatch - 1) {
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
+      for (int r = 0; r < R; ++r) {
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) acc[r] += shfl_xor_d(acc[r], off);
-  }
-  if (lane == 0) {
+        for (int off = 32; off > 0; off >>= 1) acc[r] += shfl_xor_d(acc[r], off);
+      }
+      if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) s_red[wave * R + r] = acc[r];
+        for (int r = 0; r < R; ++r) s_red[parity][wave * R + r] = acc[r];
+      }
+      __syncthreads();
+      if (wave == 0 && (lane & 15) == 0) {
+        // g = lane / 16 holds rows 4g..4g+3 of column 0
+        const int g = lane >> 4;
+        const double v[4] = {s_red[parity][4 * g], s_red[parity][4 * g + 1],
+                             s_red[parity][4 * g + 2], s_red[parity][4 * g + 3]};
+        epilogue<T, EPI>(a, tile, g, 0, v);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = 0.0;
+      parity ^= 1;
+    }
+  };
+  // the batch after (tile, bt)
+  auto advance = [&](int& t, int& b) {
+    if (++b == nbatch) {
+      b = 0;
+      t += gridDim.x;
+    }
+  };
+
+  for (;;) {
+    int nt = tile, nb = bt;
+    advance(nt, nb);
+    if (nt < ntiles) load_batch(wb, nt, nb);
+    consume(wa);
+    if (nt >= ntiles) break;
+    tile = nt;
+    bt = nb;
+    advance(nt, nb);
+    if (nt < ntiles) load_batch(wa, nt, nb);
+    consume(wb);
+    if (nt >= ntiles) break;
+    tile = nt;
+    bt = nb;
   }
-  __syncthreads();
-  if (wave != 0) return;
-  // epilogue lanes: g = lane / 16 holds rows 4g..4g+3 of column lane % 16 (= 0)
-  const int g = lane >> 4;
-  if ((lane & 15) != 0) return;
-  const double v[4] = {s_red[4 * g], s_red[4 * g + 1], s_red[4 * g + 2], s_red[4 * g + 3]};
-  epilogue<T, EPI>(a, tile, g, 0, v);
 }
 
 // ---------------------------------------------------------------------------
@@ -794,13 +827,19 @@ int gemm_tiles(int epi, int N) { return epi == EPI_SWIGLU ? (N + 7) / 8 : (N + 1
 
 int gemm_kw(int dtype, int B, int K) {
   (void)dtype;
-  if (B == 1) return 8;  // 2 rows per wave
+  // temporal projections (K >= 4096): 8 waves; depformer ones: 4 waves
   return K >= 4096 ? 8 : 4;
 }
 
+// Workgroups of the one-session projection: at most one per CU (the kernel
+// loops over row tiles), never more than there are tiles.
+static int g_gemv_grid = 256;
+void set_gemv_grid(int n) { g_gemv_grid = n > 0 ? n : 256; }
+
 template <typename T, int KW>
 static hipError_t launch_gemv_kw(int pro, int epi, const GemmArgs& a, hipStream_t st) {
-  dim3 grid(gemm_tiles(epi, a.N)), block(64 * KW);
+  const int ntiles = gemm_tiles(epi, a.N);
+  dim3 grid(ntiles < g_gemv_grid ? ntiles : g_gemv_grid), block(64 * KW);
   const size_t lds = (size_t)a.K * sizeof(T);
 #define MOSHI_GEMV_CASE(P, E)                                                  \
   if (pro == P && epi == E) {                                                 \
