@@ -43,6 +43,9 @@ def parse():
                     help="full-size frames the CPU oracle runs for its baseline")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--b16", type=int, default=1, help="also measure B=16 (elastic fills)")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (the reference "
+                         "dispatch that scales HBM byte counters)")
     return ap.parse_args()
 
 
@@ -90,6 +93,28 @@ def kernel_table(M, ctx, frames_host, n):
                      "bytes_per_step": by,
                      "GBps": round(by / (ms * 1e6), 1) if ms > 0 else None}
     return out
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "full_duplex_speech_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter runs
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the kernel
+    source has changed since they were taken."""
+    import hashlib
+    try:
+        with open(KERNEL_SRC, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                kv = dict(x.split("=", 1) for x in line.split() if "=" in x)
+                if kv.get("kernel") == kernel and kv.get("kernels_sha256") == sha:
+                    return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline(shape, weights, k, v, frames, n):
@@ -157,13 +182,23 @@ def main():
     achieved = d["bytes_per_step"] / (d["ms_per_step"] * 1e6)  # GB/s
     roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None,
+                "traffic": measured_traffic(dname),
                 "bytes_per_launch": d["bytes_per_step"] / d["launches_per_step"],
                 "ms_per_launch": d["ms_per_step"] / d["launches_per_step"]}
     step_gbs = bytes_step / (ms_wall * 1e6)
     log(f"dominant kernel {dname}: {achieved:.0f} GB/s; step {step_gbs:.0f} GB/s")
     M.moshi_destroy(ctx)
     del ctx
+
+    if args.copy_mib > 0:
+        n = args.copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
+        del src, dst
 
     # ---------------- B = 16: elastic fills ----------------
     b16 = None
@@ -207,7 +242,8 @@ def main():
     rec = {
         "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_wall, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+        "storage": "bf16 weights, embeddings, K/V rings and projection inputs",
         "data": "synthetic",
         "config": {"workload": "full frame step, B=1: temporal 4096-d/32L/32h, F 11264, ring "
                                "prefilled to the 3000-frame window; text head 32000; depformer "
