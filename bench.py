@@ -96,21 +96,29 @@ def kernel_table(M, ctx, frames_host, n):
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.txt")
-KERNEL_SRC = os.path.join(ROOT, "full_duplex_speech_amd", "csrc", "kernels.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "full_duplex_speech_amd", "csrc", f)
+               for f in ("dev.h", "kernels.h", "kernels.hip", "step.hip")]
+
+
+def kernel_sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for p in KERNEL_SRCS:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed counter runs
     (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy), or None when the kernel
-    source has changed since they were taken."""
-    import hashlib
+    sources have changed since they were taken."""
     try:
-        with open(KERNEL_SRC, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
+        sha = kernel_sources_sha256()
         with open(TRAFFIC_FILE) as f:
             for line in f:
                 kv = dict(x.split("=", 1) for x in line.split() if "=" in x)
-                if kv.get("kernel") == kernel and kv.get("kernels_sha256") == sha:
+                if kv.get("kernel") == kernel and kv.get("sources_sha256") == sha:
                     return float(kv["fetch_bytes"]) + float(kv["write_bytes"])
     except OSError:
         pass
@@ -175,16 +183,23 @@ def main():
 
     kt = kernel_table(M, ctx, frames[0][None, :], args.timing_steps)
     bytes_step = sum(x["bytes_per_step"] for x in kt.values())
-    # the dominant kernel: the temporal gate/up projection, the largest weight
-    # stream of the step (184.5 MB per launch, 32 launches)
-    dname = "temporal_gateup"
-    d = kt[dname]
-    achieved = d["bytes_per_step"] / (d["ms_per_step"] * 1e6)  # GB/s
+    if M.moshi_uses_step_kernel(ctx):
+        # the whole step is one persistent kernel: its launch duration is the
+        # event-timed step (one launch per step, back to back on the stream)
+        dname = "step_kernel"
+        d_bytes, d_ms = bytes_step, ms_gpu
+    else:
+        # the temporal gate/up projection, the largest weight stream of the
+        # step (184.5 MB per launch, 32 launches)
+        dname = "temporal_gateup"
+        d = kt[dname]
+        d_bytes = d["bytes_per_step"] / d["launches_per_step"]
+        d_ms = d["ms_per_step"] / d["launches_per_step"]
+    achieved = d_bytes / (d_ms * 1e6)  # GB/s
     roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dname),
-                "bytes_per_launch": d["bytes_per_step"] / d["launches_per_step"],
-                "ms_per_launch": d["ms_per_step"] / d["launches_per_step"]}
+                "traffic": measured_traffic(dname), "bytes_per_launch": d_bytes,
+                "ms_per_launch": round(d_ms, 5)}
     step_gbs = bytes_step / (ms_wall * 1e6)
     log(f"dominant kernel {dname}: {achieved:.0f} GB/s; step {step_gbs:.0f} GB/s")
     M.moshi_destroy(ctx)

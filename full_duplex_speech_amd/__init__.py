@@ -24,7 +24,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmoshi.so")
 _CSRC = os.path.join(_HERE, "csrc")
-_SOURCES = [os.path.join(_CSRC, "kernels.hip"), os.path.join(_CSRC, "engine.cpp")]
+_SOURCES = [os.path.join(_CSRC, "kernels.hip"), os.path.join(_CSRC, "step.hip"),
+            os.path.join(_CSRC, "engine.cpp")]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                # no packed-fp32 instructions in any kernel
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -94,6 +95,7 @@ def lib():
             "moshi_read_hidden": ([vp, vp], ctypes.c_int),
             "moshi_time_kernels": ([vp, vp, i32, vp, vp, vp, i32], ctypes.c_int),
             "moshi_kernel_class_name": ([i32], ctypes.c_char_p),
+            "moshi_uses_step_kernel": ([vp], i32),
             "moshi_strerror": ([ctypes.c_int], ctypes.c_char_p),
             "moshi_last_error": ([vp], ctypes.c_char_p),
         }
@@ -262,6 +264,11 @@ def moshi_read_hidden(ctx: Ctx):
     h = np.empty((ctx.B, ctx.D), np.float32)
     _check(lib().moshi_read_hidden(ctx.h, _p(h)), ctx)
     return h
+
+
+def moshi_uses_step_kernel(ctx: Ctx) -> bool:
+    """True when a step runs as one persistent kernel (see include/moshi.h)."""
+    return _check(lib().moshi_uses_step_kernel(ctx.h), ctx) == 1
 
 
 def moshi_kernel_class_name(c: int) -> str:

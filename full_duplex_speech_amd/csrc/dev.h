@@ -1,0 +1,993 @@
+// dev.h -- device code shared by the per-operation kernels (kernels.hip) and
+// the persistent one-session step kernel (step.hip): conversions, rounding,
+// the projection (GEMV) loop with its prologues and epilogues, and the
+// windowed-attention pieces.
+//
+// Template flag C ("coherent"): inside the persistent step kernel, vectors
+// produced by one workgroup are read by others after a grid barrier, so every
+// such load and store is an agent-scope relaxed atomic (global_load/store
+// with sc1: it bypasses the non-coherent caches, so other XCDs see it).
+// Weights, tables and anything not written during the kernel use ordinary
+// loads. With C = false (one kernel per operation) kernel boundaries order
+// everything and plain accesses are used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace moshi {
+
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // one 16-byte group
+
+template <typename T>
+struct VecOf;
+template <>
+struct VecOf<__bf16> {
+  static constexpr int N = 8;  // elements per 16-byte group
+};
+template <>
+struct VecOf<float> {
+  static constexpr int N = 4;
+};
+
+// Every device pointer here is global memory; saying so makes the compiler
+// emit global_* instead of flat_* instructions (flat ones also count against
+// lgkmcnt, so every workgroup barrier would wait for loads in flight).
+#define MOSHI_GLB __attribute__((address_space(1)))
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *(const MOSHI_GLB u32x4*)p; }
+// Weights are read once per step: stream them past the caches.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load((const MOSHI_GLB u32x4*)p);
+}
+
+// ---- activation accesses (see C above) -------------------------------------
+
+#define MOSHI_RLX __ATOMIC_RELAXED
+#define MOSHI_AGT __HIP_MEMORY_SCOPE_AGENT
+
+template <bool C>
+__device__ __forceinline__ uint64_t ld_u64(const void* p) {
+  if constexpr (C) return __hip_atomic_load((MOSHI_GLB uint64_t*)p, MOSHI_RLX, MOSHI_AGT);
+  else return *(const MOSHI_GLB uint64_t*)p;
+}
+template <bool C>
+__device__ __forceinline__ void st_u64(void* p, uint64_t v) {
+  if constexpr (C) __hip_atomic_store((MOSHI_GLB uint64_t*)p, v, MOSHI_RLX, MOSHI_AGT);
+  else *(MOSHI_GLB uint64_t*)p = v;
+}
+template <bool C>
+__device__ __forceinline__ void st_u32(void* p, uint32_t v) {
+  if constexpr (C) __hip_atomic_store((MOSHI_GLB uint32_t*)p, v, MOSHI_RLX, MOSHI_AGT);
+  else *(MOSHI_GLB uint32_t*)p = v;
+}
+template <bool C>
+__device__ __forceinline__ void st_u16(void* p, uint16_t v) {
+  if constexpr (C) __hip_atomic_store((MOSHI_GLB uint16_t*)p, v, MOSHI_RLX, MOSHI_AGT);
+  else *(MOSHI_GLB uint16_t*)p = v;
+}
+template <bool C>
+__device__ __forceinline__ int ld_i32(const int* p) {
+  if constexpr (C) return __hip_atomic_load((MOSHI_GLB int*)p, MOSHI_RLX, MOSHI_AGT);
+  else return *(const MOSHI_GLB int*)p;
+}
+template <bool C>
+__device__ __forceinline__ void st_i32(int* p, int v) {
+  if constexpr (C) __hip_atomic_store((MOSHI_GLB int*)p, v, MOSHI_RLX, MOSHI_AGT);
+  else *(MOSHI_GLB int*)p = v;
+}
+// plain read-only loads of global memory (tables, positions, gains)
+template <typename V>
+__device__ __forceinline__ V ldg(const V* p) {
+  return *(const MOSHI_GLB V*)p;
+}
+template <bool C>
+__device__ __forceinline__ double ld_f64(const double* p) {
+  return __builtin_bit_cast(double, ld_u64<C>(p));
+}
+template <bool C>
+__device__ __forceinline__ void st_f64(double* p, double v) {
+  st_u64<C>(p, __builtin_bit_cast(uint64_t, v));
+}
+// one 16-byte group
+template <bool C>
+__device__ __forceinline__ u32x4 ld_grp(const void* p) {
+  if constexpr (C) {
+    const uint64_t a = ld_u64<true>(p), b = ld_u64<true>((const char*)p + 8);
+    return u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)b, (unsigned)(b >> 32)};
+  } else {
+    return ld16(p);
+  }
+}
+template <bool C>
+__device__ __forceinline__ void st_grp(void* p, u32x4 v) {
+  if constexpr (C) {
+    st_u64<true>(p, (uint64_t)v[0] | ((uint64_t)v[1] << 32));
+    st_u64<true>((char*)p + 8, (uint64_t)v[2] | ((uint64_t)v[3] << 32));
+  } else {
+    *(MOSHI_GLB u32x4*)p = v;
+  }
+}
+
+// threadIdx.x, re-read at every use site: values derived from it are then not
+// hoisted out of the layer loops of the step kernel, where they would stay
+// live across every operation and exhaust the registers.
+__device__ __forceinline__ int tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+// ---- conversions -----------------------------------------------------------
+
+template <typename T>
+__device__ __forceinline__ void widen(u32x4 w, double* out);
+template <>
+__device__ __forceinline__ void widen<__bf16>(u32x4 w, double* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out[2 * i] = (double)__uint_as_float(w[i] << 16);
+    out[2 * i + 1] = (double)__uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void widen<float>(u32x4 w, double* out) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) out[i] = (double)__uint_as_float(w[i]);
+}
+
+__device__ __forceinline__ double to_d(__bf16 v) { return (double)(float)v; }
+__device__ __forceinline__ double to_d(float v) { return (double)v; }
+
+// bf16 bits of the value nearest to d (ties to even). Rounding d to fp32 first
+// is exact enough except when that lands exactly on a bf16 midpoint while d
+// itself is not on it; then d decides the direction.
+__device__ __forceinline__ unsigned short bf16_bits_rne(double d) {
+  const float f = (float)d;
+  unsigned int u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u)
+    return (unsigned short)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  if ((u & 0xffffu) == 0x8000u && (double)f != d) {
+    const bool up = fabs(d) > fabs((double)f);
+    return (unsigned short)((u >> 16) + (up ? 1u : 0u));
+  }
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (unsigned short)(u >> 16);
+}
+
+template <typename T>
+__device__ __forceinline__ T round_to(double d);
+template <>
+__device__ __forceinline__ __bf16 round_to<__bf16>(double d) {
+  return __builtin_bit_cast(__bf16, bf16_bits_rne(d));
+}
+template <>
+__device__ __forceinline__ float round_to<float>(double d) {
+  return (float)d;
+}
+
+// Stored bits of round_to<T>(d), zero-extended.
+template <typename T>
+__device__ __forceinline__ uint32_t stored_bits(double d);
+template <>
+__device__ __forceinline__ uint32_t stored_bits<__bf16>(double d) {
+  return bf16_bits_rne(d);
+}
+template <>
+__device__ __forceinline__ uint32_t stored_bits<float>(double d) {
+  return __float_as_uint((float)d);
+}
+
+// n consecutive rounded values (n = 1, 2 or 4) stored at p.
+template <typename T, bool C>
+__device__ __forceinline__ void store_rounded(T* p, const double* v, int n) {
+  if constexpr (sizeof(T) == 2) {
+    if (n == 4) {
+      uint64_t w = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w |= (uint64_t)stored_bits<T>(v[i]) << (16 * i);
+      st_u64<C>(p, w);
+    } else if (n == 2) {
+      st_u32<C>(p, stored_bits<T>(v[0]) | (stored_bits<T>(v[1]) << 16));
+    } else {
+      st_u16<C>(p, (uint16_t)stored_bits<T>(v[0]));
+    }
+  } else {
+    if (n == 4) {
+      st_grp<C>(p, u32x4{stored_bits<T>(v[0]), stored_bits<T>(v[1]), stored_bits<T>(v[2]),
+                         stored_bits<T>(v[3])});
+    } else if (n == 2) {
+      st_u64<C>(p, (uint64_t)stored_bits<T>(v[0]) | ((uint64_t)stored_bits<T>(v[1]) << 32));
+    } else {
+      st_u32<C>(p, stored_bits<T>(v[0]));
+    }
+  }
+}
+
+// The input vector in two steps: the raw values of one 16-byte group (its
+// loads can be issued before the norm scale is known), then the rounded
+// values as doubles and packed for storing.
+template <typename T, int PRO, bool C>
+struct XRaw {
+  static constexpr int VEC = VecOf<T>::N;
+  u32x4 w;          // PRO_DIRECT: the stored group
+  double x[VEC];    // PRO_NORM / PRO_CAST: fp64 inputs
+  double g[VEC];    // PRO_NORM: gains
+};
+
+template <typename T, int PRO, bool C>
+__device__ __forceinline__ void load_x_raw(const GemmArgs& a, int col, int k0, XRaw<T, PRO, C>& r) {
+  constexpr int VEC = VecOf<T>::N;
+  if constexpr (PRO == PRO_DIRECT) {
+    r.w = ld_grp<C>((const T*)a.X + (size_t)col * a.ldx + k0);
+  } else {
+    const double* xp = (const double*)a.X + (size_t)col * a.ldx + k0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) r.x[e] = ld_f64<C>(xp + e);
+    if constexpr (PRO == PRO_NORM) widen<T>(ld16((const T*)a.gain + k0), r.g);
+  }
+}
+
+template <typename T, int PRO, bool C>
+__device__ __forceinline__ void finish_x(const XRaw<T, PRO, C>& r, double rs, double* xv,
+                                         u32x4* packed) {
+  constexpr int VEC = VecOf<T>::N;
+  if constexpr (PRO == PRO_DIRECT) {
+    widen<T>(r.w, xv);
+    *packed = r.w;
+  } else {
+    u32x4 q;
+    T* rv = (T*)&q;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const double v = (PRO == PRO_NORM) ? r.x[e] * rs * r.g[e] : r.x[e];
+      rv[e] = round_to<T>(v);
+      xv[e] = to_d(rv[e]);
+    }
+    *packed = q;
+  }
+}
+
+// Weight row read by tile row t of tile `tile`. EPI_SWIGLU interleaves units:
+// even tile rows are gate rows, odd tile rows the matching up rows.
+template <int EPI>
+__device__ __forceinline__ int tile_row(int tile, int t, int N, bool& ok) {
+  if constexpr (EPI == EPI_SWIGLU) {
+    const int u = tile * 8 + (t >> 1);
+    ok = u < N;
+    return (t & 1) ? N + u : u;
+  } else {
+    const int r = tile * 16 + t;
+    ok = r < N;
+    return r;
+  }
+}
+
+__device__ __forceinline__ int n_tiles_of(int epi, int N) {
+  return epi == EPI_SWIGLU ? (N + 7) / 8 : (N + 15) / 16;
+}
+
+__device__ __forceinline__ bool arg_better(double v, int i, double bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+__device__ __forceinline__ double shfl_xor_d(double v, int m) {
+  return __hiloint2double(__shfl_xor(__double2hiint(v), m), __shfl_xor(__double2loint(v), m));
+}
+
+// RMSNorm scale 1/sqrt(mean(x^2) + eps) of column col from the producer's
+// per-tile sums of squares; every thread of the workgroup gets the same value.
+// Threads [0, nthr) split the tiles; fixed-order reduction through `red`.
+template <bool C>
+__device__ __forceinline__ double rms_scale(const GemmArgs& a, int col, double* red, int nthr) {
+  const int t = tid();
+  double s = 0.0;
+  for (int i = t; i < a.n_ssq; i += nthr) s += ld_f64<C>(a.ssq + (size_t)i * a.B + col);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += shfl_xor_d(s, off);
+  if ((t & 63) == 0) red[t >> 6] = s;
+  __syncthreads();
+  double tot = 0.0;
+  for (int w = 0; w < nthr / 64; ++w) tot += red[w];
+  __syncthreads();  // `red` may be reused right after
+  return 1.0 / sqrt(tot / (double)a.K + a.eps);
+}
+
+// ---- epilogue: tile rows 4g..4g+3 of column col, values v -----------------
+
+// rpre (EPI_RESID, optional): the residual values of these rows, already loaded.
+template <typename T, int EPI, bool C>
+__device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int g, int col,
+                                         const double* v, const double* rpre = nullptr) {
+  const bool cok = col < a.B;
+  if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile * 16 + 4 * g + i;
+      if (cok && row < a.N) st_f64<C>(a.out64 + (size_t)col * a.ldo + row, v[i]);
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile * 16 + 4 * g + i;
+      if (cok && row < a.N) {
+        double* p = a.resid + (size_t)col * a.ldr + row;
+        const double xn = (rpre != nullptr ? rpre[i] : ld_f64<C>(p)) + v[i];
+        st_f64<C>(p, xn);
+        ss += xn * xn;
+      }
+    }
+    // the 4 lanes of this column (g = 0..3) combine in a fixed order
+    ss += shfl_xor_d(ss, 16);
+    ss += shfl_xor_d(ss, 32);
+    if (g == 0 && cok) st_f64<C>(a.ssq_out + (size_t)tile * a.B + col, ss);
+  } else if constexpr (EPI == EPI_QKV) {
+    const int row0 = tile * 16 + 4 * g;  // 16-row tiles never straddle a part or a head
+    const int part = row0 / a.dq;
+    const int din = row0 - part * a.dq;
+    const int head = din / a.hd;
+    const int d0 = din - head * a.hd;
+    double vals[4] = {v[0], v[1], v[2], v[3]};
+    if (!cok || row0 >= a.N) return;
+    if (a.inv_freq != nullptr && part < 2) {
+      const double p = (double)ldg(a.pos + col);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const double ang = p * ldg(a.inv_freq + (d0 >> 1) + j);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const double x0 = vals[2 * j], x1 = vals[2 * j + 1];
+        vals[2 * j] = x0 * cs - x1 * sn;
+        vals[2 * j + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    if (part == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_f64<C>(a.q_out + (size_t)col * a.dq + din + i, vals[i]);
+    } else if (ldg(a.live + col)) {
+      const int widx = a.pos ? (int)(ldg(a.pos + col) % a.cap) : a.scalar_widx;
+      T* dst = (T*)(part == 1 ? a.ring_k : a.ring_v) + (size_t)col * a.slot_stride + a.layer_off +
+               (size_t)head * a.head_stride + (size_t)widx * a.hd + d0;
+      store_rounded<T, C>(dst, vals, 4);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    double r[2];
+    int n = 0;
+    const int u0 = tile * 8 + 2 * g;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int u = u0 + j;
+      if (cok && u < a.N) {
+        const double gt = v[2 * j], up = v[2 * j + 1];
+        r[j] = gt / (1.0 + exp(-gt)) * up;
+        n = j + 1;
+      }
+    }
+    if (n > 0) store_rounded<T, C>((T*)a.act + (size_t)col * a.lda + u0, r, n);
+  } else if constexpr (EPI == EPI_ARGMAX) {
+    // NaN never wins: it compares as -inf; rows past N carry index INT_MAX.
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = tile * 16 + 4 * g + i;
+      if (row < a.N) {
+        if (cok) *(MOSHI_GLB float*)(a.logits + (size_t)col * a.ldo + row) = (float)v[i];  // host reads
+        const double val = (v[i] != v[i]) ? -INFINITY : v[i];
+        if (bi == 0x7fffffff || val > bv) {
+          bv = val;
+          bi = row;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+      const double ov = shfl_xor_d(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (arg_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (g == 0 && cok) {
+      const uint64_t vb = __builtin_bit_cast(uint64_t, bv);
+      st_grp<C>(a.apart + (size_t)tile * a.B + col,
+                u32x4{(unsigned)vb, (unsigned)(vb >> 32), (unsigned)bi, 0u});
+    }
+  }
+}
+
+__device__ __forceinline__ ArgPart unpack_part(u32x4 w) {
+  ArgPart p;
+  p.v = __builtin_bit_cast(double, (uint64_t)w[0] | ((uint64_t)w[1] << 32));
+  p.i = (int)w[2];
+  p.pad = 0;
+  return p;
+}
+
+// Epilogue of the R consecutive rows tile*16 + w*R .. that one wave owns
+// (one session, column 0), run by lane 0 with the finished sums v[0..R).
+// EPI_RESID writes one sum-of-squares partial per R rows (index row0 / R).
+// rpre: EPI_RESID residual values of these rows, already loaded (or null).
+template <typename T, int EPI, bool C, int R>
+__device__ __forceinline__ void wave_epilogue(const GemmArgs& a, int tile, int w, const double* v,
+                                              const double* rpre) {
+  static_assert(EPI != EPI_ARGMAX, "argmax partials are per tile");
+  if constexpr (EPI == EPI_STORE) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = tile * 16 + w * R + r;
+      if (row < a.N) st_f64<C>(a.out64 + row, v[r]);
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    const int row0 = tile * 16 + w * R;
+    if (row0 >= a.N) return;
+    double ss = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int row = row0 + r;
+      if (row < a.N) {
+        double* p = a.resid + row;
+        const double xn = (rpre != nullptr ? rpre[r] : ld_f64<C>(p)) + v[r];
+        st_f64<C>(p, xn);
+        ss += xn * xn;
+      }
+    }
+    st_f64<C>(a.ssq_out + row0 / R, ss);
+  } else if constexpr (EPI == EPI_QKV) {
+    const int row0 = tile * 16 + w * R;  // R-row groups never straddle a part or a head
+    if (row0 >= a.N) return;
+    const int part = row0 / a.dq;
+    const int din = row0 - part * a.dq;
+    const int head = din / a.hd;
+    const int d0 = din - head * a.hd;
+    double vals[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) vals[r] = v[r];
+    if (a.inv_freq != nullptr && part < 2) {
+      const double p = (double)ldg(a.pos);
+#pragma unroll
+      for (int j = 0; j < R / 2; ++j) {
+        const double ang = p * ldg(a.inv_freq + (d0 >> 1) + j);
+        double sn, cs;
+        sincos(ang, &sn, &cs);
+        const double x0 = vals[2 * j], x1 = vals[2 * j + 1];
+        vals[2 * j] = x0 * cs - x1 * sn;
+        vals[2 * j + 1] = x0 * sn + x1 * cs;
+      }
+    }
+    if (part == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) st_f64<C>(a.q_out + din + r, vals[r]);
+    } else if (ldg(a.live)) {
+      const int widx = a.pos ? (int)(ldg(a.pos) % a.cap) : a.scalar_widx;
+      T* dst = (T*)(part == 1 ? a.ring_k : a.ring_v) + a.layer_off + (size_t)head * a.head_stride +
+               (size_t)widx * a.hd + d0;
+      store_rounded<T, C>(dst, vals, R);
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // rows alternate gate / up of units tile*8 + w*R/2 + k
+    constexpr int NU = R / 2;
+    const int u0 = tile * 8 + w * NU;
+    double r_[NU];
+    int n = 0;
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      if (u0 + k < a.N) {
+        const double gt = v[2 * k], up = v[2 * k + 1];
+        r_[k] = gt / (1.0 + exp(-gt)) * up;
+        n = k + 1;
+      }
+    }
+    if (n > 0) store_rounded<T, C>((T*)a.act + u0, r_, n);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// One session: fp64 VALU GEMV over row tiles
+// ---------------------------------------------------------------------------
+
+// Workgroup `wg` of `nwg` (KW waves) walks row tiles wg, wg+nwg, ... (16
+// output rows each); wave w owns rows w*R .. w*R+R-1 (R = 16/KW) of a tile
+// over the whole of K. The rounded input vector is built once per workgroup in
+// LDS `xs` (model dtype, K elements). Lane l covers the 16-byte groups l,
+// l+64, ... of a row, so a wave reads each row in contiguous 1 KB pieces.
+// Weights stream in batches of U groups per lane and row, double-buffered: the
+// next batch (possibly of the next tile) is requested before the current one
+// is used. Each finished row is reduced over the 64 lanes by a butterfly;
+// wave 0 applies the epilogue to the tile's 16 rows. Every thread of the
+// workgroup must call this (it synchronises the workgroup).
+// One batch of weights for wave `wave`: U groups (lanes l, l+64, ...) of each
+// of its R rows of tile `tile`, batch `bt` along K. Every lane loads: rows
+// past the matrix read row 0 and groups past K read the row's last group
+// (their sums are never used, and the consumer skips groups past K). No
+// conditional zero-fill: writing a load's destination register twice would
+// make the compiler wait for every load in flight.
+// With live = false every lane reads the matrix's first group instead (one
+// line, a placeholder that keeps the number of loads in flight the same on
+// every path, so the compiler's wait counts stay exact).
+template <typename T, int EPI, int U, int R>
+__device__ __forceinline__ void load_wbatch(const GemmArgs& a, int tile, int bt, int lane, int wave,
+                                            u32x4 (&w)[U][R], bool live = true) {
+  constexpr int VEC = VecOf<T>::N;
+  const int ngroups = a.K / VEC;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    bool ok;
+    const int rr = tile_row<EPI>(tile, wave * R + r, a.N, ok);
+    const T* wr = (const T*)a.W + (size_t)(ok ? rr : 0) * a.K;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int gi = bt * U * 64 + u * 64 + lane;
+      const T* p = wr + (size_t)(gi < ngroups ? gi : ngroups - 1) * VEC;
+      w[u][r] = ld16_stream(live ? p : (const T*)a.W);
+    }
+  }
+}
+
+template <int KW, int U_>
+struct GemvShape {
+  static constexpr int R = 16 / KW;  // rows per wave
+  static constexpr int U = U_ > 0 ? U_ : ((R <= 2) ? 8 : 4);  // groups per lane and row per batch
+};
+
+// The first weight batch of workgroup `wg` for the projection `a`, requested
+// ahead of time (before the grid barrier that precedes it) by every wave but
+// wave 0, which polls the barrier and so must not wait on these loads.
+template <typename T, int KW, int EPI, int U_>
+__device__ __forceinline__ void gemv_prefetch(const GemmArgs& a, int wg,
+                                              u32x4 (&w)[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R]) {
+  constexpr int R = GemvShape<KW, U_>::R, U = GemvShape<KW, U_>::U;
+  const int t = tid();
+  const int wave = t >> 6;
+  if (wave != 0) load_wbatch<T, EPI, U, R>(a, wg, 0, t & 63, wave, w, wg < n_tiles_of(EPI, a.N));
+}
+
+// Workgroup `wg` of `nwg` (KW waves) walks row tiles wg, wg+nwg, ... (16
+// output rows each); wave w owns rows w*R .. w*R+R-1 (R = 16/KW) of a tile
+// over the whole of K. The rounded input vector is built once per workgroup in
+// LDS `xs` (model dtype, K elements). Lane l covers the 16-byte groups l,
+// l+64, ... of a row, so a wave reads each row in contiguous 1 KB pieces.
+// Weights stream in batches of U groups per lane and row, double-buffered: the
+// next batch (possibly of the next tile) is requested before the current one
+// is used. Each finished row is reduced over the 64 lanes by a butterfly;
+// wave 0 applies the epilogue to the tile's 16 rows. PRE: waves 1.. already
+// hold their first batch in `pre` (gemv_prefetch). The first group of the
+// input and (EPI_RESID) the residual rows of the first tile are requested
+// before the norm scale is computed. Every thread of the workgroup must call
+// this (it synchronises the workgroup).
+template <typename T, int KW, int PRO, int EPI, bool C, int U_, bool PRE>
+__device__ __forceinline__ void gemv_core(
+    const GemmArgs& a, int wg, int nwg, T* xs,
+    const u32x4 (&pre)[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R]) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int R = GemvShape<KW, U_>::R;
+  constexpr int U = GemvShape<KW, U_>::U;
+  constexpr int NTH = 64 * KW;
+  const int t = tid();
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  __shared__ double s_red[2][16];
+  __shared__ double s_tmp[KW];
+
+  const int ntiles = n_tiles_of(EPI, a.N);
+  const int ngroups = a.K / VEC;  // K is a multiple of VEC
+  const int nbatch = (ngroups + U * 64 - 1) / (U * 64);
+
+  int tile = wg;
+  u32x4 wa[U][R], wb[U][R];
+  if (PRE && wave != 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int r = 0; r < R; ++r) wa[u][r] = pre[u][r];
+  } else {
+    // in flight while the input is built
+    load_wbatch<T, EPI, U, R>(a, tile, 0, lane, wave, wa, tile < ntiles);
+  }
+  // residual rows of the first tile (lane 0 of each wave holds its R rows)
+  double rpre[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) rpre[r] = 0.0;
+  if constexpr (EPI == EPI_RESID) {
+    if (tile < ntiles && lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        const int row = tile * 16 + wave * R + r;
+        if (row < a.N) rpre[r] = ld_f64<C>(a.resid + row);
+      }
+    }
+  }
+  // input vector -> LDS (rounded to the model dtype); the first group's raw
+  // values are requested before the norm scale
+  XRaw<T, PRO, C> x0;
+  if (t < ngroups) load_x_raw<T, PRO, C>(a, 0, t * VEC, x0);
+  double rs = 1.0;
+  if constexpr (PRO == PRO_NORM) rs = rms_scale<C>(a, 0, s_tmp, NTH);
+  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && wg == 0;
+  for (int gi = t; gi < ngroups; gi += NTH) {
+    double xv[VEC];
+    u32x4 packed;
+    if (gi == t) {
+      finish_x<T, PRO, C>(x0, rs, xv, &packed);
+    } else {
+      XRaw<T, PRO, C> xr;
+      load_x_raw<T, PRO, C>(a, 0, gi * VEC, xr);
+      finish_x<T, PRO, C>(xr, rs, xv, &packed);
+    }
+    *(u32x4*)(xs + (size_t)gi * VEC) = packed;
+    if (write_xn) st_grp<C>((T*)a.xn_out + (size_t)gi * VEC, packed);
+  }
+  __syncthreads();
+  if (tile < ntiles) {
+    double acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0;
+    int bt = 0, parity = 0;
+
+    // consume batch (tile, bt) held in w; finish the tile after its last batch
+    auto consume = [&](const u32x4 (&w)[U][R]) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int gi = bt * U * 64 + u * 64 + lane;
+        if (gi < ngroups) {
+          double xv[VEC];
+          widen<T>(*(const u32x4*)(xs + (size_t)gi * VEC), xv);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            double wd[VEC];
+            widen<T>(w[u][r], wd);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
+          }
+        }
+      }
+      if (bt == nbatch - 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+#pragma unroll
+          for (int off = 32; off > 0; off >>= 1) acc[r] += shfl_xor_d(acc[r], off);
+        }
+        if constexpr (EPI == EPI_ARGMAX) {
+          // per-tile (max, index) partial: wave 0 combines the tile's 16 rows
+          if (lane == 0) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) s_red[parity][wave * R + r] = acc[r];
+          }
+          __syncthreads();
+          if (wave == 0 && (lane & 15) == 0) {
+            // g = lane / 16 holds rows 4g..4g+3 of column 0
+            const int g = lane >> 4;
+            const double v[4] = {s_red[parity][4 * g], s_red[parity][4 * g + 1],
+                                 s_red[parity][4 * g + 2], s_red[parity][4 * g + 3]};
+            epilogue<T, EPI, C>(a, tile, g, 0, v);
+          }
+          parity ^= 1;
+        } else {
+          // every wave finishes its own rows: no workgroup barrier per tile
+          if (lane == 0) wave_epilogue<T, EPI, C, R>(a, tile, wave, acc, tile == wg ? rpre : nullptr);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0;
+      }
+    };
+    // the batch after (tile, bt)
+    auto advance = [&](int& tt, int& b) {
+      if (++b == nbatch) {
+        b = 0;
+        tt += nwg;
+      }
+    };
+
+    // the next batch is always requested (a placeholder past the last one)
+    for (;;) {
+      int nt = tile, nb = bt;
+      advance(nt, nb);
+      load_wbatch<T, EPI, U, R>(a, nt, nb, lane, wave, wb, nt < ntiles);
+      consume(wa);
+      if (nt >= ntiles) break;
+      tile = nt;
+      bt = nb;
+      advance(nt, nb);
+      load_wbatch<T, EPI, U, R>(a, nt, nb, lane, wave, wa, nt < ntiles);
+      consume(wb);
+      if (nt >= ntiles) break;
+      tile = nt;
+      bt = nb;
+    }
+  }
+  __syncthreads();  // xs and s_red may be reused by the caller
+}
+
+// Without a prefetched first batch.
+template <typename T, int KW, int PRO, int EPI, bool C, int U_ = 0>
+__device__ __forceinline__ void gemv_body(const GemmArgs& a, int wg, int nwg, T* xs) {
+  u32x4 none[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R];
+  gemv_core<T, KW, PRO, EPI, C, U_, false>(a, wg, nwg, xs, none);
+}
+
+// ---------------------------------------------------------------------------
+// Sliding-window decode attention over a ring of K/V
+// ---------------------------------------------------------------------------
+
+// Keys of slot b visible at its current position: ring slots [0, nvalid),
+// minus `excl` (the oldest key, under the mask-oldest reading).
+__device__ __forceinline__ void window_of(const AttnArgs& a, int b, int& nvalid, int& excl) {
+  excl = -1;
+  if (a.pos != nullptr) {
+    const int64_t p = ldg(a.pos + b);
+    nvalid = (int)(p + 1 < (int64_t)a.cap ? p + 1 : (int64_t)a.cap);
+    if (a.mask_oldest && p >= (int64_t)a.cap - 1) excl = (int)((p + 1) % a.cap);
+  } else {
+    nvalid = a.scalar_nvalid;
+  }
+}
+
+// Which ring rows were written during the running kernel (see C):
+enum KvFresh { KV_NONE = 0, KV_NEWEST = 1, KV_ALL = 2 };
+
+// K and V of one 64-key chunk as held by one thread: PASSES keys, one
+// 16-byte group of each.
+template <typename T, int HD, int NT>
+struct AttnShape {
+  static constexpr int VEC = VecOf<T>::N;
+  static constexpr int TK = HD / VEC;   // threads per key (one 16-byte group each)
+  static constexpr int KP = NT / TK;    // keys per pass
+  static constexpr int PASSES = ATTN_CHUNK / KP;
+  static_assert(TK <= 64 && (64 % TK) == 0 && PASSES >= 1 && ATTN_CHUNK % KP == 0,
+                "head dim / chunk layout");
+};
+template <typename T, int HD, int NT>
+struct KvChunk {
+  u32x4 k[AttnShape<T, HD, NT>::PASSES], v[AttnShape<T, HD, NT>::PASSES];
+};
+
+// Requests the K and V groups of `chunk` (zeros past nvalid). Rows written
+// during the running kernel (FRESH) are read coherently.
+template <typename T, int HD, int NT, int FRESH>
+__device__ __forceinline__ void attn_load(const AttnArgs& a, int chunk, int h, int b, int nvalid,
+                                          int newest, KvChunk<T, HD, NT>& kv) {
+  using S = AttnShape<T, HD, NT>;
+  const int t = tid();
+  const int kd = t % S::TK, kk = t / S::TK;
+  const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
+  const T* kbase = (const T*)a.ring_k + base;
+  const T* vbase = (const T*)a.ring_v + base;
+#pragma unroll
+  for (int ps = 0; ps < S::PASSES; ++ps) {
+    // keys past nvalid read key 0 (always written; masked out by the scores
+    // and multiplied by p = 0), so every lane loads unconditionally
+    const int j0 = chunk * ATTN_CHUNK + ps * S::KP + kk;
+    const int j = j0 < nvalid ? j0 : 0;
+    const T* kp = kbase + (size_t)j * HD + kd * S::VEC;
+    const T* vp = vbase + (size_t)j * HD + kd * S::VEC;
+    if (FRESH == KV_ALL || (FRESH == KV_NEWEST && j == newest)) {
+      kv.k[ps] = ld_grp<true>(kp);
+      kv.v[ps] = ld_grp<true>(vp);
+    } else {
+      kv.k[ps] = ld16(kp);
+      kv.v[ps] = ld16(vp);
+    }
+  }
+}
+
+// The query slice of this thread (VEC values of head h).
+template <typename T, int HD, int NT, bool C>
+__device__ __forceinline__ void attn_query(const AttnArgs& a, int h, int b, double* qv) {
+  using S = AttnShape<T, HD, NT>;
+  const int kd = tid() % S::TK;
+  const double* qp = a.q + (size_t)b * a.ldq + h * HD + kd * S::VEC;
+#pragma unroll
+  for (int e = 0; e < S::VEC; ++e) qv[e] = ld_f64<C>(qp + e);
+}
+
+// Scores, softmax and p.V of one loaded chunk in fp64. A single chunk writes
+// the rounded output directly; otherwise the (max, sum, p.V) partials go to
+// a.part. s_o: LDS [KP][HD+1] doubles. Every thread of the workgroup calls it.
+template <typename T, int HD, int NT, bool C>
+__device__ __forceinline__ void attn_compute(const AttnArgs& a, int chunk, int h, int b,
+                                             int nvalid, int excl, const double* qv,
+                                             const KvChunk<T, HD, NT>& kv, double* s_o) {
+  using S = AttnShape<T, HD, NT>;
+  constexpr int VEC = S::VEC, TK = S::TK, KP = S::KP, PASSES = S::PASSES;
+  constexpr int CH = ATTN_CHUNK;
+  constexpr int LD = HD + 1;
+  __shared__ double s_p[CH];
+  __shared__ double s_ml[2];
+  const int t = tid();
+  const int nchunks = (nvalid + CH - 1) / CH;
+  const int kd = t % TK, kk = t / TK;
+  const double scale = 1.0 / sqrt((double)HD);
+
+  // scores s_j = q.k_j / sqrt(HD)
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const int j = chunk * CH + ps * KP + kk;
+    const bool ok = j < nvalid && j != excl;
+    double kd_[VEC];
+    widen<T>(kv.k[ps], kd_);
+    double d = 0.0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) d = fma(qv[e], kd_[e], d);
+#pragma unroll
+    for (int off = TK / 2; off > 0; off >>= 1) d += shfl_xor_d(d, off);
+    if (kd == 0) s_p[ps * KP + kk] = ok ? d * scale : -INFINITY;
+  }
+  __syncthreads();
+  if (t < 64) {
+    const double sv = (t < CH) ? s_p[t] : -INFINITY;
+    double m = sv;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) m = fmax(m, shfl_xor_d(m, off));
+    const double pj = (m == -INFINITY || sv == -INFINITY) ? 0.0 : exp(sv - m);
+    double l = pj;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) l += shfl_xor_d(l, off);
+    if (t < CH) s_p[t] = pj;
+    if (t == 0) {
+      s_ml[0] = m;
+      s_ml[1] = l;
+    }
+  }
+  __syncthreads();
+
+  // p . V
+  double acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+#pragma unroll
+  for (int ps = 0; ps < PASSES; ++ps) {
+    const double pj = s_p[ps * KP + kk];
+    double vd[VEC];
+    widen<T>(kv.v[ps], vd);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = fma(pj, vd[e], acc[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) s_o[kk * LD + kd * VEC + e] = acc[e];
+  __syncthreads();
+  if (t < HD) {
+    double od = 0.0;
+    for (int r = 0; r < KP; ++r) od += s_o[r * LD + t];
+    if (nchunks == 1) {
+      const double l = s_ml[1];
+      const double ov = l > 0.0 ? od / l : 0.0;
+      store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov, 1);
+    } else {
+      double* mypart = a.part + (((size_t)b * a.n_heads + h) * a.max_chunks + chunk) * (HD + 2);
+      st_f64<C>(mypart + 2 + t, od);
+      if (t == 0) {
+        st_f64<C>(mypart, s_ml[0]);
+        st_f64<C>(mypart + 1, s_ml[1]);
+      }
+    }
+  }
+  __syncthreads();  // s_p, s_ml, s_o are reused by the next chunk
+}
+
+// One (64-key chunk, head, slot) item with NT threads.
+template <typename T, int HD, int NT, bool C, int FRESH>
+__device__ __forceinline__ void attn_item(const AttnArgs& a, int chunk, int h, int b, int nvalid,
+                                          int excl, double* s_o) {
+  int newest = -1;
+  if constexpr (FRESH == KV_NEWEST) newest = (int)(ldg(a.pos + b) % a.cap);
+  KvChunk<T, HD, NT> kv;
+  attn_load<T, HD, NT, FRESH>(a, chunk, h, b, nvalid, newest, kv);
+  double qv[AttnShape<T, HD, NT>::VEC];
+  attn_query<T, HD, NT, C>(a, h, b, qv);
+  attn_compute<T, HD, NT, C>(a, chunk, h, b, nvalid, excl, qv, kv, s_o);
+}
+
+// Chunks [c0, c1) of head h, the next chunk's K and V requested while the
+// current one is computed.
+template <typename T, int HD, int NT, bool C, int FRESH>
+__device__ __forceinline__ void attn_span(const AttnArgs& a, int c0, int c1, int h, int b,
+                                          int nvalid, int excl, double* s_o) {
+  int newest = -1;
+  if constexpr (FRESH == KV_NEWEST) newest = (int)(ldg(a.pos + b) % a.cap);
+  KvChunk<T, HD, NT> ka, kb;
+  if (c0 < c1) attn_load<T, HD, NT, FRESH>(a, c0, h, b, nvalid, newest, ka);
+  double qv[AttnShape<T, HD, NT>::VEC];
+  attn_query<T, HD, NT, C>(a, h, b, qv);
+  for (int c = c0; c < c1; c += 2) {
+    if (c + 1 < c1) attn_load<T, HD, NT, FRESH>(a, c + 1, h, b, nvalid, newest, kb);
+    attn_compute<T, HD, NT, C>(a, c, h, b, nvalid, excl, qv, ka, s_o);
+    if (c + 1 >= c1) break;
+    if (c + 2 < c1) attn_load<T, HD, NT, FRESH>(a, c + 2, h, b, nvalid, newest, ka);
+    attn_compute<T, HD, NT, C>(a, c + 1, h, b, nvalid, excl, qv, kb, s_o);
+  }
+}
+
+// Merge the chunk partials of (slot b, head h) in chunk order:
+// o = sum_c e^{m_c - M} (p.V)_c / sum_c e^{m_c - M} l_c. Threads [0, HD) work;
+// every thread of the workgroup must call this.
+template <typename T, int HD, bool C>
+__device__ __forceinline__ void combine_item(const AttnArgs& a, int h, int b, int nchunks) {
+  const int t = tid();
+  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
+  constexpr int NW = HD / 64 > 0 ? HD / 64 : 1;
+  __shared__ double s_m[NW];
+  __shared__ double s_w[ATTN_MAX_CHUNKS];
+  // M = max over the chunk maxima (exact, so any reduction order gives the same M)
+  double mloc = -INFINITY;
+  if (t < HD)
+    for (int c = t; c < nchunks; c += HD) mloc = fmax(mloc, ld_f64<C>(parts + (size_t)c * (HD + 2)));
+#pragma unroll
+  for (int off = (HD < 64 ? HD : 64) / 2; off > 0; off >>= 1)
+    mloc = fmax(mloc, shfl_xor_d(mloc, off));
+  if (t < HD && (t & 63) == 0) s_m[t >> 6] = mloc;
+  __syncthreads();
+  double M = s_m[0];
+  for (int w = 1; w < NW; ++w) M = fmax(M, s_m[w]);
+  // chunk weights e^{m_c - M}, one exp per chunk
+  if (t < HD)
+    for (int c = t; c < nchunks; c += HD) {
+      const double mc = ld_f64<C>(parts + (size_t)c * (HD + 2));
+      s_w[c] = (mc == -INFINITY) ? 0.0 : exp(mc - M);
+    }
+  __syncthreads();
+  if (t < HD) {
+    double L = 0.0, O = 0.0;
+#pragma unroll 8
+    for (int c = 0; c < nchunks; ++c) {
+      const double* pc = parts + (size_t)c * (HD + 2);
+      const double w = s_w[c];
+      L = fma(ld_f64<C>(pc + 1), w, L);
+      O = fma(ld_f64<C>(pc + 2 + t), w, O);
+    }
+    const double ov = L > 0.0 ? O / L : 0.0;
+    store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov, 1);
+  }
+  __syncthreads();
+}
+
+// The same merge as combine_item (identical arithmetic and order) by a whole
+// workgroup: the partials are first copied to LDS `s_part` ([nchunks][HD+2]
+// doubles) with every load in flight at once.
+template <typename T, int HD, int NT, bool C>
+__device__ __forceinline__ void combine_staged(const AttnArgs& a, int h, int b, int nchunks,
+                                               double* s_part) {
+  const int t = tid();
+  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
+  const int n = nchunks * (HD + 2);
+  for (int i = t; i < n; i += NT) s_part[i] = ld_f64<C>(parts + i);
+  __syncthreads();
+  constexpr int NW = HD / 64 > 0 ? HD / 64 : 1;
+  __shared__ double s_m[NW];
+  __shared__ double s_w[ATTN_MAX_CHUNKS];
+  double mloc = -INFINITY;
+  if (t < HD)
+    for (int c = t; c < nchunks; c += HD) mloc = fmax(mloc, s_part[(size_t)c * (HD + 2)]);
+#pragma unroll
+  for (int off = (HD < 64 ? HD : 64) / 2; off > 0; off >>= 1)
+    mloc = fmax(mloc, shfl_xor_d(mloc, off));
+  if (t < HD && (t & 63) == 0) s_m[t >> 6] = mloc;
+  __syncthreads();
+  double M = s_m[0];
+  for (int w = 1; w < NW; ++w) M = fmax(M, s_m[w]);
+  if (t < HD)
+    for (int c = t; c < nchunks; c += HD) {
+      const double mc = s_part[(size_t)c * (HD + 2)];
+      s_w[c] = (mc == -INFINITY) ? 0.0 : exp(mc - M);
+    }
+  __syncthreads();
+  if (t < HD) {
+    double L = 0.0, O = 0.0;
+    for (int c = 0; c < nchunks; ++c) {
+      const double* pc = s_part + (size_t)c * (HD + 2);
+      const double w = s_w[c];
+      L = fma(pc[1], w, L);
+      O = fma(pc[2 + t], w, O);
+    }
+    const double ov = L > 0.0 ? O / L : 0.0;
+    store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov, 1);
+  }
+  __syncthreads();
+}
+
+}  // namespace moshi

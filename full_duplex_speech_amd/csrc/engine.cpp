@@ -143,8 +143,19 @@ struct moshi_ctx {
   hipGraphExec_t g_temporal = nullptr, g_dep = nullptr;
   bool use_graphs = true;
 
-  // kernel timing (eager launches bracketed by events)
+  // persistent one-session step kernel (capacity 1 and an instantiated shape)
+  bool persistent = false;
+  StepArgs* d_step = nullptr;
+  unsigned* d_bar = nullptr;
+  int* d_abort = nullptr;
+  int step_grid = 0;
+  size_t step_lds = 0;
+  int step_parity = 0;
+
+  // kernel timing (eager launches bracketed by events); `dry` only records
+  // the (class, bytes) sequence of a step without launching anything
   bool timing = false;
+  bool dry = false;
   std::vector<hipEvent_t> ev;
   std::vector<int> ev_class;
   std::vector<double> ev_bytes;
@@ -184,6 +195,11 @@ hipError_t dalloc(moshi_ctx* c, void** p, size_t bytes) {
 
 template <typename F>
 hipError_t run(moshi_ctx* c, int kclass, double bytes, F&& launch) {
+  if (c->dry) {
+    c->ev_class.push_back(kclass);
+    c->ev_bytes.push_back(bytes);
+    return hipSuccess;
+  }
   if (!c->timing) return launch();
   if (c->ev_used + 2 > c->ev.size()) {
     for (int i = 0; i < 64; ++i) {
@@ -224,6 +240,157 @@ hipError_t gemm(moshi_ctx* c, int pro, int epi, const GemmArgs& a) {
   return launch_gemm(c->dtype, gemm_kw(c->dtype, a.B, a.K), pro, epi, a, c->stream);
 }
 
+// ---- argument blocks of every operation (shared by the per-operation
+// kernels and the persistent step kernel) ----
+
+// Rows per sum-of-squares partial of a residual stream, and their count.
+int ssq_rows(const moshi_ctx* c) { return c->B == 1 ? GEMV_SSQ_ROWS : 16; }
+int n_ssq(const moshi_ctx* c, int n) { return (n + ssq_rows(c) - 1) / ssq_rows(c); }
+
+EmbedArgs embed_args(const moshi_ctx* c) {
+  EmbedArgs a;
+  memset(&a, 0, sizeof(a));
+  a.tables[0] = c->emb_text;
+  for (int k = 0; k < c->S; ++k) a.tables[1 + k] = c->emb_audio[k];
+  a.frames = c->d_frames; a.live = c->d_live; a.n_ch = c->NCH; a.D = c->D; a.B = c->B;
+  a.rows_text = c->Vt + 1; a.rows_audio = c->Va + 1; a.bad_code = c->d_err;
+  a.x = c->x; a.ssq_out = c->ssq; a.ssq_rows = ssq_rows(c);
+  return a;
+}
+
+int64_t t_slot_stride(const moshi_ctx* c) { return (int64_t)c->L * c->H * c->W * c->hd; }
+int64_t t_layer_elems(const moshi_ctx* c) { return (int64_t)c->H * c->W * c->hd; }
+int64_t d_slot_stride(const moshi_ctx* c) { return (int64_t)c->Ld * c->Hd * c->S * c->hdd; }
+int64_t d_layer_elems(const moshi_ctx* c) { return (int64_t)c->Hd * c->S * c->hdd; }
+
+// RMSNorm -> q|k|v -> RoPE -> ring write
+GemmArgs t_qkv_args(const moshi_ctx* c, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->qkv[l]; a.N = 3 * c->D; a.K = c->D;
+  a.X = c->x; a.ldx = c->D; a.ssq = c->ssq; a.n_ssq = n_ssq(c, c->D); a.gain = c->attn_norm[l];
+  a.xn_out = c->B > 1 ? c->hn : nullptr;
+  a.q_out = c->q; a.dq = c->D; a.hd = c->hd; a.inv_freq = c->d_inv_freq; a.pos = c->d_pos;
+  a.ring_k = c->ring_k; a.ring_v = c->ring_v; a.slot_stride = t_slot_stride(c);
+  a.layer_off = (int64_t)l * t_layer_elems(c); a.head_stride = (int64_t)c->W * c->hd;
+  a.cap = c->W;
+  return a;
+}
+
+// window attention over the ring
+AttnArgs t_attn_args(const moshi_ctx* c, int l) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = c->q; a.ldq = c->D; a.ring_k = c->ring_k; a.ring_v = c->ring_v;
+  a.slot_stride = t_slot_stride(c); a.layer_off = (int64_t)l * t_layer_elems(c);
+  a.head_stride = (int64_t)c->W * c->hd; a.cap = c->W; a.pos = c->d_pos; a.live = c->d_live;
+  a.mask_oldest = (c->c.flags & MOSHI_FLAG_MASK_OLDEST) ? 1 : 0;
+  a.n_heads = c->H; a.max_chunks = c->max_chunks; a.part = c->attn_part;
+  a.o_out = c->o; a.ldo = c->D;
+  return a;
+}
+
+// o-projection + residual
+GemmArgs t_o_args(const moshi_ctx* c, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->wo[l]; a.N = c->D; a.K = c->D; a.X = c->o; a.ldx = c->D;
+  a.resid = c->x; a.ldr = c->D; a.ssq_out = c->ssq;
+  return a;
+}
+
+// RMSNorm -> gate|up -> SiLU(gate)*up
+GemmArgs t_gu_args(const moshi_ctx* c, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->gate_up[l]; a.N = c->F; a.K = c->D;
+  a.X = c->x; a.ldx = c->D; a.ssq = c->ssq; a.n_ssq = n_ssq(c, c->D); a.gain = c->mlp_norm[l];
+  a.xn_out = c->B > 1 ? c->hn : nullptr;
+  a.act = c->act; a.lda = c->F;
+  return a;
+}
+
+// down + residual
+GemmArgs t_dn_args(const moshi_ctx* c, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->down[l]; a.N = c->D; a.K = c->F; a.X = c->act; a.ldx = c->F;
+  a.resid = c->x; a.ldr = c->D; a.ssq_out = c->ssq;
+  return a;
+}
+
+// final norm -> hidden (kept for the depformer) -> text head logits + argmax partials
+GemmArgs t_head_args(const moshi_ctx* c) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->text_head; a.N = c->Vt; a.K = c->D;
+  a.X = c->x; a.ldx = c->D; a.ssq = c->ssq; a.n_ssq = n_ssq(c, c->D); a.gain = c->out_norm;
+  a.xn_out = c->hid;
+  a.logits = c->text_logits; a.ldo = c->Vt; a.apart = c->apart;
+  return a;
+}
+
+// y_pre[s] = W_in[s] . hidden for every substep at once
+GemmArgs d_in_args(const moshi_ctx* c) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->dep_in; a.N = c->S * c->Dd; a.K = c->D; a.X = c->hid; a.ldx = c->D;
+  a.out64 = c->pre; a.ldo = c->S * c->Dd;
+  return a;
+}
+
+GemmArgs d_qkv_args(const moshi_ctx* c, int s, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->dep_qkv[s * c->Ld + l]; a.N = 3 * c->Dd; a.K = c->Dd;
+  a.X = c->y; a.ldx = c->Dd; a.ssq = c->ssq_d; a.n_ssq = n_ssq(c, c->Dd);
+  a.gain = c->dep_attn_norm[l];
+  a.xn_out = c->B > 1 ? c->hnd : nullptr;
+  a.q_out = c->qd; a.dq = c->Dd; a.hd = c->hdd; a.inv_freq = nullptr; a.pos = nullptr;
+  a.scalar_widx = s; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v; a.slot_stride = d_slot_stride(c);
+  a.layer_off = (int64_t)l * d_layer_elems(c); a.head_stride = (int64_t)c->S * c->hdd; a.cap = c->S;
+  return a;
+}
+
+AttnArgs d_attn_args(const moshi_ctx* c, int s, int l) {
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = c->qd; a.ldq = c->Dd; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v;
+  a.slot_stride = d_slot_stride(c); a.layer_off = (int64_t)l * d_layer_elems(c);
+  a.head_stride = (int64_t)c->S * c->hdd;
+  a.cap = c->S; a.pos = nullptr; a.scalar_nvalid = s + 1; a.live = c->d_live;
+  a.n_heads = c->Hd; a.max_chunks = 1; a.part = c->attn_part;  // S <= 64: one chunk
+  a.o_out = c->od; a.ldo = c->Dd;
+  return a;
+}
+
+GemmArgs d_o_args(const moshi_ctx* c, int s, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->dep_o[s * c->Ld + l]; a.N = c->Dd; a.K = c->Dd; a.X = c->od; a.ldx = c->Dd;
+  a.resid = c->y; a.ldr = c->Dd; a.ssq_out = c->ssq_d;
+  return a;
+}
+
+GemmArgs d_gu_args(const moshi_ctx* c, int s, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->dep_gate_up[s * c->Ld + l]; a.N = c->Fd; a.K = c->Dd;
+  a.X = c->y; a.ldx = c->Dd; a.ssq = c->ssq_d; a.n_ssq = n_ssq(c, c->Dd);
+  a.gain = c->dep_mlp_norm[l];
+  a.xn_out = c->B > 1 ? c->hnd : nullptr;
+  a.act = c->actd; a.lda = c->Fd;
+  return a;
+}
+
+GemmArgs d_dn_args(const moshi_ctx* c, int s, int l) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->dep_down[s * c->Ld + l]; a.N = c->Dd; a.K = c->Fd; a.X = c->actd; a.ldx = c->Fd;
+  a.resid = c->y; a.ldr = c->Dd; a.ssq_out = c->ssq_d;
+  return a;
+}
+
+// head s on the rounded residual -> logits + argmax partials
+GemmArgs d_head_args(const moshi_ctx* c, int s) {
+  GemmArgs a = gemm_base(c);
+  a.W = c->dep_head[s]; a.N = c->Va; a.K = c->Dd; a.X = c->y; a.ldx = c->Dd;
+  a.xn_out = c->B > 1 ? c->hnd : nullptr;
+  a.logits = c->audio_logits + (size_t)s * c->Va; a.ldo = c->S * c->Va;
+  a.apart = c->apart;
+  return a;
+}
+
 // ---- the temporal step: embed, L layers, final norm + text head ----
 
 hipError_t enqueue_temporal(moshi_ctx* c) {
@@ -231,42 +398,19 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
   const double nlive = live_count(c);
   hipError_t e;
   {
-    EmbedArgs a;
-    memset(&a, 0, sizeof(a));
-    a.tables[0] = c->emb_text;
-    for (int k = 0; k < c->S; ++k) a.tables[1 + k] = c->emb_audio[k];
-    a.frames = c->d_frames; a.live = c->d_live; a.n_ch = c->NCH; a.D = D; a.B = B;
-    a.rows_text = c->Vt + 1; a.rows_audio = c->Va + 1; a.bad_code = c->d_err;
-    a.x = c->x; a.ssq_out = c->ssq;
+    EmbedArgs a = embed_args(c);
     e = run(c, KC_EMBED, nlive * c->NCH * D * es, [&] { return launch_embed(dt, a, c->stream); });
     if (e != hipSuccess) return e;
   }
-  const int nt_d = (D + 15) / 16;
-  const int64_t slot_stride = (int64_t)c->L * c->H * c->W * c->hd;
   for (int l = 0; l < c->L; ++l) {
-    {  // RMSNorm -> q|k|v -> RoPE -> ring write
-      GemmArgs a = gemm_base(c);
-      a.W = c->qkv[l]; a.N = 3 * D; a.K = D;
-      a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->attn_norm[l];
-      a.xn_out = B > 1 ? c->hn : nullptr;
-      a.q_out = c->q; a.dq = D; a.hd = c->hd; a.inv_freq = c->d_inv_freq; a.pos = c->d_pos;
-      a.ring_k = c->ring_k; a.ring_v = c->ring_v; a.slot_stride = slot_stride;
-      a.layer_off = (int64_t)l * c->H * c->W * c->hd; a.head_stride = (int64_t)c->W * c->hd;
-      a.cap = c->W;
+    {
+      GemmArgs a = t_qkv_args(c, l);
       double bytes = 3.0 * D * D * es + D * es + nlive * 2.0 * D * es;
-      e = run(c, KC_T_QKV, bytes,
-              [&] { return gemm(c, PRO_NORM, EPI_QKV, a); });
+      e = run(c, KC_T_QKV, bytes, [&] { return gemm(c, PRO_NORM, EPI_QKV, a); });
       if (e != hipSuccess) return e;
     }
-    {  // window attention over the ring
-      AttnArgs a;
-      memset(&a, 0, sizeof(a));
-      a.q = c->q; a.ldq = D; a.ring_k = c->ring_k; a.ring_v = c->ring_v;
-      a.slot_stride = slot_stride; a.layer_off = (int64_t)l * c->H * c->W * c->hd;
-      a.head_stride = (int64_t)c->W * c->hd; a.cap = c->W; a.pos = c->d_pos; a.live = c->d_live;
-      a.mask_oldest = (c->c.flags & MOSHI_FLAG_MASK_OLDEST) ? 1 : 0;
-      a.n_heads = c->H; a.max_chunks = c->max_chunks; a.part = c->attn_part;
-      a.o_out = c->o; a.ldo = D;
+    {
+      AttnArgs a = t_attn_args(c, l);
       double keys = 0;
       for (int b = 0; b < B; ++b)
         if (c->live[b]) {
@@ -283,39 +427,25 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
         if (e != hipSuccess) return e;
       }
     }
-    {  // o-projection + residual
-      GemmArgs a = gemm_base(c);
-      a.W = c->wo[l]; a.N = D; a.K = D; a.X = c->o; a.ldx = D;
-      a.resid = c->x; a.ldr = D; a.ssq_out = c->ssq;
-      e = run(c, KC_T_O, (double)D * D * es,
-              [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
+    {
+      GemmArgs a = t_o_args(c, l);
+      e = run(c, KC_T_O, (double)D * D * es, [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
       if (e != hipSuccess) return e;
     }
-    {  // RMSNorm -> gate|up -> SiLU(gate)*up
-      GemmArgs a = gemm_base(c);
-      a.W = c->gate_up[l]; a.N = F; a.K = D;
-      a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->mlp_norm[l];
-      a.xn_out = B > 1 ? c->hn : nullptr;
-      a.act = c->act; a.lda = F;
+    {
+      GemmArgs a = t_gu_args(c, l);
       e = run(c, KC_T_GATEUP, 2.0 * F * D * es + D * es,
               [&] { return gemm(c, PRO_NORM, EPI_SWIGLU, a); });
       if (e != hipSuccess) return e;
     }
-    {  // down + residual
-      GemmArgs a = gemm_base(c);
-      a.W = c->down[l]; a.N = D; a.K = F; a.X = c->act; a.ldx = F;
-      a.resid = c->x; a.ldr = D; a.ssq_out = c->ssq;
-      e = run(c, KC_T_DOWN, (double)D * F * es,
-              [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
+    {
+      GemmArgs a = t_dn_args(c, l);
+      e = run(c, KC_T_DOWN, (double)D * F * es, [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
       if (e != hipSuccess) return e;
     }
   }
-  {  // final norm -> hidden (kept for the depformer) -> text head -> greedy token
-    GemmArgs a = gemm_base(c);
-    a.W = c->text_head; a.N = c->Vt; a.K = D;
-    a.X = c->x; a.ldx = D; a.ssq = c->ssq; a.n_ssq = nt_d; a.gain = c->out_norm;
-    a.xn_out = c->hid;
-    a.logits = c->text_logits; a.ldo = c->Vt; a.apart = c->apart;
+  {
+    GemmArgs a = t_head_args(c);
     e = run(c, KC_T_HEAD, (double)c->Vt * D * es + D * es,
             [&] { return gemm(c, PRO_NORM, EPI_ARGMAX, a); });
     if (e != hipSuccess) return e;
@@ -324,7 +454,7 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
     });
     if (e != hipSuccess) return e;
   }
-  return launch_advance(c->d_pos, c->d_live, B, c->stream);
+  return c->dry ? hipSuccess : launch_advance(c->d_pos, c->d_live, B, c->stream);
 }
 
 // ---- the depformer: all substep input projections, then 16 substeps ----
@@ -333,16 +463,12 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
   const int dt = c->dtype, B = c->B, D = c->D, Dd = c->Dd, Fd = c->Fd, S = c->S, es = c->esz;
   const double nlive = live_count(c);
   hipError_t e;
-  {  // y_pre[s] = W_in[s] . hidden for every substep at once
-    GemmArgs a = gemm_base(c);
-    a.W = c->dep_in; a.N = S * Dd; a.K = D; a.X = c->hid; a.ldx = D;
-    a.out64 = c->pre; a.ldo = S * Dd;
+  {
+    GemmArgs a = d_in_args(c);
     e = run(c, KC_D_INPROJ, (double)S * Dd * D * es,
             [&] { return gemm(c, PRO_DIRECT, EPI_STORE, a); });
     if (e != hipSuccess) return e;
   }
-  const int nt_dd = (Dd + 15) / 16;
-  const int64_t slot_stride = (int64_t)c->Ld * c->Hd * S * c->hdd;
   for (int s = 0; s < S; ++s) {
     {  // entry: y = pre[s] + E_s[previous token]; for s >= 1 the previous
        // head's partials are reduced here and code s-1 is stored
@@ -352,71 +478,43 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
       a.prev = s == 0 ? c->tokens : c->codes + (s - 1); a.prev_stride = s == 0 ? 1 : S;
       a.prev_part = s == 0 ? nullptr : c->apart; a.prev_tiles = (c->Va + 15) / 16;
       a.prev_n = c->Va; a.D = Dd; a.B = B; a.y = c->y; a.ssq_out = c->ssq_d;
+      a.ssq_rows = ssq_rows(c);
       e = run(c, KC_D_ENTRY, nlive * Dd * es, [&] { return launch_entry(dt, a, c->stream); });
       if (e != hipSuccess) return e;
     }
     for (int l = 0; l < c->Ld; ++l) {
-      const int wi = s * c->Ld + l;
-      const int64_t layer_off = (int64_t)l * c->Hd * S * c->hdd;
       {
-        GemmArgs a = gemm_base(c);
-        a.W = c->dep_qkv[wi]; a.N = 3 * Dd; a.K = Dd;
-        a.X = c->y; a.ldx = Dd; a.ssq = c->ssq_d; a.n_ssq = nt_dd; a.gain = c->dep_attn_norm[l];
-        a.xn_out = B > 1 ? c->hnd : nullptr;
-        a.q_out = c->qd; a.dq = Dd; a.hd = c->hdd; a.inv_freq = nullptr; a.pos = nullptr;
-        a.scalar_widx = s; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v; a.slot_stride = slot_stride;
-        a.layer_off = layer_off; a.head_stride = (int64_t)S * c->hdd; a.cap = S;
+        GemmArgs a = d_qkv_args(c, s, l);
         e = run(c, KC_D_QKV, 3.0 * Dd * Dd * es + Dd * es + nlive * 2.0 * Dd * es,
                 [&] { return gemm(c, PRO_NORM, EPI_QKV, a); });
         if (e != hipSuccess) return e;
       }
       {
-        AttnArgs a;
-        memset(&a, 0, sizeof(a));
-        a.q = c->qd; a.ldq = Dd; a.ring_k = c->dkv_k; a.ring_v = c->dkv_v;
-        a.slot_stride = slot_stride; a.layer_off = layer_off; a.head_stride = (int64_t)S * c->hdd;
-        a.cap = S; a.pos = nullptr; a.scalar_nvalid = s + 1; a.live = c->d_live;
-        a.n_heads = c->Hd; a.max_chunks = 1; a.part = c->attn_part;  // S <= 64: one chunk
-        a.o_out = c->od; a.ldo = Dd;
+        AttnArgs a = d_attn_args(c, s, l);
         e = run(c, KC_D_ATTN, nlive * (s + 1) * 2.0 * Dd * es,
                 [&] { return launch_attn(dt, c->hdd, a, B, c->stream); });
         if (e != hipSuccess) return e;
       }
       {
-        GemmArgs a = gemm_base(c);
-        a.W = c->dep_o[wi]; a.N = Dd; a.K = Dd; a.X = c->od; a.ldx = Dd;
-        a.resid = c->y; a.ldr = Dd; a.ssq_out = c->ssq_d;
-        e = run(c, KC_D_O, (double)Dd * Dd * es,
-                [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
+        GemmArgs a = d_o_args(c, s, l);
+        e = run(c, KC_D_O, (double)Dd * Dd * es, [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
         if (e != hipSuccess) return e;
       }
       {
-        GemmArgs a = gemm_base(c);
-        a.W = c->dep_gate_up[wi]; a.N = Fd; a.K = Dd;
-        a.X = c->y; a.ldx = Dd; a.ssq = c->ssq_d; a.n_ssq = nt_dd; a.gain = c->dep_mlp_norm[l];
-        a.xn_out = B > 1 ? c->hnd : nullptr;
-        a.act = c->actd; a.lda = Fd;
+        GemmArgs a = d_gu_args(c, s, l);
         e = run(c, KC_D_GATEUP, 2.0 * Fd * Dd * es + Dd * es,
                 [&] { return gemm(c, PRO_NORM, EPI_SWIGLU, a); });
         if (e != hipSuccess) return e;
       }
       {
-        GemmArgs a = gemm_base(c);
-        a.W = c->dep_down[wi]; a.N = Dd; a.K = Fd; a.X = c->actd; a.ldx = Fd;
-        a.resid = c->y; a.ldr = Dd; a.ssq_out = c->ssq_d;
-        e = run(c, KC_D_DOWN, (double)Dd * Fd * es,
-                [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
+        GemmArgs a = d_dn_args(c, s, l);
+        e = run(c, KC_D_DOWN, (double)Dd * Fd * es, [&] { return gemm(c, PRO_DIRECT, EPI_RESID, a); });
         if (e != hipSuccess) return e;
       }
     }
-    {  // head s on the rounded residual -> code s
-      GemmArgs a = gemm_base(c);
-      a.W = c->dep_head[s]; a.N = c->Va; a.K = Dd; a.X = c->y; a.ldx = Dd;
-      a.xn_out = B > 1 ? c->hnd : nullptr;
-      a.logits = c->audio_logits + (size_t)s * c->Va; a.ldo = S * c->Va;
-      a.apart = c->apart;
-      e = run(c, KC_D_HEAD, (double)c->Va * Dd * es,
-              [&] { return gemm(c, PRO_CAST, EPI_ARGMAX, a); });
+    {
+      GemmArgs a = d_head_args(c, s);
+      e = run(c, KC_D_HEAD, (double)c->Va * Dd * es, [&] { return gemm(c, PRO_CAST, EPI_ARGMAX, a); });
       if (e != hipSuccess) return e;
     }
   }
@@ -425,6 +523,108 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
     return launch_argmax_reduce(c->apart, (c->Va + 15) / 16, c->Va, B, c->codes + (S - 1), S,
                                 c->stream);
   });
+}
+
+// ---- the persistent step kernel (one session) ----
+
+// Builds the kernel's argument block and weight-pointer tables in device
+// memory. Leaves c->persistent false when the shape or device does not allow
+// it (the per-operation kernels are used then).
+int setup_step(moshi_ctx* c) {
+  const char* env = getenv("MOSHI_STEP_KERNEL");
+  if (c->B != 1 || (env && env[0] == '0') || !step_supported(c->dtype, c->hd, c->hdd))
+    return MOSHI_OK;
+  const size_t es = c->esz, vec = es == 2 ? 8 : 4;
+  auto attn_lds = [&](int hd) { return (STEP_THREADS / (hd / vec)) * (size_t)(hd + 1) * 8; };
+  size_t kmax = c->D;
+  for (int k : {c->F, c->Dd, c->Fd}) kmax = (size_t)k > kmax ? (size_t)k : kmax;
+  size_t lds = kmax * es;
+  lds = attn_lds(c->hd) > lds ? attn_lds(c->hd) : lds;
+  lds = attn_lds(c->hdd) > lds ? attn_lds(c->hdd) : lds;
+  // a head's chunk partials, merged in LDS
+  const size_t merge = (size_t)c->max_chunks * (c->hd + 2) * 8;
+  if (merge > 96 * 1024) return MOSHI_OK;  // window too long for the merge in LDS
+  lds = merge > lds ? merge : lds;
+  const int grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);
+  if (grid < 1) return MOSHI_OK;
+
+  std::vector<const void*> tab;
+  const size_t o_tw = tab.size();
+  for (int l = 0; l < c->L; ++l)
+    for (const void* p : {c->attn_norm[l], c->qkv[l], c->wo[l], c->mlp_norm[l], c->gate_up[l],
+                          c->down[l]})
+      tab.push_back(p);
+  const size_t o_dw = tab.size();
+  for (int s = 0; s < c->S; ++s)
+    for (int l = 0; l < c->Ld; ++l) {
+      const int wi = s * c->Ld + l;
+      for (const void* p : {c->dep_qkv[wi], c->dep_o[wi], c->dep_gate_up[wi], c->dep_down[wi]})
+        tab.push_back(p);
+    }
+  const size_t o_dn = tab.size();
+  for (int l = 0; l < c->Ld; ++l) {
+    tab.push_back(c->dep_attn_norm[l]);
+    tab.push_back(c->dep_mlp_norm[l]);
+  }
+  const size_t o_de = tab.size();
+  for (int s = 0; s < c->S; ++s) tab.push_back(c->dep_emb[s]);
+  const size_t o_dh = tab.size();
+  for (int s = 0; s < c->S; ++s) tab.push_back(c->dep_head[s]);
+
+  void* d_tab = nullptr;
+  CKD(c, dalloc(c, &d_tab, tab.size() * sizeof(void*)));
+  CKD(c, hipMemcpy(d_tab, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice));
+  const void* const* dt = (const void* const*)d_tab;
+
+  StepArgs A;
+  memset(&A, 0, sizeof(A));
+  A.emb = embed_args(c);
+  A.t_qkv = t_qkv_args(c, 0); A.t_o = t_o_args(c, 0); A.t_gu = t_gu_args(c, 0);
+  A.t_dn = t_dn_args(c, 0); A.t_head = t_head_args(c); A.t_attn = t_attn_args(c, 0);
+  A.t_w = dt + o_tw; A.L = c->L; A.H = c->H; A.t_layer_elems = t_layer_elems(c);
+  A.d_in = d_in_args(c); A.d_qkv = d_qkv_args(c, 0, 0); A.d_o = d_o_args(c, 0, 0);
+  A.d_gu = d_gu_args(c, 0, 0); A.d_dn = d_dn_args(c, 0, 0); A.d_head = d_head_args(c, 0);
+  A.d_attn = d_attn_args(c, 0, 0);
+  A.d_w = dt + o_dw; A.d_norm = dt + o_dn; A.d_emb = dt + o_de; A.d_heads = dt + o_dh;
+  A.S = c->S; A.Ld = c->Ld; A.Hd = c->Hd; A.Dd = c->Dd; A.Vt = c->Vt; A.Va = c->Va;
+  A.d_layer_elems = d_layer_elems(c);
+  A.pre = c->pre; A.y = c->y; A.ssq_d = c->ssq_d; A.apart = c->apart;
+  A.audio_logits = c->audio_logits;
+  A.pos = c->d_pos; A.live = c->d_live;
+  CKD(c, dalloc(c, (void**)&c->d_bar, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
+  CKD(c, dalloc(c, (void**)&c->d_abort, sizeof(int)));
+  void* tickets = nullptr;
+  CKD(c, dalloc(c, &tickets, 2 * (size_t)c->H * 16 * sizeof(unsigned)));
+  CKD(c, hipMemset(tickets, 0, 2 * (size_t)c->H * 16 * sizeof(unsigned)));
+  A.attn_ctr = (unsigned*)tickets;
+  CKD(c, hipMemset(c->d_bar, 0, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
+  CKD(c, hipMemset(c->d_abort, 0, sizeof(int)));
+  A.bar = c->d_bar; A.abort = c->d_abort;
+  CKD(c, dalloc(c, (void**)&c->d_step, sizeof(StepArgs)));
+  CKD(c, hipMemcpy(c->d_step, &A, sizeof(StepArgs), hipMemcpyHostToDevice));
+  c->step_grid = grid;
+  c->step_lds = lds;
+  c->persistent = true;
+  return MOSHI_OK;
+}
+
+// One full step of slot 0 on the stream; outputs to text_out [1], codes_out [S].
+int launch_persistent(moshi_ctx* c, const int* frames, int* text_out, int* codes_out,
+                      uint64_t* trace = nullptr) {
+  CKD(c, launch_step(c->dtype, c->hd, c->hdd, c->d_step, frames, text_out, codes_out,
+                     c->step_parity, c->step_grid, c->step_lds, c->stream, trace));
+  c->step_parity ^= 1;
+  return MOSHI_OK;
+}
+
+// A barrier wait ran out of time in an earlier launch: the context is lost.
+int check_abort(moshi_ctx* c, int flag) {
+  if (flag) {
+    c->failed = true;
+    c->err = "step kernel: a grid barrier timed out";
+    return MOSHI_E_DEVICE;
+  }
+  return MOSHI_OK;
 }
 
 hipError_t capture(moshi_ctx* c, hipError_t (*fn)(moshi_ctx*), hipGraphExec_t* out) {
@@ -443,10 +643,10 @@ hipError_t capture(moshi_ctx* c, hipError_t (*fn)(moshi_ctx*), hipGraphExec_t* o
   return e;
 }
 
-int ensure_graphs(moshi_ctx* c) {
+int ensure_graphs(moshi_ctx* c, bool temporal, bool dep) {
   if (!c->use_graphs || c->timing) return MOSHI_OK;
-  if (!c->g_temporal) CKD(c, capture(c, enqueue_temporal, &c->g_temporal));
-  if (!c->g_dep) CKD(c, capture(c, enqueue_depformer, &c->g_dep));
+  if (temporal && !c->g_temporal) CKD(c, capture(c, enqueue_temporal, &c->g_temporal));
+  if (dep && !c->g_dep) CKD(c, capture(c, enqueue_depformer, &c->g_dep));
   return MOSHI_OK;
 }
 
@@ -511,15 +711,24 @@ int run_step(moshi_ctx* c, const int32_t* frames, int32_t* text_token, int32_t* 
   int rc = check_ctx(c);
   if (rc) return rc;
   if ((rc = validate_frames(c, frames))) return rc;
-  if ((rc = ensure_graphs(c))) return rc;
+  const bool pers = c->persistent && with_dep && !c->timing;
+  if (!pers && (rc = ensure_graphs(c, true, with_dep))) return rc;
   if ((rc = upload_step_inputs(c, frames))) return rc;
-  if ((rc = launch_part(c, true))) return rc;
-  if (with_dep && (rc = launch_part(c, false))) return rc;
+  int abort_flag = 0;
+  if (pers) {
+    if (live_count(c) > 0 && (rc = launch_persistent(c, c->d_frames, c->tokens, c->codes)))
+      return rc;
+    CKD(c, hipMemcpyAsync(&abort_flag, c->d_abort, sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  } else {
+    if ((rc = launch_part(c, true))) return rc;
+    if (with_dep && (rc = launch_part(c, false))) return rc;
+  }
   CKD(c, hipMemcpyAsync(c->h_tokens, c->tokens, sizeof(int) * c->B, hipMemcpyDeviceToHost, c->stream));
   if (with_dep)
     CKD(c, hipMemcpyAsync(c->h_codes, c->codes, sizeof(int) * c->B * c->S, hipMemcpyDeviceToHost,
                           c->stream));
   CKD(c, hipStreamSynchronize(c->stream));
+  if ((rc = check_abort(c, abort_flag))) return rc;
   for (int b = 0; b < c->B; ++b) {
     if (c->live[b]) c->pos[b] += 1;
     if (text_token) text_token[b] = c->live[b] ? c->h_tokens[b] : -1;
@@ -618,7 +827,7 @@ int alloc_buffers(moshi_ctx* c) {
       {&c->dkv_k, B * c->Ld * c->Hd * S * c->hdd * es},
       {&c->dkv_v, B * c->Ld * c->Hd * S * c->hdd * es},
       {(void**)&c->x, B * D * 8},
-      {(void**)&c->ssq, ((D + 15) / 16) * B * 8},
+      {(void**)&c->ssq, ((D + 1) / 2) * B * 8},
       {(void**)&c->q, B * D * 8},
       {&c->o, B * D * es},
       {&c->act, B * F * es},
@@ -626,7 +835,7 @@ int alloc_buffers(moshi_ctx* c) {
       {&c->hn, B * D * es},
       {(void**)&c->pre, B * S * Dd * 8},
       {(void**)&c->y, B * Dd * 8},
-      {(void**)&c->ssq_d, ((Dd + 15) / 16) * B * 8},
+      {(void**)&c->ssq_d, ((Dd + 1) / 2) * B * 8},
       {(void**)&c->qd, B * Dd * 8},
       {&c->od, B * Dd * es},
       {&c->actd, B * Fd * es},
@@ -685,6 +894,68 @@ void release(moshi_ctx* c) {
   delete c;
 }
 
+// Per-operation timing of the persistent step kernel: workgroup 0 stamps the
+// wall clock after every grid barrier; the interval that ends at barrier k is
+// charged to operation k (its work plus the barrier). The operation sequence
+// is the per-operation path's, without its argmax-reduce launches (folded into
+// the next operation) and its attention chunk merges (done inside the
+// attention operation).
+int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vector<double>& acc_ms,
+                     std::vector<double>& acc_b, std::vector<int64_t>& acc_n) {
+  int rate_khz = 0;
+  CKD(c, hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, c->device));
+  if (rate_khz <= 0) return fail(c, MOSHI_E_DEVICE, "no wall clock rate");
+  void* d_trace = nullptr;
+  CKD(c, hipMalloc(&d_trace, STEP_TRACE_MAX * sizeof(uint64_t)));
+  std::vector<uint64_t> tr(STEP_TRACE_MAX);
+  int rc = MOSHI_OK;
+  for (int it = 0; it < n_steps && rc == MOSHI_OK; ++it) {
+    c->dry = true;
+    c->ev_class.clear();
+    c->ev_bytes.clear();
+    (void)enqueue_temporal(c);
+    (void)enqueue_depformer(c);
+    c->dry = false;
+    std::vector<int> cls;
+    std::vector<double> by;
+    for (size_t i = 0; i < c->ev_class.size(); ++i) {
+      const int k = c->ev_class[i];
+      if (k == KC_ARGMAX || k == KC_T_COMBINE) continue;
+      cls.push_back(k);
+      by.push_back(c->ev_bytes[i]);
+    }
+    const size_t nb = cls.size();
+    if (nb + 2 > (size_t)STEP_TRACE_MAX || live_count(c) == 0) {
+      rc = fail(c, MOSHI_E_INVALID, "step too long to trace, or no live session");
+      break;
+    }
+    if ((rc = upload_step_inputs(c, frames))) break;
+    if ((rc = launch_persistent(c, c->d_frames, c->tokens, c->codes, (uint64_t*)d_trace))) break;
+    int abort_flag = 0;
+    hipError_t e = hipMemcpyAsync(tr.data(), d_trace, (nb + 2) * sizeof(uint64_t),
+                                  hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(&abort_flag, c->d_abort, sizeof(int), hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) {
+      rc = device_fail(c, e, "step trace");
+      break;
+    }
+    if ((rc = check_abort(c, abort_flag))) break;
+    c->pos[0] += 1;
+    const double ms_per_tick = 1.0 / (double)rate_khz;
+    for (size_t k = 0; k < nb; ++k) {
+      acc_ms[cls[k]] += (double)(tr[k + 1] - tr[k]) * ms_per_tick;
+      acc_b[cls[k]] += by[k];
+      acc_n[cls[k]] += 1;
+    }
+    acc_ms[KC_ARGMAX] += (double)(tr[nb + 1] - tr[nb]) * ms_per_tick;
+    acc_n[KC_ARGMAX] += 1;
+  }
+  (void)hipFree(d_trace);
+  return rc;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -711,6 +982,11 @@ const char* moshi_strerror(int status) {
 }
 
 const char* moshi_last_error(const moshi_ctx* ctx) { return ctx ? ctx->err.c_str() : ""; }
+
+int32_t moshi_uses_step_kernel(const moshi_ctx* ctx) {
+  if (!ctx) return MOSHI_E_INVALID;
+  return ctx->persistent ? 1 : 0;
+}
 
 const char* moshi_kernel_class_name(int32_t c) {
   return (c >= 0 && c < KC_COUNT) ? kClassNames[c] : "";
@@ -760,7 +1036,7 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
     }
     c->own_stream = true;
   }
-  if ((rc = alloc_buffers(c)) || (rc = upload_weights(c, tensors))) {
+  if ((rc = alloc_buffers(c)) || (rc = upload_weights(c, tensors)) || (rc = setup_step(c))) {
     release(c);
     return rc;
   }
@@ -806,18 +1082,31 @@ int moshi_step_enqueue(moshi_ctx* c, const int32_t* d_frames, int32_t* d_text_to
   int rc = check_ctx(c);
   if (rc) return rc;
   if (!d_frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
-  if ((rc = ensure_graphs(c))) return rc;
-  if ((rc = upload_meta(c))) return rc;
-  CKD(c, hipMemcpyAsync(c->d_frames, d_frames, sizeof(int) * c->B * c->NCH,
-                        hipMemcpyDeviceToDevice, c->stream));
-  if ((rc = launch_part(c, true))) return rc;
-  if ((rc = launch_part(c, false))) return rc;
-  if (d_text_token)
-    CKD(c, hipMemcpyAsync(d_text_token, c->tokens, sizeof(int) * c->B, hipMemcpyDeviceToDevice,
-                          c->stream));
-  if (d_audio_codes)
-    CKD(c, hipMemcpyAsync(d_audio_codes, c->codes, sizeof(int) * c->B * c->S,
+  if (c->persistent) {
+    if ((rc = upload_meta(c))) return rc;
+    if (live_count(c) > 0) {
+      if ((rc = launch_persistent(c, d_frames, d_text_token ? d_text_token : c->tokens,
+                                  d_audio_codes ? d_audio_codes : c->codes)))
+        return rc;
+    } else {
+      if (d_text_token) CKD(c, hipMemsetAsync(d_text_token, 0xff, sizeof(int) * c->B, c->stream));
+      if (d_audio_codes)
+        CKD(c, hipMemsetAsync(d_audio_codes, 0xff, sizeof(int) * c->B * c->S, c->stream));
+    }
+  } else {
+    if ((rc = ensure_graphs(c, true, true))) return rc;
+    if ((rc = upload_meta(c))) return rc;
+    CKD(c, hipMemcpyAsync(c->d_frames, d_frames, sizeof(int) * c->B * c->NCH,
                           hipMemcpyDeviceToDevice, c->stream));
+    if ((rc = launch_part(c, true))) return rc;
+    if ((rc = launch_part(c, false))) return rc;
+    if (d_text_token)
+      CKD(c, hipMemcpyAsync(d_text_token, c->tokens, sizeof(int) * c->B, hipMemcpyDeviceToDevice,
+                            c->stream));
+    if (d_audio_codes)
+      CKD(c, hipMemcpyAsync(d_audio_codes, c->codes, sizeof(int) * c->B * c->S,
+                            hipMemcpyDeviceToDevice, c->stream));
+  }
   for (int b = 0; b < c->B; ++b)
     if (c->live[b]) c->pos[b] += 1;
   return MOSHI_OK;
@@ -826,9 +1115,12 @@ int moshi_step_enqueue(moshi_ctx* c, const int32_t* d_frames, int32_t* d_text_to
 int moshi_sync(moshi_ctx* c) {
   int rc = check_ctx(c);
   if (rc) return rc;
-  int bad = 0;
+  int bad = 0, abort_flag = 0;
   CKD(c, hipMemcpyAsync(&bad, c->d_err, sizeof(int), hipMemcpyDeviceToHost, c->stream));
+  if (c->persistent)
+    CKD(c, hipMemcpyAsync(&abort_flag, c->d_abort, sizeof(int), hipMemcpyDeviceToHost, c->stream));
   CKD(c, hipStreamSynchronize(c->stream));
+  if ((rc = check_abort(c, abort_flag))) return rc;
   if (bad) {
     CKD(c, hipMemsetAsync(c->d_err, 0, sizeof(int), c->stream));
     CKD(c, hipStreamSynchronize(c->stream));
@@ -849,7 +1141,7 @@ int moshi_depformer_step(moshi_ctx* c, const void* hidden, const int32_t* text_i
   for (int b = 0; b < c->B; ++b)
     if (c->live[b] && (text_in[b] < 0 || text_in[b] > c->Vt))
       return fail(c, MOSHI_E_INVALID, "text token out of range");
-  if ((rc = ensure_graphs(c))) return rc;
+  if ((rc = ensure_graphs(c, false, true))) return rc;
   if ((rc = upload_step_inputs(c, nullptr))) return rc;
   for (int b = 0; b < c->B; ++b) c->h_tokens[b] = c->live[b] ? text_in[b] : 0;
   CKD(c, hipMemcpyAsync(c->tokens, c->h_tokens, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
@@ -956,6 +1248,16 @@ int moshi_time_kernels(moshi_ctx* c, const int32_t* frames, int32_t n_steps, dou
   if ((rc = validate_frames(c, frames))) return rc;
   std::vector<double> acc_ms(KC_COUNT, 0.0), acc_b(KC_COUNT, 0.0);
   std::vector<int64_t> acc_n(KC_COUNT, 0);
+  if (c->persistent) {
+    rc = time_step_phases(c, frames, n_steps, acc_ms, acc_b, acc_n);
+    if (rc) return rc;
+    for (int k = 0; k < n_classes && k < KC_COUNT; ++k) {
+      if (ms) ms[k] = acc_ms[k];
+      if (launches) launches[k] = acc_n[k];
+      if (bytes) bytes[k] = acc_b[k];
+    }
+    return KC_COUNT;
+  }
   c->timing = true;
   for (int it = 0; it < n_steps; ++it) {
     c->ev_used = 0;

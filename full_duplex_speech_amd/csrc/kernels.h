@@ -58,7 +58,7 @@ struct GemmArgs {
   // EPI_RESID
   double* resid;
   int ldr;
-  double* ssq_out;   // [n_tiles][B]
+  double* ssq_out;   // one session: [ceil(N/GEMV_SSQ_ROWS)]; more: [n_tiles][B]
   // EPI_SWIGLU
   void* act;
   int lda;
@@ -106,7 +106,8 @@ struct EmbedArgs {
   int rows_text, rows_audio;  // table rows (codes are clamped into range)
   int* bad_code;              // set to 1 when a live code was out of range
   double* x;                  // [B][D]
-  double* ssq_out;            // [ceil(D/16)][B]
+  double* ssq_out;            // [ceil(D/ssq_rows)][B]
+  int ssq_rows;               // rows per sum-of-squares partial (2 or 16)
 };
 
 struct EntryArgs {
@@ -125,12 +126,68 @@ struct EntryArgs {
   int D;
   int B;
   double* y;        // [B][D]
-  double* ssq_out;  // [ceil(D/16)][B]
+  double* ssq_out;  // [ceil(D/ssq_rows)][B]
+  int ssq_rows;     // rows per sum-of-squares partial (2 or 16)
 };
 
 // Keys per attention workgroup; the window is at most ATTN_CHUNK * ATTN_MAX_CHUNKS.
 constexpr int ATTN_CHUNK = 64;
 constexpr int ATTN_MAX_CHUNKS = 512;
+
+// Argument block of the persistent one-session step kernel (step.hip), kept in
+// device memory. The GemmArgs / AttnArgs are templates: the kernel fills in
+// the per-layer weights, gains and ring offsets from the pointer tables.
+struct StepArgs {
+  // temporal
+  EmbedArgs emb;  // frames come with each launch
+  GemmArgs t_qkv, t_o, t_gu, t_dn, t_head;
+  AttnArgs t_attn;
+  const void* const* t_w;  // [L][6]: attn_norm, qkv, o, mlp_norm, gate_up, down
+  int L, H;
+  int64_t t_layer_elems;   // ring elements per layer of one slot (H * W * hd)
+  // depformer
+  GemmArgs d_in, d_qkv, d_o, d_gu, d_dn, d_head;
+  AttnArgs d_attn;
+  const void* const* d_w;      // [S * Ld][4]: qkv, o, gate_up, down of (substep, layer)
+  const void* const* d_norm;   // [Ld][2]: attn_norm, mlp_norm
+  const void* const* d_emb;    // [S] previous-token tables
+  const void* const* d_heads;  // [S]
+  int S, Ld, Hd, Dd, Vt, Va;
+  int64_t d_layer_elems;       // depformer K/V elements per layer (Hd * S * hdd)
+  const double* pre;           // [S * Dd] input projections of the hidden state
+  double* y;                   // depformer residual [Dd]
+  double* ssq_d;               // its per-tile sums of squares
+  ArgPart* apart;              // argmax partials of the last head
+  float* audio_logits;         // [S][Va]
+  // bookkeeping
+  int64_t* pos;                // slot 0 position (advanced at the end)
+  const int* live;
+  unsigned* bar;               // 2 sets of STEP_BAR_WORDS barrier counters
+  unsigned* attn_ctr;          // 2 sets of H * 16 per-head attention tickets
+  int* abort;                  // set when a barrier wait times out
+};
+// One-session projections run 8 waves per workgroup; each wave owns 2 rows
+// of a 16-row tile, and the residual epilogue writes one sum-of-squares
+// partial per wave (every 2 rows). With two or more sessions the partials are
+// per 16-row tile.
+constexpr int GEMV_KW = 8;
+constexpr int GEMV_SSQ_ROWS = 16 / GEMV_KW;
+constexpr int STEP_THREADS = 512;
+constexpr int STEP_BAR_WORDS = 1024;
+
+// Whether step.hip has an instantiation for (dtype, temporal head dim,
+// depformer head dim).
+bool step_supported(int dtype, int hd, int hdd);
+// Workgroups the step kernel can keep resident on the device (0 = none).
+int step_max_grid(int dtype, int hd, int hdd, size_t lds_bytes);
+// One cooperative launch of the whole step for slot 0. `parity` alternates
+// between launches (it picks the barrier counter set). `trace`, if set,
+// receives the wall clock (100 MHz) at the start, after every grid barrier
+// and at the end, as seen by workgroup 0 (STEP_TRACE_MAX entries at most).
+hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int* frames,
+                       int* text_out, int* codes_out, int parity, int nwg, size_t lds_bytes,
+                       hipStream_t st, uint64_t* trace);
+constexpr int STEP_TRACE_MAX = 4096;
 
 int gemm_tiles(int epi, int N);  // row tiles of a projection
 // Workgroups launched for a one-session projection (the number of CUs).

@@ -1,0 +1,485 @@
+// step.hip -- the whole frame step of one session as ONE persistent kernel.
+//
+// Model and numerics are those of kernels.hip (same device functions from
+// dev.h, so results are bit-identical to the per-operation kernels): the
+// summed embedding, the temporal layers (q/k/v + RoPE + ring write, windowed
+// attention, output projection, SwiGLU MLP), the text head and its greedy
+// token, the depformer input projections and the 16 substeps with their
+// heads ("vLLM-Omni recipe: PersonaPlex", "Architecture"; mobius PR #368,
+// "P2 - Moshi LM").
+//
+// Why one kernel: at one session every operation is a GEMV of a few to a few
+// hundred MB, and a dependent kernel launch costs about 4-5 us of ramp-up and
+// drain on MI355X; the depformer alone is ~500 dependent operations. Here one
+// workgroup runs per CU for the whole step and the operations are separated
+// by grid barriers instead of launches.
+//
+// Grid barrier: two levels, because 256 workgroups incrementing one counter
+// serialise at the memory side. Each workgroup counts into the counter of its
+// XCD; the last arrival of an XCD increments the global counter; everyone
+// polls the global counter. Cross-workgroup data use agent-scope relaxed
+// atomics (sc1 loads and stores, see dev.h), each thread waits for its own
+// stores (s_waitcnt 0) before the workgroup arrives, so no cache write-back
+// or invalidate is needed. Every wait is bounded: after SPIN_LIMIT polls a
+// workgroup raises the abort flag, and every waiter that sees it leaves, so
+// the grid always drains; the host then reports a device error.
+// The launch is cooperative (every workgroup resident or the launch fails).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "dev.h"
+#include "kernels.h"
+
+namespace moshi {
+namespace {
+
+constexpr int NT = STEP_THREADS;
+constexpr int KW = NT / 64;
+static_assert(KW == GEMV_KW, "the step kernel's projections use the one-session layout");
+constexpr int GU = 4;  // weight groups per lane and row in flight (register budget)
+constexpr int SPIN_LIMIT = 1 << 21;  // polls (~1 us each) before giving up
+
+// barrier counter layout inside one set (32-bit words, 128 B apart where
+// contended): flat counter, global counter, per-XCD registration, per-XCD
+// arrival counters
+constexpr int BW_FLAT = 0, BW_GLOBAL = 32, BW_REG = 64, BW_LOCAL = 128;
+constexpr int MAX_XCC = 16;
+
+__device__ __forceinline__ unsigned xcc_id() {
+  // hardware register XCC_ID (id 20), bits [3:0]
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & (MAX_XCC - 1);
+}
+
+struct Grid {
+  unsigned* set;
+  int* abort;
+  uint64_t* trace;  // optional: barrier exit times of workgroup 0
+  unsigned idx;    // barriers passed
+  unsigned xcc;    // this workgroup's XCD
+  unsigned xcc_n;  // workgroups on it
+  unsigned n_xcc;  // XCDs with at least one workgroup
+};
+
+// Make this thread's stores visible at agent scope before arriving.
+__device__ __forceinline__ void drain_stores() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Thread 0 polls `ctr` until it reaches `target` (wrap-safe) or the abort
+// flag rises. Returns nonzero when the grid must leave.
+__device__ __forceinline__ int poll_until(unsigned* ctr, unsigned target, int* abort) {
+  int spins = 0;
+  while ((int)(__hip_atomic_load((MOSHI_GLB unsigned*)ctr, MOSHI_RLX, MOSHI_AGT) - target) < 0) {
+    __builtin_amdgcn_s_sleep(1);
+    if (++spins > SPIN_LIMIT) {
+      __hip_atomic_store((MOSHI_GLB int*)abort, 1, MOSHI_RLX, MOSHI_AGT);
+      return 1;
+    }
+    if ((spins & 15) == 0 && __hip_atomic_load((MOSHI_GLB int*)abort, MOSHI_RLX, MOSHI_AGT)) return 1;
+  }
+  return 0;
+}
+
+// Grid barrier. Every thread of every workgroup calls it, after
+// drain_stores(); true = abort. Loads still in flight (weight prefetches)
+// stay in flight: only thread 0 of wave 0 touches the counters, and wave 0
+// issues no prefetch.
+__device__ __forceinline__ bool grid_sync_drained(Grid& g) {
+  __shared__ int s_leave;
+  __syncthreads();
+  g.idx += 1;
+  if (threadIdx.x == 0) {
+    const unsigned old =
+        __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_LOCAL + 32 * g.xcc, 1u, MOSHI_RLX, MOSHI_AGT);
+    if (old + 1 == g.idx * g.xcc_n)
+      __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_GLOBAL, 1u, MOSHI_RLX, MOSHI_AGT);
+    s_leave = poll_until(g.set + BW_GLOBAL, g.idx * g.n_xcc, g.abort);
+    if (g.trace != nullptr && blockIdx.x == 0) *(MOSHI_GLB uint64_t*)(g.trace + g.idx) = wall_clock64();
+  }
+  __syncthreads();
+  return s_leave != 0;
+}
+
+__device__ __forceinline__ bool grid_sync(Grid& g) {
+  drain_stores();
+  return grid_sync_drained(g);
+}
+
+// Start of a launch: clear the other counter set (used by the next launch;
+// the previous launch, which used it, has finished), count the workgroups of
+// every XCD, and wait for all of them (flat barrier).
+__device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn_ctr, int n_heads,
+                                          int parity, int* abort, uint64_t* trace) {
+  __shared__ int s_leave;
+  __shared__ unsigned s_cnt[MAX_XCC];
+  g.set = bar + parity * STEP_BAR_WORDS;
+  g.abort = abort;
+  g.trace = trace;
+  g.idx = 0;
+  g.xcc = xcc_id();
+  unsigned* other = bar + (parity ^ 1) * STEP_BAR_WORDS;
+  if (blockIdx.x == 0 && threadIdx.x < MAX_XCC) {
+    __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_REG + threadIdx.x, 0u, MOSHI_RLX, MOSHI_AGT);
+    __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_LOCAL + 32 * threadIdx.x, 0u, MOSHI_RLX, MOSHI_AGT);
+    if (threadIdx.x == 0) {
+      __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_FLAT, 0u, MOSHI_RLX, MOSHI_AGT);
+      __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_GLOBAL, 0u, MOSHI_RLX, MOSHI_AGT);
+    }
+  }
+  if (blockIdx.x == 0)
+    for (int h = threadIdx.x; h < n_heads; h += NT)
+      __hip_atomic_store((MOSHI_GLB unsigned*)attn_ctr + ((parity ^ 1) * n_heads + h) * 16, 0u,
+                         MOSHI_RLX, MOSHI_AGT);
+  drain_stores();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_REG + g.xcc, 1u, MOSHI_RLX, MOSHI_AGT);
+    __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_FLAT, 1u, MOSHI_RLX, MOSHI_AGT);
+    s_leave = poll_until(g.set + BW_FLAT, gridDim.x, abort);
+    if (trace != nullptr && blockIdx.x == 0) *(MOSHI_GLB uint64_t*)trace = wall_clock64();
+  }
+  __syncthreads();
+  if (s_leave) return true;
+  if (threadIdx.x < MAX_XCC)
+    s_cnt[threadIdx.x] = __hip_atomic_load((MOSHI_GLB unsigned*)g.set + BW_REG + threadIdx.x, MOSHI_RLX, MOSHI_AGT);
+  __syncthreads();
+  g.n_xcc = 0;
+  for (int i = 0; i < MAX_XCC; ++i) g.n_xcc += s_cnt[i] ? 1u : 0u;
+  g.xcc_n = s_cnt[g.xcc];
+  __syncthreads();
+  return false;
+}
+
+// Greedy token from per-tile argmax partials, reduced by the whole workgroup
+// (the comparison is exact, so the winner does not depend on the order).
+__device__ __forceinline__ int reduce_token(const ArgPart* part, int n_tiles, int n_rows) {
+  __shared__ double s_v[KW];
+  __shared__ int s_i[KW];
+  const int t = tid();
+  double bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = t; i < n_tiles; i += NT) {
+    const ArgPart p = unpack_part(ld_grp<true>(part + i));
+    if (arg_better(p.v, p.i, bv, bi)) {
+      bv = p.v;
+      bi = p.i;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ov = shfl_xor_d(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (arg_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if ((t & 63) == 0) {
+    s_v[t >> 6] = bv;
+    s_i[t >> 6] = bi;
+  }
+  __syncthreads();
+  bv = s_v[0];
+  bi = s_i[0];
+  for (int w = 1; w < KW; ++w)
+    if (arg_better(s_v[w], s_i[w], bv, bi)) {
+      bv = s_v[w];
+      bi = s_i[w];
+    }
+  __syncthreads();
+  return bi < n_rows ? bi : 0;
+}
+
+// Sum of squares of GEMV_SSQ_ROWS consecutive rows held by consecutive lanes;
+// the first lane of each group stores it as the group's partial (the layout
+// the one-session residual epilogue writes).
+template <bool C>
+__device__ __forceinline__ void store_tile_ssq(double v, int row, int n_rows, double* ssq_out) {
+  double ss = v * v;
+#pragma unroll
+  for (int off = GEMV_SSQ_ROWS / 2; off > 0; off >>= 1) ss += shfl_xor_d(ss, off);
+  if (row % GEMV_SSQ_ROWS == 0 && row < n_rows) st_f64<C>(ssq_out + row / GEMV_SSQ_ROWS, ss);
+}
+
+// x = E_text[c0] + sum_k E_audio_k[c_k] for slot 0; NT rows per item.
+// A code outside its table is clamped into range and flagged for the host.
+template <typename T>
+__device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frames, int wg,
+                                            int nwg) {
+  for (int item = wg; item * NT < a.D; item += nwg) {
+    const int row = item * NT + tid();
+    double acc = 0.0;
+    if (row < a.D) {
+      for (int c0 = 0; c0 < a.n_ch; c0 += 8) {
+        double v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int c = c0 + j;
+          v[j] = 0.0;
+          if (c < a.n_ch) {
+            int code = ldg(frames + c);
+            const int rows = (c == 0) ? a.rows_text : a.rows_audio;
+            if (code < 0 || code >= rows) {
+              if (row == 0) atomicOr(a.bad_code, 1);
+              code = code < 0 ? 0 : rows - 1;
+            }
+            v[j] = to_d(ldg((const T*)a.tables[c] + (size_t)code * a.D + row));
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (c0 + j < a.n_ch) acc += v[j];
+      }
+      st_f64<true>(a.x + row, acc);
+    }
+    store_tile_ssq<true>(acc, row, a.D, a.ssq_out);
+  }
+}
+
+// Depformer substep entry for slot 0: the previous head's token (the text
+// token at s = 0), stored as an output by workgroup 0, then
+// y = W_in[s] hidden + E_s[token].
+template <typename T>
+__device__ __forceinline__ void entry_phase(const StepArgs& A, int s, int* tok_out, int wg,
+                                            int nwg) {
+  if (wg * NT >= A.Dd) return;  // no rows here
+  const int prev_rows = s == 0 ? A.Vt : A.Va;
+  const int tok = reduce_token(A.apart, (prev_rows + 15) / 16, prev_rows);
+  if (wg == 0 && threadIdx.x == 0) st_i32<true>(tok_out, tok);
+  const T* table = (const T*)A.d_emb[s];
+  for (int item = wg; item * NT < A.Dd; item += nwg) {
+    const int row = item * NT + tid();
+    double acc = 0.0;
+    if (row < A.Dd) {
+      acc = ld_f64<true>(A.pre + (size_t)s * A.Dd + row) + to_d(ldg(table + (size_t)tok * A.Dd + row));
+      st_f64<true>(A.y + row, acc);
+    }
+    store_tile_ssq<true>(acc, row, A.Dd, A.ssq_d);
+  }
+}
+
+template <typename T, int HD, int HDD>
+__global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
+                                                  const int* __restrict__ frames, int* text_out,
+                                                  int* codes_out, int parity, uint64_t* trace) {
+  extern __shared__ __align__(16) unsigned char s_dyn[];  // GEMV input or attention scratch
+  T* xs = (T*)s_dyn;
+  double* s_o = (double*)s_dyn;
+  const StepArgs& A = *P;
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  Grid g;
+  if (grid_init(g, A.bar, A.attn_ctr, A.H, parity, A.abort, trace)) return;
+  // first weight batch of the next projection, requested before each barrier
+  u32x4 pf[GU][16 / KW];
+#define PREFETCH_SYNC(EPI_, args_)                         \
+  do {                                                     \
+    drain_stores();                                        \
+    gemv_prefetch<T, KW, EPI_, GU>((args_), wg, pf);       \
+    if (grid_sync_drained(g)) return;                      \
+  } while (0)
+#define GEMV(PRO_, EPI_, args_) gemv_core<T, KW, PRO_, EPI_, true, GU, true>((args_), wg, nwg, xs, pf)
+
+  // per-layer argument blocks
+  auto t_qkv = [&](int l) {
+    GemmArgs a = A.t_qkv;
+    a.gain = A.t_w[(size_t)l * 6 + 0];
+    a.W = A.t_w[(size_t)l * 6 + 1];
+    a.layer_off = (int64_t)l * A.t_layer_elems;
+    return a;
+  };
+  auto t_o = [&](int l) {
+    GemmArgs a = A.t_o;
+    a.W = A.t_w[(size_t)l * 6 + 2];
+    return a;
+  };
+  auto t_gu = [&](int l) {
+    GemmArgs a = A.t_gu;
+    a.gain = A.t_w[(size_t)l * 6 + 3];
+    a.W = A.t_w[(size_t)l * 6 + 4];
+    return a;
+  };
+  auto t_dn = [&](int l) {
+    GemmArgs a = A.t_dn;
+    a.W = A.t_w[(size_t)l * 6 + 5];
+    return a;
+  };
+  auto d_qkv = [&](int s, int l) {
+    GemmArgs a = A.d_qkv;
+    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 0];
+    a.gain = A.d_norm[(size_t)l * 2 + 0];
+    a.scalar_widx = s;
+    a.layer_off = (int64_t)l * A.d_layer_elems;
+    return a;
+  };
+  auto d_o = [&](int s, int l) {
+    GemmArgs a = A.d_o;
+    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 1];
+    return a;
+  };
+  auto d_gu = [&](int s, int l) {
+    GemmArgs a = A.d_gu;
+    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 2];
+    a.gain = A.d_norm[(size_t)l * 2 + 1];
+    return a;
+  };
+  auto d_dn = [&](int s, int l) {
+    GemmArgs a = A.d_dn;
+    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 3];
+    return a;
+  };
+  auto d_head = [&](int s) {
+    GemmArgs a = A.d_head;
+    a.W = A.d_heads[s];
+    a.logits = A.audio_logits + (size_t)s * A.Va;
+    return a;
+  };
+
+  // ---- summed embedding ----
+  embed_phase<T>(A.emb, frames, wg, nwg);
+  PREFETCH_SYNC(EPI_QKV, t_qkv(0));
+
+  // ---- temporal layers ----
+  int nvalid, excl;
+  window_of(A.t_attn, 0, nvalid, excl);
+  const int nchunks = (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  int nspan = nwg / A.H;
+  nspan = nspan < 1 ? 1 : (nspan > nchunks ? nchunks : nspan);
+  for (int l = 0; l < A.L; ++l) {
+    GEMV(PRO_NORM, EPI_QKV, t_qkv(l));
+    PREFETCH_SYNC(EPI_RESID, t_o(l));  // held through the attention
+    {
+      // each head's chunks split into nspan contiguous spans, one per
+      // workgroup; the workgroup finishing a head's last span merges it
+      AttnArgs at = A.t_attn;
+      at.layer_off = (int64_t)l * A.t_layer_elems;
+      unsigned* tickets = A.attn_ctr + (size_t)parity * A.H * 16;
+      for (int item = wg; item < A.H * nspan; item += nwg) {
+        const int h = item / nspan, j = item % nspan;
+        attn_span<T, HD, NT, true, KV_NEWEST>(at, j * nchunks / nspan, (j + 1) * nchunks / nspan, h,
+                                              0, nvalid, excl, s_o);
+        if (nchunks > 1) {
+          __shared__ int s_last;
+          drain_stores();
+          __syncthreads();
+          if (threadIdx.x == 0) {
+            const unsigned old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)tickets + h * 16, 1u,
+                                                        MOSHI_RLX, MOSHI_AGT);
+            s_last = (old + 1 == (unsigned)((l + 1) * nspan));
+          }
+          __syncthreads();
+          if (s_last) combine_staged<T, HD, NT, true>(at, h, 0, nchunks, s_o);
+        }
+      }
+    }
+    if (grid_sync(g)) return;
+    GEMV(PRO_DIRECT, EPI_RESID, t_o(l));
+    PREFETCH_SYNC(EPI_SWIGLU, t_gu(l));
+    GEMV(PRO_NORM, EPI_SWIGLU, t_gu(l));
+    PREFETCH_SYNC(EPI_RESID, t_dn(l));
+    GEMV(PRO_DIRECT, EPI_RESID, t_dn(l));
+    if (l + 1 < A.L)
+      PREFETCH_SYNC(EPI_QKV, t_qkv(l + 1));
+    else
+      PREFETCH_SYNC(EPI_ARGMAX, A.t_head);
+  }
+  // ---- final norm -> hidden, text head (argmax partials) ----
+  GEMV(PRO_NORM, EPI_ARGMAX, A.t_head);
+  PREFETCH_SYNC(EPI_STORE, A.d_in);
+  // ---- depformer input projections of all substeps ----
+  GEMV(PRO_DIRECT, EPI_STORE, A.d_in);
+  PREFETCH_SYNC(EPI_QKV, d_qkv(0, 0));  // held through the entry
+
+  // ---- 16 substeps ----
+  for (int s = 0; s < A.S; ++s) {
+    entry_phase<T>(A, s, s == 0 ? text_out : codes_out + (s - 1), wg, nwg);
+    if (grid_sync(g)) return;
+    for (int l = 0; l < A.Ld; ++l) {
+      GEMV(PRO_NORM, EPI_QKV, d_qkv(s, l));
+      PREFETCH_SYNC(EPI_RESID, d_o(s, l));  // held through the attention
+      {
+        AttnArgs at = A.d_attn;
+        at.layer_off = (int64_t)l * A.d_layer_elems;
+        at.scalar_nvalid = s + 1;
+        for (int h = wg; h < A.Hd; h += nwg)
+          attn_item<T, HDD, NT, true, KV_ALL>(at, 0, h, 0, s + 1, -1, s_o);
+      }
+      if (grid_sync(g)) return;
+      GEMV(PRO_DIRECT, EPI_RESID, d_o(s, l));
+      PREFETCH_SYNC(EPI_SWIGLU, d_gu(s, l));
+      GEMV(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
+      PREFETCH_SYNC(EPI_RESID, d_dn(s, l));
+      GEMV(PRO_DIRECT, EPI_RESID, d_dn(s, l));
+      if (l + 1 < A.Ld)
+        PREFETCH_SYNC(EPI_QKV, d_qkv(s, l + 1));
+      else
+        PREFETCH_SYNC(EPI_ARGMAX, d_head(s));
+    }
+    GEMV(PRO_CAST, EPI_ARGMAX, d_head(s));
+    if (s + 1 < A.S)
+      PREFETCH_SYNC(EPI_QKV, d_qkv(s + 1, 0));  // held through the entry
+    else if (grid_sync(g))
+      return;
+  }
+#undef GEMV
+#undef PREFETCH_SYNC
+  // ---- last code, next position ----
+  if (wg == 0) {
+    const int tok = reduce_token(A.apart, (A.Va + 15) / 16, A.Va);
+    if (threadIdx.x == 0) {
+      *(MOSHI_GLB int*)(codes_out + A.S - 1) = tok;
+      if (ldg(A.live)) *(MOSHI_GLB int64_t*)A.pos += 1;
+    }
+  }
+  if (trace != nullptr && wg == 0 && threadIdx.x == 0) *(MOSHI_GLB uint64_t*)(trace + g.idx + 1) = wall_clock64();
+}
+
+template <typename T, int HD, int HDD>
+hipError_t launch_t(const StepArgs* dP, const int* frames, int* text_out, int* codes_out,
+                    int parity, int nwg, size_t lds, hipStream_t st, uint64_t* trace) {
+  void* args[] = {(void*)&dP,     (void*)&frames, (void*)&text_out, (void*)&codes_out,
+                  (void*)&parity, (void*)&trace};
+  return hipLaunchCooperativeKernel((const void*)step_kernel<T, HD, HDD>, dim3(nwg), dim3(NT), args,
+                                    (unsigned)lds, st);
+}
+
+template <typename T, int HD, int HDD>
+int max_grid_t(size_t lds) {
+  int per_cu = 0, dev = 0, ncu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, step_kernel<T, HD, HDD>, NT, lds) !=
+      hipSuccess)
+    return 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return per_cu > 0 ? ncu : 0;  // one workgroup per CU
+}
+
+}  // namespace
+
+// Instantiated shapes: bf16 with head dims 128 / 64 (PersonaPlex), fp32 with
+// 64 / 32 (the small fp32 test model). Other shapes use the per-operation
+// kernels.
+bool step_supported(int dtype, int hd, int hdd) {
+  return (dtype == DT_BF16 && hd == 128 && hdd == 64) || (dtype == DT_F32 && hd == 64 && hdd == 32);
+}
+
+int step_max_grid(int dtype, int hd, int hdd, size_t lds) {
+  if (dtype == DT_BF16 && hd == 128 && hdd == 64) return max_grid_t<__bf16, 128, 64>(lds);
+  if (dtype == DT_F32 && hd == 64 && hdd == 32) return max_grid_t<float, 64, 32>(lds);
+  return 0;
+}
+
+hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int* frames,
+                       int* text_out, int* codes_out, int parity, int nwg, size_t lds,
+                       hipStream_t st, uint64_t* trace) {
+  if (dtype == DT_BF16 && hd == 128 && hdd == 64)
+    return launch_t<__bf16, 128, 64>(dP, frames, text_out, codes_out, parity, nwg, lds, st, trace);
+  if (dtype == DT_F32 && hd == 64 && hdd == 32)
+    return launch_t<float, 64, 32>(dP, frames, text_out, codes_out, parity, nwg, lds, st, trace);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moshi

@@ -183,6 +183,12 @@ int moshi_time_kernels(moshi_ctx* ctx, const int32_t* frames, int32_t n_steps, d
                        int64_t* launches, double* bytes, int32_t n_classes);
 const char* moshi_kernel_class_name(int32_t c);
 
+/* 1 if moshi_step / moshi_step_enqueue run the whole frame as one persistent
+ * kernel (capacity 1 with a supported shape, unless the environment variable
+ * MOSHI_STEP_KERNEL=0 was set at creation), 0 if they run one kernel per
+ * operation; the results are identical. Negative on a NULL context. */
+int32_t moshi_uses_step_kernel(const moshi_ctx* ctx);
+
 /* Static text of a status code. */
 const char* moshi_strerror(int status);
 

@@ -151,7 +151,9 @@ def test_full_step_b1(b1, omodel):
     slot = M.moshi_session_join(ctx)
     k, v = wl.prefill_kv(SHAPE, w2.seed("prefill"), 0, SHAPE.window, threads=16)
     M.moshi_session_prefill_kv(ctx, slot, k, v)
-    frames = wl.frames(SHAPE, w2.seed("frames"), 0, 0, 2)
+    n = wl.WORKLOADS[2].frames
+    frames = wl.frames(SHAPE, w2.seed("frames"), 0, 0, n)
+    log(f"full step B=1: step kernel {M.moshi_uses_step_kernel(ctx)}")
     o = oracle.Session(omodel)
     o.prefill(k, v)
     stats = Stats()
@@ -160,6 +162,19 @@ def test_full_step_b1(b1, omodel):
         tl, al = M.moshi_read_logits(ctx)
         r = o.step(frames[t], forced_text=int(tok[0]), forced_codes=codes[0])
         compare_frame(SHAPE, stats, f"full t={t}", int(tok[0]), codes[0], tl[0], al[0], r)
+    # the rest of the 200 frames, then the last one from the read-back ring
+    for t in range(2, n - 1):
+        M.moshi_step(ctx, frames[t][None, :])
+    pos = M.moshi_session_info(ctx, slot)[0]
+    assert pos == SHAPE.window + n - 1
+    rk, rv = M.moshi_session_read_kv(ctx, slot)
+    tok, codes = M.moshi_step(ctx, frames[n - 1][None, :])
+    tl, al = M.moshi_read_logits(ctx)
+    o2 = oracle.Session(omodel)
+    o2.load_ring(pos, rk, rv)
+    r = o2.step(frames[n - 1], forced_text=int(tok[0]), forced_codes=codes[0])
+    compare_frame(SHAPE, stats, f"full t={n - 1} (from ring)", int(tok[0]), codes[0], tl[0],
+                  al[0], r)
     log(f"full step B=1 done {stats}")
     M.moshi_session_leave(ctx, slot)
 

@@ -221,3 +221,63 @@ def test_error_paths_leave_state_unchanged():
     tok, codes = M.moshi_step(ctx, f2)
     assert tok[a] == -1 and tok[b] >= 0
     M.moshi_destroy(ctx)
+
+
+def _single_session_run(shape, weights, fill, T, step_kernel, seed=5):
+    import os
+    old = os.environ.get("MOSHI_STEP_KERNEL")
+    os.environ["MOSHI_STEP_KERNEL"] = "1" if step_kernel else "0"
+    try:
+        ctx = new_engine(shape, weights, 1)
+    finally:
+        if old is None:
+            del os.environ["MOSHI_STEP_KERNEL"]
+        else:
+            os.environ["MOSHI_STEP_KERNEL"] = old
+    used = M.moshi_uses_step_kernel(ctx)
+    slot = M.moshi_session_join(ctx)
+    if fill:
+        k, v = wl.prefill_kv(shape, seed + 1, 0, fill)
+        M.moshi_session_prefill_kv(ctx, slot, k, v)
+    out = []
+    for t in range(T):
+        f = wl.frames(shape, seed, 0, t, 1)
+        tok, codes = M.moshi_step(ctx, f)
+        tl, al = M.moshi_read_logits(ctx)
+        out.append((tok.copy(), codes.copy(), tl.copy(), al.copy()))
+    info = M.moshi_session_info(ctx, slot)
+    M.moshi_destroy(ctx)
+    return used, out, info
+
+
+@pytest.mark.parametrize("case", ["ragged_bf16_w150", "tiny_fp32", "ragged_bf16_mask_oldest"])
+def test_step_kernel_matches_per_op_kernels(case):
+    """The persistent one-session step kernel and the per-operation kernels
+    give bit-identical tokens, codes and logits (several attention chunks, a
+    wrapping ring, ragged widths), and the step kernel also matches the oracle."""
+    if case == "ragged_bf16_w150":
+        shape, fill, T = spec.RAGGED.replace(window=150), 140, 30
+    elif case == "tiny_fp32":
+        shape, fill, T = spec.TINY, 0, 70
+    else:
+        shape, fill, T = spec.RAGGED.replace(window=9, mask_oldest=True), 9, 12
+    weights = wl.make_weights(shape, 47, gains="random")
+    used1, a, info1 = _single_session_run(shape, weights, fill, T, True)
+    used0, b, info0 = _single_session_run(shape, weights, fill, T, False)
+    assert used1 and not used0
+    assert info1 == info0
+    for t, (x, y) in enumerate(zip(a, b)):
+        for u, v in zip(x, y):
+            assert np.array_equal(u, v), f"{case}: step kernel differs from per-op kernels at t={t}"
+    # and against the oracle, teacher-forced
+    om = oracle.Model(shape, weights)
+    o = oracle.Session(om)
+    if fill:
+        k, v = wl.prefill_kv(shape, 6, 0, fill)
+        o.prefill(k, v)
+    stats = Stats()
+    for t in range(T):
+        tok, codes, tl, al = a[t]
+        r = o.step(wl.frames(shape, 5, 0, t, 1)[0], forced_text=int(tok[0]), forced_codes=codes[0])
+        compare_frame(shape, stats, f"{case} t={t}", int(tok[0]), codes[0], tl[0], al[0], r)
+    log(f"{case}:", stats)
