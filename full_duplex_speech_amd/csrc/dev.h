@@ -93,6 +93,15 @@ template <bool C>
 __device__ __forceinline__ void st_f64(double* p, double v) {
   st_u64<C>(p, __builtin_bit_cast(uint64_t, v));
 }
+// 16-byte coherent load at byte offset `off` from a workgroup-uniform base:
+// one buffer_load_dwordx4 with sc1 (the same count of loads in flight as a
+// plain 16-byte load, which keeps the compiler's wait counts exact).
+__device__ __forceinline__ u32x4 ld16_coh(const void* base, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, 0x7fffffff, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, /*sc1*/ 16);
+}
+
 // one 16-byte group
 template <bool C>
 __device__ __forceinline__ u32x4 ld_grp(const void* p) {
@@ -279,6 +288,45 @@ __device__ __forceinline__ double shfl_xor_d(double v, int m) {
   return __hiloint2double(__shfl_xor(__double2hiint(v), m), __shfl_xor(__double2loint(v), m));
 }
 
+// ---- wave reductions on DPP lane moves (a few cycles each, where a shuffle
+// through ds_bpermute costs ~100) ----
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+  const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+  return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+  return __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(v), lane),
+                          __builtin_amdgcn_readlane(__double2loint(v), lane));
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7-i within 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15-i within 16
+
+// Sum (MAX = false) or maximum over aligned groups of N lanes (N = 1, 2, 4,
+// 8, 16, 32, 64), the result in every lane of the group. The association is
+// fixed: pairs, quads, eights, rows of 16, then rows combined in lane order.
+// All 64 lanes must be active.
+template <int N, bool MAX = false>
+__device__ __forceinline__ double group_reduce(double v) {
+  auto op = [](double x, double y) { return MAX ? fmax(x, y) : x + y; };
+  if constexpr (N >= 2) v = op(v, dpp_d<DPP_XOR1>(v));
+  if constexpr (N >= 4) v = op(v, dpp_d<DPP_XOR2>(v));
+  if constexpr (N >= 8) v = op(v, dpp_d<DPP_HALF_MIRROR>(v));
+  if constexpr (N >= 16) v = op(v, dpp_d<DPP_MIRROR>(v));
+  if constexpr (N == 32) {
+    const double a = op(readlane_d(v, 0), readlane_d(v, 16));
+    const double b = op(readlane_d(v, 32), readlane_d(v, 48));
+    v = (__lane_id() < 32) ? a : b;
+  } else if constexpr (N == 64) {
+    v = op(op(readlane_d(v, 0), readlane_d(v, 16)), op(readlane_d(v, 32), readlane_d(v, 48)));
+  }
+  return v;
+}
+
 // RMSNorm scale 1/sqrt(mean(x^2) + eps) of column col from the producer's
 // per-tile sums of squares; every thread of the workgroup gets the same value.
 // Threads [0, nthr) split the tiles; fixed-order reduction through `red`.
@@ -287,8 +335,7 @@ __device__ __forceinline__ double rms_scale(const GemmArgs& a, int col, double* 
   const int t = tid();
   double s = 0.0;
   for (int i = t; i < a.n_ssq; i += nthr) s += ld_f64<C>(a.ssq + (size_t)i * a.B + col);
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) s += shfl_xor_d(s, off);
+  s = group_reduce<64>(s);
   if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
   double tot = 0.0;
@@ -649,10 +696,7 @@ __device__ __forceinline__ void gemv_core(
       }
       if (bt == nbatch - 1) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-#pragma unroll
-          for (int off = 32; off > 0; off >>= 1) acc[r] += shfl_xor_d(acc[r], off);
-        }
+        for (int r = 0; r < R; ++r) acc[r] = group_reduce<64>(acc[r]);
         if constexpr (EPI == EPI_ARGMAX) {
           // per-tile (max, index) partial: wave 0 combines the tile's 16 rows
           if (lane == 0) {
@@ -728,50 +772,53 @@ __device__ __forceinline__ void window_of(const AttnArgs& a, int b, int& nvalid,
   }
 }
 
-// Which ring rows were written during the running kernel (see C):
-enum KvFresh { KV_NONE = 0, KV_NEWEST = 1, KV_ALL = 2 };
-
-// K and V of one 64-key chunk as held by one thread: PASSES keys, one
-// 16-byte group of each.
+// K and V of one 64-key chunk as held by one thread of an NT-thread group:
+// PASSES keys, one 16-byte group of each. A workgroup may hold several such
+// groups (thread t is in group t / NT), each working on its own chunk; every
+// function below is called by all threads of the workgroup (they synchronise
+// it), each group with its own arguments.
 template <typename T, int HD, int NT>
 struct AttnShape {
   static constexpr int VEC = VecOf<T>::N;
   static constexpr int TK = HD / VEC;   // threads per key (one 16-byte group each)
   static constexpr int KP = NT / TK;    // keys per pass
   static constexpr int PASSES = ATTN_CHUNK / KP;
-  static_assert(TK <= 64 && (64 % TK) == 0 && PASSES >= 1 && ATTN_CHUNK % KP == 0,
+  static constexpr int SO = KP * (HD + 1);  // s_o doubles per group
+  static_assert(TK <= 64 && (64 % TK) == 0 && PASSES >= 1 && ATTN_CHUNK % KP == 0 && NT >= 64,
                 "head dim / chunk layout");
 };
 template <typename T, int HD, int NT>
 struct KvChunk {
   u32x4 k[AttnShape<T, HD, NT>::PASSES], v[AttnShape<T, HD, NT>::PASSES];
 };
+constexpr int ATTN_MAX_GROUPS = 2;
 
-// Requests the K and V groups of `chunk` (zeros past nvalid). Rows written
-// during the running kernel (FRESH) are read coherently.
-template <typename T, int HD, int NT, int FRESH>
+// Requests the K and V groups of `chunk`. Keys past nvalid (and every key
+// when live = false, a placeholder that keeps the number of loads in flight
+// the same on every path) read key 0, which is always written; they are
+// masked out by the scores and multiplied by p = 0. COH: the ring was written
+// during the running kernel (at least its newest row), so every load is
+// coherent (sc1).
+template <typename T, int HD, int NT, bool COH>
 __device__ __forceinline__ void attn_load(const AttnArgs& a, int chunk, int h, int b, int nvalid,
-                                          int newest, KvChunk<T, HD, NT>& kv) {
+                                          KvChunk<T, HD, NT>& kv, bool live = true) {
   using S = AttnShape<T, HD, NT>;
-  const int t = tid();
+  const int t = tid() % NT;
   const int kd = t % S::TK, kk = t / S::TK;
   const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
   const T* kbase = (const T*)a.ring_k + base;
   const T* vbase = (const T*)a.ring_v + base;
 #pragma unroll
   for (int ps = 0; ps < S::PASSES; ++ps) {
-    // keys past nvalid read key 0 (always written; masked out by the scores
-    // and multiplied by p = 0), so every lane loads unconditionally
     const int j0 = chunk * ATTN_CHUNK + ps * S::KP + kk;
-    const int j = j0 < nvalid ? j0 : 0;
-    const T* kp = kbase + (size_t)j * HD + kd * S::VEC;
-    const T* vp = vbase + (size_t)j * HD + kd * S::VEC;
-    if (FRESH == KV_ALL || (FRESH == KV_NEWEST && j == newest)) {
-      kv.k[ps] = ld_grp<true>(kp);
-      kv.v[ps] = ld_grp<true>(vp);
+    const int j = (live && j0 < nvalid) ? j0 : 0;
+    const uint32_t off = (uint32_t)(((size_t)j * HD + kd * S::VEC) * sizeof(T));
+    if constexpr (COH) {
+      kv.k[ps] = ld16_coh(kbase, off);
+      kv.v[ps] = ld16_coh(vbase, off);
     } else {
-      kv.k[ps] = ld16(kp);
-      kv.v[ps] = ld16(vp);
+      kv.k[ps] = ld16((const char*)kbase + off);
+      kv.v[ps] = ld16((const char*)vbase + off);
     }
   }
 }
@@ -780,7 +827,7 @@ __device__ __forceinline__ void attn_load(const AttnArgs& a, int chunk, int h, i
 template <typename T, int HD, int NT, bool C>
 __device__ __forceinline__ void attn_query(const AttnArgs& a, int h, int b, double* qv) {
   using S = AttnShape<T, HD, NT>;
-  const int kd = tid() % S::TK;
+  const int kd = (tid() % NT) % S::TK;
   const double* qp = a.q + (size_t)b * a.ldq + h * HD + kd * S::VEC;
 #pragma unroll
   for (int e = 0; e < S::VEC; ++e) qv[e] = ld_f64<C>(qp + e);
@@ -788,18 +835,24 @@ __device__ __forceinline__ void attn_query(const AttnArgs& a, int h, int b, doub
 
 // Scores, softmax and p.V of one loaded chunk in fp64. A single chunk writes
 // the rounded output directly; otherwise the (max, sum, p.V) partials go to
-// a.part. s_o: LDS [KP][HD+1] doubles. Every thread of the workgroup calls it.
+// a.part. s_o: LDS, AttnShape::SO doubles per group. active = false: the
+// group computes on placeholder data and writes nothing.
 template <typename T, int HD, int NT, bool C>
 __device__ __forceinline__ void attn_compute(const AttnArgs& a, int chunk, int h, int b,
                                              int nvalid, int excl, const double* qv,
-                                             const KvChunk<T, HD, NT>& kv, double* s_o) {
+                                             const KvChunk<T, HD, NT>& kv, double* s_o,
+                                             bool active = true) {
   using S = AttnShape<T, HD, NT>;
   constexpr int VEC = S::VEC, TK = S::TK, KP = S::KP, PASSES = S::PASSES;
   constexpr int CH = ATTN_CHUNK;
   constexpr int LD = HD + 1;
-  __shared__ double s_p[CH];
-  __shared__ double s_ml[2];
-  const int t = tid();
+  __shared__ double s_p_all[ATTN_MAX_GROUPS][CH];
+  __shared__ double s_ml_all[ATTN_MAX_GROUPS][2];
+  const int grp = tid() / NT;
+  const int t = tid() % NT;
+  double* s_p = s_p_all[grp];
+  double* s_ml = s_ml_all[grp];
+  double* so = s_o + grp * S::SO;
   const int nchunks = (nvalid + CH - 1) / CH;
   const int kd = t % TK, kk = t / TK;
   const double scale = 1.0 / sqrt((double)HD);
@@ -814,20 +867,15 @@ __device__ __forceinline__ void attn_compute(const AttnArgs& a, int chunk, int h
     double d = 0.0;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) d = fma(qv[e], kd_[e], d);
-#pragma unroll
-    for (int off = TK / 2; off > 0; off >>= 1) d += shfl_xor_d(d, off);
+    d = group_reduce<TK>(d);
     if (kd == 0) s_p[ps * KP + kk] = ok ? d * scale : -INFINITY;
   }
   __syncthreads();
   if (t < 64) {
     const double sv = (t < CH) ? s_p[t] : -INFINITY;
-    double m = sv;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) m = fmax(m, shfl_xor_d(m, off));
+    const double m = group_reduce<64, true>(sv);
     const double pj = (m == -INFINITY || sv == -INFINITY) ? 0.0 : exp(sv - m);
-    double l = pj;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) l += shfl_xor_d(l, off);
+    const double l = group_reduce<64>(pj);
     if (t < CH) s_p[t] = pj;
     if (t == 0) {
       s_ml[0] = m;
@@ -849,11 +897,11 @@ __device__ __forceinline__ void attn_compute(const AttnArgs& a, int chunk, int h
     for (int e = 0; e < VEC; ++e) acc[e] = fma(pj, vd[e], acc[e]);
   }
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) s_o[kk * LD + kd * VEC + e] = acc[e];
+  for (int e = 0; e < VEC; ++e) so[kk * LD + kd * VEC + e] = acc[e];
   __syncthreads();
-  if (t < HD) {
+  if (active && t < HD) {
     double od = 0.0;
-    for (int r = 0; r < KP; ++r) od += s_o[r * LD + t];
+    for (int r = 0; r < KP; ++r) od += so[r * LD + t];
     if (nchunks == 1) {
       const double l = s_ml[1];
       const double ov = l > 0.0 ? od / l : 0.0;
@@ -870,36 +918,37 @@ __device__ __forceinline__ void attn_compute(const AttnArgs& a, int chunk, int h
   __syncthreads();  // s_p, s_ml, s_o are reused by the next chunk
 }
 
-// One (64-key chunk, head, slot) item with NT threads.
-template <typename T, int HD, int NT, bool C, int FRESH>
+// One (64-key chunk, head, slot) item per NT-thread group.
+template <typename T, int HD, int NT, bool C>
 __device__ __forceinline__ void attn_item(const AttnArgs& a, int chunk, int h, int b, int nvalid,
-                                          int excl, double* s_o) {
-  int newest = -1;
-  if constexpr (FRESH == KV_NEWEST) newest = (int)(ldg(a.pos + b) % a.cap);
+                                          int excl, double* s_o, bool active = true) {
   KvChunk<T, HD, NT> kv;
-  attn_load<T, HD, NT, FRESH>(a, chunk, h, b, nvalid, newest, kv);
+  attn_load<T, HD, NT, C>(a, chunk, h, b, nvalid, kv, active);
   double qv[AttnShape<T, HD, NT>::VEC];
   attn_query<T, HD, NT, C>(a, h, b, qv);
-  attn_compute<T, HD, NT, C>(a, chunk, h, b, nvalid, excl, qv, kv, s_o);
+  attn_compute<T, HD, NT, C>(a, chunk, h, b, nvalid, excl, qv, kv, s_o, active);
 }
 
-// Chunks [c0, c1) of head h, the next chunk's K and V requested while the
-// current one is computed.
-template <typename T, int HD, int NT, bool C, int FRESH>
+// Chunks [c0, c1) of head h (c0 < c1) by the G groups of the workgroup:
+// group g takes chunks c0 + g, c0 + g + G, ...; each group requests its next
+// chunk's K and V while the current one is computed.
+template <typename T, int HD, int NT, int G, bool C>
 __device__ __forceinline__ void attn_span(const AttnArgs& a, int c0, int c1, int h, int b,
                                           int nvalid, int excl, double* s_o) {
-  int newest = -1;
-  if constexpr (FRESH == KV_NEWEST) newest = (int)(ldg(a.pos + b) % a.cap);
+  static_assert(G >= 1 && G <= ATTN_MAX_GROUPS, "groups per workgroup");
+  const int g = tid() / NT;
+  const int iters = (c1 - c0 + G - 1) / G;
   KvChunk<T, HD, NT> ka, kb;
-  if (c0 < c1) attn_load<T, HD, NT, FRESH>(a, c0, h, b, nvalid, newest, ka);
+  int c = c0 + g;
+  attn_load<T, HD, NT, C>(a, c, h, b, nvalid, ka, c < c1);
   double qv[AttnShape<T, HD, NT>::VEC];
   attn_query<T, HD, NT, C>(a, h, b, qv);
-  for (int c = c0; c < c1; c += 2) {
-    if (c + 1 < c1) attn_load<T, HD, NT, FRESH>(a, c + 1, h, b, nvalid, newest, kb);
-    attn_compute<T, HD, NT, C>(a, c, h, b, nvalid, excl, qv, ka, s_o);
-    if (c + 1 >= c1) break;
-    if (c + 2 < c1) attn_load<T, HD, NT, FRESH>(a, c + 2, h, b, nvalid, newest, ka);
-    attn_compute<T, HD, NT, C>(a, c + 1, h, b, nvalid, excl, qv, kb, s_o);
+  for (int it = 0; it < iters; it += 2, c += 2 * G) {
+    attn_load<T, HD, NT, C>(a, c + G, h, b, nvalid, kb, c + G < c1);
+    attn_compute<T, HD, NT, C>(a, c, h, b, nvalid, excl, qv, ka, s_o, c < c1);
+    if (it + 1 >= iters) break;
+    attn_load<T, HD, NT, C>(a, c + 2 * G, h, b, nvalid, ka, c + 2 * G < c1);
+    attn_compute<T, HD, NT, C>(a, c + G, h, b, nvalid, excl, qv, kb, s_o, c + G < c1);
   }
 }
 
@@ -917,9 +966,7 @@ __device__ __forceinline__ void combine_item(const AttnArgs& a, int h, int b, in
   double mloc = -INFINITY;
   if (t < HD)
     for (int c = t; c < nchunks; c += HD) mloc = fmax(mloc, ld_f64<C>(parts + (size_t)c * (HD + 2)));
-#pragma unroll
-  for (int off = (HD < 64 ? HD : 64) / 2; off > 0; off >>= 1)
-    mloc = fmax(mloc, shfl_xor_d(mloc, off));
+  mloc = group_reduce<(HD < 64 ? HD : 64), true>(mloc);
   if (t < HD && (t & 63) == 0) s_m[t >> 6] = mloc;
   __syncthreads();
   double M = s_m[0];
@@ -955,7 +1002,21 @@ __device__ __forceinline__ void combine_staged(const AttnArgs& a, int h, int b, 
   const int t = tid();
   const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
   const int n = nchunks * (HD + 2);
-  for (int i = t; i < n; i += NT) s_part[i] = ld_f64<C>(parts + i);
+  // all loads first, then the LDS stores (one memory latency, not one per item)
+  constexpr int BATCH = 16;
+  for (int i0 = 0; i0 < n; i0 += BATCH * NT) {
+    double v[BATCH];
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int i = i0 + k * NT + t;
+      v[k] = ld_f64<C>(parts + (i < n ? i : 0));
+    }
+#pragma unroll
+    for (int k = 0; k < BATCH; ++k) {
+      const int i = i0 + k * NT + t;
+      if (i < n) s_part[i] = v[k];
+    }
+  }
   __syncthreads();
   constexpr int NW = HD / 64 > 0 ? HD / 64 : 1;
   __shared__ double s_m[NW];
@@ -963,9 +1024,7 @@ __device__ __forceinline__ void combine_staged(const AttnArgs& a, int h, int b, 
   double mloc = -INFINITY;
   if (t < HD)
     for (int c = t; c < nchunks; c += HD) mloc = fmax(mloc, s_part[(size_t)c * (HD + 2)]);
-#pragma unroll
-  for (int off = (HD < 64 ? HD : 64) / 2; off > 0; off >>= 1)
-    mloc = fmax(mloc, shfl_xor_d(mloc, off));
+  mloc = group_reduce<(HD < 64 ? HD : 64), true>(mloc);
   if (t < HD && (t & 63) == 0) s_m[t >> 6] = mloc;
   __syncthreads();
   double M = s_m[0];

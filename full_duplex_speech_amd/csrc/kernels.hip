@@ -192,7 +192,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   int nvalid, excl;
   window_of(a, b, nvalid, excl);
   if (chunk >= (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK) return;
-  attn_item<T, HD, 256, false, KV_NONE>(a, chunk, h, b, nvalid, excl, s_o);
+  attn_item<T, HD, 256, false>(a, chunk, h, b, nvalid, excl, s_o);
 }
 
 // Chunk merge of (slot blockIdx.y, head blockIdx.x); see combine_item.

@@ -198,9 +198,7 @@ __device__ __forceinline__ int reduce_token(const ArgPart* part, int n_tiles, in
 // the one-session residual epilogue writes).
 template <bool C>
 __device__ __forceinline__ void store_tile_ssq(double v, int row, int n_rows, double* ssq_out) {
-  double ss = v * v;
-#pragma unroll
-  for (int off = GEMV_SSQ_ROWS / 2; off > 0; off >>= 1) ss += shfl_xor_d(ss, off);
+  const double ss = group_reduce<GEMV_SSQ_ROWS>(v * v);
   if (row % GEMV_SSQ_ROWS == 0 && row < n_rows) st_f64<C>(ssq_out + row / GEMV_SSQ_ROWS, ss);
 }
 
@@ -358,8 +356,8 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
       unsigned* tickets = A.attn_ctr + (size_t)parity * A.H * 16;
       for (int item = wg; item < A.H * nspan; item += nwg) {
         const int h = item / nspan, j = item % nspan;
-        attn_span<T, HD, NT, true, KV_NEWEST>(at, j * nchunks / nspan, (j + 1) * nchunks / nspan, h,
-                                              0, nvalid, excl, s_o);
+        attn_span<T, HD, NT / 2, 2, true>(at, j * nchunks / nspan, (j + 1) * nchunks / nspan,
+                                            h, 0, nvalid, excl, s_o);
         if (nchunks > 1) {
           __shared__ int s_last;
           drain_stores();
@@ -403,8 +401,11 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
         AttnArgs at = A.d_attn;
         at.layer_off = (int64_t)l * A.d_layer_elems;
         at.scalar_nvalid = s + 1;
-        for (int h = wg; h < A.Hd; h += nwg)
-          attn_item<T, HDD, NT, true, KV_ALL>(at, 0, h, 0, s + 1, -1, s_o);
+        // two heads per workgroup, one per half
+        for (int h2 = wg; 2 * h2 < A.Hd; h2 += nwg) {
+          const int h = 2 * h2 + (int)(threadIdx.x / (NT / 2));
+          attn_item<T, HDD, NT / 2, true>(at, 0, h < A.Hd ? h : 0, 0, s + 1, -1, s_o, h < A.Hd);
+        }
       }
       if (grid_sync(g)) return;
       GEMV(PRO_DIRECT, EPI_RESID, d_o(s, l));
