@@ -584,15 +584,13 @@ struct GemvShape {
 };
 
 // The first weight batch of workgroup `wg` for the projection `a`, requested
-// ahead of time (before the grid barrier that precedes it) by every wave but
-// wave 0, which polls the barrier and so must not wait on these loads.
+// ahead of time (while the grid barrier that precedes it completes).
 template <typename T, int KW, int EPI, int U_>
 __device__ __forceinline__ void gemv_prefetch(const GemmArgs& a, int wg,
                                               u32x4 (&w)[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R]) {
   constexpr int R = GemvShape<KW, U_>::R, U = GemvShape<KW, U_>::U;
   const int t = tid();
-  const int wave = t >> 6;
-  if (wave != 0) load_wbatch<T, EPI, U, R>(a, wg, 0, t & 63, wave, w, wg < n_tiles_of(EPI, a.N));
+  load_wbatch<T, EPI, U, R>(a, wg, 0, t & 63, t >> 6, w, wg < n_tiles_of(EPI, a.N));
 }
 
 // Workgroup `wg` of `nwg` (KW waves) walks row tiles wg, wg+nwg, ... (16
@@ -602,9 +600,9 @@ __device__ __forceinline__ void gemv_prefetch(const GemmArgs& a, int wg,
 // l+64, ... of a row, so a wave reads each row in contiguous 1 KB pieces.
 // Weights stream in batches of U groups per lane and row, double-buffered: the
 // next batch (possibly of the next tile) is requested before the current one
-// is used. Each finished row is reduced over the 64 lanes by a butterfly;
-// wave 0 applies the epilogue to the tile's 16 rows. PRE: waves 1.. already
-// hold their first batch in `pre` (gemv_prefetch). The first group of the
+// is used. Each finished row is reduced over the 64 lanes; the wave that owns
+// it applies the epilogue (argmax partials: wave 0, per tile). PRE: the first
+// batch is already in `pre` (gemv_prefetch). The first group of the
 // input and (EPI_RESID) the residual rows of the first tile are requested
 // before the norm scale is computed. Every thread of the workgroup must call
 // this (it synchronises the workgroup).
@@ -628,7 +626,7 @@ __device__ __forceinline__ void gemv_core(
 
   int tile = wg;
   u32x4 wa[U][R], wb[U][R];
-  if (PRE && wave != 0) {
+  if (PRE) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll

@@ -581,11 +581,17 @@ int setup_step(moshi_ctx* c) {
   A.emb = embed_args(c);
   A.t_qkv = t_qkv_args(c, 0); A.t_o = t_o_args(c, 0); A.t_gu = t_gu_args(c, 0);
   A.t_dn = t_dn_args(c, 0); A.t_head = t_head_args(c); A.t_attn = t_attn_args(c, 0);
-  A.t_w = dt + o_tw; A.L = c->L; A.H = c->H; A.t_layer_elems = t_layer_elems(c);
+  A.L = c->L; A.H = c->H; A.t_layer_elems = t_layer_elems(c);
   A.d_in = d_in_args(c); A.d_qkv = d_qkv_args(c, 0, 0); A.d_o = d_o_args(c, 0, 0);
   A.d_gu = d_gu_args(c, 0, 0); A.d_dn = d_dn_args(c, 0, 0); A.d_head = d_head_args(c, 0);
   A.d_attn = d_attn_args(c, 0, 0);
-  A.d_w = dt + o_dw; A.d_norm = dt + o_dn; A.d_emb = dt + o_de; A.d_heads = dt + o_dh;
+  A.tab = dt; A.n_tab = (int)tab.size();
+  A.o_tw = (int)o_tw; A.o_dw = (int)o_dw; A.o_dn = (int)o_dn; A.o_de = (int)o_de;
+  A.o_dh = (int)o_dh;
+  // the pointer table goes to LDS after the scratch region
+  lds = (lds + 15) / 16 * 16;
+  A.tab_lds = (int)lds;
+  lds += tab.size() * sizeof(void*);
   A.S = c->S; A.Ld = c->Ld; A.Hd = c->Hd; A.Dd = c->Dd; A.Vt = c->Vt; A.Va = c->Va;
   A.d_layer_elems = d_layer_elems(c);
   A.pre = c->pre; A.y = c->y; A.ssq_d = c->ssq_d; A.apart = c->apart;
@@ -602,7 +608,8 @@ int setup_step(moshi_ctx* c) {
   A.bar = c->d_bar; A.abort = c->d_abort;
   CKD(c, dalloc(c, (void**)&c->d_step, sizeof(StepArgs)));
   CKD(c, hipMemcpy(c->d_step, &A, sizeof(StepArgs), hipMemcpyHostToDevice));
-  c->step_grid = grid;
+  c->step_grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);  // with the final LDS size
+  if (c->step_grid < 1 || c->step_grid > grid) return MOSHI_OK;
   c->step_lds = lds;
   c->persistent = true;
   return MOSHI_OK;

@@ -142,16 +142,11 @@ struct StepArgs {
   EmbedArgs emb;  // frames come with each launch
   GemmArgs t_qkv, t_o, t_gu, t_dn, t_head;
   AttnArgs t_attn;
-  const void* const* t_w;  // [L][6]: attn_norm, qkv, o, mlp_norm, gate_up, down
   int L, H;
   int64_t t_layer_elems;   // ring elements per layer of one slot (H * W * hd)
   // depformer
   GemmArgs d_in, d_qkv, d_o, d_gu, d_dn, d_head;
   AttnArgs d_attn;
-  const void* const* d_w;      // [S * Ld][4]: qkv, o, gate_up, down of (substep, layer)
-  const void* const* d_norm;   // [Ld][2]: attn_norm, mlp_norm
-  const void* const* d_emb;    // [S] previous-token tables
-  const void* const* d_heads;  // [S]
   int S, Ld, Hd, Dd, Vt, Va;
   int64_t d_layer_elems;       // depformer K/V elements per layer (Hd * S * hdd)
   const double* pre;           // [S * Dd] input projections of the hidden state
@@ -162,6 +157,15 @@ struct StepArgs {
   // bookkeeping
   int64_t* pos;                // slot 0 position (advanced at the end)
   const int* live;
+  // weight pointers, one table (copied to LDS at tab_lds bytes into the
+  // dynamic LDS when the kernel starts), with these sections:
+  //   o_tw: [L][6] attn_norm, qkv, o, mlp_norm, gate_up, down
+  //   o_dw: [S * Ld][4] qkv, o, gate_up, down of (substep, layer)
+  //   o_dn: [Ld][2] depformer attn_norm, mlp_norm
+  //   o_de: [S] previous-token tables;  o_dh: [S] heads
+  const void* const* tab;
+  int n_tab, tab_lds;
+  int o_tw, o_dw, o_dn, o_de, o_dh;
   unsigned* bar;               // 2 sets of STEP_BAR_WORDS barrier counters
   unsigned* attn_ctr;          // 2 sets of H * 16 per-head attention tickets
   int* abort;                  // set when a barrier wait times out

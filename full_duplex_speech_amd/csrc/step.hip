@@ -61,6 +61,21 @@ struct Grid {
   unsigned n_xcc;  // XCDs with at least one workgroup
 };
 
+// A value every lane holds equally (read from LDS), as a wave-uniform (scalar)
+// value.
+template <typename X>
+__device__ __forceinline__ X uni(const X& v) {
+  static_assert(sizeof(X) % 4 == 0, "word-sized fields");
+  struct Words {
+    uint32_t w[sizeof(X) / 4];
+  };
+  const Words in = __builtin_bit_cast(Words, v);
+  Words out;
+#pragma unroll
+  for (int i = 0; i < (int)(sizeof(X) / 4); ++i) out.w[i] = __builtin_amdgcn_readfirstlane(in.w[i]);
+  return __builtin_bit_cast(X, out);
+}
+
 // Make this thread's stores visible at agent scope before arriving.
 __device__ __forceinline__ void drain_stores() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -83,17 +98,25 @@ __device__ __forceinline__ int poll_until(unsigned* ctr, unsigned target, int* a
   return 0;
 }
 
-// Grid barrier. Every thread of every workgroup calls it, after
-// drain_stores(); true = abort. Loads still in flight (weight prefetches)
-// stay in flight: only thread 0 of wave 0 touches the counters, and wave 0
-// issues no prefetch.
-__device__ __forceinline__ bool grid_sync_drained(Grid& g) {
-  __shared__ int s_leave;
-  __syncthreads();
+// Grid barrier in two halves, so that loads can be issued in between:
+// grid_arrive (after drain_stores() and a workgroup barrier) counts this
+// workgroup in; grid_wait completes the count and waits. Loads issued between
+// the two are younger than the arrival atomic, so reading its result does not
+// wait for them; the polls do, but those loads (a weight prefetch) land well
+// before the grid does. Every thread of every workgroup calls both; true =
+// abort.
+__device__ __forceinline__ unsigned grid_arrive(Grid& g) {
   g.idx += 1;
+  unsigned old = 0;
+  if (threadIdx.x == 0)
+    old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_LOCAL + 32 * g.xcc, 1u, MOSHI_RLX,
+                                 MOSHI_AGT);
+  return old;
+}
+
+__device__ __forceinline__ bool grid_wait(Grid& g, unsigned old) {
+  __shared__ int s_leave;
   if (threadIdx.x == 0) {
-    const unsigned old =
-        __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_LOCAL + 32 * g.xcc, 1u, MOSHI_RLX, MOSHI_AGT);
     if (old + 1 == g.idx * g.xcc_n)
       __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_GLOBAL, 1u, MOSHI_RLX, MOSHI_AGT);
     s_leave = poll_until(g.set + BW_GLOBAL, g.idx * g.n_xcc, g.abort);
@@ -105,7 +128,9 @@ __device__ __forceinline__ bool grid_sync_drained(Grid& g) {
 
 __device__ __forceinline__ bool grid_sync(Grid& g) {
   drain_stores();
-  return grid_sync_drained(g);
+  __syncthreads();
+  const unsigned old = grid_arrive(g);
+  return grid_wait(g, old);
 }
 
 // Start of a launch: clear the other counter set (used by the next launch;
@@ -204,58 +229,73 @@ __device__ __forceinline__ void store_tile_ssq(double v, int row, int n_rows, do
 
 // x = E_text[c0] + sum_k E_audio_k[c_k] for slot 0; NT rows per item.
 // A code outside its table is clamped into range and flagged for the host.
+// `a` is the LDS copy; its fields are read one by one (the table array is
+// indexed by channel and must not be copied into registers).
 template <typename T>
 __device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frames, int wg,
                                             int nwg) {
-  for (int item = wg; item * NT < a.D; item += nwg) {
+  const int D = uni(a.D), n_ch = uni(a.n_ch);
+  const int rows_text = uni(a.rows_text), rows_audio = uni(a.rows_audio);
+  double* x = uni(a.x);
+  double* ssq_out = uni(a.ssq_out);
+  int* bad_code = uni(a.bad_code);
+  for (int item = wg; item * NT < D; item += nwg) {
     const int row = item * NT + tid();
     double acc = 0.0;
-    if (row < a.D) {
-      for (int c0 = 0; c0 < a.n_ch; c0 += 8) {
+    if (row < D) {
+      for (int c0 = 0; c0 < n_ch; c0 += 8) {
         double v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int c = c0 + j;
           v[j] = 0.0;
-          if (c < a.n_ch) {
+          if (c < n_ch) {
             int code = ldg(frames + c);
-            const int rows = (c == 0) ? a.rows_text : a.rows_audio;
+            const int rows = (c == 0) ? rows_text : rows_audio;
             if (code < 0 || code >= rows) {
-              if (row == 0) atomicOr(a.bad_code, 1);
+              if (row == 0) atomicOr(bad_code, 1);
               code = code < 0 ? 0 : rows - 1;
             }
-            v[j] = to_d(ldg((const T*)a.tables[c] + (size_t)code * a.D + row));
+            const T* table = (const T*)uni(a.tables[c]);
+            v[j] = to_d(ldg(table + (size_t)code * D + row));
           }
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (c0 + j < a.n_ch) acc += v[j];
+          if (c0 + j < n_ch) acc += v[j];
       }
-      st_f64<true>(a.x + row, acc);
+      st_f64<true>(x + row, acc);
     }
-    store_tile_ssq<true>(acc, row, a.D, a.ssq_out);
+    store_tile_ssq<true>(acc, row, D, ssq_out);
   }
 }
 
 // Depformer substep entry for slot 0: the previous head's token (the text
 // token at s = 0), stored as an output by workgroup 0, then
 // y = W_in[s] hidden + E_s[token].
+struct EntryPhase {
+  const ArgPart* apart;
+  const double* pre;
+  double* y;
+  double* ssq;
+  const void* table;
+  int Dd, prev_rows;
+};
 template <typename T>
-__device__ __forceinline__ void entry_phase(const StepArgs& A, int s, int* tok_out, int wg,
+__device__ __forceinline__ void entry_phase(const EntryPhase& E, int s, int* tok_out, int wg,
                                             int nwg) {
-  if (wg * NT >= A.Dd) return;  // no rows here
-  const int prev_rows = s == 0 ? A.Vt : A.Va;
-  const int tok = reduce_token(A.apart, (prev_rows + 15) / 16, prev_rows);
+  if (wg * NT >= E.Dd) return;  // no rows here
+  const int tok = reduce_token(E.apart, (E.prev_rows + 15) / 16, E.prev_rows);
   if (wg == 0 && threadIdx.x == 0) st_i32<true>(tok_out, tok);
-  const T* table = (const T*)A.d_emb[s];
-  for (int item = wg; item * NT < A.Dd; item += nwg) {
+  const T* table = (const T*)E.table;
+  for (int item = wg; item * NT < E.Dd; item += nwg) {
     const int row = item * NT + tid();
     double acc = 0.0;
-    if (row < A.Dd) {
-      acc = ld_f64<true>(A.pre + (size_t)s * A.Dd + row) + to_d(ldg(table + (size_t)tok * A.Dd + row));
-      st_f64<true>(A.y + row, acc);
+    if (row < E.Dd) {
+      acc = ld_f64<true>(E.pre + (size_t)s * E.Dd + row) + to_d(ldg(table + (size_t)tok * E.Dd + row));
+      st_f64<true>(E.y + row, acc);
     }
-    store_tile_ssq<true>(acc, row, A.Dd, A.ssq_d);
+    store_tile_ssq<true>(acc, row, E.Dd, E.ssq);
   }
 }
 
@@ -266,72 +306,98 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   extern __shared__ __align__(16) unsigned char s_dyn[];  // GEMV input or attention scratch
   T* xs = (T*)s_dyn;
   double* s_o = (double*)s_dyn;
-  const StepArgs& A = *P;
+  // The argument block and the weight pointers live in LDS for the whole
+  // launch: every operation reads its arguments there (as wave-uniform
+  // values) instead of from global memory after each barrier.
+  __shared__ __align__(16) StepArgs sA;
+  {
+    const uint32_t* src = (const uint32_t*)P;
+    uint32_t* dst = (uint32_t*)&sA;
+    for (int i = tid(); i < (int)(sizeof(StepArgs) / 4); i += NT) dst[i] = ldg(src + i);
+  }
+  __syncthreads();
+  const StepArgs& A = sA;
+  const void** s_tab = (const void**)(s_dyn + uni(A.tab_lds));
+  {
+    const void* const* tab = uni(A.tab);
+    const int n_tab = uni(A.n_tab);
+    for (int i = tid(); i < n_tab; i += NT) s_tab[i] = ldg(tab + i);
+  }
+  __syncthreads();
+  auto tab = [&](int i) { return uni(s_tab[i]); };
   const int wg = blockIdx.x, nwg = gridDim.x;
+  const int L = uni(A.L), H = uni(A.H), S = uni(A.S), Ld = uni(A.Ld), Hd = uni(A.Hd);
+  const int Va = uni(A.Va);
+  const int o_tw = uni(A.o_tw), o_dw = uni(A.o_dw), o_dn = uni(A.o_dn), o_de = uni(A.o_de),
+            o_dh = uni(A.o_dh);
+  const int64_t t_lel = uni(A.t_layer_elems), d_lel = uni(A.d_layer_elems);
   Grid g;
-  if (grid_init(g, A.bar, A.attn_ctr, A.H, parity, A.abort, trace)) return;
+  if (grid_init(g, uni(A.bar), uni(A.attn_ctr), H, parity, uni(A.abort), trace)) return;
   // first weight batch of the next projection, requested before each barrier
   u32x4 pf[GU][16 / KW];
 #define PREFETCH_SYNC(EPI_, args_)                         \
   do {                                                     \
+    const GemmArgs na_ = (args_);                          \
     drain_stores();                                        \
-    gemv_prefetch<T, KW, EPI_, GU>((args_), wg, pf);       \
-    if (grid_sync_drained(g)) return;                      \
+    __syncthreads();                                       \
+    const unsigned old_ = grid_arrive(g);                  \
+    gemv_prefetch<T, KW, EPI_, GU>(na_, wg, pf);           \
+    if (grid_wait(g, old_)) return;                        \
   } while (0)
 #define GEMV(PRO_, EPI_, args_) gemv_core<T, KW, PRO_, EPI_, true, GU, true>((args_), wg, nwg, xs, pf)
 
   // per-layer argument blocks
   auto t_qkv = [&](int l) {
-    GemmArgs a = A.t_qkv;
-    a.gain = A.t_w[(size_t)l * 6 + 0];
-    a.W = A.t_w[(size_t)l * 6 + 1];
-    a.layer_off = (int64_t)l * A.t_layer_elems;
+    GemmArgs a = uni(A.t_qkv);
+    a.gain = tab(o_tw + l * 6 + 0);
+    a.W = tab(o_tw + l * 6 + 1);
+    a.layer_off = (int64_t)l * t_lel;
     return a;
   };
   auto t_o = [&](int l) {
-    GemmArgs a = A.t_o;
-    a.W = A.t_w[(size_t)l * 6 + 2];
+    GemmArgs a = uni(A.t_o);
+    a.W = tab(o_tw + l * 6 + 2);
     return a;
   };
   auto t_gu = [&](int l) {
-    GemmArgs a = A.t_gu;
-    a.gain = A.t_w[(size_t)l * 6 + 3];
-    a.W = A.t_w[(size_t)l * 6 + 4];
+    GemmArgs a = uni(A.t_gu);
+    a.gain = tab(o_tw + l * 6 + 3);
+    a.W = tab(o_tw + l * 6 + 4);
     return a;
   };
   auto t_dn = [&](int l) {
-    GemmArgs a = A.t_dn;
-    a.W = A.t_w[(size_t)l * 6 + 5];
+    GemmArgs a = uni(A.t_dn);
+    a.W = tab(o_tw + l * 6 + 5);
     return a;
   };
   auto d_qkv = [&](int s, int l) {
-    GemmArgs a = A.d_qkv;
-    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 0];
-    a.gain = A.d_norm[(size_t)l * 2 + 0];
+    GemmArgs a = uni(A.d_qkv);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 0);
+    a.gain = tab(o_dn + l * 2 + 0);
     a.scalar_widx = s;
-    a.layer_off = (int64_t)l * A.d_layer_elems;
+    a.layer_off = (int64_t)l * d_lel;
     return a;
   };
   auto d_o = [&](int s, int l) {
-    GemmArgs a = A.d_o;
-    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 1];
+    GemmArgs a = uni(A.d_o);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 1);
     return a;
   };
   auto d_gu = [&](int s, int l) {
-    GemmArgs a = A.d_gu;
-    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 2];
-    a.gain = A.d_norm[(size_t)l * 2 + 1];
+    GemmArgs a = uni(A.d_gu);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 2);
+    a.gain = tab(o_dn + l * 2 + 1);
     return a;
   };
   auto d_dn = [&](int s, int l) {
-    GemmArgs a = A.d_dn;
-    a.W = A.d_w[((size_t)s * A.Ld + l) * 4 + 3];
+    GemmArgs a = uni(A.d_dn);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 3);
     return a;
   };
   auto d_head = [&](int s) {
-    GemmArgs a = A.d_head;
-    a.W = A.d_heads[s];
-    a.logits = A.audio_logits + (size_t)s * A.Va;
+    GemmArgs a = uni(A.d_head);
+    a.W = tab(o_dh + s);
+    a.logits = uni(A.audio_logits) + (size_t)s * Va;
     return a;
   };
 
@@ -341,20 +407,20 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
 
   // ---- temporal layers ----
   int nvalid, excl;
-  window_of(A.t_attn, 0, nvalid, excl);
+  window_of(uni(A.t_attn), 0, nvalid, excl);
   const int nchunks = (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK;
-  int nspan = nwg / A.H;
+  int nspan = nwg / H;
   nspan = nspan < 1 ? 1 : (nspan > nchunks ? nchunks : nspan);
-  for (int l = 0; l < A.L; ++l) {
+  for (int l = 0; l < L; ++l) {
     GEMV(PRO_NORM, EPI_QKV, t_qkv(l));
     PREFETCH_SYNC(EPI_RESID, t_o(l));  // held through the attention
     {
       // each head's chunks split into nspan contiguous spans, one per
       // workgroup; the workgroup finishing a head's last span merges it
-      AttnArgs at = A.t_attn;
-      at.layer_off = (int64_t)l * A.t_layer_elems;
-      unsigned* tickets = A.attn_ctr + (size_t)parity * A.H * 16;
-      for (int item = wg; item < A.H * nspan; item += nwg) {
+      AttnArgs at = uni(A.t_attn);
+      at.layer_off = (int64_t)l * t_lel;
+      unsigned* tickets = uni(A.attn_ctr) + (size_t)parity * H * 16;
+      for (int item = wg; item < H * nspan; item += nwg) {
         const int h = item / nspan, j = item % nspan;
         attn_span<T, HD, NT / 2, 2, true>(at, j * nchunks / nspan, (j + 1) * nchunks / nspan,
                                             h, 0, nvalid, excl, s_o);
@@ -378,33 +444,43 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     GEMV(PRO_NORM, EPI_SWIGLU, t_gu(l));
     PREFETCH_SYNC(EPI_RESID, t_dn(l));
     GEMV(PRO_DIRECT, EPI_RESID, t_dn(l));
-    if (l + 1 < A.L)
+    if (l + 1 < L)
       PREFETCH_SYNC(EPI_QKV, t_qkv(l + 1));
     else
-      PREFETCH_SYNC(EPI_ARGMAX, A.t_head);
+      PREFETCH_SYNC(EPI_ARGMAX, uni(A.t_head));
   }
   // ---- final norm -> hidden, text head (argmax partials) ----
-  GEMV(PRO_NORM, EPI_ARGMAX, A.t_head);
-  PREFETCH_SYNC(EPI_STORE, A.d_in);
+  GEMV(PRO_NORM, EPI_ARGMAX, uni(A.t_head));
+  PREFETCH_SYNC(EPI_STORE, uni(A.d_in));
   // ---- depformer input projections of all substeps ----
-  GEMV(PRO_DIRECT, EPI_STORE, A.d_in);
+  GEMV(PRO_DIRECT, EPI_STORE, uni(A.d_in));
   PREFETCH_SYNC(EPI_QKV, d_qkv(0, 0));  // held through the entry
 
   // ---- 16 substeps ----
-  for (int s = 0; s < A.S; ++s) {
-    entry_phase<T>(A, s, s == 0 ? text_out : codes_out + (s - 1), wg, nwg);
+  for (int s = 0; s < S; ++s) {
+    {
+      EntryPhase E;
+      E.apart = uni(A.apart);
+      E.pre = uni(A.pre);
+      E.y = uni(A.y);
+      E.ssq = uni(A.ssq_d);
+      E.table = tab(o_de + s);
+      E.Dd = uni(A.Dd);
+      E.prev_rows = s == 0 ? uni(A.Vt) : Va;
+      entry_phase<T>(E, s, s == 0 ? text_out : codes_out + (s - 1), wg, nwg);
+    }
     if (grid_sync(g)) return;
-    for (int l = 0; l < A.Ld; ++l) {
+    for (int l = 0; l < Ld; ++l) {
       GEMV(PRO_NORM, EPI_QKV, d_qkv(s, l));
       PREFETCH_SYNC(EPI_RESID, d_o(s, l));  // held through the attention
       {
-        AttnArgs at = A.d_attn;
-        at.layer_off = (int64_t)l * A.d_layer_elems;
+        AttnArgs at = uni(A.d_attn);
+        at.layer_off = (int64_t)l * d_lel;
         at.scalar_nvalid = s + 1;
         // two heads per workgroup, one per half
-        for (int h2 = wg; 2 * h2 < A.Hd; h2 += nwg) {
+        for (int h2 = wg; 2 * h2 < Hd; h2 += nwg) {
           const int h = 2 * h2 + (int)(threadIdx.x / (NT / 2));
-          attn_item<T, HDD, NT / 2, true>(at, 0, h < A.Hd ? h : 0, 0, s + 1, -1, s_o, h < A.Hd);
+          attn_item<T, HDD, NT / 2, true>(at, 0, h < Hd ? h : 0, 0, s + 1, -1, s_o, h < Hd);
         }
       }
       if (grid_sync(g)) return;
@@ -413,13 +489,13 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
       GEMV(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
       PREFETCH_SYNC(EPI_RESID, d_dn(s, l));
       GEMV(PRO_DIRECT, EPI_RESID, d_dn(s, l));
-      if (l + 1 < A.Ld)
+      if (l + 1 < Ld)
         PREFETCH_SYNC(EPI_QKV, d_qkv(s, l + 1));
       else
         PREFETCH_SYNC(EPI_ARGMAX, d_head(s));
     }
     GEMV(PRO_CAST, EPI_ARGMAX, d_head(s));
-    if (s + 1 < A.S)
+    if (s + 1 < S)
       PREFETCH_SYNC(EPI_QKV, d_qkv(s + 1, 0));  // held through the entry
     else if (grid_sync(g))
       return;
@@ -428,10 +504,11 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
 #undef PREFETCH_SYNC
   // ---- last code, next position ----
   if (wg == 0) {
-    const int tok = reduce_token(A.apart, (A.Va + 15) / 16, A.Va);
+    const int tok = reduce_token(uni(A.apart), (Va + 15) / 16, Va);
     if (threadIdx.x == 0) {
-      *(MOSHI_GLB int*)(codes_out + A.S - 1) = tok;
-      if (ldg(A.live)) *(MOSHI_GLB int64_t*)A.pos += 1;
+      *(MOSHI_GLB int*)(codes_out + S - 1) = tok;
+      int64_t* pos = uni(A.pos);
+      if (ldg(uni(A.live))) *(MOSHI_GLB int64_t*)pos += 1;
     }
   }
   if (trace != nullptr && wg == 0 && threadIdx.x == 0) *(MOSHI_GLB uint64_t*)(trace + g.idx + 1) = wall_clock64();
