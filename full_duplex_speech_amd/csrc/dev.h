@@ -649,24 +649,27 @@ __device__ __forceinline__ void gemv_core(
     }
   }
   // input vector -> LDS (rounded to the model dtype); the first group's raw
-  // values are requested before the norm scale
-  XRaw<T, PRO, C> x0;
-  if (t < ngroups) load_x_raw<T, PRO, C>(a, 0, t * VEC, x0);
-  double rs = 1.0;
-  if constexpr (PRO == PRO_NORM) rs = rms_scale<C>(a, 0, s_tmp, NTH);
-  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && wg == 0;
-  for (int gi = t; gi < ngroups; gi += NTH) {
-    double xv[VEC];
-    u32x4 packed;
-    if (gi == t) {
-      finish_x<T, PRO, C>(x0, rs, xv, &packed);
-    } else {
-      XRaw<T, PRO, C> xr;
-      load_x_raw<T, PRO, C>(a, 0, gi * VEC, xr);
-      finish_x<T, PRO, C>(xr, rs, xv, &packed);
+  // values are requested before the norm scale. PRO_LDS: the caller has
+  // already put it there.
+  if constexpr (PRO != PRO_LDS) {
+    XRaw<T, PRO, C> x0;
+    if (t < ngroups) load_x_raw<T, PRO, C>(a, 0, t * VEC, x0);
+    double rs = 1.0;
+    if constexpr (PRO == PRO_NORM) rs = rms_scale<C>(a, 0, s_tmp, NTH);
+    const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && wg == 0;
+    for (int gi = t; gi < ngroups; gi += NTH) {
+      double xv[VEC];
+      u32x4 packed;
+      if (gi == t) {
+        finish_x<T, PRO, C>(x0, rs, xv, &packed);
+      } else {
+        XRaw<T, PRO, C> xr;
+        load_x_raw<T, PRO, C>(a, 0, gi * VEC, xr);
+        finish_x<T, PRO, C>(xr, rs, xv, &packed);
+      }
+      *(u32x4*)(xs + (size_t)gi * VEC) = packed;
+      if (write_xn) st_grp<C>((T*)a.xn_out + (size_t)gi * VEC, packed);
     }
-    *(u32x4*)(xs + (size_t)gi * VEC) = packed;
-    if (write_xn) st_grp<C>((T*)a.xn_out + (size_t)gi * VEC, packed);
   }
   __syncthreads();
   if (tile < ntiles) {
@@ -1043,6 +1046,119 @@ __device__ __forceinline__ void combine_staged(const AttnArgs& a, int h, int b, 
     }
     const double ov = L > 0.0 ? O / L : 0.0;
     store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov, 1);
+  }
+  __syncthreads();
+}
+
+// Depformer attention (all heads of slot b, keys 0 .. nvalid-1, nvalid <=
+// DEP_MAX_KEYS) by one workgroup of NTH threads: wave w takes heads w, w + NW,
+// ..., two at a time (every load of both heads is requested before either is
+// used). Scores: TK lanes per key, fp64 dot products reduced in the lanes;
+// softmax over the keys in fp64; p.V: one lane per output dim, an fp64 fma
+// chain over the keys in order. The rounded outputs go to LDS `lds_out` (the
+// next projection's input, in the step kernel) or, if it is null, to
+// a.o_out. C: the K/V were written during the running kernel (coherent
+// loads). Every thread of the workgroup calls it.
+constexpr int DEP_MAX_KEYS = DEP_MAX_KEYS_HOST;
+template <typename T, int HD, int NTH, bool C>
+__device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int n_heads, int nvalid,
+                                              T* lds_out) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int TK = HD / VEC;        // lanes per key for the scores
+  constexpr int KPW = 64 / TK;        // keys per wave pass
+  constexpr int NP = (DEP_MAX_KEYS + KPW - 1) / KPW;
+  constexpr int NW = NTH / 64;
+  constexpr int DPL = HD > 64 ? HD / 64 : 1;  // output dims per lane
+  constexpr int NH = 2;                        // heads per wave at a time
+  static_assert(TK <= 64 && 64 % TK == 0, "head dim");
+  __shared__ double s_sc[NW][NH][64];
+  const int t = tid();
+  const int lane = t & 63, w = t >> 6;
+  const int kd = lane % TK, kq = lane / TK;
+  const double scale = 1.0 / sqrt((double)HD);
+  for (int h0 = w; h0 < n_heads; h0 += NH * NW) {
+    u32x4 kw[NH][NP];
+    uint32_t vr[NH][DEP_MAX_KEYS][DPL];
+    double qv[NH][VEC];
+    // every load of the NH heads first (heads past n_heads read head 0)
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      const int h = h0 + k * NW < n_heads ? h0 + k * NW : 0;
+      const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
+      const T* kbase = (const T*)a.ring_k + base;
+      const T* vbase = (const T*)a.ring_v + base;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int j = p * KPW + kq;
+        const int jc = j < nvalid ? j : 0;
+        const uint32_t off = (uint32_t)(((size_t)jc * HD + kd * VEC) * sizeof(T));
+        if constexpr (C) kw[k][p] = ld16_coh(kbase, off);
+        else kw[k][p] = ld16((const char*)kbase + off);
+      }
+#pragma unroll
+      for (int j = 0; j < DEP_MAX_KEYS; ++j) {
+        const int jc = j < nvalid ? j : 0;
+#pragma unroll
+        for (int i = 0; i < DPL; ++i) {
+          const int dd = (lane + 64 * i) < HD ? lane + 64 * i : 0;
+          const T* vp = vbase + (size_t)jc * HD + dd;
+          if constexpr (sizeof(T) == 2) {
+            vr[k][j][i] = C ? (uint32_t)__hip_atomic_load((MOSHI_GLB uint16_t*)vp, MOSHI_RLX, MOSHI_AGT)
+                            : (uint32_t)ldg((const uint16_t*)vp);
+          } else {
+            vr[k][j][i] = C ? __hip_atomic_load((MOSHI_GLB uint32_t*)vp, MOSHI_RLX, MOSHI_AGT)
+                            : ldg((const uint32_t*)vp);
+          }
+        }
+      }
+      const double* qp = a.q + (size_t)b * a.ldq + h * HD + kd * VEC;
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qv[k][e] = ld_f64<C>(qp + e);
+    }
+#pragma unroll
+    for (int k = 0; k < NH; ++k) {
+      const int h = h0 + k * NW;
+      double* sp = s_sc[w][k];
+      // scores
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        double kv_[VEC];
+        widen<T>(kw[k][p], kv_);
+        double d = 0.0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) d = fma(qv[k][e], kv_[e], d);
+        d = group_reduce<TK>(d);
+        const int j = p * KPW + kq;
+        if (kd == 0 && j < DEP_MAX_KEYS) sp[j] = d * scale;
+      }
+      // softmax over the valid keys
+      const double sv = lane < nvalid ? sp[lane] : -INFINITY;
+      const double m = group_reduce<64, true>(sv);
+      const double pj = (sv == -INFINITY) ? 0.0 : exp(sv - m);
+      const double l = group_reduce<64>(pj);
+      sp[lane] = pj;
+      // p.V
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) {
+        double od = 0.0;
+#pragma unroll
+        for (int j = 0; j < DEP_MAX_KEYS; ++j) {
+          if (j < nvalid) {
+            const double vv = sizeof(T) == 2 ? (double)__uint_as_float(vr[k][j][i] << 16)
+                                             : (double)__uint_as_float(vr[k][j][i]);
+            od = fma(sp[j], vv, od);
+          }
+        }
+        const int dd = lane + 64 * i;
+        if (h < n_heads && dd < HD) {
+          const double ov = l > 0.0 ? od / l : 0.0;
+          if (lds_out != nullptr)
+            lds_out[h * HD + dd] = round_to<T>(ov);
+          else
+            store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + dd, &ov, 1);
+        }
+      }
+    }
   }
   __syncthreads();
 }

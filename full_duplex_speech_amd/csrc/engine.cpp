@@ -491,8 +491,10 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
       }
       {
         AttnArgs a = d_attn_args(c, s, l);
-        e = run(c, KC_D_ATTN, nlive * (s + 1) * 2.0 * Dd * es,
-                [&] { return launch_attn(dt, c->hdd, a, B, c->stream); });
+        e = run(c, KC_D_ATTN, nlive * (s + 1) * 2.0 * Dd * es, [&] {
+          return S <= DEP_MAX_KEYS_HOST ? launch_dep_attn(dt, c->hdd, a, B, c->stream)
+                                        : launch_attn(dt, c->hdd, a, B, c->stream);
+        });
         if (e != hipSuccess) return e;
       }
       {
@@ -532,7 +534,8 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
 // it (the per-operation kernels are used then).
 int setup_step(moshi_ctx* c) {
   const char* env = getenv("MOSHI_STEP_KERNEL");
-  if (c->B != 1 || (env && env[0] == '0') || !step_supported(c->dtype, c->hd, c->hdd))
+  if (c->B != 1 || (env && env[0] == '0') || !step_supported(c->dtype, c->hd, c->hdd) ||
+      c->S > DEP_MAX_KEYS_HOST)
     return MOSHI_OK;
   const size_t es = c->esz, vec = es == 2 ? 8 : 4;
   auto attn_lds = [&](int hd) { return (STEP_THREADS / (hd / vec)) * (size_t)(hd + 1) * 8; };
@@ -927,7 +930,7 @@ int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vect
     std::vector<double> by;
     for (size_t i = 0; i < c->ev_class.size(); ++i) {
       const int k = c->ev_class[i];
-      if (k == KC_ARGMAX || k == KC_T_COMBINE) continue;
+      if (k == KC_ARGMAX || k == KC_T_COMBINE || k == KC_D_ATTN) continue;
       cls.push_back(k);
       by.push_back(c->ev_bytes[i]);
     }

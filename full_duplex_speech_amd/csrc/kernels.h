@@ -19,6 +19,7 @@ enum Prologue {
   PRO_DIRECT = 0,  // X already stored in the model dtype [B][ldx]
   PRO_NORM = 1,    // X = round(x * rms_scale * gain): x fp64 [B][ldx] + per-tile sums of squares
   PRO_CAST = 2,    // X = round(x): x fp64 [B][ldx], no scaling
+  PRO_LDS = 3,     // (one session, step kernel) the caller has built X in LDS
 };
 
 // What a projection kernel does with its 16-row output tile.
@@ -203,6 +204,10 @@ int gemm_kw(int dtype, int B, int K);
 // [B][K] buffer: the rounded input vectors are written there first.
 hipError_t launch_gemm(int dtype, int kw, int pro, int epi, const GemmArgs& a, hipStream_t st);
 hipError_t launch_attn(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st);
+// Depformer attention over a.scalar_nvalid <= DEP_MAX_KEYS entries, one
+// workgroup per slot, every head.
+hipError_t launch_dep_attn(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st);
+constexpr int DEP_MAX_KEYS_HOST = 16;  // equals DEP_MAX_KEYS in dev.h
 // Merges the per-chunk partials of every (slot, head) with more than one chunk.
 hipError_t launch_attn_combine(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st);
 // tok[b*stride] = argmax over the per-tile partials of column b (lowest index on ties).

@@ -195,6 +195,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
   attn_item<T, HD, 256, false>(a, chunk, h, b, nvalid, excl, s_o);
 }
 
+// Depformer attention of slot blockIdx.x, every head (see dep_attention).
+template <typename T, int HD>
+__global__ __launch_bounds__(512) void dep_attn_kernel(AttnArgs a) {
+  const int b = blockIdx.x;
+  if (!ldg(a.live + b)) return;
+  dep_attention<T, HD, 512, false>(a, b, a.n_heads, a.scalar_nvalid, nullptr);
+}
+
 // Chunk merge of (slot blockIdx.y, head blockIdx.x); see combine_item.
 template <typename T, int HD>
 __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
@@ -441,6 +449,23 @@ static hipError_t launch_attn_t(int hd, const AttnArgs& a, int B, hipStream_t st
 
 hipError_t launch_attn(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st) {
   return dtype == DT_BF16 ? launch_attn_t<__bf16>(hd, a, B, st) : launch_attn_t<float>(hd, a, B, st);
+}
+
+template <typename T>
+static hipError_t launch_dep_attn_t(int hd, const AttnArgs& a, int B, hipStream_t st) {
+  if (a.scalar_nvalid < 1 || a.scalar_nvalid > DEP_MAX_KEYS) return hipErrorInvalidValue;
+  switch (hd) {
+    case 32: hipLaunchKernelGGL((dep_attn_kernel<T, 32>), dim3(B), dim3(512), 0, st, a); break;
+    case 64: hipLaunchKernelGGL((dep_attn_kernel<T, 64>), dim3(B), dim3(512), 0, st, a); break;
+    case 128: hipLaunchKernelGGL((dep_attn_kernel<T, 128>), dim3(B), dim3(512), 0, st, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dep_attn(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st) {
+  return dtype == DT_BF16 ? launch_dep_attn_t<__bf16>(hd, a, B, st)
+                          : launch_dep_attn_t<float>(hd, a, B, st);
 }
 
 template <typename T>

@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   auto tab = [&](int i) { return uni(s_tab[i]); };
   const int wg = blockIdx.x, nwg = gridDim.x;
   const int L = uni(A.L), H = uni(A.H), S = uni(A.S), Ld = uni(A.Ld), Hd = uni(A.Hd);
-  const int Va = uni(A.Va);
+  const int Va = uni(A.Va), Dd = uni(A.Dd);
   const int o_tw = uni(A.o_tw), o_dw = uni(A.o_dw), o_dn = uni(A.o_dn), o_de = uni(A.o_de),
             o_dh = uni(A.o_dh);
   const int64_t t_lel = uni(A.t_layer_elems), d_lel = uni(A.d_layer_elems);
@@ -465,26 +465,22 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
       E.y = uni(A.y);
       E.ssq = uni(A.ssq_d);
       E.table = tab(o_de + s);
-      E.Dd = uni(A.Dd);
+      E.Dd = Dd;
       E.prev_rows = s == 0 ? uni(A.Vt) : Va;
       entry_phase<T>(E, s, s == 0 ? text_out : codes_out + (s - 1), wg, nwg);
     }
     if (grid_sync(g)) return;
     for (int l = 0; l < Ld; ++l) {
       GEMV(PRO_NORM, EPI_QKV, d_qkv(s, l));
-      PREFETCH_SYNC(EPI_RESID, d_o(s, l));  // held through the attention
+      PREFETCH_SYNC(EPI_RESID, d_o(s, l));
       {
+        // every workgroup with output-projection rows computes the attention
+        // of all heads itself, straight into the projection's LDS input
         AttnArgs at = uni(A.d_attn);
         at.layer_off = (int64_t)l * d_lel;
-        at.scalar_nvalid = s + 1;
-        // two heads per workgroup, one per half
-        for (int h2 = wg; 2 * h2 < Hd; h2 += nwg) {
-          const int h = 2 * h2 + (int)(threadIdx.x / (NT / 2));
-          attn_item<T, HDD, NT / 2, true>(at, 0, h < Hd ? h : 0, 0, s + 1, -1, s_o, h < Hd);
-        }
+        if (wg < (Dd + 15) / 16) dep_attention<T, HDD, NT, true>(at, 0, Hd, s + 1, xs);
       }
-      if (grid_sync(g)) return;
-      GEMV(PRO_DIRECT, EPI_RESID, d_o(s, l));
+      GEMV(PRO_LDS, EPI_RESID, d_o(s, l));
       PREFETCH_SYNC(EPI_SWIGLU, d_gu(s, l));
       GEMV(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
       PREFETCH_SYNC(EPI_RESID, d_dn(s, l));
