@@ -928,11 +928,16 @@ int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vect
     c->dry = false;
     std::vector<int> cls;
     std::vector<double> by;
+    double carry = 0.0;  // bytes of an operation folded into the next one
     for (size_t i = 0; i < c->ev_class.size(); ++i) {
       const int k = c->ev_class[i];
-      if (k == KC_ARGMAX || k == KC_T_COMBINE || k == KC_D_ATTN) continue;
+      if (k == KC_ARGMAX || k == KC_T_COMBINE || k == KC_D_ATTN) {
+        carry += c->ev_bytes[i];  // the depformer attention runs inside the o-projection
+        continue;
+      }
       cls.push_back(k);
-      by.push_back(c->ev_bytes[i]);
+      by.push_back(c->ev_bytes[i] + carry);
+      carry = 0.0;
     }
     const size_t nb = cls.size();
     if (nb + 2 > (size_t)STEP_TRACE_MAX || live_count(c) == 0) {
