@@ -16,8 +16,8 @@
 //
 // Grid barrier: two levels, because 256 workgroups incrementing one counter
 // serialise at the memory side. Each workgroup counts into the counter of its
-// XCD; the last arrival of an XCD increments the global counter; everyone
-// polls the global counter. Cross-workgroup data use agent-scope relaxed
+// XCD; the last arrival of an XCD increments the global counter; the last of
+// those writes a release word that everyone polls. Cross-workgroup data use agent-scope relaxed
 // atomics (sc1 loads and stores, see dev.h), each thread waits for its own
 // stores (s_waitcnt 0) before the workgroup arrives, so no cache write-back
 // or invalidate is needed. Every wait is bounded: after SPIN_LIMIT polls a
@@ -37,13 +37,18 @@ namespace {
 constexpr int NT = STEP_THREADS;
 constexpr int KW = NT / 64;
 static_assert(KW == GEMV_KW, "the step kernel's projections use the one-session layout");
-constexpr int GU = 4;  // weight groups per lane and row in flight (register budget)
+// Weight groups per lane and row in flight: 4 for the temporal projections
+// (long streams), 2 for the depformer ones (short, latency-bound operations
+// whose code must stay small: the whole depformer loop is re-entered ~100
+// times per frame and the instruction cache is 64 KB).
+constexpr int GU = 4;
+constexpr int GUD = 2;
 constexpr int SPIN_LIMIT = 1 << 21;  // polls (~1 us each) before giving up
 
 // barrier counter layout inside one set (32-bit words, 128 B apart where
-// contended): flat counter, global counter, per-XCD registration, per-XCD
-// arrival counters
-constexpr int BW_FLAT = 0, BW_GLOBAL = 32, BW_REG = 64, BW_LOCAL = 128;
+// contended): flat counter, global counter, per-XCD registration, release
+// word, per-XCD arrival counters
+constexpr int BW_FLAT = 0, BW_GLOBAL = 32, BW_REG = 64, BW_RELEASE = 96, BW_LOCAL = 128;
 constexpr int MAX_XCC = 16;
 
 __device__ __forceinline__ unsigned xcc_id() {
@@ -117,9 +122,15 @@ __device__ __forceinline__ unsigned grid_arrive(Grid& g) {
 __device__ __forceinline__ bool grid_wait(Grid& g, unsigned old) {
   __shared__ int s_leave;
   if (threadIdx.x == 0) {
-    if (old + 1 == g.idx * g.xcc_n)
-      __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_GLOBAL, 1u, MOSHI_RLX, MOSHI_AGT);
-    s_leave = poll_until(g.set + BW_GLOBAL, g.idx * g.n_xcc, g.abort);
+    // the last arrival of the last XCD releases everyone through a word of
+    // its own (polling the counters themselves slows their increments)
+    if (old + 1 == g.idx * g.xcc_n) {
+      const unsigned og =
+          __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_GLOBAL, 1u, MOSHI_RLX, MOSHI_AGT);
+      if (og + 1 == g.idx * g.n_xcc)
+        __hip_atomic_store((MOSHI_GLB unsigned*)g.set + BW_RELEASE, g.idx, MOSHI_RLX, MOSHI_AGT);
+    }
+    s_leave = poll_until(g.set + BW_RELEASE, g.idx, g.abort);
     if (g.trace != nullptr && blockIdx.x == 0) *(MOSHI_GLB uint64_t*)(g.trace + g.idx) = wall_clock64();
   }
   __syncthreads();
@@ -152,6 +163,7 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
     if (threadIdx.x == 0) {
       __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_FLAT, 0u, MOSHI_RLX, MOSHI_AGT);
       __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_GLOBAL, 0u, MOSHI_RLX, MOSHI_AGT);
+      __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_RELEASE, 0u, MOSHI_RLX, MOSHI_AGT);
     }
   }
   if (blockIdx.x == 0)
@@ -335,16 +347,21 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   if (grid_init(g, uni(A.bar), uni(A.attn_ctr), H, parity, uni(A.abort), trace)) return;
   // first weight batch of the next projection, requested before each barrier
   u32x4 pf[GU][16 / KW];
-#define PREFETCH_SYNC(EPI_, args_)                         \
+  u32x4 pfd[GUD][16 / KW];
+#define PREFETCH_SYNC_G(EPI_, args_, GU_, PF_)             \
   do {                                                     \
     const GemmArgs na_ = (args_);                          \
     drain_stores();                                        \
     __syncthreads();                                       \
     const unsigned old_ = grid_arrive(g);                  \
-    gemv_prefetch<T, KW, EPI_, GU>(na_, wg, pf);           \
+    gemv_prefetch<T, KW, EPI_, GU_>(na_, wg, PF_);         \
     if (grid_wait(g, old_)) return;                        \
   } while (0)
+#define PREFETCH_SYNC(EPI_, args_) PREFETCH_SYNC_G(EPI_, args_, GU, pf)
+#define PREFETCH_SYNC_D(EPI_, args_) PREFETCH_SYNC_G(EPI_, args_, GUD, pfd)
 #define GEMV(PRO_, EPI_, args_) gemv_core<T, KW, PRO_, EPI_, true, GU, true>((args_), wg, nwg, xs, pf)
+#define GEMV_D(PRO_, EPI_, args_) \
+  gemv_core<T, KW, PRO_, EPI_, true, GUD, true>((args_), wg, nwg, xs, pfd)
 
   // per-layer argument blocks
   auto t_qkv = [&](int l) {
@@ -454,7 +471,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   PREFETCH_SYNC(EPI_STORE, uni(A.d_in));
   // ---- depformer input projections of all substeps ----
   GEMV(PRO_DIRECT, EPI_STORE, uni(A.d_in));
-  PREFETCH_SYNC(EPI_QKV, d_qkv(0, 0));  // held through the entry
+  PREFETCH_SYNC_D(EPI_QKV, d_qkv(0, 0));  // held through the entry
 
   // ---- 16 substeps ----
   for (int s = 0; s < S; ++s) {
@@ -471,8 +488,8 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     }
     if (grid_sync(g)) return;
     for (int l = 0; l < Ld; ++l) {
-      GEMV(PRO_NORM, EPI_QKV, d_qkv(s, l));
-      PREFETCH_SYNC(EPI_RESID, d_o(s, l));
+      GEMV_D(PRO_NORM, EPI_QKV, d_qkv(s, l));
+      PREFETCH_SYNC_D(EPI_RESID, d_o(s, l));
       {
         // every workgroup with output-projection rows computes the attention
         // of all heads itself, straight into the projection's LDS input
@@ -480,24 +497,27 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
         at.layer_off = (int64_t)l * d_lel;
         if (wg < (Dd + 15) / 16) dep_attention<T, HDD, NT, true>(at, 0, Hd, s + 1, xs);
       }
-      GEMV(PRO_LDS, EPI_RESID, d_o(s, l));
-      PREFETCH_SYNC(EPI_SWIGLU, d_gu(s, l));
-      GEMV(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
-      PREFETCH_SYNC(EPI_RESID, d_dn(s, l));
-      GEMV(PRO_DIRECT, EPI_RESID, d_dn(s, l));
+      GEMV_D(PRO_LDS, EPI_RESID, d_o(s, l));
+      PREFETCH_SYNC_D(EPI_SWIGLU, d_gu(s, l));
+      GEMV_D(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
+      PREFETCH_SYNC_D(EPI_RESID, d_dn(s, l));
+      GEMV_D(PRO_DIRECT, EPI_RESID, d_dn(s, l));
       if (l + 1 < Ld)
-        PREFETCH_SYNC(EPI_QKV, d_qkv(s, l + 1));
+        PREFETCH_SYNC_D(EPI_QKV, d_qkv(s, l + 1));
       else
-        PREFETCH_SYNC(EPI_ARGMAX, d_head(s));
+        PREFETCH_SYNC_D(EPI_ARGMAX, d_head(s));
     }
-    GEMV(PRO_CAST, EPI_ARGMAX, d_head(s));
+    GEMV_D(PRO_CAST, EPI_ARGMAX, d_head(s));
     if (s + 1 < S)
-      PREFETCH_SYNC(EPI_QKV, d_qkv(s + 1, 0));  // held through the entry
+      PREFETCH_SYNC_D(EPI_QKV, d_qkv(s + 1, 0));  // held through the entry
     else if (grid_sync(g))
       return;
   }
 #undef GEMV
+#undef GEMV_D
 #undef PREFETCH_SYNC
+#undef PREFETCH_SYNC_D
+#undef PREFETCH_SYNC_G
   // ---- last code, next position ----
   if (wg == 0) {
     const int tok = reduce_token(uni(A.apart), (Va + 15) / 16, Va);
