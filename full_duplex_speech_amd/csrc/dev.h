@@ -649,27 +649,24 @@ __device__ __forceinline__ void gemv_core(
     }
   }
   // input vector -> LDS (rounded to the model dtype); the first group's raw
-  // values are requested before the norm scale. PRO_LDS: the caller has
-  // already put it there.
-  if constexpr (PRO != PRO_LDS) {
-    XRaw<T, PRO, C> x0;
-    if (t < ngroups) load_x_raw<T, PRO, C>(a, 0, t * VEC, x0);
-    double rs = 1.0;
-    if constexpr (PRO == PRO_NORM) rs = rms_scale<C>(a, 0, s_tmp, NTH);
-    const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && wg == 0;
-    for (int gi = t; gi < ngroups; gi += NTH) {
-      double xv[VEC];
-      u32x4 packed;
-      if (gi == t) {
-        finish_x<T, PRO, C>(x0, rs, xv, &packed);
-      } else {
-        XRaw<T, PRO, C> xr;
-        load_x_raw<T, PRO, C>(a, 0, gi * VEC, xr);
-        finish_x<T, PRO, C>(xr, rs, xv, &packed);
-      }
-      *(u32x4*)(xs + (size_t)gi * VEC) = packed;
-      if (write_xn) st_grp<C>((T*)a.xn_out + (size_t)gi * VEC, packed);
+  // values are requested before the norm scale
+  XRaw<T, PRO, C> x0;
+  if (t < ngroups) load_x_raw<T, PRO, C>(a, 0, t * VEC, x0);
+  double rs = 1.0;
+  if constexpr (PRO == PRO_NORM) rs = rms_scale<C>(a, 0, s_tmp, NTH);
+  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && wg == 0;
+  for (int gi = t; gi < ngroups; gi += NTH) {
+    double xv[VEC];
+    u32x4 packed;
+    if (gi == t) {
+      finish_x<T, PRO, C>(x0, rs, xv, &packed);
+    } else {
+      XRaw<T, PRO, C> xr;
+      load_x_raw<T, PRO, C>(a, 0, gi * VEC, xr);
+      finish_x<T, PRO, C>(xr, rs, xv, &packed);
     }
+    *(u32x4*)(xs + (size_t)gi * VEC) = packed;
+    if (write_xn) st_grp<C>((T*)a.xn_out + (size_t)gi * VEC, packed);
   }
   __syncthreads();
   if (tile < ntiles) {
@@ -1050,26 +1047,25 @@ __device__ __forceinline__ void combine_staged(const AttnArgs& a, int h, int b, 
   __syncthreads();
 }
 
-// Depformer attention (all heads of slot b, keys 0 .. nvalid-1, nvalid <=
-// DEP_MAX_KEYS) by one workgroup of NTH threads: wave w takes heads w, w + NW,
-// ..., two at a time (every load of both heads is requested before either is
-// used). Scores: TK lanes per key, fp64 dot products reduced in the lanes;
-// softmax over the keys in fp64; p.V: one lane per output dim, an fp64 fma
-// chain over the keys in order. The rounded outputs go to LDS `lds_out` (the
-// next projection's input, in the step kernel) or, if it is null, to
-// a.o_out. C: the K/V were written during the running kernel (coherent
+// Depformer attention of slot b, heads head0 .. head0+n_heads-1, keys 0 ..
+// nvalid-1 (nvalid <= DEP_MAX_KEYS), by one workgroup of NTH threads: wave w
+// takes heads w, w + NW, ..., NH at a time (every load of those heads is
+// requested before any is used). Scores: TK lanes per key, fp64 dot products
+// reduced in the lanes; softmax over the keys in fp64; p.V: one lane per
+// output dim, an fp64 fma chain over the keys in order. The rounded outputs
+// go to a.o_out. The arithmetic of a head does not depend on NH or on which
+// wave takes it. C: q/K/V were written during the running kernel (coherent
 // loads). Every thread of the workgroup calls it.
 constexpr int DEP_MAX_KEYS = DEP_MAX_KEYS_HOST;
-template <typename T, int HD, int NTH, bool C>
-__device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int n_heads, int nvalid,
-                                              T* lds_out) {
+template <typename T, int HD, int NTH, bool C, int NH>
+__device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int head0, int n_heads,
+                                              int nvalid) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int TK = HD / VEC;        // lanes per key for the scores
   constexpr int KPW = 64 / TK;        // keys per wave pass
   constexpr int NP = (DEP_MAX_KEYS + KPW - 1) / KPW;
   constexpr int NW = NTH / 64;
   constexpr int DPL = HD > 64 ? HD / 64 : 1;  // output dims per lane
-  constexpr int NH = 2;                        // heads per wave at a time
   static_assert(TK <= 64 && 64 % TK == 0, "head dim");
   __shared__ double s_sc[NW][NH][64];
   const int t = tid();
@@ -1083,7 +1079,7 @@ __device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int n_he
     // every load of the NH heads first (heads past n_heads read head 0)
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
-      const int h = h0 + k * NW < n_heads ? h0 + k * NW : 0;
+      const int h = head0 + (h0 + k * NW < n_heads ? h0 + k * NW : 0);
       const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
       const T* kbase = (const T*)a.ring_k + base;
       const T* vbase = (const T*)a.ring_v + base;
@@ -1152,10 +1148,7 @@ __device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int n_he
         const int dd = lane + 64 * i;
         if (h < n_heads && dd < HD) {
           const double ov = l > 0.0 ? od / l : 0.0;
-          if (lds_out != nullptr)
-            lds_out[h * HD + dd] = round_to<T>(ov);
-          else
-            store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + dd, &ov, 1);
+          store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + (head0 + h) * HD + dd, &ov, 1);
         }
       }
     }

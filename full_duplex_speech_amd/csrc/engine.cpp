@@ -602,9 +602,11 @@ int setup_step(moshi_ctx* c) {
   A.pos = c->d_pos; A.live = c->d_live;
   CKD(c, dalloc(c, (void**)&c->d_bar, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
   CKD(c, dalloc(c, (void**)&c->d_abort, sizeof(int)));
+  // attention tickets, two sets (launch parity): temporal heads, then depformer heads
   void* tickets = nullptr;
-  CKD(c, dalloc(c, &tickets, 2 * (size_t)c->H * 16 * sizeof(unsigned)));
-  CKD(c, hipMemset(tickets, 0, 2 * (size_t)c->H * 16 * sizeof(unsigned)));
+  const size_t n_tickets = 2 * (size_t)(c->H + c->Hd) * 16;
+  CKD(c, dalloc(c, &tickets, n_tickets * sizeof(unsigned)));
+  CKD(c, hipMemset(tickets, 0, n_tickets * sizeof(unsigned)));
   A.attn_ctr = (unsigned*)tickets;
   CKD(c, hipMemset(c->d_bar, 0, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
   CKD(c, hipMemset(c->d_abort, 0, sizeof(int)));
@@ -931,8 +933,12 @@ int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vect
     double carry = 0.0;  // bytes of an operation folded into the next one
     for (size_t i = 0; i < c->ev_class.size(); ++i) {
       const int k = c->ev_class[i];
-      if (k == KC_ARGMAX || k == KC_T_COMBINE || k == KC_D_ATTN) {
-        carry += c->ev_bytes[i];  // the depformer attention runs inside the o-projection
+      if (k == KC_D_ATTN && !by.empty()) {
+        by.back() += c->ev_bytes[i];  // the depformer attention ends the q/k/v phase
+        continue;
+      }
+      if (k == KC_ARGMAX || k == KC_T_COMBINE) {
+        carry += c->ev_bytes[i];
         continue;
       }
       cls.push_back(k);

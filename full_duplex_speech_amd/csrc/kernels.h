@@ -19,7 +19,6 @@ enum Prologue {
   PRO_DIRECT = 0,  // X already stored in the model dtype [B][ldx]
   PRO_NORM = 1,    // X = round(x * rms_scale * gain): x fp64 [B][ldx] + per-tile sums of squares
   PRO_CAST = 2,    // X = round(x): x fp64 [B][ldx], no scaling
-  PRO_LDS = 3,     // (one session, step kernel) the caller has built X in LDS
 };
 
 // What a projection kernel does with its 16-row output tile.

@@ -200,7 +200,7 @@ template <typename T, int HD>
 __global__ __launch_bounds__(512) void dep_attn_kernel(AttnArgs a) {
   const int b = blockIdx.x;
   if (!ldg(a.live + b)) return;
-  dep_attention<T, HD, 512, false>(a, b, a.n_heads, a.scalar_nvalid, nullptr);
+  dep_attention<T, HD, 512, false, 2>(a, b, 0, a.n_heads, a.scalar_nvalid);
 }
 
 // Chunk merge of (slot blockIdx.y, head blockIdx.x); see combine_item.

@@ -315,6 +315,8 @@ template <typename T, int HD, int HDD>
 __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
                                                   const int* __restrict__ frames, int* text_out,
                                                   int* codes_out, int parity, uint64_t* trace) {
+  static_assert(HDD % 16 == 0, "a depformer q/k/v tile holds rows of one head");
+  constexpr int DEP_TILES_PER_HEAD = 3 * HDD / 16;  // q, k and v tiles
   extern __shared__ __align__(16) unsigned char s_dyn[];  // GEMV input or attention scratch
   T* xs = (T*)s_dyn;
   double* s_o = (double*)s_dyn;
@@ -344,7 +346,9 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
             o_dh = uni(A.o_dh);
   const int64_t t_lel = uni(A.t_layer_elems), d_lel = uni(A.d_layer_elems);
   Grid g;
-  if (grid_init(g, uni(A.bar), uni(A.attn_ctr), H, parity, uni(A.abort), trace)) return;
+  // attention tickets of this launch: temporal heads, then depformer heads
+  if (grid_init(g, uni(A.bar), uni(A.attn_ctr), H + Hd, parity, uni(A.abort), trace)) return;
+  unsigned* const tickets = uni(A.attn_ctr) + (size_t)parity * (H + Hd) * 16;
   // first weight batch of the next projection, requested before each barrier
   u32x4 pf[GU][16 / KW];
   u32x4 pfd[GUD][16 / KW];
@@ -436,7 +440,6 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
       // workgroup; the workgroup finishing a head's last span merges it
       AttnArgs at = uni(A.t_attn);
       at.layer_off = (int64_t)l * t_lel;
-      unsigned* tickets = uni(A.attn_ctr) + (size_t)parity * H * 16;
       for (int item = wg; item < H * nspan; item += nwg) {
         const int h = item / nspan, j = item % nspan;
         attn_span<T, HD, NT / 2, 2, true>(at, j * nchunks / nspan, (j + 1) * nchunks / nspan,
@@ -489,15 +492,29 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     if (grid_sync(g)) return;
     for (int l = 0; l < Ld; ++l) {
       GEMV_D(PRO_NORM, EPI_QKV, d_qkv(s, l));
-      PREFETCH_SYNC_D(EPI_RESID, d_o(s, l));
       {
-        // every workgroup with output-projection rows computes the attention
-        // of all heads itself, straight into the projection's LDS input
+        // A q/k/v tile holds 16 rows of one head. The workgroup that stores
+        // the last of a head's tiles computes that head's attention.
         AttnArgs at = uni(A.d_attn);
         at.layer_off = (int64_t)l * d_lel;
-        if (wg < (Dd + 15) / 16) dep_attention<T, HDD, NT, true>(at, 0, Hd, s + 1, xs);
+        const unsigned goal = (unsigned)((s * Ld + l + 1) * DEP_TILES_PER_HEAD);
+        __shared__ int s_last;
+        drain_stores();
+        __syncthreads();
+        for (int tile = wg; tile * 16 < 3 * Dd; tile += nwg) {
+          const int h = (tile * 16 % Dd) / HDD;
+          if (threadIdx.x == 0) {
+            const unsigned old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)tickets + (H + h) * 16, 1u,
+                                                        MOSHI_RLX, MOSHI_AGT);
+            s_last = old + 1 == goal;
+          }
+          __syncthreads();
+          if (s_last) dep_attention<T, HDD, NT, true, 1>(at, 0, h, 1, s + 1);
+          __syncthreads();
+        }
       }
-      GEMV_D(PRO_LDS, EPI_RESID, d_o(s, l));
+      PREFETCH_SYNC_D(EPI_RESID, d_o(s, l));
+      GEMV_D(PRO_DIRECT, EPI_RESID, d_o(s, l));
       PREFETCH_SYNC_D(EPI_SWIGLU, d_gu(s, l));
       GEMV_D(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
       PREFETCH_SYNC_D(EPI_RESID, d_dn(s, l));
