@@ -154,18 +154,19 @@ __device__ __forceinline__ double to_d(float v) { return (double)v; }
 
 // bf16 bits of the value nearest to d (ties to even). Rounding d to fp32 first
 // is exact enough except when that lands exactly on a bf16 midpoint while d
-// itself is not on it; then d decides the direction.
+// itself is not on it; then d decides the direction. Inf/NaN keep their
+// class (a NaN stays quiet). All cases are computed and selected, so a wave
+// does not branch per value.
 __device__ __forceinline__ unsigned short bf16_bits_rne(double d) {
   const float f = (float)d;
-  unsigned int u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u)
-    return (unsigned short)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  if ((u & 0xffffu) == 0x8000u && (double)f != d) {
-    const bool up = fabs(d) > fabs((double)f);
-    return (unsigned short)((u >> 16) + (up ? 1u : 0u));
-  }
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (unsigned short)(u >> 16);
+  const unsigned int u = __float_as_uint(f);
+  const unsigned int hi = u >> 16, lo = u & 0xffffu;
+  const unsigned int special = hi | (lo ? 0x40u : 0u);
+  const unsigned int tie = hi + (fabs(d) > fabs((double)f) ? 1u : 0u);
+  const unsigned int rne = (u + 0x7fffu + (hi & 1u)) >> 16;
+  unsigned int r = (lo == 0x8000u && (double)f != d) ? tie : rne;
+  r = (u & 0x7f800000u) == 0x7f800000u ? special : r;
+  return (unsigned short)r;
 }
 
 template <typename T>
@@ -217,47 +218,37 @@ __device__ __forceinline__ void store_rounded(T* p, const double* v, int n) {
   }
 }
 
-// The input vector in two steps: the raw values of one 16-byte group (its
-// loads can be issued before the norm scale is known), then the rounded
-// values as doubles and packed for storing.
-template <typename T, int PRO, bool C>
-struct XRaw {
-  static constexpr int VEC = VecOf<T>::N;
-  u32x4 w;          // PRO_DIRECT: the stored group
-  double x[VEC];    // PRO_NORM / PRO_CAST: fp64 inputs
-  double g[VEC];    // PRO_NORM: gains
-};
+// ---- the one-session input vector (built in LDS, rounded to the model dtype)
 
-template <typename T, int PRO, bool C>
-__device__ __forceinline__ void load_x_raw(const GemmArgs& a, int col, int k0, XRaw<T, PRO, C>& r) {
-  constexpr int VEC = VecOf<T>::N;
-  if constexpr (PRO == PRO_DIRECT) {
-    r.w = ld_grp<C>((const T*)a.X + (size_t)col * a.ldx + k0);
-  } else {
-    const double* xp = (const double*)a.X + (size_t)col * a.ldx + k0;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) r.x[e] = ld_f64<C>(xp + e);
-    if constexpr (PRO == PRO_NORM) widen<T>(ld16((const T*)a.gain + k0), r.g);
-  }
+// Elements 2p, 2p+1 of an fp64 vector: one 16-byte load (coherent: sc1).
+template <bool C>
+__device__ __forceinline__ void ld_pair_f64(const double* x, int p, double& v0, double& v1) {
+  const u32x4 q = C ? ld16_coh(x, (uint32_t)p * 16u) : ld16(x + 2 * (size_t)p);
+  v0 = __hiloint2double((int)q[1], (int)q[0]);
+  v1 = __hiloint2double((int)q[3], (int)q[2]);
 }
-
-template <typename T, int PRO, bool C>
-__device__ __forceinline__ void finish_x(const XRaw<T, PRO, C>& r, double rs, double* xv,
-                                         u32x4* packed) {
-  constexpr int VEC = VecOf<T>::N;
-  if constexpr (PRO == PRO_DIRECT) {
-    widen<T>(r.w, xv);
-    *packed = r.w;
+// Elements 2p, 2p+1 of a model-dtype vector (gains), as doubles.
+__device__ __forceinline__ void ld_pair_d(const __bf16* g, int p, double& v0, double& v1) {
+  const uint32_t u = ldg((const uint32_t*)g + p);
+  v0 = (double)__uint_as_float(u << 16);
+  v1 = (double)__uint_as_float(u & 0xffff0000u);
+}
+__device__ __forceinline__ void ld_pair_d(const float* g, int p, double& v0, double& v1) {
+  const uint64_t u = ldg((const uint64_t*)g + p);
+  v0 = (double)__uint_as_float((uint32_t)u);
+  v1 = (double)__uint_as_float((uint32_t)(u >> 32));
+}
+// Rounded pair stored to LDS (and, if xn, to global memory).
+template <typename T, bool C>
+__device__ __forceinline__ void put_pair(T* xs, T* xn, int p, double v0, double v1) {
+  if constexpr (sizeof(T) == 2) {
+    const uint32_t u = stored_bits<T>(v0) | (stored_bits<T>(v1) << 16);
+    *(uint32_t*)(xs + 2 * p) = u;
+    if (xn != nullptr) st_u32<C>(xn + 2 * p, u);
   } else {
-    u32x4 q;
-    T* rv = (T*)&q;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      const double v = (PRO == PRO_NORM) ? r.x[e] * rs * r.g[e] : r.x[e];
-      rv[e] = round_to<T>(v);
-      xv[e] = to_d(rv[e]);
-    }
-    *packed = q;
+    const uint64_t u = (uint64_t)stored_bits<T>(v0) | ((uint64_t)stored_bits<T>(v1) << 32);
+    *(uint64_t*)(xs + 2 * p) = u;
+    if (xn != nullptr) st_u64<C>(xn + 2 * p, u);
   }
 }
 
@@ -330,11 +321,10 @@ __device__ __forceinline__ double group_reduce(double v) {
 // RMSNorm scale 1/sqrt(mean(x^2) + eps) of column col from the producer's
 // per-tile sums of squares; every thread of the workgroup gets the same value.
 // Threads [0, nthr) split the tiles; fixed-order reduction through `red`.
-template <bool C>
-__device__ __forceinline__ double rms_scale(const GemmArgs& a, int col, double* red, int nthr) {
+// rms_finish: the same from each thread's sum of its partials i = t, t +
+// nthr, ... (summed in that order).
+__device__ __forceinline__ double rms_finish(double s, const GemmArgs& a, double* red, int nthr) {
   const int t = tid();
-  double s = 0.0;
-  for (int i = t; i < a.n_ssq; i += nthr) s += ld_f64<C>(a.ssq + (size_t)i * a.B + col);
   s = group_reduce<64>(s);
   if ((t & 63) == 0) red[t >> 6] = s;
   __syncthreads();
@@ -343,13 +333,84 @@ __device__ __forceinline__ double rms_scale(const GemmArgs& a, int col, double* 
   __syncthreads();  // `red` may be reused right after
   return 1.0 / sqrt(tot / (double)a.K + a.eps);
 }
+template <bool C>
+__device__ __forceinline__ double rms_scale(const GemmArgs& a, int col, double* red, int nthr) {
+  double s = 0.0;
+  for (int i = tid(); i < a.n_ssq; i += nthr) s += ld_f64<C>(a.ssq + (size_t)i * a.B + col);
+  return rms_finish(s, a, red, nthr);
+}
+
+// The one-session input vector -> LDS `xs`, rounded to the model dtype.
+// Every thread requests its first XP items (16-byte groups for PRO_DIRECT;
+// fp64 element pairs with their gains and the sum-of-squares partials
+// otherwise) before it uses any; addresses are clamped, so every lane loads
+// and a wave reads contiguous memory. Items past XP per thread are loaded a
+// pass at a time. PRO_NORM / PRO_CAST with xn_out: the workgroup with
+// `first` also stores the rounded vector there.
+template <typename T, int PRO, bool C, int NTH, int XP>
+__device__ __forceinline__ void build_input(const GemmArgs& a, T* xs, double* red, bool first) {
+  constexpr int VEC = VecOf<T>::N;
+  const int t = tid();
+  if constexpr (PRO == PRO_DIRECT) {
+    const int ng = a.K / VEC;
+    auto ld_g = [&](int gi) {
+      return C ? ld16_coh(a.X, (uint32_t)gi * 16u) : ld16((const T*)a.X + (size_t)gi * VEC);
+    };
+    u32x4 q[XP];
+#pragma unroll
+    for (int j = 0; j < XP; ++j) q[j] = ld_g(t + j * NTH < ng ? t + j * NTH : ng - 1);
+#pragma unroll
+    for (int j = 0; j < XP; ++j)
+      if (t + j * NTH < ng) *(u32x4*)(xs + (size_t)(t + j * NTH) * VEC) = q[j];
+    for (int gi = t + XP * NTH; gi < ng; gi += NTH) *(u32x4*)(xs + (size_t)gi * VEC) = ld_g(gi);
+  } else {
+    const int np = a.K / 2;
+    const double* x = (const double*)a.X;
+    const T* g = (const T*)a.gain;
+    T* xn = first ? (T*)a.xn_out : nullptr;
+    double xv[XP][2], gv[XP][2];
+#pragma unroll
+    for (int j = 0; j < XP; ++j) {
+      const int p = t + j * NTH < np ? t + j * NTH : np - 1;
+      ld_pair_f64<C>(x, p, xv[j][0], xv[j][1]);
+      if constexpr (PRO == PRO_NORM) ld_pair_d(g, p, gv[j][0], gv[j][1]);
+    }
+    double rs = 1.0;
+    if constexpr (PRO == PRO_NORM) {
+      const int n = a.n_ssq;
+      double sq[XP];
+#pragma unroll
+      for (int j = 0; j < XP; ++j)
+        sq[j] = ld_f64<C>(a.ssq + (size_t)(t + j * NTH < n ? t + j * NTH : n - 1) * a.B);
+      double sum = 0.0;
+#pragma unroll
+      for (int j = 0; j < XP; ++j)
+        if (t + j * NTH < n) sum += sq[j];
+      for (int i = t + XP * NTH; i < n; i += NTH) sum += ld_f64<C>(a.ssq + (size_t)i * a.B);
+      rs = rms_finish(sum, a, red, NTH);
+    }
+    auto put = [&](int p, const double (&xp)[2], const double (&gp)[2]) {
+      const double v0 = PRO == PRO_NORM ? xp[0] * rs * gp[0] : xp[0];
+      const double v1 = PRO == PRO_NORM ? xp[1] * rs * gp[1] : xp[1];
+      put_pair<T, C>(xs, xn, p, v0, v1);
+    };
+#pragma unroll
+    for (int j = 0; j < XP; ++j)
+      if (t + j * NTH < np) put(t + j * NTH, xv[j], gv[j]);
+    for (int p = t + XP * NTH; p < np; p += NTH) {
+      double xp[2], gp[2] = {1.0, 1.0};
+      ld_pair_f64<C>(x, p, xp[0], xp[1]);
+      if constexpr (PRO == PRO_NORM) ld_pair_d(g, p, gp[0], gp[1]);
+      put(p, xp, gp);
+    }
+  }
+}
 
 // ---- epilogue: tile rows 4g..4g+3 of column col, values v -----------------
 
-// rpre (EPI_RESID, optional): the residual values of these rows, already loaded.
 template <typename T, int EPI, bool C>
 __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int g, int col,
-                                         const double* v, const double* rpre = nullptr) {
+                                         const double* v) {
   const bool cok = col < a.B;
   if constexpr (EPI == EPI_STORE) {
 #pragma unroll
@@ -364,7 +425,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& a, int tile, int g, int
       const int row = tile * 16 + 4 * g + i;
       if (cok && row < a.N) {
         double* p = a.resid + (size_t)col * a.ldr + row;
-        const double xn = (rpre != nullptr ? rpre[i] : ld_f64<C>(p)) + v[i];
+        const double xn = ld_f64<C>(p) + v[i];
         st_f64<C>(p, xn);
         ss += xn * xn;
       }
@@ -460,10 +521,43 @@ __device__ __forceinline__ ArgPart unpack_part(u32x4 w) {
 // Epilogue of the R consecutive rows tile*16 + w*R .. that one wave owns
 // (one session, column 0), run by lane 0 with the finished sums v[0..R).
 // EPI_RESID writes one sum-of-squares partial per R rows (index row0 / R).
-// rpre: EPI_RESID residual values of these rows, already loaded (or null).
+// Inputs of the one-session q/k/v epilogue, read when the projection starts
+// so that no tile's epilogue waits on memory (a wait for a load also waits
+// for the weight batch in flight): whether the session is live, the ring
+// slot written at this step, and with RoPE the cos/sin of position * each
+// inverse frequency (LDS, [hd/2][2]; null without RoPE).
+struct QkvIn {
+  int live, widx;
+  const double* cs;
+};
+
+// The RoPE table for QkvIn at the session's position: threads [0, nthr)
+// compute entries t, t + nthr, ... (hd / 2 <= 64). The caller synchronises
+// the workgroup before it is read.
+__device__ __forceinline__ void rope_table(const GemmArgs& a, double (*cs)[2], int nthr) {
+  const double p = (double)ldg(a.pos);
+  for (int i = tid(); i < a.hd / 2; i += nthr) {
+    double sn, c;
+    sincos(p * ldg(a.inv_freq + i), &sn, &c);
+    cs[i][0] = c;
+    cs[i][1] = sn;
+  }
+}
+
+__device__ __forceinline__ QkvIn qkv_in(const GemmArgs& a, const double (*rope)[2]) {
+  QkvIn q;
+  q.live = ldg(a.live);
+  q.widx = a.pos ? (int)(ldg(a.pos) % a.cap) : a.scalar_widx;
+  q.cs = a.inv_freq != nullptr ? &rope[0][0] : nullptr;
+  return q;
+}
+
+// EPI_RESID: rpre holds the residual values of these rows if pre_ok (else
+// they are loaded here). EPI_QKV: qin.
 template <typename T, int EPI, bool C, int R>
 __device__ __forceinline__ void wave_epilogue(const GemmArgs& a, int tile, int w, const double* v,
-                                              const double* rpre) {
+                                              const double (&rpre)[R], bool pre_ok,
+                                              const QkvIn& qin) {
   static_assert(EPI != EPI_ARGMAX, "argmax partials are per tile");
   if constexpr (EPI == EPI_STORE) {
 #pragma unroll
@@ -474,15 +568,25 @@ __device__ __forceinline__ void wave_epilogue(const GemmArgs& a, int tile, int w
   } else if constexpr (EPI == EPI_RESID) {
     const int row0 = tile * 16 + w * R;
     if (row0 >= a.N) return;
+    // every load before the first store: a wait for a load also waits for
+    // the stores issued before it
+    double xn[R];
+    if (pre_ok) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) xn[r] = rpre[r] + v[r];
+    } else {
+      double rv[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) rv[r] = ld_f64<C>(a.resid + (row0 + r < a.N ? row0 + r : row0));
+#pragma unroll
+      for (int r = 0; r < R; ++r) xn[r] = rv[r] + v[r];
+    }
     double ss = 0.0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int row = row0 + r;
-      if (row < a.N) {
-        double* p = a.resid + row;
-        const double xn = (rpre != nullptr ? rpre[r] : ld_f64<C>(p)) + v[r];
-        st_f64<C>(p, xn);
-        ss += xn * xn;
+      if (row0 + r < a.N) {
+        st_f64<C>(a.resid + row0 + r, xn[r]);
+        ss += xn[r] * xn[r];
       }
     }
     st_f64<C>(a.ssq_out + row0 / R, ss);
@@ -496,13 +600,10 @@ __device__ __forceinline__ void wave_epilogue(const GemmArgs& a, int tile, int w
     double vals[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) vals[r] = v[r];
-    if (a.inv_freq != nullptr && part < 2) {
-      const double p = (double)ldg(a.pos);
+    if (qin.cs != nullptr && part < 2) {
 #pragma unroll
       for (int j = 0; j < R / 2; ++j) {
-        const double ang = p * ldg(a.inv_freq + (d0 >> 1) + j);
-        double sn, cs;
-        sincos(ang, &sn, &cs);
+        const double cs = qin.cs[2 * ((d0 >> 1) + j)], sn = qin.cs[2 * ((d0 >> 1) + j) + 1];
         const double x0 = vals[2 * j], x1 = vals[2 * j + 1];
         vals[2 * j] = x0 * cs - x1 * sn;
         vals[2 * j + 1] = x0 * sn + x1 * cs;
@@ -511,10 +612,9 @@ __device__ __forceinline__ void wave_epilogue(const GemmArgs& a, int tile, int w
     if (part == 0) {
 #pragma unroll
       for (int r = 0; r < R; ++r) st_f64<C>(a.q_out + din + r, vals[r]);
-    } else if (ldg(a.live)) {
-      const int widx = a.pos ? (int)(ldg(a.pos) % a.cap) : a.scalar_widx;
+    } else if (qin.live) {
       T* dst = (T*)(part == 1 ? a.ring_k : a.ring_v) + a.layer_off + (size_t)head * a.head_stride +
-               (size_t)widx * a.hd + d0;
+               (size_t)qin.widx * a.hd + d0;
       store_rounded<T, C>(dst, vals, R);
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -539,16 +639,6 @@ __device__ __forceinline__ void wave_epilogue(const GemmArgs& a, int tile, int w
 // One session: fp64 VALU GEMV over row tiles
 // ---------------------------------------------------------------------------
 
-// Workgroup `wg` of `nwg` (KW waves) walks row tiles wg, wg+nwg, ... (16
-// output rows each); wave w owns rows w*R .. w*R+R-1 (R = 16/KW) of a tile
-// over the whole of K. The rounded input vector is built once per workgroup in
-// LDS `xs` (model dtype, K elements). Lane l covers the 16-byte groups l,
-// l+64, ... of a row, so a wave reads each row in contiguous 1 KB pieces.
-// Weights stream in batches of U groups per lane and row, double-buffered: the
-// next batch (possibly of the next tile) is requested before the current one
-// is used. Each finished row is reduced over the 64 lanes by a butterfly;
-// wave 0 applies the epilogue to the tile's 16 rows. Every thread of the
-// workgroup must call this (it synchronises the workgroup).
 // One batch of weights for wave `wave`: U groups (lanes l, l+64, ...) of each
 // of its R rows of tile `tile`, batch `bt` along K. Every lane loads: rows
 // past the matrix read row 0 and groups past K read the row's last group
@@ -593,6 +683,51 @@ __device__ __forceinline__ void gemv_prefetch(const GemmArgs& a, int wg,
   load_wbatch<T, EPI, U, R>(a, wg, 0, t & 63, t >> 6, w, wg < n_tiles_of(EPI, a.N));
 }
 
+// EPI_RESID: the residual values of wave `wave`'s rows of tile `tile`
+// (rows past the matrix, or a tile past the last, read row 0; every lane of
+// the wave reads the same address).
+template <int EPI, bool C, int R>
+__device__ __forceinline__ void load_rpre(const GemmArgs& a, int tile, int wave, double (&rpre)[R]) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    rpre[r] = 0.0;
+    if constexpr (EPI == EPI_RESID) {
+      const int row = tile * 16 + wave * R + r;
+      rpre[r] = ld_f64<C>(a.resid + (row < a.N ? row : 0));
+    }
+  }
+}
+
+// A finished tile: each of the wave's R row sums is reduced over the 64
+// lanes; the wave applies the epilogue to its own rows (argmax partials:
+// wave 0 combines the tile's 16 rows through s_red, double-buffered by
+// `parity`). rpre: residual values of the rows, valid if pre_ok.
+template <typename T, int EPI, bool C, int R>
+__device__ __forceinline__ void finish_tile(const GemmArgs& a, int tile, int wave, int lane,
+                                            double (&acc)[R], const double (&rpre)[R], bool pre_ok,
+                                            const QkvIn& qin, double (&s_red)[2][16], int& parity) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = group_reduce<64>(acc[r]);
+  if constexpr (EPI == EPI_ARGMAX) {
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s_red[parity][wave * R + r] = acc[r];
+    }
+    __syncthreads();
+    if (wave == 0 && (lane & 15) == 0) {
+      // g = lane / 16 holds rows 4g..4g+3 of column 0
+      const int g = lane >> 4;
+      const double v[4] = {s_red[parity][4 * g], s_red[parity][4 * g + 1], s_red[parity][4 * g + 2],
+                           s_red[parity][4 * g + 3]};
+      epilogue<T, EPI, C>(a, tile, g, 0, v);
+    }
+    parity ^= 1;
+  } else {
+    // every wave finishes its own rows: no workgroup barrier per tile
+    if (lane == 0) wave_epilogue<T, EPI, C, R>(a, tile, wave, acc, rpre, pre_ok, qin);
+  }
+}
+
 // Workgroup `wg` of `nwg` (KW waves) walks row tiles wg, wg+nwg, ... (16
 // output rows each); wave w owns rows w*R .. w*R+R-1 (R = 16/KW) of a tile
 // over the whole of K. The rounded input vector is built once per workgroup in
@@ -602,14 +737,15 @@ __device__ __forceinline__ void gemv_prefetch(const GemmArgs& a, int wg,
 // next batch (possibly of the next tile) is requested before the current one
 // is used. Each finished row is reduced over the 64 lanes; the wave that owns
 // it applies the epilogue (argmax partials: wave 0, per tile). PRE: the first
-// batch is already in `pre` (gemv_prefetch). The first group of the
-// input and (EPI_RESID) the residual rows of the first tile are requested
-// before the norm scale is computed. Every thread of the workgroup must call
-// this (it synchronises the workgroup).
-template <typename T, int KW, int PRO, int EPI, bool C, int U_, bool PRE>
+// batch is already in `pre` (gemv_prefetch). The residual rows of the first
+// tile (EPI_RESID) and the first XP input items of every thread (see
+// build_input) are requested before the norm scale is computed. Every thread
+// of the workgroup must call this (it synchronises the workgroup).
+template <typename T, int KW, int PRO, int EPI, bool C, int U_, bool PRE, int XP = 4>
 __device__ __forceinline__ void gemv_core(
     const GemmArgs& a, int wg, int nwg, T* xs,
-    const u32x4 (&pre)[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R]) {
+    const u32x4 (&pre)[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R],
+    const double (*rope)[2] = nullptr) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int R = GemvShape<KW, U_>::R;
   constexpr int U = GemvShape<KW, U_>::U;
@@ -635,39 +771,20 @@ __device__ __forceinline__ void gemv_core(
     // in flight while the input is built
     load_wbatch<T, EPI, U, R>(a, tile, 0, lane, wave, wa, tile < ntiles);
   }
-  // residual rows of the first tile (lane 0 of each wave holds its R rows)
+  // residual rows of the first tile (one address per wave; clamped, so
+  // every wave loads)
   double rpre[R];
-#pragma unroll
-  for (int r = 0; r < R; ++r) rpre[r] = 0.0;
-  if constexpr (EPI == EPI_RESID) {
-    if (tile < ntiles && lane == 0) {
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const int row = tile * 16 + wave * R + r;
-        if (row < a.N) rpre[r] = ld_f64<C>(a.resid + row);
-      }
+  load_rpre<EPI, C, R>(a, wg, wave, rpre);
+  QkvIn qin{};
+  if constexpr (EPI == EPI_QKV) {
+    __shared__ double s_rope[64][2];
+    if (a.inv_freq != nullptr && rope == nullptr) {
+      rope_table(a, s_rope, NTH);  // read after the barrier below
+      rope = s_rope;
     }
+    qin = qkv_in(a, rope);
   }
-  // input vector -> LDS (rounded to the model dtype); the first group's raw
-  // values are requested before the norm scale
-  XRaw<T, PRO, C> x0;
-  if (t < ngroups) load_x_raw<T, PRO, C>(a, 0, t * VEC, x0);
-  double rs = 1.0;
-  if constexpr (PRO == PRO_NORM) rs = rms_scale<C>(a, 0, s_tmp, NTH);
-  const bool write_xn = (PRO != PRO_DIRECT) && a.xn_out != nullptr && wg == 0;
-  for (int gi = t; gi < ngroups; gi += NTH) {
-    double xv[VEC];
-    u32x4 packed;
-    if (gi == t) {
-      finish_x<T, PRO, C>(x0, rs, xv, &packed);
-    } else {
-      XRaw<T, PRO, C> xr;
-      load_x_raw<T, PRO, C>(a, 0, gi * VEC, xr);
-      finish_x<T, PRO, C>(xr, rs, xv, &packed);
-    }
-    *(u32x4*)(xs + (size_t)gi * VEC) = packed;
-    if (write_xn) st_grp<C>((T*)a.xn_out + (size_t)gi * VEC, packed);
-  }
+  build_input<T, PRO, C, NTH, XP>(a, xs, s_tmp, wg == 0);
   __syncthreads();
   if (tile < ntiles) {
     double acc[R];
@@ -693,27 +810,7 @@ __device__ __forceinline__ void gemv_core(
         }
       }
       if (bt == nbatch - 1) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) acc[r] = group_reduce<64>(acc[r]);
-        if constexpr (EPI == EPI_ARGMAX) {
-          // per-tile (max, index) partial: wave 0 combines the tile's 16 rows
-          if (lane == 0) {
-#pragma unroll
-            for (int r = 0; r < R; ++r) s_red[parity][wave * R + r] = acc[r];
-          }
-          __syncthreads();
-          if (wave == 0 && (lane & 15) == 0) {
-            // g = lane / 16 holds rows 4g..4g+3 of column 0
-            const int g = lane >> 4;
-            const double v[4] = {s_red[parity][4 * g], s_red[parity][4 * g + 1],
-                                 s_red[parity][4 * g + 2], s_red[parity][4 * g + 3]};
-            epilogue<T, EPI, C>(a, tile, g, 0, v);
-          }
-          parity ^= 1;
-        } else {
-          // every wave finishes its own rows: no workgroup barrier per tile
-          if (lane == 0) wave_epilogue<T, EPI, C, R>(a, tile, wave, acc, tile == wg ? rpre : nullptr);
-        }
+        finish_tile<T, EPI, C, R>(a, tile, wave, lane, acc, rpre, tile == wg, qin, s_red, parity);
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0;
       }
@@ -751,6 +848,149 @@ template <typename T, int KW, int PRO, int EPI, bool C, int U_ = 0>
 __device__ __forceinline__ void gemv_body(const GemmArgs& a, int wg, int nwg, T* xs) {
   u32x4 none[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R];
   gemv_core<T, KW, PRO, EPI, C, U_, false>(a, wg, nwg, xs, none);
+}
+
+// ---- one session, weight slice staged in LDS ------------------------------
+//
+// For short projections whose whole per-workgroup slice fits in LDS: every
+// weight group of the workgroup's rows is requested at once with LDS-direct
+// loads (global_load_lds_dwordx4) while the preceding grid barrier completes,
+// then the projection runs from LDS.
+//
+// Work items: a wave always owns row pairs (the rows one sum-of-squares
+// partial or one SwiGLU unit covers). q/k/v and argmax projections keep the
+// 16-row tiles of gemv_core (tile i of the workgroup: wave w takes pair w),
+// because attention tickets and argmax partials are per tile. The others
+// spread pairs evenly: workgroup wg takes pairs [wg*P/nwg, (wg+1)*P/nwg) and
+// wave w every KW-th of them from the w-th. Each row is still summed by one
+// wave in gemv_core's order (lane l: groups l, l+64, ...; then the 64-lane
+// reduction), so results are bit-identical to it whatever the mapping.
+//
+// Slot layout: lane l of wave w puts its 16-byte group of (the wave's item j,
+// column pass c, row r of the pair) at byte ((((j * CPL + c) * 2 + r) * KW +
+// w) * 64 + l) * 16, CPL = column passes per row (ceil(K / VEC / 64)); the
+// same lane reads it back, so the only wait needed is the wave's own. The
+// host sizes the buffer with staged_slice_bytes.
+
+#define MOSHI_LDS __attribute__((address_space(3)))
+
+template <typename T>
+__device__ __forceinline__ int staged_cpl(int K) {
+  return (K / VecOf<T>::N + 63) / 64;
+}
+
+template <int EPI>
+constexpr bool staged_by_tile() {
+  return EPI == EPI_QKV || EPI == EPI_ARGMAX;
+}
+
+// Item j of wave `wave` as (tile, pair in tile) of gemv_core's numbering;
+// false past the wave's last item.
+template <int EPI, int KW>
+__device__ __forceinline__ bool staged_item(const GemmArgs& a, int wg, int nwg, int wave, int j,
+                                            int& te, int& we) {
+  if constexpr (staged_by_tile<EPI>()) {
+    te = wg + j * nwg;
+    we = wave;
+    return te < n_tiles_of(EPI, a.N);
+  } else {
+    const int P = EPI == EPI_SWIGLU ? a.N : (a.N + 1) / 2;
+    const int lo = wg * P / nwg, hi = (wg + 1) * P / nwg;  // nwg * P < 2^31
+    const int p = lo + wave + j * KW;
+    te = p / KW;
+    we = p % KW;
+    return p < hi;
+  }
+}
+
+template <typename T, int KW, int EPI>
+__device__ __forceinline__ void gemv_stage(const GemmArgs& a, int wg, int nwg, unsigned char* wbuf) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int R = 16 / KW;
+  static_assert(R == 2, "staged projections work on row pairs");
+  const int t = tid();
+  const int lane = t & 63, wave = t >> 6;
+  const int ngroups = a.K / VEC;
+  const int cpl = staged_cpl<T>(a.K);
+  MOSHI_LDS unsigned char* base = (MOSHI_LDS unsigned char*)wbuf;
+  int slot = 0, te, we;
+  for (int j = 0; staged_item<EPI, KW>(a, wg, nwg, wave, j, te, we); ++j) {
+    for (int c = 0; c < cpl; ++c) {
+      const int gi = c * 64 + lane;
+      const int gic = gi < ngroups ? gi : ngroups - 1;
+#pragma unroll
+      for (int r = 0; r < R; ++r, ++slot) {
+        bool ok;
+        const int rr = tile_row<EPI>(te, we * R + r, a.N, ok);
+        const T* src = (const T*)a.W + (size_t)(ok ? rr : 0) * a.K + (size_t)gic * VEC;
+        // nontemporal: the weights are read once per step
+        __builtin_amdgcn_global_load_lds((const MOSHI_GLB void*)src,
+                                         (MOSHI_LDS void*)(base + (slot * KW + wave) * 1024), 16, 0,
+                                         /*nt*/ 2);
+      }
+    }
+  }
+}
+
+// The projection from a slice staged by gemv_stage (same arguments). Every
+// thread of the workgroup must call this (it synchronises the workgroup).
+template <typename T, int KW, int PRO, int EPI, bool C>
+__device__ __forceinline__ void gemv_staged(const GemmArgs& a, int wg, int nwg, T* xs,
+                                            const unsigned char* wbuf,
+                                            const double (*rope)[2] = nullptr) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int R = 16 / KW;
+  constexpr int NTH = 64 * KW;
+  const int t = tid();
+  const int lane = t & 63, wave = t >> 6;
+  __shared__ double s_red[2][16];
+  __shared__ double s_tmp[KW];
+  const int ngroups = a.K / VEC;
+  const int cpl = staged_cpl<T>(a.K);
+  int te, we;
+  // residual rows of the wave's first item (row 0 if it has none)
+  const bool any = staged_item<EPI, KW>(a, wg, nwg, wave, 0, te, we);
+  double rpre[R];
+  load_rpre<EPI, C, R>(a, any ? te : 0, any ? we : 0, rpre);
+  QkvIn qin{};
+  if constexpr (EPI == EPI_QKV) {
+    __shared__ double s_rope[64][2];
+    if (a.inv_freq != nullptr && rope == nullptr) {
+      rope_table(a, s_rope, NTH);  // read after the barrier below
+      rope = s_rope;
+    }
+    qin = qkv_in(a, rope);
+  }
+  build_input<T, PRO, C, NTH, 1>(a, xs, s_tmp, wg == 0);
+  __syncthreads();
+  // this wave's LDS-direct loads have landed (they were issued before its
+  // input loads, which it has already waited for; this makes it explicit)
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const MOSHI_LDS unsigned char* base = (const MOSHI_LDS unsigned char*)wbuf;
+  int parity = 0, slot = 0;
+  for (int j = 0; staged_item<EPI, KW>(a, wg, nwg, wave, j, te, we); ++j) {
+    double acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0;
+    for (int c = 0; c < cpl; ++c, slot += R) {
+      const int gi = c * 64 + lane;
+      if (gi < ngroups) {
+        double xv[VEC];
+        widen<T>(*(const u32x4*)(xs + (size_t)gi * VEC), xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          double wd[VEC];
+          widen<T>(*(const MOSHI_LDS u32x4*)(base + (((slot + r) * KW + wave) * 64 + lane) * 16), wd);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
+        }
+      }
+    }
+    finish_tile<T, EPI, C, R>(a, te, we, lane, acc, rpre, j == 0, qin, s_red, parity);
+  }
+  __syncthreads();  // xs, s_red and the slots may be reused by the caller
 }
 
 // ---------------------------------------------------------------------------

@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "../../include/moshi.h"
@@ -550,6 +551,22 @@ int setup_step(moshi_ctx* c) {
   lds = merge > lds ? merge : lds;
   const int grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);
   if (grid < 1) return MOSHI_OK;
+  // the depformer projections stage their weight slices in LDS, after the
+  // largest depformer input vector
+  const size_t wbuf = ((size_t)(c->Dd > c->Fd ? c->Dd : c->Fd) * es + 1023) / 1024 * 1024;
+  if ((int64_t)grid * (3 * c->Dd > c->Fd ? 3 * c->Dd : c->Fd) >= (1LL << 31)) return MOSHI_OK;
+  int64_t staged = 0;
+  {
+    const GemmArgs q = d_qkv_args(c, 0, 0), o = d_o_args(c, 0, 0), gu = d_gu_args(c, 0, 0),
+                   dn = d_dn_args(c, 0, 0), hd = d_head_args(c, 0);
+    const std::pair<int, const GemmArgs*> ops[] = {
+        {EPI_QKV, &q}, {EPI_RESID, &o}, {EPI_SWIGLU, &gu}, {EPI_RESID, &dn}, {EPI_ARGMAX, &hd}};
+    for (const auto& op : ops) {
+      const int64_t b = staged_slice_bytes((int)vec, op.first, op.second->N, op.second->K, grid);
+      staged = b > staged ? b : staged;
+    }
+  }
+  lds = wbuf + staged > lds ? wbuf + staged : lds;
 
   std::vector<const void*> tab;
   const size_t o_tw = tab.size();
@@ -591,6 +608,7 @@ int setup_step(moshi_ctx* c) {
   A.tab = dt; A.n_tab = (int)tab.size();
   A.o_tw = (int)o_tw; A.o_dw = (int)o_dw; A.o_dn = (int)o_dn; A.o_de = (int)o_de;
   A.o_dh = (int)o_dh;
+  A.wbuf_lds = (int)wbuf;
   // the pointer table goes to LDS after the scratch region
   lds = (lds + 15) / 16 * 16;
   A.tab_lds = (int)lds;
@@ -614,7 +632,7 @@ int setup_step(moshi_ctx* c) {
   CKD(c, dalloc(c, (void**)&c->d_step, sizeof(StepArgs)));
   CKD(c, hipMemcpy(c->d_step, &A, sizeof(StepArgs), hipMemcpyHostToDevice));
   c->step_grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);  // with the final LDS size
-  if (c->step_grid < 1 || c->step_grid > grid) return MOSHI_OK;
+  if (c->step_grid != grid) return MOSHI_OK;  // the staged slices are sized for `grid`
   c->step_lds = lds;
   c->persistent = true;
   return MOSHI_OK;

@@ -165,6 +165,9 @@ struct StepArgs {
   //   o_de: [S] previous-token tables;  o_dh: [S] heads
   const void* const* tab;
   int n_tab, tab_lds;
+  // depformer projections: the workgroup's weight slice is staged in the
+  // dynamic LDS at wbuf_lds bytes (see staged_slice_bytes)
+  int wbuf_lds;
   int o_tw, o_dw, o_dn, o_de, o_dh;
   unsigned* bar;               // 2 sets of STEP_BAR_WORDS barrier counters
   unsigned* attn_ctr;          // 2 sets of H * 16 per-head attention tickets
@@ -192,6 +195,22 @@ hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int
                        int* text_out, int* codes_out, int parity, int nwg, size_t lds_bytes,
                        hipStream_t st, uint64_t* trace);
 constexpr int STEP_TRACE_MAX = 4096;
+// LDS bytes of one workgroup's staged weight slice in the step kernel: the
+// most row pairs one of its GEMV_KW waves takes (q/k/v and argmax: one per
+// 16-row tile of the workgroup; others: row pairs spread evenly over nwg
+// workgroups, then over the waves) x column passes (ceil(K / vec / 64)) x
+// 16 KB (2 rows x GEMV_KW waves x 64 lanes x 16 bytes). vec = elements per
+// 16 bytes.
+inline int64_t staged_slice_bytes(int vec, int epi, int N, int K, int nwg) {
+  int64_t items;
+  if (epi == EPI_QKV || epi == EPI_ARGMAX) {
+    items = ((N + 15) / 16 + nwg - 1) / nwg;
+  } else {
+    const int64_t pairs = epi == EPI_SWIGLU ? N : (N + 1) / 2;
+    items = ((pairs + nwg - 1) / nwg + GEMV_KW - 1) / GEMV_KW;
+  }
+  return items * ((K / vec + 63) / 64) * 16 * 1024;
+}
 
 int gemm_tiles(int epi, int N);  // row tiles of a projection
 // Workgroups launched for a one-session projection (the number of CUs).

@@ -37,12 +37,10 @@ namespace {
 constexpr int NT = STEP_THREADS;
 constexpr int KW = NT / 64;
 static_assert(KW == GEMV_KW, "the step kernel's projections use the one-session layout");
-// Weight groups per lane and row in flight: 4 for the temporal projections
-// (long streams), 2 for the depformer ones (short, latency-bound operations
-// whose code must stay small: the whole depformer loop is re-entered ~100
-// times per frame and the instruction cache is 64 KB).
+// Weight groups per lane and row in flight in the temporal projections (long
+// streams). The depformer projections instead stage their whole weight slice
+// in LDS during the barrier before them (gemv_stage / gemv_staged).
 constexpr int GU = 4;
-constexpr int GUD = 2;
 constexpr int SPIN_LIMIT = 1 << 21;  // polls (~1 us each) before giving up
 
 // barrier counter layout inside one set (32-bit words, 128 B apart where
@@ -351,7 +349,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   unsigned* const tickets = uni(A.attn_ctr) + (size_t)parity * (H + Hd) * 16;
   // first weight batch of the next projection, requested before each barrier
   u32x4 pf[GU][16 / KW];
-  u32x4 pfd[GUD][16 / KW];
+  unsigned char* const wbuf = s_dyn + uni(A.wbuf_lds);
 #define PREFETCH_SYNC_G(EPI_, args_, GU_, PF_)             \
   do {                                                     \
     const GemmArgs na_ = (args_);                          \
@@ -362,10 +360,19 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     if (grid_wait(g, old_)) return;                        \
   } while (0)
 #define PREFETCH_SYNC(EPI_, args_) PREFETCH_SYNC_G(EPI_, args_, GU, pf)
-#define PREFETCH_SYNC_D(EPI_, args_) PREFETCH_SYNC_G(EPI_, args_, GUD, pfd)
-#define GEMV(PRO_, EPI_, args_) gemv_core<T, KW, PRO_, EPI_, true, GU, true>((args_), wg, nwg, xs, pf)
-#define GEMV_D(PRO_, EPI_, args_) \
-  gemv_core<T, KW, PRO_, EPI_, true, GUD, true>((args_), wg, nwg, xs, pfd)
+#define GEMV(PRO_, EPI_, args_) \
+  gemv_core<T, KW, PRO_, EPI_, true, GU, true>((args_), wg, nwg, xs, pf, s_rope)
+  // depformer: the next projection's weight slice goes to LDS during the barrier
+#define STAGE_SYNC(EPI_, args_)                            \
+  do {                                                     \
+    const GemmArgs na_ = (args_);                          \
+    drain_stores();                                        \
+    __syncthreads();                                       \
+    const unsigned old_ = grid_arrive(g);                  \
+    gemv_stage<T, KW, EPI_>(na_, wg, nwg, wbuf);           \
+    if (grid_wait(g, old_)) return;                        \
+  } while (0)
+#define GEMV_S(PRO_, EPI_, args_) gemv_staged<T, KW, PRO_, EPI_, true>((args_), wg, nwg, xs, wbuf)
 
   // per-layer argument blocks
   auto t_qkv = [&](int l) {
@@ -422,6 +429,12 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     return a;
   };
 
+  // RoPE cos/sin at this step's position, for every temporal q/k/v epilogue
+  __shared__ double s_rope[HD / 2][2];
+  {
+    const GemmArgs q0 = uni(A.t_qkv);
+    if (q0.inv_freq != nullptr) rope_table(q0, s_rope, NT);
+  }
   // ---- summed embedding ----
   embed_phase<T>(A.emb, frames, wg, nwg);
   PREFETCH_SYNC(EPI_QKV, t_qkv(0));
@@ -474,7 +487,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   PREFETCH_SYNC(EPI_STORE, uni(A.d_in));
   // ---- depformer input projections of all substeps ----
   GEMV(PRO_DIRECT, EPI_STORE, uni(A.d_in));
-  PREFETCH_SYNC_D(EPI_QKV, d_qkv(0, 0));  // held through the entry
+  STAGE_SYNC(EPI_QKV, d_qkv(0, 0));  // held through the entry
 
   // ---- 16 substeps ----
   for (int s = 0; s < S; ++s) {
@@ -491,7 +504,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     }
     if (grid_sync(g)) return;
     for (int l = 0; l < Ld; ++l) {
-      GEMV_D(PRO_NORM, EPI_QKV, d_qkv(s, l));
+      GEMV_S(PRO_NORM, EPI_QKV, d_qkv(s, l));
       {
         // A q/k/v tile holds 16 rows of one head. The workgroup that stores
         // the last of a head's tiles computes that head's attention.
@@ -513,27 +526,27 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
           __syncthreads();
         }
       }
-      PREFETCH_SYNC_D(EPI_RESID, d_o(s, l));
-      GEMV_D(PRO_DIRECT, EPI_RESID, d_o(s, l));
-      PREFETCH_SYNC_D(EPI_SWIGLU, d_gu(s, l));
-      GEMV_D(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
-      PREFETCH_SYNC_D(EPI_RESID, d_dn(s, l));
-      GEMV_D(PRO_DIRECT, EPI_RESID, d_dn(s, l));
+      STAGE_SYNC(EPI_RESID, d_o(s, l));
+      GEMV_S(PRO_DIRECT, EPI_RESID, d_o(s, l));
+      STAGE_SYNC(EPI_SWIGLU, d_gu(s, l));
+      GEMV_S(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
+      STAGE_SYNC(EPI_RESID, d_dn(s, l));
+      GEMV_S(PRO_DIRECT, EPI_RESID, d_dn(s, l));
       if (l + 1 < Ld)
-        PREFETCH_SYNC_D(EPI_QKV, d_qkv(s, l + 1));
+        STAGE_SYNC(EPI_QKV, d_qkv(s, l + 1));
       else
-        PREFETCH_SYNC_D(EPI_ARGMAX, d_head(s));
+        STAGE_SYNC(EPI_ARGMAX, d_head(s));
     }
-    GEMV_D(PRO_CAST, EPI_ARGMAX, d_head(s));
+    GEMV_S(PRO_CAST, EPI_ARGMAX, d_head(s));
     if (s + 1 < S)
-      PREFETCH_SYNC_D(EPI_QKV, d_qkv(s + 1, 0));  // held through the entry
+      STAGE_SYNC(EPI_QKV, d_qkv(s + 1, 0));  // held through the entry
     else if (grid_sync(g))
       return;
   }
 #undef GEMV
-#undef GEMV_D
+#undef GEMV_S
 #undef PREFETCH_SYNC
-#undef PREFETCH_SYNC_D
+#undef STAGE_SYNC
 #undef PREFETCH_SYNC_G
   // ---- last code, next position ----
   if (wg == 0) {
