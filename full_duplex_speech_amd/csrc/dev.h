@@ -944,7 +944,6 @@ __device__ __forceinline__ void gemv_staged(const GemmArgs& a, int wg, int nwg, 
   const int t = tid();
   const int lane = t & 63, wave = t >> 6;
   __shared__ double s_red[2][16];
-  __shared__ double s_tmp[KW];
   const int ngroups = a.K / VEC;
   const int cpl = staged_cpl<T>(a.K);
   int te, we;
@@ -961,6 +960,7 @@ __device__ __forceinline__ void gemv_staged(const GemmArgs& a, int wg, int nwg, 
     }
     qin = qkv_in(a, rope);
   }
+  __shared__ double s_tmp[KW];
   build_input<T, PRO, C, NTH, 1>(a, xs, s_tmp, wg == 0);
   __syncthreads();
   // this wave's LDS-direct loads have landed (they were issued before its
@@ -974,6 +974,7 @@ __device__ __forceinline__ void gemv_staged(const GemmArgs& a, int wg, int nwg, 
     double acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0;
+#pragma unroll 2
     for (int c = 0; c < cpl; ++c, slot += R) {
       const int gi = c * 64 + lane;
       if (gi < ngroups) {
@@ -1010,47 +1011,59 @@ __device__ __forceinline__ void window_of(const AttnArgs& a, int b, int& nvalid,
   }
 }
 
-// K and V of one 64-key chunk as held by one thread of an NT-thread group:
-// PASSES keys, one 16-byte group of each. A workgroup may hold several such
-// groups (thread t is in group t / NT), each working on its own chunk; every
-// function below is called by all threads of the workgroup (they synchronise
-// it), each group with its own arguments.
-template <typename T, int HD, int NT>
-struct AttnShape {
+// One workgroup of NTH threads computes the attention of (slot b, head h)
+// over the keys [k0, k1) of its window (a "span"); the span partials of a
+// head are merged afterwards (combine_item / combine_staged), or, for a
+// single span, the output is written directly.
+//
+// Each wave takes a contiguous run of the span's keys: wave w of NW gets
+// [k0 + w*(k1-k0)/NW, k0 + (w+1)*(k1-k0)/NW). A wave holds TK = HD/VEC lanes
+// per key (one 16-byte group each, dims kd*VEC ..) and KPW = 64/TK keys per
+// pass; KB passes make a block of BK keys, and the wave streams its blocks
+// double-buffered (the next block's K and V are requested before the
+// current one is used). Per block, in fp64: scores s_j = (q.k_j) / sqrt(HD)
+// (lane dot products, then a TK-lane reduction), the block maximum over the
+// wave, and the online-softmax update with the running maximum m:
+//   m' = max(m, block max);  c = e^{m - m'};  l <- l*c + sum_j e^{s_j - m'};
+//   acc <- acc*c + sum_j e^{s_j - m'} v_j      (per lane: its key row, dims)
+// Masked keys (past nvalid, past the run, or the excluded oldest key) have
+// s = -inf and p = 0. Then the workgroup merges its waves in a fixed order
+// (threads t < HD, dim t):
+//   M = max_w m_w;  e_w = e^{m_w - M};  L = sum_w sum_r e_w l_{w,r};
+//   O = sum_w sum_r e_w acc_{w,r}   (r: the KPW key rows of wave w)
+// giving the span partial (M, L, O), or O / L for a single span.
+template <typename T, int HD>
+struct SpanShape {
   static constexpr int VEC = VecOf<T>::N;
-  static constexpr int TK = HD / VEC;   // threads per key (one 16-byte group each)
-  static constexpr int KP = NT / TK;    // keys per pass
-  static constexpr int PASSES = ATTN_CHUNK / KP;
-  static constexpr int SO = KP * (HD + 1);  // s_o doubles per group
-  static_assert(TK <= 64 && (64 % TK) == 0 && PASSES >= 1 && ATTN_CHUNK % KP == 0 && NT >= 64,
-                "head dim / chunk layout");
+  static constexpr int TK = HD / VEC;   // lanes per key
+  static constexpr int KPW = 64 / TK;   // keys per wave pass
+  static constexpr int KB = KPW < 16 ? 16 / KPW : 1;  // passes per block
+  static constexpr int BK = KB * KPW;                 // keys per block (16)
+  static_assert(TK <= 64 && 64 % TK == 0, "head dim");
 };
-template <typename T, int HD, int NT>
-struct KvChunk {
-  u32x4 k[AttnShape<T, HD, NT>::PASSES], v[AttnShape<T, HD, NT>::PASSES];
-};
-constexpr int ATTN_MAX_GROUPS = 2;
+// LDS doubles attn_span needs (per-wave accumulators, sums and maxima).
+template <typename T, int HD, int NTH>
+constexpr int span_lds_doubles() {
+  return (NTH / 64) * SpanShape<T, HD>::KPW * (HD + 1) + NTH / 64;
+}
 
-// Requests the K and V groups of `chunk`. Keys past nvalid (and every key
-// when live = false, a placeholder that keeps the number of loads in flight
-// the same on every path) read key 0, which is always written; they are
-// masked out by the scores and multiplied by p = 0. COH: the ring was written
-// during the running kernel (at least its newest row), so every load is
-// coherent (sc1).
-template <typename T, int HD, int NT, bool COH>
-__device__ __forceinline__ void attn_load(const AttnArgs& a, int chunk, int h, int b, int nvalid,
-                                          KvChunk<T, HD, NT>& kv, bool live = true) {
-  using S = AttnShape<T, HD, NT>;
-  const int t = tid() % NT;
-  const int kd = t % S::TK, kk = t / S::TK;
-  const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
-  const T* kbase = (const T*)a.ring_k + base;
-  const T* vbase = (const T*)a.ring_v + base;
+template <typename T, int HD>
+struct KvBlock {
+  u32x4 k[SpanShape<T, HD>::KB], v[SpanShape<T, HD>::KB];
+};
+
+// Requests block keys j0 + ps*KPW + kk (ps < KB) of this lane. Keys at or
+// past nvalid read key 0 (always written; masked by the caller). COH: the
+// ring was written during the running kernel (its newest row), so every
+// load is coherent (sc1).
+template <typename T, int HD, bool COH>
+__device__ __forceinline__ void load_kv_block(const T* kbase, const T* vbase, int j0, int kk,
+                                              int kd, int nvalid, KvBlock<T, HD>& kv) {
+  using S = SpanShape<T, HD>;
 #pragma unroll
-  for (int ps = 0; ps < S::PASSES; ++ps) {
-    const int j0 = chunk * ATTN_CHUNK + ps * S::KP + kk;
-    const int j = (live && j0 < nvalid) ? j0 : 0;
-    const uint32_t off = (uint32_t)(((size_t)j * HD + kd * S::VEC) * sizeof(T));
+  for (int ps = 0; ps < S::KB; ++ps) {
+    const int j = j0 + ps * S::KPW + kk;
+    const uint32_t off = (uint32_t)(((size_t)(j < nvalid ? j : 0) * HD + kd * S::VEC) * sizeof(T));
     if constexpr (COH) {
       kv.k[ps] = ld16_coh(kbase, off);
       kv.v[ps] = ld16_coh(vbase, off);
@@ -1061,142 +1074,131 @@ __device__ __forceinline__ void attn_load(const AttnArgs& a, int chunk, int h, i
   }
 }
 
-// The query slice of this thread (VEC values of head h).
-template <typename T, int HD, int NT, bool C>
-__device__ __forceinline__ void attn_query(const AttnArgs& a, int h, int b, double* qv) {
-  using S = AttnShape<T, HD, NT>;
-  const int kd = (tid() % NT) % S::TK;
-  const double* qp = a.q + (size_t)b * a.ldq + h * HD + kd * S::VEC;
-#pragma unroll
-  for (int e = 0; e < S::VEC; ++e) qv[e] = ld_f64<C>(qp + e);
-}
-
-// Scores, softmax and p.V of one loaded chunk in fp64. A single chunk writes
-// the rounded output directly; otherwise the (max, sum, p.V) partials go to
-// a.part. s_o: LDS, AttnShape::SO doubles per group. active = false: the
-// group computes on placeholder data and writes nothing.
-template <typename T, int HD, int NT, bool C>
-__device__ __forceinline__ void attn_compute(const AttnArgs& a, int chunk, int h, int b,
-                                             int nvalid, int excl, const double* qv,
-                                             const KvChunk<T, HD, NT>& kv, double* s_o,
-                                             bool active = true) {
-  using S = AttnShape<T, HD, NT>;
-  constexpr int VEC = S::VEC, TK = S::TK, KP = S::KP, PASSES = S::PASSES;
-  constexpr int CH = ATTN_CHUNK;
-  constexpr int LD = HD + 1;
-  __shared__ double s_p_all[ATTN_MAX_GROUPS][CH];
-  __shared__ double s_ml_all[ATTN_MAX_GROUPS][2];
-  const int grp = tid() / NT;
-  const int t = tid() % NT;
-  double* s_p = s_p_all[grp];
-  double* s_ml = s_ml_all[grp];
-  double* so = s_o + grp * S::SO;
-  const int nchunks = (nvalid + CH - 1) / CH;
-  const int kd = t % TK, kk = t / TK;
+// direct: write O / L to a.o_out (the only span); else the partial goes to
+// part (HD + 2 doubles: M, L, O). s_w: LDS, span_lds_doubles() doubles.
+// Every thread of the workgroup calls it.
+template <typename T, int HD, int NTH, bool C>
+__device__ __forceinline__ void attn_span(const AttnArgs& a, int h, int b, int k0, int k1,
+                                          int nvalid, int excl, double* s_w, double* part,
+                                          bool direct) {
+  using S = SpanShape<T, HD>;
+  constexpr int VEC = S::VEC, TK = S::TK, KPW = S::KPW, KB = S::KB, BK = S::BK;
+  constexpr int NW = NTH / 64;
+  const int t = tid();
+  const int lane = t & 63, w = t >> 6;
+  const int kd = lane % TK, kk = lane / TK;
+  const int ws = k0 + w * (k1 - k0) / NW, we = k0 + (w + 1) * (k1 - k0) / NW;
+  const int nb = (we - ws + BK - 1) / BK;
+  const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
+  const T* kbase = (const T*)a.ring_k + base;
+  const T* vbase = (const T*)a.ring_v + base;
   const double scale = 1.0 / sqrt((double)HD);
 
-  // scores s_j = q.k_j / sqrt(HD)
+  KvBlock<T, HD> ka, kb;
+  load_kv_block<T, HD, C>(kbase, vbase, ws, kk, kd, nvalid, ka);
+  double qv[VEC];
+  {
+    const double* qp = a.q + (size_t)b * a.ldq + h * HD + kd * VEC;
 #pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) {
-    const int j = chunk * CH + ps * KP + kk;
-    const bool ok = j < nvalid && j != excl;
-    double kd_[VEC];
-    widen<T>(kv.k[ps], kd_);
-    double d = 0.0;
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) d = fma(qv[e], kd_[e], d);
-    d = group_reduce<TK>(d);
-    if (kd == 0) s_p[ps * KP + kk] = ok ? d * scale : -INFINITY;
+    for (int e = 0; e < VEC; ++e) qv[e] = ld_f64<C>(qp + e);
   }
-  __syncthreads();
-  if (t < 64) {
-    const double sv = (t < CH) ? s_p[t] : -INFINITY;
-    const double m = group_reduce<64, true>(sv);
-    const double pj = (m == -INFINITY || sv == -INFINITY) ? 0.0 : exp(sv - m);
-    const double l = group_reduce<64>(pj);
-    if (t < CH) s_p[t] = pj;
-    if (t == 0) {
-      s_ml[0] = m;
-      s_ml[1] = l;
-    }
-  }
-  __syncthreads();
-
-  // p . V
-  double acc[VEC];
+  double m = -INFINITY, l = 0.0, acc[VEC];
 #pragma unroll
   for (int e = 0; e < VEC; ++e) acc[e] = 0.0;
+
+  auto block = [&](const KvBlock<T, HD>& kv, int j0) {
+    double sc[KB];
+    double mloc = -INFINITY;
 #pragma unroll
-  for (int ps = 0; ps < PASSES; ++ps) {
-    const double pj = s_p[ps * KP + kk];
-    double vd[VEC];
-    widen<T>(kv.v[ps], vd);
+    for (int ps = 0; ps < KB; ++ps) {
+      const int j = j0 + ps * KPW + kk;
+      double kx[VEC];
+      widen<T>(kv.k[ps], kx);
+      double d = 0.0;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] = fma(pj, vd[e], acc[e]);
+      for (int e = 0; e < VEC; ++e) d = fma(qv[e], kx[e], d);
+      d = group_reduce<TK>(d);
+      sc[ps] = (j < we && j < nvalid && j != excl) ? d * scale : -INFINITY;
+      mloc = fmax(mloc, sc[ps]);
+    }
+    const double mn = fmax(m, group_reduce<64, true>(mloc));
+    const double c = m == -INFINITY ? 0.0 : exp(m - mn);
+    l *= c;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] *= c;
+#pragma unroll
+    for (int ps = 0; ps < KB; ++ps) {
+      const double p = sc[ps] == -INFINITY ? 0.0 : exp(sc[ps] - mn);
+      l += p;
+      double vx[VEC];
+      widen<T>(kv.v[ps], vx);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc[e] = fma(p, vx[e], acc[e]);
+    }
+    m = mn;
+  };
+  // the next block is always requested (past the run it re-reads key 0)
+  for (int i = 0; i < nb; i += 2) {
+    load_kv_block<T, HD, C>(kbase, vbase, ws + (i + 1) * BK, kk, kd, i + 1 < nb ? nvalid : 0, kb);
+    block(ka, ws + i * BK);
+    if (i + 1 >= nb) break;
+    load_kv_block<T, HD, C>(kbase, vbase, ws + (i + 2) * BK, kk, kd, i + 2 < nb ? nvalid : 0, ka);
+    block(kb, ws + (i + 1) * BK);
   }
+
+  // workgroup merge of the waves (fixed order)
+  double* s_acc = s_w;                       // [NW][KPW][HD + 1]
+  double* s_m = s_w + NW * KPW * (HD + 1);   // [NW]
+  double* row = s_acc + (size_t)(w * KPW + kk) * (HD + 1);
 #pragma unroll
-  for (int e = 0; e < VEC; ++e) so[kk * LD + kd * VEC + e] = acc[e];
+  for (int e = 0; e < VEC; ++e) row[kd * VEC + e] = acc[e];
+  if (kd == 0) row[HD] = l;
+  if (lane == 0) s_m[w] = m;
   __syncthreads();
-  if (active && t < HD) {
-    double od = 0.0;
-    for (int r = 0; r < KP; ++r) od += so[r * LD + t];
-    if (nchunks == 1) {
-      const double l = s_ml[1];
-      const double ov = l > 0.0 ? od / l : 0.0;
+  if (t < HD) {
+    double M = s_m[0];
+    for (int v = 1; v < NW; ++v) M = fmax(M, s_m[v]);
+    double L = 0.0, O = 0.0;
+#pragma unroll 1
+    for (int v = 0; v < NW; ++v) {
+      const double ev = s_m[v] == -INFINITY ? 0.0 : exp(s_m[v] - M);
+#pragma unroll 4
+      for (int r = 0; r < KPW; ++r) {
+        const double* rr = s_acc + (size_t)(v * KPW + r) * (HD + 1);
+        L = fma(ev, rr[HD], L);
+        O = fma(ev, rr[t], O);
+      }
+    }
+    if (direct) {
+      const double ov = L > 0.0 ? O / L : 0.0;
       store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov, 1);
     } else {
-      double* mypart = a.part + (((size_t)b * a.n_heads + h) * a.max_chunks + chunk) * (HD + 2);
-      st_f64<C>(mypart + 2 + t, od);
+      st_f64<C>(part + 2 + t, O);
       if (t == 0) {
-        st_f64<C>(mypart, s_ml[0]);
-        st_f64<C>(mypart + 1, s_ml[1]);
+        st_f64<C>(part, M);
+        st_f64<C>(part + 1, L);
       }
     }
   }
-  __syncthreads();  // s_p, s_ml, s_o are reused by the next chunk
+  __syncthreads();  // s_w is reused by the caller
 }
 
-// One (64-key chunk, head, slot) item per NT-thread group.
-template <typename T, int HD, int NT, bool C>
-__device__ __forceinline__ void attn_item(const AttnArgs& a, int chunk, int h, int b, int nvalid,
-                                          int excl, double* s_o, bool active = true) {
-  KvChunk<T, HD, NT> kv;
-  attn_load<T, HD, NT, C>(a, chunk, h, b, nvalid, kv, active);
-  double qv[AttnShape<T, HD, NT>::VEC];
-  attn_query<T, HD, NT, C>(a, h, b, qv);
-  attn_compute<T, HD, NT, C>(a, chunk, h, b, nvalid, excl, qv, kv, s_o, active);
+// Spans of a slot's window: at most a.max_spans (the spans per head the
+// grid provides), and about ATTN_CHUNK keys or more each. Span j covers keys
+// [j*nvalid/n, (j+1)*nvalid/n).
+__device__ __forceinline__ int n_spans(const AttnArgs& a, int nvalid) {
+  const int by_len = (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  const int n = a.max_spans < by_len ? a.max_spans : by_len;
+  return n < 1 ? 1 : n;
 }
 
-// Chunks [c0, c1) of head h (c0 < c1) by the G groups of the workgroup:
-// group g takes chunks c0 + g, c0 + g + G, ...; each group requests its next
-// chunk's K and V while the current one is computed.
-template <typename T, int HD, int NT, int G, bool C>
-__device__ __forceinline__ void attn_span(const AttnArgs& a, int c0, int c1, int h, int b,
-                                          int nvalid, int excl, double* s_o) {
-  static_assert(G >= 1 && G <= ATTN_MAX_GROUPS, "groups per workgroup");
-  const int g = tid() / NT;
-  const int iters = (c1 - c0 + G - 1) / G;
-  KvChunk<T, HD, NT> ka, kb;
-  int c = c0 + g;
-  attn_load<T, HD, NT, C>(a, c, h, b, nvalid, ka, c < c1);
-  double qv[AttnShape<T, HD, NT>::VEC];
-  attn_query<T, HD, NT, C>(a, h, b, qv);
-  for (int it = 0; it < iters; it += 2, c += 2 * G) {
-    attn_load<T, HD, NT, C>(a, c + G, h, b, nvalid, kb, c + G < c1);
-    attn_compute<T, HD, NT, C>(a, c, h, b, nvalid, excl, qv, ka, s_o, c < c1);
-    if (it + 1 >= iters) break;
-    attn_load<T, HD, NT, C>(a, c + 2 * G, h, b, nvalid, ka, c + 2 * G < c1);
-    attn_compute<T, HD, NT, C>(a, c + G, h, b, nvalid, excl, qv, kb, s_o, c + G < c1);
-  }
-}
-
-// Merge the chunk partials of (slot b, head h) in chunk order:
-// o = sum_c e^{m_c - M} (p.V)_c / sum_c e^{m_c - M} l_c. Threads [0, HD) work;
+// Merge the span partials of (slot b, head h) in span order:
+// o = sum_c e^{m_c - M} O_c / sum_c e^{m_c - M} L_c. Threads [0, HD) work;
 // every thread of the workgroup must call this.
 template <typename T, int HD, bool C>
 __device__ __forceinline__ void combine_item(const AttnArgs& a, int h, int b, int nchunks) {
   const int t = tid();
-  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
+  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_spans * (HD + 2);
   constexpr int NW = HD / 64 > 0 ? HD / 64 : 1;
   __shared__ double s_m[NW];
   __shared__ double s_w[ATTN_MAX_CHUNKS];
@@ -1238,7 +1240,7 @@ template <typename T, int HD, int NT, bool C>
 __device__ __forceinline__ void combine_staged(const AttnArgs& a, int h, int b, int nchunks,
                                                double* s_part) {
   const int t = tid();
-  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_chunks * (HD + 2);
+  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_spans * (HD + 2);
   const int n = nchunks * (HD + 2);
   // all loads first, then the LDS stores (one memory latency, not one per item)
   constexpr int BATCH = 16;

@@ -127,7 +127,8 @@ struct moshi_ctx {
   int* d_err = nullptr;  // set by the embedding when a live code was out of range
   double *d_inv_freq = nullptr;
   void* staging = nullptr;  // one layer of prefill K or V
-  int max_chunks = 0;
+  int max_spans = 0;  // temporal attention spans per (slot, head)
+  int ncu = 1;        // compute units of the device
 
   // host state (the device copies of live / pos are refreshed only when
   // `meta_dirty`; the step itself advances the device positions)
@@ -285,7 +286,7 @@ AttnArgs t_attn_args(const moshi_ctx* c, int l) {
   a.slot_stride = t_slot_stride(c); a.layer_off = (int64_t)l * t_layer_elems(c);
   a.head_stride = (int64_t)c->W * c->hd; a.cap = c->W; a.pos = c->d_pos; a.live = c->d_live;
   a.mask_oldest = (c->c.flags & MOSHI_FLAG_MASK_OLDEST) ? 1 : 0;
-  a.n_heads = c->H; a.max_chunks = c->max_chunks; a.part = c->attn_part;
+  a.n_heads = c->H; a.max_spans = c->max_spans; a.part = c->attn_part;
   a.o_out = c->o; a.ldo = c->D;
   return a;
 }
@@ -353,7 +354,7 @@ AttnArgs d_attn_args(const moshi_ctx* c, int s, int l) {
   a.slot_stride = d_slot_stride(c); a.layer_off = (int64_t)l * d_layer_elems(c);
   a.head_stride = (int64_t)c->S * c->hdd;
   a.cap = c->S; a.pos = nullptr; a.scalar_nvalid = s + 1; a.live = c->d_live;
-  a.n_heads = c->Hd; a.max_chunks = 1; a.part = c->attn_part;  // S <= 64: one chunk
+  a.n_heads = c->Hd; a.max_spans = 1; a.part = c->attn_part;  // S <= 64: one span
   a.o_out = c->od; a.ldo = c->Dd;
   return a;
 }
@@ -423,7 +424,7 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
       e = run(c, KC_T_ATTN, keys * 2.0 * D * es,
               [&] { return launch_attn(dt, c->hd, a, B, c->stream); });
       if (e != hipSuccess) return e;
-      if (c->max_chunks > 1) {
+      if (c->max_spans > 1) {
         e = run(c, KC_T_COMBINE, 0.0, [&] { return launch_attn_combine(dt, c->hd, a, B, c->stream); });
         if (e != hipSuccess) return e;
       }
@@ -539,14 +540,17 @@ int setup_step(moshi_ctx* c) {
       c->S > DEP_MAX_KEYS_HOST)
     return MOSHI_OK;
   const size_t es = c->esz, vec = es == 2 ? 8 : 4;
-  auto attn_lds = [&](int hd) { return (STEP_THREADS / (hd / vec)) * (size_t)(hd + 1) * 8; };
+  // attention span scratch: per wave, 64 / (hd / vec) key rows of hd + 1 doubles, and a maximum
+  auto attn_lds = [&](int hd) {
+    return ((STEP_THREADS / (hd / vec)) * (size_t)(hd + 1) + STEP_THREADS / 64) * 8;
+  };
   size_t kmax = c->D;
   for (int k : {c->F, c->Dd, c->Fd}) kmax = (size_t)k > kmax ? (size_t)k : kmax;
   size_t lds = kmax * es;
   lds = attn_lds(c->hd) > lds ? attn_lds(c->hd) : lds;
   lds = attn_lds(c->hdd) > lds ? attn_lds(c->hdd) : lds;
-  // a head's chunk partials, merged in LDS
-  const size_t merge = (size_t)c->max_chunks * (c->hd + 2) * 8;
+  // a head's span partials, merged in LDS
+  const size_t merge = (size_t)c->max_spans * (c->hd + 2) * 8;
   if (merge > 96 * 1024) return MOSHI_OK;  // window too long for the merge in LDS
   lds = merge > lds ? merge : lds;
   const int grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);
@@ -847,7 +851,14 @@ int alloc_buffers(moshi_ctx* c) {
     void** p;
     size_t bytes;
   };
-  c->max_chunks = (c->W + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  // temporal attention: one workgroup per (slot, head, key span); with one
+  // session the spans of all heads fill the CUs once
+  {
+    const int by_len = (c->W + ATTN_CHUNK - 1) / ATTN_CHUNK;
+    int n = c->ncu / c->H;
+    n = n < 1 ? 1 : n;
+    c->max_spans = n < by_len ? n : by_len;
+  }
   const size_t hmax = c->H > c->Hd ? c->H : c->Hd;
   const size_t hdmax = c->hd > c->hdd ? c->hd : c->hdd;
   const size_t ntile_max = ((size_t)(c->Vt > c->Va ? c->Vt : c->Va) + 15) / 16;  // argmax tiles
@@ -875,7 +886,7 @@ int alloc_buffers(moshi_ctx* c) {
       {(void**)&c->tokens, B * 4},
       {(void**)&c->codes, B * S * 4},
       {(void**)&c->apart, ntile_max * B * sizeof(ArgPart)},
-      {(void**)&c->attn_part, B * hmax * c->max_chunks * (hdmax + 2) * 8},
+      {(void**)&c->attn_part, B * hmax * c->max_spans * (hdmax + 2) * 8},
       {(void**)&c->d_frames, B * c->NCH * 4},
       {(void**)&c->d_live, B * 4},
       {(void**)&c->d_pos, B * 8},
@@ -1064,6 +1075,7 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
     int ncu = 0;
     if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess)
       set_gemv_grid(ncu);
+    c->ncu = ncu > 0 ? ncu : 1;
   }
   int rc = MOSHI_OK;
   if (hip_stream) {

@@ -88,8 +88,8 @@ struct AttnArgs {
   const int* live;
   int mask_oldest;
   int n_heads;
-  int max_chunks;
-  double* part;  // [B][H][max_chunks][HD + 2]: (max, sum, p.V) of each key chunk
+  int max_spans;  // key spans per (slot, head): one workgroup each (see n_spans)
+  double* part;   // [B][H][max_spans][HD + 2]: (max, sum, p.V) of each span
   void* o_out;   // [B][ldo] model dtype
   int ldo;
 };
@@ -130,7 +130,8 @@ struct EntryArgs {
   int ssq_rows;     // rows per sum-of-squares partial (2 or 16)
 };
 
-// Keys per attention workgroup; the window is at most ATTN_CHUNK * ATTN_MAX_CHUNKS.
+// Attention spans hold about ATTN_CHUNK keys or more; the window is at most
+// ATTN_CHUNK * ATTN_MAX_CHUNKS keys.
 constexpr int ATTN_CHUNK = 64;
 constexpr int ATTN_MAX_CHUNKS = 512;
 
@@ -180,7 +181,7 @@ struct StepArgs {
 constexpr int GEMV_KW = 8;
 constexpr int GEMV_SSQ_ROWS = 16 / GEMV_KW;
 constexpr int STEP_THREADS = 512;
-constexpr int STEP_BAR_WORDS = 1024;
+constexpr int STEP_BAR_WORDS = 17 * 1024;  // one barrier counter set (17 pages of 4 KB)
 
 // Whether step.hip has an instantiation for (dtype, temporal head dim,
 // depformer head dim).

@@ -182,17 +182,19 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const ArgPart* part,
 // Sliding-window decode attention over a ring of K/V
 // ---------------------------------------------------------------------------
 
-// One workgroup per (64-key chunk, head, slot); see attn_item.
+// One workgroup per (key span, head, slot); see attn_span.
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-  constexpr int TK = HD / VecOf<T>::N;
-  __shared__ double s_o[(256 / TK) * (HD + 1)];
-  const int chunk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
+  __shared__ double s_w[span_lds_doubles<T, HD, 512>()];
+  const int span = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   if (!a.live[b]) return;
   int nvalid, excl;
   window_of(a, b, nvalid, excl);
-  if (chunk >= (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK) return;
-  attn_item<T, HD, 256, false>(a, chunk, h, b, nvalid, excl, s_o);
+  const int ns = n_spans(a, nvalid);
+  if (span >= ns) return;
+  double* part = a.part + (((size_t)b * a.n_heads + h) * a.max_spans + span) * (HD + 2);
+  attn_span<T, HD, 512, false>(a, h, b, span * nvalid / ns, (span + 1) * nvalid / ns, nvalid, excl,
+                               s_w, part, ns == 1);
 }
 
 // Depformer attention of slot blockIdx.x, every head (see dep_attention).
@@ -203,16 +205,16 @@ __global__ __launch_bounds__(512) void dep_attn_kernel(AttnArgs a) {
   dep_attention<T, HD, 512, false, 2>(a, b, 0, a.n_heads, a.scalar_nvalid);
 }
 
-// Chunk merge of (slot blockIdx.y, head blockIdx.x); see combine_item.
+// Span merge of (slot blockIdx.y, head blockIdx.x); see combine_item.
 template <typename T, int HD>
 __global__ __launch_bounds__(HD) void attn_combine_kernel(AttnArgs a) {
   const int h = blockIdx.x, b = blockIdx.y;
   if (!a.live[b]) return;
   int nvalid, excl;
   window_of(a, b, nvalid, excl);
-  const int nchunks = (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK;
-  if (nchunks <= 1) return;  // written directly by attn_kernel
-  combine_item<T, HD, false>(a, h, b, nchunks);
+  const int ns = n_spans(a, nvalid);
+  if (ns <= 1) return;  // written directly by attn_kernel
+  combine_item<T, HD, false>(a, h, b, ns);
 }
 
 // ---------------------------------------------------------------------------
@@ -437,7 +439,7 @@ hipError_t launch_gemm(int dtype, int kw, int pro, int epi, const GemmArgs& a, h
 
 template <typename T>
 static hipError_t launch_attn_t(int hd, const AttnArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.max_chunks, a.n_heads, B), block(256);
+  dim3 grid(a.max_spans, a.n_heads, B), block(512);
   switch (hd) {
     case 32: hipLaunchKernelGGL((attn_kernel<T, 32>), grid, block, 0, st, a); break;
     case 64: hipLaunchKernelGGL((attn_kernel<T, 64>), grid, block, 0, st, a); break;

@@ -43,11 +43,17 @@ static_assert(KW == GEMV_KW, "the step kernel's projections use the one-session 
 constexpr int GU = 4;
 constexpr int SPIN_LIMIT = 1 << 21;  // polls (~1 us each) before giving up
 
-// barrier counter layout inside one set (32-bit words, 128 B apart where
-// contended): flat counter, global counter, per-XCD registration, release
-// word, per-XCD arrival counters
-constexpr int BW_FLAT = 0, BW_GLOBAL = 32, BW_REG = 64, BW_RELEASE = 96, BW_LOCAL = 128;
+// Barrier words of one set (32-bit words): one 4 KB page per XCD holding its
+// arrival counter, its registration count and its release word (each on a
+// 128-byte line of its own), then a page with the grid-wide counters. The
+// pages keep different XCDs' counters, and the release words every
+// workgroup polls, in different memory channels: 256 workgroups polling one
+// word would queue every other access to that word's channel behind them.
 constexpr int MAX_XCC = 16;
+constexpr int BW_PAGE = 1024;
+constexpr int BW_LOCAL = 0, BW_REG = 32, BW_RELEASE = 64;  // within an XCD's page
+constexpr int BW_FLAT = MAX_XCC * BW_PAGE, BW_GLOBAL = BW_FLAT + 32;
+static_assert(STEP_BAR_WORDS >= (MAX_XCC + 1) * BW_PAGE, "barrier words");
 
 __device__ __forceinline__ unsigned xcc_id() {
   // hardware register XCC_ID (id 20), bits [3:0]
@@ -112,23 +118,26 @@ __device__ __forceinline__ unsigned grid_arrive(Grid& g) {
   g.idx += 1;
   unsigned old = 0;
   if (threadIdx.x == 0)
-    old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_LOCAL + 32 * g.xcc, 1u, MOSHI_RLX,
-                                 MOSHI_AGT);
+    old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + g.xcc * BW_PAGE + BW_LOCAL, 1u,
+                                 MOSHI_RLX, MOSHI_AGT);
   return old;
 }
 
 __device__ __forceinline__ bool grid_wait(Grid& g, unsigned old) {
   __shared__ int s_leave;
   if (threadIdx.x == 0) {
-    // the last arrival of the last XCD releases everyone through a word of
-    // its own (polling the counters themselves slows their increments)
+    // the last arrival of the last XCD releases everyone through the release
+    // words, one per XCD (polling the counters themselves slows their
+    // increments)
     if (old + 1 == g.idx * g.xcc_n) {
       const unsigned og =
           __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_GLOBAL, 1u, MOSHI_RLX, MOSHI_AGT);
       if (og + 1 == g.idx * g.n_xcc)
-        __hip_atomic_store((MOSHI_GLB unsigned*)g.set + BW_RELEASE, g.idx, MOSHI_RLX, MOSHI_AGT);
+        for (int x = 0; x < MAX_XCC; ++x)
+          __hip_atomic_store((MOSHI_GLB unsigned*)g.set + x * BW_PAGE + BW_RELEASE, g.idx, MOSHI_RLX,
+                             MOSHI_AGT);
     }
-    s_leave = poll_until(g.set + BW_RELEASE, g.idx, g.abort);
+    s_leave = poll_until(g.set + g.xcc * BW_PAGE + BW_RELEASE, g.idx, g.abort);
     if (g.trace != nullptr && blockIdx.x == 0) *(MOSHI_GLB uint64_t*)(g.trace + g.idx) = wall_clock64();
   }
   __syncthreads();
@@ -156,12 +165,13 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
   g.xcc = xcc_id();
   unsigned* other = bar + (parity ^ 1) * STEP_BAR_WORDS;
   if (blockIdx.x == 0 && threadIdx.x < MAX_XCC) {
-    __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_REG + threadIdx.x, 0u, MOSHI_RLX, MOSHI_AGT);
-    __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_LOCAL + 32 * threadIdx.x, 0u, MOSHI_RLX, MOSHI_AGT);
+    unsigned* page = other + threadIdx.x * BW_PAGE;
+    __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_LOCAL, 0u, MOSHI_RLX, MOSHI_AGT);
+    __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_REG, 0u, MOSHI_RLX, MOSHI_AGT);
+    __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_RELEASE, 0u, MOSHI_RLX, MOSHI_AGT);
     if (threadIdx.x == 0) {
       __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_FLAT, 0u, MOSHI_RLX, MOSHI_AGT);
       __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_GLOBAL, 0u, MOSHI_RLX, MOSHI_AGT);
-      __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_RELEASE, 0u, MOSHI_RLX, MOSHI_AGT);
     }
   }
   if (blockIdx.x == 0)
@@ -171,7 +181,8 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
   drain_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_REG + g.xcc, 1u, MOSHI_RLX, MOSHI_AGT);
+    __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + g.xcc * BW_PAGE + BW_REG, 1u, MOSHI_RLX,
+                           MOSHI_AGT);
     __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_FLAT, 1u, MOSHI_RLX, MOSHI_AGT);
     s_leave = poll_until(g.set + BW_FLAT, gridDim.x, abort);
     if (trace != nullptr && blockIdx.x == 0) *(MOSHI_GLB uint64_t*)trace = wall_clock64();
@@ -179,7 +190,8 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
   __syncthreads();
   if (s_leave) return true;
   if (threadIdx.x < MAX_XCC)
-    s_cnt[threadIdx.x] = __hip_atomic_load((MOSHI_GLB unsigned*)g.set + BW_REG + threadIdx.x, MOSHI_RLX, MOSHI_AGT);
+    s_cnt[threadIdx.x] = __hip_atomic_load((MOSHI_GLB unsigned*)g.set + threadIdx.x * BW_PAGE + BW_REG,
+                                           MOSHI_RLX, MOSHI_AGT);
   __syncthreads();
   g.n_xcc = 0;
   for (int i = 0; i < MAX_XCC; ++i) g.n_xcc += s_cnt[i] ? 1u : 0u;
@@ -442,22 +454,22 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   // ---- temporal layers ----
   int nvalid, excl;
   window_of(uni(A.t_attn), 0, nvalid, excl);
-  const int nchunks = (nvalid + ATTN_CHUNK - 1) / ATTN_CHUNK;
-  int nspan = nwg / H;
-  nspan = nspan < 1 ? 1 : (nspan > nchunks ? nchunks : nspan);
+  const int nspan = n_spans(uni(A.t_attn), nvalid);
   for (int l = 0; l < L; ++l) {
     GEMV(PRO_NORM, EPI_QKV, t_qkv(l));
-    PREFETCH_SYNC(EPI_RESID, t_o(l));  // held through the attention
+    if (grid_sync(g)) return;
     {
-      // each head's chunks split into nspan contiguous spans, one per
-      // workgroup; the workgroup finishing a head's last span merges it
+      // each head's window split into nspan key spans, one per workgroup
+      // (the per-operation kernel's split); the workgroup finishing a
+      // head's last span merges the span partials
       AttnArgs at = uni(A.t_attn);
       at.layer_off = (int64_t)l * t_lel;
       for (int item = wg; item < H * nspan; item += nwg) {
         const int h = item / nspan, j = item % nspan;
-        attn_span<T, HD, NT / 2, 2, true>(at, j * nchunks / nspan, (j + 1) * nchunks / nspan,
-                                            h, 0, nvalid, excl, s_o);
-        if (nchunks > 1) {
+        double* part = at.part + ((size_t)h * at.max_spans + j) * (HD + 2);
+        attn_span<T, HD, NT, true>(at, h, 0, j * nvalid / nspan, (j + 1) * nvalid / nspan, nvalid,
+                                   excl, s_o, part, nspan == 1);
+        if (nspan > 1) {
           __shared__ int s_last;
           drain_stores();
           __syncthreads();
@@ -467,11 +479,11 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
             s_last = (old + 1 == (unsigned)((l + 1) * nspan));
           }
           __syncthreads();
-          if (s_last) combine_staged<T, HD, NT, true>(at, h, 0, nchunks, s_o);
+          if (s_last) combine_staged<T, HD, NT, true>(at, h, 0, nspan, s_o);
         }
       }
     }
-    if (grid_sync(g)) return;
+    PREFETCH_SYNC(EPI_RESID, t_o(l));
     GEMV(PRO_DIRECT, EPI_RESID, t_o(l));
     PREFETCH_SYNC(EPI_SWIGLU, t_gu(l));
     GEMV(PRO_NORM, EPI_SWIGLU, t_gu(l));
