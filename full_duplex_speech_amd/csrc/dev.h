@@ -40,7 +40,8 @@ struct VecOf<float> {
 #define MOSHI_GLB __attribute__((address_space(1)))
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *(const MOSHI_GLB u32x4*)p; }
-// Weights are read once per step: stream them past the caches.
+// Weights are read once per step: stream them past the caches (in the long
+// projections this beats plain loads, which evict the rings and activations).
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load((const MOSHI_GLB u32x4*)p);
 }
@@ -923,10 +924,9 @@ __device__ __forceinline__ void gemv_stage(const GemmArgs& a, int wg, int nwg, u
         bool ok;
         const int rr = tile_row<EPI>(te, we * R + r, a.N, ok);
         const T* src = (const T*)a.W + (size_t)(ok ? rr : 0) * a.K + (size_t)gic * VEC;
-        // nontemporal: the weights are read once per step
         __builtin_amdgcn_global_load_lds((const MOSHI_GLB void*)src,
                                          (MOSHI_LDS void*)(base + (slot * KW + wave) * 1024), 16, 0,
-                                         /*nt*/ 2);
+                                         0);
       }
     }
   }

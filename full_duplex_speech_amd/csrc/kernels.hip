@@ -182,10 +182,13 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const ArgPart* part,
 // Sliding-window decode attention over a ring of K/V
 // ---------------------------------------------------------------------------
 
-// One workgroup per (key span, head, slot); see attn_span.
-template <typename T, int HD>
-__global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
-  __shared__ double s_w[span_lds_doubles<T, HD, 512>()];
+// One workgroup per (key span, head, slot); see attn_span. NTH = 512 with one
+// session (the step kernel's workgroup shape, so both give identical bits);
+// 256 with several, so that a few workgroups share a CU and hide each
+// other's first-block latency.
+template <typename T, int HD, int NTH>
+__global__ __launch_bounds__(NTH) void attn_kernel(AttnArgs a) {
+  __shared__ double s_w[span_lds_doubles<T, HD, NTH>()];
   const int span = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   if (!a.live[b]) return;
   int nvalid, excl;
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(512) void attn_kernel(AttnArgs a) {
   const int ns = n_spans(a, nvalid);
   if (span >= ns) return;
   double* part = a.part + (((size_t)b * a.n_heads + h) * a.max_spans + span) * (HD + 2);
-  attn_span<T, HD, 512, false>(a, h, b, span * nvalid / ns, (span + 1) * nvalid / ns, nvalid, excl,
+  attn_span<T, HD, NTH, false>(a, h, b, span * nvalid / ns, (span + 1) * nvalid / ns, nvalid, excl,
                                s_w, part, ns == 1);
 }
 
@@ -439,12 +442,21 @@ hipError_t launch_gemm(int dtype, int kw, int pro, int epi, const GemmArgs& a, h
 
 template <typename T>
 static hipError_t launch_attn_t(int hd, const AttnArgs& a, int B, hipStream_t st) {
-  dim3 grid(a.max_spans, a.n_heads, B), block(512);
-  switch (hd) {
-    case 32: hipLaunchKernelGGL((attn_kernel<T, 32>), grid, block, 0, st, a); break;
-    case 64: hipLaunchKernelGGL((attn_kernel<T, 64>), grid, block, 0, st, a); break;
-    case 128: hipLaunchKernelGGL((attn_kernel<T, 128>), grid, block, 0, st, a); break;
-    default: return hipErrorInvalidValue;
+  const dim3 grid(a.max_spans, a.n_heads, B);
+  if (B == 1) {
+    switch (hd) {
+      case 32: hipLaunchKernelGGL((attn_kernel<T, 32, 512>), grid, dim3(512), 0, st, a); break;
+      case 64: hipLaunchKernelGGL((attn_kernel<T, 64, 512>), grid, dim3(512), 0, st, a); break;
+      case 128: hipLaunchKernelGGL((attn_kernel<T, 128, 512>), grid, dim3(512), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
+  } else {
+    switch (hd) {
+      case 32: hipLaunchKernelGGL((attn_kernel<T, 32, 256>), grid, dim3(256), 0, st, a); break;
+      case 64: hipLaunchKernelGGL((attn_kernel<T, 64, 256>), grid, dim3(256), 0, st, a); break;
+      case 128: hipLaunchKernelGGL((attn_kernel<T, 128, 256>), grid, dim3(256), 0, st, a); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
