@@ -1044,7 +1044,7 @@ struct SpanShape {
 // LDS doubles attn_span needs (per-wave accumulators, sums and maxima).
 template <typename T, int HD, int NTH>
 constexpr int span_lds_doubles() {
-  return (NTH / 64) * SpanShape<T, HD>::KPW * (HD + 1) + NTH / 64;
+  return (NTH / 64) * SpanShape<T, HD>::KPW * (HD + 1) + NTH / 64 + 1;
 }
 
 template <typename T, int HD>
@@ -1146,22 +1146,32 @@ __device__ __forceinline__ void attn_span(const AttnArgs& a, int h, int b, int k
     block(kb, ws + (i + 1) * BK);
   }
 
-  // workgroup merge of the waves (fixed order)
+  // workgroup merge of the waves (fixed order); the wave weights e_v are
+  // computed once each, in parallel
   double* s_acc = s_w;                       // [NW][KPW][HD + 1]
-  double* s_m = s_w + NW * KPW * (HD + 1);   // [NW]
+  double* s_m = s_w + NW * KPW * (HD + 1);   // [NW]: wave maxima, then weights
   double* row = s_acc + (size_t)(w * KPW + kk) * (HD + 1);
 #pragma unroll
   for (int e = 0; e < VEC; ++e) row[kd * VEC + e] = acc[e];
   if (kd == 0) row[HD] = l;
   if (lane == 0) s_m[w] = m;
   __syncthreads();
-  if (t < HD) {
+  double ew = 0.0;
+  if (t < NW) {
     double M = s_m[0];
     for (int v = 1; v < NW; ++v) M = fmax(M, s_m[v]);
+    ew = s_m[t] == -INFINITY ? 0.0 : exp(s_m[t] - M);
+    if (t == 0) s_w[NW * KPW * (HD + 1) + NW] = M;
+  }
+  __syncthreads();
+  if (t < NW) s_m[t] = ew;
+  __syncthreads();
+  if (t < HD) {
+    const double M = s_w[NW * KPW * (HD + 1) + NW];
     double L = 0.0, O = 0.0;
 #pragma unroll 1
     for (int v = 0; v < NW; ++v) {
-      const double ev = s_m[v] == -INFINITY ? 0.0 : exp(s_m[v] - M);
+      const double ev = s_m[v];
 #pragma unroll 4
       for (int r = 0; r < KPW; ++r) {
         const double* rr = s_acc + (size_t)(v * KPW + r) * (HD + 1);
@@ -1233,60 +1243,48 @@ __device__ __forceinline__ void combine_item(const AttnArgs& a, int h, int b, in
   __syncthreads();
 }
 
-// The same merge as combine_item (identical arithmetic and order) by a whole
-// workgroup: the partials are first copied to LDS `s_part` ([nchunks][HD+2]
-// doubles) with every load in flight at once.
-template <typename T, int HD, int NT, bool C>
-__device__ __forceinline__ void combine_staged(const AttnArgs& a, int h, int b, int nchunks,
-                                               double* s_part) {
+// The same merge as combine_item (identical arithmetic and order) without
+// LDS or workgroup barriers: threads [0, HD) request every partial they need
+// at once and each forms the span weights itself. Every thread of the
+// workgroup calls it.
+template <typename T, int HD, bool C>
+__device__ __forceinline__ void combine_direct(const AttnArgs& a, int h, int b, int nspans) {
+  constexpr int NS = 8;  // spans whose partials are requested up front
   const int t = tid();
-  const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_spans * (HD + 2);
-  const int n = nchunks * (HD + 2);
-  // all loads first, then the LDS stores (one memory latency, not one per item)
-  constexpr int BATCH = 16;
-  for (int i0 = 0; i0 < n; i0 += BATCH * NT) {
-    double v[BATCH];
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int i = i0 + k * NT + t;
-      v[k] = ld_f64<C>(parts + (i < n ? i : 0));
-    }
-#pragma unroll
-    for (int k = 0; k < BATCH; ++k) {
-      const int i = i0 + k * NT + t;
-      if (i < n) s_part[i] = v[k];
-    }
-  }
-  __syncthreads();
-  constexpr int NW = HD / 64 > 0 ? HD / 64 : 1;
-  __shared__ double s_m[NW];
-  __shared__ double s_w[ATTN_MAX_CHUNKS];
-  double mloc = -INFINITY;
-  if (t < HD)
-    for (int c = t; c < nchunks; c += HD) mloc = fmax(mloc, s_part[(size_t)c * (HD + 2)]);
-  mloc = group_reduce<(HD < 64 ? HD : 64), true>(mloc);
-  if (t < HD && (t & 63) == 0) s_m[t >> 6] = mloc;
-  __syncthreads();
-  double M = s_m[0];
-  for (int w = 1; w < NW; ++w) M = fmax(M, s_m[w]);
-  if (t < HD)
-    for (int c = t; c < nchunks; c += HD) {
-      const double mc = s_part[(size_t)c * (HD + 2)];
-      s_w[c] = (mc == -INFINITY) ? 0.0 : exp(mc - M);
-    }
-  __syncthreads();
   if (t < HD) {
-    double L = 0.0, O = 0.0;
-    for (int c = 0; c < nchunks; ++c) {
-      const double* pc = s_part + (size_t)c * (HD + 2);
-      const double w = s_w[c];
-      L = fma(pc[1], w, L);
-      O = fma(pc[2 + t], w, O);
+    const double* parts = a.part + ((size_t)b * a.n_heads + h) * a.max_spans * (HD + 2);
+    double mv[NS], lv[NS], ov[NS];
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      const double* pc = parts + (size_t)(c < nspans ? c : 0) * (HD + 2);
+      mv[c] = ld_f64<C>(pc);
+      lv[c] = ld_f64<C>(pc + 1);
+      ov[c] = ld_f64<C>(pc + 2 + t);
     }
-    const double ov = L > 0.0 ? O / L : 0.0;
-    store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov, 1);
+    double M = -INFINITY;
+#pragma unroll
+    for (int c = 0; c < NS; ++c)
+      if (c < nspans) M = fmax(M, mv[c]);
+    for (int c = NS; c < nspans; ++c) M = fmax(M, ld_f64<C>(parts + (size_t)c * (HD + 2)));
+    double L = 0.0, O = 0.0;
+#pragma unroll
+    for (int c = 0; c < NS; ++c) {
+      if (c < nspans) {
+        const double w = (mv[c] == -INFINITY) ? 0.0 : exp(mv[c] - M);
+        L = fma(lv[c], w, L);
+        O = fma(ov[c], w, O);
+      }
+    }
+    for (int c = NS; c < nspans; ++c) {
+      const double* pc = parts + (size_t)c * (HD + 2);
+      const double mc = ld_f64<C>(pc);
+      const double w = (mc == -INFINITY) ? 0.0 : exp(mc - M);
+      L = fma(ld_f64<C>(pc + 1), w, L);
+      O = fma(ld_f64<C>(pc + 2 + t), w, O);
+    }
+    const double ov_ = L > 0.0 ? O / L : 0.0;
+    store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov_, 1);
   }
-  __syncthreads();
 }
 
 // Depformer attention of slot b, heads head0 .. head0+n_heads-1, keys 0 ..

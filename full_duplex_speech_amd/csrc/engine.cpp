@@ -542,17 +542,13 @@ int setup_step(moshi_ctx* c) {
   const size_t es = c->esz, vec = es == 2 ? 8 : 4;
   // attention span scratch: per wave, 64 / (hd / vec) key rows of hd + 1 doubles, and a maximum
   auto attn_lds = [&](int hd) {
-    return ((STEP_THREADS / (hd / vec)) * (size_t)(hd + 1) + STEP_THREADS / 64) * 8;
+    return ((STEP_THREADS / (hd / vec)) * (size_t)(hd + 1) + STEP_THREADS / 64 + 1) * 8;
   };
   size_t kmax = c->D;
   for (int k : {c->F, c->Dd, c->Fd}) kmax = (size_t)k > kmax ? (size_t)k : kmax;
   size_t lds = kmax * es;
   lds = attn_lds(c->hd) > lds ? attn_lds(c->hd) : lds;
   lds = attn_lds(c->hdd) > lds ? attn_lds(c->hdd) : lds;
-  // a head's span partials, merged in LDS
-  const size_t merge = (size_t)c->max_spans * (c->hd + 2) * 8;
-  if (merge > 96 * 1024) return MOSHI_OK;  // window too long for the merge in LDS
-  lds = merge > lds ? merge : lds;
   const int grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);
   if (grid < 1) return MOSHI_OK;
   // the depformer projections stage their weight slices in LDS, after the
@@ -939,7 +935,7 @@ void release(moshi_ctx* c) {
 // wall clock after every grid barrier; the interval that ends at barrier k is
 // charged to operation k (its work plus the barrier). The operation sequence
 // is the per-operation path's, without its argmax-reduce launches (folded into
-// the next operation) and its attention chunk merges (done inside the
+// the next operation) and its attention span merges (done inside the
 // attention operation).
 int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vector<double>& acc_ms,
                      std::vector<double>& acc_b, std::vector<int64_t>& acc_n) {

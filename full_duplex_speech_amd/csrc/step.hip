@@ -41,7 +41,7 @@ static_assert(KW == GEMV_KW, "the step kernel's projections use the one-session 
 // streams). The depformer projections instead stage their whole weight slice
 // in LDS during the barrier before them (gemv_stage / gemv_staged).
 constexpr int GU = 4;
-constexpr int SPIN_LIMIT = 1 << 21;  // polls (~1 us each) before giving up
+constexpr int SPIN_LIMIT = 1 << 21;  // polls (one memory round trip each, ~0.5 us) before giving up
 
 // Barrier words of one set (32-bit words): one 4 KB page per XCD holding its
 // arrival counter, its registration count and its release word (each on a
@@ -97,7 +97,6 @@ __device__ __forceinline__ void drain_stores() {
 __device__ __forceinline__ int poll_until(unsigned* ctr, unsigned target, int* abort) {
   int spins = 0;
   while ((int)(__hip_atomic_load((MOSHI_GLB unsigned*)ctr, MOSHI_RLX, MOSHI_AGT) - target) < 0) {
-    __builtin_amdgcn_s_sleep(1);
     if (++spins > SPIN_LIMIT) {
       __hip_atomic_store((MOSHI_GLB int*)abort, 1, MOSHI_RLX, MOSHI_AGT);
       return 1;
@@ -479,7 +478,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
             s_last = (old + 1 == (unsigned)((l + 1) * nspan));
           }
           __syncthreads();
-          if (s_last) combine_staged<T, HD, NT, true>(at, h, 0, nspan, s_o);
+          if (s_last) combine_direct<T, HD, true>(at, h, 0, nspan);
         }
       }
     }
