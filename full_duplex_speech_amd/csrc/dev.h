@@ -1122,13 +1122,30 @@ __device__ __forceinline__ void attn_span(const AttnArgs& a, int h, int b, int k
       mloc = fmax(mloc, sc[ps]);
     }
     const double mn = fmax(m, group_reduce<64, true>(mloc));
-    const double c = m == -INFINITY ? 0.0 : exp(m - mn);
-    l *= c;
+    if (mn != m) {  // wave-uniform; with m = mn the rescale is by e^0 = 1
+      const double c = m == -INFINITY ? 0.0 : exp(m - mn);
+      l *= c;
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[e] *= c;
+      for (int e = 0; e < VEC; ++e) acc[e] *= c;
+    }
+    // softmax weights: with 16 lanes per key, lane ps of each 16-lane row
+    // computes the weight of pass ps and the row shares it (one exp per lane)
+    double pw[KB];
+    if constexpr (TK == 16 && KB == 4) {
+      const int mine = kd & 3;
+      const double sm = mine == 0 ? sc[0] : mine == 1 ? sc[1] : mine == 2 ? sc[2] : sc[3];
+      const double pm = sm == -INFINITY ? 0.0 : exp(sm - mn);
+      pw[0] = dpp_d<0x150>(pm);  // row_newbcast: lane n of each row to the row
+      pw[1] = dpp_d<0x151>(pm);
+      pw[2] = dpp_d<0x152>(pm);
+      pw[3] = dpp_d<0x153>(pm);
+    } else {
+#pragma unroll
+      for (int ps = 0; ps < KB; ++ps) pw[ps] = sc[ps] == -INFINITY ? 0.0 : exp(sc[ps] - mn);
+    }
 #pragma unroll
     for (int ps = 0; ps < KB; ++ps) {
-      const double p = sc[ps] == -INFINITY ? 0.0 : exp(sc[ps] - mn);
+      const double p = pw[ps];
       l += p;
       double vx[VEC];
       widen<T>(kv.v[ps], vx);
