@@ -1044,7 +1044,7 @@ struct SpanShape {
 // LDS doubles attn_span needs (per-wave accumulators, sums and maxima).
 template <typename T, int HD, int NTH>
 constexpr int span_lds_doubles() {
-  return (NTH / 64) * SpanShape<T, HD>::KPW * (HD + 1) + NTH / 64 + 1;
+  return (NTH / 64) * SpanShape<T, HD>::KPW * (HD + 1) + NTH / 64;
 }
 
 template <typename T, int HD>
@@ -1163,33 +1163,28 @@ __device__ __forceinline__ void attn_span(const AttnArgs& a, int h, int b, int k
     block(kb, ws + (i + 1) * BK);
   }
 
-  // workgroup merge of the waves (fixed order); the wave weights e_v are
-  // computed once each, in parallel
+  // workgroup merge of the waves (fixed order); lane v of each merging wave
+  // forms the weight of wave v, read by the others with readlane
+  static_assert(NW <= 64, "waves per workgroup");
   double* s_acc = s_w;                       // [NW][KPW][HD + 1]
-  double* s_m = s_w + NW * KPW * (HD + 1);   // [NW]: wave maxima, then weights
+  double* s_m = s_w + NW * KPW * (HD + 1);   // [NW]
   double* row = s_acc + (size_t)(w * KPW + kk) * (HD + 1);
 #pragma unroll
   for (int e = 0; e < VEC; ++e) row[kd * VEC + e] = acc[e];
   if (kd == 0) row[HD] = l;
   if (lane == 0) s_m[w] = m;
   __syncthreads();
-  double ew = 0.0;
-  if (t < NW) {
-    double M = s_m[0];
-    for (int v = 1; v < NW; ++v) M = fmax(M, s_m[v]);
-    ew = s_m[t] == -INFINITY ? 0.0 : exp(s_m[t] - M);
-    if (t == 0) s_w[NW * KPW * (HD + 1) + NW] = M;
-  }
-  __syncthreads();
-  if (t < NW) s_m[t] = ew;
-  __syncthreads();
   if (t < HD) {
-    const double M = s_w[NW * KPW * (HD + 1) + NW];
+    double M = s_m[0];
+#pragma unroll
+    for (int v = 1; v < NW; ++v) M = fmax(M, s_m[v]);
+    const double mine = s_m[lane % NW];
+    const double emine = mine == -INFINITY ? 0.0 : exp(mine - M);
     double L = 0.0, O = 0.0;
-#pragma unroll 1
+#pragma unroll
     for (int v = 0; v < NW; ++v) {
-      const double ev = s_m[v];
-#pragma unroll 4
+      const double ev = readlane_d(emine, v);
+#pragma unroll
       for (int r = 0; r < KPW; ++r) {
         const double* rr = s_acc + (size_t)(v * KPW + r) * (HD + 1);
         L = fma(ev, rr[HD], L);
@@ -1283,11 +1278,17 @@ __device__ __forceinline__ void combine_direct(const AttnArgs& a, int h, int b, 
     for (int c = 0; c < NS; ++c)
       if (c < nspans) M = fmax(M, mv[c]);
     for (int c = NS; c < nspans; ++c) M = fmax(M, ld_f64<C>(parts + (size_t)c * (HD + 2)));
+    // lane c forms the weight of span c; the others read it with readlane
+    const int lc = tid() & (NS - 1);
+    double mine = mv[0];
+#pragma unroll
+    for (int c = 1; c < NS; ++c) mine = lc == c ? mv[c] : mine;
+    const double emine = (mine == -INFINITY) ? 0.0 : exp(mine - M);
     double L = 0.0, O = 0.0;
 #pragma unroll
     for (int c = 0; c < NS; ++c) {
       if (c < nspans) {
-        const double w = (mv[c] == -INFINITY) ? 0.0 : exp(mv[c] - M);
+        const double w = readlane_d(emine, c);
         L = fma(lv[c], w, L);
         O = fma(ov[c], w, O);
       }
