@@ -519,6 +519,49 @@ __device__ __forceinline__ ArgPart unpack_part(u32x4 w) {
   return p;
 }
 
+// Greedy token from per-tile argmax partials [n_tiles] (one session), reduced
+// by the whole workgroup of NTH threads (the comparison is exact, so the
+// winner does not depend on the order). Indices past n_rows read as 0.
+template <int NTH>
+__device__ __forceinline__ int reduce_token(const ArgPart* part, int n_tiles, int n_rows) {
+  constexpr int NW = NTH / 64;
+  __shared__ double s_v[NW];
+  __shared__ int s_i[NW];
+  const int t = tid();
+  double bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = t; i < n_tiles; i += NTH) {
+    const ArgPart p = unpack_part(ld_grp<true>(part + i));
+    if (arg_better(p.v, p.i, bv, bi)) {
+      bv = p.v;
+      bi = p.i;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ov = shfl_xor_d(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (arg_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if ((t & 63) == 0) {
+    s_v[t >> 6] = bv;
+    s_i[t >> 6] = bi;
+  }
+  __syncthreads();
+  bv = s_v[0];
+  bi = s_i[0];
+  for (int w = 1; w < NW; ++w)
+    if (arg_better(s_v[w], s_i[w], bv, bi)) {
+      bv = s_v[w];
+      bi = s_i[w];
+    }
+  __syncthreads();
+  return bi < n_rows ? bi : 0;
+}
+
 // Epilogue of the R consecutive rows tile*16 + w*R .. that one wave owns
 // (one session, column 0), run by lane 0 with the finished sums v[0..R).
 // EPI_RESID writes one sum-of-squares partial per R rows (index row0 / R).
@@ -934,10 +977,86 @@ __device__ __forceinline__ void gemv_stage(const GemmArgs& a, int wg, int nwg, u
 
 // The projection from a slice staged by gemv_stage (same arguments). Every
 // thread of the workgroup must call this (it synchronises the workgroup).
-template <typename T, int KW, int PRO, int EPI, bool C>
+// Entry of a depformer substep (one session): the substep's residual starts
+// as y = pre + E_prev[tok], its own projection of the temporal hidden state
+// plus its own embedding of the previous substep's greedy token (the text
+// token first; mobius PR #368, "P2 - Moshi LM" and "P3 - ONNX Runtime example").
+struct EntryIn {
+  const ArgPart* apart;  // previous head's per-tile argmax partials
+  int prev_rows;         // rows of the previous head
+  const double* pre;     // [K] the substep's projection of the temporal hidden state
+  const void* table;     // [prev_rows][K] model dtype: embedding of the previous token
+  double* y;             // [K] residual, stored by the `first` workgroup
+  int* tok_out;          // previous token, stored by the `first` workgroup
+};
+
+// Sum of squares of a pair, each product rounded on its own before the sum
+// (the order of two lanes that hold one element each and add their squares).
+__device__ __forceinline__ double sq_pair(double v0, double v1) {
+#pragma clang fp contract(off)
+  return v0 * v0 + v1 * v1;
+}
+
+// PRO_NORM input of the substep's first q/k/v projection built straight from
+// the entry: every workgroup forms y for its element pairs, their
+// sums of squares in the layout the residual epilogue writes (one per pair,
+// a.n_ssq == a.K / 2), and the norm scale in build_input's order, so the
+// rounded input is the one build_input makes from the stored y.
+template <typename T, bool C, int NTH>
+__device__ __forceinline__ void build_entry_input(const GemmArgs& a, const EntryIn& E, T* xs,
+                                                  double* red, bool first) {
+  const int t = tid();
+  const int np = a.K / 2;
+  const T* g = (const T*)a.gain;
+  T* xn = first ? (T*)a.xn_out : nullptr;
+  // the token does not decide these: request them first
+  const int p0 = t < np ? t : np - 1;
+  double pv[2], gv[2];
+  ld_pair_f64<C>(E.pre, p0, pv[0], pv[1]);
+  ld_pair_d(g, p0, gv[0], gv[1]);
+  const int tok = reduce_token<NTH>(E.apart, (E.prev_rows + 15) / 16, E.prev_rows);
+  if (first && t == 0) st_i32<C>(E.tok_out, tok);
+  const T* row = (const T*)E.table + (size_t)tok * a.K;
+  double ev[2];
+  ld_pair_d(row, p0, ev[0], ev[1]);
+  double y0 = pv[0] + ev[0], y1 = pv[1] + ev[1];
+  double sum = 0.0;
+  if (t < np) {
+    if (first) {
+      st_f64<C>(E.y + 2 * t, y0);
+      st_f64<C>(E.y + 2 * t + 1, y1);
+    }
+    sum += sq_pair(y0, y1);
+  }
+  for (int p = t + NTH; p < np; p += NTH) {  // pairs past the first pass
+    double q0, q1, e0, e1;
+    ld_pair_f64<C>(E.pre, p, q0, q1);
+    ld_pair_d(row, p, e0, e1);
+    q0 += e0;
+    q1 += e1;
+    if (first) {
+      st_f64<C>(E.y + 2 * p, q0);
+      st_f64<C>(E.y + 2 * p + 1, q1);
+    }
+    sum += sq_pair(q0, q1);
+  }
+  const double rs = rms_finish(sum, a, red, NTH);
+  if (t < np) put_pair<T, C>(xs, xn, t, y0 * rs * gv[0], y1 * rs * gv[1]);
+  for (int p = t + NTH; p < np; p += NTH) {
+    double q0, q1, e0, e1, g0, g1;
+    ld_pair_f64<C>(E.pre, p, q0, q1);
+    ld_pair_d(row, p, e0, e1);
+    ld_pair_d(g, p, g0, g1);
+    put_pair<T, C>(xs, xn, p, (q0 + e0) * rs * g0, (q1 + e1) * rs * g1);
+  }
+}
+
+template <typename T, int KW, int PRO, int EPI, bool C, bool ENTRY = false>
 __device__ __forceinline__ void gemv_staged(const GemmArgs& a, int wg, int nwg, T* xs,
                                             const unsigned char* wbuf,
-                                            const double (*rope)[2] = nullptr) {
+                                            const double (*rope)[2] = nullptr,
+                                            const EntryIn* ent = nullptr) {
+  static_assert(!ENTRY || PRO == PRO_NORM, "the substep entry feeds a normed projection");
   constexpr int VEC = VecOf<T>::N;
   constexpr int R = 16 / KW;
   constexpr int NTH = 64 * KW;
@@ -961,7 +1080,10 @@ __device__ __forceinline__ void gemv_staged(const GemmArgs& a, int wg, int nwg, 
     qin = qkv_in(a, rope);
   }
   __shared__ double s_tmp[KW];
-  build_input<T, PRO, C, NTH, 1>(a, xs, s_tmp, wg == 0);
+  if constexpr (ENTRY)
+    build_entry_input<T, C, NTH>(a, *ent, xs, s_tmp, wg == 0);
+  else
+    build_input<T, PRO, C, NTH, 1>(a, xs, s_tmp, wg == 0);
   __syncthreads();
   // this wave's LDS-direct loads have landed (they were issued before its
   // input loads, which it has already waited for; this makes it explicit)

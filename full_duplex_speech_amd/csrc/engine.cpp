@@ -934,9 +934,9 @@ void release(moshi_ctx* c) {
 // Per-operation timing of the persistent step kernel: workgroup 0 stamps the
 // wall clock after every grid barrier; the interval that ends at barrier k is
 // charged to operation k (its work plus the barrier). The operation sequence
-// is the per-operation path's, without its argmax-reduce launches (folded into
-// the next operation) and its attention span merges (done inside the
-// attention operation).
+// is the per-operation path's, without its argmax-reduce launches and
+// depformer substep entries (folded into the next operation) and its
+// attention span merges (done inside the attention operation).
 int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vector<double>& acc_ms,
                      std::vector<double>& acc_b, std::vector<int64_t>& acc_n) {
   int rate_khz = 0;
@@ -962,7 +962,7 @@ int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vect
         by.back() += c->ev_bytes[i];  // the depformer attention ends the q/k/v phase
         continue;
       }
-      if (k == KC_ARGMAX || k == KC_T_COMBINE) {
+      if (k == KC_ARGMAX || k == KC_T_COMBINE || k == KC_D_ENTRY) {
         carry += c->ev_bytes[i];
         continue;
       }

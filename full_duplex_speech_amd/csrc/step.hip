@@ -199,46 +199,6 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
   return false;
 }
 
-// Greedy token from per-tile argmax partials, reduced by the whole workgroup
-// (the comparison is exact, so the winner does not depend on the order).
-__device__ __forceinline__ int reduce_token(const ArgPart* part, int n_tiles, int n_rows) {
-  __shared__ double s_v[KW];
-  __shared__ int s_i[KW];
-  const int t = tid();
-  double bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int i = t; i < n_tiles; i += NT) {
-    const ArgPart p = unpack_part(ld_grp<true>(part + i));
-    if (arg_better(p.v, p.i, bv, bi)) {
-      bv = p.v;
-      bi = p.i;
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    const double ov = shfl_xor_d(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (arg_better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-  if ((t & 63) == 0) {
-    s_v[t >> 6] = bv;
-    s_i[t >> 6] = bi;
-  }
-  __syncthreads();
-  bv = s_v[0];
-  bi = s_i[0];
-  for (int w = 1; w < KW; ++w)
-    if (arg_better(s_v[w], s_i[w], bv, bi)) {
-      bv = s_v[w];
-      bi = s_i[w];
-    }
-  __syncthreads();
-  return bi < n_rows ? bi : 0;
-}
-
 // Sum of squares of GEMV_SSQ_ROWS consecutive rows held by consecutive lanes;
 // the first lane of each group stores it as the group's partial (the layout
 // the one-session residual epilogue writes).
@@ -294,32 +254,6 @@ __device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frame
 // Depformer substep entry for slot 0: the previous head's token (the text
 // token at s = 0), stored as an output by workgroup 0, then
 // y = W_in[s] hidden + E_s[token].
-struct EntryPhase {
-  const ArgPart* apart;
-  const double* pre;
-  double* y;
-  double* ssq;
-  const void* table;
-  int Dd, prev_rows;
-};
-template <typename T>
-__device__ __forceinline__ void entry_phase(const EntryPhase& E, int s, int* tok_out, int wg,
-                                            int nwg) {
-  if (wg * NT >= E.Dd) return;  // no rows here
-  const int tok = reduce_token(E.apart, (E.prev_rows + 15) / 16, E.prev_rows);
-  if (wg == 0 && threadIdx.x == 0) st_i32<true>(tok_out, tok);
-  const T* table = (const T*)E.table;
-  for (int item = wg; item * NT < E.Dd; item += nwg) {
-    const int row = item * NT + tid();
-    double acc = 0.0;
-    if (row < E.Dd) {
-      acc = ld_f64<true>(E.pre + (size_t)s * E.Dd + row) + to_d(ldg(table + (size_t)tok * E.Dd + row));
-      st_f64<true>(E.y + row, acc);
-    }
-    store_tile_ssq<true>(acc, row, E.Dd, E.ssq);
-  }
-}
-
 template <typename T, int HD, int HDD>
 __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
                                                   const int* __restrict__ frames, int* text_out,
@@ -498,24 +432,27 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   PREFETCH_SYNC(EPI_STORE, uni(A.d_in));
   // ---- depformer input projections of all substeps ----
   GEMV(PRO_DIRECT, EPI_STORE, uni(A.d_in));
-  STAGE_SYNC(EPI_QKV, d_qkv(0, 0));  // held through the entry
+  STAGE_SYNC(EPI_QKV, d_qkv(0, 0));
 
   // ---- 16 substeps ----
   for (int s = 0; s < S; ++s) {
-    {
-      EntryPhase E;
-      E.apart = uni(A.apart);
-      E.pre = uni(A.pre);
-      E.y = uni(A.y);
-      E.ssq = uni(A.ssq_d);
-      E.table = tab(o_de + s);
-      E.Dd = Dd;
-      E.prev_rows = s == 0 ? uni(A.Vt) : Va;
-      entry_phase<T>(E, s, s == 0 ? text_out : codes_out + (s - 1), wg, nwg);
-    }
-    if (grid_sync(g)) return;
     for (int l = 0; l < Ld; ++l) {
-      GEMV_S(PRO_NORM, EPI_QKV, d_qkv(s, l));
+      if (l == 0) {
+        // The substep's entry (previous token -> residual) is folded into its
+        // first q/k/v projection: every workgroup forms the normed input from
+        // the previous head's partials itself; workgroup 0 stores the
+        // residual and the token.
+        EntryIn E;
+        E.apart = uni(A.apart);
+        E.prev_rows = s == 0 ? uni(A.Vt) : Va;
+        E.pre = uni(A.pre) + (size_t)s * Dd;
+        E.table = tab(o_de + s);
+        E.y = uni(A.y);
+        E.tok_out = s == 0 ? text_out : codes_out + (s - 1);
+        gemv_staged<T, KW, PRO_NORM, EPI_QKV, true, true>(d_qkv(s, 0), wg, nwg, xs, wbuf, nullptr, &E);
+      } else {
+        GEMV_S(PRO_NORM, EPI_QKV, d_qkv(s, l));
+      }
       {
         // A q/k/v tile holds 16 rows of one head. The workgroup that stores
         // the last of a head's tiles computes that head's attention.
@@ -550,7 +487,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     }
     GEMV_S(PRO_CAST, EPI_ARGMAX, d_head(s));
     if (s + 1 < S)
-      STAGE_SYNC(EPI_QKV, d_qkv(s + 1, 0));  // held through the entry
+      STAGE_SYNC(EPI_QKV, d_qkv(s + 1, 0));
     else if (grid_sync(g))
       return;
   }
@@ -561,7 +498,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
 #undef PREFETCH_SYNC_G
   // ---- last code, next position ----
   if (wg == 0) {
-    const int tok = reduce_token(uni(A.apart), (Va + 15) / 16, Va);
+    const int tok = reduce_token<NT>(uni(A.apart), (Va + 15) / 16, Va);
     if (threadIdx.x == 0) {
       *(MOSHI_GLB int*)(codes_out + S - 1) = tok;
       int64_t* pos = uni(A.pos);
