@@ -153,6 +153,7 @@ struct moshi_ctx {
   int step_grid = 0;
   size_t step_lds = 0;
   int step_parity = 0;
+  uint32_t step_seq = 0;  // sequence number of the last step kernel launch
 
   // kernel timing (eager launches bracketed by events); `dry` only records
   // the (class, bytes) sequence of a step without launching anything
@@ -539,6 +540,11 @@ int setup_step(moshi_ctx* c) {
   if (c->B != 1 || (env && env[0] == '0') || !step_supported(c->dtype, c->hd, c->hdd) ||
       c->S > DEP_MAX_KEYS_HOST)
     return MOSHI_OK;
+  // the flagged depformer inputs: a normed input pair per thread, at most 4
+  // two-value lines per thread for a model-dtype input, whole lines
+  if (c->Dd % 2 || c->Fd % 2 || c->Dd > 2 * STEP_THREADS || c->Fd > 8 * STEP_THREADS ||
+      step_ll_words(c->S, c->Ld, c->Dd, c->Fd, c->Va) * 8 >= (1LL << 31))
+    return MOSHI_OK;
   const size_t es = c->esz, vec = es == 2 ? 8 : 4;
   // attention span scratch: per wave, 64 / (hd / vec) key rows of hd + 1 doubles, and a maximum
   auto attn_lds = [&](int hd) {
@@ -629,6 +635,12 @@ int setup_step(moshi_ctx* c) {
   CKD(c, hipMemset(c->d_bar, 0, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
   CKD(c, hipMemset(c->d_abort, 0, sizeof(int)));
   A.bar = c->d_bar; A.abort = c->d_abort;
+  {
+    const size_t ll_bytes =
+        (size_t)step_ll_words(c->S, c->Ld, c->Dd, c->Fd, c->Va) * sizeof(uint64_t);
+    CKD(c, dalloc(c, (void**)&A.ll, ll_bytes));
+    CKD(c, hipMemset(A.ll, 0, ll_bytes));
+  }
   CKD(c, dalloc(c, (void**)&c->d_step, sizeof(StepArgs)));
   CKD(c, hipMemcpy(c->d_step, &A, sizeof(StepArgs), hipMemcpyHostToDevice));
   c->step_grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);  // with the final LDS size
@@ -641,8 +653,9 @@ int setup_step(moshi_ctx* c) {
 // One full step of slot 0 on the stream; outputs to text_out [1], codes_out [S].
 int launch_persistent(moshi_ctx* c, const int* frames, int* text_out, int* codes_out,
                       uint64_t* trace = nullptr) {
+  if (++c->step_seq == 0) c->step_seq = 1;  // 0 is the arena's initial flag
   CKD(c, launch_step(c->dtype, c->hd, c->hdd, c->d_step, frames, text_out, codes_out,
-                     c->step_parity, c->step_grid, c->step_lds, c->stream, trace));
+                     c->step_parity, c->step_seq, c->step_grid, c->step_lds, c->stream, trace));
   c->step_parity ^= 1;
   return MOSHI_OK;
 }

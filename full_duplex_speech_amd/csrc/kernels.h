@@ -172,7 +172,10 @@ struct StepArgs {
   int o_tw, o_dw, o_dn, o_de, o_dh;
   unsigned* bar;               // 2 sets of STEP_BAR_WORDS barrier counters
   unsigned* attn_ctr;          // 2 sets of H * 16 per-head attention tickets
-  int* abort;                  // set when a barrier wait times out
+  int* abort;                  // set when a barrier or flag wait times out
+  // flagged vectors the depformer operations hand on (step.hip); zeroed at
+  // creation, step_ll_words() words of 8 bytes
+  uint64_t* ll;
 };
 // One-session projections run 8 waves per workgroup; each wave owns 2 rows
 // of a 16-row tile, and the residual epilogue writes one sum-of-squares
@@ -192,9 +195,16 @@ int step_max_grid(int dtype, int hd, int hdd, size_t lds_bytes);
 // between launches (it picks the barrier counter set). `trace`, if set,
 // receives the wall clock (100 MHz) at the start, after every grid barrier
 // and at the end, as seen by workgroup 0 (STEP_TRACE_MAX entries at most).
+// `seq` is the launch's sequence number (nonzero, different from the previous
+// launch's): the flag of the vectors it writes.
 hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int* frames,
-                       int* text_out, int* codes_out, int parity, int nwg, size_t lds_bytes,
-                       hipStream_t st, uint64_t* trace);
+                       int* text_out, int* codes_out, int parity, uint32_t seq, int nwg,
+                       size_t lds_bytes, hipStream_t st, uint64_t* trace);
+// Words of the flagged depformer vectors (step.hip's layout): per substep and
+// layer 11 Dd + Fd, then per substep 2 Dd + 4 ceil(Va / 16).
+inline int64_t step_ll_words(int S, int Ld, int Dd, int Fd, int Va) {
+  return (int64_t)S * Ld * (11LL * Dd + Fd) + (int64_t)S * (2LL * Dd + 4LL * ((Va + 15) / 16));
+}
 constexpr int STEP_TRACE_MAX = 4096;
 // LDS bytes of one workgroup's staged weight slice in the step kernel: the
 // most row pairs one of its GEMV_KW waves takes (q/k/v and argmax: one per

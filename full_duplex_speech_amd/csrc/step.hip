@@ -251,13 +251,591 @@ __device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frame
   }
 }
 
-// Depformer substep entry for slot 0: the previous head's token (the text
-// token at s = 0), stored as an output by workgroup 0, then
-// y = W_in[s] hidden + E_s[token].
+// ---- flagged vectors: the depformer's exchange between workgroups ---------
+//
+// The 16 substeps are ~400 dependent projections of a few MB each; a grid
+// barrier between them costs several memory round trips (store
+// acknowledgement, two counter atomics, the release word). Instead each
+// vector a projection hands on is written as flagged 8-byte words
+// {payload, flag}, flag = the launch's sequence number, and its readers poll
+// the words themselves until every flag is current: one round trip after
+// the last producer's store lands. Every flagged vector is written once per
+// launch (one buffer per substep and layer), so a word never needs clearing
+// and a reader never races a later write of the same word; the sequence
+// number differs from the previous launch's, and the buffers start zeroed
+// with sequence numbers starting at 1.
+//
+// fp64 element i of a vector: words 2i (low half) and 2i+1 (high half), one
+// 16-byte line. Model-dtype element i: word i (the value's stored bits).
+// Writers use one 8-byte store per word, readers 16-byte sc1 loads of whole
+// lines (two words, each read whole), so a word is never seen half written.
+//
+// Layout (in words) of the flagged arena: for each (substep s, layer l), in
+// order s * Ld + l, a block of 11 Dd + Fd words
+//   R1 [2 Dd] residual after the output projection, S1 [Dd] its sums of
+//   squares per row pair, R2 [2 Dd] residual after the down projection, S2
+//   [Dd], Q [2 Dd] queries, K [Dd], V [Dd] (rounded), O [Dd] attention
+//   output (rounded), A [Fd] SwiGLU output (rounded);
+// then for each substep, Y [2 Dd] (the substep's input residual) and AP
+// [4 ceil(Va / 16)] (per-tile argmax partials of its head: value low, value
+// high, index, 0).
+
+constexpr int LL_SPIN_LIMIT = 1 << 20;
+
+struct LLCtx {
+  uint64_t* w;     // the flagged arena
+  uint32_t flag;   // this launch's sequence number
+  int* abort;
+};
+
+struct LLMap {
+  int Dd, Fd, Ld, nta;
+  __device__ size_t layer(int s, int l) const { return (size_t)(s * Ld + l) * (11 * Dd + Fd); }
+  __device__ size_t R1(int s, int l) const { return layer(s, l); }
+  __device__ size_t S1(int s, int l) const { return layer(s, l) + 2 * Dd; }
+  __device__ size_t R2(int s, int l) const { return layer(s, l) + 3 * Dd; }
+  __device__ size_t S2(int s, int l) const { return layer(s, l) + 5 * Dd; }
+  __device__ size_t Q(int s, int l) const { return layer(s, l) + 6 * Dd; }
+  __device__ size_t K(int s, int l) const { return layer(s, l) + 8 * Dd; }
+  __device__ size_t V(int s, int l) const { return layer(s, l) + 9 * Dd; }
+  __device__ size_t O(int s, int l) const { return layer(s, l) + 10 * Dd; }
+  __device__ size_t A(int s, int l) const { return layer(s, l) + 11 * Dd; }
+  __device__ size_t sub(int s, int S) const {
+    return layer(S, 0) + (size_t)s * (2 * Dd + 4 * nta);
+  }
+  __device__ size_t Y(int s, int S) const { return sub(s, S); }
+  __device__ size_t AP(int s, int S) const { return sub(s, S) + 2 * Dd; }
+};
+
+__device__ __forceinline__ void ll_put(const LLCtx& c, size_t word, uint32_t payload) {
+  st_u64<true>(c.w + word, (uint64_t)payload | ((uint64_t)c.flag << 32));
+}
+__device__ __forceinline__ void ll_put_f64(const LLCtx& c, size_t word, double v) {
+  const uint64_t b = __builtin_bit_cast(uint64_t, v);
+  ll_put(c, word, (uint32_t)b);
+  ll_put(c, word + 1, (uint32_t)(b >> 32));
+}
+// the line holding words `word` (even) and word + 1
+__device__ __forceinline__ u32x4 ll_ld(const LLCtx& c, size_t word) {
+  return ld16_coh(c.w, (uint32_t)(word * 8));
+}
+__device__ __forceinline__ bool ll_fresh(const u32x4& q, uint32_t flag) {
+  return (q[1] == flag) & (q[3] == flag);
+}
+__device__ __forceinline__ double ll_f64(const u32x4& q) {
+  return __hiloint2double((int)q[2], (int)q[0]);
+}
+
+// Waits until the N lines starting at the even words addr(j) are current,
+// re-reading stale ones (LOADED: the first reads are already in q). False
+// when the wait timed out or another workgroup gave up (the abort flag).
+// Addresses are recomputed for each re-read rather than held in registers.
+template <int N, bool LOADED = false, typename F>
+__device__ __forceinline__ bool ll_wait(const LLCtx& c, F addr, u32x4 (&q)[N]) {
+  if (!LOADED) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) q[j] = ll_ld(c, addr(j));
+  }
+  for (int spins = 0;; ++spins) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < N; ++j) ok = ok & ll_fresh(q[j], c.flag);
+    if (ok) return true;
+    if (spins > LL_SPIN_LIMIT) {
+      __hip_atomic_store((MOSHI_GLB int*)c.abort, 1, MOSHI_RLX, MOSHI_AGT);
+      return false;
+    }
+    if ((spins & 15) == 15 && __hip_atomic_load((MOSHI_GLB int*)c.abort, MOSHI_RLX, MOSHI_AGT))
+      return false;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if (!ll_fresh(q[j], c.flag)) q[j] = ll_ld(c, addr(j));
+  }
+}
+
+// The same for N single words (8-byte loads) at words addr(j).
+template <int N, typename F>
+__device__ __forceinline__ bool ll_wait_words(const LLCtx& c, F addr, uint64_t (&q)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) q[j] = ld_u64<true>(c.w + addr(j));
+  for (int spins = 0;; ++spins) {
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < N; ++j) ok = ok & ((uint32_t)(q[j] >> 32) == c.flag);
+    if (ok) return true;
+    if (spins > LL_SPIN_LIMIT) {
+      __hip_atomic_store((MOSHI_GLB int*)c.abort, 1, MOSHI_RLX, MOSHI_AGT);
+      return false;
+    }
+    if ((spins & 15) == 15 && __hip_atomic_load((MOSHI_GLB int*)c.abort, MOSHI_RLX, MOSHI_AGT))
+      return false;
+    __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int j = 0; j < N; ++j)
+      if ((uint32_t)(q[j] >> 32) != c.flag) q[j] = ld_u64<true>(c.w + addr(j));
+  }
+}
+
+// Stored bits of a model-dtype value in a word's payload, as a double.
+template <typename T>
+__device__ __forceinline__ double ll_val(uint32_t payload) {
+  return sizeof(T) == 2 ? (double)__uint_as_float(payload << 16) : (double)__uint_as_float(payload);
+}
+
+// PRO_NORM / PRO_CAST input from a flagged fp64 vector at word ox (PRO_NORM:
+// sums of squares per pair at word os), in build_input's arithmetic: pair
+// p = t (K / 2 <= NTH), partial t, the scale from rms_finish. False = leave.
+template <typename T, int PRO, int NTH>
+__device__ __forceinline__ bool ll_input_x(const GemmArgs& a, const LLCtx& c, size_t ox, size_t os,
+                                           T* xs, double* red) {
+  const int t = tid();
+  const int np = a.K / 2;
+  const int p = t < np ? t : np - 1;
+  double g0 = 1.0, g1 = 1.0;
+  if constexpr (PRO == PRO_NORM) ld_pair_d((const T*)a.gain, p, g0, g1);
+  const int n = a.n_ssq;
+  const int pn = t < n ? t : n - 1;
+  auto wd = [&](int j) {
+    return j < 2 ? ox + 4 * (size_t)p + 2 * j : (PRO == PRO_NORM ? os + 2 * (size_t)pn : ox);
+  };
+  u32x4 q[3];
+  const bool ok = ll_wait<3>(c, wd, q);
+  if (__syncthreads_or(!ok)) return false;
+  const double x0 = ll_f64(q[0]), x1 = ll_f64(q[1]);
+  double rs = 1.0;
+  if constexpr (PRO == PRO_NORM) {
+    double sum = 0.0;
+    if (t < n) sum += ll_f64(q[2]);
+    rs = rms_finish(sum, a, red, NTH);
+  }
+  if (t < np) {
+    const double v0 = PRO == PRO_NORM ? x0 * rs * g0 : x0;
+    const double v1 = PRO == PRO_NORM ? x1 * rs * g1 : x1;
+    put_pair<T, false>(xs, nullptr, t, v0, v1);
+  }
+  return true;
+}
+
+// PRO_DIRECT input from a flagged model-dtype vector at word ov (K <= 8 NTH).
+template <typename T, int NTH>
+__device__ __forceinline__ bool ll_input_direct(const GemmArgs& a, const LLCtx& c, size_t ov,
+                                                T* xs) {
+  constexpr int ML = 4;
+  const int t = tid();
+  const int nl = a.K / 2;  // lines, two values each
+  auto wd = [&](int j) {
+    const int i = t + j * NTH;
+    return ov + 2 * (size_t)(i < nl ? i : nl - 1);
+  };
+  u32x4 q[ML];
+  const bool ok = ll_wait<ML>(c, wd, q);
+#pragma unroll
+  for (int j = 0; j < ML; ++j) {
+    const int i = t + j * NTH;
+    if (i < nl) {
+      if constexpr (sizeof(T) == 2) {
+        *(uint32_t*)(xs + 2 * i) = (q[j][0] & 0xffffu) | (q[j][2] << 16);
+      } else {
+        *(uint64_t*)(xs + 2 * i) = (uint64_t)q[j][0] | ((uint64_t)q[j][2] << 32);
+      }
+    }
+  }
+  return !__syncthreads_or(!ok);
+}
+
+// Greedy token from flagged per-tile argmax partials at word ap, in
+// reduce_token's arithmetic. ok = false when a wait gave up.
+template <int NTH>
+__device__ __forceinline__ int ll_reduce_token(const LLCtx& c, size_t ap, int n_tiles, int n_rows,
+                                               bool& ok) {
+  constexpr int NW = NTH / 64;
+  __shared__ double s_v[NW];
+  __shared__ int s_i[NW];
+  const int t = tid();
+  double bv = -INFINITY;
+  int bi = 0x7fffffff;
+  ok = true;
+  for (int i = t; i < n_tiles; i += NTH) {
+    u32x4 q[2];
+    ok = ok & ll_wait<2>(c, [&](int j) { return ap + 4 * (size_t)i + 2 * j; }, q);
+    const double v = ll_f64(q[0]);
+    const int idx = (int)q[1][0];
+    if (arg_better(v, idx, bv, bi)) {
+      bv = v;
+      bi = idx;
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const double ov = shfl_xor_d(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (arg_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if ((t & 63) == 0) {
+    s_v[t >> 6] = bv;
+    s_i[t >> 6] = bi;
+  }
+  __syncthreads();
+  bv = s_v[0];
+  bi = s_i[0];
+  for (int w = 1; w < NW; ++w)
+    if (arg_better(s_v[w], s_i[w], bv, bi)) {
+      bv = s_v[w];
+      bi = s_i[w];
+    }
+  __syncthreads();
+  return bi < n_rows ? bi : 0;
+}
+
+// Input of a substep's first q/k/v projection (build_entry_input's
+// arithmetic): the previous token (from the text head's partials at s = 0,
+// else from the previous substep's flagged head partials), y = pre + E[tok];
+// the `first` workgroup stores y as the flagged vector Y and the token.
+struct EntryLL {
+  const ArgPart* text_part;  // s = 0: the text head's partials (plain)
+  size_t ap;                 // s > 0: word of the previous head's flagged partials
+  int prev_rows;
+  const double* pre;
+  const void* table;
+  size_t y;                  // word of Y[s]
+  int* tok_out;
+};
+
+template <typename T, int NTH>
+__device__ __forceinline__ bool ll_input_entry(const GemmArgs& a, const LLCtx& c, const EntryLL& E,
+                                               T* xs, double* red, bool first) {
+  const int t = tid();
+  const int np = a.K / 2;  // <= NTH
+  const T* g = (const T*)a.gain;
+  const int p0 = t < np ? t : np - 1;
+  double pv[2], gv[2];
+  ld_pair_f64<true>(E.pre, p0, pv[0], pv[1]);
+  ld_pair_d(g, p0, gv[0], gv[1]);
+  const int n_tiles = (E.prev_rows + 15) / 16;
+  bool ok = true;
+  const int tok = E.text_part != nullptr ? reduce_token<NTH>(E.text_part, n_tiles, E.prev_rows)
+                                         : ll_reduce_token<NTH>(c, E.ap, n_tiles, E.prev_rows, ok);
+  if (__syncthreads_or(!ok)) return false;
+  if (first && t == 0) st_i32<true>(E.tok_out, tok);
+  const T* row = (const T*)E.table + (size_t)tok * a.K;
+  double ev[2];
+  ld_pair_d(row, p0, ev[0], ev[1]);
+  const double y0 = pv[0] + ev[0], y1 = pv[1] + ev[1];
+  double sum = 0.0;
+  if (t < np) {
+    if (first) {
+      ll_put_f64(c, E.y + 4 * (size_t)t, y0);
+      ll_put_f64(c, E.y + 4 * (size_t)t + 2, y1);
+    }
+    sum += sq_pair(y0, y1);
+  }
+  const double rs = rms_finish(sum, a, red, NTH);
+  if (t < np) put_pair<T, false>(xs, nullptr, t, y0 * rs * gv[0], y1 * rs * gv[1]);
+  return true;
+}
+
+// Where a flagged projection reads and writes (word offsets in the arena).
+struct LLIo {
+  size_t x, ss;      // PRO_NORM / PRO_CAST input (fp64) and its sums of squares; PRO_DIRECT: x
+  size_t resid;      // EPI_RESID: residual rows (fp64)
+  size_t out, out_ss;  // EPI_RESID: new residual, its sums of squares; EPI_SWIGLU: act;
+                       // EPI_ARGMAX: partials
+  size_t q, k, v;    // EPI_QKV
+};
+
+// Epilogue of the R = 2 rows a wave owns (lane 0), flagged outputs:
+// wave_epilogue's arithmetic. rv: the residual rows (EPI_RESID).
+template <typename T, int EPI>
+__device__ __forceinline__ void ll_wave_epilogue(const GemmArgs& a, const LLCtx& c, const LLIo& io,
+                                                 int tile, int w, const double* v,
+                                                 const double* rv) {
+  constexpr int R = 2;
+  if constexpr (EPI == EPI_RESID) {
+    const int row0 = tile * 16 + w * R;
+    if (row0 >= a.N) return;
+    double xn[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) xn[r] = rv[r] + v[r];
+    double ss = 0.0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (row0 + r < a.N) {
+        ll_put_f64(c, io.out + 2 * (size_t)(row0 + r), xn[r]);
+        ss += xn[r] * xn[r];
+      }
+    }
+    ll_put_f64(c, io.out_ss + 2 * (size_t)(row0 / R), ss);
+  } else if constexpr (EPI == EPI_QKV) {
+    const int row0 = tile * 16 + w * R;
+    if (row0 >= a.N) return;
+    const int part = row0 / a.dq;
+    const int din = row0 - part * a.dq;
+    if (part == 0) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) ll_put_f64(c, io.q + 2 * (size_t)(din + r), v[r]);
+    } else {
+      const size_t base = (part == 1 ? io.k : io.v) + din;
+#pragma unroll
+      for (int r = 0; r < R; ++r) ll_put(c, base + r, stored_bits<T>(v[r]));
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    const int u0 = tile * 8 + w;
+    if (u0 < a.N) {
+      const double gt = v[0], up = v[1];
+      const double r_ = gt / (1.0 + exp(-gt)) * up;
+      ll_put(c, io.out + u0, stored_bits<T>(r_));
+    }
+  }
+}
+
+// Argmax partial of a finished 16-row tile (epilogue's EPI_ARGMAX for one
+// session): lanes 0, 16, 32, 48 of wave 0 hold rows 4g..4g+3 in v.
+template <typename T>
+__device__ __forceinline__ void ll_argmax_epilogue(const GemmArgs& a, const LLCtx& c,
+                                                   const LLIo& io, int tile, int g,
+                                                   const double* v) {
+  double bv = -INFINITY;
+  int bi = 0x7fffffff;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tile * 16 + 4 * g + i;
+    if (row < a.N) {
+      *(MOSHI_GLB float*)(a.logits + row) = (float)v[i];  // host reads
+      const double val = (v[i] != v[i]) ? -INFINITY : v[i];
+      if (bi == 0x7fffffff || val > bv) {
+        bv = val;
+        bi = row;
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 16; off <= 32; off <<= 1) {
+    const double ov = shfl_xor_d(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (arg_better(ov, oi, bv, bi)) {
+      bv = ov;
+      bi = oi;
+    }
+  }
+  if (g == 0) {
+    ll_put_f64(c, io.out + 4 * (size_t)tile, bv);
+    ll_put(c, io.out + 4 * (size_t)tile + 2, (uint32_t)bi);
+    ll_put(c, io.out + 4 * (size_t)tile + 3, 0u);
+  }
+}
+
+// A projection from a weight slice staged by gemv_stage (gemv_staged's
+// arithmetic and work split) whose input and outputs are flagged vectors.
+// Workgroups without rows skip it, except workgroup 0, which always waits
+// for the input (its trace stamp marks the end of the previous operation).
+// False = leave (a wait gave up).
+template <typename T, int KW, int PRO, int EPI, bool ENTRY = false>
+__device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const LLIo& io, int wg,
+                                        int nwg, T* xs, const unsigned char* wbuf,
+                                        const EntryLL* ent, uint64_t* stamp) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int R = 16 / KW;
+  constexpr int NTH = 64 * KW;
+  static_assert(R == 2, "row pairs");
+  const int t = tid();
+  const int lane = t & 63, wave = t >> 6;
+  __shared__ double s_red[2][16];
+  __shared__ double s_tmp[KW];
+  const int ngroups = a.K / VEC;
+  const int cpl = staged_cpl<T>(a.K);
+  bool wg_any;
+  if constexpr (staged_by_tile<EPI>()) {
+    wg_any = wg < n_tiles_of(EPI, a.N);
+  } else {
+    const int P = EPI == EPI_SWIGLU ? a.N : (a.N + 1) / 2;
+    wg_any = wg * P / nwg < (wg + 1) * P / nwg;
+  }
+  if (!wg_any && wg != 0) return true;
+  int te, we;
+  const bool any = staged_item<EPI, KW>(a, wg, nwg, wave, 0, te, we);
+  // residual rows of the wave's first item, requested before the input
+  u32x4 rq[2];
+  const int rrow0 = any ? te * 16 + we * R : 0;
+  auto rw = [&](int r) { return io.resid + 2 * (size_t)(rrow0 + r < a.N ? rrow0 + r : rrow0); };
+  if constexpr (EPI == EPI_RESID) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) rq[r] = ll_ld(c, rw(r));
+  }
+  bool ok;
+  if constexpr (ENTRY)
+    ok = ll_input_entry<T, NTH>(a, c, *ent, xs, s_tmp, wg == 0);
+  else if constexpr (PRO == PRO_DIRECT)
+    ok = ll_input_direct<T, NTH>(a, c, io.x, xs);
+  else
+    ok = ll_input_x<T, PRO, NTH>(a, c, io.x, io.ss, xs, s_tmp);
+  if (!ok) return false;
+  if constexpr (EPI == EPI_RESID) {
+    const bool rok = ll_wait<2, true>(c, rw, rq);
+    if (__syncthreads_or(!rok)) return false;
+  }
+  if (stamp != nullptr && wg == 0 && t == 0) *(MOSHI_GLB uint64_t*)stamp = wall_clock64();
+  __syncthreads();
+  if (!wg_any) return true;
+  // this wave's LDS-direct loads have landed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  const MOSHI_LDS unsigned char* base = (const MOSHI_LDS unsigned char*)wbuf;
+  int parity = 0, slot = 0;
+  for (int j = 0; staged_item<EPI, KW>(a, wg, nwg, wave, j, te, we); ++j) {
+    double acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.0;
+#pragma unroll 2
+    for (int cc = 0; cc < cpl; ++cc, slot += R) {
+      const int gi = cc * 64 + lane;
+      if (gi < ngroups) {
+        double xv[VEC];
+        widen<T>(*(const u32x4*)(xs + (size_t)gi * VEC), xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          double wd[VEC];
+          widen<T>(*(const MOSHI_LDS u32x4*)(base + (((slot + r) * KW + wave) * 64 + lane) * 16), wd);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = group_reduce<64>(acc[r]);
+    if constexpr (EPI == EPI_ARGMAX) {
+      if (lane == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) s_red[parity][wave * R + r] = acc[r];
+      }
+      __syncthreads();
+      if (wave == 0 && (lane & 15) == 0) {
+        const int g = lane >> 4;
+        const double v[4] = {s_red[parity][4 * g], s_red[parity][4 * g + 1],
+                             s_red[parity][4 * g + 2], s_red[parity][4 * g + 3]};
+        ll_argmax_epilogue<T>(a, c, io, te, g, v);
+      }
+      parity ^= 1;
+    } else {
+      if (lane == 0) {
+        double rv[R] = {0.0, 0.0};
+        if constexpr (EPI == EPI_RESID) {
+          if (j == 0) {
+            rv[0] = ll_f64(rq[0]);
+            rv[1] = ll_f64(rq[1]);
+          } else {
+            // later items (only with many rows per workgroup): wait here
+            const int row0 = te * 16 + we * R;
+            u32x4 q2[2];
+            (void)ll_wait<2>(
+                c,
+                [&](int r) { return io.resid + 2 * (size_t)(row0 + r < a.N ? row0 + r : row0); },
+                q2);  // a timeout raises the abort flag; the host fails the step
+            rv[0] = ll_f64(q2[0]);
+            rv[1] = ll_f64(q2[1]);
+          }
+        }
+        ll_wave_epilogue<T, EPI>(a, c, io, te, we, acc, rv);
+      }
+    }
+  }
+  __syncthreads();  // xs, s_red and the slots may be reused by the caller
+  return true;
+}
+
+// Attention of depformer head h at substep s (keys: entries 0..s of this
+// layer), by wave 0 of one workgroup, from the flagged q, K and V: the
+// arithmetic of dep_attention for one head. The output goes to the flagged
+// O[s][l]. False = leave.
+template <typename T, int HD, int NTH>
+__device__ __forceinline__ bool ll_dep_attention(const LLCtx& c, const LLMap& M, int s, int l,
+                                                 int h) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int TK = HD / VEC;
+  constexpr int KPW = 64 / TK;
+  constexpr int NP = (DEP_MAX_KEYS + KPW - 1) / KPW;
+  constexpr int DPL = HD > 64 ? HD / 64 : 1;
+  constexpr int KL = NP * VEC / 2;  // K lines per lane
+  __shared__ double s_sc[64];
+  __shared__ int s_bad;
+  const int t = tid();
+  const int lane = t & 63;
+  const int kd = lane % TK, kq = lane / TK;
+  const int nvalid = s + 1;
+  if (t == 0) s_bad = 0;
+  __syncthreads();
+  if (t < 64) {
+    const double scale = 1.0 / sqrt((double)HD);
+    // q (VEC fp64 lines) and K (VEC/2 lines per key pass)
+    auto wq = [&](int e) { return M.Q(s, l) + 2 * (size_t)(h * HD + kd * VEC + e); };
+    auto wk = [&](int i) {
+      const int p = i / (VEC / 2), e2 = i % (VEC / 2);
+      const int j = p * KPW + kq;
+      return M.K(j < nvalid ? j : 0, l) + (size_t)(h * HD + kd * VEC + 2 * e2);
+    };
+    bool ok;
+    {
+      u32x4 qq[VEC], kk[KL];
+      ok = ll_wait<VEC>(c, wq, qq);
+      ok = ok & ll_wait<KL>(c, wk, kk);
+      double qv[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qv[e] = ll_f64(qq[e]);
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        double d = 0.0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          const u32x4& q = kk[p * (VEC / 2) + e / 2];
+          d = fma(qv[e], ll_val<T>(q[2 * (e & 1)]), d);
+        }
+        d = group_reduce<TK>(d);
+        const int j = p * KPW + kq;
+        if (kd == 0 && j < DEP_MAX_KEYS) s_sc[j] = d * scale;
+      }
+    }
+    // V: entry j, dims lane + 64 i (one word each)
+    auto wv = [&](int n) {
+      const int j = n / DPL, i = n % DPL;
+      const int dd = (lane + 64 * i) < HD ? lane + 64 * i : 0;
+      return M.V(j < nvalid ? j : 0, l) + (size_t)(h * HD + dd);
+    };
+    uint64_t vq[DEP_MAX_KEYS * DPL];
+    ok = ok & ll_wait_words<DEP_MAX_KEYS * DPL>(c, wv, vq);
+    // softmax over the valid keys
+    const double sv = lane < nvalid ? s_sc[lane] : -INFINITY;
+    const double m = group_reduce<64, true>(sv);
+    const double pj = (sv == -INFINITY) ? 0.0 : exp(sv - m);
+    const double lsum = group_reduce<64>(pj);
+    s_sc[lane] = pj;
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      const int dd = lane + 64 * i;
+      double od = 0.0;
+#pragma unroll
+      for (int j = 0; j < DEP_MAX_KEYS; ++j) {
+        if (j < nvalid) od = fma(s_sc[j], ll_val<T>((uint32_t)vq[j * DPL + i]), od);
+      }
+      if (dd < HD) {
+        const double ov = lsum > 0.0 ? od / lsum : 0.0;
+        ll_put(c, M.O(s, l) + (size_t)(h * HD + dd), stored_bits<T>(ov));
+      }
+    }
+    if (!ok) s_bad = 1;
+  }
+  __syncthreads();
+  return s_bad == 0;
+}
+
 template <typename T, int HD, int HDD>
 __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
                                                   const int* __restrict__ frames, int* text_out,
-                                                  int* codes_out, int parity, uint64_t* trace) {
+                                                  int* codes_out, int parity, uint32_t seq,
+                                                  uint64_t* trace) {
   static_assert(HDD % 16 == 0, "a depformer q/k/v tile holds rows of one head");
   constexpr int DEP_TILES_PER_HEAD = 3 * HDD / 16;  // q, k and v tiles
   extern __shared__ __align__(16) unsigned char s_dyn[];  // GEMV input or attention scratch
@@ -434,62 +1012,92 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   GEMV(PRO_DIRECT, EPI_STORE, uni(A.d_in));
   STAGE_SYNC(EPI_QKV, d_qkv(0, 0));
 
-  // ---- 16 substeps ----
+  // ---- 16 substeps: the operations hand on flagged vectors, no grid barriers ----
+  LLCtx c;
+  c.w = uni(A.ll);
+  c.flag = seq;
+  c.abort = uni(A.abort);
+  LLMap M;
+  M.Dd = Dd;
+  M.Fd = uni(A.d_gu.N);
+  M.Ld = Ld;
+  M.nta = (Va + 15) / 16;
+  const int nqkv = 3 * Dd / 16;  // q/k/v tiles; head h's attention runs on workgroup (nqkv + h) % nwg
+  unsigned tix = g.idx;          // trace entry of the last operation's end
+  auto stamp = [&]() -> uint64_t* {
+    ++tix;
+    return trace != nullptr ? trace + tix : nullptr;
+  };
   for (int s = 0; s < S; ++s) {
     for (int l = 0; l < Ld; ++l) {
+      LLIo io{};
+      io.q = M.Q(s, l);
+      io.k = M.K(s, l);
+      io.v = M.V(s, l);
       if (l == 0) {
-        // The substep's entry (previous token -> residual) is folded into its
-        // first q/k/v projection: every workgroup forms the normed input from
-        // the previous head's partials itself; workgroup 0 stores the
-        // residual and the token.
-        EntryIn E;
-        E.apart = uni(A.apart);
+        // the substep's entry (previous token -> residual) is folded into its
+        // first q/k/v projection: every workgroup forms the normed input
+        // itself; workgroup 0 stores the residual Y and the token
+        EntryLL E;
+        E.text_part = s == 0 ? uni(A.apart) : nullptr;
+        E.ap = s == 0 ? 0 : M.AP(s - 1, S);
         E.prev_rows = s == 0 ? uni(A.Vt) : Va;
         E.pre = uni(A.pre) + (size_t)s * Dd;
         E.table = tab(o_de + s);
-        E.y = uni(A.y);
+        E.y = M.Y(s, S);
         E.tok_out = s == 0 ? text_out : codes_out + (s - 1);
-        gemv_staged<T, KW, PRO_NORM, EPI_QKV, true, true>(d_qkv(s, 0), wg, nwg, xs, wbuf, nullptr, &E);
+        // at s = 0 the grid barrier after the input projections ended the
+        // previous operation
+        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, true>(d_qkv(s, 0), c, io, wg, nwg, xs, wbuf, &E,
+                                                     s == 0 ? nullptr : stamp()))
+          return;
       } else {
-        GEMV_S(PRO_NORM, EPI_QKV, d_qkv(s, l));
+        io.x = M.R2(s, l - 1);
+        io.ss = M.S2(s, l - 1);
+        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV>(d_qkv(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
+                                               stamp()))
+          return;
       }
-      {
-        // A q/k/v tile holds 16 rows of one head. The workgroup that stores
-        // the last of a head's tiles computes that head's attention.
-        AttnArgs at = uni(A.d_attn);
-        at.layer_off = (int64_t)l * d_lel;
-        const unsigned goal = (unsigned)((s * Ld + l + 1) * DEP_TILES_PER_HEAD);
-        __shared__ int s_last;
-        drain_stores();
-        __syncthreads();
-        for (int tile = wg; tile * 16 < 3 * Dd; tile += nwg) {
-          const int h = (tile * 16 % Dd) / HDD;
-          if (threadIdx.x == 0) {
-            const unsigned old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)tickets + (H + h) * 16, 1u,
-                                                        MOSHI_RLX, MOSHI_AGT);
-            s_last = old + 1 == goal;
-          }
-          __syncthreads();
-          if (s_last) dep_attention<T, HDD, NT, true, 1>(at, 0, h, 1, s + 1);
-          __syncthreads();
-        }
-      }
-      STAGE_SYNC(EPI_RESID, d_o(s, l));
-      GEMV_S(PRO_DIRECT, EPI_RESID, d_o(s, l));
-      STAGE_SYNC(EPI_SWIGLU, d_gu(s, l));
-      GEMV_S(PRO_NORM, EPI_SWIGLU, d_gu(s, l));
-      STAGE_SYNC(EPI_RESID, d_dn(s, l));
-      GEMV_S(PRO_DIRECT, EPI_RESID, d_dn(s, l));
+      gemv_stage<T, KW, EPI_RESID>(d_o(s, l), wg, nwg, wbuf);
+      for (int h = 0; h < Hd; ++h)
+        if ((nqkv + h) % nwg == wg && !ll_dep_attention<T, HDD, NT>(c, M, s, l, h)) return;
+      io = LLIo{};
+      io.x = M.O(s, l);
+      io.resid = l == 0 ? M.Y(s, S) : M.R2(s, l - 1);
+      io.out = M.R1(s, l);
+      io.out_ss = M.S1(s, l);
+      if (!ll_gemv<T, KW, PRO_DIRECT, EPI_RESID>(d_o(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
+                                                 stamp()))
+        return;
+      gemv_stage<T, KW, EPI_SWIGLU>(d_gu(s, l), wg, nwg, wbuf);
+      io = LLIo{};
+      io.x = M.R1(s, l);
+      io.ss = M.S1(s, l);
+      io.out = M.A(s, l);
+      if (!ll_gemv<T, KW, PRO_NORM, EPI_SWIGLU>(d_gu(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
+                                                stamp()))
+        return;
+      gemv_stage<T, KW, EPI_RESID>(d_dn(s, l), wg, nwg, wbuf);
+      io = LLIo{};
+      io.x = M.A(s, l);
+      io.resid = M.R1(s, l);
+      io.out = M.R2(s, l);
+      io.out_ss = M.S2(s, l);
+      if (!ll_gemv<T, KW, PRO_DIRECT, EPI_RESID>(d_dn(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
+                                                 stamp()))
+        return;
       if (l + 1 < Ld)
-        STAGE_SYNC(EPI_QKV, d_qkv(s, l + 1));
+        gemv_stage<T, KW, EPI_QKV>(d_qkv(s, l + 1), wg, nwg, wbuf);
       else
-        STAGE_SYNC(EPI_ARGMAX, d_head(s));
+        gemv_stage<T, KW, EPI_ARGMAX>(d_head(s), wg, nwg, wbuf);
     }
-    GEMV_S(PRO_CAST, EPI_ARGMAX, d_head(s));
-    if (s + 1 < S)
-      STAGE_SYNC(EPI_QKV, d_qkv(s + 1, 0));
-    else if (grid_sync(g))
+    LLIo io{};
+    io.x = M.R2(s, Ld - 1);
+    io.out = M.AP(s, S);
+    if (!ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX>(d_head(s), c, io, wg, nwg, xs, wbuf, nullptr,
+                                              stamp()))
       return;
+    if (s + 1 < S) gemv_stage<T, KW, EPI_QKV>(d_qkv(s + 1, 0), wg, nwg, wbuf);
   }
 #undef GEMV
 #undef GEMV_S
@@ -498,21 +1106,25 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
 #undef PREFETCH_SYNC_G
   // ---- last code, next position ----
   if (wg == 0) {
-    const int tok = reduce_token<NT>(uni(A.apart), (Va + 15) / 16, Va);
+    bool ok;
+    const int tok = ll_reduce_token<NT>(c, M.AP(S - 1, S), (Va + 15) / 16, Va, ok);
+    uint64_t* st = stamp();
     if (threadIdx.x == 0) {
+      if (st != nullptr) *(MOSHI_GLB uint64_t*)st = wall_clock64();
       *(MOSHI_GLB int*)(codes_out + S - 1) = tok;
       int64_t* pos = uni(A.pos);
       if (ldg(uni(A.live))) *(MOSHI_GLB int64_t*)pos += 1;
+      if (trace != nullptr) *(MOSHI_GLB uint64_t*)(trace + tix + 1) = wall_clock64();
     }
   }
-  if (trace != nullptr && wg == 0 && threadIdx.x == 0) *(MOSHI_GLB uint64_t*)(trace + g.idx + 1) = wall_clock64();
 }
 
 template <typename T, int HD, int HDD>
 hipError_t launch_t(const StepArgs* dP, const int* frames, int* text_out, int* codes_out,
-                    int parity, int nwg, size_t lds, hipStream_t st, uint64_t* trace) {
+                    int parity, uint32_t seq, int nwg, size_t lds, hipStream_t st,
+                    uint64_t* trace) {
   void* args[] = {(void*)&dP,     (void*)&frames, (void*)&text_out, (void*)&codes_out,
-                  (void*)&parity, (void*)&trace};
+                  (void*)&parity, (void*)&seq,    (void*)&trace};
   return hipLaunchCooperativeKernel((const void*)step_kernel<T, HD, HDD>, dim3(nwg), dim3(NT), args,
                                     (unsigned)lds, st);
 }
@@ -545,12 +1157,14 @@ int step_max_grid(int dtype, int hd, int hdd, size_t lds) {
 }
 
 hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int* frames,
-                       int* text_out, int* codes_out, int parity, int nwg, size_t lds,
-                       hipStream_t st, uint64_t* trace) {
+                       int* text_out, int* codes_out, int parity, uint32_t seq, int nwg,
+                       size_t lds, hipStream_t st, uint64_t* trace) {
   if (dtype == DT_BF16 && hd == 128 && hdd == 64)
-    return launch_t<__bf16, 128, 64>(dP, frames, text_out, codes_out, parity, nwg, lds, st, trace);
+    return launch_t<__bf16, 128, 64>(dP, frames, text_out, codes_out, parity, seq, nwg, lds, st,
+                                      trace);
   if (dtype == DT_F32 && hd == 64 && hdd == 32)
-    return launch_t<float, 64, 32>(dP, frames, text_out, codes_out, parity, nwg, lds, st, trace);
+    return launch_t<float, 64, 32>(dP, frames, text_out, codes_out, parity, seq, nwg, lds, st,
+                                     trace);
   return hipErrorInvalidValue;
 }
 
