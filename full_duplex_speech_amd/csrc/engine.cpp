@@ -567,9 +567,17 @@ int setup_step(moshi_ctx* c) {
                    dn = d_dn_args(c, 0, 0), hd = d_head_args(c, 0);
     const std::pair<int, const GemmArgs*> ops[] = {
         {EPI_QKV, &q}, {EPI_RESID, &o}, {EPI_SWIGLU, &gu}, {EPI_RESID, &dn}, {EPI_ARGMAX, &hd}};
+    // the kernel's register copies of each wave's slice are sized per operation
+    const int max_i[] = {LLR_QKV_I, LLR_O_I, LLR_GU_I, LLR_DN_I, LLR_HD_I};
+    const int max_c[] = {LLR_QKV_C, LLR_O_C, LLR_GU_C, LLR_DN_C, LLR_HD_C};
+    int k = 0;
     for (const auto& op : ops) {
       const int64_t b = staged_slice_bytes((int)vec, op.first, op.second->N, op.second->K, grid);
       staged = b > staged ? b : staged;
+      const int cpl = (int)((op.second->K / (int)vec + 63) / 64);
+      if (staged_items_per_wave(op.first, op.second->N, grid) > max_i[k] || cpl > max_c[k])
+        return MOSHI_OK;
+      ++k;
     }
   }
   lds = wbuf + staged > lds ? wbuf + staged : lds;

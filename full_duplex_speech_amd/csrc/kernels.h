@@ -201,9 +201,24 @@ hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int
                        int* text_out, int* codes_out, int parity, uint32_t seq, int nwg,
                        size_t lds_bytes, hipStream_t st, uint64_t* trace);
 // Words of the flagged depformer vectors (step.hip's layout): per substep and
-// layer 11 Dd + Fd, then per substep 2 Dd + 4 ceil(Va / 16).
+// layer 11 Dd + Fd, then per substep 2 Dd + 32 ceil(Va / 16).
 inline int64_t step_ll_words(int S, int Ld, int Dd, int Fd, int Va) {
-  return (int64_t)S * Ld * (11LL * Dd + Fd) + (int64_t)S * (2LL * Dd + 4LL * ((Va + 15) / 16));
+  return (int64_t)S * Ld * (11LL * Dd + Fd) + (int64_t)S * (2LL * Dd + 32LL * ((Va + 15) / 16));
+}
+// Register copies of the depformer weight slices in the step kernel: at most
+// I items (row pairs) per wave and C column passes (ceil(K / vec / 64)) for
+// the q/k/v, output, gate/up, down and head projections.
+constexpr int LLR_QKV_I = 1, LLR_QKV_C = 2;
+constexpr int LLR_O_I = 1, LLR_O_C = 2;
+constexpr int LLR_GU_I = 2, LLR_GU_C = 2;
+constexpr int LLR_DN_I = 1, LLR_DN_C = 6;
+constexpr int LLR_HD_I = 1, LLR_HD_C = 2;
+// Items per wave of a one-session staged projection on nwg workgroups (the
+// split of gemv_stage).
+inline int staged_items_per_wave(int epi, int N, int nwg) {
+  if (epi == EPI_QKV || epi == EPI_ARGMAX) return ((N + 15) / 16 + nwg - 1) / nwg;
+  const int64_t pairs = epi == EPI_SWIGLU ? N : (N + 1) / 2;
+  return (int)(((pairs + nwg - 1) / nwg + GEMV_KW - 1) / GEMV_KW);
 }
 constexpr int STEP_TRACE_MAX = 4096;
 // LDS bytes of one workgroup's staged weight slice in the step kernel: the

@@ -277,8 +277,8 @@ __device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frame
 //   [Dd], Q [2 Dd] queries, K [Dd], V [Dd] (rounded), O [Dd] attention
 //   output (rounded), A [Fd] SwiGLU output (rounded);
 // then for each substep, Y [2 Dd] (the substep's input residual) and AP
-// [4 ceil(Va / 16)] (per-tile argmax partials of its head: value low, value
-// high, index, 0).
+// [32 ceil(Va / 16)] (argmax partials of its head, one per row pair: value
+// low, value high, index, 0).
 
 constexpr int LL_SPIN_LIMIT = 1 << 20;
 
@@ -290,34 +290,35 @@ struct LLCtx {
 
 struct LLMap {
   int Dd, Fd, Ld, nta;
-  __device__ size_t layer(int s, int l) const { return (size_t)(s * Ld + l) * (11 * Dd + Fd); }
-  __device__ size_t R1(int s, int l) const { return layer(s, l); }
-  __device__ size_t S1(int s, int l) const { return layer(s, l) + 2 * Dd; }
-  __device__ size_t R2(int s, int l) const { return layer(s, l) + 3 * Dd; }
-  __device__ size_t S2(int s, int l) const { return layer(s, l) + 5 * Dd; }
-  __device__ size_t Q(int s, int l) const { return layer(s, l) + 6 * Dd; }
-  __device__ size_t K(int s, int l) const { return layer(s, l) + 8 * Dd; }
-  __device__ size_t V(int s, int l) const { return layer(s, l) + 9 * Dd; }
-  __device__ size_t O(int s, int l) const { return layer(s, l) + 10 * Dd; }
-  __device__ size_t A(int s, int l) const { return layer(s, l) + 11 * Dd; }
-  __device__ size_t sub(int s, int S) const {
-    return layer(S, 0) + (size_t)s * (2 * Dd + 4 * nta);
+  // word indices (the host keeps the arena under 2 GB, so they fit 32 bits)
+  __device__ uint32_t layer(int s, int l) const { return (uint32_t)(s * Ld + l) * (11 * Dd + Fd); }
+  __device__ uint32_t R1(int s, int l) const { return layer(s, l); }
+  __device__ uint32_t S1(int s, int l) const { return layer(s, l) + 2 * Dd; }
+  __device__ uint32_t R2(int s, int l) const { return layer(s, l) + 3 * Dd; }
+  __device__ uint32_t S2(int s, int l) const { return layer(s, l) + 5 * Dd; }
+  __device__ uint32_t Q(int s, int l) const { return layer(s, l) + 6 * Dd; }
+  __device__ uint32_t K(int s, int l) const { return layer(s, l) + 8 * Dd; }
+  __device__ uint32_t V(int s, int l) const { return layer(s, l) + 9 * Dd; }
+  __device__ uint32_t O(int s, int l) const { return layer(s, l) + 10 * Dd; }
+  __device__ uint32_t A(int s, int l) const { return layer(s, l) + 11 * Dd; }
+  __device__ uint32_t sub(int s, int S) const {
+    return layer(S, 0) + (uint32_t)s * (2 * Dd + 32 * nta);
   }
-  __device__ size_t Y(int s, int S) const { return sub(s, S); }
-  __device__ size_t AP(int s, int S) const { return sub(s, S) + 2 * Dd; }
+  __device__ uint32_t Y(int s, int S) const { return sub(s, S); }
+  __device__ uint32_t AP(int s, int S) const { return sub(s, S) + 2 * Dd; }
 };
 
-__device__ __forceinline__ void ll_put(const LLCtx& c, size_t word, uint32_t payload) {
+__device__ __forceinline__ void ll_put(const LLCtx& c, uint32_t word, uint32_t payload) {
   st_u64<true>(c.w + word, (uint64_t)payload | ((uint64_t)c.flag << 32));
 }
-__device__ __forceinline__ void ll_put_f64(const LLCtx& c, size_t word, double v) {
+__device__ __forceinline__ void ll_put_f64(const LLCtx& c, uint32_t word, double v) {
   const uint64_t b = __builtin_bit_cast(uint64_t, v);
   ll_put(c, word, (uint32_t)b);
   ll_put(c, word + 1, (uint32_t)(b >> 32));
 }
 // the line holding words `word` (even) and word + 1
-__device__ __forceinline__ u32x4 ll_ld(const LLCtx& c, size_t word) {
-  return ld16_coh(c.w, (uint32_t)(word * 8));
+__device__ __forceinline__ u32x4 ll_ld(const LLCtx& c, uint32_t word) {
+  return ld16_coh(c.w, word * 8u);
 }
 __device__ __forceinline__ bool ll_fresh(const u32x4& q, uint32_t flag) {
   return (q[1] == flag) & (q[3] == flag);
@@ -355,10 +356,12 @@ __device__ __forceinline__ bool ll_wait(const LLCtx& c, F addr, u32x4 (&q)[N]) {
 }
 
 // The same for N single words (8-byte loads) at words addr(j).
-template <int N, typename F>
+template <int N, bool LOADED = false, typename F>
 __device__ __forceinline__ bool ll_wait_words(const LLCtx& c, F addr, uint64_t (&q)[N]) {
+  if (!LOADED) {
 #pragma unroll
-  for (int j = 0; j < N; ++j) q[j] = ld_u64<true>(c.w + addr(j));
+    for (int j = 0; j < N; ++j) q[j] = ld_u64<true>(c.w + addr(j));
+  }
   for (int spins = 0;; ++spins) {
     bool ok = true;
 #pragma unroll
@@ -387,7 +390,7 @@ __device__ __forceinline__ double ll_val(uint32_t payload) {
 // sums of squares per pair at word os), in build_input's arithmetic: pair
 // p = t (K / 2 <= NTH), partial t, the scale from rms_finish. False = leave.
 template <typename T, int PRO, int NTH>
-__device__ __forceinline__ bool ll_input_x(const GemmArgs& a, const LLCtx& c, size_t ox, size_t os,
+__device__ __forceinline__ bool ll_input_x(const GemmArgs& a, const LLCtx& c, uint32_t ox, uint32_t os,
                                            T* xs, double* red) {
   const int t = tid();
   const int np = a.K / 2;
@@ -397,7 +400,7 @@ __device__ __forceinline__ bool ll_input_x(const GemmArgs& a, const LLCtx& c, si
   const int n = a.n_ssq;
   const int pn = t < n ? t : n - 1;
   auto wd = [&](int j) {
-    return j < 2 ? ox + 4 * (size_t)p + 2 * j : (PRO == PRO_NORM ? os + 2 * (size_t)pn : ox);
+    return j < 2 ? ox + 4 * (uint32_t)p + 2 * j : (PRO == PRO_NORM ? os + 2 * (uint32_t)pn : ox);
   };
   u32x4 q[3];
   const bool ok = ll_wait<3>(c, wd, q);
@@ -419,14 +422,14 @@ __device__ __forceinline__ bool ll_input_x(const GemmArgs& a, const LLCtx& c, si
 
 // PRO_DIRECT input from a flagged model-dtype vector at word ov (K <= 8 NTH).
 template <typename T, int NTH>
-__device__ __forceinline__ bool ll_input_direct(const GemmArgs& a, const LLCtx& c, size_t ov,
+__device__ __forceinline__ bool ll_input_direct(const GemmArgs& a, const LLCtx& c, uint32_t ov,
                                                 T* xs) {
   constexpr int ML = 4;
   const int t = tid();
   const int nl = a.K / 2;  // lines, two values each
   auto wd = [&](int j) {
     const int i = t + j * NTH;
-    return ov + 2 * (size_t)(i < nl ? i : nl - 1);
+    return ov + 2 * (uint32_t)(i < nl ? i : nl - 1);
   };
   u32x4 q[ML];
   const bool ok = ll_wait<ML>(c, wd, q);
@@ -444,10 +447,12 @@ __device__ __forceinline__ bool ll_input_direct(const GemmArgs& a, const LLCtx& 
   return !__syncthreads_or(!ok);
 }
 
-// Greedy token from flagged per-tile argmax partials at word ap, in
-// reduce_token's arithmetic. ok = false when a wait gave up.
+// Greedy token from flagged argmax partials at word ap (n_part of them, one
+// per row pair), in reduce_token's arithmetic: the comparison is exact and
+// ties go to the lowest index, so the winner does not depend on how rows
+// were grouped into partials. ok = false when a wait gave up.
 template <int NTH>
-__device__ __forceinline__ int ll_reduce_token(const LLCtx& c, size_t ap, int n_tiles, int n_rows,
+__device__ __forceinline__ int ll_reduce_token(const LLCtx& c, uint32_t ap, int n_part, int n_rows,
                                                bool& ok) {
   constexpr int NW = NTH / 64;
   __shared__ double s_v[NW];
@@ -455,10 +460,27 @@ __device__ __forceinline__ int ll_reduce_token(const LLCtx& c, size_t ap, int n_
   const int t = tid();
   double bv = -INFINITY;
   int bi = 0x7fffffff;
-  ok = true;
-  for (int i = t; i < n_tiles; i += NTH) {
+  // partials t and t + NTH in one wait (clamped; duplicates are harmless)
+  {
+    auto wd = [&](int j) {
+      const int i = t + (j >> 1) * NTH;
+      return ap + 4 * (uint32_t)(i < n_part ? i : n_part - 1) + 2 * (j & 1);
+    };
+    u32x4 q[4];
+    ok = ll_wait<4>(c, wd, q);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const double v = ll_f64(q[2 * k]);
+      const int idx = (int)q[2 * k + 1][0];
+      if (t + k * NTH < n_part && arg_better(v, idx, bv, bi)) {
+        bv = v;
+        bi = idx;
+      }
+    }
+  }
+  for (int i = t + 2 * NTH; i < n_part; i += NTH) {
     u32x4 q[2];
-    ok = ok & ll_wait<2>(c, [&](int j) { return ap + 4 * (size_t)i + 2 * j; }, q);
+    ok = ok & ll_wait<2>(c, [&](int j) { return ap + 4 * (uint32_t)i + 2 * j; }, q);
     const double v = ll_f64(q[0]);
     const int idx = (int)q[1][0];
     if (arg_better(v, idx, bv, bi)) {
@@ -497,11 +519,11 @@ __device__ __forceinline__ int ll_reduce_token(const LLCtx& c, size_t ap, int n_
 // the `first` workgroup stores y as the flagged vector Y and the token.
 struct EntryLL {
   const ArgPart* text_part;  // s = 0: the text head's partials (plain)
-  size_t ap;                 // s > 0: word of the previous head's flagged partials
+  uint32_t ap;               // s > 0: word of the previous head's flagged partials
   int prev_rows;
   const double* pre;
   const void* table;
-  size_t y;                  // word of Y[s]
+  uint32_t y;                // word of Y[s]
   int* tok_out;
 };
 
@@ -517,19 +539,20 @@ __device__ __forceinline__ bool ll_input_entry(const GemmArgs& a, const LLCtx& c
   ld_pair_d(g, p0, gv[0], gv[1]);
   const int n_tiles = (E.prev_rows + 15) / 16;
   bool ok = true;
-  const int tok = E.text_part != nullptr ? reduce_token<NTH>(E.text_part, n_tiles, E.prev_rows)
-                                         : ll_reduce_token<NTH>(c, E.ap, n_tiles, E.prev_rows, ok);
+  const int tok = E.text_part != nullptr
+                      ? reduce_token<NTH>(E.text_part, n_tiles, E.prev_rows)
+                      : ll_reduce_token<NTH>(c, E.ap, 8 * n_tiles, E.prev_rows, ok);
   if (__syncthreads_or(!ok)) return false;
   if (first && t == 0) st_i32<true>(E.tok_out, tok);
-  const T* row = (const T*)E.table + (size_t)tok * a.K;
+  const T* row = (const T*)E.table + (uint32_t)tok * a.K;
   double ev[2];
   ld_pair_d(row, p0, ev[0], ev[1]);
   const double y0 = pv[0] + ev[0], y1 = pv[1] + ev[1];
   double sum = 0.0;
   if (t < np) {
     if (first) {
-      ll_put_f64(c, E.y + 4 * (size_t)t, y0);
-      ll_put_f64(c, E.y + 4 * (size_t)t + 2, y1);
+      ll_put_f64(c, E.y + 4 * (uint32_t)t, y0);
+      ll_put_f64(c, E.y + 4 * (uint32_t)t + 2, y1);
     }
     sum += sq_pair(y0, y1);
   }
@@ -540,11 +563,11 @@ __device__ __forceinline__ bool ll_input_entry(const GemmArgs& a, const LLCtx& c
 
 // Where a flagged projection reads and writes (word offsets in the arena).
 struct LLIo {
-  size_t x, ss;      // PRO_NORM / PRO_CAST input (fp64) and its sums of squares; PRO_DIRECT: x
-  size_t resid;      // EPI_RESID: residual rows (fp64)
-  size_t out, out_ss;  // EPI_RESID: new residual, its sums of squares; EPI_SWIGLU: act;
-                       // EPI_ARGMAX: partials
-  size_t q, k, v;    // EPI_QKV
+  uint32_t x, ss;      // PRO_NORM / PRO_CAST input (fp64), its sums of squares; PRO_DIRECT: x
+  uint32_t resid;      // EPI_RESID: residual rows (fp64)
+  uint32_t out, out_ss;  // EPI_RESID: new residual, its sums of squares; EPI_SWIGLU: act;
+                         // EPI_ARGMAX: partials
+  uint32_t q, k, v;    // EPI_QKV
 };
 
 // Epilogue of the R = 2 rows a wave owns (lane 0), flagged outputs:
@@ -564,11 +587,11 @@ __device__ __forceinline__ void ll_wave_epilogue(const GemmArgs& a, const LLCtx&
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       if (row0 + r < a.N) {
-        ll_put_f64(c, io.out + 2 * (size_t)(row0 + r), xn[r]);
+        ll_put_f64(c, io.out + 2 * (uint32_t)(row0 + r), xn[r]);
         ss += xn[r] * xn[r];
       }
     }
-    ll_put_f64(c, io.out_ss + 2 * (size_t)(row0 / R), ss);
+    ll_put_f64(c, io.out_ss + 2 * (uint32_t)(row0 / R), ss);
   } else if constexpr (EPI == EPI_QKV) {
     const int row0 = tile * 16 + w * R;
     if (row0 >= a.N) return;
@@ -576,9 +599,9 @@ __device__ __forceinline__ void ll_wave_epilogue(const GemmArgs& a, const LLCtx&
     const int din = row0 - part * a.dq;
     if (part == 0) {
 #pragma unroll
-      for (int r = 0; r < R; ++r) ll_put_f64(c, io.q + 2 * (size_t)(din + r), v[r]);
+      for (int r = 0; r < R; ++r) ll_put_f64(c, io.q + 2 * (uint32_t)(din + r), v[r]);
     } else {
-      const size_t base = (part == 1 ? io.k : io.v) + din;
+      const uint32_t base = (part == 1 ? io.k : io.v) + din;
 #pragma unroll
       for (int r = 0; r < R; ++r) ll_put(c, base + r, stored_bits<T>(v[r]));
     }
@@ -592,58 +615,54 @@ __device__ __forceinline__ void ll_wave_epilogue(const GemmArgs& a, const LLCtx&
   }
 }
 
-// Argmax partial of a finished 16-row tile (epilogue's EPI_ARGMAX for one
-// session): lanes 0, 16, 32, 48 of wave 0 hold rows 4g..4g+3 in v.
+// Argmax partial of the row pair of wave w in tile `tile` (lane 0): the
+// logits of its rows (fp32 copy for the host) and (max, lowest index) of the
+// pair, NaN counting as -inf; partial number tile * 8 + w. A pair past the
+// last row still writes its partial (index INT_MAX, never chosen).
 template <typename T>
-__device__ __forceinline__ void ll_argmax_epilogue(const GemmArgs& a, const LLCtx& c,
-                                                   const LLIo& io, int tile, int g,
-                                                   const double* v) {
+__device__ __forceinline__ void ll_argmax_pair(const GemmArgs& a, const LLCtx& c, const LLIo& io,
+                                               int tile, int w, const double* v) {
   double bv = -INFINITY;
   int bi = 0x7fffffff;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = tile * 16 + 4 * g + i;
+  for (int r = 0; r < 2; ++r) {
+    const int row = tile * 16 + w * 2 + r;
     if (row < a.N) {
-      *(MOSHI_GLB float*)(a.logits + row) = (float)v[i];  // host reads
-      const double val = (v[i] != v[i]) ? -INFINITY : v[i];
+      *(MOSHI_GLB float*)(a.logits + row) = (float)v[r];  // host reads
+      const double val = (v[r] != v[r]) ? -INFINITY : v[r];
       if (bi == 0x7fffffff || val > bv) {
         bv = val;
         bi = row;
       }
     }
   }
-#pragma unroll
-  for (int off = 16; off <= 32; off <<= 1) {
-    const double ov = shfl_xor_d(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (arg_better(ov, oi, bv, bi)) {
-      bv = ov;
-      bi = oi;
-    }
-  }
-  if (g == 0) {
-    ll_put_f64(c, io.out + 4 * (size_t)tile, bv);
-    ll_put(c, io.out + 4 * (size_t)tile + 2, (uint32_t)bi);
-    ll_put(c, io.out + 4 * (size_t)tile + 3, 0u);
-  }
+  const uint32_t pw = io.out + 4 * (uint32_t)(tile * 8 + w);
+  ll_put_f64(c, pw, bv);
+  ll_put(c, pw + 2, (uint32_t)bi);
+  ll_put(c, pw + 3, 0u);
 }
 
 // A projection from a weight slice staged by gemv_stage (gemv_staged's
 // arithmetic and work split) whose input and outputs are flagged vectors.
-// Workgroups without rows skip it, except workgroup 0, which always waits
-// for the input (its trace stamp marks the end of the previous operation).
-// False = leave (a wait gave up).
-template <typename T, int KW, int PRO, int EPI, bool ENTRY = false>
+// Once the input has arrived, each wave copies its weight slots (at most MI
+// items x MC column passes) and its input groups from LDS to registers, and
+// the next operation's slice is requested into LDS (stage_next) before this
+// one computes: a wave's loads complete in issue order, so staging issued
+// before the next input poll would hold that poll back until it lands.
+// Workgroups without rows skip the projection (but still stage the next
+// one), except workgroup 0, which always waits for the input (its trace
+// stamp marks the end of the previous operation). False = leave (a wait gave
+// up). Argmax projections write one partial per row pair.
+template <typename T, int KW, int PRO, int EPI, int MI, int MC, bool ENTRY = false, typename FN>
 __device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const LLIo& io, int wg,
                                         int nwg, T* xs, const unsigned char* wbuf,
-                                        const EntryLL* ent, uint64_t* stamp) {
+                                        const EntryLL* ent, uint64_t* stamp, FN stage_next) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int R = 16 / KW;
   constexpr int NTH = 64 * KW;
   static_assert(R == 2, "row pairs");
   const int t = tid();
   const int lane = t & 63, wave = t >> 6;
-  __shared__ double s_red[2][16];
   __shared__ double s_tmp[KW];
   const int ngroups = a.K / VEC;
   const int cpl = staged_cpl<T>(a.K);
@@ -654,13 +673,22 @@ __device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const
     const int P = EPI == EPI_SWIGLU ? a.N : (a.N + 1) / 2;
     wg_any = wg * P / nwg < (wg + 1) * P / nwg;
   }
-  if (!wg_any && wg != 0) return true;
-  int te, we;
-  const bool any = staged_item<EPI, KW>(a, wg, nwg, wave, 0, te, we);
+  if (!wg_any && wg != 0) {
+    stage_next();
+    return true;
+  }
+  // this wave's items (staged_item is false from the first missing one on)
+  int te[MI], we[MI], nit = 0;
+#pragma unroll
+  for (int j = 0; j < MI; ++j) {
+    te[j] = 0;
+    we[j] = 0;
+    if (staged_item<EPI, KW>(a, wg, nwg, wave, j, te[j], we[j])) nit = j + 1;
+  }
   // residual rows of the wave's first item, requested before the input
   u32x4 rq[2];
-  const int rrow0 = any ? te * 16 + we * R : 0;
-  auto rw = [&](int r) { return io.resid + 2 * (size_t)(rrow0 + r < a.N ? rrow0 + r : rrow0); };
+  const int rrow0 = nit > 0 ? te[0] * 16 + we[0] * R : 0;
+  auto rw = [&](int r) { return io.resid + 2 * (uint32_t)(rrow0 + r < a.N ? rrow0 + r : rrow0); };
   if constexpr (EPI == EPI_RESID) {
 #pragma unroll
     for (int r = 0; r < 2; ++r) rq[r] = ll_ld(c, rw(r));
@@ -679,71 +707,85 @@ __device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const
   }
   if (stamp != nullptr && wg == 0 && t == 0) *(MOSHI_GLB uint64_t*)stamp = wall_clock64();
   __syncthreads();
-  if (!wg_any) return true;
-  // this wave's LDS-direct loads have landed
+  if (!wg_any) {
+    stage_next();
+    return true;
+  }
+  // this wave's LDS-direct loads have landed (the input waits above already
+  // waited for them)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   const MOSHI_LDS unsigned char* base = (const MOSHI_LDS unsigned char*)wbuf;
-  int parity = 0, slot = 0;
-  for (int j = 0; staged_item<EPI, KW>(a, wg, nwg, wave, j, te, we); ++j) {
-    double acc[R];
+  u32x4 wr[MI][MC][2], xr[MC];
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = 0.0;
-#pragma unroll 2
-    for (int cc = 0; cc < cpl; ++cc, slot += R) {
-      const int gi = cc * 64 + lane;
-      if (gi < ngroups) {
-        double xv[VEC];
-        widen<T>(*(const u32x4*)(xs + (size_t)gi * VEC), xv);
+  for (int cc = 0; cc < MC; ++cc) {
+    const int gi = cc * 64 + lane;
+    xr[cc] = *(const u32x4*)(xs + (uint32_t)(gi < ngroups ? gi : 0) * VEC);
+  }
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          double wd[VEC];
-          widen<T>(*(const MOSHI_LDS u32x4*)(base + (((slot + r) * KW + wave) * 64 + lane) * 16), wd);
+  for (int j = 0; j < MI; ++j)
 #pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
-        }
+    for (int cc = 0; cc < MC; ++cc)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        // slot (j * cpl + cc) * 2 + r of gemv_stage's layout (clamped to slot 0 when unused)
+        const int slot = (j < nit && cc < cpl) ? (j * cpl + cc) * 2 + r : 0;
+        wr[j][cc][r] = *(const MOSHI_LDS u32x4*)(base + ((slot * KW + wave) * 64 + lane) * 16);
       }
-    }
+  // every read of this wave's slots and of xs has returned before the next
+  // slice overwrites them; the workgroup barrier covers the other waves' reads of xs
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __syncthreads();
+  stage_next();
 #pragma unroll
-    for (int r = 0; r < R; ++r) acc[r] = group_reduce<64>(acc[r]);
-    if constexpr (EPI == EPI_ARGMAX) {
-      if (lane == 0) {
+  for (int j = 0; j < MI; ++j) {
+    if (j < nit) {
+      double acc[R] = {0.0, 0.0};
 #pragma unroll
-        for (int r = 0; r < R; ++r) s_red[parity][wave * R + r] = acc[r];
-      }
-      __syncthreads();
-      if (wave == 0 && (lane & 15) == 0) {
-        const int g = lane >> 4;
-        const double v[4] = {s_red[parity][4 * g], s_red[parity][4 * g + 1],
-                             s_red[parity][4 * g + 2], s_red[parity][4 * g + 3]};
-        ll_argmax_epilogue<T>(a, c, io, te, g, v);
-      }
-      parity ^= 1;
-    } else {
-      if (lane == 0) {
-        double rv[R] = {0.0, 0.0};
-        if constexpr (EPI == EPI_RESID) {
-          if (j == 0) {
-            rv[0] = ll_f64(rq[0]);
-            rv[1] = ll_f64(rq[1]);
-          } else {
-            // later items (only with many rows per workgroup): wait here
-            const int row0 = te * 16 + we * R;
-            u32x4 q2[2];
-            (void)ll_wait<2>(
-                c,
-                [&](int r) { return io.resid + 2 * (size_t)(row0 + r < a.N ? row0 + r : row0); },
-                q2);  // a timeout raises the abort flag; the host fails the step
-            rv[0] = ll_f64(q2[0]);
-            rv[1] = ll_f64(q2[1]);
+      for (int cc = 0; cc < MC; ++cc) {
+        const int gi = cc * 64 + lane;
+        if (cc < cpl && gi < ngroups) {
+          double xv[VEC];
+          widen<T>(xr[cc], xv);
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            double wd[VEC];
+            widen<T>(wr[j][cc][r], wd);
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
           }
         }
-        ll_wave_epilogue<T, EPI>(a, c, io, te, we, acc, rv);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[r] = group_reduce<64>(acc[r]);
+      if (lane == 0) {
+        if constexpr (EPI == EPI_ARGMAX) {
+          ll_argmax_pair<T>(a, c, io, te[j], we[j], acc);
+        } else {
+          double rv[R] = {0.0, 0.0};
+          if constexpr (EPI == EPI_RESID) {
+            if (j == 0) {
+              rv[0] = ll_f64(rq[0]);
+              rv[1] = ll_f64(rq[1]);
+            } else {
+              // later items (only with many rows per workgroup): wait here
+              const int row0 = te[j] * 16 + we[j] * R;
+              u32x4 q2[2];
+              (void)ll_wait<2>(  // a timeout raises the abort flag; the host fails the step
+                  c,
+                  [&](int r) { return io.resid + 2 * (uint32_t)(row0 + r < a.N ? row0 + r : row0); },
+                  q2);
+              rv[0] = ll_f64(q2[0]);
+              rv[1] = ll_f64(q2[1]);
+            }
+          }
+          ll_wave_epilogue<T, EPI>(a, c, io, te[j], we[j], acc, rv);
+        }
       }
     }
   }
-  __syncthreads();  // xs, s_red and the slots may be reused by the caller
+  __syncthreads();  // xs may be rewritten by the next operation
   return true;
 }
 
@@ -770,18 +812,37 @@ __device__ __forceinline__ bool ll_dep_attention(const LLCtx& c, const LLMap& M,
   __syncthreads();
   if (t < 64) {
     const double scale = 1.0 / sqrt((double)HD);
-    // q (VEC fp64 lines) and K (VEC/2 lines per key pass)
-    auto wq = [&](int e) { return M.Q(s, l) + 2 * (size_t)(h * HD + kd * VEC + e); };
-    auto wk = [&](int i) {
-      const int p = i / (VEC / 2), e2 = i % (VEC / 2);
+    // q (VEC fp64 lines), K (VEC/2 lines per key pass) and V (one word per
+    // entry j and dim lane + 64 i), all requested before any is waited for
+    const uint32_t qb = M.Q(s, l) + 2 * (uint32_t)(h * HD + kd * VEC);
+    uint32_t kb[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
       const int j = p * KPW + kq;
-      return M.K(j < nvalid ? j : 0, l) + (size_t)(h * HD + kd * VEC + 2 * e2);
+      kb[p] = M.K(j < nvalid ? j : 0, l) + (uint32_t)(h * HD + kd * VEC);
+    }
+    const uint32_t vstep = M.V(1, l) - M.V(0, l);  // words between entries
+    const uint32_t vb = M.V(0, l) + (uint32_t)(h * HD);
+    auto wv = [&](int n) {
+      const int j = n / DPL, i = n % DPL;
+      const int dd = (lane + 64 * i) < HD ? lane + 64 * i : 0;
+      return vb + (uint32_t)(j < nvalid ? j : 0) * vstep + (uint32_t)dd;
     };
+    constexpr int NV = DEP_MAX_KEYS * DPL;
+    uint64_t vq[NV];
+    auto wq = [&](int e) { return qb + 2 * e; };
+    auto wk = [&](int i) { return kb[i / (VEC / 2)] + 2 * (i % (VEC / 2)); };
     bool ok;
     {
       u32x4 qq[VEC], kk[KL];
-      ok = ll_wait<VEC>(c, wq, qq);
-      ok = ok & ll_wait<KL>(c, wk, kk);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) qq[e] = ll_ld(c, wq(e));
+#pragma unroll
+      for (int i = 0; i < KL; ++i) kk[i] = ll_ld(c, wk(i));
+#pragma unroll
+      for (int n = 0; n < NV; ++n) vq[n] = ld_u64<true>(c.w + wv(n));
+      ok = ll_wait<VEC, true>(c, wq, qq);
+      ok = ok & ll_wait<KL, true>(c, wk, kk);
       double qv[VEC];
 #pragma unroll
       for (int e = 0; e < VEC; ++e) qv[e] = ll_f64(qq[e]);
@@ -798,14 +859,7 @@ __device__ __forceinline__ bool ll_dep_attention(const LLCtx& c, const LLMap& M,
         if (kd == 0 && j < DEP_MAX_KEYS) s_sc[j] = d * scale;
       }
     }
-    // V: entry j, dims lane + 64 i (one word each)
-    auto wv = [&](int n) {
-      const int j = n / DPL, i = n % DPL;
-      const int dd = (lane + 64 * i) < HD ? lane + 64 * i : 0;
-      return M.V(j < nvalid ? j : 0, l) + (size_t)(h * HD + dd);
-    };
-    uint64_t vq[DEP_MAX_KEYS * DPL];
-    ok = ok & ll_wait_words<DEP_MAX_KEYS * DPL>(c, wv, vq);
+    ok = ok & ll_wait_words<NV, true>(c, wv, vq);
     // softmax over the valid keys
     const double sv = lane < nvalid ? s_sc[lane] : -INFINITY;
     const double m = group_reduce<64, true>(sv);
@@ -822,7 +876,7 @@ __device__ __forceinline__ bool ll_dep_attention(const LLCtx& c, const LLMap& M,
       }
       if (dd < HD) {
         const double ov = lsum > 0.0 ? od / lsum : 0.0;
-        ll_put(c, M.O(s, l) + (size_t)(h * HD + dd), stored_bits<T>(ov));
+        ll_put(c, M.O(s, l) + (uint32_t)(h * HD + dd), stored_bits<T>(ov));
       }
     }
     if (!ok) s_bad = 1;
@@ -1028,6 +1082,23 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     ++tix;
     return trace != nullptr ? trace + tix : nullptr;
   };
+  // the next operation's weight slice, requested by each projection once its
+  // own slice is in registers
+  auto st_qkv = [&](int s_, int l_) {
+    return [&, s_, l_]() { gemv_stage<T, KW, EPI_QKV>(d_qkv(s_, l_), wg, nwg, wbuf); };
+  };
+  auto st_o = [&](int s_, int l_) {
+    return [&, s_, l_]() { gemv_stage<T, KW, EPI_RESID>(d_o(s_, l_), wg, nwg, wbuf); };
+  };
+  auto st_gu = [&](int s_, int l_) {
+    return [&, s_, l_]() { gemv_stage<T, KW, EPI_SWIGLU>(d_gu(s_, l_), wg, nwg, wbuf); };
+  };
+  auto st_dn = [&](int s_, int l_) {
+    return [&, s_, l_]() { gemv_stage<T, KW, EPI_RESID>(d_dn(s_, l_), wg, nwg, wbuf); };
+  };
+  auto st_head = [&](int s_) {
+    return [&, s_]() { gemv_stage<T, KW, EPI_ARGMAX>(d_head(s_), wg, nwg, wbuf); };
+  };
   for (int s = 0; s < S; ++s) {
     for (int l = 0; l < Ld; ++l) {
       LLIo io{};
@@ -1048,17 +1119,16 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
         E.tok_out = s == 0 ? text_out : codes_out + (s - 1);
         // at s = 0 the grid barrier after the input projections ended the
         // previous operation
-        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, true>(d_qkv(s, 0), c, io, wg, nwg, xs, wbuf, &E,
-                                                     s == 0 ? nullptr : stamp()))
+        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, LLR_QKV_I, LLR_QKV_C, true>(
+                d_qkv(s, 0), c, io, wg, nwg, xs, wbuf, &E, s == 0 ? nullptr : stamp(), st_o(s, 0)))
           return;
       } else {
         io.x = M.R2(s, l - 1);
         io.ss = M.S2(s, l - 1);
-        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV>(d_qkv(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
-                                               stamp()))
+        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, LLR_QKV_I, LLR_QKV_C>(
+                d_qkv(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_o(s, l)))
           return;
       }
-      gemv_stage<T, KW, EPI_RESID>(d_o(s, l), wg, nwg, wbuf);
       for (int h = 0; h < Hd; ++h)
         if ((nqkv + h) % nwg == wg && !ll_dep_attention<T, HDD, NT>(c, M, s, l, h)) return;
       io = LLIo{};
@@ -1066,38 +1136,41 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
       io.resid = l == 0 ? M.Y(s, S) : M.R2(s, l - 1);
       io.out = M.R1(s, l);
       io.out_ss = M.S1(s, l);
-      if (!ll_gemv<T, KW, PRO_DIRECT, EPI_RESID>(d_o(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
-                                                 stamp()))
+      if (!ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_O_I, LLR_O_C>(
+              d_o(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_gu(s, l)))
         return;
-      gemv_stage<T, KW, EPI_SWIGLU>(d_gu(s, l), wg, nwg, wbuf);
       io = LLIo{};
       io.x = M.R1(s, l);
       io.ss = M.S1(s, l);
       io.out = M.A(s, l);
-      if (!ll_gemv<T, KW, PRO_NORM, EPI_SWIGLU>(d_gu(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
-                                                stamp()))
+      if (!ll_gemv<T, KW, PRO_NORM, EPI_SWIGLU, LLR_GU_I, LLR_GU_C>(
+              d_gu(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_dn(s, l)))
         return;
-      gemv_stage<T, KW, EPI_RESID>(d_dn(s, l), wg, nwg, wbuf);
       io = LLIo{};
       io.x = M.A(s, l);
       io.resid = M.R1(s, l);
       io.out = M.R2(s, l);
       io.out_ss = M.S2(s, l);
-      if (!ll_gemv<T, KW, PRO_DIRECT, EPI_RESID>(d_dn(s, l), c, io, wg, nwg, xs, wbuf, nullptr,
-                                                 stamp()))
-        return;
+      bool ok;
       if (l + 1 < Ld)
-        gemv_stage<T, KW, EPI_QKV>(d_qkv(s, l + 1), wg, nwg, wbuf);
+        ok = ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_DN_I, LLR_DN_C>(
+            d_dn(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_qkv(s, l + 1));
       else
-        gemv_stage<T, KW, EPI_ARGMAX>(d_head(s), wg, nwg, wbuf);
+        ok = ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_DN_I, LLR_DN_C>(
+            d_dn(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_head(s));
+      if (!ok) return;
     }
     LLIo io{};
     io.x = M.R2(s, Ld - 1);
     io.out = M.AP(s, S);
-    if (!ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX>(d_head(s), c, io, wg, nwg, xs, wbuf, nullptr,
-                                              stamp()))
-      return;
-    if (s + 1 < S) gemv_stage<T, KW, EPI_QKV>(d_qkv(s + 1, 0), wg, nwg, wbuf);
+    bool ok;
+    if (s + 1 < S)
+      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C>(
+          d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_qkv(s + 1, 0));
+    else
+      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C>(
+          d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), []() {});
+    if (!ok) return;
   }
 #undef GEMV
 #undef GEMV_S
@@ -1107,7 +1180,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   // ---- last code, next position ----
   if (wg == 0) {
     bool ok;
-    const int tok = ll_reduce_token<NT>(c, M.AP(S - 1, S), (Va + 15) / 16, Va, ok);
+    const int tok = ll_reduce_token<NT>(c, M.AP(S - 1, S), 8 * M.nta, Va, ok);
     uint64_t* st = stamp();
     if (threadIdx.x == 0) {
       if (st != nullptr) *(MOSHI_GLB uint64_t*)st = wall_clock64();
