@@ -57,7 +57,7 @@ __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
 // The fp64 16x16 result puts row (lane/16) + 4i in element i of a lane, so A
 // row m carries tile row 4*(m%4) + m/4: element i of lane group g is then tile
 // row 4g + i, the layout the epilogues use.
-template <typename T, int NB, int KW, int EPI>
+template <typename T, int NB, int KW, int EPI, bool DB>
 __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int KSTEP = 4 * VEC;
@@ -79,9 +79,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
   f64x4 acc[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) acc[nb] = f64x4{0.0, 0.0, 0.0, 0.0};
-  for (int st = s0; st < s1; st += U) {
-    u32x4 wv[U];
-    u32x4 xw[U][NB];
+  // batch of U k-steps starting at st: weights and input groups
+  auto load = [&](int st, u32x4 (&wv)[U], u32x4 (&xw)[U][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int k0 = (st + u) * KSTEP + g * VEC;
@@ -94,6 +93,8 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
                                        : u32x4{0u, 0u, 0u, 0u};
       }
     }
+  };
+  auto compute = [&](const u32x4 (&wv)[U], const u32x4 (&xw)[U][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       double wd[VEC];
@@ -106,6 +107,25 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
         for (int e = 0; e < VEC; ++e)
           acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(wd[e], xd[e], acc[nb], 0, 0, 0);
       }
+    }
+  };
+  if constexpr (DB) {
+    // double-buffered: the next batch is requested before this one is used
+    u32x4 wa[U], xa[U][NB], wb[U], xb[U][NB];
+    if (s0 < s1) load(s0, wa, xa);
+    for (int st = s0; st < s1; st += 2 * U) {
+      if (st + U < s1) load(st + U, wb, xb);
+      compute(wa, xa);
+      if (st + U >= s1) break;
+      if (st + 2 * U < s1) load(st + 2 * U, wa, xa);
+      compute(wb, xb);
+    }
+  } else {
+    for (int st = s0; st < s1; st += U) {
+      u32x4 wv[U];
+      u32x4 xw[U][NB];
+      load(st, wv, xw);
+      compute(wv, xw);
     }
   }
 #pragma unroll
@@ -350,9 +370,10 @@ int gemm_kw(int dtype, int B, int K) {
   (void)dtype;
   (void)K;
   // one session: 8 waves (the sum-of-squares partials assume 2 rows per
-  // wave); more sessions: 8 waves for the temporal widths, 4 for the rest
+  // wave); more sessions: 8 waves (a shorter stretch of K per wave; up to 32
+  // sessions; 4 waves at 64, see launch_gemm_t)
   if (B == 1) return GEMV_KW;
-  return K >= 4096 ? 8 : 4;
+  return 8;
 }
 
 // Workgroups of the one-session projection: at most one per CU (the kernel
@@ -380,28 +401,38 @@ static hipError_t launch_gemv_kw(int pro, int epi, const GemmArgs& a, hipStream_
   return hipErrorInvalidValue;
 }
 
-template <typename T, int NB, int KW>
-static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
+template <typename T, int NB, int KW, bool DB>
+static hipError_t launch_gemm_db(int epi, const GemmArgs& a, hipStream_t st) {
   dim3 grid(gemm_tiles(epi, a.N)), block(64 * KW);
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE, DB>), grid, block, 0, st, a);
       break;
     case EPI_RESID:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_RESID>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_RESID, DB>), grid, block, 0, st, a);
       break;
     case EPI_QKV:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_QKV>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_QKV, DB>), grid, block, 0, st, a);
       break;
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_SWIGLU>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_SWIGLU, DB>), grid, block, 0, st, a);
       break;
     case EPI_ARGMAX:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_ARGMAX>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_ARGMAX, DB>), grid, block, 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+// Double-buffered batches for inputs narrower than 4096 (the depformer's:
+// few k-steps per wave, latency-bound); the temporal widths keep single
+// batches, whose lower register count fits more workgroups per CU (measured
+// faster at 16 sessions).
+template <typename T, int NB, int KW>
+static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
+  if (NB <= 2 && a.K < 4096) return launch_gemm_db<T, NB, KW, NB <= 2>(epi, a, st);
+  return launch_gemm_db<T, NB, KW, false>(epi, a, st);
 }
 
 template <typename T>
