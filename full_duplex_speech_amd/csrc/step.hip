@@ -645,15 +645,20 @@ __device__ __forceinline__ void ll_argmax_pair(const GemmArgs& a, const LLCtx& c
 // A projection from a weight slice staged by gemv_stage (gemv_staged's
 // arithmetic and work split) whose input and outputs are flagged vectors.
 // Once the input has arrived, each wave copies its weight slots (at most MI
-// items x MC column passes) and its input groups from LDS to registers, and
-// the next operation's slice is requested into LDS (stage_next) before this
-// one computes: a wave's loads complete in issue order, so staging issued
-// before the next input poll would hold that poll back until it lands.
+// items x MC column passes) and its input groups from LDS to registers, then
+// requests the next operation's slice into LDS (stage_next): before computing
+// (EARLY: the slice has the longest time to land before the next operation
+// needs it) or after its outputs are stored (issuing it then does not delay
+// them). Either way it streams while the next input is awaited; a wave's
+// loads complete in issue order, so that first poll returns once the slice
+// has landed. Which is faster depends on the sizes of the next slices
+// (measured per operation).
 // Workgroups without rows skip the projection (but still stage the next
 // one), except workgroup 0, which always waits for the input (its trace
 // stamp marks the end of the previous operation). False = leave (a wait gave
 // up). Argmax projections write one partial per row pair.
-template <typename T, int KW, int PRO, int EPI, int MI, int MC, bool ENTRY = false, typename FN>
+template <typename T, int KW, int PRO, int EPI, int MI, int MC, bool EARLY, bool ENTRY = false,
+          typename FN>
 __device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const LLIo& io, int wg,
                                         int nwg, T* xs, const unsigned char* wbuf,
                                         const EntryLL* ent, uint64_t* stamp, FN stage_next) {
@@ -737,11 +742,15 @@ __device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const
   // slice overwrites them; the workgroup barrier covers the other waves' reads of xs
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
   __syncthreads();
-  stage_next();
+  if constexpr (EARLY) stage_next();
+  // every item's row sums, then the items' epilogues in parallel lanes
+  // (lane j takes item j; the reduction leaves the sums in every lane)
+  double acc[MI][R];
 #pragma unroll
   for (int j = 0; j < MI; ++j) {
+    acc[j][0] = 0.0;
+    acc[j][1] = 0.0;
     if (j < nit) {
-      double acc[R] = {0.0, 0.0};
 #pragma unroll
       for (int cc = 0; cc < MC; ++cc) {
         const int gi = cc * 64 + lane;
@@ -753,38 +762,53 @@ __device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const
             double wd[VEC];
             widen<T>(wr[j][cc][r], wd);
 #pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[r] = fma(wd[e], xv[e], acc[r]);
+            for (int e = 0; e < VEC; ++e) acc[j][r] = fma(wd[e], xv[e], acc[j][r]);
           }
-        }
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r) acc[r] = group_reduce<64>(acc[r]);
-      if (lane == 0) {
-        if constexpr (EPI == EPI_ARGMAX) {
-          ll_argmax_pair<T>(a, c, io, te[j], we[j], acc);
-        } else {
-          double rv[R] = {0.0, 0.0};
-          if constexpr (EPI == EPI_RESID) {
-            if (j == 0) {
-              rv[0] = ll_f64(rq[0]);
-              rv[1] = ll_f64(rq[1]);
-            } else {
-              // later items (only with many rows per workgroup): wait here
-              const int row0 = te[j] * 16 + we[j] * R;
-              u32x4 q2[2];
-              (void)ll_wait<2>(  // a timeout raises the abort flag; the host fails the step
-                  c,
-                  [&](int r) { return io.resid + 2 * (uint32_t)(row0 + r < a.N ? row0 + r : row0); },
-                  q2);
-              rv[0] = ll_f64(q2[0]);
-              rv[1] = ll_f64(q2[1]);
-            }
-          }
-          ll_wave_epilogue<T, EPI>(a, c, io, te[j], we[j], acc, rv);
         }
       }
     }
   }
+#pragma unroll
+  for (int j = 0; j < MI; ++j)
+    if (j < nit) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) acc[j][r] = group_reduce<64>(acc[j][r]);
+    }
+  if (lane < nit) {
+    const int j = lane;
+    double v[R] = {acc[0][0], acc[0][1]};
+    int tj = te[0], wj = we[0];
+#pragma unroll
+    for (int i = 1; i < MI; ++i)
+      if (j == i) {
+        v[0] = acc[i][0];
+        v[1] = acc[i][1];
+        tj = te[i];
+        wj = we[i];
+      }
+    if constexpr (EPI == EPI_ARGMAX) {
+      ll_argmax_pair<T>(a, c, io, tj, wj, v);
+    } else {
+      double rv[R] = {0.0, 0.0};
+      if constexpr (EPI == EPI_RESID) {
+        if (j == 0) {
+          rv[0] = ll_f64(rq[0]);
+          rv[1] = ll_f64(rq[1]);
+        } else {
+          // later items (only with many rows per workgroup): wait here
+          const int row0 = tj * 16 + wj * R;
+          u32x4 q2[2];
+          (void)ll_wait<2>(  // a timeout raises the abort flag; the host fails the step
+              c, [&](int r) { return io.resid + 2 * (uint32_t)(row0 + r < a.N ? row0 + r : row0); },
+              q2);
+          rv[0] = ll_f64(q2[0]);
+          rv[1] = ll_f64(q2[1]);
+        }
+      }
+      ll_wave_epilogue<T, EPI>(a, c, io, tj, wj, v, rv);
+    }
+  }
+  if constexpr (!EARLY) stage_next();
   __syncthreads();  // xs may be rewritten by the next operation
   return true;
 }
@@ -1119,13 +1143,13 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
         E.tok_out = s == 0 ? text_out : codes_out + (s - 1);
         // at s = 0 the grid barrier after the input projections ended the
         // previous operation
-        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, LLR_QKV_I, LLR_QKV_C, true>(
+        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, LLR_QKV_I, LLR_QKV_C, false, true>(
                 d_qkv(s, 0), c, io, wg, nwg, xs, wbuf, &E, s == 0 ? nullptr : stamp(), st_o(s, 0)))
           return;
       } else {
         io.x = M.R2(s, l - 1);
         io.ss = M.S2(s, l - 1);
-        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, LLR_QKV_I, LLR_QKV_C>(
+        if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, LLR_QKV_I, LLR_QKV_C, false>(
                 d_qkv(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_o(s, l)))
           return;
       }
@@ -1136,14 +1160,14 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
       io.resid = l == 0 ? M.Y(s, S) : M.R2(s, l - 1);
       io.out = M.R1(s, l);
       io.out_ss = M.S1(s, l);
-      if (!ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_O_I, LLR_O_C>(
+      if (!ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_O_I, LLR_O_C, false>(
               d_o(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_gu(s, l)))
         return;
       io = LLIo{};
       io.x = M.R1(s, l);
       io.ss = M.S1(s, l);
       io.out = M.A(s, l);
-      if (!ll_gemv<T, KW, PRO_NORM, EPI_SWIGLU, LLR_GU_I, LLR_GU_C>(
+      if (!ll_gemv<T, KW, PRO_NORM, EPI_SWIGLU, LLR_GU_I, LLR_GU_C, false>(
               d_gu(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_dn(s, l)))
         return;
       io = LLIo{};
@@ -1153,10 +1177,10 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
       io.out_ss = M.S2(s, l);
       bool ok;
       if (l + 1 < Ld)
-        ok = ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_DN_I, LLR_DN_C>(
+        ok = ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_DN_I, LLR_DN_C, false>(
             d_dn(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_qkv(s, l + 1));
       else
-        ok = ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_DN_I, LLR_DN_C>(
+        ok = ll_gemv<T, KW, PRO_DIRECT, EPI_RESID, LLR_DN_I, LLR_DN_C, false>(
             d_dn(s, l), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_head(s));
       if (!ok) return;
     }
@@ -1165,10 +1189,10 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     io.out = M.AP(s, S);
     bool ok;
     if (s + 1 < S)
-      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C>(
+      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C, true>(
           d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_qkv(s + 1, 0));
     else
-      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C>(
+      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C, true>(
           d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), []() {});
     if (!ok) return;
   }
