@@ -785,11 +785,14 @@ __device__ __forceinline__ void finish_tile(const GemmArgs& a, int tile, int wav
 // tile (EPI_RESID) and the first XP input items of every thread (see
 // build_input) are requested before the norm scale is computed. Every thread
 // of the workgroup must call this (it synchronises the workgroup).
-template <typename T, int KW, int PRO, int EPI, bool C, int U_, bool PRE, int XP = 4>
+// IB (optional): ib(xs) builds the input vector in place of build_input
+// (every thread calls it).
+template <typename T, int KW, int PRO, int EPI, bool C, int U_, bool PRE, int XP = 4,
+          typename IB = decltype(nullptr)>
 __device__ __forceinline__ void gemv_core(
     const GemmArgs& a, int wg, int nwg, T* xs,
     const u32x4 (&pre)[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R],
-    const double (*rope)[2] = nullptr) {
+    const double (*rope)[2] = nullptr, IB ib = nullptr) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int R = GemvShape<KW, U_>::R;
   constexpr int U = GemvShape<KW, U_>::U;
@@ -828,7 +831,10 @@ __device__ __forceinline__ void gemv_core(
     }
     qin = qkv_in(a, rope);
   }
-  build_input<T, PRO, C, NTH, XP>(a, xs, s_tmp, wg == 0);
+  if constexpr (!__is_same(IB, decltype(nullptr)))
+    ib(xs);
+  else
+    build_input<T, PRO, C, NTH, XP>(a, xs, s_tmp, wg == 0);
   __syncthreads();
   if (tile < ntiles) {
     double acc[R];
@@ -1199,10 +1205,12 @@ __device__ __forceinline__ void load_kv_block(const T* kbase, const T* vbase, in
 // direct: write O / L to a.o_out (the only span); else the partial goes to
 // part (HD + 2 doubles: M, L, O). s_w: LDS, span_lds_doubles() doubles.
 // Every thread of the workgroup calls it.
-template <typename T, int HD, int NTH, bool C>
+// PUT (optional): put(t, M, L, O, direct) takes each thread t < HD's results
+// instead of the stores to part / a.o_out.
+template <typename T, int HD, int NTH, bool C, typename PUT = decltype(nullptr)>
 __device__ __forceinline__ void attn_span(const AttnArgs& a, int h, int b, int k0, int k1,
                                           int nvalid, int excl, double* s_w, double* part,
-                                          bool direct) {
+                                          bool direct, PUT put = nullptr) {
   using S = SpanShape<T, HD>;
   constexpr int VEC = S::VEC, TK = S::TK, KPW = S::KPW, KB = S::KB, BK = S::BK;
   constexpr int NW = NTH / 64;
@@ -1313,7 +1321,9 @@ __device__ __forceinline__ void attn_span(const AttnArgs& a, int h, int b, int k
         O = fma(ev, rr[t], O);
       }
     }
-    if (direct) {
+    if constexpr (!__is_same(PUT, decltype(nullptr))) {
+      put(t, M, L, O, direct);
+    } else if (direct) {
       const double ov = L > 0.0 ? O / L : 0.0;
       store_rounded<T, C>((T*)a.o_out + (size_t)b * a.ldo + h * HD + t, &ov, 1);
     } else {

@@ -543,7 +543,9 @@ int setup_step(moshi_ctx* c) {
   // the flagged depformer inputs: a normed input pair per thread, at most 4
   // two-value lines per thread for a model-dtype input, whole lines
   if (c->Dd % 2 || c->Fd % 2 || c->Dd > 2 * STEP_THREADS || c->Fd > 8 * STEP_THREADS ||
-      step_ll_words(c->S, c->Ld, c->Dd, c->Fd, c->Va) * 8 >= (1LL << 31))
+      c->D % 2 || c->D > 8 * STEP_THREADS || c->max_spans > 8 ||
+      step_ll_words(c->S, c->Ld, c->Dd, c->Fd, c->Va, c->L, c->H, c->hd, c->max_spans, c->D) * 8 >=
+          (1LL << 31))
     return MOSHI_OK;
   const size_t es = c->esz, vec = es == 2 ? 8 : 4;
   // attention span scratch: per wave, 64 / (hd / vec) key rows of hd + 1 doubles, and a maximum
@@ -645,7 +647,9 @@ int setup_step(moshi_ctx* c) {
   A.bar = c->d_bar; A.abort = c->d_abort;
   {
     const size_t ll_bytes =
-        (size_t)step_ll_words(c->S, c->Ld, c->Dd, c->Fd, c->Va) * sizeof(uint64_t);
+        (size_t)step_ll_words(c->S, c->Ld, c->Dd, c->Fd, c->Va, c->L, c->H, c->hd, c->max_spans,
+                              c->D) *
+        sizeof(uint64_t);
     CKD(c, dalloc(c, (void**)&A.ll, ll_bytes));
     CKD(c, hipMemset(A.ll, 0, ll_bytes));
   }
@@ -875,6 +879,7 @@ int alloc_buffers(moshi_ctx* c) {
     int n = c->ncu / c->H;
     n = n < 1 ? 1 : n;
     c->max_spans = n < by_len ? n : by_len;
+    if (c->max_spans > 8) c->max_spans = 8;  // the step kernel merges at most 8 span partials
   }
   const size_t hmax = c->H > c->Hd ? c->H : c->Hd;
   const size_t hdmax = c->hd > c->hdd ? c->hd : c->hdd;

@@ -200,10 +200,14 @@ int step_max_grid(int dtype, int hd, int hdd, size_t lds_bytes);
 hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int* frames,
                        int* text_out, int* codes_out, int parity, uint32_t seq, int nwg,
                        size_t lds_bytes, hipStream_t st, uint64_t* trace);
-// Words of the flagged depformer vectors (step.hip's layout): per substep and
-// layer 11 Dd + Fd, then per substep 2 Dd + 32 ceil(Va / 16).
-inline int64_t step_ll_words(int S, int Ld, int Dd, int Fd, int Va) {
-  return (int64_t)S * Ld * (11LL * Dd + Fd) + (int64_t)S * (2LL * Dd + 32LL * ((Va + 15) / 16));
+// Words of the flagged vectors of the step kernel (step.hip's layout): per
+// depformer substep and layer 11 Dd + Fd, then per substep 2 Dd + 32
+// ceil(Va / 16); then per temporal layer, head and key span 2 (hd + 2), then
+// per temporal layer D.
+inline int64_t step_ll_words(int S, int Ld, int Dd, int Fd, int Va, int L, int H, int hd, int nsp,
+                             int D) {
+  return (int64_t)S * Ld * (11LL * Dd + Fd) + (int64_t)S * (2LL * Dd + 32LL * ((Va + 15) / 16)) +
+         (int64_t)L * H * nsp * 2LL * (hd + 2) + (int64_t)L * D;
 }
 // Register copies of the depformer weight slices in the step kernel: at most
 // I items (row pairs) per wave and C column passes (ceil(K / vec / 64)) for

@@ -65,6 +65,7 @@ struct Grid {
   int* abort;
   uint64_t* trace;  // optional: barrier exit times of workgroup 0
   unsigned idx;    // barriers passed
+  unsigned tshift; // trace entries written at flagged hand-offs (no barrier)
   unsigned xcc;    // this workgroup's XCD
   unsigned xcc_n;  // workgroups on it
   unsigned n_xcc;  // XCDs with at least one workgroup
@@ -137,7 +138,8 @@ __device__ __forceinline__ bool grid_wait(Grid& g, unsigned old) {
                              MOSHI_AGT);
     }
     s_leave = poll_until(g.set + g.xcc * BW_PAGE + BW_RELEASE, g.idx, g.abort);
-    if (g.trace != nullptr && blockIdx.x == 0) *(MOSHI_GLB uint64_t*)(g.trace + g.idx) = wall_clock64();
+    if (g.trace != nullptr && blockIdx.x == 0)
+      *(MOSHI_GLB uint64_t*)(g.trace + g.idx + g.tshift) = wall_clock64();
   }
   __syncthreads();
   return s_leave != 0;
@@ -161,6 +163,7 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
   g.abort = abort;
   g.trace = trace;
   g.idx = 0;
+  g.tshift = 0;
   g.xcc = xcc_id();
   unsigned* other = bar + (parity ^ 1) * STEP_BAR_WORDS;
   if (blockIdx.x == 0 && threadIdx.x < MAX_XCC) {
@@ -278,7 +281,9 @@ __device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frame
 //   output (rounded), A [Fd] SwiGLU output (rounded);
 // then for each substep, Y [2 Dd] (the substep's input residual) and AP
 // [32 ceil(Va / 16)] (argmax partials of its head, one per row pair: value
-// low, value high, index, 0).
+// low, value high, index, 0); then the temporal attention's: for each layer,
+// head and key span, the span partial [2 (hd + 2)] (M, L, O[hd]); then for
+// each layer the merged attention output O [D] (rounded).
 
 constexpr int LL_SPIN_LIMIT = 1 << 20;
 
@@ -306,6 +311,16 @@ struct LLMap {
   }
   __device__ uint32_t Y(int s, int S) const { return sub(s, S); }
   __device__ uint32_t AP(int s, int S) const { return sub(s, S) + 2 * Dd; }
+  // temporal attention, after the depformer's vectors: per layer, the span
+  // partials of every head (M, L, O[hd], fp64) and the merged output [D]
+  int S, H, HD, NSP, L, D;
+  __device__ uint32_t tbase() const { return sub(S, S); }
+  __device__ uint32_t TP(int l, int h, int j) const {
+    return tbase() + (uint32_t)((l * H + h) * NSP + j) * (2 * (HD + 2));
+  }
+  __device__ uint32_t TO(int l) const {
+    return tbase() + (uint32_t)(L * H * NSP) * (2 * (HD + 2)) + (uint32_t)l * D;
+  }
 };
 
 __device__ __forceinline__ void ll_put(const LLCtx& c, uint32_t word, uint32_t payload) {
@@ -813,6 +828,52 @@ __device__ __forceinline__ bool ll_gemv(const GemmArgs& a, const LLCtx& c, const
   return true;
 }
 
+// Merge of the flagged span partials of temporal head h (layer l) for the
+// output dims [d0, d1) this workgroup takes: combine_direct's arithmetic
+// (span weights e^{m_c - M}, sums in span order), by wave 0 (lane i: dim
+// d0 + i; every lane takes part so that lanes 0..7 form the span weights).
+// The rounded outputs go to the flagged O[l]. False = a wait gave up.
+template <typename T, int HD>
+__device__ __forceinline__ bool ll_span_merge(const LLCtx& c, const LLMap& M, int l, int h,
+                                              int nspans, int d0, int d1) {
+  constexpr int NS = 8;  // spans per head at most (the grid's split)
+  bool ok = true;
+  if (tid() < 64) {
+    const int lane = tid();
+    const int d = d0 + lane < d1 ? d0 + lane : d0;
+    const int lc = lane & (NS - 1);  // lanes c < NS also fetch span c's M and L
+    // lines: M and L of span lc, then O[d] of spans 0..NS-1 (spans past
+    // nspans read span 0)
+    auto wd = [&](int i) {
+      const int cc = i < 2 ? (lc < nspans ? lc : 0) : (i - 2 < nspans ? i - 2 : 0);
+      const uint32_t pw = M.TP(l, h, cc);
+      return i == 0 ? pw : i == 1 ? pw + 2 : pw + 4 + 2 * (uint32_t)d;
+    };
+    u32x4 q[2 + NS];
+    ok = ll_wait<2 + NS>(c, wd, q);
+    const double mine = ll_f64(q[0]), lmine = ll_f64(q[1]);
+    double Mx = -INFINITY;
+#pragma unroll
+    for (int cc = 0; cc < NS; ++cc)
+      if (cc < nspans) Mx = fmax(Mx, readlane_d(mine, cc));
+    const double emine = (mine == -INFINITY) ? 0.0 : exp(mine - Mx);
+    double Ls = 0.0, Os = 0.0;
+#pragma unroll
+    for (int cc = 0; cc < NS; ++cc) {
+      if (cc < nspans) {
+        const double w = readlane_d(emine, cc);
+        Ls = fma(readlane_d(lmine, cc), w, Ls);
+        Os = fma(ll_f64(q[2 + cc]), w, Os);
+      }
+    }
+    if (d0 + lane < d1) {
+      const double o = Ls > 0.0 ? Os / Ls : 0.0;
+      ll_put(c, M.TO(l) + (uint32_t)(h * HD + d), stored_bits<T>(o));
+    }
+  }
+  return ok;
+}
+
 // Attention of depformer head h at substep s (keys: entries 0..s of this
 // layer), by wave 0 of one workgroup, from the flagged q, K and V: the
 // arithmetic of dep_attention for one head. The output goes to the flagged
@@ -1040,6 +1101,23 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   embed_phase<T>(A.emb, frames, wg, nwg);
   PREFETCH_SYNC(EPI_QKV, t_qkv(0));
 
+  // flagged vectors (the temporal attention's outputs, the depformer's hand-offs)
+  LLCtx c;
+  c.w = uni(A.ll);
+  c.flag = seq;
+  c.abort = uni(A.abort);
+  LLMap M;
+  M.Dd = Dd;
+  M.Fd = uni(A.d_gu.N);
+  M.Ld = Ld;
+  M.nta = (Va + 15) / 16;
+  M.S = S;
+  M.H = H;
+  M.HD = HD;
+  M.NSP = uni(A.t_attn.max_spans);
+  M.L = L;
+  M.D = uni(A.emb.D);
+
   // ---- temporal layers ----
   int nvalid, excl;
   window_of(uni(A.t_attn), 0, nvalid, excl);
@@ -1049,31 +1127,49 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     if (grid_sync(g)) return;
     {
       // each head's window split into nspan key spans, one per workgroup
-      // (the per-operation kernel's split); the workgroup finishing a
-      // head's last span merges the span partials
+      // (the per-operation kernel's split); the span partials (or, with one
+      // span, the output) are flagged vectors
       AttnArgs at = uni(A.t_attn);
       at.layer_off = (int64_t)l * t_lel;
       for (int item = wg; item < H * nspan; item += nwg) {
         const int h = item / nspan, j = item % nspan;
-        double* part = at.part + ((size_t)h * at.max_spans + j) * (HD + 2);
-        attn_span<T, HD, NT, true>(at, h, 0, j * nvalid / nspan, (j + 1) * nvalid / nspan, nvalid,
-                                   excl, s_o, part, nspan == 1);
-        if (nspan > 1) {
-          __shared__ int s_last;
-          drain_stores();
-          __syncthreads();
-          if (threadIdx.x == 0) {
-            const unsigned old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)tickets + h * 16, 1u,
-                                                        MOSHI_RLX, MOSHI_AGT);
-            s_last = (old + 1 == (unsigned)((l + 1) * nspan));
+        auto put = [&](int t, double Mv, double Lv, double Ov, bool direct) {
+          if (direct) {
+            const double o = Lv > 0.0 ? Ov / Lv : 0.0;
+            ll_put(c, M.TO(l) + (uint32_t)(h * HD + t), stored_bits<T>(o));
+          } else {
+            const uint32_t pw = M.TP(l, h, j);
+            ll_put_f64(c, pw + 4 + 2 * (uint32_t)t, Ov);
+            if (t == 0) {
+              ll_put_f64(c, pw, Mv);
+              ll_put_f64(c, pw + 2, Lv);
+            }
           }
-          __syncthreads();
-          if (s_last) combine_direct<T, HD, true>(at, h, 0, nspan);
-        }
+        };
+        attn_span<T, HD, NT, true>(at, h, 0, j * nvalid / nspan, (j + 1) * nvalid / nspan, nvalid,
+                                   excl, s_o, nullptr, nspan == 1, put);
       }
     }
-    PREFETCH_SYNC(EPI_RESID, t_o(l));
-    GEMV(PRO_DIRECT, EPI_RESID, t_o(l));
+    // the workgroups of a head's spans merge its partials, each for its
+    // share of the output dims; then the output projection's first batch
+    if (nspan > 1)
+      for (int item = wg; item < H * nspan; item += nwg) {
+        const int h = item / nspan, j = item % nspan;
+        (void)ll_span_merge<T, HD>(c, M, l, h, nspan, j * HD / nspan, (j + 1) * HD / nspan);
+      }
+    gemv_prefetch<T, KW, EPI_RESID, GU>(t_o(l), wg, pf);
+    {
+      // output projection, its input polled from the flagged O[l] (no grid
+      // barrier after the attention; a timed-out wait raises the abort flag,
+      // which ends the launch at the next barrier)
+      ++g.tshift;
+      auto ib = [&](T* xs_) {
+        (void)ll_input_direct<T, NT>(t_o(l), c, M.TO(l), xs_);
+        if (trace != nullptr && wg == 0 && tid() == 0)
+          *(MOSHI_GLB uint64_t*)(trace + g.idx + g.tshift) = wall_clock64();
+      };
+      gemv_core<T, KW, PRO_DIRECT, EPI_RESID, true, GU, true, 4>(t_o(l), wg, nwg, xs, pf, s_rope, ib);
+    }
     PREFETCH_SYNC(EPI_SWIGLU, t_gu(l));
     GEMV(PRO_NORM, EPI_SWIGLU, t_gu(l));
     PREFETCH_SYNC(EPI_RESID, t_dn(l));
@@ -1091,17 +1187,8 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   STAGE_SYNC(EPI_QKV, d_qkv(0, 0));
 
   // ---- 16 substeps: the operations hand on flagged vectors, no grid barriers ----
-  LLCtx c;
-  c.w = uni(A.ll);
-  c.flag = seq;
-  c.abort = uni(A.abort);
-  LLMap M;
-  M.Dd = Dd;
-  M.Fd = uni(A.d_gu.N);
-  M.Ld = Ld;
-  M.nta = (Va + 15) / 16;
   const int nqkv = 3 * Dd / 16;  // q/k/v tiles; head h's attention runs on workgroup (nqkv + h) % nwg
-  unsigned tix = g.idx;          // trace entry of the last operation's end
+  unsigned tix = g.idx + g.tshift;  // trace entry of the last operation's end
   auto stamp = [&]() -> uint64_t* {
     ++tix;
     return trace != nullptr ? trace + tix : nullptr;
