@@ -281,3 +281,53 @@ def test_step_kernel_matches_per_op_kernels(case):
         r = o.step(wl.frames(shape, 5, 0, t, 1)[0], forced_text=int(tok[0]), forced_codes=codes[0])
         compare_frame(shape, stats, f"{case} t={t}", int(tok[0]), codes[0], tl[0], al[0], r)
     log(f"{case}:", stats)
+
+
+@pytest.mark.parametrize("case", ["tiny_fp32", "ragged_bf16_w150"])
+def test_step_kernel_phase_timing(case):
+    """The per-operation timing hook of the persistent step kernel (workgroup
+    0's wall clock after every grid barrier or flagged input wait): each
+    operation class gets its count per step and positive, bounded intervals
+    (a stamp at the wrong entry shows up as a negative or huge one); the timed
+    steps advance the position; and a regular step afterwards still matches
+    the oracle (the ragged case uses the three-span attention merge)."""
+    if case == "tiny_fp32":
+        shape, fill = spec.TINY, 0
+    else:
+        shape, fill = spec.RAGGED.replace(window=150), 140
+    weights = wl.make_weights(shape, 47, gains="random")
+    ctx = new_engine(shape, weights, 1)
+    assert M.moshi_uses_step_kernel(ctx)
+    slot = M.moshi_session_join(ctx)
+    o = oracle.Session(oracle.Model(shape, weights))
+    if fill:
+        k, v = wl.prefill_kv(shape, 6, 0, fill)
+        M.moshi_session_prefill_kv(ctx, slot, k, v)
+        o.prefill(k, v)
+    n = 3
+    fr = wl.frames(shape, 5, 0, 0, 2)
+    t = M.moshi_time_kernels(ctx, fr[0][None, :], n)
+    L, S, Ld = shape.n_layers, shape.n_substeps, shape.dep_layers
+    per_step = {"embed": 1, "temporal_qkv": L, "temporal_attn": L, "temporal_o": L,
+                "temporal_gateup": L, "temporal_down": L, "text_head": 1, "dep_inproj": 1,
+                "dep_qkv": S * Ld, "dep_o": S * Ld, "dep_gateup": S * Ld, "dep_down": S * Ld,
+                "dep_head": S, "argmax_reduce": 1}
+    for name, rec in t.items():
+        want = per_step.get(name, 0) * n
+        assert rec["launches"] == want, f"{case}: {name} counted {rec['launches']}, expected {want}"
+        if want:
+            avg = rec["ms"] / want
+            assert np.isfinite(avg) and 0.0 < avg < 10.0, f"{case}: {name} interval {avg} ms"
+    total = sum(rec["ms"] for rec in t.values()) / n
+    log(f"{case}: {total * 1000:.1f} us per timed step")
+    assert M.moshi_session_info(ctx, slot)[0] == fill + n
+    for _ in range(n):
+        o.step(fr[0])
+    tok, codes = M.moshi_step(ctx, fr[1][None, :])
+    tl, al = M.moshi_read_logits(ctx)
+    r = o.step(fr[1], forced_text=int(tok[slot]), forced_codes=codes[slot])
+    stats = Stats()
+    compare_frame(shape, stats, f"{case} after timing", int(tok[slot]), codes[slot], tl[slot],
+                  al[slot], r)
+    assert M.moshi_session_info(ctx, slot) == o.info()
+    M.moshi_destroy(ctx)
