@@ -331,3 +331,32 @@ def test_step_kernel_phase_timing(case):
                   al[slot], r)
     assert M.moshi_session_info(ctx, slot) == o.info()
     M.moshi_destroy(ctx)
+
+
+def test_two_engines_interleaved():
+    """Two one-session engines with different weights, alive at once and
+    stepped alternately, each match their own oracle: every context has its
+    own barrier counters, flagged-vector buffers and launch sequence numbers
+    (both start at 1), so neither sees the other's words."""
+    shape = spec.TINY
+    runs = []
+    for seed in (47, 48):
+        weights = wl.make_weights(shape, seed, gains="random")
+        ctx = new_engine(shape, weights, 1)
+        assert M.moshi_uses_step_kernel(ctx)
+        slot = M.moshi_session_join(ctx)
+        runs.append((ctx, slot, oracle.Session(oracle.Model(shape, weights))))
+    stats = Stats()
+    T = 12
+    for t in range(T):
+        for i, (ctx, slot, o) in enumerate(runs):
+            f = wl.frames(shape, 9 + i, 0, t, 1)[0]
+            tok, codes = M.moshi_step(ctx, f[None, :])
+            tl, al = M.moshi_read_logits(ctx)
+            r = o.step(f, forced_text=int(tok[slot]), forced_codes=codes[slot])
+            compare_frame(shape, stats, f"engine {i} t={t}", int(tok[slot]), codes[slot],
+                          tl[slot], al[slot], r)
+            assert M.moshi_session_info(ctx, slot) == o.info()
+    for ctx, _, _ in runs:
+        M.moshi_destroy(ctx)
+    log("two engines:", stats)
