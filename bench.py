@@ -275,6 +275,10 @@ def main():
         "kernels": kt,
     }
     print(json.dumps(rec), flush=True)
+    # every context is destroyed: unload the library now, so that its HIP
+    # module teardown does not run among the exit handlers (after a profiler
+    # attached to the process may have finalised)
+    M.unload()
 
 
 if __name__ == "__main__":

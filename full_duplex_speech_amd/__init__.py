@@ -17,6 +17,7 @@ Typical use::
 import ctypes
 import os
 import subprocess
+import weakref
 
 import numpy as np
 
@@ -35,8 +36,11 @@ MOSHI_OK, MOSHI_E_INVALID, MOSHI_E_FULL, MOSHI_E_NOSESSION, MOSHI_E_DEVICE, MOSH
     0, -1, -2, -3, -4, -5
 MOSHI_F32, MOSHI_BF16 = 0, 1
 MOSHI_FLAG_MASK_OLDEST = 1
+MOSHI_FLAG_DEP_FINAL_NORM = 2
+MOSHI_FLAG_DEP_REF_RING = 4
 
 _lib = None
+_live_ctx = weakref.WeakSet()
 
 
 def build(verbose=False) -> str:
@@ -65,7 +69,8 @@ class moshi_config(ctypes.Structure):
         "dep_dim", "dep_layers", "dep_heads", "dep_ffn_hidden", "n_substeps",
         "text_vocab", "audio_card")] + [
         ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_double),
-        ("dtype", ctypes.c_int32), ("max_sessions", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+        ("dtype", ctypes.c_int32), ("max_sessions", ctypes.c_int32), ("flags", ctypes.c_uint32),
+        ("dep_q", ctypes.c_int32)]
 
 
 def lib():
@@ -84,6 +89,8 @@ def lib():
             "moshi_session_join": ([vp, ctypes.POINTER(i32)], ctypes.c_int),
             "moshi_session_leave": ([vp, i32], ctypes.c_int),
             "moshi_step": ([vp, vp, vp, vp], ctypes.c_int),
+            "moshi_step_forced": ([vp, vp, vp, vp, vp], ctypes.c_int),
+            "moshi_test_set_spin_limit": ([vp, i32], ctypes.c_int),
             "moshi_temporal_step": ([vp, vp, vp], ctypes.c_int),
             "moshi_step_enqueue": ([vp, vp, vp, vp], ctypes.c_int),
             "moshi_sync": ([vp], ctypes.c_int),
@@ -107,6 +114,22 @@ def lib():
     return _lib
 
 
+def unload():
+    """Unloads libmoshi.so (after every context has been destroyed), so that
+    its HIP module teardown runs now, while the GPU runtime is fully alive,
+    rather than among the process's exit handlers."""
+    global _lib
+    if _lib is None:
+        return
+    alive = [c for c in _live_ctx if c.h]
+    if alive:
+        raise RuntimeError(f"{len(alive)} moshi context(s) still alive: destroy them first")
+    import _ctypes
+    h = _lib._handle
+    _lib = None
+    _ctypes.dlclose(h)
+
+
 def _p(a):
     return None if a is None else a.ctypes.data
 
@@ -122,7 +145,7 @@ def _check(status, ctx=None):
 
 def make_config(dim, n_layers, n_heads, ffn_hidden, window, dep_dim, dep_layers, dep_heads,
                 dep_ffn_hidden, n_substeps, text_vocab, audio_card, rope_theta=1e4,
-                norm_eps=1e-8, dtype="bf16", max_sessions=1, flags=0) -> moshi_config:
+                norm_eps=1e-8, dtype="bf16", max_sessions=1, flags=0, dep_q=0) -> moshi_config:
     c = moshi_config()
     c.dim, c.n_layers, c.n_heads, c.ffn_hidden, c.window = dim, n_layers, n_heads, ffn_hidden, window
     c.dep_dim, c.dep_layers, c.dep_heads = dep_dim, dep_layers, dep_heads
@@ -130,7 +153,7 @@ def make_config(dim, n_layers, n_heads, ffn_hidden, window, dep_dim, dep_layers,
     c.text_vocab, c.audio_card = text_vocab, audio_card
     c.rope_theta, c.norm_eps = rope_theta, norm_eps
     c.dtype = MOSHI_BF16 if dtype in ("bf16", MOSHI_BF16) else MOSHI_F32
-    c.max_sessions, c.flags = max_sessions, flags
+    c.max_sessions, c.flags, c.dep_q = max_sessions, flags, dep_q
     return c
 
 
@@ -167,7 +190,9 @@ def moshi_create(cfg, tensors, hip_stream=None) -> Ctx:
     st = _check(lib().moshi_create(ctypes.byref(cfg), ptrs, len(arrs), hip_stream,
                                    ctypes.byref(out)))
     del st
-    return Ctx(out.value, cfg)
+    ctx = Ctx(out.value, cfg)
+    _live_ctx.add(ctx)
+    return ctx
 
 
 def moshi_destroy(ctx: Ctx):
@@ -193,6 +218,21 @@ def moshi_step(ctx: Ctx, frames):
     codes = np.empty((ctx.B, ctx.S), np.int32)
     _check(lib().moshi_step(ctx.h, _p(f), _p(tok), _p(codes)), ctx)
     return tok, codes
+
+
+def moshi_step_forced(ctx: Ctx, frames, forced=None):
+    """frames int32 [B, 1+S]; forced int32 [B, 1+S] (-1 = not forced) or None
+    -> (text_token [B], audio_codes [B, S])."""
+    f = np.ascontiguousarray(frames, np.int32).reshape(ctx.B, ctx.S + 1)
+    fc = None if forced is None else np.ascontiguousarray(forced, np.int32).reshape(ctx.B, ctx.S + 1)
+    tok = np.empty(ctx.B, np.int32)
+    codes = np.empty((ctx.B, ctx.S), np.int32)
+    _check(lib().moshi_step_forced(ctx.h, _p(f), _p(fc), _p(tok), _p(codes)), ctx)
+    return tok, codes
+
+
+def moshi_test_set_spin_limit(ctx: Ctx, limit: int):
+    _check(lib().moshi_test_set_spin_limit(ctx.h, int(limit)), ctx)
 
 
 def moshi_step_enqueue(ctx: Ctx, d_frames: int, d_text_token: int = None,

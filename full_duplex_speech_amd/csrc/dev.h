@@ -1438,7 +1438,8 @@ __device__ __forceinline__ void combine_direct(const AttnArgs& a, int h, int b, 
 }
 
 // Depformer attention of slot b, heads head0 .. head0+n_heads-1, keys 0 ..
-// nvalid-1 (nvalid <= DEP_MAX_KEYS), by one workgroup of NTH threads: wave w
+// nvalid-1 except key `excl` (-1: none; nvalid <= DEP_MAX_KEYS), by one
+// workgroup of NTH threads: wave w
 // takes heads w, w + NW, ..., NH at a time (every load of those heads is
 // requested before any is used). Scores: TK lanes per key, fp64 dot products
 // reduced in the lanes; softmax over the keys in fp64; p.V: one lane per
@@ -1449,7 +1450,7 @@ __device__ __forceinline__ void combine_direct(const AttnArgs& a, int h, int b, 
 constexpr int DEP_MAX_KEYS = DEP_MAX_KEYS_HOST;
 template <typename T, int HD, int NTH, bool C, int NH>
 __device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int head0, int n_heads,
-                                              int nvalid) {
+                                              int nvalid, int excl) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int TK = HD / VEC;        // lanes per key for the scores
   constexpr int KPW = 64 / TK;        // keys per wave pass
@@ -1517,8 +1518,8 @@ __device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int head
         const int j = p * KPW + kq;
         if (kd == 0 && j < DEP_MAX_KEYS) sp[j] = d * scale;
       }
-      // softmax over the valid keys
-      const double sv = lane < nvalid ? sp[lane] : -INFINITY;
+      // softmax over the valid keys (entry `excl` masked)
+      const double sv = (lane < nvalid && lane != excl) ? sp[lane] : -INFINITY;
       const double m = group_reduce<64, true>(sv);
       const double pj = (sv == -INFINITY) ? 0.0 : exp(sv - m);
       const double l = group_reduce<64>(pj);

@@ -20,9 +20,11 @@
 #include <vector>
 
 #include "../../include/moshi.h"
+#include "host.h"
 #include "kernels.h"
 
 using namespace moshi;
+using moshi_host::SlotTable;
 
 namespace {
 
@@ -53,40 +55,8 @@ const char* kClassNames[KC_COUNT] = {
     "dep_attn",   "dep_o",         "dep_gateup",    "dep_down",      "dep_head",
     "temporal_attn_combine", "argmax_reduce"};
 
-bool valid_head_dim(int hd) { return hd == 32 || hd == 64 || hd == 128; }
-
-int32_t tensor_count(const moshi_config* c) {
-  const int S = c->n_substeps, L = c->n_layers, Ld = c->dep_layers;
-  return 1 + S + 6 * L + 2 + S + S + 2 * Ld + 4 * S * Ld + S;
-}
-
-const char* config_error(const moshi_config* c) {
-  if (!c) return "config is NULL";
-  if (c->dtype != MOSHI_F32 && c->dtype != MOSHI_BF16) return "dtype must be MOSHI_F32 or MOSHI_BF16";
-  const int vec = c->dtype == MOSHI_BF16 ? 8 : 4;
-  if (c->dim <= 0 || c->n_heads <= 0 || c->dim % c->n_heads) return "dim must be a positive multiple of n_heads";
-  if (!valid_head_dim(c->dim / c->n_heads)) return "temporal head_dim must be 32, 64 or 128";
-  if (c->dep_dim <= 0 || c->dep_heads <= 0 || c->dep_dim % c->dep_heads) return "dep_dim must be a positive multiple of dep_heads";
-  if (!valid_head_dim(c->dep_dim / c->dep_heads)) return "depformer head_dim must be 32, 64 or 128";
-  if (c->n_layers < 1 || c->dep_layers < 1) return "n_layers and dep_layers must be >= 1";
-  if (c->n_substeps < 1 || c->n_substeps > 64) return "n_substeps must be in [1, 64]";
-  if (c->ffn_hidden <= 0 || c->dep_ffn_hidden <= 0) return "ffn widths must be positive";
-  if (c->dim % vec || c->ffn_hidden % vec || c->dep_dim % vec || c->dep_ffn_hidden % vec)
-    return "widths must be multiples of 8 (bf16) / 4 (fp32)";
-  if (c->window < 1 || c->window > ATTN_CHUNK * ATTN_MAX_CHUNKS) return "window must be in [1, 32768]";
-  {
-    const int esz = c->dtype == MOSHI_BF16 ? 2 : 4;
-    const int kmax = c->ffn_hidden > c->dim ? c->ffn_hidden : c->dim;
-    if ((long)kmax * esz > 49152 || (long)c->dep_ffn_hidden * esz > 49152)
-      return "projection inputs must fit 48 KB of LDS (ffn_hidden * element size)";
-  }
-  if ((c->flags & MOSHI_FLAG_MASK_OLDEST) && c->window < 2) return "mask-oldest needs window >= 2";
-  if (c->flags & ~MOSHI_FLAG_MASK_OLDEST) return "unknown flag bits";
-  if (c->text_vocab < 2 || c->audio_card < 2) return "vocabularies must have >= 2 entries";
-  if (c->max_sessions < 1 || c->max_sessions > 64) return "max_sessions must be in [1, 64]";
-  if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0)) return "rope_theta must be > 0 and norm_eps >= 0";
-  return nullptr;
-}
+int32_t tensor_count(const moshi_config* c) { return moshi_host::tensor_count(c); }
+const char* config_error(const moshi_config* c) { return moshi_host::config_error(c); }
 
 }  // namespace
 
@@ -95,6 +65,7 @@ struct moshi_ctx {
   int B = 0, dtype = 0, esz = 0, device = 0;
   int D = 0, H = 0, hd = 0, F = 0, W = 0, L = 0;
   int Dd = 0, Hd = 0, hdd = 0, Fd = 0, Ld = 0, S = 0, Vt = 0, Va = 0, NCH = 0;
+  int S_run = 0;  // depformer substeps run per frame
   hipStream_t stream = nullptr;
   bool own_stream = false;
   bool failed = false;
@@ -109,6 +80,7 @@ struct moshi_ctx {
   const void* dep_in = nullptr;  // [S*Dd][D], contiguous
   std::vector<const void*> dep_emb, dep_attn_norm, dep_mlp_norm, dep_qkv, dep_o, dep_gate_up,
       dep_down, dep_head;
+  const void* dep_out_norm = nullptr;  // MOSHI_FLAG_DEP_FINAL_NORM only
 
   // state and activations (device)
   void *ring_k = nullptr, *ring_v = nullptr;  // [B][L][H][W][hd]
@@ -125,19 +97,26 @@ struct moshi_ctx {
   int *d_frames = nullptr, *d_live = nullptr;
   int64_t* d_pos = nullptr;
   int* d_err = nullptr;  // set by the embedding when a live code was out of range
+  int* d_forced = nullptr;  // [B][1+S] forced text / codes, -1 = not forced
   double *d_inv_freq = nullptr;
   void* staging = nullptr;  // one layer of prefill K or V
   int max_spans = 0;  // temporal attention spans per (slot, head)
   int ncu = 1;        // compute units of the device
 
-  // host state (the device copies of live / pos are refreshed only when
-  // `meta_dirty`; the step itself advances the device positions)
-  std::vector<int> live;
-  std::vector<int64_t> pos;
-  bool meta_dirty = true;
+  // host state: the slot table (the device copies of live / pos are
+  // refreshed only when it is dirty; the step itself advances the device
+  // positions)
+  SlotTable slots;
   int* h_frames = nullptr;  // pinned
   int* h_live = nullptr;
   int64_t* h_pos = nullptr;
+  int* h_forced = nullptr;
+  bool forced_on_device = false;  // d_forced holds a forced step's values
+  // recorded after the last copy out of h_live / h_pos / h_forced: those
+  // pinned buffers are rewritten only once it has completed, so a step
+  // enqueued earlier still reads its own metadata
+  hipEvent_t meta_ev = nullptr;
+  bool meta_ev_pending = false;
   int* h_tokens = nullptr;
   int* h_codes = nullptr;
 
@@ -154,6 +133,7 @@ struct moshi_ctx {
   size_t step_lds = 0;
   int step_parity = 0;
   uint32_t step_seq = 0;  // sequence number of the last step kernel launch
+  StepArgs step_host{};   // host copy of *d_step
 
   // kernel timing (eager launches bracketed by events); `dry` only records
   // the (class, bytes) sequence of a step without launching anything
@@ -224,11 +204,7 @@ hipError_t run(moshi_ctx* c, int kclass, double bytes, F&& launch) {
   return hipSuccess;
 }
 
-int live_count(const moshi_ctx* c) {
-  int n = 0;
-  for (int v : c->live) n += v;
-  return n;
-}
+int live_count(const moshi_ctx* c) { return c->slots.live_count(); }
 
 GemmArgs gemm_base(const moshi_ctx* c) {
   GemmArgs a;
@@ -328,10 +304,11 @@ GemmArgs t_head_args(const moshi_ctx* c) {
   return a;
 }
 
-// y_pre[s] = W_in[s] . hidden for every substep at once
+// y_pre[s] = W_in[s] . hidden for every substep run, at once (the input
+// projections of all substeps are one [S * Dd, D] matrix)
 GemmArgs d_in_args(const moshi_ctx* c) {
   GemmArgs a = gemm_base(c);
-  a.W = c->dep_in; a.N = c->S * c->Dd; a.K = c->D; a.X = c->hid; a.ldx = c->D;
+  a.W = c->dep_in; a.N = c->S_run * c->Dd; a.K = c->D; a.X = c->hid; a.ldx = c->D;
   a.out64 = c->pre; a.ldo = c->S * c->Dd;
   return a;
 }
@@ -355,6 +332,8 @@ AttnArgs d_attn_args(const moshi_ctx* c, int s, int l) {
   a.slot_stride = d_slot_stride(c); a.layer_off = (int64_t)l * d_layer_elems(c);
   a.head_stride = (int64_t)c->S * c->hdd;
   a.cap = c->S; a.pos = nullptr; a.scalar_nvalid = s + 1; a.live = c->d_live;
+  // the depformer ring reading masks entry 0 at the last substep run
+  a.scalar_excl = ((c->c.flags & MOSHI_FLAG_DEP_REF_RING) && s == c->S_run - 1) ? 0 : -1;
   a.n_heads = c->Hd; a.max_spans = 1; a.part = c->attn_part;  // S <= 64: one span
   a.o_out = c->od; a.ldo = c->Dd;
   return a;
@@ -384,10 +363,15 @@ GemmArgs d_dn_args(const moshi_ctx* c, int s, int l) {
   return a;
 }
 
-// head s on the rounded residual -> logits + argmax partials
+// head s on the rounded residual (or, with the final-norm reading, on its
+// RMSNorm) -> logits + argmax partials
+bool dep_final_norm(const moshi_ctx* c) { return (c->c.flags & MOSHI_FLAG_DEP_FINAL_NORM) != 0; }
 GemmArgs d_head_args(const moshi_ctx* c, int s) {
   GemmArgs a = gemm_base(c);
   a.W = c->dep_head[s]; a.N = c->Va; a.K = c->Dd; a.X = c->y; a.ldx = c->Dd;
+  if (dep_final_norm(c)) {
+    a.ssq = c->ssq_d; a.n_ssq = n_ssq(c, c->Dd); a.gain = c->dep_out_norm;
+  }
   a.xn_out = c->B > 1 ? c->hnd : nullptr;
   a.logits = c->audio_logits + (size_t)s * c->Va; a.ldo = c->S * c->Va;
   a.apart = c->apart;
@@ -416,8 +400,8 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
       AttnArgs a = t_attn_args(c, l);
       double keys = 0;
       for (int b = 0; b < B; ++b)
-        if (c->live[b]) {
-          int64_t p = c->pos[b];
+        if (c->slots.live[b]) {
+          int64_t p = c->slots.pos[b];
           int64_t n = p + 1 < c->W ? p + 1 : c->W;
           if (a.mask_oldest && p >= c->W - 1) n -= 1;
           keys += (double)n;
@@ -453,7 +437,8 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
             [&] { return gemm(c, PRO_NORM, EPI_ARGMAX, a); });
     if (e != hipSuccess) return e;
     e = run(c, KC_ARGMAX, 0.0, [&] {
-      return launch_argmax_reduce(c->apart, (c->Vt + 15) / 16, c->Vt, B, c->tokens, 1, c->stream);
+      return launch_argmax_reduce(c->apart, (c->Vt + 15) / 16, c->Vt, B, c->tokens, 1, c->d_forced,
+                                  c->NCH, 0, c->stream);
     });
     if (e != hipSuccess) return e;
   }
@@ -468,19 +453,23 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
   hipError_t e;
   {
     GemmArgs a = d_in_args(c);
-    e = run(c, KC_D_INPROJ, (double)S * Dd * D * es,
+    e = run(c, KC_D_INPROJ, (double)c->S_run * Dd * D * es,
             [&] { return gemm(c, PRO_DIRECT, EPI_STORE, a); });
     if (e != hipSuccess) return e;
   }
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s < c->S_run; ++s) {
     {  // entry: y = pre[s] + E_s[previous token]; for s >= 1 the previous
-       // head's partials are reduced here and code s-1 is stored
+       // head's partials are reduced here (or the forced code taken) and
+       // code s-1 is stored
       EntryArgs a;
       memset(&a, 0, sizeof(a));
       a.pre = c->pre; a.ldpre = S * Dd; a.s = s; a.table = c->dep_emb[s];
       a.prev = s == 0 ? c->tokens : c->codes + (s - 1); a.prev_stride = s == 0 ? 1 : S;
       a.prev_part = s == 0 ? nullptr : c->apart; a.prev_tiles = (c->Va + 15) / 16;
       a.prev_n = c->Va; a.D = Dd; a.B = B; a.y = c->y; a.ssq_out = c->ssq_d;
+      if (s > 0) {
+        a.forced = c->d_forced; a.forced_stride = c->NCH; a.forced_col = s;
+      }
       a.ssq_rows = ssq_rows(c);
       e = run(c, KC_D_ENTRY, nlive * Dd * es, [&] { return launch_entry(dt, a, c->stream); });
       if (e != hipSuccess) return e;
@@ -519,14 +508,22 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
     }
     {
       GemmArgs a = d_head_args(c, s);
-      e = run(c, KC_D_HEAD, (double)c->Va * Dd * es, [&] { return gemm(c, PRO_CAST, EPI_ARGMAX, a); });
+      const int pro = dep_final_norm(c) ? PRO_NORM : PRO_CAST;
+      e = run(c, KC_D_HEAD, (double)c->Va * Dd * es + (dep_final_norm(c) ? Dd * es : 0.0),
+              [&] { return gemm(c, pro, EPI_ARGMAX, a); });
       if (e != hipSuccess) return e;
     }
   }
   // the last substep's code (earlier ones are stored by the next entry)
+  const int sl = c->S_run - 1;
+  e = run(c, KC_ARGMAX, 0.0, [&] {
+    return launch_argmax_reduce(c->apart, (c->Va + 15) / 16, c->Va, B, c->codes + sl, S,
+                                c->d_forced, c->NCH, sl + 1, c->stream);
+  });
+  if (e != hipSuccess) return e;
+  // free slots and substeps not run read -1
   return run(c, KC_ARGMAX, 0.0, [&] {
-    return launch_argmax_reduce(c->apart, (c->Va + 15) / 16, c->Va, B, c->codes + (S - 1), S,
-                                c->stream);
+    return launch_finish_outputs(c->tokens, c->codes, c->d_live, B, S, c->S_run, c->stream);
   });
 }
 
@@ -630,6 +627,12 @@ int setup_step(moshi_ctx* c) {
   A.tab_lds = (int)lds;
   lds += tab.size() * sizeof(void*);
   A.S = c->S; A.Ld = c->Ld; A.Hd = c->Hd; A.Dd = c->Dd; A.Vt = c->Vt; A.Va = c->Va;
+  A.S_run = c->S_run;
+  A.dep_final_norm = dep_final_norm(c) ? 1 : 0;
+  A.d_attn.scalar_excl = (c->c.flags & MOSHI_FLAG_DEP_REF_RING) ? 0 : -1;  // on / off
+  A.forced = c->d_forced;
+  A.spin_limit = STEP_SPIN_LIMIT;
+  A.ll_spin_limit = STEP_LL_SPIN_LIMIT;
   A.d_layer_elems = d_layer_elems(c);
   A.pre = c->pre; A.y = c->y; A.ssq_d = c->ssq_d; A.apart = c->apart;
   A.audio_logits = c->audio_logits;
@@ -655,6 +658,7 @@ int setup_step(moshi_ctx* c) {
   }
   CKD(c, dalloc(c, (void**)&c->d_step, sizeof(StepArgs)));
   CKD(c, hipMemcpy(c->d_step, &A, sizeof(StepArgs), hipMemcpyHostToDevice));
+  c->step_host = A;
   c->step_grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);  // with the final LDS size
   if (c->step_grid != grid) return MOSHI_OK;  // the staged slices are sized for `grid`
   c->step_lds = lds;
@@ -723,29 +727,56 @@ int check_ctx(moshi_ctx* c) {
 }
 
 int validate_frames(moshi_ctx* c, const int32_t* frames) {
-  if (!frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
-  for (int b = 0; b < c->B; ++b) {
-    if (!c->live[b]) continue;
-    const int32_t* f = frames + (size_t)b * c->NCH;
-    if (f[0] < 0 || f[0] > c->Vt) return fail(c, MOSHI_E_INVALID, "text code out of range");
-    for (int k = 1; k < c->NCH; ++k)
-      if (f[k] < 0 || f[k] > c->Va) return fail(c, MOSHI_E_INVALID, "audio code out of range");
+  const char* e = moshi_host::frames_error(c->slots, frames, c->NCH, c->Vt, c->Va);
+  return e ? fail(c, MOSHI_E_INVALID, e) : MOSHI_OK;
+}
+
+// The pinned metadata buffers may be rewritten: every copy out of them that
+// an earlier call enqueued has completed.
+int wait_meta(moshi_ctx* c) {
+  if (c->meta_ev_pending) {
+    CKD(c, hipEventSynchronize(c->meta_ev));
+    c->meta_ev_pending = false;
   }
   return MOSHI_OK;
 }
 
+int record_meta(moshi_ctx* c) {
+  CKD(c, hipEventRecord(c->meta_ev, c->stream));
+  c->meta_ev_pending = true;
+  return MOSHI_OK;
+}
+
 // Refresh the device copies of liveness and positions after a join, leave or
-// prefill (the step advances the device positions itself).
+// prefill (the step advances the device positions itself). Stream-ordered:
+// steps enqueued before keep the metadata they were enqueued with.
 int upload_meta(moshi_ctx* c) {
-  if (!c->meta_dirty) return MOSHI_OK;
+  if (!c->slots.dirty) return MOSHI_OK;
+  int rc = wait_meta(c);
+  if (rc) return rc;
   for (int b = 0; b < c->B; ++b) {
-    c->h_live[b] = c->live[b];
-    c->h_pos[b] = c->pos[b];
+    c->h_live[b] = c->slots.live[b];
+    c->h_pos[b] = c->slots.pos[b];
   }
   CKD(c, hipMemcpyAsync(c->d_live, c->h_live, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
   CKD(c, hipMemcpyAsync(c->d_pos, c->h_pos, sizeof(int64_t) * c->B, hipMemcpyHostToDevice, c->stream));
-  c->meta_dirty = false;
-  return MOSHI_OK;
+  c->slots.dirty = false;
+  return record_meta(c);
+}
+
+// The forced tokens of the next step ([B][1+S], -1 = not forced; NULL = none
+// forced), copied to the device only when they change.
+int upload_forced(moshi_ctx* c, const int32_t* forced) {
+  if (!forced && !c->forced_on_device) return MOSHI_OK;
+  int rc = wait_meta(c);
+  if (rc) return rc;
+  const size_t n = (size_t)c->B * c->NCH;
+  for (size_t i = 0; i < n; ++i)
+    c->h_forced[i] = (forced && c->slots.live[i / c->NCH]) ? forced[i] : -1;
+  CKD(c, hipMemcpyAsync(c->d_forced, c->h_forced, sizeof(int) * n, hipMemcpyHostToDevice,
+                        c->stream));
+  c->forced_on_device = forced != nullptr;
+  return record_meta(c);
 }
 
 // Stage the host frames (zeros for free slots) and the slot metadata.
@@ -755,20 +786,23 @@ int upload_step_inputs(moshi_ctx* c, const int32_t* frames) {
   if (!frames) return MOSHI_OK;
   for (int b = 0; b < c->B; ++b)
     for (int k = 0; k < c->NCH; ++k)
-      c->h_frames[(size_t)b * c->NCH + k] = c->live[b] ? frames[(size_t)b * c->NCH + k] : 0;
+      c->h_frames[(size_t)b * c->NCH + k] = c->slots.live[b] ? frames[(size_t)b * c->NCH + k] : 0;
   CKD(c, hipMemcpyAsync(c->d_frames, c->h_frames, sizeof(int) * c->B * c->NCH,
                         hipMemcpyHostToDevice, c->stream));
   return MOSHI_OK;
 }
 
 int run_step(moshi_ctx* c, const int32_t* frames, int32_t* text_token, int32_t* audio_codes,
-             bool with_dep) {
+             bool with_dep, const int32_t* forced = nullptr) {
   int rc = check_ctx(c);
   if (rc) return rc;
   if ((rc = validate_frames(c, frames))) return rc;
+  if (const char* e = moshi_host::forced_error(c->slots, forced, c->NCH, c->Vt, c->Va))
+    return fail(c, MOSHI_E_INVALID, e);
   const bool pers = c->persistent && with_dep && !c->timing;
   if (!pers && (rc = ensure_graphs(c, true, with_dep))) return rc;
   if ((rc = upload_step_inputs(c, frames))) return rc;
+  if ((rc = upload_forced(c, forced))) return rc;
   int abort_flag = 0;
   if (pers) {
     if (live_count(c) > 0 && (rc = launch_persistent(c, c->d_frames, c->tokens, c->codes)))
@@ -783,13 +817,15 @@ int run_step(moshi_ctx* c, const int32_t* frames, int32_t* text_token, int32_t* 
     CKD(c, hipMemcpyAsync(c->h_codes, c->codes, sizeof(int) * c->B * c->S, hipMemcpyDeviceToHost,
                           c->stream));
   CKD(c, hipStreamSynchronize(c->stream));
+  c->meta_ev_pending = false;
   if ((rc = check_abort(c, abort_flag))) return rc;
+  c->slots.advance();
   for (int b = 0; b < c->B; ++b) {
-    if (c->live[b]) c->pos[b] += 1;
-    if (text_token) text_token[b] = c->live[b] ? c->h_tokens[b] : -1;
+    if (text_token) text_token[b] = c->slots.live[b] ? c->h_tokens[b] : -1;
     if (with_dep && audio_codes)
       for (int s = 0; s < c->S; ++s)
-        audio_codes[(size_t)b * c->S + s] = c->live[b] ? c->h_codes[(size_t)b * c->S + s] : -1;
+        audio_codes[(size_t)b * c->S + s] =
+            (c->slots.live[b] && s < c->S_run) ? c->h_codes[(size_t)b * c->S + s] : -1;
   }
   return MOSHI_OK;
 }
@@ -862,6 +898,7 @@ int upload_weights(moshi_ctx* c, const void* const* t) {
   c->dep_head.resize(S);
   for (int s = 0; s < S; ++s)
     if ((rc = put(t[i++], (size_t)Va * Dd, &c->dep_head[s]))) return rc;
+  if (dep_final_norm(c) && (rc = put(t[i++], Dd, &c->dep_out_norm))) return rc;
   return MOSHI_OK;
 }
 
@@ -913,6 +950,7 @@ int alloc_buffers(moshi_ctx* c) {
       {(void**)&c->d_live, B * 4},
       {(void**)&c->d_pos, B * 8},
       {(void**)&c->d_err, 4},
+      {(void**)&c->d_forced, B * c->NCH * 4},
       {(void**)&c->d_inv_freq, (size_t)(c->hd / 2) * 8},
       {&c->staging, (size_t)c->W * D * es},
   };
@@ -926,6 +964,7 @@ int alloc_buffers(moshi_ctx* c) {
   // are ever attended.
   for (size_t i = 4; i < sizeof(reqs) / sizeof(reqs[0]); ++i)
     CKD(c, hipMemsetAsync(*reqs[i].p, 0, reqs[i].bytes, c->stream));
+  CKD(c, hipMemsetAsync(c->d_forced, 0xff, B * c->NCH * 4, c->stream));  // -1: nothing forced
   std::vector<double> inv(c->hd / 2);
   for (int i = 0; i < c->hd / 2; ++i) inv[i] = pow((double)c->c.rope_theta, -2.0 * i / c->hd);
   CKD(c, hipMemcpyAsync(c->d_inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice,
@@ -937,6 +976,8 @@ int alloc_buffers(moshi_ctx* c) {
   CKD(c, hipHostMalloc((void**)&c->h_pos, sizeof(int64_t) * B, hipHostMallocDefault));
   CKD(c, hipHostMalloc((void**)&c->h_tokens, sizeof(int) * B, hipHostMallocDefault));
   CKD(c, hipHostMalloc((void**)&c->h_codes, sizeof(int) * B * S, hipHostMallocDefault));
+  CKD(c, hipHostMalloc((void**)&c->h_forced, sizeof(int) * B * c->NCH, hipHostMallocDefault));
+  CKD(c, hipEventCreateWithFlags(&c->meta_ev, hipEventDisableTiming));
   return MOSHI_OK;
 }
 
@@ -953,6 +994,8 @@ void release(moshi_ctx* c) {
   if (c->h_pos) (void)hipHostFree(c->h_pos);
   if (c->h_tokens) (void)hipHostFree(c->h_tokens);
   if (c->h_codes) (void)hipHostFree(c->h_codes);
+  if (c->h_forced) (void)hipHostFree(c->h_forced);
+  if (c->meta_ev) (void)hipEventDestroy(c->meta_ev);
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
   delete c;
 }
@@ -1014,7 +1057,7 @@ int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vect
       break;
     }
     if ((rc = check_abort(c, abort_flag))) break;
-    c->pos[0] += 1;
+    c->slots.advance();
     const double ms_per_tick = 1.0 / (double)rate_khz;
     for (size_t k = 0; k < nb; ++k) {
       acc_ms[cls[k]] += (double)(tr[k + 1] - tr[k]) * ms_per_tick;
@@ -1085,8 +1128,8 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
   c->Dd = cfg->dep_dim; c->Hd = cfg->dep_heads; c->hdd = cfg->dep_dim / cfg->dep_heads;
   c->Fd = cfg->dep_ffn_hidden; c->Ld = cfg->dep_layers; c->S = cfg->n_substeps;
   c->Vt = cfg->text_vocab; c->Va = cfg->audio_card; c->NCH = 1 + cfg->n_substeps;
-  c->live.assign(c->B, 0);
-  c->pos.assign(c->B, 0);
+  c->slots.init(c->B);
+  c->S_run = moshi_host::dep_steps(cfg);
   const char* ng = getenv("MOSHI_NO_GRAPH");
   c->use_graphs = !(ng && ng[0] == '1');
   if (hipGetDevice(&c->device) != hipSuccess) {
@@ -1125,24 +1168,16 @@ int moshi_destroy(moshi_ctx* ctx) {
 int moshi_session_join(moshi_ctx* ctx, int32_t* slot_out) {
   if (!ctx || !slot_out) return MOSHI_E_INVALID;
   if (ctx->failed) return MOSHI_E_DEVICE;
-  for (int b = 0; b < ctx->B; ++b)
-    if (!ctx->live[b]) {
-      ctx->live[b] = 1;
-      ctx->pos[b] = 0;
-      ctx->meta_dirty = true;
-      *slot_out = b;
-      return MOSHI_OK;
-    }
-  return fail(ctx, MOSHI_E_FULL, "every slot is live");
+  const int b = ctx->slots.join();
+  if (b < 0) return fail(ctx, MOSHI_E_FULL, "every slot is live");
+  *slot_out = b;
+  return MOSHI_OK;
 }
 
 int moshi_session_leave(moshi_ctx* ctx, int32_t slot) {
   if (!ctx) return MOSHI_E_INVALID;
   if (ctx->failed) return MOSHI_E_DEVICE;
-  if (slot < 0 || slot >= ctx->B || !ctx->live[slot]) return fail(ctx, MOSHI_E_NOSESSION, "slot not live");
-  ctx->live[slot] = 0;
-  ctx->pos[slot] = 0;
-  ctx->meta_dirty = true;
+  if (!ctx->slots.leave(slot)) return fail(ctx, MOSHI_E_NOSESSION, "slot not live");
   return MOSHI_OK;
 }
 
@@ -1150,11 +1185,29 @@ int moshi_step(moshi_ctx* ctx, const int32_t* frames, int32_t* text_token, int32
   return run_step(ctx, frames, text_token, audio_codes, true);
 }
 
+int moshi_step_forced(moshi_ctx* ctx, const int32_t* frames, const int32_t* forced,
+                      int32_t* text_token, int32_t* audio_codes) {
+  return run_step(ctx, frames, text_token, audio_codes, true, forced);
+}
+
+int moshi_test_set_spin_limit(moshi_ctx* c, int32_t limit) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (limit < 1) return fail(c, MOSHI_E_INVALID, "spin limit must be >= 1");
+  if (!c->persistent) return fail(c, MOSHI_E_INVALID, "no step kernel on this context");
+  c->step_host.spin_limit = limit;
+  c->step_host.ll_spin_limit = limit;
+  CKD(c, hipStreamSynchronize(c->stream));
+  CKD(c, hipMemcpy(c->d_step, &c->step_host, sizeof(StepArgs), hipMemcpyHostToDevice));
+  return MOSHI_OK;
+}
+
 int moshi_step_enqueue(moshi_ctx* c, const int32_t* d_frames, int32_t* d_text_token,
                        int32_t* d_audio_codes) {
   int rc = check_ctx(c);
   if (rc) return rc;
   if (!d_frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
+  if ((rc = upload_forced(c, nullptr))) return rc;
   if (c->persistent) {
     if ((rc = upload_meta(c))) return rc;
     if (live_count(c) > 0) {
@@ -1180,8 +1233,7 @@ int moshi_step_enqueue(moshi_ctx* c, const int32_t* d_frames, int32_t* d_text_to
       CKD(c, hipMemcpyAsync(d_audio_codes, c->codes, sizeof(int) * c->B * c->S,
                             hipMemcpyDeviceToDevice, c->stream));
   }
-  for (int b = 0; b < c->B; ++b)
-    if (c->live[b]) c->pos[b] += 1;
+  c->slots.advance();
   return MOSHI_OK;
 }
 
@@ -1212,27 +1264,30 @@ int moshi_depformer_step(moshi_ctx* c, const void* hidden, const int32_t* text_i
   if (rc) return rc;
   if (!hidden || !text_in) return fail(c, MOSHI_E_INVALID, "NULL argument");
   for (int b = 0; b < c->B; ++b)
-    if (c->live[b] && (text_in[b] < 0 || text_in[b] > c->Vt))
+    if (c->slots.live[b] && (text_in[b] < 0 || text_in[b] > c->Vt))
       return fail(c, MOSHI_E_INVALID, "text token out of range");
   if ((rc = ensure_graphs(c, false, true))) return rc;
   if ((rc = upload_step_inputs(c, nullptr))) return rc;
-  for (int b = 0; b < c->B; ++b) c->h_tokens[b] = c->live[b] ? text_in[b] : 0;
+  if ((rc = upload_forced(c, nullptr))) return rc;
+  for (int b = 0; b < c->B; ++b) c->h_tokens[b] = c->slots.live[b] ? text_in[b] : 0;
   CKD(c, hipMemcpyAsync(c->tokens, c->h_tokens, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
   CKD(c, hipMemcpyAsync(c->hid, hidden, (size_t)c->B * c->D * c->esz, hipMemcpyHostToDevice, c->stream));
   if ((rc = launch_part(c, false))) return rc;
   CKD(c, hipMemcpyAsync(c->h_codes, c->codes, sizeof(int) * c->B * c->S, hipMemcpyDeviceToHost, c->stream));
   CKD(c, hipStreamSynchronize(c->stream));
+  c->meta_ev_pending = false;
   if (audio_codes)
     for (int b = 0; b < c->B; ++b)
       for (int s = 0; s < c->S; ++s)
-        audio_codes[(size_t)b * c->S + s] = c->live[b] ? c->h_codes[(size_t)b * c->S + s] : -1;
+        audio_codes[(size_t)b * c->S + s] =
+            (c->slots.live[b] && s < c->S_run) ? c->h_codes[(size_t)b * c->S + s] : -1;
   return MOSHI_OK;
 }
 
 int moshi_session_prefill_kv(moshi_ctx* c, int32_t slot, int32_t n, const void* k, const void* v) {
   int rc = check_ctx(c);
   if (rc) return rc;
-  if (slot < 0 || slot >= c->B || !c->live[slot]) return fail(c, MOSHI_E_NOSESSION, "slot not live");
+  if (!c->slots.is_live(slot)) return fail(c, MOSHI_E_NOSESSION, "slot not live");
   if (n < 0 || n > c->W) return fail(c, MOSHI_E_INVALID, "prefill length outside [0, window]");
   if (n > 0 && (!k || !v)) return fail(c, MOSHI_E_INVALID, "NULL prefill data");
   const size_t layer_elems = (size_t)n * c->D;
@@ -1248,15 +1303,14 @@ int moshi_session_prefill_kv(moshi_ctx* c, int32_t slot, int32_t n, const void* 
     }
   }
   CKD(c, hipStreamSynchronize(c->stream));
-  c->pos[slot] = n;
-  c->meta_dirty = true;
+  c->slots.set_pos(slot, n);
   return MOSHI_OK;
 }
 
 int moshi_session_read_kv(moshi_ctx* c, int32_t slot, void* k, void* v) {
   int rc = check_ctx(c);
   if (rc) return rc;
-  if (slot < 0 || slot >= c->B || !c->live[slot]) return fail(c, MOSHI_E_NOSESSION, "slot not live");
+  if (!c->slots.is_live(slot)) return fail(c, MOSHI_E_NOSESSION, "slot not live");
   if (!k || !v) return fail(c, MOSHI_E_INVALID, "NULL output");
   const size_t layer_elems = (size_t)c->W * c->D;
   const int64_t slot_stride = (int64_t)c->L * c->H * c->W * c->hd;
@@ -1276,22 +1330,23 @@ int moshi_session_read_kv(moshi_ctx* c, int32_t slot, void* k, void* v) {
 
 int moshi_session_info(moshi_ctx* c, int32_t slot, int64_t* pos, int32_t* fill, int32_t* write_idx) {
   if (!c) return MOSHI_E_INVALID;
-  if (slot < 0 || slot >= c->B || !c->live[slot]) return fail(c, MOSHI_E_NOSESSION, "slot not live");
-  const int64_t p = c->pos[slot];
-  if (pos) *pos = p;
-  if (fill) *fill = (int32_t)(p < c->W ? p : c->W);
-  if (write_idx) *write_idx = (int32_t)(p % c->W);
+  if (!c->slots.is_live(slot)) return fail(c, MOSHI_E_NOSESSION, "slot not live");
+  c->slots.info(slot, c->W, pos, fill, write_idx);
   return MOSHI_OK;
 }
 
+// Copies of the last step's outputs are ordered after every step enqueued on
+// the context's stream.
 int moshi_read_logits(moshi_ctx* c, float* text, float* audio) {
   int rc = check_ctx(c);
   if (rc) return rc;
   if (text)
-    CKD(c, hipMemcpy(text, c->text_logits, sizeof(float) * c->B * c->Vt, hipMemcpyDeviceToHost));
+    CKD(c, hipMemcpyAsync(text, c->text_logits, sizeof(float) * c->B * c->Vt,
+                          hipMemcpyDeviceToHost, c->stream));
   if (audio)
-    CKD(c, hipMemcpy(audio, c->audio_logits, sizeof(float) * c->B * c->S * c->Va,
-                     hipMemcpyDeviceToHost));
+    CKD(c, hipMemcpyAsync(audio, c->audio_logits, sizeof(float) * c->B * c->S * c->Va,
+                          hipMemcpyDeviceToHost, c->stream));
+  CKD(c, hipStreamSynchronize(c->stream));
   return MOSHI_OK;
 }
 
@@ -1301,10 +1356,12 @@ int moshi_read_hidden(moshi_ctx* c, float* hidden) {
   if (!hidden) return fail(c, MOSHI_E_INVALID, "NULL argument");
   const size_t n = (size_t)c->B * c->D;
   if (c->dtype == DT_F32) {
-    CKD(c, hipMemcpy(hidden, c->hid, n * 4, hipMemcpyDeviceToHost));
+    CKD(c, hipMemcpyAsync(hidden, c->hid, n * 4, hipMemcpyDeviceToHost, c->stream));
+    CKD(c, hipStreamSynchronize(c->stream));
   } else {
     std::vector<uint16_t> tmp(n);
-    CKD(c, hipMemcpy(tmp.data(), c->hid, n * 2, hipMemcpyDeviceToHost));
+    CKD(c, hipMemcpyAsync(tmp.data(), c->hid, n * 2, hipMemcpyDeviceToHost, c->stream));
+    CKD(c, hipStreamSynchronize(c->stream));
     for (size_t i = 0; i < n; ++i) {
       uint32_t u = (uint32_t)tmp[i] << 16;
       memcpy(&hidden[i], &u, 4);

@@ -85,6 +85,7 @@ struct AttnArgs {
   int cap;
   const int64_t* pos;  // per-slot position (temporal); null = all slots use scalar_nvalid
   int scalar_nvalid;
+  int scalar_excl;     // with pos null: a key index masked out (-1: none)
   const int* live;
   int mask_oldest;
   int n_heads;
@@ -123,6 +124,10 @@ struct EntryArgs {
   const ArgPart* prev_part;  // [prev_tiles][B] or null
   int prev_tiles;
   int prev_n;  // rows of the previous head (index bound)
+  // teacher forcing: where forced[b*forced_stride + forced_col] >= 0 it is
+  // the previous token instead (and is what gets stored to prev); null = none
+  const int* forced;
+  int forced_stride, forced_col;
   int D;
   int B;
   double* y;        // [B][D]
@@ -155,6 +160,11 @@ struct StepArgs {
   double* ssq_d;               // its per-tile sums of squares
   ArgPart* apart;              // argmax partials of the last head
   float* audio_logits;         // [S][Va]
+  int S_run;                   // substeps run per frame (<= S)
+  int dep_final_norm;          // heads read RMSNorm(y) * gain (d_head.gain) instead of y
+  const int* forced;           // [1 + S] forced text / codes of slot 0 (-1: not forced)
+  int spin_limit;              // polls before a grid-barrier wait gives up
+  int ll_spin_limit;           // polls before a flagged-vector wait gives up
   // bookkeeping
   int64_t* pos;                // slot 0 position (advanced at the end)
   const int* live;
@@ -184,6 +194,10 @@ struct StepArgs {
 constexpr int GEMV_KW = 8;
 constexpr int GEMV_SSQ_ROWS = 16 / GEMV_KW;
 constexpr int STEP_THREADS = 512;
+// Default bounds of the step kernel's waits (polls; one memory round trip,
+// ~0.5 us, each): a wait that runs out raises the abort flag.
+constexpr int STEP_SPIN_LIMIT = 1 << 21;
+constexpr int STEP_LL_SPIN_LIMIT = 1 << 20;
 constexpr int STEP_BAR_WORDS = 17 * 1024;  // one barrier counter set (17 pages of 4 KB)
 
 // Whether step.hip has an instantiation for (dtype, temporal head dim,
@@ -258,9 +272,15 @@ hipError_t launch_dep_attn(int dtype, int hd, const AttnArgs& a, int B, hipStrea
 constexpr int DEP_MAX_KEYS_HOST = 16;  // equals DEP_MAX_KEYS in dev.h
 // Merges the per-chunk partials of every (slot, head) with more than one chunk.
 hipError_t launch_attn_combine(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st);
-// tok[b*stride] = argmax over the per-tile partials of column b (lowest index on ties).
+// tok[b*stride] = argmax over the per-tile partials of column b (lowest index
+// on ties), or forced[b*forced_stride + forced_col] where that is >= 0
+// (forced may be null).
 hipError_t launch_argmax_reduce(const ArgPart* part, int n_tiles, int n_rows, int B, int* tok,
-                                int stride, hipStream_t st);
+                                int stride, const int* forced, int forced_stride, int forced_col,
+                                hipStream_t st);
+// Outputs of free slots become -1, and codes of substeps past s_run too.
+hipError_t launch_finish_outputs(int* tokens, int* codes, const int* live, int B, int S, int s_run,
+                                 hipStream_t st);
 hipError_t launch_embed(int dtype, const EmbedArgs& a, hipStream_t st);
 hipError_t launch_entry(int dtype, const EntryArgs& a, hipStream_t st);
 hipError_t launch_advance(int64_t* pos, const int* live, int B, hipStream_t st);

@@ -160,7 +160,8 @@ __global__ __launch_bounds__(256) void norm_kernel(GemmArgs a) {
 // Greedy token of column blockIdx.x from per-tile (max, index) partials.
 __global__ __launch_bounds__(256) void argmax_reduce_kernel(const ArgPart* part, int n_tiles,
                                                             int n_rows, int B, int* tok,
-                                                            int stride) {
+                                                            int stride, const int* forced,
+                                                            int forced_stride, int forced_col) {
   const int b = blockIdx.x;
   const int t = threadIdx.x;
   __shared__ double s_v[4];
@@ -194,8 +195,26 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const ArgPart* part,
         bv = s_v[w];
         bi = s_i[w];
       }
-    tok[(size_t)b * stride] = (bi < n_rows) ? bi : 0;
+    int r = (bi < n_rows) ? bi : 0;
+    if (forced != nullptr) {
+      const int f = forced[(size_t)b * forced_stride + forced_col];
+      if (f >= 0) r = f;
+    }
+    tok[(size_t)b * stride] = r;
   }
+}
+
+// Outputs of free slots read -1, and so do the codes of substeps not run.
+__global__ __launch_bounds__(64) void finish_outputs_kernel(int* tokens, int* codes,
+                                                            const int* live, int B, int S,
+                                                            int s_run) {
+  const int b = blockIdx.x;
+  const int s = threadIdx.x;
+  if (b >= B) return;
+  const bool lv = live[b] != 0;
+  if (s == 0 && !lv) tokens[b] = -1;
+  for (int k = s; k < S; k += 64)
+    if (!lv || k >= s_run) codes[(size_t)b * S + k] = -1;
 }
 
 // ---------------------------------------------------------------------------
@@ -225,7 +244,7 @@ template <typename T, int HD>
 __global__ __launch_bounds__(512) void dep_attn_kernel(AttnArgs a) {
   const int b = blockIdx.x;
   if (!ldg(a.live + b)) return;
-  dep_attention<T, HD, 512, false, 2>(a, b, 0, a.n_heads, a.scalar_nvalid);
+  dep_attention<T, HD, 512, false, 2>(a, b, 0, a.n_heads, a.scalar_nvalid, a.scalar_excl);
 }
 
 // Span merge of (slot blockIdx.y, head blockIdx.x); see combine_item.
@@ -311,9 +330,14 @@ __global__ __launch_bounds__(64) void entry_kernel(EntryArgs a) {
       }
     }
     tok = (bi < a.prev_n) ? bi : 0;
+    if (a.forced != nullptr && b < a.B) {
+      const int f = a.forced[(size_t)b * a.forced_stride + a.forced_col];
+      if (f >= 0) tok = f;
+    }
     if (blockIdx.x == 0 && r == 0 && b < a.B) a.prev[(size_t)b * a.prev_stride] = tok;
   } else if (b < a.B) {
     tok = a.prev[(size_t)b * a.prev_stride];
+    tok = tok < 0 ? 0 : tok;  // a free slot's token (never used) may read -1
   }
   double acc = 0.0;
   if (b < a.B && row < a.D) {
@@ -531,9 +555,17 @@ hipError_t launch_attn_combine(int dtype, int hd, const AttnArgs& a, int B, hipS
 }
 
 hipError_t launch_argmax_reduce(const ArgPart* part, int n_tiles, int n_rows, int B, int* tok,
-                                int stride, hipStream_t st) {
+                                int stride, const int* forced, int forced_stride, int forced_col,
+                                hipStream_t st) {
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3(B), dim3(256), 0, st, part, n_tiles, n_rows, B,
-                     tok, stride);
+                     tok, stride, forced, forced_stride, forced_col);
+  return hipGetLastError();
+}
+
+hipError_t launch_finish_outputs(int* tokens, int* codes, const int* live, int B, int S, int s_run,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(finish_outputs_kernel, dim3(B), dim3(64), 0, st, tokens, codes, live, B, S,
+                     s_run);
   return hipGetLastError();
 }
 

@@ -41,7 +41,6 @@ static_assert(KW == GEMV_KW, "the step kernel's projections use the one-session 
 // streams). The depformer projections instead stage their whole weight slice
 // in LDS during the barrier before them (gemv_stage / gemv_staged).
 constexpr int GU = 4;
-constexpr int SPIN_LIMIT = 1 << 21;  // polls (one memory round trip each, ~0.5 us) before giving up
 
 // Barrier words of one set (32-bit words): one 4 KB page per XCD holding its
 // arrival counter, its registration count and its release word (each on a
@@ -63,6 +62,7 @@ __device__ __forceinline__ unsigned xcc_id() {
 struct Grid {
   unsigned* set;
   int* abort;
+  int limit;        // polls before a wait gives up (STEP_SPIN_LIMIT unless a test lowers it)
   uint64_t* trace;  // optional: barrier exit times of workgroup 0
   unsigned idx;    // barriers passed
   unsigned tshift; // trace entries written at flagged hand-offs (no barrier)
@@ -94,11 +94,11 @@ __device__ __forceinline__ void drain_stores() {
 }
 
 // Thread 0 polls `ctr` until it reaches `target` (wrap-safe) or the abort
-// flag rises. Returns nonzero when the grid must leave.
-__device__ __forceinline__ int poll_until(unsigned* ctr, unsigned target, int* abort) {
+// flag rises, at most `limit` times. Returns nonzero when the grid must leave.
+__device__ __forceinline__ int poll_until(unsigned* ctr, unsigned target, int* abort, int limit) {
   int spins = 0;
   while ((int)(__hip_atomic_load((MOSHI_GLB unsigned*)ctr, MOSHI_RLX, MOSHI_AGT) - target) < 0) {
-    if (++spins > SPIN_LIMIT) {
+    if (++spins > limit) {
       __hip_atomic_store((MOSHI_GLB int*)abort, 1, MOSHI_RLX, MOSHI_AGT);
       return 1;
     }
@@ -137,7 +137,7 @@ __device__ __forceinline__ bool grid_wait(Grid& g, unsigned old) {
           __hip_atomic_store((MOSHI_GLB unsigned*)g.set + x * BW_PAGE + BW_RELEASE, g.idx, MOSHI_RLX,
                              MOSHI_AGT);
     }
-    s_leave = poll_until(g.set + g.xcc * BW_PAGE + BW_RELEASE, g.idx, g.abort);
+    s_leave = poll_until(g.set + g.xcc * BW_PAGE + BW_RELEASE, g.idx, g.abort, g.limit);
     if (g.trace != nullptr && blockIdx.x == 0)
       *(MOSHI_GLB uint64_t*)(g.trace + g.idx + g.tshift) = wall_clock64();
   }
@@ -156,11 +156,12 @@ __device__ __forceinline__ bool grid_sync(Grid& g) {
 // the previous launch, which used it, has finished), count the workgroups of
 // every XCD, and wait for all of them (flat barrier).
 __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn_ctr, int n_heads,
-                                          int parity, int* abort, uint64_t* trace) {
+                                          int parity, int* abort, int limit, uint64_t* trace) {
   __shared__ int s_leave;
   __shared__ unsigned s_cnt[MAX_XCC];
   g.set = bar + parity * STEP_BAR_WORDS;
   g.abort = abort;
+  g.limit = limit;
   g.trace = trace;
   g.idx = 0;
   g.tshift = 0;
@@ -186,7 +187,7 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
     __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + g.xcc * BW_PAGE + BW_REG, 1u, MOSHI_RLX,
                            MOSHI_AGT);
     __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_FLAT, 1u, MOSHI_RLX, MOSHI_AGT);
-    s_leave = poll_until(g.set + BW_FLAT, gridDim.x, abort);
+    s_leave = poll_until(g.set + BW_FLAT, gridDim.x, abort, limit);
     if (trace != nullptr && blockIdx.x == 0) *(MOSHI_GLB uint64_t*)trace = wall_clock64();
   }
   __syncthreads();
@@ -285,12 +286,11 @@ __device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frame
 // head and key span, the span partial [2 (hd + 2)] (M, L, O[hd]); then for
 // each layer the merged attention output O [D] (rounded).
 
-constexpr int LL_SPIN_LIMIT = 1 << 20;
-
 struct LLCtx {
   uint64_t* w;     // the flagged arena
   uint32_t flag;   // this launch's sequence number
   int* abort;
+  int limit;       // polls before a wait gives up
 };
 
 struct LLMap {
@@ -357,7 +357,7 @@ __device__ __forceinline__ bool ll_wait(const LLCtx& c, F addr, u32x4 (&q)[N]) {
 #pragma unroll
     for (int j = 0; j < N; ++j) ok = ok & ll_fresh(q[j], c.flag);
     if (ok) return true;
-    if (spins > LL_SPIN_LIMIT) {
+    if (spins > c.limit) {
       __hip_atomic_store((MOSHI_GLB int*)c.abort, 1, MOSHI_RLX, MOSHI_AGT);
       return false;
     }
@@ -382,7 +382,7 @@ __device__ __forceinline__ bool ll_wait_words(const LLCtx& c, F addr, uint64_t (
 #pragma unroll
     for (int j = 0; j < N; ++j) ok = ok & ((uint32_t)(q[j] >> 32) == c.flag);
     if (ok) return true;
-    if (spins > LL_SPIN_LIMIT) {
+    if (spins > c.limit) {
       __hip_atomic_store((MOSHI_GLB int*)c.abort, 1, MOSHI_RLX, MOSHI_AGT);
       return false;
     }
@@ -540,6 +540,7 @@ struct EntryLL {
   const void* table;
   uint32_t y;                // word of Y[s]
   int* tok_out;
+  const int* forced;         // teacher forcing: the token when forced[0] >= 0 (null: none)
 };
 
 template <typename T, int NTH>
@@ -558,8 +559,13 @@ __device__ __forceinline__ bool ll_input_entry(const GemmArgs& a, const LLCtx& c
                       ? reduce_token<NTH>(E.text_part, n_tiles, E.prev_rows)
                       : ll_reduce_token<NTH>(c, E.ap, 8 * n_tiles, E.prev_rows, ok);
   if (__syncthreads_or(!ok)) return false;
-  if (first && t == 0) st_i32<true>(E.tok_out, tok);
-  const T* row = (const T*)E.table + (uint32_t)tok * a.K;
+  int tk = tok;
+  if (E.forced != nullptr) {
+    const int f = ldg(E.forced);
+    tk = f >= 0 ? f : tk;
+  }
+  if (first && t == 0) st_i32<true>(E.tok_out, tk);
+  const T* row = (const T*)E.table + (uint32_t)tk * a.K;
   double ev[2];
   ld_pair_d(row, p0, ev[0], ev[1]);
   const double y0 = pv[0] + ev[0], y1 = pv[1] + ev[1];
@@ -875,12 +881,12 @@ __device__ __forceinline__ bool ll_span_merge(const LLCtx& c, const LLMap& M, in
 }
 
 // Attention of depformer head h at substep s (keys: entries 0..s of this
-// layer), by wave 0 of one workgroup, from the flagged q, K and V: the
-// arithmetic of dep_attention for one head. The output goes to the flagged
-// O[s][l]. False = leave.
+// layer except entry `excl`, -1 = none), by wave 0 of one workgroup, from the
+// flagged q, K and V: the arithmetic of dep_attention for one head. The
+// output goes to the flagged O[s][l]. False = leave.
 template <typename T, int HD, int NTH>
 __device__ __forceinline__ bool ll_dep_attention(const LLCtx& c, const LLMap& M, int s, int l,
-                                                 int h) {
+                                                 int h, int excl) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int TK = HD / VEC;
   constexpr int KPW = 64 / TK;
@@ -946,7 +952,7 @@ __device__ __forceinline__ bool ll_dep_attention(const LLCtx& c, const LLMap& M,
     }
     ok = ok & ll_wait_words<NV, true>(c, wv, vq);
     // softmax over the valid keys
-    const double sv = lane < nvalid ? s_sc[lane] : -INFINITY;
+    const double sv = (lane < nvalid && lane != excl) ? s_sc[lane] : -INFINITY;
     const double m = group_reduce<64, true>(sv);
     const double pj = (sv == -INFINITY) ? 0.0 : exp(sv - m);
     const double lsum = group_reduce<64>(pj);
@@ -1007,7 +1013,9 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   const int64_t t_lel = uni(A.t_layer_elems), d_lel = uni(A.d_layer_elems);
   Grid g;
   // attention tickets of this launch: temporal heads, then depformer heads
-  if (grid_init(g, uni(A.bar), uni(A.attn_ctr), H + Hd, parity, uni(A.abort), trace)) return;
+  if (grid_init(g, uni(A.bar), uni(A.attn_ctr), H + Hd, parity, uni(A.abort), uni(A.spin_limit),
+                trace))
+    return;
   unsigned* const tickets = uni(A.attn_ctr) + (size_t)parity * (H + Hd) * 16;
   // first weight batch of the next projection, requested before each barrier
   u32x4 pf[GU][16 / KW];
@@ -1085,11 +1093,16 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     return a;
   };
   auto d_head = [&](int s) {
-    GemmArgs a = uni(A.d_head);
+    GemmArgs a = uni(A.d_head);  // with the final norm: its gain and sums of squares set
     a.W = tab(o_dh + s);
     a.logits = uni(A.audio_logits) + (size_t)s * Va;
     return a;
   };
+  const int S_run = uni(A.S_run);
+  const bool dep_final_norm = uni(A.dep_final_norm) != 0;
+  const int* const forced = uni(A.forced);
+  // the depformer ring reading masks entry 0 at the last substep (-1 = off)
+  const int ref_excl_at = uni(A.d_attn.scalar_excl) >= 0 ? S_run - 1 : -1;
 
   // RoPE cos/sin at this step's position, for every temporal q/k/v epilogue
   __shared__ double s_rope[HD / 2][2];
@@ -1106,6 +1119,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   c.w = uni(A.ll);
   c.flag = seq;
   c.abort = uni(A.abort);
+  c.limit = uni(A.ll_spin_limit);
   LLMap M;
   M.Dd = Dd;
   M.Fd = uni(A.d_gu.N);
@@ -1210,7 +1224,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
   auto st_head = [&](int s_) {
     return [&, s_]() { gemv_stage<T, KW, EPI_ARGMAX>(d_head(s_), wg, nwg, wbuf); };
   };
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s < S_run; ++s) {
     for (int l = 0; l < Ld; ++l) {
       LLIo io{};
       io.q = M.Q(s, l);
@@ -1228,6 +1242,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
         E.table = tab(o_de + s);
         E.y = M.Y(s, S);
         E.tok_out = s == 0 ? text_out : codes_out + (s - 1);
+        E.forced = forced != nullptr ? forced + s : nullptr;
         // at s = 0 the grid barrier after the input projections ended the
         // previous operation
         if (!ll_gemv<T, KW, PRO_NORM, EPI_QKV, LLR_QKV_I, LLR_QKV_C, false, true>(
@@ -1241,7 +1256,9 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
           return;
       }
       for (int h = 0; h < Hd; ++h)
-        if ((nqkv + h) % nwg == wg && !ll_dep_attention<T, HDD, NT>(c, M, s, l, h)) return;
+        if ((nqkv + h) % nwg == wg &&
+            !ll_dep_attention<T, HDD, NT>(c, M, s, l, h, s == ref_excl_at ? 0 : -1))
+          return;
       io = LLIo{};
       io.x = M.O(s, l);
       io.resid = l == 0 ? M.Y(s, S) : M.R2(s, l - 1);
@@ -1273,14 +1290,18 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     }
     LLIo io{};
     io.x = M.R2(s, Ld - 1);
+    io.ss = M.S2(s, Ld - 1);
     io.out = M.AP(s, S);
-    bool ok;
-    if (s + 1 < S)
-      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C, true>(
-          d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), st_qkv(s + 1, 0));
-    else
-      ok = ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C, true>(
-          d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), []() {});
+    // the head reads the rounded residual, or with the final norm its
+    // RMSNorm (same input path as a normed projection)
+    auto head = [&](auto next) {
+      if (dep_final_norm)
+        return ll_gemv<T, KW, PRO_NORM, EPI_ARGMAX, LLR_HD_I, LLR_HD_C, true>(
+            d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), next);
+      return ll_gemv<T, KW, PRO_CAST, EPI_ARGMAX, LLR_HD_I, LLR_HD_C, true>(
+          d_head(s), c, io, wg, nwg, xs, wbuf, nullptr, stamp(), next);
+    };
+    const bool ok = s + 1 < S_run ? head(st_qkv(s + 1, 0)) : head([]() {});
     if (!ok) return;
   }
 #undef GEMV
@@ -1288,14 +1309,19 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
 #undef PREFETCH_SYNC
 #undef STAGE_SYNC
 #undef PREFETCH_SYNC_G
-  // ---- last code, next position ----
+  // ---- last code (forced if asked), codes of substeps not run, next position ----
   if (wg == 0) {
     bool ok;
-    const int tok = ll_reduce_token<NT>(c, M.AP(S - 1, S), 8 * M.nta, Va, ok);
+    int tok = ll_reduce_token<NT>(c, M.AP(S_run - 1, S), 8 * M.nta, Va, ok);
+    if (forced != nullptr) {
+      const int f = ldg(forced + S_run);
+      tok = f >= 0 ? f : tok;
+    }
     uint64_t* st = stamp();
+    for (int k = S_run + (int)threadIdx.x; k < S; k += NT) *(MOSHI_GLB int*)(codes_out + k) = -1;
     if (threadIdx.x == 0) {
       if (st != nullptr) *(MOSHI_GLB uint64_t*)st = wall_clock64();
-      *(MOSHI_GLB int*)(codes_out + S - 1) = tok;
+      *(MOSHI_GLB int*)(codes_out + S_run - 1) = tok;
       int64_t* pos = uni(A.pos);
       if (ldg(uni(A.live))) *(MOSHI_GLB int64_t*)pos += 1;
       if (trace != nullptr) *(MOSHI_GLB uint64_t*)(trace + tix + 1) = wall_clock64();

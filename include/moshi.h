@@ -45,10 +45,23 @@ enum {
 
 enum { MOSHI_F32 = 0, MOSHI_BF16 = 1 };
 
-/* Window reading flag: once a session's ring is full, also mask the oldest
- * key (W-1 keys attended instead of W) -- the SGLang-Omni cookbook's
- * "Known limitations" mentions such a masked oldest slot. Default off. */
+/* Reading flags (create-time; default off).
+ * MOSHI_FLAG_MASK_OLDEST: once a session's ring is full, also mask the oldest
+ *   key (W-1 keys attended instead of W) -- SGLang-Omni cookbook
+ *   "PersonaPlex", "Known limitations": the temporal window follows the
+ *   streaming ring, including the masked oldest slot once the cache fills.
+ * MOSHI_FLAG_DEP_FINAL_NORM: each depformer head reads RMSNorm(y) times one
+ *   more gain tensor (dep.out_norm [Dd], appended after the heads) instead of
+ *   the residual y itself -- the other reading of where the depformer's
+ *   norms stop (mobius PR #368, "P2 - Moshi LM", names pre-norm layers and
+ *   no final depformer norm).
+ * MOSHI_FLAG_DEP_REF_RING: the substep K/V behaves as a ring whose capacity
+ *   is the number of substeps run; at the last substep, once it is full,
+ *   entry 0 is masked -- cookbook "Reference parity": the last depformer step
+ *   matches the reference only with its ring behaviour emulated. */
 #define MOSHI_FLAG_MASK_OLDEST 1u
+#define MOSHI_FLAG_DEP_FINAL_NORM 2u
+#define MOSHI_FLAG_DEP_REF_RING 4u
 
 /* Model shape and engine capacity.
  * Temporal transformer: `dim`, `n_layers`, `n_heads` (head_dim = dim/n_heads
@@ -61,6 +74,10 @@ enum { MOSHI_F32 = 0, MOSHI_BF16 = 1 };
  * has 1 + n_substeps rows and every embedding table has card+1 rows.
  * `dtype` MOSHI_BF16 or MOSHI_F32 (weights, K/V and linear inputs);
  * `max_sessions` = capacity B (1..64), fixed for the life of the context.
+ * `flags`: MOSHI_FLAG_* above. `dep_q`: depformer substeps run per frame,
+ * 1..n_substeps, 0 = all (the cookbook's "Known limitations" runs 8: the
+ * agent's codebooks; the recipe's "Architecture": 16 codebooks, 8 vocoded);
+ * codes of substeps not run are returned as -1.
  * Every width (dim, ffn_hidden, dep_dim, dep_ffn_hidden) must be a multiple of
  * 8 (bf16) or 4 (fp32). */
 typedef struct {
@@ -70,10 +87,11 @@ typedef struct {
   double rope_theta, norm_eps;
   int32_t dtype, max_sessions;
   uint32_t flags;
+  int32_t dep_q;
 } moshi_config;
 
 /* Number of weight tensors moshi_create expects for this config (< 0 on a bad
- * config). */
+ * config); the list is in moshi_create's comment. */
 int32_t moshi_n_tensors(const moshi_config* cfg);
 
 /* Creates a context and uploads the weights.
@@ -88,7 +106,10 @@ int32_t moshi_n_tensors(const moshi_config* cfg);
  *   per depformer layer l: attn_norm [Dd], mlp_norm [Dd] (shared by substeps);
  *   per substep s, per layer l: qkv [3Dd, Dd], o [Dd, Dd],
  *     gate_up [2Fd, Dd], down [Dd, Fd];
- *   dep.head.s [Va, Dd] for s < S.
+ *   dep.head.s [Va, Dd] for s < S;
+ *   dep.out_norm [Dd] (MOSHI_FLAG_DEP_FINAL_NORM only).
+ * (Shapes: mobius PR #368, "P2 - Moshi LM": FusedGateUpMLP, weights_per_step
+ * = 16; recipe "Architecture": the 17-row token column.)
  * hip_stream: a hipStream_t created by the caller (not the legacy default
  * stream) that every launch and copy uses, or NULL for a library-owned
  * stream. A borrowed stream is never destroyed.
@@ -97,19 +118,29 @@ int32_t moshi_n_tensors(const moshi_config* cfg);
 int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_tensors,
                  void* hip_stream, moshi_ctx** out);
 
-/* Frees the context and its device memory. NULL is accepted. */
+/* Frees the context and its device memory (every call enqueued on it is
+ * waited for first). NULL is accepted. */
 int moshi_destroy(moshi_ctx* ctx);
 
-/* Opens a session in the lowest free slot: position 0, empty window.
- * MOSHI_E_FULL when all B slots are live. */
+/* Opens a session in the lowest free slot: position 0, empty window
+ * (recipe "When to use this recipe": sessions join on any tick; "Notes": a
+ * recycled slot behaves exactly like a fresh engine).
+ * MOSHI_E_FULL when all B slots are live ("Notes": connections beyond N are
+ * rejected until a slot frees). Host bookkeeping only; it takes effect at the
+ * next step, and steps already enqueued keep the slots they were enqueued
+ * with. */
 int moshi_session_join(moshi_ctx* ctx, int32_t* slot_out);
 
-/* Closes a live session; its slot becomes free for the next join.
+/* Closes a live session; its slot becomes free for the next join (recipe
+ * "When to use this recipe": leaving does not disturb the other slots).
  * MOSHI_E_NOSESSION if the slot is out of range or not live. */
 int moshi_session_leave(moshi_ctx* ctx, int32_t slot);
 
 /* One frame for every live slot (synchronous: returns when the outputs are on
- * the host).
+ * the host) -- recipe "Why it is different": one user frame in, one agent
+ * frame and one text token out per 80 ms tick; mobius PR #368 "P3 - ONNX
+ * Runtime example": the temporal step, greedy text, then the autoregressive
+ * depformer substeps.
  * frames [B, 1+S] int32: row = slot; text code in [0, Vt], audio codes in
  *   [0, Va] (the last row of each table is the initial token). Any live row
  *   out of range -> MOSHI_E_INVALID before any device work, state unchanged.
@@ -120,9 +151,22 @@ int moshi_session_leave(moshi_ctx* ctx, int32_t slot);
  * the slot's ring at position mod W. */
 int moshi_step(moshi_ctx* ctx, const int32_t* frames, int32_t* text_token, int32_t* audio_codes);
 
+/* moshi_step with teacher forcing (mobius PR #368, the persona/voice commit:
+ * the step teacher-forces the agent audio stream for priming; the sampling
+ * commit: an explicitly supplied text token replaces the generated one).
+ * forced [B, 1+S] int32 or NULL: where forced[b][0] >= 0 it is slot b's text
+ * token (fed to depformer substep 0 and returned instead of the model's
+ * choice); where forced[b][1+s] >= 0 it is code s (fed to substep s+1 and
+ * returned). -1 = not forced. Forced text must lie in [0, Vt), forced codes
+ * in [0, Va); anything else -> MOSHI_E_INVALID before any device work. The
+ * logits stay the model's own. */
+int moshi_step_forced(moshi_ctx* ctx, const int32_t* frames, const int32_t* forced,
+                      int32_t* text_token, int32_t* audio_codes);
+
 /* Device-resident step, for callers whose codes already live in HBM (a codec
- * on the same GPU): enqueues one moshi_step on the context's stream and
- * returns without waiting.
+ * on the same GPU; mobius PR #368, the device-resident KV commit: keep the
+ * step's state on the device): enqueues one moshi_step on the context's
+ * stream and returns without waiting.
  * d_frames: DEVICE pointer to [B, 1+S] int32 codes, read when the step runs.
  *   Codes are not checked on the host; a live code outside its table is
  *   clamped to the nearest valid row and reported by the next moshi_sync.
@@ -133,46 +177,59 @@ int moshi_step_enqueue(moshi_ctx* ctx, const int32_t* d_frames, int32_t* d_text_
                        int32_t* d_audio_codes);
 
 /* Waits for every enqueued step. MOSHI_E_INVALID if a clamped code was seen
- * since the last call (the flag is then cleared). */
+ * since the last call (the flag is then cleared); MOSHI_E_DEVICE if a step
+ * kernel gave up waiting (the context is then unusable). */
 int moshi_sync(moshi_ctx* ctx);
 
 /* ---- test and benchmark hooks (same kernels as moshi_step) ---- */
 
 /* Temporal transformer and text head only (the depformer is not run); the
- * positions advance as in moshi_step. text_token [B]. */
+ * positions advance as in moshi_step. text_token [B]. (mobius PR #368, "P2 -
+ * Moshi LM": the temporal task returns the hidden state and text logits.) */
 int moshi_temporal_step(moshi_ctx* ctx, const int32_t* frames, int32_t* text_token);
 
 /* Depformer only, from a given hidden state: hidden [B, D] in the config's
  * dtype (the temporal output after its final norm), text_in [B] in [0, Vt].
- * audio_codes [B, S]. Positions do not move. Rows of non-live slots ignored. */
+ * audio_codes [B, S]. Positions do not move. Rows of non-live slots ignored.
+ * (mobius PR #368, "P2 - Moshi LM": the depformer task takes the hidden
+ * state and the previous token.) */
 int moshi_depformer_step(moshi_ctx* ctx, const void* hidden, const int32_t* text_in,
                          int32_t* audio_codes);
 
 /* Loads K and V of positions 0..n-1 of a live slot (n in [0, W]) and sets its
  * position to n. k, v: [L][n][D] in the config's dtype, already rotated
- * (post-RoPE), head h at columns h*head_dim.. of each row. */
+ * (post-RoPE), head h at columns h*head_dim.. of each row. (A conversation
+ * already n frames into the recipe's 3000-frame ring, "Architecture".)
+ * MOSHI_E_INVALID for n outside [0, W] or NULL data; state unchanged. */
 int moshi_session_prefill_kv(moshi_ctx* ctx, int32_t slot, int32_t n, const void* k,
                              const void* v);
 
 /* Copies a live slot's whole ring out: k, v [L][W][D] in the config's dtype,
  * ring slot j (row j) holding the position congruent to j mod W; rows the
- * session has not written yet are unspecified. */
+ * session has not written yet are unspecified. (The recipe's ring KV cache,
+ * "Architecture".) */
 int moshi_session_read_kv(moshi_ctx* ctx, int32_t slot, void* k, void* v);
 
-/* Bookkeeping of a live slot's next step: absolute position (frames consumed),
- * fill = min(pos, W), ring write index = pos mod W. */
+/* Bookkeeping of a live slot's next step: absolute position (frames consumed;
+ * the RoPE offset, which mobius PR #368 derives from the cache length),
+ * fill = min(pos, W), ring write index = pos mod W (recipe "Notes": the ring
+ * recycles beyond 3000 frames). */
 int moshi_session_info(moshi_ctx* ctx, int32_t slot, int64_t* pos, int32_t* fill,
                        int32_t* write_idx);
 
 /* Logits of the last step: text [B, Vt] and/or audio [B, S, Va] (float32;
- * either may be NULL). Rows of non-live slots are unspecified. */
+ * either may be NULL). Rows of non-live slots, and of substeps not run, are
+ * unspecified. Ordered after every step enqueued on the context's stream.
+ * (mobius PR #368, "P2 - Moshi LM": text_logits and the depformer logits.) */
 int moshi_read_logits(moshi_ctx* ctx, float* text, float* audio);
 
 /* Temporal hidden state of the last step (after the final norm and rounding),
- * [B, D] float32. */
+ * [B, D] float32 (the "hidden" output of mobius PR #368's temporal task). */
 int moshi_read_hidden(moshi_ctx* ctx, float* hidden);
 
-/* Kernel timing. Runs `n_steps` full steps (frames as in moshi_step, outputs
+/* Kernel timing (measurement hook; the per-frame budget of the recipe's
+ * "Notes" and of mobius PR #368's RTF reports). Runs `n_steps` full steps
+ * (frames as in moshi_step, outputs
  * discarded; positions advance) launching every kernel eagerly with a HIP
  * event pair around it on the library's stream, and returns per kernel class
  * c < n_classes: the summed device time in ms (ms[c]), the launch count
@@ -183,11 +240,20 @@ int moshi_time_kernels(moshi_ctx* ctx, const int32_t* frames, int32_t n_steps, d
                        int64_t* launches, double* bytes, int32_t n_classes);
 const char* moshi_kernel_class_name(int32_t c);
 
-/* 1 if moshi_step / moshi_step_enqueue run the whole frame as one persistent
+/* Which implementation runs the step (measurement hook).
+ * 1 if moshi_step / moshi_step_enqueue run the whole frame as one persistent
  * kernel (capacity 1 with a supported shape, unless the environment variable
  * MOSHI_STEP_KERNEL=0 was set at creation), 0 if they run one kernel per
  * operation; the results are identical. Negative on a NULL context. */
 int32_t moshi_uses_step_kernel(const moshi_ctx* ctx);
+
+/* Test hook of the step kernel's bounded waits (the failure path that keeps
+ * a lost hand-off from hanging the GPU): every later launch on this context
+ * gives up after `limit` polls (>= 1) of a grid barrier or flagged input,
+ * raises the context's abort flag, and every workgroup leaves; the call then
+ * fails with MOSHI_E_DEVICE and the context stays failed. MOSHI_E_INVALID if
+ * the context does not use the step kernel. */
+int moshi_test_set_spin_limit(moshi_ctx* ctx, int32_t limit);
 
 /* Static text of a status code. */
 const char* moshi_strerror(int status);

@@ -37,7 +37,8 @@ class Config(ctypes.Structure):
         "dep_dim", "dep_layers", "dep_heads", "dep_ffn_hidden", "n_substeps",
         "text_vocab", "audio_card")] + [
         ("rope_theta", ctypes.c_double), ("norm_eps", ctypes.c_double),
-        ("bf16", ctypes.c_int32), ("mask_oldest", ctypes.c_int32)]
+        ("bf16", ctypes.c_int32), ("mask_oldest", ctypes.c_int32), ("dep_q", ctypes.c_int32),
+        ("dep_final_norm", ctypes.c_int32), ("dep_ref_ring", ctypes.c_int32)]
 
 
 def _p(a):
@@ -168,6 +169,9 @@ def make_config(shape) -> Config:
     c.rope_theta, c.norm_eps = shape.rope_theta, shape.norm_eps
     c.bf16 = 1 if shape.dtype == "bf16" else 0
     c.mask_oldest = 1 if shape.mask_oldest else 0
+    c.dep_q = shape.dep_q
+    c.dep_final_norm = 1 if shape.dep_final_norm else 0
+    c.dep_ref_ring = 1 if shape.dep_ref_ring else 0
     return c
 
 

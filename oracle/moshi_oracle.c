@@ -55,6 +55,9 @@ typedef struct {
   double rope_theta, norm_eps;
   int32_t bf16;        /* 1: bf16 weights, K/V and rounding points; 0: fp32, none */
   int32_t mask_oldest; /* window reading flag (see header) */
+  int32_t dep_q;          /* depformer substeps run per frame; 0 = all n_substeps */
+  int32_t dep_final_norm; /* RMSNorm (gain dep.out_norm) on the residual before each head */
+  int32_t dep_ref_ring;   /* mask substep K/V entry 0 at the last substep run */
 } orc_config;
 
 typedef struct {
@@ -71,6 +74,7 @@ typedef struct {
   const void **dep_attn_norm, **dep_mlp_norm; /* [Ld] */
   const void **dep_qkv, **dep_o, **dep_gate_up, **dep_down; /* [S*Ld] */
   const void** dep_head; /* [S] */
+  const void* dep_out_norm; /* [Dd], with dep_final_norm only */
 } orc_model;
 
 typedef struct {
@@ -213,7 +217,12 @@ int32_t orc_argmax(const double* v, int n, double* margin) {
 
 int32_t orc_n_tensors(const orc_config* c) {
   int S = c->n_substeps, L = c->n_layers, Ld = c->dep_layers;
-  return 1 + S + 6 * L + 2 + S + S + 2 * Ld + 4 * S * Ld + S;
+  return 1 + S + 6 * L + 2 + S + S + 2 * Ld + 4 * S * Ld + S + (c->dep_final_norm ? 1 : 0);
+}
+
+/* Substeps the depformer runs per frame. */
+static int dep_run(const orc_config* c) {
+  return (c->dep_q > 0 && c->dep_q < c->n_substeps) ? c->dep_q : c->n_substeps;
 }
 
 void orc_model_free(orc_model* m) {
@@ -233,6 +242,8 @@ orc_model* orc_model_new(const orc_config* c, const void* const* t, int32_t n) {
   if (c->dep_dim <= 0 || c->dep_heads <= 0 || c->dep_dim % c->dep_heads) return NULL;
   if (c->window < 1 || (c->mask_oldest && c->window < 2)) return NULL;
   if (c->n_substeps < 1 || c->text_vocab < 2 || c->audio_card < 2) return NULL;
+  if (c->dep_q < 0 || c->dep_q > c->n_substeps) return NULL;
+  if (c->dep_ref_ring && dep_run(c) < 2) return NULL;
   if (n != orc_n_tensors(c)) return NULL;
   orc_model* m = (orc_model*)calloc(1, sizeof(orc_model));
   m->c = *c;
@@ -272,6 +283,7 @@ orc_model* orc_model_new(const orc_config* c, const void* const* t, int32_t n) {
     }
   ARR(dep_head, S);
   for (int s = 0; s < S; ++s) m->dep_head[s] = t[i++];
+  if (c->dep_final_norm) m->dep_out_norm = t[i++];
 #undef ARR
   return m;
 }
@@ -510,8 +522,20 @@ int orc_temporal(orc_session* s, const int32_t* frame, double* hidden_out, doubl
  * projection of `hid`, runs every depformer layer with substep s's linears
  * over the substep K/V entries 0..s (cleared at s = 0), and its own head picks
  * code s. forced (optional, [S]) replaces code s as the next substep's input
- * (teacher forcing); the returned codes are always the oracle's own argmax.
- * logits (optional) [S][Va]; margins (optional) [S]. */
+ * (teacher forcing) where it is >= 0; the returned codes are always the
+ * oracle's own argmax. logits (optional) [S][Va]; margins (optional) [S].
+ *
+ * Variants (config flags; readings of the SGLang-Omni cookbook, "Known
+ * limitations": only 8 depformer steps run there, and "Reference parity":
+ * the last depformer step matches the reference only with its ring
+ * behaviour emulated):
+ *  - dep_q > 0: only substeps 0..dep_q-1 run (the agent's codebooks); codes
+ *    of the others are -1, their margins +inf and logits 0;
+ *  - dep_ref_ring: the substep K/V is a ring whose capacity is the number of
+ *    substeps run; once it is full (the last substep) its oldest entry,
+ *    entry 0, is masked, as the temporal ring masks its oldest key;
+ *  - dep_final_norm: each head reads RMSNorm(y) * dep.out_norm (rounded)
+ *    instead of the rounded residual y. */
 int orc_depformer(const orc_model* m, const double* hid, int32_t text_in, const int32_t* forced,
                   double* logits, int32_t* codes, double* margins) {
   const orc_config* c = &m->c;
@@ -520,7 +544,7 @@ int orc_depformer(const orc_model* m, const double* hid, int32_t text_in, const 
   if (text_in < 0 || text_in > c->text_vocab) return -1;
   if (forced)
     for (int s = 0; s < S; ++s)
-      if (forced[s] < 0 || forced[s] > Va) return -1;
+      if (forced[s] < -1 || forced[s] > Va) return -1;
   double* y = (double*)malloc(sizeof(double) * Dd);
   double* h = (double*)malloc(sizeof(double) * Dd);
   double* qkv = (double*)malloc(sizeof(double) * 3 * Dd);
@@ -534,8 +558,14 @@ int orc_depformer(const orc_model* m, const double* hid, int32_t text_in, const 
   double* hid_r = (double*)malloc(sizeof(double) * D);
   for (int i = 0; i < D; ++i) hid_r[i] = rnd(m, hid[i]);
 
+  int S_run = dep_run(c);
+  for (int s = S_run; s < S; ++s) {
+    if (codes) codes[s] = -1;
+    if (margins) margins[s] = INFINITY;
+    if (logits) memset(logits + (size_t)s * Va, 0, sizeof(double) * Va);
+  }
   int32_t prev = text_in;
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s < S_run; ++s) {
     linear(m, m->dep_in[s], Dd, D, hid_r, y);
     for (int i = 0; i < Dd; ++i) y[i] += wget(m, m->dep_emb[s], (size_t)prev * Dd + i);
     for (int l = 0; l < Ld; ++l) {
@@ -549,9 +579,12 @@ int orc_depformer(const orc_model* m, const double* hid, int32_t text_in, const 
         kr[i] = rnd(m, qkv[Dd + i]);
         vr[i] = rnd(m, qkv[2 * Dd + i]);
       }
+      /* entries first..s; the ring reading masks entry 0 at the last substep */
+      int first = (c->dep_ref_ring && s == S_run - 1) ? 1 : 0;
       for (int hh = 0; hh < Hd; ++hh)
-        orc_attend(qkv + hh * hdd, kc + (size_t)l * S * Dd + hh * hdd,
-                   vc + (size_t)l * S * Dd + hh * hdd, s + 1, hdd, Dd, o + hh * hdd);
+        orc_attend(qkv + hh * hdd, kc + ((size_t)l * S + first) * Dd + hh * hdd,
+                   vc + ((size_t)l * S + first) * Dd + hh * hdd, s + 1 - first, hdd, Dd,
+                   o + hh * hdd);
       for (int i = 0; i < Dd; ++i) o[i] = rnd(m, o[i]);
       linear(m, m->dep_o[wi], Dd, Dd, o, t);
       for (int i = 0; i < Dd; ++i) y[i] += t[i];
@@ -562,14 +595,19 @@ int orc_depformer(const orc_model* m, const double* hid, int32_t text_in, const 
       linear(m, m->dep_down[wi], Dd, Fd, a, t);
       for (int i = 0; i < Dd; ++i) y[i] += t[i];
     }
-    for (int i = 0; i < Dd; ++i) h[i] = rnd(m, y[i]);
+    if (c->dep_final_norm) {
+      rmsnorm_w(m, y, m->dep_out_norm, Dd, h);
+      for (int i = 0; i < Dd; ++i) h[i] = rnd(m, h[i]);
+    } else {
+      for (int i = 0; i < Dd; ++i) h[i] = rnd(m, y[i]);
+    }
     linear(m, m->dep_head[s], Va, Dd, h, lg);
     double mg;
     int32_t code = orc_argmax(lg, Va, &mg);
     if (codes) codes[s] = code;
     if (margins) margins[s] = mg;
     if (logits) memcpy(logits + (size_t)s * Va, lg, sizeof(double) * Va);
-    prev = forced ? forced[s] : code;
+    prev = (forced && forced[s] >= 0) ? forced[s] : code;
   }
   free(y); free(h); free(qkv); free(o); free(t); free(gu); free(a); free(kc); free(vc); free(lg);
   free(hid_r);

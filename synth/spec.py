@@ -36,6 +36,9 @@ class ModelShape:
     norm_eps: float = 1e-8
     dtype: str = "bf16"          # "bf16" or "f32"
     mask_oldest: bool = False    # window reading flag (attend W-1 keys once full)
+    dep_q: int = 0               # depformer substeps run per frame (0 = all)
+    dep_final_norm: bool = False # RMSNorm (gain dep.out_norm) before each depformer head
+    dep_ref_ring: bool = False   # mask substep entry 0 at the last substep run
 
     @property
     def head_dim(self):
@@ -48,6 +51,10 @@ class ModelShape:
     @property
     def n_channels(self):
         return 1 + self.n_substeps
+
+    @property
+    def dep_steps(self):
+        return self.dep_q if 0 < self.dep_q < self.n_substeps else self.n_substeps
 
     @property
     def elem_bytes(self):
@@ -112,6 +119,8 @@ def tensor_list(m: ModelShape):
             t.append((f"dep.{s}.layer.{l}.down", (Dd, Fd), "normal"))
     for s in range(S):
         t.append((f"dep.head.{s}", (Va, Dd), "normal"))
+    if m.dep_final_norm:
+        t.append(("dep.out_norm", (Dd,), "gain"))
     return t
 
 

@@ -121,17 +121,22 @@ def temporal_fullseq(w: Weights, frames, prefill=None):
 
 
 def depformer_fullseq(w: Weights, hidden, text_in, tokens):
-    """Logits [S, Va] of all substeps of one frame, teacher-forced: the input
-    token of substep s is text_in for s = 0 and tokens[s-1] after."""
+    """Logits [S_run, Va] of the substeps run in one frame (S_run = dep_q or
+    all), teacher-forced: the input token of substep s is text_in for s = 0
+    and tokens[s-1] after. The depformer variants of the shape are applied as
+    a mask (ring reading: the last row also excludes column 0) and as a norm
+    on the head input (final-norm reading)."""
     s = w.s
     bf = s.dtype == "bf16"
-    S, Dd, Hd, hdd, Fd = s.n_substeps, s.dep_dim, s.dep_heads, s.dep_head_dim, s.dep_ffn
+    S, Dd, Hd, hdd, Fd = s.dep_steps, s.dep_dim, s.dep_heads, s.dep_head_dim, s.dep_ffn
     hid = bf_round(np.asarray(hidden, np.float64), bf)
     prev = [int(text_in)] + [int(t) for t in tokens[:S - 1]]
     Win = np.stack([w[f"dep.in.{i}"] for i in range(S)])               # [S, Dd, D]
     y = np.einsum("sod,d->so", Win, hid)
     y = y + np.stack([w[f"dep.emb.{i}"][prev[i]] for i in range(S)])
     causal = np.tril(np.ones((S, S), bool))
+    if s.dep_ref_ring:
+        causal[S - 1, 0] = False
     for l in range(s.dep_layers):
         Wqkv = np.stack([w[f"dep.{i}.layer.{l}.qkv"] for i in range(S)])
         Wo = np.stack([w[f"dep.{i}.layer.{l}.o"] for i in range(S)])
@@ -156,4 +161,6 @@ def depformer_fullseq(w: Weights, hidden, text_in, tokens):
         a = bf_round(g / (1.0 + np.exp(-g)) * u, bf)
         y = y + np.einsum("sod,sd->so", Wdn, a)
     Whd = np.stack([w[f"dep.head.{i}"] for i in range(S)])
+    if s.dep_final_norm:
+        y = _rms(y, w["dep.out_norm"], s.norm_eps)
     return np.einsum("sod,sd->so", Whd, bf_round(y, bf))

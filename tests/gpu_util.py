@@ -24,14 +24,16 @@ def log(*a):
 
 
 def cfg_of(shape: spec.ModelShape, B: int):
-    flags = M.MOSHI_FLAG_MASK_OLDEST if shape.mask_oldest else 0
+    flags = (M.MOSHI_FLAG_MASK_OLDEST if shape.mask_oldest else 0) | \
+        (M.MOSHI_FLAG_DEP_FINAL_NORM if shape.dep_final_norm else 0) | \
+        (M.MOSHI_FLAG_DEP_REF_RING if shape.dep_ref_ring else 0)
     return M.make_config(dim=shape.dim, n_layers=shape.n_layers, n_heads=shape.n_heads,
                          ffn_hidden=shape.ffn, window=shape.window, dep_dim=shape.dep_dim,
                          dep_layers=shape.dep_layers, dep_heads=shape.dep_heads,
                          dep_ffn_hidden=shape.dep_ffn, n_substeps=shape.n_substeps,
                          text_vocab=shape.text_vocab, audio_card=shape.audio_card,
                          rope_theta=shape.rope_theta, norm_eps=shape.norm_eps,
-                         dtype=shape.dtype, max_sessions=B, flags=flags)
+                         dtype=shape.dtype, max_sessions=B, flags=flags, dep_q=shape.dep_q)
 
 
 def tolerances(shape):

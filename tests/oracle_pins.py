@@ -240,7 +240,94 @@ def check_sizes():
     assert m.window * gold["frame_ms"]["value"] / 1000 / 60 == gold["window_minutes"]["value"]
 
 
+def check_ring_transfer():
+    """read_ring -> load_ring into a fresh session continues bit-identically
+    (the state transfer the full-size GPU checks rely on): after T frames that
+    wrap the ring, and after a prefill. The bf16 ring is stored as bf16, so the
+    transfer is lossless; the fp32 model's oracle ring holds fp64 values and
+    the transfer rounds them to fp32, so there it is checked to 1e-6 relative."""
+    for dt, W, T, pre in (("f32", 5, 12, 0), ("bf16", 7, 4, 6), ("bf16", 4, 9, 3),
+                          ("bf16", 5, 13, 0)):
+        s = mini(dt, window=W)
+        w, M = _model(s, 51)
+        fr = wl.frames(s, 52, 0, 0, T + 2)
+        a = oracle.Session(M)
+        if pre:
+            k, v = wl.prefill_kv(s, 53, 0, pre)
+            a.prefill(k, v)
+        for t in range(T):
+            a.step(fr[t])
+        rk, rv = a.read_ring()
+        b = oracle.Session(M)
+        b.load_ring(a.info()[0], rk, rv)
+        assert b.info() == a.info(), "ring transfer: bookkeeping"
+        for t in range(T, T + 2):
+            x = a.step(fr[t])
+            y = b.step(fr[t], forced_text=x["text_token"], forced_codes=x["codes"])
+            for key in ("text_logits", "audio_logits", "hidden"):
+                if dt == "bf16":
+                    ok = np.array_equal(x[key], y[key])
+                else:
+                    ok = np.max(np.abs(x[key] - y[key])) < 1e-6 * max(1.0, np.max(np.abs(x[key])))
+                assert ok, f"ring transfer: {key} differs ({dt}, W={W})"
+        # both sessions wrote the same rows since (bf16: lossless transfer)
+        if dt == "bf16":
+            k2, v2 = b.read_ring()
+            k1, v1 = a.read_ring()
+            assert np.array_equal(k2, k1) and np.array_equal(v2, v1), "ring transfer: rows"
+
+
+def check_depformer_variants():
+    """dep_q, the ring reading and the final-norm reading, each against the
+    full-sequence form and an invariant of its own."""
+    base = mini("f32")
+    g = np.random.default_rng(61)
+    hid = g.normal(size=base.dim)
+    forced = g.integers(0, base.audio_card, size=base.n_substeps).astype(np.int32)
+    w0, M0 = _model(base, 62)
+    full = M0.depformer(hid, 9, forced=forced)
+    for shape in (base.replace(dep_q=8), base.replace(dep_ref_ring=True),
+                  base.replace(dep_q=8, dep_ref_ring=True), base.replace(dep_q=2, dep_ref_ring=True),
+                  base.replace(dep_final_norm=True), base.replace(dep_q=5, dep_final_norm=True),
+                  mini("bf16").replace(dep_q=8, dep_ref_ring=True, dep_final_norm=True)):
+        w, M = _model(shape, 62)
+        n = shape.dep_steps
+        out = M.depformer(hid if shape.dtype == "f32" else ref.bf_round(hid), 9, forced=forced)
+        want = ref.depformer_fullseq(ref.Weights(shape, w),
+                                     hid if shape.dtype == "f32" else ref.bf_round(hid), 9, forced)
+        assert np.max(np.abs(out["audio_logits"][:n] - want)) < TOL, f"variant {shape}"
+        assert (out["codes"][n:] == -1).all() and np.isinf(out["audio_margins"][n:]).all(), \
+            "substeps past dep_q must not run"
+        assert np.array_equal(out["codes"][:n], np.argmax(want, axis=1))
+    # dep_q: the substeps that run are those of the full depformer (a prefix)
+    w, M = _model(base.replace(dep_q=5), 62)
+    part = M.depformer(hid, 9, forced=forced)
+    assert np.array_equal(part["audio_logits"][:5], full["audio_logits"][:5]), "dep_q prefix"
+    # ring reading with 2 substeps: substep 1 attends itself only, so substep
+    # 0's attention weights cannot reach it; without the reading they do
+    for ring in (True, False):
+        shp = base.replace(dep_q=2, dep_ref_ring=ring)
+        w, M = _model(shp, 63)
+        a = M.depformer(hid, 9, forced=forced)["audio_logits"][1]
+        names = [t[0] for t in spec.tensor_list(shp)]
+        w2 = [x.copy() for x in w]
+        w2[names.index("dep.0.layer.0.qkv")] *= 3.0
+        b = oracle.Model(shp, w2).depformer(hid, 9, forced=forced)["audio_logits"][1]
+        assert np.array_equal(a, b) == ring, f"ring reading (on={ring}): substep 1 and entry 0"
+    # final norm: doubling its gain doubles every head's logits exactly
+    shp = mini("bf16").replace(dep_final_norm=True)
+    w, M = _model(shp, 64)
+    names = [t[0] for t in spec.tensor_list(shp)]
+    h16 = ref.bf_round(hid)
+    a = M.depformer(h16, 9, forced=forced)
+    w2 = [x.copy() for x in w]
+    gi = names.index("dep.out_norm")
+    w2[gi] = rng.f32_to_bf16(rng.bf16_to_f32(w2[gi]) * 2.0)
+    b = oracle.Model(shp, w2).depformer(h16, 9, forced=forced)
+    assert np.array_equal(b["audio_logits"], 2.0 * a["audio_logits"]), "final norm gain"
+
+
 ALL = [check_bf16_round, check_rmsnorm, check_rope, check_attend, check_silu_argmax,
        check_embedding_onehot, check_ring_window_fp32, check_ring_window_mask_oldest,
        check_incremental_equals_fullseq_bf16, check_depformer_fullseq, check_step_composition,
-       check_sizes]
+       check_sizes, check_ring_transfer, check_depformer_variants]

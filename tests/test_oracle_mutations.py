@@ -43,9 +43,21 @@ MUTATIONS = [
     ("embed_channel_shift", "(size_t)frame[1 + k] * D", "(size_t)frame[k] * D", 0),
     ("final_norm_gain", "rmsnorm_w(m, x, m->out_norm, D, h);",
      "rmsnorm_w(m, x, m->mlp_norm[c->n_layers - 1], D, h);", 0),
-    ("dep_forcing_ignored", "prev = forced ? forced[s] : code;", "prev = code;", 0),
-    ("dep_self_excluded", "vc + (size_t)l * S * Dd + hh * hdd, s + 1, hdd",
-     "vc + (size_t)l * S * Dd + hh * hdd, s > 0 ? s : 1, hdd", 0),
+    ("dep_forcing_ignored", "prev = (forced && forced[s] >= 0) ? forced[s] : code;",
+     "prev = code;", 0),
+    ("dep_self_excluded", "hh * hdd, s + 1 - first, hdd", "hh * hdd, s > first ? s - first : 1, hdd",
+     0),
+    ("dep_q_ignored", "int S_run = dep_run(c);", "int S_run = S;", 0),
+    ("dep_ring_reading_ignored", "int first = (c->dep_ref_ring && s == S_run - 1) ? 1 : 0;",
+     "int first = 0;", 0),
+    ("dep_ring_reading_wrong_step", "int first = (c->dep_ref_ring && s == S_run - 1) ? 1 : 0;",
+     "int first = (c->dep_ref_ring && s == S_run - 2) ? 1 : 0;", 0),
+    ("dep_final_norm_skipped", "if (c->dep_final_norm) {", "if (0) {", 0),
+    ("dep_final_norm_wrong_gain", "rmsnorm_w(m, y, m->dep_out_norm, Dd, h);",
+     "rmsnorm_w(m, y, m->dep_mlp_norm[Ld - 1], Dd, h);", 0),
+    ("load_ring_row_shift", "ring_put(s, s->k_ring, l, j, kv);",
+     "ring_put(s, s->k_ring, l, (j + 1) % W, kv);", 0),
+    ("load_ring_position", "  s->pos = pos;\n", "  s->pos = pos + 1;\n", 0),
     ("dep_inproj_shared", "linear(m, m->dep_in[s], Dd, D, hid_r, y);",
      "linear(m, m->dep_in[0], Dd, D, hid_r, y);", 0),
     ("dep_embedding_shared", "wget(m, m->dep_emb[s], (size_t)prev * Dd + i)",
