@@ -92,3 +92,46 @@ def frames_matrix(shape, B, rows):
     for slot, fr in rows.items():
         f[slot] = fr
     return f
+
+
+class DevBuf:
+    """A device buffer from the HIP runtime libmoshi.so itself uses (loaded
+    through ctypes), for tests of the device-resident entry points. (torch
+    would bring up its own copy of the runtime, which cannot start once
+    libmoshi's has.)"""
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            import ctypes
+            M.lib()  # the runtime libmoshi.so links against is loaded now
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+            h.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+            h.hipFree.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self, host: np.ndarray):
+        import ctypes
+        self.shape, self.dtype = host.shape, host.dtype
+        self.nbytes = host.nbytes
+        p = ctypes.c_void_p()
+        assert self.hip().hipMalloc(ctypes.byref(p), self.nbytes) == 0, "hipMalloc failed"
+        self.ptr = p.value
+        self.write(host)
+
+    def write(self, host):
+        a = np.ascontiguousarray(host, self.dtype)
+        assert self.hip().hipMemcpy(self.ptr, a.ctypes.data, self.nbytes, 1) == 0  # H2D
+
+    def read(self):
+        a = np.empty(self.shape, self.dtype)
+        assert self.hip().hipMemcpy(a.ctypes.data, self.ptr, self.nbytes, 2) == 0  # D2H
+        return a
+
+    def __del__(self):
+        if getattr(self, "ptr", None):
+            self.hip().hipFree(self.ptr)
+            self.ptr = None

@@ -11,7 +11,7 @@ import pytest
 import full_duplex_speech_amd as M
 import oracle
 from synth import spec, workloads as wl
-from gpu_util import Stats, compare_frame, frames_matrix, log, new_engine
+from gpu_util import DevBuf, Stats, compare_frame, frames_matrix, log, new_engine
 
 pytestmark = pytest.mark.gpu
 
@@ -130,17 +130,12 @@ def test_depformer_variants_parity(variant):
     log(f"{variant}: tiny {sa}; ragged {sr}")
 
 
-def _dev(torch, a):
-    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
-
-
 @pytest.mark.parametrize("case", ["tiny_fp32_b1", "ragged_bf16_b3"])
 def test_enqueue_with_churn_matches_step(case):
     """Device-resident steps enqueued back to back while sessions join,
     prefill and leave between them (the metadata of an earlier step must not
     be overwritten before it runs), then one sync: tokens, codes and slot
     bookkeeping equal the same sequence run through moshi_step."""
-    import torch
     if case == "tiny_fp32_b1":
         shape, B = spec.TINY, 1
         plan = [("join", 0), ("step",), ("step",), ("leave", 0), ("step",), ("join", 1),
@@ -151,43 +146,53 @@ def test_enqueue_with_churn_matches_step(case):
                 ("step",), ("leave", 0), ("step",), ("join", 3), ("step",), ("leave", 2),
                 ("prefill", 1, 3), ("step",)]
     weights = wl.make_weights(shape, 77, gains="random")
+    # the frames of every step, from the plan (joins take the lowest free slot)
+    step_frames, slot_of, t_of = [], {}, {}
+    for act in plan:
+        if act[0] == "join":
+            slot_of[act[1]] = min(set(range(B)) - set(slot_of.values()))
+            t_of[act[1]] = 0
+        elif act[0] == "leave":
+            slot_of.pop(act[1])
+        elif act[0] == "step":
+            step_frames.append(frames_matrix(shape, B, {
+                s: wl.frames(shape, 9, sid, t_of[sid], 1)[0] for sid, s in slot_of.items()}))
+            for sid in slot_of:
+                t_of[sid] += 1
+    # every device buffer is ready before the first enqueue (no allocation or
+    # copy between enqueued steps that could wait for them to finish)
+    dev = [(DevBuf(fr), DevBuf(np.full(B, -7, np.int32)),
+            DevBuf(np.full((B, shape.n_substeps), -7, np.int32))) for fr in step_frames]
     results = []
     for mode in ("enqueue", "sync"):
         ctx = new_engine(shape, weights, B)
-        slot_of, t_of, outs, infos = {}, {}, [], []
-        dev_bufs = []
+        slot_of, outs, infos, k = {}, [], [], 0
+        frames_of_step = []
         for act in plan:
             if act[0] == "join":
                 slot_of[act[1]] = M.moshi_session_join(ctx)
-                t_of[act[1]] = 0
             elif act[0] == "leave":
                 M.moshi_session_leave(ctx, slot_of.pop(act[1]))
             elif act[0] == "prefill":
-                k, v = wl.prefill_kv(shape, 5, act[1], act[2])
-                M.moshi_session_prefill_kv(ctx, slot_of[act[1]], k, v)
+                kk, vv = wl.prefill_kv(shape, 5, act[1], act[2])
+                M.moshi_session_prefill_kv(ctx, slot_of[act[1]], kk, vv)
             else:
-                fr = frames_matrix(shape, B, {s: wl.frames(shape, 9, sid, t_of[sid], 1)[0]
-                                              for sid, s in slot_of.items()})
-                for sid in slot_of:
-                    t_of[sid] += 1
+                fr = step_frames[k]
+                frames_of_step.append(fr)
                 if mode == "sync":
                     tok, codes = M.moshi_step(ctx, fr)
                     outs.append((tok.copy(), codes.copy()))
                 else:
-                    d_fr = _dev(torch, fr)
-                    d_tok = torch.full((B,), -7, dtype=torch.int32, device="cuda")
-                    d_codes = torch.full((B, shape.n_substeps), -7, dtype=torch.int32, device="cuda")
-                    torch.cuda.synchronize()
-                    M.moshi_step_enqueue(ctx, d_fr.data_ptr(), d_tok.data_ptr(), d_codes.data_ptr())
-                    dev_bufs.append((d_fr, d_tok, d_codes))
+                    d_fr, d_tok, d_codes = dev[k]
+                    M.moshi_step_enqueue(ctx, d_fr.ptr, d_tok.ptr, d_codes.ptr)
+                k += 1
                 infos.append({sid: M.moshi_session_info(ctx, s) for sid, s in slot_of.items()})
         if mode == "enqueue":
             M.moshi_sync(ctx)
-            torch.cuda.synchronize()
-            outs = [(t.cpu().numpy(), c.cpu().numpy()) for _, t, c in dev_bufs]
-        results.append((outs, infos))
+            outs = [(t.read(), c.read()) for _, t, c in dev]
+        results.append((outs, infos, frames_of_step))
         M.moshi_destroy(ctx)
-    (oe, ie), (os_, is_) = results
+    (oe, ie, _), (os_, is_, _) = results
     assert ie == is_
     for i, ((t1, c1), (t2, c2)) in enumerate(zip(oe, os_)):
         assert np.array_equal(t1, t2) and np.array_equal(c1, c2), f"{case}: step {i} differs"
