@@ -26,7 +26,7 @@ _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmoshi.so")
 _CSRC = os.path.join(_HERE, "csrc")
 _SOURCES = [os.path.join(_CSRC, "kernels.hip"), os.path.join(_CSRC, "step.hip"),
-            os.path.join(_CSRC, "engine.cpp")]
+            os.path.join(_CSRC, "static_step.hip"), os.path.join(_CSRC, "engine.cpp")]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                # no packed-fp32 instructions in any kernel
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -93,6 +93,7 @@ def lib():
             "moshi_test_set_spin_limit": ([vp, i32], ctypes.c_int),
             "moshi_temporal_step": ([vp, vp, vp], ctypes.c_int),
             "moshi_step_enqueue": ([vp, vp, vp, vp], ctypes.c_int),
+            "moshi_step_enqueue_noalloc": ([vp, vp, vp, vp], ctypes.c_int),
             "moshi_sync": ([vp], ctypes.c_int),
             "moshi_depformer_step": ([vp, vp, vp, vp], ctypes.c_int),
             "moshi_session_prefill_kv": ([vp, i32, i32, vp, vp], ctypes.c_int),
@@ -243,6 +244,16 @@ def moshi_step_enqueue(ctx: Ctx, d_frames: int, d_text_token: int = None,
         if p is not None and not isinstance(p, int):
             raise TypeError("device addresses must be ints")
     _check(lib().moshi_step_enqueue(ctx.h, d_frames, d_text_token, d_audio_codes), ctx)
+
+
+def moshi_step_enqueue_noalloc(ctx: Ctx, d_frames: int, d_text_token: int = None,
+                               d_audio_codes: int = None):
+    """moshi_step_enqueue whose kernel scratch is the library's static device
+    array (allocates nothing); device addresses as ints."""
+    for p in (d_frames, d_text_token, d_audio_codes):
+        if p is not None and not isinstance(p, int):
+            raise TypeError("device addresses must be ints")
+    _check(lib().moshi_step_enqueue_noalloc(ctx.h, d_frames, d_text_token, d_audio_codes), ctx)
 
 
 def moshi_sync(ctx: Ctx):

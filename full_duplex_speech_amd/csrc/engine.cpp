@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "../../include/moshi.h"
+#include "engine_internal.h"
 #include "host.h"
 #include "kernels.h"
 
@@ -134,6 +135,10 @@ struct moshi_ctx {
   int step_parity = 0;
   uint32_t step_seq = 0;  // sequence number of the last step kernel launch
   StepArgs step_host{};   // host copy of *d_step
+  // the same step with its synchronisation scratch in the static scratch of
+  // static_step.hip (moshi_step_enqueue_noalloc); null when it does not fit
+  StepArgs* d_step_static = nullptr;
+  std::string static_why;  // why there is no static variant
 
   // kernel timing (eager launches bracketed by events); `dry` only records
   // the (class, bytes) sequence of a step without launching anything
@@ -639,12 +644,6 @@ int setup_step(moshi_ctx* c) {
   A.pos = c->d_pos; A.live = c->d_live;
   CKD(c, dalloc(c, (void**)&c->d_bar, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
   CKD(c, dalloc(c, (void**)&c->d_abort, sizeof(int)));
-  // attention tickets, two sets (launch parity): temporal heads, then depformer heads
-  void* tickets = nullptr;
-  const size_t n_tickets = 2 * (size_t)(c->H + c->Hd) * 16;
-  CKD(c, dalloc(c, &tickets, n_tickets * sizeof(unsigned)));
-  CKD(c, hipMemset(tickets, 0, n_tickets * sizeof(unsigned)));
-  A.attn_ctr = (unsigned*)tickets;
   CKD(c, hipMemset(c->d_bar, 0, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
   CKD(c, hipMemset(c->d_abort, 0, sizeof(int)));
   A.bar = c->d_bar; A.abort = c->d_abort;
@@ -659,6 +658,31 @@ int setup_step(moshi_ctx* c) {
   CKD(c, dalloc(c, (void**)&c->d_step, sizeof(StepArgs)));
   CKD(c, hipMemcpy(c->d_step, &A, sizeof(StepArgs), hipMemcpyHostToDevice));
   c->step_host = A;
+  {
+    // the allocation-free variant: barrier counters at the start of the
+    // static scratch, the flagged arena after them; the abort flag stays the
+    // context's (it reports back to this context's host calls)
+    size_t sbytes = 0;
+    void* sp = moshi_internal::static_scratch_setup(c->device, &sbytes);
+    const size_t bar_bytes = 2 * (size_t)STEP_BAR_WORDS * sizeof(unsigned);
+    const size_t arena_off = (bar_bytes + 65535) / 65536 * 65536;
+    const size_t ll_bytes =
+        (size_t)step_ll_words(c->S, c->Ld, c->Dd, c->Fd, c->Va, c->L, c->H, c->hd, c->max_spans,
+                              c->D) *
+        sizeof(uint64_t);
+    if (sp == nullptr) {
+      c->static_why = "the static scratch's address could not be found on this device";
+    } else if (arena_off + ll_bytes > sbytes) {
+      c->static_why = "this model's step needs " + std::to_string(arena_off + ll_bytes) +
+                      " bytes of scratch; the static scratch holds " + std::to_string(sbytes);
+    } else {
+      StepArgs As = A;
+      As.bar = (unsigned*)sp;
+      As.ll = (uint64_t*)((char*)sp + arena_off);
+      CKD(c, dalloc(c, (void**)&c->d_step_static, sizeof(StepArgs)));
+      CKD(c, hipMemcpy(c->d_step_static, &As, sizeof(StepArgs), hipMemcpyHostToDevice));
+    }
+  }
   c->step_grid = step_max_grid(c->dtype, c->hd, c->hdd, lds);  // with the final LDS size
   if (c->step_grid != grid) return MOSHI_OK;  // the staged slices are sized for `grid`
   c->step_lds = lds;
@@ -1419,3 +1443,28 @@ int moshi_time_kernels(moshi_ctx* c, const int32_t* frames, int32_t n_steps, dou
 }
 
 }  // extern "C"
+
+int moshi_internal::ctx_device(const moshi_ctx* c) { return c ? c->device : -1; }
+
+int moshi_internal::enqueue_static(moshi_ctx* c, const int32_t* d_frames, int32_t* d_text_token,
+                                   int32_t* d_audio_codes, uint32_t seq) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!d_frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
+  if (!c->persistent)
+    return fail(c, MOSHI_E_INVALID, "the allocation-free step needs the one-session step kernel");
+  if (!c->d_step_static) return fail(c, MOSHI_E_INVALID, c->static_why);
+  if ((rc = upload_forced(c, nullptr))) return rc;
+  if ((rc = upload_meta(c))) return rc;
+  int* tok = d_text_token ? d_text_token : c->tokens;
+  int* codes = d_audio_codes ? d_audio_codes : c->codes;
+  if (live_count(c) > 0) {
+    CKD(c, launch_step(c->dtype, c->hd, c->hdd, c->d_step_static, d_frames, tok, codes,
+                       (int)(seq & 1u), seq, c->step_grid, c->step_lds, c->stream, nullptr));
+  } else {
+    // no live session: every output reads -1 (a fill kernel, no memset)
+    CKD(c, launch_finish_outputs(tok, codes, c->d_live, c->B, c->S, c->S_run, c->stream));
+  }
+  c->slots.advance();
+  return MOSHI_OK;
+}

@@ -181,7 +181,6 @@ struct StepArgs {
   int wbuf_lds;
   int o_tw, o_dw, o_dn, o_de, o_dh;
   unsigned* bar;               // 2 sets of STEP_BAR_WORDS barrier counters
-  unsigned* attn_ctr;          // 2 sets of H * 16 per-head attention tickets
   int* abort;                  // set when a barrier or flag wait times out
   // flagged vectors the depformer operations hand on (step.hip); zeroed at
   // creation, step_ll_words() words of 8 bytes

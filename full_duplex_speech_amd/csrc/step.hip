@@ -155,8 +155,8 @@ __device__ __forceinline__ bool grid_sync(Grid& g) {
 // Start of a launch: clear the other counter set (used by the next launch;
 // the previous launch, which used it, has finished), count the workgroups of
 // every XCD, and wait for all of them (flat barrier).
-__device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn_ctr, int n_heads,
-                                          int parity, int* abort, int limit, uint64_t* trace) {
+__device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, int parity, int* abort, int limit,
+                                          uint64_t* trace) {
   __shared__ int s_leave;
   __shared__ unsigned s_cnt[MAX_XCC];
   g.set = bar + parity * STEP_BAR_WORDS;
@@ -177,10 +177,6 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, unsigned* attn
       __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_GLOBAL, 0u, MOSHI_RLX, MOSHI_AGT);
     }
   }
-  if (blockIdx.x == 0)
-    for (int h = threadIdx.x; h < n_heads; h += NT)
-      __hip_atomic_store((MOSHI_GLB unsigned*)attn_ctr + ((parity ^ 1) * n_heads + h) * 16, 0u,
-                         MOSHI_RLX, MOSHI_AGT);
   drain_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -1012,11 +1008,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
             o_dh = uni(A.o_dh);
   const int64_t t_lel = uni(A.t_layer_elems), d_lel = uni(A.d_layer_elems);
   Grid g;
-  // attention tickets of this launch: temporal heads, then depformer heads
-  if (grid_init(g, uni(A.bar), uni(A.attn_ctr), H + Hd, parity, uni(A.abort), uni(A.spin_limit),
-                trace))
-    return;
-  unsigned* const tickets = uni(A.attn_ctr) + (size_t)parity * (H + Hd) * 16;
+  if (grid_init(g, uni(A.bar), parity, uni(A.abort), uni(A.spin_limit), trace)) return;
   // first weight batch of the next projection, requested before each barrier
   u32x4 pf[GU][16 / KW];
   unsigned char* const wbuf = s_dyn + uni(A.wbuf_lds);

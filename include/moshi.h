@@ -176,6 +176,22 @@ int moshi_step_forced(moshi_ctx* ctx, const int32_t* frames, const int32_t* forc
 int moshi_step_enqueue(moshi_ctx* ctx, const int32_t* d_frames, int32_t* d_text_token,
                        int32_t* d_audio_codes);
 
+/* moshi_step_enqueue for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * one-session step kernel and results, with its synchronisation scratch --
+ * grid-barrier counters and the flagged hand-off arena -- in a static device
+ * array of the library (40 MiB per GPU, held until the process ends) instead
+ * of the context's buffers. The call allocates nothing.
+ * Only for contexts that use the step kernel (moshi_uses_step_kernel == 1)
+ * whose scratch fits the array (the PersonaPlex shape needs 29.7 MB);
+ * otherwise MOSHI_E_INVALID with the sizes in moshi_last_error. Calls that
+ * overlap on one GPU (other streams or threads using this entry point at the
+ * same time) race: serialise them. Arguments, outputs and errors as for
+ * moshi_step_enqueue; moshi_sync waits for it. A join, leave or prefill since
+ * the last step enqueues one small host-to-device copy of the slot table. */
+int moshi_step_enqueue_noalloc(moshi_ctx* ctx, const int32_t* d_frames, int32_t* d_text_token,
+                               int32_t* d_audio_codes);
+
 /* Waits for every enqueued step. MOSHI_E_INVALID if a clamped code was seen
  * since the last call (the flag is then cleared); MOSHI_E_DEVICE if a step
  * kernel gave up waiting (the context is then unusable). */
