@@ -26,7 +26,8 @@ _ROOT = os.path.dirname(_HERE)
 LIB_PATH = os.path.join(_HERE, "libmoshi.so")
 _CSRC = os.path.join(_HERE, "csrc")
 _SOURCES = [os.path.join(_CSRC, "kernels.hip"), os.path.join(_CSRC, "step.hip"),
-            os.path.join(_CSRC, "static_step.hip"), os.path.join(_CSRC, "engine.cpp")]
+            os.path.join(_CSRC, "static_step.hip"), os.path.join(_CSRC, "engine.cpp"),
+            os.path.join(_CSRC, "stream.cpp")]
 HIPCC_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
                # no packed-fp32 instructions in any kernel
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -86,6 +87,12 @@ def lib():
             "moshi_n_tensors": ([cfgp], i32),
             "moshi_create": ([cfgp, vp, i32, vp, ctypes.POINTER(vp)], ctypes.c_int),
             "moshi_destroy": ([vp], ctypes.c_int),
+            "moshi_get_config": ([vp, cfgp], ctypes.c_int),
+            "moshi_stream_create": ([vp, i32, vp, ctypes.POINTER(vp)], ctypes.c_int),
+            "moshi_stream_destroy": ([vp], ctypes.c_int),
+            "moshi_stream_reset": ([vp, i32], ctypes.c_int),
+            "moshi_stream_step": ([vp, vp, vp, vp, vp, vp, vp], ctypes.c_int),
+            "moshi_stream_last_error": ([vp], ctypes.c_char_p),
             "moshi_session_join": ([vp, ctypes.POINTER(i32)], ctypes.c_int),
             "moshi_session_leave": ([vp, i32], ctypes.c_int),
             "moshi_step": ([vp, vp, vp, vp], ctypes.c_int),
@@ -341,3 +348,60 @@ def moshi_time_kernels(ctx: Ctx, frames, n_steps: int, n_classes: int = 32):
 
 def moshi_last_error(ctx: Ctx) -> str:
     return lib().moshi_last_error(ctx.h).decode()
+
+
+class Stream:
+    """Owning handle of a moshi_stream (the delayed-stream wrapper)."""
+
+    def __init__(self, h, ctx, n_agent):
+        self.h = h
+        self.ctx = ctx
+        self.A = n_agent
+
+    def __del__(self):
+        if getattr(self, "h", None) and _lib is not None:
+            _lib.moshi_stream_destroy(self.h)
+            self.h = None
+
+
+def _check_stream(status, st):
+    if status < 0:
+        raise MoshiError(status, lib().moshi_stream_last_error(st.h).decode())
+    return status
+
+
+def moshi_get_config(ctx: Ctx) -> moshi_config:
+    c = moshi_config()
+    _check(lib().moshi_get_config(ctx.h, ctypes.byref(c)), ctx)
+    return c
+
+
+def moshi_stream_create(ctx: Ctx, n_agent: int, delays=None) -> Stream:
+    d = None if delays is None else np.ascontiguousarray(delays, np.int32)
+    out = ctypes.c_void_p()
+    _check(lib().moshi_stream_create(ctx.h, int(n_agent), _p(d), ctypes.byref(out)), ctx)
+    return Stream(out.value, ctx, n_agent)
+
+
+def moshi_stream_destroy(st: Stream):
+    if st.h:
+        lib().moshi_stream_destroy(st.h)
+        st.h = None
+
+
+def moshi_stream_reset(st: Stream, slot: int):
+    _check_stream(lib().moshi_stream_reset(st.h, int(slot)), st)
+
+
+def moshi_stream_step(st: Stream, user, forced=None):
+    """user int32 [B, S-A]; forced int32 [B, 1+A] or None -> (frames [B, 1+A],
+    ready [B], step_text [B], step_codes [B, S])."""
+    B, S, A = st.ctx.B, st.ctx.S, st.A
+    u = np.ascontiguousarray(user, np.int32).reshape(B, S - A)
+    f = None if forced is None else np.ascontiguousarray(forced, np.int32).reshape(B, 1 + A)
+    fr = np.empty((B, 1 + A), np.int32)
+    ready = np.empty(B, np.int32)
+    tt = np.empty(B, np.int32)
+    tc = np.empty((B, S), np.int32)
+    _check_stream(lib().moshi_stream_step(st.h, _p(u), _p(f), _p(fr), _p(ready), _p(tt), _p(tc)), st)
+    return fr, ready, tt, tc

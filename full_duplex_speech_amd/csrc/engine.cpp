@@ -1184,6 +1184,12 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
   return MOSHI_OK;
 }
 
+int moshi_get_config(const moshi_ctx* ctx, moshi_config* out) {
+  if (!ctx || !out) return MOSHI_E_INVALID;
+  *out = ctx->c;
+  return MOSHI_OK;
+}
+
 int moshi_destroy(moshi_ctx* ctx) {
   release(ctx);
   return MOSHI_OK;

@@ -122,6 +122,9 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
  * waited for first). NULL is accepted. */
 int moshi_destroy(moshi_ctx* ctx);
 
+/* The config a context was created with (*out; MOSHI_E_INVALID on NULL). */
+int moshi_get_config(const moshi_ctx* ctx, moshi_config* out);
+
 /* Opens a session in the lowest free slot: position 0, empty window
  * (recipe "When to use this recipe": sessions join on any tick; "Notes": a
  * recycled slot behaves exactly like a fresh engine).
@@ -196,6 +199,56 @@ int moshi_step_enqueue_noalloc(moshi_ctx* ctx, const int32_t* d_frames, int32_t*
  * since the last call (the flag is then cleared); MOSHI_E_DEVICE if a step
  * kernel gave up waiting (the context is then unusable). */
 int moshi_sync(moshi_ctx* ctx);
+
+/* ---- delayed-stream wrapper (host-side, over moshi_step_forced) ----
+ * The user contract of the pages' runtime (mobius PR #368, "P3 - ONNX
+ * Runtime example": the port of Kyutai's LMGen.step keeps a ring cache with
+ * per-codebook delays [0,0,1,1,1,1,1,1,1,0,1,1,1,1,1,1,1] and collects the
+ * delayed outputs; the persona/voice commit teacher-forces the agent audio
+ * (codebooks 1..8) and the text stream to prime a conversation).
+ * Channels: 0 text, 1..A the agent's codebooks (the depformer's first A
+ * substeps), A+1..S the user's. Channel k of stream column c carries its
+ * token of acoustic frame c - d_k, the initial token (row Vt of the text
+ * table, row card of an audio table) where c - d_k < 0. Step t feeds column
+ * t to moshi_step_forced, writes the generated text and agent codes into
+ * column t+1 (column 0 of those channels is initial), and puts the user's
+ * frame t into column t + d_k. After step t the acoustic frame
+ * t + 1 - max(d) is complete and is returned when it is >= 1: with delays of
+ * at most 1, n steps return n - 1 frames. The object is host memory; the
+ * caller owns it and must not use it with other threads at the same time. */
+typedef struct moshi_stream moshi_stream;
+
+/* A wrapper over every slot of `ctx` (the context must outlive it).
+ * n_agent = A, 1 <= A < n_substeps, A <= the substeps run (dep_q).
+ * delays [1+S] (each 0..8) or NULL for the pages' pattern: 0 for the text,
+ * and in each half of the audio channels 0 for the first codebook and 1 for
+ * the others. MOSHI_E_INVALID on bad arguments. */
+int moshi_stream_create(moshi_ctx* ctx, int32_t n_agent, const int32_t* delays,
+                        moshi_stream** out);
+int moshi_stream_destroy(moshi_stream* s);
+
+/* Starts the stream of a live slot afresh (call after moshi_session_join,
+ * and after moshi_session_prefill_kv if the session is primed from K/V).
+ * MOSHI_E_NOSESSION if the slot is not live. */
+int moshi_stream_reset(moshi_stream* s, int32_t slot);
+
+/* One step of every live slot of the context.
+ * user [B, S-A]: the user's codes of this acoustic frame, each in [0, card).
+ * forced [B, 1+A] or NULL: what this step generates for column t+1, -1 = the
+ *   model's own choice: [0] the text token (in [0, Vt); also depformer
+ *   substep 0's input), [k] agent codebook k (in [0, card); substep k's input).
+ * out_frames [B, 1+A]: the completed acoustic frame (text, agent codes) of
+ *   slots whose out_ready [B] is 1; -1 elsewhere.
+ * step_text [B], step_codes [B, S] (either may be NULL): the step's raw
+ *   tokens (the user channels' substeps included; -1 past dep_q).
+ * A live slot that was not reset since it joined (or that another caller
+ * stepped) -> MOSHI_E_INVALID, nothing changes; see moshi_stream_last_error. */
+int moshi_stream_step(moshi_stream* s, const int32_t* user, const int32_t* forced,
+                      int32_t* out_frames, int32_t* out_ready, int32_t* step_text,
+                      int32_t* step_codes);
+
+/* Detail of the last error of a wrapper (never NULL). */
+const char* moshi_stream_last_error(const moshi_stream* s);
 
 /* ---- test and benchmark hooks (same kernels as moshi_step) ---- */
 
