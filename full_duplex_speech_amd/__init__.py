@@ -39,6 +39,7 @@ MOSHI_F32, MOSHI_BF16 = 0, 1
 MOSHI_FLAG_MASK_OLDEST = 1
 MOSHI_FLAG_DEP_FINAL_NORM = 2
 MOSHI_FLAG_DEP_REF_RING = 4
+MOSHI_FLAG_SAMPLING = 8
 
 _lib = None
 _live_ctx = weakref.WeakSet()
@@ -74,6 +75,12 @@ class moshi_config(ctypes.Structure):
         ("dep_q", ctypes.c_int32)]
 
 
+class moshi_sampling(ctypes.Structure):
+    _fields_ = [("text_temperature", ctypes.c_double), ("text_top_k", ctypes.c_int32),
+                ("audio_temperature", ctypes.c_double), ("audio_top_k", ctypes.c_int32),
+                ("seed", ctypes.c_uint64)]
+
+
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
@@ -95,6 +102,7 @@ def lib():
             "moshi_stream_last_error": ([vp], ctypes.c_char_p),
             "moshi_session_join": ([vp, ctypes.POINTER(i32)], ctypes.c_int),
             "moshi_session_leave": ([vp, i32], ctypes.c_int),
+            "moshi_session_set_sampling": ([vp, i32, ctypes.POINTER(moshi_sampling)], ctypes.c_int),
             "moshi_step": ([vp, vp, vp, vp], ctypes.c_int),
             "moshi_step_forced": ([vp, vp, vp, vp, vp], ctypes.c_int),
             "moshi_test_set_spin_limit": ([vp, i32], ctypes.c_int),
@@ -217,6 +225,17 @@ def moshi_session_join(ctx: Ctx) -> int:
 
 def moshi_session_leave(ctx: Ctx, slot: int):
     _check(lib().moshi_session_leave(ctx.h, int(slot)), ctx)
+
+
+def moshi_session_set_sampling(ctx: Ctx, slot: int, text_temperature=0.0, text_top_k=0,
+                               audio_temperature=0.0, audio_top_k=0, seed=0, greedy=False):
+    """Temperature + top-k draws for one session (greedy=True: back to greedy)."""
+    if greedy:
+        _check(lib().moshi_session_set_sampling(ctx.h, int(slot), None), ctx)
+        return
+    p = moshi_sampling(float(text_temperature), int(text_top_k), float(audio_temperature),
+                       int(audio_top_k), int(seed) & (2**64 - 1))
+    _check(lib().moshi_session_set_sampling(ctx.h, int(slot), ctypes.byref(p)), ctx)
 
 
 def moshi_step(ctx: Ctx, frames):

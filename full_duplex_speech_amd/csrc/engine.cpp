@@ -48,13 +48,14 @@ enum KClass {
   KC_D_HEAD,
   KC_T_COMBINE,
   KC_ARGMAX,
+  KC_SAMPLE,
   KC_COUNT
 };
 const char* kClassNames[KC_COUNT] = {
     "embed",      "temporal_qkv",  "temporal_attn", "temporal_o",    "temporal_gateup",
     "temporal_down", "text_head",  "dep_inproj",    "dep_entry",     "dep_qkv",
     "dep_attn",   "dep_o",         "dep_gateup",    "dep_down",      "dep_head",
-    "temporal_attn_combine", "argmax_reduce"};
+    "temporal_attn_combine", "argmax_reduce", "sample"};
 
 int32_t tensor_count(const moshi_config* c) { return moshi_host::tensor_count(c); }
 const char* config_error(const moshi_config* c) { return moshi_host::config_error(c); }
@@ -99,6 +100,8 @@ struct moshi_ctx {
   int64_t* d_pos = nullptr;
   int* d_err = nullptr;  // set by the embedding when a live code was out of range
   int* d_forced = nullptr;  // [B][1+S] forced text / codes, -1 = not forced
+  SampleParams* d_samp = nullptr;  // [B] sampling parameters (MOSHI_FLAG_SAMPLING)
+  bool sampling = false;
   double *d_inv_freq = nullptr;
   void* staging = nullptr;  // one layer of prefill K or V
   int max_spans = 0;  // temporal attention spans per (slot, head)
@@ -113,6 +116,9 @@ struct moshi_ctx {
   int64_t* h_pos = nullptr;
   int* h_forced = nullptr;
   bool forced_on_device = false;  // d_forced holds a forced step's values
+  std::vector<SampleParams> samp;  // per slot
+  bool samp_dirty = false;
+  SampleParams* h_samp = nullptr;  // pinned staging
   // recorded after the last copy out of h_live / h_pos / h_forced: those
   // pinned buffers are rewritten only once it has completed, so a step
   // enqueued earlier still reads its own metadata
@@ -383,6 +389,19 @@ GemmArgs d_head_args(const moshi_ctx* c, int s) {
   return a;
 }
 
+// Draws of head `stream` (0 text, 1 + s substep s) for the sessions that
+// sample; the others keep the argmax (or forced token) already in `out`.
+SampleArgs sample_args(const moshi_ctx* c, const float* logits, int ld, int n, int which, int stream,
+                       int pos_off, int* out, int out_stride, int forced_col) {
+  SampleArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logits = logits; a.ld = ld; a.n = n; a.params = c->d_samp; a.which = which;
+  a.stream = stream; a.pos = c->d_pos; a.pos_off = pos_off; a.live = c->d_live;
+  a.forced = c->d_forced; a.forced_stride = c->NCH; a.forced_col = forced_col;
+  a.out = out; a.out_stride = out_stride; a.B = c->B;
+  return a;
+}
+
 // ---- the temporal step: embed, L layers, final norm + text head ----
 
 hipError_t enqueue_temporal(moshi_ctx* c) {
@@ -446,6 +465,11 @@ hipError_t enqueue_temporal(moshi_ctx* c) {
                                   c->NCH, 0, c->stream);
     });
     if (e != hipSuccess) return e;
+    if (c->sampling) {  // sessions that sample replace the argmax by a draw
+      const SampleArgs sa = sample_args(c, c->text_logits, c->Vt, c->Vt, 0, 0, 0, c->tokens, 1, 0);
+      e = run(c, KC_SAMPLE, 0.0, [&] { return launch_sample(sa, c->stream); });
+      if (e != hipSuccess) return e;
+    }
   }
   return c->dry ? hipSuccess : launch_advance(c->d_pos, c->d_live, B, c->stream);
 }
@@ -470,9 +494,12 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
       memset(&a, 0, sizeof(a));
       a.pre = c->pre; a.ldpre = S * Dd; a.s = s; a.table = c->dep_emb[s];
       a.prev = s == 0 ? c->tokens : c->codes + (s - 1); a.prev_stride = s == 0 ? 1 : S;
-      a.prev_part = s == 0 ? nullptr : c->apart; a.prev_tiles = (c->Va + 15) / 16;
+      // with sampling every code is settled (argmax, draw or forced) right
+      // after its head; otherwise the entry reduces the previous head's
+      // partials itself
+      a.prev_part = (s == 0 || c->sampling) ? nullptr : c->apart; a.prev_tiles = (c->Va + 15) / 16;
       a.prev_n = c->Va; a.D = Dd; a.B = B; a.y = c->y; a.ssq_out = c->ssq_d;
-      if (s > 0) {
+      if (s > 0 && !c->sampling) {
         a.forced = c->d_forced; a.forced_stride = c->NCH; a.forced_col = s;
       }
       a.ssq_rows = ssq_rows(c);
@@ -518,6 +545,19 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
               [&] { return gemm(c, pro, EPI_ARGMAX, a); });
       if (e != hipSuccess) return e;
     }
+    if (c->sampling && s + 1 < c->S_run) {
+      // code s now: argmax or forced, then the draws (the last code below)
+      e = run(c, KC_ARGMAX, 0.0, [&] {
+        return launch_argmax_reduce(c->apart, (c->Va + 15) / 16, c->Va, B, c->codes + s, S,
+                                    c->d_forced, c->NCH, s + 1, c->stream);
+      });
+      if (e != hipSuccess) return e;
+      // the temporal step advanced the positions: this frame's is pos - 1
+      const SampleArgs sa = sample_args(c, c->audio_logits + (size_t)s * c->Va, S * c->Va, c->Va, 1,
+                                        1 + s, -1, c->codes + s, S, s + 1);
+      e = run(c, KC_SAMPLE, 0.0, [&] { return launch_sample(sa, c->stream); });
+      if (e != hipSuccess) return e;
+    }
   }
   // the last substep's code (earlier ones are stored by the next entry)
   const int sl = c->S_run - 1;
@@ -526,6 +566,12 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
                                 c->d_forced, c->NCH, sl + 1, c->stream);
   });
   if (e != hipSuccess) return e;
+  if (c->sampling) {
+    const SampleArgs sa = sample_args(c, c->audio_logits + (size_t)sl * c->Va, S * c->Va, c->Va, 1,
+                                      1 + sl, -1, c->codes + sl, S, sl + 1);
+    e = run(c, KC_SAMPLE, 0.0, [&] { return launch_sample(sa, c->stream); });
+    if (e != hipSuccess) return e;
+  }
   // free slots and substeps not run read -1
   return run(c, KC_ARGMAX, 0.0, [&] {
     return launch_finish_outputs(c->tokens, c->codes, c->d_live, B, S, c->S_run, c->stream);
@@ -540,7 +586,7 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
 int setup_step(moshi_ctx* c) {
   const char* env = getenv("MOSHI_STEP_KERNEL");
   if (c->B != 1 || (env && env[0] == '0') || !step_supported(c->dtype, c->hd, c->hdd) ||
-      c->S > DEP_MAX_KEYS_HOST)
+      c->S > DEP_MAX_KEYS_HOST || c->sampling)
     return MOSHI_OK;
   // the flagged depformer inputs: a normed input pair per thread, at most 4
   // two-value lines per thread for a model-dtype input, whole lines
@@ -775,16 +821,24 @@ int record_meta(moshi_ctx* c) {
 // prefill (the step advances the device positions itself). Stream-ordered:
 // steps enqueued before keep the metadata they were enqueued with.
 int upload_meta(moshi_ctx* c) {
-  if (!c->slots.dirty) return MOSHI_OK;
+  if (!c->slots.dirty && !c->samp_dirty) return MOSHI_OK;
   int rc = wait_meta(c);
   if (rc) return rc;
-  for (int b = 0; b < c->B; ++b) {
-    c->h_live[b] = c->slots.live[b];
-    c->h_pos[b] = c->slots.pos[b];
+  if (c->slots.dirty) {
+    for (int b = 0; b < c->B; ++b) {
+      c->h_live[b] = c->slots.live[b];
+      c->h_pos[b] = c->slots.pos[b];
+    }
+    CKD(c, hipMemcpyAsync(c->d_live, c->h_live, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
+    CKD(c, hipMemcpyAsync(c->d_pos, c->h_pos, sizeof(int64_t) * c->B, hipMemcpyHostToDevice, c->stream));
+    c->slots.dirty = false;
   }
-  CKD(c, hipMemcpyAsync(c->d_live, c->h_live, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
-  CKD(c, hipMemcpyAsync(c->d_pos, c->h_pos, sizeof(int64_t) * c->B, hipMemcpyHostToDevice, c->stream));
-  c->slots.dirty = false;
+  if (c->samp_dirty) {
+    for (int b = 0; b < c->B; ++b) c->h_samp[b] = c->samp[b];
+    CKD(c, hipMemcpyAsync(c->d_samp, c->h_samp, sizeof(SampleParams) * c->B, hipMemcpyHostToDevice,
+                          c->stream));
+    c->samp_dirty = false;
+  }
   return record_meta(c);
 }
 
@@ -975,6 +1029,7 @@ int alloc_buffers(moshi_ctx* c) {
       {(void**)&c->d_pos, B * 8},
       {(void**)&c->d_err, 4},
       {(void**)&c->d_forced, B * c->NCH * 4},
+      {(void**)&c->d_samp, B * sizeof(SampleParams)},
       {(void**)&c->d_inv_freq, (size_t)(c->hd / 2) * 8},
       {&c->staging, (size_t)c->W * D * es},
   };
@@ -1001,6 +1056,7 @@ int alloc_buffers(moshi_ctx* c) {
   CKD(c, hipHostMalloc((void**)&c->h_tokens, sizeof(int) * B, hipHostMallocDefault));
   CKD(c, hipHostMalloc((void**)&c->h_codes, sizeof(int) * B * S, hipHostMallocDefault));
   CKD(c, hipHostMalloc((void**)&c->h_forced, sizeof(int) * B * c->NCH, hipHostMallocDefault));
+  CKD(c, hipHostMalloc((void**)&c->h_samp, sizeof(SampleParams) * B, hipHostMallocDefault));
   CKD(c, hipEventCreateWithFlags(&c->meta_ev, hipEventDisableTiming));
   return MOSHI_OK;
 }
@@ -1019,6 +1075,7 @@ void release(moshi_ctx* c) {
   if (c->h_tokens) (void)hipHostFree(c->h_tokens);
   if (c->h_codes) (void)hipHostFree(c->h_codes);
   if (c->h_forced) (void)hipHostFree(c->h_forced);
+  if (c->h_samp) (void)hipHostFree(c->h_samp);
   if (c->meta_ev) (void)hipEventDestroy(c->meta_ev);
   if (c->own_stream && c->stream) (void)hipStreamDestroy(c->stream);
   delete c;
@@ -1154,6 +1211,8 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
   c->Vt = cfg->text_vocab; c->Va = cfg->audio_card; c->NCH = 1 + cfg->n_substeps;
   c->slots.init(c->B);
   c->S_run = moshi_host::dep_steps(cfg);
+  c->sampling = (cfg->flags & MOSHI_FLAG_SAMPLING) != 0;
+  c->samp.assign(c->B, SampleParams{});  // temperature 0: greedy
   const char* ng = getenv("MOSHI_NO_GRAPH");
   c->use_graphs = !(ng && ng[0] == '1');
   if (hipGetDevice(&c->device) != hipSuccess) {
@@ -1200,7 +1259,35 @@ int moshi_session_join(moshi_ctx* ctx, int32_t* slot_out) {
   if (ctx->failed) return MOSHI_E_DEVICE;
   const int b = ctx->slots.join();
   if (b < 0) return fail(ctx, MOSHI_E_FULL, "every slot is live");
+  if (ctx->sampling) {
+    ctx->samp[b] = SampleParams{};  // a new session is greedy until told otherwise
+    ctx->samp_dirty = true;
+  }
   *slot_out = b;
+  return MOSHI_OK;
+}
+
+int moshi_session_set_sampling(moshi_ctx* ctx, int32_t slot, const moshi_sampling* p) {
+  if (!ctx) return MOSHI_E_INVALID;
+  if (ctx->failed) return MOSHI_E_DEVICE;
+  if (!ctx->slots.is_live(slot)) return fail(ctx, MOSHI_E_NOSESSION, "slot not live");
+  SampleParams q{};
+  if (p) {
+    q.temperature[0] = p->text_temperature > 0.0 ? p->text_temperature : 0.0;
+    q.temperature[1] = p->audio_temperature > 0.0 ? p->audio_temperature : 0.0;
+    q.top_k[0] = p->text_top_k;
+    q.top_k[1] = p->audio_top_k;
+    q.seed = p->seed;
+    if (!(p->text_temperature == p->text_temperature) ||
+        !(p->audio_temperature == p->audio_temperature))
+      return fail(ctx, MOSHI_E_INVALID, "temperature is NaN");
+  }
+  const bool draws = q.temperature[0] > 0.0 || q.temperature[1] > 0.0;
+  if (draws && !ctx->sampling)
+    return fail(ctx, MOSHI_E_INVALID, "the context was created without MOSHI_FLAG_SAMPLING");
+  if (!ctx->sampling) return MOSHI_OK;  // greedy is all it does
+  ctx->samp[slot] = q;
+  ctx->samp_dirty = true;
   return MOSHI_OK;
 }
 

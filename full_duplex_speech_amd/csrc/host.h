@@ -32,8 +32,10 @@ inline int32_t tensor_count(const moshi_config* c) {
   return 1 + S + 6 * L + 2 + S + S + 2 * Ld + 4 * S * Ld + S + extra;
 }
 
-constexpr uint32_t kKnownFlags =
-    MOSHI_FLAG_MASK_OLDEST | MOSHI_FLAG_DEP_FINAL_NORM | MOSHI_FLAG_DEP_REF_RING;
+constexpr uint32_t kKnownFlags = MOSHI_FLAG_MASK_OLDEST | MOSHI_FLAG_DEP_FINAL_NORM |
+                                 MOSHI_FLAG_DEP_REF_RING | MOSHI_FLAG_SAMPLING;
+// Largest vocabulary the sampling kernel takes (1024 threads x 32 values).
+constexpr int kMaxSampledVocab = 32768;
 
 // Largest window the attention kernels accept (64-key spans, 512 of them).
 constexpr int kMaxWindow = 64 * 512;
@@ -64,6 +66,9 @@ inline const char* config_error(const moshi_config* c) {
   if ((c->flags & MOSHI_FLAG_DEP_REF_RING) && dep_steps(c) < 2)
     return "the depformer ring reading needs at least 2 substeps";
   if (c->flags & ~kKnownFlags) return "unknown flag bits";
+  if ((c->flags & MOSHI_FLAG_SAMPLING) &&
+      (c->text_vocab > kMaxSampledVocab || c->audio_card > kMaxSampledVocab))
+    return "sampling takes vocabularies of at most 32768 entries";
   if (c->text_vocab < 2 || c->audio_card < 2) return "vocabularies must have >= 2 entries";
   if (c->max_sessions < 1 || c->max_sessions > 64) return "max_sessions must be in [1, 64]";
   if (!(c->rope_theta > 0.0) || !(c->norm_eps >= 0.0)) return "rope_theta must be > 0 and norm_eps >= 0";

@@ -135,6 +135,32 @@ struct EntryArgs {
   int ssq_rows;     // rows per sum-of-squares partial (2 or 16)
 };
 
+// Per-slot sampling parameters (moshi_session_set_sampling).
+struct SampleParams {
+  double temperature[2];  // [0] text, [1] audio codes; <= 0: greedy (the argmax stands)
+  int top_k[2];           // <= 0 or >= the vocabulary: every token is a candidate
+  uint64_t seed;          // the session's seed (child streams per head)
+};
+
+// One temperature + top-k draw per live column b (see sample_kernel).
+struct SampleArgs {
+  const float* logits;  // column b at logits + b * ld, n values
+  int ld, n;
+  const SampleParams* params;  // [B]
+  int which;                   // 0 text, 1 audio
+  int stream;                  // the draw's stream: 0 text, 1 + s depformer substep s
+  const int64_t* pos;          // [B] positions; the draw uses pos[b] + pos_off
+  int pos_off;
+  const int* live;             // [B]
+  const int* forced;           // [B][forced_stride]; a forced column keeps its token
+  int forced_stride, forced_col;
+  int* out;                    // out[b * out_stride]: the drawn token
+  int out_stride;
+  int B;
+};
+constexpr int SAMPLE_THREADS = 1024;
+constexpr int SAMPLE_MAX_PER_THREAD = 32;  // vocabularies up to 32768
+
 // Attention spans hold about ATTN_CHUNK keys or more; the window is at most
 // ATTN_CHUNK * ATTN_MAX_CHUNKS keys.
 constexpr int ATTN_CHUNK = 64;
@@ -277,6 +303,9 @@ hipError_t launch_attn_combine(int dtype, int hd, const AttnArgs& a, int B, hipS
 hipError_t launch_argmax_reduce(const ArgPart* part, int n_tiles, int n_rows, int B, int* tok,
                                 int stride, const int* forced, int forced_stride, int forced_col,
                                 hipStream_t st);
+// Temperature + top-k draws of every live column that samples (one workgroup
+// of SAMPLE_THREADS per column; greedy and forced columns keep their token).
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st);
 // Outputs of free slots become -1, and codes of substeps past s_run too.
 hipError_t launch_finish_outputs(int* tokens, int* codes, const int* live, int B, int S, int s_run,
                                  hipStream_t st);

@@ -204,6 +204,223 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const ArgPart* part,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Temperature + top-k sampling (SGLang-Omni cookbook "PersonaPlex", "Request
+// parameters": text 0.7 / 25, audio 0.8 / 250, a seed with a child stream per
+// head; mobius PR #368's sampling commit)
+// ---------------------------------------------------------------------------
+
+// splitmix64 (Steele, Lea and Flood, OOPSLA 2014): output n of a generator
+// seeded with `seed` is this mix of seed + n * gamma.
+__device__ __forceinline__ uint64_t sm64(uint64_t seed, uint64_t n) {
+  uint64_t z = seed + n * 0x9E3779B97F4A7C15ull;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+// The draw in [0, 1) of stream `stream` at position pos: output pos+1 of the
+// generator seeded with the stream's child seed (output stream+1 of the
+// session seed's generator), top 53 bits.
+__device__ __forceinline__ double draw_uniform(uint64_t seed, int stream, int64_t pos) {
+  const uint64_t child = sm64(seed, (uint64_t)stream + 1);
+  return (double)(sm64(child, (uint64_t)pos + 1) >> 11) * 0x1.0p-53;
+}
+
+// fp32 value -> unsigned key with the same order (IEEE total order: -0
+// below +0).
+__device__ __forceinline__ uint32_t f32_key(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float key_f32(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+__device__ __forceinline__ double shfl_up_d(double v, int d) {
+  return __hiloint2double(__shfl_up(__double2hiint(v), d), __shfl_up(__double2loint(v), d));
+}
+
+// Exclusive prefix of x over the workgroup's threads in thread order (waves
+// scanned with shuffles, wave totals in order by thread 0); `total` gets the
+// sum. Every thread calls it.
+template <typename V, int NT>
+__device__ __forceinline__ V block_exclusive(V x, V& total) {
+  constexpr int NW = NT / 64;
+  __shared__ V s_w[NW + 1];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  V inc = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    V y;
+    if constexpr (sizeof(V) == 8) y = shfl_up_d(inc, off);
+    else y = __shfl_up(inc, off);
+    if (lane >= off) inc += y;
+  }
+  V ex;
+  if constexpr (sizeof(V) == 8) ex = shfl_up_d(inc, 1);
+  else ex = __shfl_up(inc, 1);
+  if (lane == 0) ex = V(0);
+  if (lane == 63) s_w[w] = inc;
+  __syncthreads();
+  if (t == 0) {
+    V acc = V(0);
+    for (int i = 0; i < NW; ++i) {
+      const V v = s_w[i];
+      s_w[i] = acc;
+      acc += v;
+    }
+    s_w[NW] = acc;
+  }
+  __syncthreads();
+  const V r = s_w[w] + ex;
+  total = s_w[NW];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per column b. The candidates are the top_k largest fp32
+// logits (lowest index first among equal values), found by a 4-pass radix
+// select of the k-th largest key and a prefix count of the keys equal to it;
+// weights w_i = exp((l_i - l_max) / T) in fp64; each thread holds a
+// contiguous run of indices, so an exclusive scan of the threads' sums in
+// thread order gives every candidate's running sum in index order; the draw
+// is the lowest index whose running sum exceeds u * (the total), or the last
+// candidate if none does (the oracle's definition; only the rounding of the
+// sums differs).
+__global__ __launch_bounds__(SAMPLE_THREADS) void sample_kernel(SampleArgs a) {
+  constexpr int NT = SAMPLE_THREADS, MC = SAMPLE_MAX_PER_THREAD;
+  const int b = blockIdx.x, t = threadIdx.x;
+  if (b >= a.B || !a.live[b]) return;
+  if (a.forced != nullptr && a.forced[(size_t)b * a.forced_stride + a.forced_col] >= 0) return;
+  const SampleParams& P = a.params[b];
+  const double T = P.temperature[a.which];
+  if (!(T > 0.0)) return;  // greedy: the argmax already written stands
+  const int n = a.n;
+  int k = P.top_k[a.which];
+  if (k <= 0 || k >= n) k = n;
+  const float* L = a.logits + (size_t)b * a.ld;
+  const int c = (n + NT - 1) / NT;
+  const int i0 = t * c;
+  float val[MC];
+#pragma unroll
+  for (int j = 0; j < MC; ++j) val[j] = (j < c && i0 + j < n) ? L[i0 + j] : 0.0f;
+  auto valid = [&](int j) { return j < c && i0 + j < n; };
+
+  // the k-th largest key and how many keys equal to it are candidates
+  __shared__ unsigned hist[256];
+  __shared__ unsigned s_sel[2];
+  uint32_t kth = 0, need_eq = 0;
+  if (k < n) {
+    uint32_t prefix = 0, pmask = 0, krem = (uint32_t)k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int i = t; i < 256; i += NT) hist[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < MC; ++j) {
+        if (!valid(j)) continue;
+        const uint32_t key = f32_key(val[j]);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (t == 0) {
+        uint32_t acc = 0;
+        int bin = 255;
+        for (; bin > 0; --bin) {
+          if (acc + hist[bin] >= krem) break;
+          acc += hist[bin];
+        }
+        s_sel[0] = (uint32_t)bin;
+        s_sel[1] = krem - acc;
+      }
+      __syncthreads();
+      prefix |= s_sel[0] << shift;
+      pmask |= 0xffu << shift;
+      krem = s_sel[1];
+      __syncthreads();
+    }
+    kth = prefix;
+    need_eq = krem;
+  }
+  // candidates: keys above kth, and the first need_eq keys equal to it
+  unsigned my_eq = 0;
+#pragma unroll
+  for (int j = 0; j < MC; ++j)
+    if (valid(j) && k < n && f32_key(val[j]) == kth) ++my_eq;
+  unsigned eq_total;
+  const unsigned eq_base = block_exclusive<unsigned, NT>(my_eq, eq_total);
+  uint32_t member = 0;  // bit j: element j is a candidate
+  {
+    unsigned r = eq_base;
+#pragma unroll
+    for (int j = 0; j < MC; ++j) {
+      if (!valid(j)) continue;
+      const uint32_t key = f32_key(val[j]);
+      bool m = true;
+      if (k < n) {
+        m = key > kth;
+        if (key == kth) {
+          m = r < need_eq;
+          ++r;
+        }
+      }
+      if (m) member |= 1u << j;
+    }
+  }
+  // the largest value (always a candidate)
+  __shared__ uint32_t s_kmax[NT / 64];
+  uint32_t km = 0;
+#pragma unroll
+  for (int j = 0; j < MC; ++j)
+    if (valid(j)) km = max(km, f32_key(val[j]));
+  for (int off = 32; off > 0; off >>= 1) km = max(km, (uint32_t)__shfl_xor((int)km, off));
+  if ((t & 63) == 0) s_kmax[t >> 6] = km;
+  __syncthreads();
+  km = s_kmax[0];
+  for (int w = 1; w < NT / 64; ++w) km = max(km, s_kmax[w]);
+  const double lmax = (double)key_f32(km);
+  // weights, the threads' sums in index order, the draw
+  double mine = 0.0;
+#pragma unroll
+  for (int j = 0; j < MC; ++j)
+    if (member & (1u << j)) mine += exp(((double)val[j] - lmax) / T);
+  double total;
+  const double before = block_exclusive<double, NT>(mine, total);
+  const double target = draw_uniform(P.seed, a.stream, ldg(a.pos + b) + a.pos_off) * total;
+  int cand = 0x7fffffff, last = -1;
+  double run = before;
+#pragma unroll
+  for (int j = 0; j < MC; ++j) {
+    if (!(member & (1u << j))) continue;
+    last = i0 + j;
+    run += exp(((double)val[j] - lmax) / T);
+    if (cand == 0x7fffffff && run > target) cand = i0 + j;
+  }
+  __shared__ int s_c[NT / 64], s_l[NT / 64];
+  for (int off = 32; off > 0; off >>= 1) {
+    cand = min(cand, __shfl_xor(cand, off));
+    last = max(last, __shfl_xor(last, off));
+  }
+  if ((t & 63) == 0) {
+    s_c[t >> 6] = cand;
+    s_l[t >> 6] = last;
+  }
+  __syncthreads();
+  if (t == 0) {
+    for (int w = 1; w < NT / 64; ++w) {
+      cand = min(cand, s_c[w]);
+      last = max(last, s_l[w]);
+    }
+    a.out[(size_t)b * a.out_stride] = cand != 0x7fffffff ? cand : last;
+  }
+}
+
+hipError_t launch_sample(const SampleArgs& a, hipStream_t st) {
+  if (a.n < 1 || a.n > SAMPLE_THREADS * SAMPLE_MAX_PER_THREAD) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(sample_kernel, dim3(a.B), dim3(SAMPLE_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
 // Outputs of free slots read -1, and so do the codes of substeps not run.
 __global__ __launch_bounds__(64) void finish_outputs_kernel(int* tokens, int* codes,
                                                             const int* live, int B, int S,

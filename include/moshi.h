@@ -62,6 +62,11 @@ enum { MOSHI_F32 = 0, MOSHI_BF16 = 1 };
 #define MOSHI_FLAG_MASK_OLDEST 1u
 #define MOSHI_FLAG_DEP_FINAL_NORM 2u
 #define MOSHI_FLAG_DEP_REF_RING 4u
+/* MOSHI_FLAG_SAMPLING: the context can draw tokens by temperature + top-k
+ *   (moshi_session_set_sampling; vocabularies up to 32768). Without it every
+ *   head is greedy. Contexts with it run one kernel per operation (the
+ *   capacity-1 step kernel is greedy only). */
+#define MOSHI_FLAG_SAMPLING 8u
 
 /* Model shape and engine capacity.
  * Temporal transformer: `dim`, `n_layers`, `n_heads` (head_dim = dim/n_heads
@@ -133,6 +138,37 @@ int moshi_get_config(const moshi_ctx* ctx, moshi_config* out);
  * next step, and steps already enqueued keep the slots they were enqueued
  * with. */
 int moshi_session_join(moshi_ctx* ctx, int32_t* slot_out);
+
+/* Sampling parameters of one session (SGLang-Omni cookbook "PersonaPlex",
+ * "Request parameters": text temperature / top-k 0.7 / 25 by default,
+ * temperature 0 = greedy; audio 0.8 / 250; a seed that makes both draws
+ * reproducible, with a child seed each; mobius PR #368's sampling commit:
+ * temperature + top-k instead of greedy). top_k <= 0 or >= the vocabulary:
+ * no top-k filter.
+ * The draw (the same definition as the repository's CPU reference): it is
+ * decided on the fp32 logits; the candidates are the top_k largest (lowest
+ * index first among equal values, -0 below +0); weights exp((l - l_max) / T)
+ * in fp64; the token is the first candidate in ascending index order whose
+ * running sum of weights exceeds u * (their sum), the last candidate if none
+ * does. u = (output pos+1 of a splitmix64 generator seeded with the stream's
+ * child seed) >> 11, times 2^-53, where the child seed is output stream+1 of
+ * a splitmix64 generator seeded with `seed`, stream 0 is the text head and
+ * 1 + s depformer substep s, and pos is the number of frames the session had
+ * consumed before this one. Forced tokens (moshi_step_forced) win over
+ * drawn ones. */
+typedef struct {
+  double text_temperature;
+  int32_t text_top_k;
+  double audio_temperature;
+  int32_t audio_top_k;
+  uint64_t seed;
+} moshi_sampling;
+
+/* Sets a live session's sampling (NULL: greedy, the default after a join).
+ * Takes effect at the next step. MOSHI_E_INVALID without MOSHI_FLAG_SAMPLING
+ * (unless NULL or both temperatures <= 0); MOSHI_E_NOSESSION if the slot is
+ * not live. */
+int moshi_session_set_sampling(moshi_ctx* ctx, int32_t slot, const moshi_sampling* p);
 
 /* Closes a live session; its slot becomes free for the next join (recipe
  * "When to use this recipe": leaving does not disturb the other slots).

@@ -87,6 +87,12 @@ def _bind(L):
     L.orc_silu.restype = dbl
     L.orc_argmax.argtypes = [vp, ctypes.c_int, vp]
     L.orc_argmax.restype = i32
+    L.orc_splitmix64.argtypes = [ctypes.c_uint64, ctypes.c_uint64]
+    L.orc_splitmix64.restype = ctypes.c_uint64
+    L.orc_uniform.argtypes = [ctypes.c_uint64, i32, i64]
+    L.orc_uniform.restype = dbl
+    L.orc_sample.argtypes = [vp, ctypes.c_int, dbl, ctypes.c_int, dbl, vp]
+    L.orc_sample.restype = i32
     L.orc_n_tensors.argtypes = [ctypes.POINTER(Config)]
     L.orc_n_tensors.restype = i32
     L.orc_model_new.argtypes = [ctypes.POINTER(Config), vp, i32]
@@ -154,6 +160,24 @@ def argmax(v):
     v = np.ascontiguousarray(v, np.float64)
     m = np.zeros(1, np.float64)
     i = lib().orc_argmax(_p(v), v.size, _p(m))
+    return int(i), float(m[0])
+
+
+def splitmix64(seed: int, n: int) -> int:
+    return int(lib().orc_splitmix64(seed & (2**64 - 1), n))
+
+
+def uniform(seed: int, stream: int, pos: int) -> float:
+    """The session's draw in [0, 1) for a stream (0 text, 1+s substep s) at a position."""
+    return float(lib().orc_uniform(seed & (2**64 - 1), int(stream), int(pos)))
+
+
+def sample(logits, temperature: float, top_k: int, u: float):
+    """Temperature + top-k draw (decided on the fp32 values of the logits);
+    returns (index, margin)."""
+    v = np.ascontiguousarray(logits, np.float64)
+    m = np.zeros(1, np.float64)
+    i = lib().orc_sample(_p(v), v.size, float(temperature), int(top_k), float(u), _p(m))
     return int(i), float(m[0])
 
 

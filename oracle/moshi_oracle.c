@@ -212,6 +212,104 @@ int32_t orc_argmax(const double* v, int n, double* margin) {
 }
 
 /* ------------------------------------------------------------------ */
+/* sampling (SGLang-Omni cookbook "PersonaPlex", "Request parameters":  */
+/* text temperature/top-k 0.7/25, audio 0.8/250, a seed that makes both */
+/* draws reproducible with a child seed each; mobius PR #368's sampling  */
+/* commit: temperature + top-k instead of greedy)                        */
+/* ------------------------------------------------------------------ */
+
+/* splitmix64's output function (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", 2014): the generator adds the golden
+ * gamma to its state and returns this mix of the new state. */
+static uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ULL;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBULL;
+  return z ^ (z >> 31);
+}
+#define SM64_GAMMA 0x9E3779B97F4A7C15ULL
+
+/* Output n (n >= 1) of a splitmix64 generator seeded with `seed`. */
+uint64_t orc_splitmix64(uint64_t seed, uint64_t n) { return sm64_mix(seed + n * SM64_GAMMA); }
+
+/* The uniform draw in [0, 1) of a session's stream at one frame: the
+ * stream's child seed is output stream+1 of the session seed's generator
+ * (stream 0: text; 1 + s: depformer substep s), the draw is output pos+1 of
+ * the child's generator (pos: frames the session consumed before this one),
+ * keeping its top 53 bits. */
+double orc_uniform(uint64_t seed, int32_t stream, int64_t pos) {
+  uint64_t child = orc_splitmix64(seed, (uint64_t)stream + 1);
+  return (double)(orc_splitmix64(child, (uint64_t)pos + 1) >> 11) * (1.0 / 9007199254740992.0);
+}
+
+typedef struct {
+  float v;
+  int32_t i;
+} orc_cand;
+
+/* Order of the candidates: larger fp32 value first (IEEE total order: -0
+ * below +0), lower index first on equal bits. */
+static uint32_t f32_order_key(float v) {
+  uint32_t b;
+  memcpy(&b, &v, 4);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+static int cand_cmp(const void* a, const void* b) {
+  const orc_cand* x = (const orc_cand*)a;
+  const orc_cand* y = (const orc_cand*)b;
+  uint32_t kx = f32_order_key(x->v), ky = f32_order_key(y->v);
+  if (kx != ky) return kx > ky ? -1 : 1;
+  return x->i < y->i ? -1 : (x->i > y->i);
+}
+
+/* Temperature + top-k draw from n logits, decided on their fp32 values:
+ * the top_k largest (all of them when top_k <= 0 or >= n) are the
+ * candidates; weight w_i = exp((l_i - l_max) / temperature) in fp64; the
+ * draw is the first candidate, in ascending index order, whose running sum
+ * of weights exceeds u * (sum of all weights); the last candidate if none
+ * does. *margin (optional): distance of u * sum to the nearest running sum
+ * around the choice, divided by the sum (how far the draw is from choosing
+ * a neighbour). temperature must be > 0. */
+int32_t orc_sample(const double* logits, int n, double temperature, int top_k, double u,
+                   double* margin) {
+  int k = (top_k <= 0 || top_k >= n) ? n : top_k;
+  orc_cand* c = (orc_cand*)malloc(sizeof(orc_cand) * n);
+  for (int i = 0; i < n; ++i) {
+    c[i].v = (float)logits[i];
+    c[i].i = i;
+  }
+  qsort(c, n, sizeof(orc_cand), cand_cmp);
+  double lmax = (double)c[0].v;
+  char* member = (char*)calloc(n, 1);
+  for (int j = 0; j < k; ++j) member[c[j].i] = 1;
+  double total = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (member[i]) total += exp(((double)(float)logits[i] - lmax) / temperature);
+  double target = u * total, run = 0.0, before = 0.0;
+  int32_t pick = -1, last = -1;
+  for (int i = 0; i < n; ++i) {
+    if (!member[i]) continue;
+    last = i;
+    before = run;
+    run += exp(((double)(float)logits[i] - lmax) / temperature);
+    if (run > target) {
+      pick = i;
+      break;
+    }
+  }
+  if (pick < 0) {
+    pick = last;
+    before = run;
+  }
+  if (margin) {
+    double a = fabs(target - before), b = fabs(run - target);
+    *margin = (a < b ? a : b) / total;
+  }
+  free(c);
+  free(member);
+  return pick;
+}
+
+/* ------------------------------------------------------------------ */
 /* model                                                               */
 /* ------------------------------------------------------------------ */
 

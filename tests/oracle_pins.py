@@ -327,7 +327,79 @@ def check_depformer_variants():
     assert np.array_equal(b["audio_logits"], 2.0 * a["audio_logits"]), "final norm gain"
 
 
+def check_splitmix64_published():
+    """The counter generator behind the sampling draws is splitmix64: its
+    published first outputs for seed 0 (tests/golden/splitmix64_seed0.json)."""
+    import json, os
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "splitmix64_seed0.json")))
+    got = [oracle.splitmix64(0, n) for n in range(1, 5)]
+    assert got == [int(h, 16) for h in gold["outputs_hex"]], "splitmix64 outputs"
+
+
+def check_uniform_draws():
+    """Draws lie in [0, 1), look uniform (mean, variance, a 10-bin histogram
+    over 20000 positions), and the streams of one seed and the same stream
+    of two seeds differ."""
+    u = np.array([oracle.uniform(7, 0, p) for p in range(20000)])
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert abs(u.mean() - 0.5) < 0.01 and abs(u.var() - 1 / 12) < 0.005
+    h = np.histogram(u, bins=10, range=(0, 1))[0]
+    assert np.all(np.abs(h - 2000) < 200), "uniform histogram"
+    a = [oracle.uniform(7, 1, p) for p in range(50)]
+    b = [oracle.uniform(7, 2, p) for p in range(50)]
+    c = [oracle.uniform(8, 1, p) for p in range(50)]
+    assert len(set(a) & set(b)) == 0 and len(set(a) & set(c)) == 0
+    assert oracle.uniform(7, 1, 3) == oracle.uniform(7, 1, 3)
+
+
+def check_sampling():
+    """Temperature + top-k draws against numpy: on a grid of u the number of
+    grid points that choose each token is N * p within one, p the softmax of
+    logits / T over the top k (ties at the boundary to the lower index);
+    top-k 1 is the argmax; doubling the logits and the temperature changes
+    nothing; the draw is decided on the fp32 values."""
+    g = np.random.default_rng(71)
+    N = 4000
+    for n, T, k in ((37, 0.7, 5), (300, 0.8, 250), (60, 1.3, -1), (50, 0.5, 50)):
+        lg = g.normal(0, 1.5, n)
+        l32 = lg.astype(np.float32).astype(np.float64)
+        order = sorted(range(n), key=lambda i: (-l32[i], i))
+        kk = n if (k <= 0 or k >= n) else k
+        members = np.zeros(n, bool)
+        members[order[:kk]] = True
+        w = np.where(members, np.exp((l32 - l32.max()) / T), 0.0)
+        p = w / w.sum()
+        counts = np.zeros(n)
+        for j in range(N):
+            i, _ = oracle.sample(lg, T, k, (j + 0.5) / N)
+            counts[i] += 1
+        assert np.all(np.abs(counts - N * p) <= 1.0 + 1e-9), f"sampling distribution n={n} k={k}"
+        assert counts[~members].sum() == 0, "a token outside the top k was drawn"
+        for u in (0.0, 0.3, 0.999):
+            a = oracle.sample(lg, T, k, u)
+            b = oracle.sample(2.0 * lg, 2.0 * T, k, u)
+            assert a == b, "temperature must divide the logit differences"
+        i1, _ = oracle.sample(lg, T, 1, 0.77)
+        assert i1 == order[0], "top-k 1 is the argmax"
+    # ties at the top-k boundary: the lower indices are the candidates
+    lg = np.array([1.0, 3.0, 3.0, 3.0, 0.0])
+    picks = {oracle.sample(lg, 1.0, 2, u)[0] for u in np.linspace(0.01, 0.99, 30)}
+    assert picks == {1, 2}, f"boundary ties: {picks}"
+    # decided on fp32: logits that round to the same fp32 values draw the same
+    lg = g.normal(0, 1, 40)
+    l2 = lg.astype(np.float32).astype(np.float64) + 1e-12 * g.normal(size=40)
+    assert all(oracle.sample(lg, 0.9, 7, u)[0] == oracle.sample(l2, 0.9, 7, u)[0]
+               for u in np.linspace(0.05, 0.95, 19))
+    # ... where fp32 rounding matters: 1e8 + 3 and 1e8 + 2 round to 1e8
+    # (fp32 spacing 8 there), so the three tokens weigh the same and u = 0.34
+    # draws token 1; in fp64 their weights e^{3/4}, e^{2/4}, 1 would draw token 0
+    lg = np.array([1e8 + 3, 1e8 + 2, 1e8])
+    assert oracle.sample(lg, 4.0, -1, 0.34)[0] == 1, "decided on the fp32 values"
+    assert oracle.sample(lg, 4.0, -1, 0.30)[0] == 0 and oracle.sample(lg, 4.0, -1, 0.7)[0] == 2
+
+
 ALL = [check_bf16_round, check_rmsnorm, check_rope, check_attend, check_silu_argmax,
        check_embedding_onehot, check_ring_window_fp32, check_ring_window_mask_oldest,
        check_incremental_equals_fullseq_bf16, check_depformer_fullseq, check_step_composition,
-       check_sizes, check_ring_transfer, check_depformer_variants]
+       check_sizes, check_ring_transfer, check_depformer_variants, check_splitmix64_published,
+       check_uniform_draws, check_sampling]

@@ -61,8 +61,8 @@ def test_n_tensors_matches_the_weight_list():
 
 @pytest.mark.parametrize("field,value", [
     ("n_heads", 3), ("dim", 0), ("dep_heads", 5), ("window", 0), ("max_sessions", 0),
-    ("max_sessions", 65), ("dtype", 7), ("ffn_hidden", 1001), ("text_vocab", 1), ("flags", 8),
-    ("n_substeps", 0), ("n_layers", 0), ("rope_theta", 0.0),
+    ("max_sessions", 65), ("dtype", 7), ("ffn_hidden", 1001), ("text_vocab", 1), ("flags", 16),
+    ("n_substeps", 0), ("n_layers", 0), ("rope_theta", 0.0), ("dep_q", 17), ("dep_q", -1),
 ])
 def test_bad_configs_are_rejected(field, value):
     _lib()
@@ -72,6 +72,14 @@ def test_bad_configs_are_rejected(field, value):
     ptrs = (ctypes.c_void_p * 1)()
     rc = M.lib().moshi_create(ctypes.byref(c), ptrs, 1, None, ctypes.byref(out))
     assert rc == M.MOSHI_E_INVALID and not out.value
+
+
+def test_sampling_vocabulary_limit():
+    _lib()
+    c = _cfg(spec.PERSONAPLEX, flags=M.MOSHI_FLAG_SAMPLING)
+    assert M.moshi_n_tensors(c) == spec.n_tensors(spec.PERSONAPLEX)
+    c = _cfg(spec.PERSONAPLEX.replace(text_vocab=40000), flags=M.MOSHI_FLAG_SAMPLING)
+    assert M.moshi_n_tensors(c) == M.MOSHI_E_INVALID
 
 
 def test_null_and_count_errors_need_no_device():

@@ -58,6 +58,21 @@ MUTATIONS = [
     ("load_ring_row_shift", "ring_put(s, s->k_ring, l, j, kv);",
      "ring_put(s, s->k_ring, l, (j + 1) % W, kv);", 0),
     ("load_ring_position", "  s->pos = pos;\n", "  s->pos = pos + 1;\n", 0),
+    ("splitmix_constant", "0xBF58476D1CE4E5B9ULL", "0xBF58476D1CE4E5B7ULL", 0),
+    ("uniform_bits", "(double)(orc_splitmix64(child, (uint64_t)pos + 1) >> 11)",
+     "(double)(orc_splitmix64(child, (uint64_t)pos + 1) >> 12)", 0),
+    ("sample_topk_short", "for (int j = 0; j < k; ++j) member[c[j].i] = 1;",
+     "for (int j = 0; j + 1 < k; ++j) member[c[j].i] = 1;", 0),
+    ("sample_temperature_total", "total += exp(((double)(float)logits[i] - lmax) / temperature);",
+     "total += exp(((double)(float)logits[i] - lmax));", 0),
+    ("sample_temperature_run", "run += exp(((double)(float)logits[i] - lmax) / temperature);",
+     "run += exp(((double)(float)logits[i] - lmax) * temperature);", 0),
+    ("sample_tie_order", "return x->i < y->i ? -1 : (x->i > y->i);",
+     "return x->i > y->i ? -1 : (x->i < y->i);", 0),
+    ("sample_order_reversed", "if (kx != ky) return kx > ky ? -1 : 1;",
+     "if (kx != ky) return kx < ky ? -1 : 1;", 0),
+    ("sample_fp64_weights", "run += exp(((double)(float)logits[i] - lmax) / temperature);",
+     "run += exp((logits[i] - lmax) / temperature);", 0),
     ("dep_inproj_shared", "linear(m, m->dep_in[s], Dd, D, hid_r, y);",
      "linear(m, m->dep_in[0], Dd, D, hid_r, y);", 0),
     ("dep_embedding_shared", "wget(m, m->dep_emb[s], (size_t)prev * Dd + i)",
