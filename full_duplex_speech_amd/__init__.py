@@ -114,6 +114,7 @@ def lib():
             "moshi_session_prefill_kv": ([vp, i32, i32, vp, vp], ctypes.c_int),
             "moshi_session_info": ([vp, i32, vp, vp, vp], ctypes.c_int),
             "moshi_session_read_kv": ([vp, i32, vp, vp], ctypes.c_int),
+            "moshi_session_prefill_frames": ([vp, i32, i32, vp, vp, vp], ctypes.c_int),
             "moshi_read_logits": ([vp, vp, vp], ctypes.c_int),
             "moshi_read_hidden": ([vp, vp], ctypes.c_int),
             "moshi_time_kernels": ([vp, vp, i32, vp, vp, vp, i32], ctypes.c_int),
@@ -309,6 +310,17 @@ def moshi_session_prefill_kv(ctx: Ctx, slot: int, k, v):
     k = None if n == 0 else np.ascontiguousarray(k)
     v = None if n == 0 else np.ascontiguousarray(v)
     _check(lib().moshi_session_prefill_kv(ctx.h, int(slot), n, _p(k), _p(v)), ctx)
+
+
+def moshi_session_prefill_frames(ctx: Ctx, slot: int, frames, want_logits=False):
+    """frames int32 [n, 1+S] of one session -> (text_tokens [n], text_logits
+    [n, Vt] or None); the temporal transformer over all n frames at once."""
+    f = np.ascontiguousarray(frames, np.int32).reshape(-1, ctx.S + 1)
+    n = f.shape[0]
+    tok = np.empty(n, np.int32)
+    tl = np.empty((n, ctx.cfg.text_vocab), np.float32) if want_logits else None
+    _check(lib().moshi_session_prefill_frames(ctx.h, int(slot), n, _p(f), _p(tok), _p(tl)), ctx)
+    return tok, tl
 
 
 def moshi_session_read_kv(ctx: Ctx, slot: int):

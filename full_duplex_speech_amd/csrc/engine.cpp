@@ -62,6 +62,18 @@ const char* config_error(const moshi_config* c) { return moshi_host::config_erro
 
 }  // namespace
 
+// Workspace of the multi-frame prefill (up to 64 frames per chunk).
+struct PrefillWs {
+  bool ready = false;
+  int rows = 0, spans = 1;
+  double *x = nullptr, *ssq = nullptr, *q = nullptr, *part = nullptr;
+  void *hn = nullptr, *o = nullptr, *act = nullptr, *hid = nullptr, *wk = nullptr, *wv = nullptr;
+  float* logits = nullptr;
+  moshi::ArgPart* apart = nullptr;
+  int *tok = nullptr, *live = nullptr, *frames = nullptr, *key0 = nullptr, *nkeys = nullptr;
+  int64_t* pos = nullptr;
+};
+
 struct moshi_ctx {
   moshi_config c{};
   int B = 0, dtype = 0, esz = 0, device = 0;
@@ -141,6 +153,7 @@ struct moshi_ctx {
   int step_parity = 0;
   uint32_t step_seq = 0;  // sequence number of the last step kernel launch
   StepArgs step_host{};   // host copy of *d_step
+  PrefillWs pf;
   // the same step with its synchronisation scratch in the static scratch of
   // static_step.hip (moshi_step_enqueue_noalloc); null when it does not fit
   StepArgs* d_step_static = nullptr;
@@ -576,6 +589,142 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
   return run(c, KC_ARGMAX, 0.0, [&] {
     return launch_finish_outputs(c->tokens, c->codes, c->d_live, B, S, c->S_run, c->stream);
   });
+}
+
+// ---- multi-frame prefill of one session (moshi_session_prefill_frames) ----
+
+constexpr int PF_COLS = 64;  // frames per chunk: the MFMA kernels' widest column tile set
+
+// The chunk workspace, allocated at the first prefill.
+int ensure_prefill(moshi_ctx* c) {
+  if (c->pf.ready) return MOSHI_OK;
+  PrefillWs& p = c->pf;
+  const size_t NC = PF_COLS, D = c->D, F = c->F, es = c->esz;
+  const size_t rows = (size_t)c->W - 1 + NC;  // window rows: W - 1 earlier positions + the chunk
+  p.spans = (c->W + ATTN_CHUNK - 1) / ATTN_CHUNK;
+  if (p.spans > 4) p.spans = 4;
+  const size_t nssq = (D + 1) / 2 > ((D + 15) / 16) * NC ? (D + 1) / 2 : ((D + 15) / 16) * NC;
+  struct Req {
+    void** ptr;
+    size_t bytes;
+  } reqs[] = {
+      {(void**)&p.x, NC * D * 8},
+      {(void**)&p.ssq, nssq * 8},
+      {(void**)&p.q, NC * D * 8},
+      {&p.hn, NC * D * es},
+      {&p.o, NC * D * es},
+      {&p.act, NC * F * es},
+      {&p.hid, NC * D * es},
+      {(void**)&p.logits, NC * c->Vt * 4},
+      {(void**)&p.apart, (size_t)((c->Vt + 15) / 16) * NC * sizeof(ArgPart)},
+      {(void**)&p.tok, NC * 4},
+      {(void**)&p.pos, NC * 8},
+      {(void**)&p.live, NC * 4},
+      {(void**)&p.frames, NC * c->NCH * 4},
+      {(void**)&p.key0, NC * 4},
+      {(void**)&p.nkeys, NC * 4},
+      {(void**)&p.part, NC * c->H * p.spans * (size_t)(c->hd + 2) * 8},
+      {&p.wk, (size_t)c->H * rows * c->hd * es},
+      {&p.wv, (size_t)c->H * rows * c->hd * es},
+  };
+  for (auto& r : reqs) {
+    hipError_t e = dalloc(c, r.ptr, r.bytes);
+    if (e == hipErrorOutOfMemory || e == hipErrorMemoryAllocation)
+      return fail(c, MOSHI_E_OOM, "prefill workspace: out of device memory");
+    if (e != hipSuccess) return device_fail(c, e, "hipMalloc(prefill)");
+  }
+  for (size_t i = 0; i < 11; ++i) CKD(c, hipMemsetAsync(*reqs[i].ptr, 0, reqs[i].bytes, c->stream));
+  std::vector<int> ones(NC, 1);
+  CKD(c, hipMemcpyAsync(p.live, ones.data(), NC * 4, hipMemcpyHostToDevice, c->stream));
+  CKD(c, hipStreamSynchronize(c->stream));
+  p.rows = (int)rows;
+  p.ready = true;
+  return MOSHI_OK;
+}
+
+// One chunk of m frames (positions p0 .. p0 + m - 1) of slot `slot`.
+hipError_t prefill_chunk(moshi_ctx* c, int slot, int64_t p0, int m) {
+  PrefillWs& p = c->pf;
+  const int dt = c->dtype, D = c->D, F = c->F, H = c->H, hd = c->hd, W = c->W;
+  const int sr = m == 1 ? GEMV_SSQ_ROWS : 16;  // rows per sum-of-squares partial
+  const int nss_D = (D + sr - 1) / sr;
+  // window rows: row i holds position s0 + i; the chunk starts at row p0 - s0
+  const int64_t s0 = p0 - (W - 1) > 0 ? p0 - (W - 1) : 0;
+  const int c0 = (int)(p0 - s0);
+  auto base = [&](GemmArgs a) {
+    a.B = m;
+    a.live = p.live;
+    return a;
+  };
+  hipError_t e;
+  {
+    EmbedArgs a = embed_args(c);
+    a.frames = p.frames; a.live = p.live; a.B = m; a.x = p.x; a.ssq_out = p.ssq; a.ssq_rows = sr;
+    if ((e = launch_embed(dt, a, c->stream)) != hipSuccess) return e;
+  }
+  const int64_t ring_slot = (int64_t)slot * t_slot_stride(c);
+  const int64_t ring_head = (int64_t)W * hd, win_head = (int64_t)p.rows * hd;
+  for (int l = 0; l < c->L; ++l) {
+    char* rk = (char*)c->ring_k + (ring_slot + l * t_layer_elems(c)) * c->esz;
+    char* rv = (char*)c->ring_v + (ring_slot + l * t_layer_elems(c)) * c->esz;
+    // the ring's earlier positions into the window's first rows
+    if ((e = launch_window_copy(dt, p.wk, rk, 0, c0, s0, W, H, hd, win_head, ring_head, 0,
+                                c->stream)) != hipSuccess ||
+        (e = launch_window_copy(dt, p.wv, rv, 0, c0, s0, W, H, hd, win_head, ring_head, 0,
+                                c->stream)) != hipSuccess)
+      return e;
+    {  // RMSNorm -> q|k|v -> RoPE(pos) -> the chunk's rows of the window
+      GemmArgs a = base(t_qkv_args(c, l));
+      a.X = p.x; a.ssq = p.ssq; a.n_ssq = nss_D; a.xn_out = m > 1 ? p.hn : nullptr;
+      a.q_out = p.q; a.pos = p.pos;
+      a.ring_k = (char*)p.wk + (size_t)c0 * hd * c->esz;
+      a.ring_v = (char*)p.wv + (size_t)c0 * hd * c->esz;
+      a.slot_stride = hd; a.layer_off = 0; a.head_stride = win_head; a.cap = 1;
+      if ((e = gemm(c, PRO_NORM, EPI_QKV, a)) != hipSuccess) return e;
+    }
+    {
+      PrefillAttnArgs pa;
+      memset(&pa, 0, sizeof(pa));
+      pa.a.q = p.q; pa.a.ldq = D; pa.a.ring_k = p.wk; pa.a.ring_v = p.wv;
+      pa.a.head_stride = win_head; pa.a.cap = p.rows; pa.a.n_heads = H;
+      pa.a.max_spans = p.spans; pa.a.part = p.part; pa.a.o_out = p.o; pa.a.ldo = D;
+      pa.a.scalar_excl = -1;
+      pa.key0 = p.key0; pa.nkeys = p.nkeys; pa.m = m;
+      if ((e = launch_prefill_attn(dt, hd, pa, c->stream)) != hipSuccess) return e;
+    }
+    // the chunk's rows into the ring (the last W of them, later rows win)
+    const int first = c0 + (m > W ? m - W : 0);
+    if ((e = launch_window_copy(dt, p.wk, rk, first, c0 + m, s0, W, H, hd, win_head, ring_head, 1,
+                                c->stream)) != hipSuccess ||
+        (e = launch_window_copy(dt, p.wv, rv, first, c0 + m, s0, W, H, hd, win_head, ring_head, 1,
+                                c->stream)) != hipSuccess)
+      return e;
+    {
+      GemmArgs a = base(t_o_args(c, l));
+      a.X = p.o; a.resid = p.x; a.ssq_out = p.ssq;
+      if ((e = gemm(c, PRO_DIRECT, EPI_RESID, a)) != hipSuccess) return e;
+    }
+    {
+      GemmArgs a = base(t_gu_args(c, l));
+      a.X = p.x; a.ssq = p.ssq; a.n_ssq = nss_D; a.xn_out = m > 1 ? p.hn : nullptr; a.act = p.act;
+      if ((e = gemm(c, PRO_NORM, EPI_SWIGLU, a)) != hipSuccess) return e;
+    }
+    {
+      GemmArgs a = base(t_dn_args(c, l));
+      a.X = p.act; a.resid = p.x; a.ssq_out = p.ssq;
+      if ((e = gemm(c, PRO_DIRECT, EPI_RESID, a)) != hipSuccess) return e;
+    }
+  }
+  {
+    GemmArgs a = base(t_head_args(c));
+    a.X = p.x; a.ssq = p.ssq; a.n_ssq = nss_D; a.xn_out = p.hid; a.logits = p.logits;
+    a.ldo = c->Vt; a.apart = p.apart;
+    if ((e = gemm(c, PRO_NORM, EPI_ARGMAX, a)) != hipSuccess) return e;
+    if ((e = launch_argmax_reduce(p.apart, (c->Vt + 15) / 16, c->Vt, m, p.tok, 1, nullptr, 0, 0,
+                                  c->stream)) != hipSuccess)
+      return e;
+  }
+  return hipSuccess;
 }
 
 // ---- the persistent step kernel (one session) ----
@@ -1421,6 +1570,58 @@ int moshi_session_prefill_kv(moshi_ctx* c, int32_t slot, int32_t n, const void* 
   }
   CKD(c, hipStreamSynchronize(c->stream));
   c->slots.set_pos(slot, n);
+  return MOSHI_OK;
+}
+
+int moshi_session_prefill_frames(moshi_ctx* c, int32_t slot, int32_t n, const int32_t* frames,
+                                 int32_t* text_tokens, float* text_logits) {
+  int rc = check_ctx(c);
+  if (rc) return rc;
+  if (!c->slots.is_live(slot)) return fail(c, MOSHI_E_NOSESSION, "slot not live");
+  if (n < 0) return fail(c, MOSHI_E_INVALID, "negative frame count");
+  if (n == 0) return MOSHI_OK;
+  if (!frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
+  for (int64_t i = 0; i < (int64_t)n * c->NCH; ++i) {
+    const int k = (int)(i % c->NCH);
+    if (frames[i] < 0 || frames[i] > (k == 0 ? c->Vt : c->Va))
+      return fail(c, MOSHI_E_INVALID, "frame code out of range");
+  }
+  if ((rc = ensure_prefill(c))) return rc;
+  PrefillWs& p = c->pf;
+  const int64_t p0 = c->slots.pos[slot];
+  const int W = c->W;
+  const bool mo = (c->c.flags & MOSHI_FLAG_MASK_OLDEST) != 0;
+  std::vector<int64_t> pos(PF_COLS);
+  std::vector<int> key0(PF_COLS), nkeys(PF_COLS), tok(PF_COLS);
+  for (int j0 = 0; j0 < n; j0 += PF_COLS) {
+    const int m = n - j0 < PF_COLS ? n - j0 : PF_COLS;
+    const int64_t P0 = p0 + j0;
+    const int64_t s0 = P0 - (W - 1) > 0 ? P0 - (W - 1) : 0;
+    for (int j = 0; j < m; ++j) {
+      const int64_t P = P0 + j;
+      int64_t lo = P - W + 1;
+      if (mo && P >= W - 1) lo = P - W + 2;
+      if (lo < 0) lo = 0;
+      pos[j] = P;
+      key0[j] = (int)(lo - s0);
+      nkeys[j] = (int)(P - lo + 1);
+    }
+    CKD(c, hipMemcpyAsync(p.frames, frames + (size_t)j0 * c->NCH, sizeof(int) * m * c->NCH,
+                          hipMemcpyHostToDevice, c->stream));
+    CKD(c, hipMemcpyAsync(p.pos, pos.data(), sizeof(int64_t) * m, hipMemcpyHostToDevice, c->stream));
+    CKD(c, hipMemcpyAsync(p.key0, key0.data(), sizeof(int) * m, hipMemcpyHostToDevice, c->stream));
+    CKD(c, hipMemcpyAsync(p.nkeys, nkeys.data(), sizeof(int) * m, hipMemcpyHostToDevice, c->stream));
+    CKD(c, prefill_chunk(c, slot, P0, m));
+    CKD(c, hipMemcpyAsync(tok.data(), p.tok, sizeof(int) * m, hipMemcpyDeviceToHost, c->stream));
+    if (text_logits)
+      CKD(c, hipMemcpyAsync(text_logits + (size_t)j0 * c->Vt, p.logits, sizeof(float) * m * c->Vt,
+                            hipMemcpyDeviceToHost, c->stream));
+    CKD(c, hipStreamSynchronize(c->stream));
+    if (text_tokens)
+      for (int j = 0; j < m; ++j) text_tokens[j0 + j] = tok[j];
+  }
+  c->meta_ev_pending = false;
+  c->slots.set_pos(slot, p0 + n);
   return MOSHI_OK;
 }
 

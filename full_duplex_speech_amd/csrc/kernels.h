@@ -158,6 +158,24 @@ struct SampleArgs {
   int out_stride;
   int B;
 };
+// Attention of a multi-frame prefill chunk (prefill_attn_kernel): query
+// column b attends rows [key0[b], key0[b] + nkeys[b]) of a window buffer whose
+// head h starts at a.ring_k / a.ring_v + h * a.head_stride; q [m][a.ldq],
+// outputs a.o_out [m][a.ldo], span partials a.part [m][H][max_spans][HD + 2].
+struct PrefillAttnArgs {
+  AttnArgs a;
+  const int* key0;
+  const int* nkeys;
+  int m;
+};
+hipError_t launch_prefill_attn(int dtype, int hd, const PrefillAttnArgs& p, hipStream_t st);
+// Rows [i0, i1) of a window buffer (head stride win_head_stride) <-> one
+// layer of a session's ring (head stride ring_head_stride; row i is ring
+// slot (s0 + i) mod W); to_ring picks the direction.
+hipError_t launch_window_copy(int dtype, void* win, void* ring, int i0, int i1, int64_t s0, int W,
+                              int H, int hd, int64_t win_head_stride, int64_t ring_head_stride,
+                              int to_ring, hipStream_t st);
+
 constexpr int SAMPLE_THREADS = 1024;
 constexpr int SAMPLE_MAX_PER_THREAD = 32;  // vocabularies up to 32768
 

@@ -602,6 +602,103 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* ring, T* dst, int 
 }
 
 // ---------------------------------------------------------------------------
+// Multi-frame prefill of one session (mobius PR #368, "P2 - Moshi LM": the
+// temporal task takes input_frame[B, 17, S] with S > 1; priming runs whole
+// prompts through it): the frames are the columns of the projections, and
+// each layer's keys and values sit in a window buffer, per head
+// [rows][HD], row i holding position s0 + i (the ring's rows of earlier
+// positions gathered in front, the chunk's own rows written after them by
+// the q/k/v epilogue), so every query column attends a contiguous run.
+// ---------------------------------------------------------------------------
+
+// Rows [i0, i1) of the window buffer <-> the session's ring (ring slot of
+// position s0 + i is (s0 + i) mod W): to_ring = 0 copies ring -> window,
+// 1 copies window -> ring. One thread per element.
+template <typename T>
+__global__ __launch_bounds__(256) void window_copy_kernel(T* win, T* ring, int i0, int i1, int64_t s0,
+                                                          int W, int H, int hd,
+                                                          int64_t win_head_stride,
+                                                          int64_t ring_head_stride, int to_ring) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t per_head = (int64_t)(i1 - i0) * hd;
+  if (e >= per_head * H) return;
+  const int64_t h = e / per_head;
+  const int64_t r = e - h * per_head;
+  const int64_t i = i0 + r / hd;
+  const int64_t d = r - (r / hd) * hd;
+  T* w = win + h * win_head_stride + i * hd + d;
+  T* g = ring + h * ring_head_stride + ((s0 + i) % W) * hd + d;
+  if (to_ring) *g = *w;
+  else *w = *g;
+}
+
+// Attention of query column b = blockIdx.z, head blockIdx.y, key span
+// blockIdx.x over window rows [key0[b], key0[b] + nkeys[b]) (attn_span's
+// arithmetic; spans merged by prefill_combine_kernel in span order).
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillAttnArgs p) {
+  __shared__ double s_w[span_lds_doubles<T, HD, 256>()];
+  const int span = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int nvalid = p.nkeys[b];
+  const int ns = n_spans(p.a, nvalid);
+  if (span >= ns) return;
+  AttnArgs a = p.a;
+  a.slot_stride = 0;  // the column's window starts key0[b] rows into the buffer
+  a.ring_k = (const T*)p.a.ring_k + (size_t)p.key0[b] * HD;
+  a.ring_v = (const T*)p.a.ring_v + (size_t)p.key0[b] * HD;
+  double* part = a.part + (((size_t)b * a.n_heads + h) * a.max_spans + span) * (HD + 2);
+  attn_span<T, HD, 256, false>(a, h, b, span * nvalid / ns, (span + 1) * nvalid / ns, nvalid, -1,
+                               s_w, part, ns == 1);
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(HD) void prefill_combine_kernel(PrefillAttnArgs p) {
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int ns = n_spans(p.a, p.nkeys[b]);
+  if (ns <= 1) return;  // written directly
+  combine_item<T, HD, false>(p.a, h, b, ns);
+}
+
+template <typename T>
+static hipError_t launch_prefill_attn_t(int hd, const PrefillAttnArgs& p, hipStream_t st) {
+  const dim3 grid(p.a.max_spans, p.a.n_heads, p.m), cgrid(p.a.n_heads, p.m);
+#define MOSHI_PF(HDV)                                                                 \
+  case HDV:                                                                           \
+    hipLaunchKernelGGL((prefill_attn_kernel<T, HDV>), grid, dim3(256), 0, st, p);     \
+    hipLaunchKernelGGL((prefill_combine_kernel<T, HDV>), cgrid, dim3(HDV), 0, st, p); \
+    break;
+  switch (hd) {
+    MOSHI_PF(32)
+    MOSHI_PF(64)
+    MOSHI_PF(128)
+    default: return hipErrorInvalidValue;
+  }
+#undef MOSHI_PF
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(int dtype, int hd, const PrefillAttnArgs& p, hipStream_t st) {
+  if (p.m < 1 || p.a.max_spans < 1) return hipErrorInvalidValue;
+  return dtype == DT_BF16 ? launch_prefill_attn_t<__bf16>(hd, p, st)
+                          : launch_prefill_attn_t<float>(hd, p, st);
+}
+
+hipError_t launch_window_copy(int dtype, void* win, void* ring, int i0, int i1, int64_t s0, int W,
+                              int H, int hd, int64_t win_head_stride, int64_t ring_head_stride,
+                              int to_ring, hipStream_t st) {
+  const int64_t total = (int64_t)(i1 - i0) * hd * H;
+  if (total <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256)), block(256);
+  if (dtype == DT_BF16)
+    hipLaunchKernelGGL(window_copy_kernel<__bf16>, grid, block, 0, st, (__bf16*)win, (__bf16*)ring,
+                       i0, i1, s0, W, H, hd, win_head_stride, ring_head_stride, to_ring);
+  else
+    hipLaunchKernelGGL(window_copy_kernel<float>, grid, block, 0, st, (float*)win, (float*)ring, i0,
+                       i1, s0, W, H, hd, win_head_stride, ring_head_stride, to_ring);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 

@@ -309,6 +309,22 @@ int moshi_depformer_step(moshi_ctx* ctx, const void* hidden, const int32_t* text
 int moshi_session_prefill_kv(moshi_ctx* ctx, int32_t slot, int32_t n, const void* k,
                              const void* v);
 
+/* Multi-frame prefill (mobius PR #368, "P2 - Moshi LM": the temporal task
+ * takes input_frame[B, 17, S] with S > 1; the persona/voice commit primes a
+ * conversation in about 2 s): runs the temporal transformer and text head
+ * over n consecutive frames of one live session at once -- the same result
+ * as n temporal-only steps (moshi_temporal_step) of that session, with every
+ * projection an MFMA product over up to 64 frames at a time. The depformer
+ * does not run. The frames' K/V are written into the session's ring and its
+ * position advances by n; other slots are untouched.
+ * frames [n, 1+S] int32 (codes as in moshi_step; any out of range ->
+ *   MOSHI_E_INVALID before any device work); text_tokens [n] (greedy) and
+ *   text_logits [n, Vt] float32 receive each frame's outputs (either may be
+ *   NULL). A workspace (~60 MB at the PersonaPlex shape) is allocated at the
+ *   first call. Synchronous. */
+int moshi_session_prefill_frames(moshi_ctx* ctx, int32_t slot, int32_t n, const int32_t* frames,
+                                 int32_t* text_tokens, float* text_logits);
+
 /* Copies a live slot's whole ring out: k, v [L][W][D] in the config's dtype,
  * ring slot j (row j) holding the position congruent to j mod W; rows the
  * session has not written yet are unspecified. (The recipe's ring KV cache,
