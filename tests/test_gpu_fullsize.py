@@ -338,3 +338,74 @@ def test_w5_b64_full_rings(weights, omodel):
     for (tag, tok, codes, tl, al), r in zip(meta, res):
         compare_frame(SHAPE, stats, tag, tok, codes, tl, al, r)
     log(f"w5 oracle samples ok {stats}")
+
+
+def test_prefill_frames_b1_full_ring(b1, omodel):
+    """64 frames prefilled at once after the full 3000-frame ring (positions
+    3000..3063, one MFMA chunk): frames 0 and 1 against the oracle stepped
+    from the seeded prefill, frame 63 against the oracle stepped from the
+    GPU's ring after the call, with the K/V rows of those positions."""
+    ctx = b1
+    w2 = wl.WORKLOADS[2]
+    slot = M.moshi_session_join(ctx)
+    k, v = wl.prefill_kv(SHAPE, w2.seed("prefill"), 0, SHAPE.window, threads=16)
+    M.moshi_session_prefill_kv(ctx, slot, k, v)
+    n = 64
+    frames = wl.frames(SHAPE, w2.seed("frames") + 100, 0, 0, n)
+    tok, tl = M.moshi_session_prefill_frames(ctx, slot, frames, want_logits=True)
+    assert M.moshi_session_info(ctx, slot)[0] == SHAPE.window + n
+    rk, rv = M.moshi_session_read_kv(ctx, slot)
+    M.moshi_session_leave(ctx, slot)
+    log("prefill of 64 frames done on the GPU")
+    stats = Stats()
+
+    def first_frames():
+        o = oracle.Session(omodel)
+        o.prefill(k, v)
+        out = [o.temporal(frames[j]) for j in range(2)]
+        return out, o.read_ring()
+
+    def last_frame():
+        o = oracle.Session(omodel)
+        o.load_ring(SHAPE.window + n - 1, rk, rv)
+        r = o.temporal(frames[n - 1])
+        return r, o.read_ring()
+
+    (firsts, ring_a), (last, ring_b) = _parallel([first_frames, last_frame])
+    for j, r in enumerate(firsts):
+        compare_frame(SHAPE, stats, f"prefill frame {j}", int(tok[j]), None, tl[j], None, r)
+    compare_frame(SHAPE, stats, f"prefill frame {n - 1}", int(tok[n - 1]), None, tl[n - 1], None,
+                  last)
+    _kv_rows_match("prefill frames 0-1", rk, rv, ring_a[0], ring_a[1], [0, 1])
+    _kv_rows_match("prefill frame 63", rk, rv, ring_b[0], ring_b[1], [(SHAPE.window + n - 1) % SHAPE.window])
+    log(f"prefill 64 frames: {stats}")
+
+
+def test_dep_q8_full_step_b1(weights):
+    """The 8-substep depformer reading (dep_q = 8) at full size through the
+    step kernel: the first frames from the seeded prefill against the oracle
+    of the same reading; codes of substeps 8..15 are -1."""
+    shape = SHAPE.replace(dep_q=8)
+    ctx = M.moshi_create(cfg_of(shape, 1), weights)
+    assert M.moshi_uses_step_kernel(ctx)
+    om = oracle.Model(shape, weights)
+    w2 = wl.WORKLOADS[2]
+    slot = M.moshi_session_join(ctx)
+    k, v = wl.prefill_kv(shape, w2.seed("prefill"), 0, shape.window, threads=16)
+    M.moshi_session_prefill_kv(ctx, slot, k, v)
+    frames = wl.frames(shape, w2.seed("frames"), 0, 0, 3)
+    o = oracle.Session(om)
+    o.prefill(k, v)
+    stats = Stats()
+    n = shape.dep_steps
+    for t in range(3):
+        tok, codes = M.moshi_step(ctx, frames[t][None, :])
+        tl, al = M.moshi_read_logits(ctx)
+        assert (codes[0][n:] == -1).all()
+        r = o.step(frames[t], forced_text=int(tok[0]), forced_codes=codes[0])
+        r2 = dict(r, audio_logits=r["audio_logits"][:n], codes=r["codes"][:n],
+                  audio_margins=r["audio_margins"][:n])
+        compare_frame(shape.replace(n_substeps=n), stats, f"dep_q8 t={t}", int(tok[0]),
+                      codes[0][:n], tl[0], al[0][:n], r2)
+    M.moshi_destroy(ctx)
+    log(f"dep_q=8 full step: {stats}")
