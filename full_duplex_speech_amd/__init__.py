@@ -120,6 +120,7 @@ def lib():
             "moshi_time_kernels": ([vp, vp, i32, vp, vp, vp, i32], ctypes.c_int),
             "moshi_kernel_class_name": ([i32], ctypes.c_char_p),
             "moshi_uses_step_kernel": ([vp], i32),
+            "moshi_uses_dep_kernel": ([vp], i32),
             "moshi_strerror": ([ctypes.c_int], ctypes.c_char_p),
             "moshi_last_error": ([vp], ctypes.c_char_p),
         }
@@ -358,6 +359,11 @@ def moshi_read_hidden(ctx: Ctx):
 def moshi_uses_step_kernel(ctx: Ctx) -> bool:
     """True when a step runs as one persistent kernel (see include/moshi.h)."""
     return _check(lib().moshi_uses_step_kernel(ctx.h), ctx) == 1
+
+
+def moshi_uses_dep_kernel(ctx: Ctx) -> bool:
+    """True if the depformer runs as one persistent kernel for all slots."""
+    return _check(lib().moshi_uses_dep_kernel(ctx.h), ctx) == 1
 
 
 def moshi_kernel_class_name(c: int) -> str:

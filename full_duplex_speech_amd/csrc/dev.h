@@ -1471,6 +1471,9 @@ __device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int head
 #pragma unroll
     for (int k = 0; k < NH; ++k) {
       const int h = head0 + (h0 + k * NW < n_heads ? h0 + k * NW : 0);
+      // the slot's layer (workgroup-uniform: the base of a coherent buffer
+      // load) and the head within it
+      const T* lbase = (const T*)a.ring_k + (size_t)b * a.slot_stride + a.layer_off;
       const size_t base = (size_t)b * a.slot_stride + a.layer_off + (size_t)h * a.head_stride;
       const T* kbase = (const T*)a.ring_k + base;
       const T* vbase = (const T*)a.ring_v + base;
@@ -1479,8 +1482,10 @@ __device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int head
         const int j = p * KPW + kq;
         const int jc = j < nvalid ? j : 0;
         const uint32_t off = (uint32_t)(((size_t)jc * HD + kd * VEC) * sizeof(T));
-        if constexpr (C) kw[k][p] = ld16_coh(kbase, off);
-        else kw[k][p] = ld16((const char*)kbase + off);
+        if constexpr (C)
+          kw[k][p] = ld16_coh(lbase, off + (uint32_t)((size_t)h * a.head_stride * sizeof(T)));
+        else
+          kw[k][p] = ld16((const char*)kbase + off);
       }
 #pragma unroll
       for (int j = 0; j < DEP_MAX_KEYS; ++j) {
@@ -1545,6 +1550,273 @@ __device__ __forceinline__ void dep_attention(const AttnArgs& a, int b, int head
     }
   }
   __syncthreads();
+}
+
+// EPI_RESID with the residual rows already loaded (r): the same arithmetic as
+// epilogue<.., EPI_RESID, ..>.
+template <bool C>
+__device__ __forceinline__ void epilogue_resid(const GemmArgs& a, int tile, int g, int col,
+                                               const double* v, const double* r) {
+  const bool cok = col < a.B;
+  double ss = 0.0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = tile * 16 + 4 * g + i;
+    if (cok && row < a.N) {
+      const double xn = r[i] + v[i];
+      st_f64<C>(a.resid + (size_t)col * a.ldr + row, xn);
+      ss += xn * xn;
+    }
+  }
+  ss += shfl_xor_d(ss, 16);
+  ss += shfl_xor_d(ss, 32);
+  if (g == 0 && cok) st_f64<C>(a.ssq_out + (size_t)tile * a.B + col, ss);
+}
+
+// ---- operations of two or more sessions (per-operation kernels in
+// kernels.hip, and the multi-session depformer kernel in step.hip) ----------
+
+// One 16-row tile x NB 16-column blocks (columns col0 .. col0 + 16 NB - 1) of a
+// projection as fp64 MFMA 16x16x4 products.
+// A = 16 weight rows x 4 k (lane: row lane%16, k-slot lane/16), B = 4 k x 16
+// session columns (lane: column lane%16, same k-slot). A lane loads 16 bytes of
+// its row (VEC consecutive k) and of its column's input; element e of every
+// lane feeds MFMA e, so both operands map k-slot g to k0 + VEC*g + e.
+// The fp64 16x16 result puts row (lane/16) + 4i in element i of a lane, so A
+// row m carries tile row 4*(m%4) + m/4: element i of lane group g is then tile
+// row 4g + i, the layout the epilogues use.
+// Wave w of KW sums k-steps [w n / KW, (w+1) n / KW) in order; the waves'
+// sums are added in wave order by wave 0, which runs the epilogue. A column's
+// value therefore depends on KW and K only (not on NB, col0 or DB). DB:
+// double-buffered batches. C: X was written during the running kernel
+// (coherent loads). wpre (DB only; null = none): the wave's first batch of
+// weights, already loaded by gemm_tile_weights for this tile. The residual
+// epilogue's inputs are
+// requested before the products (by wave 0, which runs it). s_acc: KW * NB *
+// 64 f64x4 of LDS. Every thread of the 64 KW calls it; the caller
+// synchronises before reusing s_acc.
+constexpr int GEMM_U = 4;  // k-steps per batch
+
+// A lane's weight groups of the U k-steps from st of tile `tile` (zero past
+// its wave's k-range or the matrix).
+template <typename T, int KW, int EPI>
+__device__ __forceinline__ void gemm_tile_weights(const GemmArgs& a, int tile, int st_off,
+                                                  u32x4 (&wv)[GEMM_U]) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int KSTEP = 4 * VEC;
+  const int lane = tid() & 63, wave = tid() >> 6, r16 = lane & 15, g = lane >> 4;
+  bool rok;
+  const int wrow = tile_row<EPI>(tile, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
+  const T* wbase = (const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + g * VEC;
+  const int nsteps = (a.K + KSTEP - 1) / KSTEP;
+  const int s1 = ((wave + 1) * nsteps) / KW;
+  const int st = (wave * nsteps) / KW + st_off;
+#pragma unroll
+  for (int u = 0; u < GEMM_U; ++u) {
+    const int k0 = (st + u) * KSTEP + g * VEC;
+    const bool kok = (st + u < s1) && (k0 < a.K);
+    wv[u] = (kok && rok) ? ld16_stream(wbase + (size_t)(st + u) * KSTEP) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <typename T, int NB, int KW, int EPI, bool DB, bool C>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0, f64x4* s_acc,
+                                          const u32x4* wpre = nullptr) {
+  constexpr int VEC = VecOf<T>::N;
+  constexpr int KSTEP = 4 * VEC;
+  constexpr int U = GEMM_U;
+  const int lane = tid() & 63;
+  const int wave = tid() >> 6;
+  const int r16 = lane & 15;
+  const int g = lane >> 4;
+
+  bool rok;
+  const int wrow = tile_row<EPI>(tile, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
+  const T* wbase = (const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + g * VEC;
+  const int nsteps = (a.K + KSTEP - 1) / KSTEP;
+  const int s0 = (wave * nsteps) / KW;
+  const int s1 = ((wave + 1) * nsteps) / KW;
+
+  f64x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // the residual rows this lane's epilogue adds to (written before this operation)
+  double rpre[NB][4];
+  if constexpr (EPI == EPI_RESID) {
+    if (wave == 0)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = col0 + nb * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = tile * 16 + 4 * g + i;
+          rpre[nb][i] = (col < a.B && row < a.N) ? ld_f64<C>(a.resid + (size_t)col * a.ldr + row) : 0.0;
+        }
+      }
+  }
+  // batch of U k-steps starting at st: weights and input groups (the
+  // weights only where `w`)
+  auto load = [&](int st, u32x4 (&wv)[U], u32x4 (&xw)[U][NB], bool w = true) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int k0 = (st + u) * KSTEP + g * VEC;
+      const bool kok = (st + u < s1) && (k0 < a.K);
+      if (w) wv[u] = (kok && rok) ? ld16_stream(wbase + (size_t)(st + u) * KSTEP) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = col0 + nb * 16 + r16;
+        if constexpr (C)
+          xw[u][nb] = (kok && col < a.B)
+                          ? ld16_coh(a.X, (uint32_t)(((size_t)col * a.ldx + k0) * sizeof(T)))
+                          : u32x4{0u, 0u, 0u, 0u};
+        else
+          xw[u][nb] = (kok && col < a.B) ? ld16((const T*)a.X + (size_t)col * a.ldx + k0)
+                                         : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto compute = [&](const u32x4 (&wv)[U], const u32x4 (&xw)[U][NB]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      double wd[VEC];
+      widen<T>(wv[u], wd);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        double xd[VEC];
+        widen<T>(xw[u][nb], xd);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(wd[e], xd[e], acc[nb], 0, 0, 0);
+      }
+    }
+  };
+  if constexpr (DB) {
+    // the next batch is requested before this one is used
+    u32x4 wa[U], xa[U][NB], wb[U], xb[U][NB];
+    if (wpre != nullptr) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) wa[u] = wpre[u];
+    }
+    if (s0 < s1) load(s0, wa, xa, wpre == nullptr);
+    for (int st = s0; st < s1; st += 2 * U) {
+      if (st + U < s1) load(st + U, wb, xb);
+      compute(wa, xa);
+      if (st + U >= s1) break;
+      if (st + 2 * U < s1) load(st + 2 * U, wa, xa);
+      compute(wb, xb);
+    }
+  } else {
+    for (int st = s0; st < s1; st += U) {
+      u32x4 wv[U];
+      u32x4 xw[U][NB];
+      load(st, wv, xw);
+      compute(wv, xw);
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) s_acc[(wave * NB + nb) * 64 + lane] = acc[nb];
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    f64x4 sm = s_acc[nb * 64 + lane];
+    for (int w = 1; w < KW; ++w) sm += s_acc[(w * NB + nb) * 64 + lane];
+    const double v[4] = {sm[0], sm[1], sm[2], sm[3]};
+    if constexpr (EPI == EPI_RESID)
+      epilogue_resid<C>(a, tile, g, col0 + nb * 16 + r16, v, rpre[nb]);
+    else
+      epilogue<T, EPI, C>(a, tile, g, col0 + nb * 16 + r16, v);
+  }
+}
+
+// The MFMA path's input vector of column b: xn[b][k] = round(x[b][k] *
+// scale_b * g[k]) (PRO_NORM) or round(x[b][k]) (PRO_CAST). The scale comes
+// from threads [0, 256) exactly as rms_scale with 256 threads (the others add
+// nothing), so any workgroup of 256 or more threads gives the same bits.
+// `red` holds NTH / 64 doubles. Every thread of the workgroup calls it.
+template <typename T, int PRO, bool C, int NTH>
+__device__ __forceinline__ void norm_column(const GemmArgs& a, int b, double* red) {
+  static_assert(NTH >= 256, "the scale uses 256 threads");
+  constexpr int PF = 4;  // elements per thread requested before the scale is formed
+  const double* x = (const double*)a.X + (size_t)b * a.ldx;
+  T* out = (T*)a.xn_out + (size_t)b * a.K;
+  double xp[PF];
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int k = tid() + j * NTH;
+    xp[j] = k < a.K ? ld_f64<C>(x + k) : 0.0;
+  }
+  double rs = 1.0;
+  if constexpr (PRO == PRO_NORM) {
+    double s = 0.0;
+    if (tid() < 256)
+      for (int i = tid(); i < a.n_ssq; i += 256) s += ld_f64<C>(a.ssq + (size_t)i * a.B + b);
+    rs = rms_finish(s, a, red, 256);
+  }
+  auto put = [&](int k, double xv) {
+    const double v = (PRO == PRO_NORM) ? xv * rs * to_d(((const T*)a.gain)[k]) : xv;
+    store_rounded<T, C>(out + k, &v, 1);
+  };
+#pragma unroll
+  for (int j = 0; j < PF; ++j) {
+    const int k = tid() + j * NTH;
+    if (k < a.K) put(k, xp[j]);
+  }
+  for (int k = tid() + PF * NTH; k < a.K; k += NTH) put(k, ld_f64<C>(x + k));
+}
+
+// Depformer substep entry of rows bx*16 .. bx*16+15 and columns by*4 ..
+// by*4+3 by one wave (lane: row lane%16, column by*4 + lane/16):
+// y = (W_in[s] hidden) + E_s[previous token]. With prev_part the previous
+// head's per-tile argmax partials of the column are reduced over its 16 lanes
+// (or the forced token taken) and stored to prev by the items of row tile 0.
+// Sums of squares per ssq_rows rows, combined across lanes in a fixed order.
+template <typename T, bool C>
+__device__ __forceinline__ void entry_item(const EntryArgs& a, int bx, int by, int lane) {
+  const int r = lane & 15;
+  const int b = by * 4 + (lane >> 4);
+  const int row = bx * 16 + r;
+  int tok = 0;
+  if (a.prev_part != nullptr) {
+    double bv = -INFINITY;
+    int bi = 0x7fffffff;
+    if (b < a.B)
+      for (int i = r; i < a.prev_tiles; i += 16) {
+        const ArgPart p = unpack_part(ld_grp<C>(a.prev_part + (size_t)i * a.B + b));
+        if (arg_better(p.v, p.i, bv, bi)) {
+          bv = p.v;
+          bi = p.i;
+        }
+      }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) {
+      const double ov = shfl_xor_d(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (arg_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    tok = (bi < a.prev_n) ? bi : 0;
+    if (a.forced != nullptr && b < a.B) {
+      const int f = a.forced[(size_t)b * a.forced_stride + a.forced_col];
+      if (f >= 0) tok = f;
+    }
+    if (bx == 0 && r == 0 && b < a.B) st_i32<C>(a.prev + (size_t)b * a.prev_stride, tok);
+  } else if (b < a.B) {
+    tok = ld_i32<C>(a.prev + (size_t)b * a.prev_stride);
+    tok = tok < 0 ? 0 : tok;  // a free slot's token (never used) may read -1
+  }
+  double acc = 0.0;
+  if (b < a.B && row < a.D) {
+    acc = ld_f64<C>(a.pre + (size_t)b * a.ldpre + (size_t)a.s * a.D + row) +
+          to_d(((const T*)a.table)[(size_t)tok * a.D + row]);
+    st_f64<C>(a.y + (size_t)b * a.D + row, acc);
+  }
+  double ss = acc * acc;
+  for (int off = a.ssq_rows / 2; off > 0; off >>= 1) ss += shfl_xor_d(ss, off);
+  if (r % a.ssq_rows == 0 && b < a.B && row < a.D)
+    st_f64<C>(a.ssq_out + (size_t)(row / a.ssq_rows) * a.B + b, ss);
 }
 
 }  // namespace moshi

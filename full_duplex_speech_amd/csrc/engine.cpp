@@ -159,6 +159,15 @@ struct moshi_ctx {
   StepArgs* d_step_static = nullptr;
   std::string static_why;  // why there is no static variant
 
+  // persistent multi-session depformer kernel (capacity 2..64, an
+  // instantiated shape, no sampling); it shares d_abort's role
+  bool dep_multi = false;
+  DepMultiArgs* d_dm = nullptr;
+  DepMultiArgs dm_host{};
+  int dm_grid = 0;
+  size_t dm_lds = 0;
+  int dm_parity = 0;
+
   // kernel timing (eager launches bracketed by events); `dry` only records
   // the (class, bytes) sequence of a step without launching anything
   bool timing = false;
@@ -732,6 +741,81 @@ hipError_t prefill_chunk(moshi_ctx* c, int slot, int64_t p0, int m) {
 // Builds the kernel's argument block and weight-pointer tables in device
 // memory. Leaves c->persistent false when the shape or device does not allow
 // it (the per-operation kernels are used then).
+// The depformer's sections of a weight pointer table: [S * Ld][4] qkv, o,
+// gate_up, down of (substep, layer); [Ld][2] attn_norm, mlp_norm; [S]
+// previous-token tables; [S] heads.
+void append_dep_tables(const moshi_ctx* c, std::vector<const void*>& tab, int* o_dw, int* o_dn,
+                       int* o_de, int* o_dh) {
+  *o_dw = (int)tab.size();
+  for (int s = 0; s < c->S; ++s)
+    for (int l = 0; l < c->Ld; ++l) {
+      const int wi = s * c->Ld + l;
+      for (const void* p : {c->dep_qkv[wi], c->dep_o[wi], c->dep_gate_up[wi], c->dep_down[wi]})
+        tab.push_back(p);
+    }
+  *o_dn = (int)tab.size();
+  for (int l = 0; l < c->Ld; ++l) {
+    tab.push_back(c->dep_attn_norm[l]);
+    tab.push_back(c->dep_mlp_norm[l]);
+  }
+  *o_de = (int)tab.size();
+  for (int s = 0; s < c->S; ++s) tab.push_back(c->dep_emb[s]);
+  *o_dh = (int)tab.size();
+  for (int s = 0; s < c->S; ++s) tab.push_back(c->dep_head[s]);
+}
+
+// The multi-session depformer kernel: used at capacity 2..64 for an
+// instantiated shape unless sampling is on (the draws run per operation) or
+// MOSHI_DEP_MULTI=0 (the per-operation graph instead).
+int setup_dep_multi(moshi_ctx* c) {
+  const char* env = getenv("MOSHI_DEP_MULTI");
+  if (c->B < 2 || (env && env[0] == '0') || !dep_multi_supported(c->dtype, c->hdd) ||
+      c->S > DEP_MAX_KEYS_HOST || c->sampling)
+    return MOSHI_OK;
+  std::vector<const void*> tab;
+  int o_dw, o_dn, o_de, o_dh;
+  append_dep_tables(c, tab, &o_dw, &o_dn, &o_de, &o_dh);
+  const size_t lds = tab.size() * sizeof(void*);  // the pointer table
+  const int grid = dep_multi_grid(c->dtype, c->hdd, c->B, lds);
+  if (grid < 1) return MOSHI_OK;
+  void* d_tab = nullptr;
+  CKD(c, dalloc(c, &d_tab, tab.size() * sizeof(void*)));
+  CKD(c, hipMemcpy(d_tab, tab.data(), tab.size() * sizeof(void*), hipMemcpyHostToDevice));
+
+  DepMultiArgs A;
+  memset(&A, 0, sizeof(A));
+  A.d_in = d_in_args(c); A.d_qkv = d_qkv_args(c, 0, 0); A.d_o = d_o_args(c, 0, 0);
+  A.d_gu = d_gu_args(c, 0, 0); A.d_dn = d_dn_args(c, 0, 0); A.d_head = d_head_args(c, 0);
+  A.d_attn = d_attn_args(c, 0, 0);
+  EntryArgs& e = A.entry;
+  e.pre = c->pre; e.ldpre = c->S * c->Dd; e.prev_tiles = (c->Va + 15) / 16; e.prev_n = c->Va;
+  e.D = c->Dd; e.B = c->B; e.y = c->y; e.ssq_out = c->ssq_d; e.ssq_rows = ssq_rows(c);
+  A.S = c->S; A.S_run = c->S_run; A.Ld = c->Ld; A.Dd = c->Dd; A.Va = c->Va; A.B = c->B;
+  A.nch = c->NCH;
+  A.d_layer_elems = d_layer_elems(c);
+  A.dep_final_norm = dep_final_norm(c) ? 1 : 0;
+  A.ref_excl_at = (c->c.flags & MOSHI_FLAG_DEP_REF_RING) ? c->S_run - 1 : -1;
+  A.forced = c->d_forced; A.tokens = c->tokens; A.codes = c->codes; A.live = c->d_live;
+  A.apart = c->apart;
+  A.tab = (const void* const*)d_tab; A.n_tab = (int)tab.size();
+  A.o_dw = o_dw; A.o_dn = o_dn; A.o_de = o_de; A.o_dh = o_dh;
+  CKD(c, dalloc(c, (void**)&A.bar, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
+  CKD(c, hipMemset(A.bar, 0, 2 * STEP_BAR_WORDS * sizeof(unsigned)));
+  if (!c->d_abort) {
+    CKD(c, dalloc(c, (void**)&c->d_abort, sizeof(int)));
+    CKD(c, hipMemset(c->d_abort, 0, sizeof(int)));
+  }
+  A.abort = c->d_abort;
+  A.spin_limit = STEP_SPIN_LIMIT;
+  CKD(c, dalloc(c, (void**)&c->d_dm, sizeof(DepMultiArgs)));
+  CKD(c, hipMemcpy(c->d_dm, &A, sizeof(DepMultiArgs), hipMemcpyHostToDevice));
+  c->dm_host = A;
+  c->dm_grid = grid;
+  c->dm_lds = lds;
+  c->dep_multi = true;
+  return MOSHI_OK;
+}
+
 int setup_step(moshi_ctx* c) {
   const char* env = getenv("MOSHI_STEP_KERNEL");
   if (c->B != 1 || (env && env[0] == '0') || !step_supported(c->dtype, c->hd, c->hdd) ||
@@ -787,22 +871,8 @@ int setup_step(moshi_ctx* c) {
     for (const void* p : {c->attn_norm[l], c->qkv[l], c->wo[l], c->mlp_norm[l], c->gate_up[l],
                           c->down[l]})
       tab.push_back(p);
-  const size_t o_dw = tab.size();
-  for (int s = 0; s < c->S; ++s)
-    for (int l = 0; l < c->Ld; ++l) {
-      const int wi = s * c->Ld + l;
-      for (const void* p : {c->dep_qkv[wi], c->dep_o[wi], c->dep_gate_up[wi], c->dep_down[wi]})
-        tab.push_back(p);
-    }
-  const size_t o_dn = tab.size();
-  for (int l = 0; l < c->Ld; ++l) {
-    tab.push_back(c->dep_attn_norm[l]);
-    tab.push_back(c->dep_mlp_norm[l]);
-  }
-  const size_t o_de = tab.size();
-  for (int s = 0; s < c->S; ++s) tab.push_back(c->dep_emb[s]);
-  const size_t o_dh = tab.size();
-  for (int s = 0; s < c->S; ++s) tab.push_back(c->dep_head[s]);
+  int o_dw, o_dn, o_de, o_dh;
+  append_dep_tables(c, tab, &o_dw, &o_dn, &o_de, &o_dh);
 
   void* d_tab = nullptr;
   CKD(c, dalloc(c, &d_tab, tab.size() * sizeof(void*)));
@@ -819,8 +889,7 @@ int setup_step(moshi_ctx* c) {
   A.d_gu = d_gu_args(c, 0, 0); A.d_dn = d_dn_args(c, 0, 0); A.d_head = d_head_args(c, 0);
   A.d_attn = d_attn_args(c, 0, 0);
   A.tab = dt; A.n_tab = (int)tab.size();
-  A.o_tw = (int)o_tw; A.o_dw = (int)o_dw; A.o_dn = (int)o_dn; A.o_de = (int)o_de;
-  A.o_dh = (int)o_dh;
+  A.o_tw = (int)o_tw; A.o_dw = o_dw; A.o_dn = o_dn; A.o_de = o_de; A.o_dh = o_dh;
   A.wbuf_lds = (int)wbuf;
   // the pointer table goes to LDS after the scratch region
   lds = (lds + 15) / 16 * 16;
@@ -899,7 +968,7 @@ int launch_persistent(moshi_ctx* c, const int* frames, int* text_out, int* codes
 int check_abort(moshi_ctx* c, int flag) {
   if (flag) {
     c->failed = true;
-    c->err = "step kernel: a grid barrier timed out";
+    c->err = "persistent kernel: a grid barrier or flagged wait timed out";
     return MOSHI_E_DEVICE;
   }
   return MOSHI_OK;
@@ -924,11 +993,17 @@ hipError_t capture(moshi_ctx* c, hipError_t (*fn)(moshi_ctx*), hipGraphExec_t* o
 int ensure_graphs(moshi_ctx* c, bool temporal, bool dep) {
   if (!c->use_graphs || c->timing) return MOSHI_OK;
   if (temporal && !c->g_temporal) CKD(c, capture(c, enqueue_temporal, &c->g_temporal));
-  if (dep && !c->g_dep) CKD(c, capture(c, enqueue_depformer, &c->g_dep));
+  if (dep && !c->g_dep && !c->dep_multi) CKD(c, capture(c, enqueue_depformer, &c->g_dep));
   return MOSHI_OK;
 }
 
 int launch_part(moshi_ctx* c, bool temporal) {
+  if (!temporal && c->dep_multi && !c->timing) {
+    CKD(c, launch_dep_multi(c->dtype, c->hdd, c->B, c->d_dm, c->dm_parity, c->dm_grid, c->dm_lds,
+                            c->stream));
+    c->dm_parity ^= 1;
+    return MOSHI_OK;
+  }
   if (c->use_graphs && !c->timing) {
     CKD(c, hipGraphLaunch(temporal ? c->g_temporal : c->g_dep, c->stream));
   } else {
@@ -1038,6 +1113,9 @@ int run_step(moshi_ctx* c, const int32_t* frames, int32_t* text_token, int32_t* 
   } else {
     if ((rc = launch_part(c, true))) return rc;
     if (with_dep && (rc = launch_part(c, false))) return rc;
+    if (with_dep && c->dep_multi && !c->timing)
+      CKD(c, hipMemcpyAsync(&abort_flag, c->d_abort, sizeof(int), hipMemcpyDeviceToHost,
+                            c->stream));
   }
   CKD(c, hipMemcpyAsync(c->h_tokens, c->tokens, sizeof(int) * c->B, hipMemcpyDeviceToHost, c->stream));
   if (with_dep)
@@ -1301,6 +1379,85 @@ int time_step_phases(moshi_ctx* c, const int32_t* frames, int n_steps, std::vect
   return rc;
 }
 
+// Kernel timing with the multi-session depformer kernel: the temporal
+// step's kernels bracketed by events, the depformer kernel's phases from its
+// trace, each under the class of the per-operation kernel it replaces (a norm
+// phase under the projection it feeds, the last code under argmax_reduce),
+// with that path's byte counts.
+int time_dep_multi(moshi_ctx* c, const int32_t* frames, int n_steps, std::vector<double>& acc_ms,
+                   std::vector<double>& acc_b, std::vector<int64_t>& acc_n) {
+  int rate_khz = 0;
+  CKD(c, hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, c->device));
+  if (rate_khz <= 0) return fail(c, MOSHI_E_DEVICE, "no wall clock rate");
+  std::vector<int> phases{KC_D_INPROJ};
+  for (int s = 0; s < c->S_run; ++s) {
+    phases.push_back(KC_D_ENTRY);
+    for (int l = 0; l < c->Ld; ++l)
+      for (int k : {KC_D_QKV, KC_D_QKV, KC_D_ATTN, KC_D_O, KC_D_GATEUP, KC_D_GATEUP, KC_D_DOWN})
+        phases.push_back(k);
+    phases.push_back(KC_D_HEAD);
+    phases.push_back(KC_D_HEAD);
+  }
+  phases.push_back(KC_ARGMAX);
+  if (phases.size() + 1 > (size_t)STEP_TRACE_MAX) return fail(c, MOSHI_E_INVALID, "step too long to trace");
+  std::vector<double> dep_bytes(KC_COUNT, 0.0);
+  c->dry = true;
+  c->ev_class.clear();
+  c->ev_bytes.clear();
+  (void)enqueue_depformer(c);
+  c->dry = false;
+  for (size_t i = 0; i < c->ev_class.size(); ++i) dep_bytes[c->ev_class[i]] += c->ev_bytes[i];
+  void* d_trace = nullptr;
+  CKD(c, hipMalloc(&d_trace, STEP_TRACE_MAX * sizeof(uint64_t)));
+  std::vector<uint64_t> tr(phases.size() + 1);
+  int rc = MOSHI_OK;
+  for (int it = 0; it < n_steps && rc == MOSHI_OK; ++it) {
+    c->ev_used = 0;
+    c->ev_class.clear();
+    c->ev_bytes.clear();
+    if ((rc = upload_step_inputs(c, frames)) || (rc = upload_forced(c, nullptr))) break;
+    c->timing = true;
+    hipError_t e = enqueue_temporal(c);
+    c->timing = false;
+    if (e == hipSuccess)
+      e = launch_dep_multi(c->dtype, c->hdd, c->B, c->d_dm, c->dm_parity, c->dm_grid, c->dm_lds,
+                           c->stream, (uint64_t*)d_trace);
+    c->dm_parity ^= 1;
+    int abort_flag = 0;
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(tr.data(), d_trace, tr.size() * sizeof(uint64_t), hipMemcpyDeviceToHost,
+                         c->stream);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(&abort_flag, c->d_abort, sizeof(int), hipMemcpyDeviceToHost, c->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(c->stream);
+    if (e != hipSuccess) {
+      rc = device_fail(c, e, "depformer kernel trace");
+      break;
+    }
+    c->meta_ev_pending = false;
+    if ((rc = check_abort(c, abort_flag))) break;
+    c->slots.advance();
+    for (size_t i = 0; i < c->ev_class.size(); ++i) {
+      float t = 0.f;
+      if ((e = hipEventElapsedTime(&t, c->ev[2 * i], c->ev[2 * i + 1])) != hipSuccess) {
+        rc = device_fail(c, e, "hipEventElapsedTime");
+        break;
+      }
+      acc_ms[c->ev_class[i]] += t;
+      acc_b[c->ev_class[i]] += c->ev_bytes[i];
+      acc_n[c->ev_class[i]] += 1;
+    }
+    const double ms_per_tick = 1.0 / (double)rate_khz;
+    for (size_t k = 0; k < phases.size(); ++k) {
+      acc_ms[phases[k]] += (double)(tr[k + 1] - tr[k]) * ms_per_tick;
+      acc_n[phases[k]] += 1;
+    }
+    for (int k = 0; k < KC_COUNT; ++k) acc_b[k] += dep_bytes[k];
+  }
+  (void)hipFree(d_trace);
+  return rc;
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -1331,6 +1488,11 @@ const char* moshi_last_error(const moshi_ctx* ctx) { return ctx ? ctx->err.c_str
 int32_t moshi_uses_step_kernel(const moshi_ctx* ctx) {
   if (!ctx) return MOSHI_E_INVALID;
   return ctx->persistent ? 1 : 0;
+}
+
+int32_t moshi_uses_dep_kernel(const moshi_ctx* ctx) {
+  if (!ctx) return MOSHI_E_INVALID;
+  return ctx->dep_multi ? 1 : 0;
 }
 
 const char* moshi_kernel_class_name(int32_t c) {
@@ -1384,7 +1546,8 @@ int moshi_create(const moshi_config* cfg, const void* const* tensors, int32_t n_
     }
     c->own_stream = true;
   }
-  if ((rc = alloc_buffers(c)) || (rc = upload_weights(c, tensors)) || (rc = setup_step(c))) {
+  if ((rc = alloc_buffers(c)) || (rc = upload_weights(c, tensors)) || (rc = setup_step(c)) ||
+      (rc = setup_dep_multi(c))) {
     release(c);
     return rc;
   }
@@ -1460,11 +1623,18 @@ int moshi_test_set_spin_limit(moshi_ctx* c, int32_t limit) {
   int rc = check_ctx(c);
   if (rc) return rc;
   if (limit < 1) return fail(c, MOSHI_E_INVALID, "spin limit must be >= 1");
-  if (!c->persistent) return fail(c, MOSHI_E_INVALID, "no step kernel on this context");
-  c->step_host.spin_limit = limit;
-  c->step_host.ll_spin_limit = limit;
+  if (!c->persistent && !c->dep_multi)
+    return fail(c, MOSHI_E_INVALID, "no persistent kernel on this context");
   CKD(c, hipStreamSynchronize(c->stream));
-  CKD(c, hipMemcpy(c->d_step, &c->step_host, sizeof(StepArgs), hipMemcpyHostToDevice));
+  if (c->persistent) {
+    c->step_host.spin_limit = limit;
+    c->step_host.ll_spin_limit = limit;
+    CKD(c, hipMemcpy(c->d_step, &c->step_host, sizeof(StepArgs), hipMemcpyHostToDevice));
+  }
+  if (c->dep_multi) {
+    c->dm_host.spin_limit = limit;
+    CKD(c, hipMemcpy(c->d_dm, &c->dm_host, sizeof(DepMultiArgs), hipMemcpyHostToDevice));
+  }
   return MOSHI_OK;
 }
 
@@ -1508,7 +1678,7 @@ int moshi_sync(moshi_ctx* c) {
   if (rc) return rc;
   int bad = 0, abort_flag = 0;
   CKD(c, hipMemcpyAsync(&bad, c->d_err, sizeof(int), hipMemcpyDeviceToHost, c->stream));
-  if (c->persistent)
+  if (c->persistent || c->dep_multi)
     CKD(c, hipMemcpyAsync(&abort_flag, c->d_abort, sizeof(int), hipMemcpyDeviceToHost, c->stream));
   CKD(c, hipStreamSynchronize(c->stream));
   if ((rc = check_abort(c, abort_flag))) return rc;
@@ -1539,9 +1709,13 @@ int moshi_depformer_step(moshi_ctx* c, const void* hidden, const int32_t* text_i
   CKD(c, hipMemcpyAsync(c->tokens, c->h_tokens, sizeof(int) * c->B, hipMemcpyHostToDevice, c->stream));
   CKD(c, hipMemcpyAsync(c->hid, hidden, (size_t)c->B * c->D * c->esz, hipMemcpyHostToDevice, c->stream));
   if ((rc = launch_part(c, false))) return rc;
+  int abort_flag = 0;
+  if (c->dep_multi && !c->timing)
+    CKD(c, hipMemcpyAsync(&abort_flag, c->d_abort, sizeof(int), hipMemcpyDeviceToHost, c->stream));
   CKD(c, hipMemcpyAsync(c->h_codes, c->codes, sizeof(int) * c->B * c->S, hipMemcpyDeviceToHost, c->stream));
   CKD(c, hipStreamSynchronize(c->stream));
   c->meta_ev_pending = false;
+  if ((rc = check_abort(c, abort_flag))) return rc;
   if (audio_codes)
     for (int b = 0; b < c->B; ++b)
       for (int s = 0; s < c->S; ++s)
@@ -1696,8 +1870,9 @@ int moshi_time_kernels(moshi_ctx* c, const int32_t* frames, int32_t n_steps, dou
   if ((rc = validate_frames(c, frames))) return rc;
   std::vector<double> acc_ms(KC_COUNT, 0.0), acc_b(KC_COUNT, 0.0);
   std::vector<int64_t> acc_n(KC_COUNT, 0);
-  if (c->persistent) {
-    rc = time_step_phases(c, frames, n_steps, acc_ms, acc_b, acc_n);
+  if (c->persistent || c->dep_multi) {
+    rc = c->persistent ? time_step_phases(c, frames, n_steps, acc_ms, acc_b, acc_n)
+                       : time_dep_multi(c, frames, n_steps, acc_ms, acc_b, acc_n);
     if (rc) return rc;
     for (int k = 0; k < n_classes && k < KC_COUNT; ++k) {
       if (ms) ms[k] = acc_ms[k];

@@ -230,6 +230,45 @@ struct StepArgs {
   // creation, step_ll_words() words of 8 bytes
   uint64_t* ll;
 };
+// Argument block of the multi-session depformer kernel (step.hip; capacity
+// 2..64): the per-operation argument blocks of substep 0, layer 0 (for B
+// columns) as templates, completed per (substep, layer) from the pointer
+// table, whose sections are as in StepArgs: o_dw [S * Ld][4] qkv, o, gate_up,
+// down; o_dn [Ld][2] attn_norm, mlp_norm; o_de [S] previous-token tables;
+// o_dh [S] heads.
+struct DepMultiArgs {
+  GemmArgs d_in, d_qkv, d_o, d_gu, d_dn, d_head;
+  AttnArgs d_attn;
+  EntryArgs entry;
+  int S, S_run, Ld, Dd, Va, B, nch;
+  int64_t d_layer_elems;
+  int dep_final_norm;
+  int ref_excl_at;      // substep whose depformer attention masks entry 0 (-1: none)
+  const int* forced;    // [B][nch]
+  int* tokens;          // [B] the text tokens (substep 0's input)
+  int* codes;           // [B][S]
+  const int* live;
+  ArgPart* apart;
+  const void* const* tab;
+  int n_tab, o_dw, o_dn, o_de, o_dh;
+  unsigned* bar;        // 2 sets of STEP_BAR_WORDS barrier counters
+  int* abort;
+  int spin_limit;
+};
+bool dep_multi_supported(int dtype, int hdd);
+// Workgroups of the multi-session depformer kernel resident at once (one per
+// CU), 0 if it cannot run.
+int dep_multi_grid(int dtype, int hdd, int B, size_t lds_bytes);
+// One cooperative launch of the depformer of every live slot (B columns).
+// `trace`, if set, receives the wall clock (100 MHz) when the grid has
+// started, after every grid barrier, and when workgroup 0 ends, as seen by
+// workgroup 0: one entry per phase boundary (the phases: the input
+// projections; per substep run its entry, per layer the q/k/v norm, q/k/v,
+// attention, output projection, gate/up norm, gate/up, down; its head's
+// norm and head; then the last code).
+hipError_t launch_dep_multi(int dtype, int hdd, int B, const DepMultiArgs* dP, int parity, int nwg,
+                            size_t lds_bytes, hipStream_t st, uint64_t* trace = nullptr);
+
 // One-session projections run 8 waves per workgroup; each wave owns 2 rows
 // of a 16-row tile, and the residual epilogue writes one sum-of-squares
 // partial per wave (every 2 rows). With two or more sessions the partials are

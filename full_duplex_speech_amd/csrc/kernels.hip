@@ -50,111 +50,19 @@ __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
 // Two or more sessions: fp64 MFMA 16x16x4 tiles
 // ---------------------------------------------------------------------------
 
-// A = 16 weight rows x 4 k (lane: row lane%16, k-slot lane/16), B = 4 k x 16
-// session columns (lane: column lane%16, same k-slot). A lane loads 16 bytes of
-// its row (VEC consecutive k) and of its column's input; element e of every
-// lane feeds MFMA e, so both operands map k-slot g to k0 + VEC*g + e.
-// The fp64 16x16 result puts row (lane/16) + 4i in element i of a lane, so A
-// row m carries tile row 4*(m%4) + m/4: element i of lane group g is then tile
-// row 4g + i, the layout the epilogues use.
+// 16 weight rows x 16 NB session columns per workgroup (see gemm_tile).
 template <typename T, int NB, int KW, int EPI, bool DB>
 __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
-  constexpr int VEC = VecOf<T>::N;
-  constexpr int KSTEP = 4 * VEC;
-  constexpr int U = 4;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r16 = lane & 15;
-  const int g = lane >> 4;
-  const int tile = blockIdx.x;
-  __shared__ f64x4 s_acc[KW][NB][64];
-
-  bool rok;
-  const int wrow = tile_row<EPI>(tile, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
-  const T* wbase = (const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + g * VEC;
-  const int nsteps = (a.K + KSTEP - 1) / KSTEP;
-  const int s0 = (wave * nsteps) / KW;
-  const int s1 = ((wave + 1) * nsteps) / KW;
-
-  f64x4 acc[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f64x4{0.0, 0.0, 0.0, 0.0};
-  // batch of U k-steps starting at st: weights and input groups
-  auto load = [&](int st, u32x4 (&wv)[U], u32x4 (&xw)[U][NB]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int k0 = (st + u) * KSTEP + g * VEC;
-      const bool kok = (st + u < s1) && (k0 < a.K);
-      wv[u] = (kok && rok) ? ld16_stream(wbase + (size_t)(st + u) * KSTEP) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        const int col = nb * 16 + r16;
-        xw[u][nb] = (kok && col < a.B) ? ld16((const T*)a.X + (size_t)col * a.ldx + k0)
-                                       : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto compute = [&](const u32x4 (&wv)[U], const u32x4 (&xw)[U][NB]) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      double wd[VEC];
-      widen<T>(wv[u], wd);
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        double xd[VEC];
-        widen<T>(xw[u][nb], xd);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(wd[e], xd[e], acc[nb], 0, 0, 0);
-      }
-    }
-  };
-  if constexpr (DB) {
-    // double-buffered: the next batch is requested before this one is used
-    u32x4 wa[U], xa[U][NB], wb[U], xb[U][NB];
-    if (s0 < s1) load(s0, wa, xa);
-    for (int st = s0; st < s1; st += 2 * U) {
-      if (st + U < s1) load(st + U, wb, xb);
-      compute(wa, xa);
-      if (st + U >= s1) break;
-      if (st + 2 * U < s1) load(st + 2 * U, wa, xa);
-      compute(wb, xb);
-    }
-  } else {
-    for (int st = s0; st < s1; st += U) {
-      u32x4 wv[U];
-      u32x4 xw[U][NB];
-      load(st, wv, xw);
-      compute(wv, xw);
-    }
-  }
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) s_acc[wave][nb][lane] = acc[nb];
-  __syncthreads();
-  if (wave != 0) return;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    f64x4 s = s_acc[0][nb][lane];
-    for (int w = 1; w < KW; ++w) s += s_acc[w][nb][lane];
-    const double v[4] = {s[0], s[1], s[2], s[3]};
-    epilogue<T, EPI, false>(a, tile, g, nb * 16 + r16, v);
-  }
+  __shared__ f64x4 s_acc[KW * NB * 64];
+  gemm_tile<T, NB, KW, EPI, DB, false>(a, blockIdx.x, 0, s_acc);
 }
 
 // Input vectors for the MFMA path: xn[b][k] = round(x[b][k] * scale_b * g[k])
 // (PRO_NORM) or round(x[b][k]) (PRO_CAST); one workgroup per column.
 template <typename T, int PRO>
 __global__ __launch_bounds__(256) void norm_kernel(GemmArgs a) {
-  const int b = blockIdx.x;
   __shared__ double s_tmp[4];
-  double rs = 1.0;
-  if constexpr (PRO == PRO_NORM) rs = rms_scale<false>(a, b, s_tmp, 256);
-  const double* x = (const double*)a.X + (size_t)b * a.ldx;
-  T* out = (T*)a.xn_out + (size_t)b * a.K;
-  for (int k = threadIdx.x; k < a.K; k += 256) {
-    const double v = (PRO == PRO_NORM) ? x[k] * rs * to_d(((const T*)a.gain)[k]) : x[k];
-    out[k] = round_to<T>(v);
-  }
+  norm_column<T, PRO, false, 256>(a, blockIdx.x, s_tmp);
 }
 
 // Greedy token of column blockIdx.x from per-tile (max, index) partials.
@@ -518,53 +426,10 @@ __global__ __launch_bounds__(64) void embed_kernel(EmbedArgs a) {
   if (r % a.ssq_rows == 0 && b < a.B && row < a.D) a.ssq_out[(size_t)(row / a.ssq_rows) * a.B + b] = ss;
 }
 
-// Depformer substep entry: y = (W_in[s] hidden) + E_s[previous token].
+// Depformer substep entry (see entry_item): one wave per 16 rows x 4 columns.
 template <typename T>
 __global__ __launch_bounds__(64) void entry_kernel(EntryArgs a) {
-  const int r = threadIdx.x & 15;
-  const int b = blockIdx.y * 4 + (threadIdx.x >> 4);
-  const int row = blockIdx.x * 16 + r;
-  int tok = 0;
-  if (a.prev_part != nullptr) {
-    // reduce the previous head's partials of column b over the 16 lanes of this column
-    double bv = -INFINITY;
-    int bi = 0x7fffffff;
-    if (b < a.B)
-      for (int i = r; i < a.prev_tiles; i += 16) {
-        const ArgPart p = a.prev_part[(size_t)i * a.B + b];
-        if (arg_better(p.v, p.i, bv, bi)) {
-          bv = p.v;
-          bi = p.i;
-        }
-      }
-#pragma unroll
-    for (int off = 8; off > 0; off >>= 1) {
-      const double ov = shfl_xor_d(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (arg_better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    tok = (bi < a.prev_n) ? bi : 0;
-    if (a.forced != nullptr && b < a.B) {
-      const int f = a.forced[(size_t)b * a.forced_stride + a.forced_col];
-      if (f >= 0) tok = f;
-    }
-    if (blockIdx.x == 0 && r == 0 && b < a.B) a.prev[(size_t)b * a.prev_stride] = tok;
-  } else if (b < a.B) {
-    tok = a.prev[(size_t)b * a.prev_stride];
-    tok = tok < 0 ? 0 : tok;  // a free slot's token (never used) may read -1
-  }
-  double acc = 0.0;
-  if (b < a.B && row < a.D) {
-    acc = a.pre[(size_t)b * a.ldpre + (size_t)a.s * a.D + row] +
-          to_d(((const T*)a.table)[(size_t)tok * a.D + row]);
-    a.y[(size_t)b * a.D + row] = acc;
-  }
-  double ss = acc * acc;
-  for (int off = a.ssq_rows / 2; off > 0; off >>= 1) ss += shfl_xor_d(ss, off);
-  if (r % a.ssq_rows == 0 && b < a.B && row < a.D) a.ssq_out[(size_t)(row / a.ssq_rows) * a.B + b] = ss;
+  entry_item<T, false>(a, blockIdx.x, blockIdx.y, threadIdx.x);
 }
 
 // End of a temporal step: every live slot moves to its next position.

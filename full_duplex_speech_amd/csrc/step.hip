@@ -1343,6 +1343,280 @@ int max_grid_t(size_t lds) {
   return per_cu > 0 ? ncu : 0;  // one workgroup per CU
 }
 
+// ===========================================================================
+// The depformer of two or more sessions as one persistent kernel
+// ===========================================================================
+// At 2..64 sessions every depformer operation is a small MFMA product (a few
+// MB of weights, 16-64 columns), and the ~45 dependent operations per substep
+// cost a kernel launch each (~700 per frame). Here they are grid-stride
+// phases of one cooperative launch, separated by the grid barrier above. Each
+// phase runs the per-operation kernels' device code (gemm_tile, entry_item,
+// dep_attention) with the thread counts its arithmetic depends on (KW waves
+// per projection tile), so every value is bit-identical to the per-operation
+// path. Data written in one phase and read in a later one use coherent
+// accesses (C = true). (Building each tile's normed input itself instead of
+// a norm phase was measured slower: every workgroup then re-reads its
+// columns' fp64 residual, ~24 MB of coherent loads per phase at 16 sessions.)
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
+
+template <typename T, int HDD, int KW>
+__global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* P, int parity,
+                                                            uint64_t* trace) {
+  constexpr int NTH = 64 * KW;
+  constexpr int NW = KW;
+  extern __shared__ __align__(16) unsigned char s_dyn[];  // the weight pointer table
+  __shared__ __align__(16) DepMultiArgs sA;
+  __shared__ f64x4 s_acc[KW * 64];
+  __shared__ double s_red[NW];
+  __shared__ double s_v[NW];
+  __shared__ int s_i[NW];
+  {
+    const uint32_t* src = (const uint32_t*)P;
+    uint32_t* dst = (uint32_t*)&sA;
+    for (int i = tid(); i < (int)(sizeof(DepMultiArgs) / 4); i += NTH) dst[i] = ldg(src + i);
+  }
+  __syncthreads();
+  const DepMultiArgs& A = sA;
+  const void** s_tab = (const void**)s_dyn;
+  {
+    const void* const* tab = uni(A.tab);
+    const int n_tab = uni(A.n_tab);
+    for (int i = tid(); i < n_tab; i += NTH) s_tab[i] = ldg(tab + i);
+  }
+  __syncthreads();
+  auto tab = [&](int i) { return uni(s_tab[i]); };
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int S = uni(A.S), S_run = uni(A.S_run), Ld = uni(A.Ld), Va = uni(A.Va), B = uni(A.B);
+  const int o_dw = uni(A.o_dw), o_dn = uni(A.o_dn), o_de = uni(A.o_de), o_dh = uni(A.o_dh);
+  const int64_t d_lel = uni(A.d_layer_elems);
+  const int* const live = uni(A.live);
+  const int* const forced = uni(A.forced);
+  const int nch = uni(A.nch);
+  // the input projections' first weight batch, requested before the start barrier
+  u32x4 wpf[GEMM_U];
+  {
+    const GemmArgs a = uni(A.d_in);
+    const int nt = n_tiles_of(EPI_STORE, a.N);
+    if (wg < nt * ((a.B + 15) / 16)) gemm_tile_weights<T, KW, EPI_STORE>(a, wg % nt, 0, wpf);
+  }
+  Grid g;
+  if (grid_init(g, uni(A.bar), parity, uni(A.abort), uni(A.spin_limit), trace)) return;
+#define DM_SYNC()               \
+  do {                          \
+    if (grid_sync(g)) return;   \
+  } while (0)
+
+  // projection tiles: (row tile, 16-column block); the blocks of one tile are
+  // nt items apart, so with nt a multiple of 8 they run on the same XCD and
+  // share its L2 copy of the tile's weights. The first item's first weight
+  // batch was requested during the barrier before the phase (sync_pf).
+  auto gemm_phase = [&](auto epi_c, const GemmArgs& a) {
+    constexpr int EPI = decltype(epi_c)::value;
+    const int nt = n_tiles_of(EPI, a.N), ncb = (a.B + 15) / 16;
+    for (int item = wg; item < nt * ncb; item += nwg) {
+      gemm_tile<T, 1, KW, EPI, true, true>(a, item % nt, (item / nt) * 16, s_acc,
+                                           item == wg ? wpf : nullptr);
+      __syncthreads();
+    }
+  };
+  // grid barrier; in between its two halves this workgroup requests the first
+  // weight batch of its first tile of the projection `next` (weights do not
+  // depend on the phase that ends). True: leave (abort).
+  auto sync_pf = [&](auto epi_c, const GemmArgs& next) {
+    constexpr int EPI = decltype(epi_c)::value;
+    drain_stores();
+    __syncthreads();
+    const unsigned old = grid_arrive(g);
+    const int nt = n_tiles_of(EPI, next.N);
+    if (wg < nt * ((next.B + 15) / 16)) gemm_tile_weights<T, KW, EPI>(next, wg % nt, 0, wpf);
+    return grid_wait(g, old);
+  };
+  // rounded (normed) input vectors, one column per workgroup; the projection
+  // then reads them as its input
+  auto norm_phase = [&](auto pro_c, const GemmArgs& a) {
+    constexpr int PRO = decltype(pro_c)::value;
+    for (int b = wg; b < a.B; b += nwg) norm_column<T, PRO, true, NTH>(a, b, s_red);
+  };
+  auto normed = [&](GemmArgs a) {
+    a.X = a.xn_out;
+    a.ldx = a.K;
+    return a;
+  };
+  auto d_qkv = [&](int s, int l) {
+    GemmArgs a = uni(A.d_qkv);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 0);
+    a.gain = tab(o_dn + l * 2 + 0);
+    a.scalar_widx = s;
+    a.layer_off = (int64_t)l * d_lel;
+    return a;
+  };
+  auto d_o = [&](int s, int l) {
+    GemmArgs a = uni(A.d_o);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 1);
+    return a;
+  };
+  auto d_gu = [&](int s, int l) {
+    GemmArgs a = uni(A.d_gu);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 2);
+    a.gain = tab(o_dn + l * 2 + 1);
+    return a;
+  };
+  auto d_dn = [&](int s, int l) {
+    GemmArgs a = uni(A.d_dn);
+    a.W = tab(o_dw + (s * Ld + l) * 4 + 3);
+    return a;
+  };
+  auto d_head = [&](int s) {
+    GemmArgs a = uni(A.d_head);  // with the final norm: its gain and sums of squares set
+    a.W = tab(o_dh + s);
+    a.logits += (size_t)s * Va;
+    return a;
+  };
+  const bool final_norm = uni(A.dep_final_norm) != 0;
+  const int ref_excl_at = uni(A.ref_excl_at);
+
+  // ---- input projections of every substep run ----
+  gemm_phase(IntC<EPI_STORE>{}, uni(A.d_in));
+  DM_SYNC();
+  for (int s = 0; s < S_run; ++s) {
+    {  // entry: y = pre[s] + E_s[previous token]; from s = 1 on the previous
+       // head's partials are reduced here (or the forced code taken) and code
+       // s - 1 is stored
+      EntryArgs e = uni(A.entry);
+      e.s = s;
+      e.table = tab(o_de + s);
+      e.prev = s == 0 ? uni(A.tokens) : uni(A.codes) + (s - 1);
+      e.prev_stride = s == 0 ? 1 : S;
+      e.prev_part = s == 0 ? nullptr : uni(A.apart);
+      e.forced = s == 0 ? nullptr : forced;
+      e.forced_stride = nch;
+      e.forced_col = s;
+      const int nbx = (e.D + 15) / 16, nby = (e.B + 3) / 4;
+      for (int item = wg * NW + (tid() >> 6); item < nbx * nby; item += nwg * NW)
+        entry_item<T, true>(e, item % nbx, item / nbx, tid() & 63);
+    }
+    DM_SYNC();
+    for (int l = 0; l < Ld; ++l) {
+      norm_phase(IntC<PRO_NORM>{}, d_qkv(s, l));
+      if (sync_pf(IntC<EPI_QKV>{}, d_qkv(s, l))) return;
+      gemm_phase(IntC<EPI_QKV>{}, normed(d_qkv(s, l)));
+      DM_SYNC();
+      {  // causal attention over substeps 0..s, NW heads of one slot per item
+        AttnArgs at = uni(A.d_attn);
+        at.layer_off = (int64_t)l * d_lel;
+        const int Hd = at.n_heads;
+        const int nhc = (Hd + NW - 1) / NW;
+        for (int item = wg; item < B * nhc; item += nwg) {
+          const int b = item / nhc, h0 = (item % nhc) * NW;
+          if (!ldg(live + b)) continue;
+          dep_attention<T, HDD, NTH, true, 1>(at, b, h0, Hd - h0 < NW ? Hd - h0 : NW, s + 1,
+                                              s == ref_excl_at ? 0 : -1);
+        }
+      }
+      if (sync_pf(IntC<EPI_RESID>{}, d_o(s, l))) return;
+      gemm_phase(IntC<EPI_RESID>{}, d_o(s, l));
+      DM_SYNC();
+      norm_phase(IntC<PRO_NORM>{}, d_gu(s, l));
+      if (sync_pf(IntC<EPI_SWIGLU>{}, d_gu(s, l))) return;
+      gemm_phase(IntC<EPI_SWIGLU>{}, normed(d_gu(s, l)));
+      if (sync_pf(IntC<EPI_RESID>{}, d_dn(s, l))) return;
+      gemm_phase(IntC<EPI_RESID>{}, d_dn(s, l));
+      DM_SYNC();
+    }
+    // head s on the rounded residual, or with the final-norm reading on its RMSNorm
+    if (final_norm)
+      norm_phase(IntC<PRO_NORM>{}, d_head(s));
+    else
+      norm_phase(IntC<PRO_CAST>{}, d_head(s));
+    if (sync_pf(IntC<EPI_ARGMAX>{}, d_head(s))) return;
+    gemm_phase(IntC<EPI_ARGMAX>{}, normed(d_head(s)));
+    DM_SYNC();
+  }
+#undef DM_SYNC
+  // ---- the last code (forced if asked); free slots and substeps not run read -1 ----
+  {
+    const ArgPart* ap = uni(A.apart);
+    int* codes = uni(A.codes);
+    int* tokens = uni(A.tokens);
+    const int nt = (Va + 15) / 16;
+    for (int b = wg; b < B; b += nwg) {
+      double bv = -INFINITY;
+      int bi = 0x7fffffff;
+      for (int i = tid(); i < nt; i += NTH) {
+        const ArgPart p = unpack_part(ld_grp<true>(ap + (size_t)i * B + b));
+        if (arg_better(p.v, p.i, bv, bi)) {
+          bv = p.v;
+          bi = p.i;
+        }
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) {
+        const double ov = shfl_xor_d(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (arg_better(ov, oi, bv, bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if ((tid() & 63) == 0) {
+        s_v[tid() >> 6] = bv;
+        s_i[tid() >> 6] = bi;
+      }
+      __syncthreads();
+      const bool lv = ldg(live + b) != 0;
+      if (tid() == 0) {
+        for (int w = 1; w < NW; ++w)
+          if (arg_better(s_v[w], s_i[w], bv, bi)) {
+            bv = s_v[w];
+            bi = s_i[w];
+          }
+        int r = bi < Va ? bi : 0;
+        if (forced != nullptr) {
+          const int f = ldg(forced + (size_t)b * nch + S_run);
+          if (f >= 0) r = f;
+        }
+        *(MOSHI_GLB int*)(codes + (size_t)b * S + S_run - 1) = lv ? r : -1;
+        if (!lv) *(MOSHI_GLB int*)(tokens + b) = -1;
+      }
+      for (int k = tid(); k < S; k += NTH)
+        if (!lv || k >= S_run) *(MOSHI_GLB int*)(codes + (size_t)b * S + k) = -1;
+      __syncthreads();
+    }
+  }
+  if (trace != nullptr && wg == 0 && tid() == 0)
+    *(MOSHI_GLB uint64_t*)(trace + g.idx + 1) = wall_clock64();
+}
+
+template <typename T, int HDD, int KW>
+int dep_multi_grid_t(size_t lds) {
+  int per_cu = 0, dev = 0, ncu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, dep_multi_kernel<T, HDD, KW>, 64 * KW,
+                                                   lds) != hipSuccess)
+    return 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  // one workgroup of 8 waves per CU; two of 4 waves where they fit
+  const int want = KW == 4 ? 2 : 1;
+  return per_cu < 1 ? 0 : ncu * (per_cu < want ? per_cu : want);
+}
+
+template <typename T, int HDD, int KW>
+hipError_t launch_dep_multi_t(const DepMultiArgs* dP, int parity, int nwg, size_t lds,
+                              hipStream_t st, uint64_t* trace) {
+  void* args[] = {(void*)&dP, (void*)&parity, (void*)&trace};
+  return hipLaunchCooperativeKernel((const void*)dep_multi_kernel<T, HDD, KW>, dim3(nwg),
+                                    dim3(64 * KW), args, (unsigned)lds, st);
+}
+
+// Waves per projection tile: the per-operation path's (8 up to 32 sessions,
+// 4 at 33..64; see launch_gemm).
+int dep_multi_kw(int B) { return B <= 32 ? 8 : 4; }
+
 }  // namespace
 
 // Instantiated shapes: bf16 with head dims 128 / 64 (PersonaPlex), fp32 with
@@ -1367,6 +1641,32 @@ hipError_t launch_step(int dtype, int hd, int hdd, const StepArgs* dP, const int
   if (dtype == DT_F32 && hd == 64 && hdd == 32)
     return launch_t<float, 64, 32>(dP, frames, text_out, codes_out, parity, seq, nwg, lds, st,
                                      trace);
+  return hipErrorInvalidValue;
+}
+
+// Instantiated: bf16 with depformer head dim 64, fp32 with 32.
+bool dep_multi_supported(int dtype, int hdd) {
+  return (dtype == DT_BF16 && hdd == 64) || (dtype == DT_F32 && hdd == 32);
+}
+
+int dep_multi_grid(int dtype, int hdd, int B, size_t lds) {
+  const int kw = dep_multi_kw(B);
+  if (dtype == DT_BF16 && hdd == 64)
+    return kw == 8 ? dep_multi_grid_t<__bf16, 64, 8>(lds) : dep_multi_grid_t<__bf16, 64, 4>(lds);
+  if (dtype == DT_F32 && hdd == 32)
+    return kw == 8 ? dep_multi_grid_t<float, 32, 8>(lds) : dep_multi_grid_t<float, 32, 4>(lds);
+  return 0;
+}
+
+hipError_t launch_dep_multi(int dtype, int hdd, int B, const DepMultiArgs* dP, int parity, int nwg,
+                            size_t lds, hipStream_t st, uint64_t* trace) {
+  const int kw = dep_multi_kw(B);
+  if (dtype == DT_BF16 && hdd == 64)
+    return kw == 8 ? launch_dep_multi_t<__bf16, 64, 8>(dP, parity, nwg, lds, st, trace)
+                   : launch_dep_multi_t<__bf16, 64, 4>(dP, parity, nwg, lds, st, trace);
+  if (dtype == DT_F32 && hdd == 32)
+    return kw == 8 ? launch_dep_multi_t<float, 32, 8>(dP, parity, nwg, lds, st, trace)
+                   : launch_dep_multi_t<float, 32, 4>(dP, parity, nwg, lds, st, trace);
   return hipErrorInvalidValue;
 }
 

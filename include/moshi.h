@@ -356,6 +356,10 @@ int moshi_read_hidden(moshi_ctx* ctx, float* hidden);
  * c < n_classes: the summed device time in ms (ms[c]), the launch count
  * (launches[c]) and the algorithmic bytes moved (bytes[c]: weights read once,
  * K/V attended and written). Class names: moshi_kernel_class_name(c).
+ * Where a persistent kernel runs (moshi_uses_step_kernel or
+ * moshi_uses_dep_kernel) its operations are instead timed from workgroup 0's
+ * clock at each grid barrier or hand-off, under the class of the kernel each
+ * replaces, and launches[c] counts those phases.
  * Returns the number of classes (>= 0) or an error. */
 int moshi_time_kernels(moshi_ctx* ctx, const int32_t* frames, int32_t n_steps, double* ms,
                        int64_t* launches, double* bytes, int32_t n_classes);
@@ -368,12 +372,21 @@ const char* moshi_kernel_class_name(int32_t c);
  * operation; the results are identical. Negative on a NULL context. */
 int32_t moshi_uses_step_kernel(const moshi_ctx* ctx);
 
-/* Test hook of the step kernel's bounded waits (the failure path that keeps
- * a lost hand-off from hanging the GPU): every later launch on this context
+/* 1 if the depformer of every step (the 16 substeps of "vLLM-Omni recipe:
+ * PersonaPlex", "Architecture") runs as one persistent kernel for all slots:
+ * capacity 2..64 with a supported shape and without MOSHI_FLAG_SAMPLING,
+ * unless the environment variable MOSHI_DEP_MULTI=0 was set at creation;
+ * 0 if it runs one kernel per operation. The results are identical.
+ * Negative on a NULL context. */
+int32_t moshi_uses_dep_kernel(const moshi_ctx* ctx);
+
+/* Test hook of the persistent kernels' bounded waits (the failure path that
+ * keeps a lost hand-off from hanging the GPU): every later launch of the step
+ * kernel or of the multi-session depformer kernel on this context
  * gives up after `limit` polls (>= 1) of a grid barrier or flagged input,
  * raises the context's abort flag, and every workgroup leaves; the call then
  * fails with MOSHI_E_DEVICE and the context stays failed. MOSHI_E_INVALID if
- * the context does not use the step kernel. */
+ * the context uses neither. */
 int moshi_test_set_spin_limit(moshi_ctx* ctx, int32_t limit);
 
 /* Static text of a status code. */
