@@ -1586,19 +1586,19 @@ __device__ __forceinline__ void epilogue_resid(const GemmArgs& a, int tile, int 
 // row m carries tile row 4*(m%4) + m/4: element i of lane group g is then tile
 // row 4g + i, the layout the epilogues use.
 // Wave w of KW sums k-steps [w n / KW, (w+1) n / KW) in order; the waves'
-// sums are added in wave order by wave 0, which runs the epilogue. A column's
+// sums are added in wave order by wave 0, which runs the epilogue. (Two
+// accumulator chains per wave were measured slower.) A column's
 // value therefore depends on KW and K only (not on NB, col0 or DB). DB:
 // double-buffered batches. C: X was written during the running kernel
 // (coherent loads). wpre (DB only; null = none): the wave's first batch of
 // weights, already loaded by gemm_tile_weights for this tile. The residual
-// epilogue's inputs are
-// requested before the products (by wave 0, which runs it). s_acc: KW * NB *
-// 64 f64x4 of LDS. Every thread of the 64 KW calls it; the caller
-// synchronises before reusing s_acc.
+// epilogue's inputs are requested before the products (by wave 0, which runs
+// it). s_acc: KW * NB * 64 f64x4 of LDS. Every thread of the 64 KW calls it;
+// the caller synchronises before reusing s_acc.
 constexpr int GEMM_U = 4;  // k-steps per batch
 
 // A lane's weight groups of the U k-steps from st of tile `tile` (zero past
-// its wave's k-range or the matrix).
+// its wave's k-range or the matrix; rows past N may read anything).
 template <typename T, int KW, int EPI>
 __device__ __forceinline__ void gemm_tile_weights(const GemmArgs& a, int tile, int st_off,
                                                   u32x4 (&wv)[GEMM_U]) {
@@ -1626,16 +1626,21 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
   constexpr int KSTEP = 4 * VEC;
   constexpr int U = GEMM_U;
   const int lane = tid() & 63;
-  const int wave = tid() >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid() >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
+  // Rows past N read row 0 and columns past B read column B - 1 (their sums
+  // are never stored), so loads need no mask: a batch's loads are issued
+  // together. k-steps past the wave's range re-read its last step and skip
+  // their products (a wave-uniform branch); only when K is not a multiple of
+  // KSTEP are the groups past K zeroed per lane.
   bool rok;
   const int wrow = tile_row<EPI>(tile, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
-  const T* wbase = (const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + g * VEC;
   const int nsteps = (a.K + KSTEP - 1) / KSTEP;
   const int s0 = (wave * nsteps) / KW;
   const int s1 = ((wave + 1) * nsteps) / KW;
+  const bool ktail = (a.K % KSTEP) != 0;
 
   f64x4 acc[NB];
 #pragma unroll
@@ -1657,27 +1662,37 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
   // batch of U k-steps starting at st: weights and input groups (the
   // weights only where `w`)
   auto load = [&](int st, u32x4 (&wv)[U], u32x4 (&xw)[U][NB], bool w = true) {
+    int k0[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int k0 = (st + u) * KSTEP + g * VEC;
-      const bool kok = (st + u < s1) && (k0 < a.K);
-      if (w) wv[u] = (kok && rok) ? ld16_stream(wbase + (size_t)(st + u) * KSTEP) : u32x4{0u, 0u, 0u, 0u};
+      const int su = st + u < s1 ? st + u : s1 - 1;
+      k0[u] = su * KSTEP + g * VEC;
+      if (ktail) k0[u] = k0[u] < a.K ? k0[u] : 0;
+      if (w) wv[u] = ld16_stream((const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + k0[u]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int col = col0 + nb * 16 + r16;
+        int col = col0 + nb * 16 + r16;
+        col = col < a.B ? col : a.B - 1;
         if constexpr (C)
-          xw[u][nb] = (kok && col < a.B)
-                          ? ld16_coh(a.X, (uint32_t)(((size_t)col * a.ldx + k0) * sizeof(T)))
-                          : u32x4{0u, 0u, 0u, 0u};
+          xw[u][nb] = ld16_coh(a.X, (uint32_t)(((size_t)col * a.ldx + k0[u]) * sizeof(T)));
         else
-          xw[u][nb] = (kok && col < a.B) ? ld16((const T*)a.X + (size_t)col * a.ldx + k0)
-                                         : u32x4{0u, 0u, 0u, 0u};
+          xw[u][nb] = ld16((const T*)a.X + (size_t)col * a.ldx + k0[u]);
       }
     }
+    if (ktail) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if ((st + u) * KSTEP + g * VEC >= a.K) {
+          if (w) wv[u] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) xw[u][nb] = u32x4{0u, 0u, 0u, 0u};
+        }
+    }
   };
-  auto compute = [&](const u32x4 (&wv)[U], const u32x4 (&xw)[U][NB]) {
+  auto compute = [&](int st, const u32x4 (&wv)[U], const u32x4 (&xw)[U][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
+      if (st + u >= s1) break;  // wave-uniform: past the wave's k-range
       double wd[VEC];
       widen<T>(wv[u], wd);
 #pragma unroll
@@ -1700,17 +1715,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
     if (s0 < s1) load(s0, wa, xa, wpre == nullptr);
     for (int st = s0; st < s1; st += 2 * U) {
       if (st + U < s1) load(st + U, wb, xb);
-      compute(wa, xa);
+      compute(st, wa, xa);
       if (st + U >= s1) break;
       if (st + 2 * U < s1) load(st + 2 * U, wa, xa);
-      compute(wb, xb);
+      compute(st + U, wb, xb);
     }
   } else {
     for (int st = s0; st < s1; st += U) {
       u32x4 wv[U];
       u32x4 xw[U][NB];
       load(st, wv, xw);
-      compute(wv, xw);
+      compute(st, wv, xw);
     }
   }
 #pragma unroll
@@ -1729,22 +1744,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
   }
 }
 
-// The MFMA path's input vector of column b: xn[b][k] = round(x[b][k] *
-// scale_b * g[k]) (PRO_NORM) or round(x[b][k]) (PRO_CAST). The scale comes
-// from threads [0, 256) exactly as rms_scale with 256 threads (the others add
-// nothing), so any workgroup of 256 or more threads gives the same bits.
-// `red` holds NTH / 64 doubles. Every thread of the workgroup calls it.
+// The MFMA path's input vector of column b, elements [k0, k1):
+// xn[b][k] = round(x[b][k] * scale_b * g[k]) (PRO_NORM) or round(x[b][k])
+// (PRO_CAST). The scale comes from threads [0, 256) exactly as rms_scale with
+// 256 threads (the others add nothing), so any workgroup of 256 or more
+// threads, for any range, gives the same bits. `red` holds NTH / 64 doubles.
+// Every thread of the workgroup calls it.
 template <typename T, int PRO, bool C, int NTH>
-__device__ __forceinline__ void norm_column(const GemmArgs& a, int b, double* red) {
+__device__ __forceinline__ void norm_column(const GemmArgs& a, int b, double* red, int k0 = 0,
+                                            int k1 = 0x7fffffff) {
   static_assert(NTH >= 256, "the scale uses 256 threads");
   constexpr int PF = 4;  // elements per thread requested before the scale is formed
   const double* x = (const double*)a.X + (size_t)b * a.ldx;
   T* out = (T*)a.xn_out + (size_t)b * a.K;
+  k1 = k1 < a.K ? k1 : a.K;
   double xp[PF];
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
-    const int k = tid() + j * NTH;
-    xp[j] = k < a.K ? ld_f64<C>(x + k) : 0.0;
+    const int k = k0 + tid() + j * NTH;
+    xp[j] = k < k1 ? ld_f64<C>(x + k) : 0.0;
   }
   double rs = 1.0;
   if constexpr (PRO == PRO_NORM) {
@@ -1759,10 +1777,10 @@ __device__ __forceinline__ void norm_column(const GemmArgs& a, int b, double* re
   };
 #pragma unroll
   for (int j = 0; j < PF; ++j) {
-    const int k = tid() + j * NTH;
-    if (k < a.K) put(k, xp[j]);
+    const int k = k0 + tid() + j * NTH;
+    if (k < k1) put(k, xp[j]);
   }
-  for (int k = tid() + PF * NTH; k < a.K; k += NTH) put(k, ld_f64<C>(x + k));
+  for (int k = k0 + tid() + PF * NTH; k < k1; k += NTH) put(k, ld_f64<C>(x + k));
 }
 
 // Depformer substep entry of rows bx*16 .. bx*16+15 and columns by*4 ..

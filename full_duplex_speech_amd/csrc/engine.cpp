@@ -249,7 +249,8 @@ GemmArgs gemm_base(const moshi_ctx* c) {
 }
 
 hipError_t gemm(moshi_ctx* c, int pro, int epi, const GemmArgs& a) {
-  return launch_gemm(c->dtype, gemm_kw(c->dtype, a.B, a.K), pro, epi, a, c->stream);
+  return launch_gemm(c->dtype, gemm_kw(c->dtype, a.B, a.K, gemm_tiles(epi, a.N)), pro, epi, a,
+                     c->stream);
 }
 
 // ---- argument blocks of every operation (shared by the per-operation
@@ -503,9 +504,12 @@ hipError_t enqueue_depformer(moshi_ctx* c) {
   const double nlive = live_count(c);
   hipError_t e;
   {
+    // the depformer's wave split (8 / 4) also for its 4096-wide input
+    // projections: the multi-session depformer kernel computes the same bits
     GemmArgs a = d_in_args(c);
+    const int kw = B == 1 ? GEMV_KW : (B <= 32 ? 8 : 4);
     e = run(c, KC_D_INPROJ, (double)c->S_run * Dd * D * es,
-            [&] { return gemm(c, PRO_DIRECT, EPI_STORE, a); });
+            [&] { return launch_gemm(dt, kw, PRO_DIRECT, EPI_STORE, a, c->stream); });
     if (e != hipSuccess) return e;
   }
   for (int s = 0; s < c->S_run; ++s) {

@@ -341,11 +341,14 @@ inline int64_t staged_slice_bytes(int vec, int epi, int N, int K, int nwg) {
 int gemm_tiles(int epi, int N);  // row tiles of a projection
 // Workgroups launched for a one-session projection (the number of CUs).
 void set_gemv_grid(int n);
-// Waves per workgroup for a projection with K inputs and B sessions (8 for
-// the 4096-wide temporal inputs, 4 for the depformer's).
-int gemm_kw(int dtype, int B, int K);
-// kw from gemm_kw. With B > 1 and PRO_NORM / PRO_CAST, xn_out must be a
-// [B][K] buffer: the rounded input vectors are written there first.
+// Waves per workgroup for a projection of `tiles` row tiles with K inputs
+// and B sessions: one session 8; more: 16 (up to 32 sessions) or 12 / 4
+// (33..64, at most / more than 512 tiles) for inputs of 4096 or wider, 8 / 4
+// for narrower ones (up to 32 / 33..64 sessions).
+int gemm_kw(int dtype, int B, int K, int tiles);
+// kw from gemm_kw (B > 1: 16 or 8 up to 32 sessions, 12 or 4 above). With
+// B > 1 and PRO_NORM / PRO_CAST, xn_out must be a [B][K] buffer: the rounded
+// input vectors are written there first.
 hipError_t launch_gemm(int dtype, int kw, int pro, int epi, const GemmArgs& a, hipStream_t st);
 hipError_t launch_attn(int dtype, int hd, const AttnArgs& a, int B, hipStream_t st);
 // Depformer attention over a.scalar_nvalid <= DEP_MAX_KEYS entries, one

@@ -59,10 +59,11 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
 
 // Input vectors for the MFMA path: xn[b][k] = round(x[b][k] * scale_b * g[k])
 // (PRO_NORM) or round(x[b][k]) (PRO_CAST); one workgroup per column.
+// (column blockIdx.x, elements [1024 blockIdx.y, 1024 blockIdx.y + 1024))
 template <typename T, int PRO>
 __global__ __launch_bounds__(256) void norm_kernel(GemmArgs a) {
   __shared__ double s_tmp[4];
-  norm_column<T, PRO, false, 256>(a, blockIdx.x, s_tmp);
+  norm_column<T, PRO, false, 256>(a, blockIdx.x, s_tmp, blockIdx.y * 1024, blockIdx.y * 1024 + 1024);
 }
 
 // Greedy token of column blockIdx.x from per-tile (max, index) partials.
@@ -569,14 +570,17 @@ hipError_t launch_window_copy(int dtype, void* win, void* ring, int i0, int i1, 
 
 int gemm_tiles(int epi, int N) { return epi == EPI_SWIGLU ? (N + 7) / 8 : (N + 15) / 16; }
 
-int gemm_kw(int dtype, int B, int K) {
+int gemm_kw(int dtype, int B, int K, int tiles) {
   (void)dtype;
-  (void)K;
   // one session: 8 waves (the sum-of-squares partials assume 2 rows per
-  // wave); more sessions: 8 waves (a shorter stretch of K per wave; up to 32
-  // sessions; 4 waves at 64, see launch_gemm_t)
+  // wave). More sessions, inputs of 4096 or wider (the temporal projections):
+  // up to 32 sessions 16 waves; at 33..64, 12 waves for projections of at
+  // most 512 row tiles (three 4-wave workgroups fit a CU, so fewer tiles
+  // would leave SIMDs with one wave) and 4 above (measured). Narrower inputs
+  // (the depformer's) take 8 waves up to 32 sessions and 4 at 33..64.
   if (B == 1) return GEMV_KW;
-  return 8;
+  if (K >= 4096) return B <= 32 ? 16 : (tiles <= 512 ? 12 : 4);
+  return B <= 32 ? 8 : 4;
 }
 
 // Workgroups of the one-session projection: at most one per CU (the kernel
@@ -634,7 +638,8 @@ static hipError_t launch_gemm_db(int epi, const GemmArgs& a, hipStream_t st) {
 // faster at 16 sessions).
 template <typename T, int NB, int KW>
 static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
-  if (NB <= 2 && a.K < 4096) return launch_gemm_db<T, NB, KW, NB <= 2>(epi, a, st);
+  if constexpr (NB <= 2 && KW <= 8)
+    if (a.K < 4096) return launch_gemm_db<T, NB, KW, true>(epi, a, st);
   return launch_gemm_db<T, NB, KW, false>(epi, a, st);
 }
 
@@ -650,22 +655,29 @@ static hipError_t launch_gemm_t(int kw, int pro, int epi, const GemmArgs& a, hip
   GemmArgs b = a;
   if (pro != PRO_DIRECT) {
     if (a.xn_out == nullptr) return hipErrorInvalidValue;  // the caller provides the buffer
+    const dim3 ng(a.B, (a.K + 1023) / 1024);
     if (pro == PRO_NORM)
-      hipLaunchKernelGGL((norm_kernel<T, PRO_NORM>), dim3(a.B), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((norm_kernel<T, PRO_NORM>), ng, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL((norm_kernel<T, PRO_CAST>), dim3(a.B), dim3(256), 0, st, a);
+      hipLaunchKernelGGL((norm_kernel<T, PRO_CAST>), ng, dim3(256), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     b.X = a.xn_out;
     b.ldx = a.K;
   }
+  // waves per tile: 16 or 8 (up to 32 sessions), 12 or 4 (33..64)
   const int nb = a.B <= 16 ? 1 : (a.B <= 32 ? 2 : 4);
-  const int kwm = kw >= 8 ? 8 : 4;
-  if (nb == 1)
-    return kwm == 8 ? launch_gemm_kw<T, 1, 8>(epi, b, st) : launch_gemm_kw<T, 1, 4>(epi, b, st);
-  if (nb == 2)
-    return kwm == 8 ? launch_gemm_kw<T, 2, 8>(epi, b, st) : launch_gemm_kw<T, 2, 4>(epi, b, st);
-  return launch_gemm_kw<T, 4, 4>(epi, b, st);
+  if (nb == 1) {
+    if (kw == 16) return launch_gemm_kw<T, 1, 16>(epi, b, st);
+    if (kw == 8) return launch_gemm_kw<T, 1, 8>(epi, b, st);
+  } else if (nb == 2) {
+    if (kw == 16) return launch_gemm_kw<T, 2, 16>(epi, b, st);
+    if (kw == 8) return launch_gemm_kw<T, 2, 8>(epi, b, st);
+  } else {
+    if (kw == 12) return launch_gemm_kw<T, 4, 12>(epi, b, st);
+    if (kw == 4) return launch_gemm_kw<T, 4, 4>(epi, b, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(int dtype, int kw, int pro, int epi, const GemmArgs& a, hipStream_t st) {
