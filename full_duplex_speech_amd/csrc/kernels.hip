@@ -632,12 +632,14 @@ static hipError_t launch_gemm_db(int epi, const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// Double-buffered batches for inputs narrower than 4096 (the depformer's:
-// few k-steps per wave, latency-bound); the temporal widths keep single
-// batches, whose lower register count fits more workgroups per CU (measured
-// faster at 16 sessions).
+// Double-buffered batches (the next batch requested before this one is
+// used) where the registers allow it.
 template <typename T, int NB, int KW>
 static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
+  // double-buffered batches only for narrow inputs at 8 or fewer waves: the
+  // wide ones need every wave slot (single batches: 54 VGPRs, two 16-wave
+  // workgroups per CU; double-buffered ones lose half of that, or spill;
+  // measured slower)
   if constexpr (NB <= 2 && KW <= 8)
     if (a.K < 4096) return launch_gemm_db<T, NB, KW, true>(epi, a, st);
   return launch_gemm_db<T, NB, KW, false>(epi, a, st);
