@@ -47,11 +47,19 @@ def parse():
     ap.add_argument("--cpu-frames", type=int, default=2,
                     help="full-size frames the CPU oracle runs for its B=1 baseline")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--b1", type=int, default=1,
+                    help="measure the B=1 headline workload (0: only the other workloads, "
+                         "e.g. for counter runs; value is then null)")
     ap.add_argument("--b16", type=int, default=1, help="also measure B=16 (elastic fills)")
     ap.add_argument("--b64", type=int, default=1, help="also measure B=64 (full rings)")
     ap.add_argument("--extra", type=int, default=1,
                     help="also measure the tiny model, the temporal / depformer steps alone, "
                          "dep_q = 8 and the 64-frame prefill")
+    ap.add_argument("--profile-b16", type=int, default=0,
+                    help="only run this many host-synchronous steps of the B=16 workload "
+                         "through the library's own stream, without torch (for hardware "
+                         "counter runs: rocprofv3's SQ counters have crashed processes "
+                         "that run torch), and exit")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (the reference "
                          "dispatch that scales HBM byte counters)")
@@ -67,6 +75,10 @@ def make_engine(M, shape, weights, B, stream, flags=0):
                         rope_theta=shape.rope_theta, norm_eps=shape.norm_eps,
                         dtype=shape.dtype, max_sessions=B, flags=flags, dep_q=shape.dep_q)
     return M.moshi_create(cfg, weights, hip_stream=stream.cuda_stream)
+
+
+def rnd(x, n):
+    return None if x is None else round(x, n)
 
 
 def ticks_stats(ticks):
@@ -207,8 +219,46 @@ def cpu_baseline_b16(shape, weights, w4, initial, threads):
     return len(th) / dt, dt
 
 
+def profile_b16(n):
+    """n host-synchronous steps of the B=16 workload (workload 4's initial
+    fills), library only: no torch in the process."""
+    import numpy as np
+
+    import full_duplex_speech_amd as M
+    from synth import spec, workloads as wl
+
+    shape = spec.PERSONAPLEX
+    weights = wl.make_weights(shape, wl.MODEL_SEEDS["personaplex"], threads=16)
+    cfg = M.make_config(dim=shape.dim, n_layers=shape.n_layers, n_heads=shape.n_heads,
+                        ffn_hidden=shape.ffn, window=shape.window, dep_dim=shape.dep_dim,
+                        dep_layers=shape.dep_layers, dep_heads=shape.dep_heads,
+                        dep_ffn_hidden=shape.dep_ffn, n_substeps=shape.n_substeps,
+                        text_vocab=shape.text_vocab, audio_card=shape.audio_card,
+                        rope_theta=shape.rope_theta, norm_eps=shape.norm_eps,
+                        dtype=shape.dtype, max_sessions=16)
+    ctx = M.moshi_create(cfg, weights)
+    w4 = wl.WORKLOADS[4]
+    initial, _ = wl.churn_schedule(w4)
+    for sid, fill in initial:
+        s = M.moshi_session_join(ctx)
+        kk, vv = wl.prefill_kv(shape, w4.seed("prefill"), sid, fill, threads=16)
+        M.moshi_session_prefill_kv(ctx, s, kk, vv)
+    fr = np.stack([wl.frames(shape, w4.seed("frames"), sid, 0, n) for sid, _ in initial], axis=1)
+    t0 = time.perf_counter()
+    for t in range(n):
+        M.moshi_step(ctx, fr[t])
+    ms = (time.perf_counter() - t0) * 1000.0 / max(n, 1)
+    print(json.dumps({"profile_b16_steps": n, "ms_per_step_host_sync": round(ms, 3),
+                      "dep_kernel": M.moshi_uses_dep_kernel(ctx)}), flush=True)
+    M.moshi_destroy(ctx)
+    M.unload()
+
+
 def main():
     args = parse()
+    if args.profile_b16 > 0:
+        profile_b16(args.profile_b16)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (sessions would shard "
               "one engine per GPU with no exchange); run with --gpus 1", file=sys.stderr)
@@ -228,107 +278,110 @@ def main():
     lines = {}
 
     # ---------------- B = 1: the headline workload ----------------
-    ctx = make_engine(M, shape, weights, 1, stream)
-    slot = M.moshi_session_join(ctx)
     wk = wl.WORKLOADS[2]
     k, v = wl.prefill_kv(shape, wk.seed("prefill"), 0, W, threads=16)
-    M.moshi_session_prefill_kv(ctx, slot, k, v)
     nfr = args.warmup + args.steps
     frames = wl.frames(shape, wk.seed("frames"), 0, 0, nfr)
-    d_frames = torch.from_numpy(frames.reshape(nfr, 1, -1)).to("cuda")
-    d_text = torch.zeros((args.steps, 1), dtype=torch.int32, device="cuda")
-    d_codes = torch.zeros((args.steps, 1, shape.n_substeps), dtype=torch.int32, device="cuda")
-    torch.cuda.synchronize()
-    log("B=1 engine ready")
-    ms_wall, ms_gpu, ticks1 = timed_steps(M, torch, ctx, stream, d_frames, d_text, d_codes,
-                                          args.warmup, args.steps)
-    fps = 1000.0 / ms_wall
-    log(f"B=1: {ms_wall:.3f} ms/step wall, {ms_gpu:.3f} ms/step events, {fps:.1f} frames/s")
-
-    # host-synchronous step (frames from host, tokens back to host every step)
-    t1 = time.perf_counter()
-    nsync = 20
-    for i in range(nsync):
-        M.moshi_step(ctx, frames[i % nfr][None, :])
-    ms_sync = (time.perf_counter() - t1) * 1000.0 / nsync
-
-    kt = kernel_table(M, ctx, frames[0][None, :], args.timing_steps)
-    bytes_step = sum(x["bytes_per_step"] for x in kt.values())
-    if M.moshi_uses_step_kernel(ctx):
-        # the whole step is one persistent kernel: its launch duration is the
-        # event-timed step (one launch per step, back to back on the stream)
-        dname = "step_kernel"
-        d_bytes, d_ms = bytes_step, ms_gpu
-    else:
-        dname = "temporal_gateup"
-        d = kt[dname]
-        d_bytes = d["bytes_per_step"] / d["launches_per_step"]
-        d_ms = d["ms_per_step"] / d["launches_per_step"]
-    achieved = d_bytes / (d_ms * 1e6)  # GB/s
-    roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dname), "bytes_per_launch": d_bytes,
-                "ms_per_launch": round(d_ms, 5)}
-    step_gbs = bytes_step / (ms_wall * 1e6)
-    log(f"dominant kernel {dname}: {achieved:.0f} GB/s; step {step_gbs:.0f} GB/s")
-
-    if args.extra:
-        # workload 2 (temporal alone) and 3 (depformer alone): their phases
-        # inside the step kernel (per-operation timestamps), and the
-        # temporal-only / depformer-only entry points (per-operation kernels,
-        # host-synchronous)
-        tms, tby = phase(kt, TEMPORAL_CLASSES)
-        dms, dby = phase(kt, DEPFORMER_CLASSES)
-        t1 = time.perf_counter()
-        for i in range(10):
-            M.moshi_temporal_step(ctx, frames[i % nfr][None, :])
-        t_entry = (time.perf_counter() - t1) * 100.0
-        w3 = wl.WORKLOADS[3]
-        hids, toks = wl.dep_inputs(shape, w3.seed("dep"), 0, 10)
-        t1 = time.perf_counter()
-        for i in range(10):
-            M.moshi_depformer_step(ctx, hids[i][None, :], toks[i:i + 1])
-        d_entry = (time.perf_counter() - t1) * 100.0
-        lines["temporal_b1"] = {
-            "workload": "temporal step alone, B=1, ring full at 3000 (workload 2)",
-            "ms_in_step_kernel": round(tms, 4), "frames_per_s": round(1000.0 / tms, 1),
-            "bytes_per_frame": tby, "hbm_frac": round(tby / (tms * 1e6) / HBM_PEAK_GBS, 4),
-            "ms_temporal_entry_host_sync": round(t_entry, 4)}
-        lines["depformer_b1"] = {
-            "workload": "16 depformer substeps alone, B=1 (workload 3)",
-            "ms_in_step_kernel": round(dms, 4), "frames_per_s": round(1000.0 / dms, 1),
-            "bytes_per_frame": dby, "hbm_frac": round(dby / (dms * 1e6) / HBM_PEAK_GBS, 4),
-            "ms_depformer_entry_host_sync": round(d_entry, 4)}
-        log(f"temporal phase {tms:.3f} ms, depformer phase {dms:.3f} ms")
-
-        # 64 frames prefilled at once after the full ring (MFMA columns)
-        M.moshi_session_leave(ctx, slot)
+    fps = ms_wall = ms_gpu = ms_sync = bytes_step = step_gbs = None
+    ticks1, roofline, kt = None, None, {}
+    if args.b1:
+        ctx = make_engine(M, shape, weights, 1, stream)
         slot = M.moshi_session_join(ctx)
         M.moshi_session_prefill_kv(ctx, slot, k, v)
-        pf = wl.frames(shape, wk.seed("frames") + 100, 0, 0, 64)
-        M.moshi_session_prefill_frames(ctx, slot, pf)  # workspace + warm-up
-        reps = 3
+        d_frames = torch.from_numpy(frames.reshape(nfr, 1, -1)).to("cuda")
+        d_text = torch.zeros((args.steps, 1), dtype=torch.int32, device="cuda")
+        d_codes = torch.zeros((args.steps, 1, shape.n_substeps), dtype=torch.int32, device="cuda")
         torch.cuda.synchronize()
+        log("B=1 engine ready")
+        ms_wall, ms_gpu, ticks1 = timed_steps(M, torch, ctx, stream, d_frames, d_text, d_codes,
+                                              args.warmup, args.steps)
+        fps = 1000.0 / ms_wall
+        log(f"B=1: {ms_wall:.3f} ms/step wall, {ms_gpu:.3f} ms/step events, {fps:.1f} frames/s")
+
+        # host-synchronous step (frames from host, tokens back to host every step)
         t1 = time.perf_counter()
-        for _ in range(reps):
+        nsync = 20
+        for i in range(nsync):
+            M.moshi_step(ctx, frames[i % nfr][None, :])
+        ms_sync = (time.perf_counter() - t1) * 1000.0 / nsync
+
+        kt = kernel_table(M, ctx, frames[0][None, :], args.timing_steps)
+        bytes_step = sum(x["bytes_per_step"] for x in kt.values())
+        if M.moshi_uses_step_kernel(ctx):
+            # the whole step is one persistent kernel: its launch duration is the
+            # event-timed step (one launch per step, back to back on the stream)
+            dname = "step_kernel"
+            d_bytes, d_ms = bytes_step, ms_gpu
+        else:
+            dname = "temporal_gateup"
+            d = kt[dname]
+            d_bytes = d["bytes_per_step"] / d["launches_per_step"]
+            d_ms = d["ms_per_step"] / d["launches_per_step"]
+        achieved = d_bytes / (d_ms * 1e6)  # GB/s
+        roofline = {"bound": "hbm", "kernel": dname, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(dname), "bytes_per_launch": d_bytes,
+                    "ms_per_launch": round(d_ms, 5)}
+        step_gbs = bytes_step / (ms_wall * 1e6)
+        log(f"dominant kernel {dname}: {achieved:.0f} GB/s; step {step_gbs:.0f} GB/s")
+
+        if args.extra:
+            # workload 2 (temporal alone) and 3 (depformer alone): their phases
+            # inside the step kernel (per-operation timestamps), and the
+            # temporal-only / depformer-only entry points (per-operation kernels,
+            # host-synchronous)
+            tms, tby = phase(kt, TEMPORAL_CLASSES)
+            dms, dby = phase(kt, DEPFORMER_CLASSES)
+            t1 = time.perf_counter()
+            for i in range(10):
+                M.moshi_temporal_step(ctx, frames[i % nfr][None, :])
+            t_entry = (time.perf_counter() - t1) * 100.0
+            w3 = wl.WORKLOADS[3]
+            hids, toks = wl.dep_inputs(shape, w3.seed("dep"), 0, 10)
+            t1 = time.perf_counter()
+            for i in range(10):
+                M.moshi_depformer_step(ctx, hids[i][None, :], toks[i:i + 1])
+            d_entry = (time.perf_counter() - t1) * 100.0
+            lines["temporal_b1"] = {
+                "workload": "temporal step alone, B=1, ring full at 3000 (workload 2)",
+                "ms_in_step_kernel": round(tms, 4), "frames_per_s": round(1000.0 / tms, 1),
+                "bytes_per_frame": tby, "hbm_frac": round(tby / (tms * 1e6) / HBM_PEAK_GBS, 4),
+                "ms_temporal_entry_host_sync": round(t_entry, 4)}
+            lines["depformer_b1"] = {
+                "workload": "16 depformer substeps alone, B=1 (workload 3)",
+                "ms_in_step_kernel": round(dms, 4), "frames_per_s": round(1000.0 / dms, 1),
+                "bytes_per_frame": dby, "hbm_frac": round(dby / (dms * 1e6) / HBM_PEAK_GBS, 4),
+                "ms_depformer_entry_host_sync": round(d_entry, 4)}
+            log(f"temporal phase {tms:.3f} ms, depformer phase {dms:.3f} ms")
+
+            # 64 frames prefilled at once after the full ring (MFMA columns)
             M.moshi_session_leave(ctx, slot)
             slot = M.moshi_session_join(ctx)
-            M.moshi_session_prefill_frames(ctx, slot, pf)
-        ms_pf = (time.perf_counter() - t1) * 1000.0 / reps
-        D, F, L = shape.dim, shape.ffn, shape.n_layers
-        flops = 64 * (2.0 * (4 * D * D + 3 * F * D) * L + 2.0 * shape.text_vocab * D)
-        tfs = flops / (ms_pf * 1e9)
-        lines["b1_prefill_64"] = {
-            "workload": "64 frames of one session prefilled at once (positions 0..63; "
-                        "the projections as fp64 MFMA products over 64 columns)",
-            "ms_per_call": round(ms_pf, 4), "frames_per_s": round(64 * 1000.0 / ms_pf, 1),
-            "roofline": {"bound": "mfma", "achieved": round(tfs, 2),
-                         "peak": FP64_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                         "frac": round(tfs / FP64_MFMA_PEAK_TFS, 4)},
-            "flops_per_call": flops}
-        log(f"prefill 64 frames: {ms_pf:.2f} ms ({tfs:.1f} TFLOP/s)")
-    M.moshi_destroy(ctx)
-    del ctx
+            M.moshi_session_prefill_kv(ctx, slot, k, v)
+            pf = wl.frames(shape, wk.seed("frames") + 100, 0, 0, 64)
+            M.moshi_session_prefill_frames(ctx, slot, pf)  # workspace + warm-up
+            reps = 3
+            torch.cuda.synchronize()
+            t1 = time.perf_counter()
+            for _ in range(reps):
+                M.moshi_session_leave(ctx, slot)
+                slot = M.moshi_session_join(ctx)
+                M.moshi_session_prefill_frames(ctx, slot, pf)
+            ms_pf = (time.perf_counter() - t1) * 1000.0 / reps
+            D, F, L = shape.dim, shape.ffn, shape.n_layers
+            flops = 64 * (2.0 * (4 * D * D + 3 * F * D) * L + 2.0 * shape.text_vocab * D)
+            tfs = flops / (ms_pf * 1e9)
+            lines["b1_prefill_64"] = {
+                "workload": "64 frames of one session prefilled at once (positions 0..63; "
+                            "the projections as fp64 MFMA products over 64 columns)",
+                "ms_per_call": round(ms_pf, 4), "frames_per_s": round(64 * 1000.0 / ms_pf, 1),
+                "roofline": {"bound": "mfma", "achieved": round(tfs, 2),
+                             "peak": FP64_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                             "frac": round(tfs / FP64_MFMA_PEAK_TFS, 4)},
+                "flops_per_call": flops}
+            log(f"prefill 64 frames: {ms_pf:.2f} ms ({tfs:.1f} TFLOP/s)")
+        M.moshi_destroy(ctx)
+        del ctx
 
     if args.copy_mib > 0:
         n = args.copy_mib << 20
@@ -340,7 +393,7 @@ def main():
         log(f"copy probe: {args.copy_mib} MiB read + {args.copy_mib} MiB written")
         del src, dst
 
-    if args.extra:
+    if args.extra and args.b1:
         # the 8-substep depformer reading (dep_q = 8), B=1, full ring
         sh8 = shape.replace(dep_q=8)
         ctx = make_engine(M, sh8, weights, 1, stream)
@@ -454,8 +507,8 @@ def main():
             log(f"CPU oracle B=16: {fps16:.4f} frames/s on {nth} threads")
 
     rec = {
-        "metric": METRIC, "value": round(fps, 2), "unit": "frames/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_wall, 4),
+        "metric": METRIC, "value": rnd(fps, 2), "unit": "frames/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": rnd(ms_wall, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
         "storage": "bf16 weights, embeddings, K/V rings and projection inputs",
         "data": "synthetic",
@@ -463,12 +516,12 @@ def main():
                                "prefilled to the 3000-frame window; text head 32000; depformer "
                                "1024-d/6L/16h, F 2816, 16 substeps with per-substep weights",
                    "batch": 1, "ring_fill": W, "parallelism": "none (one GPU)"},
-        "rtf": round(ms_wall / FRAME_MS, 5),
-        "ms_per_step_events": round(ms_gpu, 4),
-        "ms_per_step_host_sync": round(ms_sync, 4),
-        "ticks_ms": ticks_stats(ticks1),
+        "rtf": rnd(ms_wall / FRAME_MS if ms_wall else None, 5),
+        "ms_per_step_events": rnd(ms_gpu, 4),
+        "ms_per_step_host_sync": rnd(ms_sync, 4),
+        "ticks_ms": ticks_stats(ticks1) if ticks1 else None,
         "bytes_per_step": bytes_step,
-        "hbm_frac_step": round(step_gbs / HBM_PEAK_GBS, 4),
+        "hbm_frac_step": rnd(step_gbs / HBM_PEAK_GBS if step_gbs else None, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
         "b16": b16,
