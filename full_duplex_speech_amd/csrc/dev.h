@@ -1196,8 +1196,8 @@ __device__ __forceinline__ void load_kv_block(const T* kbase, const T* vbase, in
       kv.k[ps] = ld16_coh(kbase, off);
       kv.v[ps] = ld16_coh(vbase, off);
     } else {
-      kv.k[ps] = ld16((const char*)kbase + off);
-      kv.v[ps] = ld16((const char*)vbase + off);
+      kv.k[ps] = ld16_stream((const char*)kbase + off);
+      kv.v[ps] = ld16_stream((const char*)vbase + off);
     }
   }
 }
@@ -1619,56 +1619,72 @@ __device__ __forceinline__ void gemm_tile_weights(const GemmArgs& a, int tile, i
   }
 }
 
-template <typename T, int NB, int KW, int EPI, bool DB, bool C>
+template <typename T, int NB, int KW, int EPI, bool DB, bool C, int RT = 1>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0, f64x4* s_acc,
                                           const u32x4* wpre = nullptr) {
+  // RT row tiles (tile .. tile + RT - 1) share each input group's conversion;
+  // each tile's sums are those of RT = 1 (same order), so RT changes no value
   constexpr int VEC = VecOf<T>::N;
   constexpr int KSTEP = 4 * VEC;
   constexpr int U = GEMM_U;
+  static_assert(RT == 1 || !DB, "several row tiles: single batches");
+  static_assert(RT <= KW, "one epilogue wave per row tile");
   const int lane = tid() & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid() >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
+  const int ntiles = n_tiles_of(EPI, a.N);
 
   // Rows past N read row 0 and columns past B read column B - 1 (their sums
   // are never stored), so loads need no mask: a batch's loads are issued
   // together. k-steps past the wave's range re-read its last step and skip
   // their products (a wave-uniform branch); only when K is not a multiple of
   // KSTEP are the groups past K zeroed per lane.
-  bool rok;
-  const int wrow = tile_row<EPI>(tile, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
+  int wrow[RT];
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    bool rok;
+    wrow[r] = tile_row<EPI>(tile + r, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
+    wrow[r] = rok ? wrow[r] : 0;
+  }
   const int nsteps = (a.K + KSTEP - 1) / KSTEP;
   const int s0 = (wave * nsteps) / KW;
   const int s1 = ((wave + 1) * nsteps) / KW;
   const bool ktail = (a.K % KSTEP) != 0;
 
-  f64x4 acc[NB];
+  f64x4 acc[RT][NB];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) acc[nb] = f64x4{0.0, 0.0, 0.0, 0.0};
-  // the residual rows this lane's epilogue adds to (written before this operation)
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) acc[r][nb] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // the residual rows this lane's epilogue adds to (written before this
+  // operation): wave r runs tile r's epilogue
   double rpre[NB][4];
   if constexpr (EPI == EPI_RESID) {
-    if (wave == 0)
+    if (wave < RT)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         const int col = col0 + nb * 16 + r16;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = tile * 16 + 4 * g + i;
+          const int row = (tile + wave) * 16 + 4 * g + i;
           rpre[nb][i] = (col < a.B && row < a.N) ? ld_f64<C>(a.resid + (size_t)col * a.ldr + row) : 0.0;
         }
       }
   }
   // batch of U k-steps starting at st: weights and input groups (the
   // weights only where `w`)
-  auto load = [&](int st, u32x4 (&wv)[U], u32x4 (&xw)[U][NB], bool w = true) {
+  auto load = [&](int st, u32x4 (&wv)[U][RT], u32x4 (&xw)[U][NB], bool w = true) {
     int k0[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int su = st + u < s1 ? st + u : s1 - 1;
       k0[u] = su * KSTEP + g * VEC;
       if (ktail) k0[u] = k0[u] < a.K ? k0[u] : 0;
-      if (w) wv[u] = ld16_stream((const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + k0[u]);
+      if (w)
+#pragma unroll
+        for (int r = 0; r < RT; ++r)
+          wv[u][r] = ld16_stream((const T*)a.W + (size_t)wrow[r] * a.K + k0[u]);
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         int col = col0 + nb * 16 + r16;
@@ -1683,34 +1699,52 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if ((st + u) * KSTEP + g * VEC >= a.K) {
-          if (w) wv[u] = u32x4{0u, 0u, 0u, 0u};
+          if (w)
+#pragma unroll
+            for (int r = 0; r < RT; ++r) wv[u][r] = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) xw[u][nb] = u32x4{0u, 0u, 0u, 0u};
         }
     }
   };
-  auto compute = [&](int st, const u32x4 (&wv)[U], const u32x4 (&xw)[U][NB]) {
+  auto compute = [&](int st, const u32x4 (&wv)[U][RT], const u32x4 (&xw)[U][NB]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (st + u >= s1) break;  // wave-uniform: past the wave's k-range
-      double wd[VEC];
-      widen<T>(wv[u], wd);
+      if constexpr (RT == 1) {
+        double wd[VEC];
+        widen<T>(wv[u][0], wd);
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-        double xd[VEC];
-        widen<T>(xw[u][nb], xd);
+        for (int nb = 0; nb < NB; ++nb) {
+          double xd[VEC];
+          widen<T>(xw[u][nb], xd);
 #pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          acc[nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(wd[e], xd[e], acc[nb], 0, 0, 0);
+          for (int e = 0; e < VEC; ++e)
+            acc[0][nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(wd[e], xd[e], acc[0][nb], 0, 0, 0);
+        }
+      } else {
+        double wd[RT][VEC];
+#pragma unroll
+        for (int r = 0; r < RT; ++r) widen<T>(wv[u][r], wd[r]);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          double xd[VEC];
+          widen<T>(xw[u][nb], xd);
+#pragma unroll
+          for (int r = 0; r < RT; ++r)
+#pragma unroll
+            for (int e = 0; e < VEC; ++e)
+              acc[r][nb] = __builtin_amdgcn_mfma_f64_16x16x4f64(wd[r][e], xd[e], acc[r][nb], 0, 0, 0);
+        }
       }
     }
   };
   if constexpr (DB) {
     // the next batch is requested before this one is used
-    u32x4 wa[U], xa[U][NB], wb[U], xb[U][NB];
+    u32x4 wa[U][1], xa[U][NB], wb[U][1], xb[U][NB];
     if (wpre != nullptr) {
 #pragma unroll
-      for (int u = 0; u < U; ++u) wa[u] = wpre[u];
+      for (int u = 0; u < U; ++u) wa[u][0] = wpre[u];
     }
     if (s0 < s1) load(s0, wa, xa, wpre == nullptr);
     for (int st = s0; st < s1; st += 2 * U) {
@@ -1722,25 +1756,27 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
     }
   } else {
     for (int st = s0; st < s1; st += U) {
-      u32x4 wv[U];
+      u32x4 wv[U][RT];
       u32x4 xw[U][NB];
       load(st, wv, xw);
       compute(st, wv, xw);
     }
   }
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) s_acc[(wave * NB + nb) * 64 + lane] = acc[nb];
+  for (int r = 0; r < RT; ++r)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) s_acc[((wave * RT + r) * NB + nb) * 64 + lane] = acc[r][nb];
   __syncthreads();
-  if (wave != 0) return;
+  if (wave >= RT || tile + wave >= ntiles) return;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    f64x4 sm = s_acc[nb * 64 + lane];
-    for (int w = 1; w < KW; ++w) sm += s_acc[(w * NB + nb) * 64 + lane];
+    f64x4 sm = s_acc[(wave * NB + nb) * 64 + lane];
+    for (int w = 1; w < KW; ++w) sm += s_acc[((w * RT + wave) * NB + nb) * 64 + lane];
     const double v[4] = {sm[0], sm[1], sm[2], sm[3]};
     if constexpr (EPI == EPI_RESID)
-      epilogue_resid<C>(a, tile, g, col0 + nb * 16 + r16, v, rpre[nb]);
+      epilogue_resid<C>(a, tile + wave, g, col0 + nb * 16 + r16, v, rpre[nb]);
     else
-      epilogue<T, EPI, C>(a, tile, g, col0 + nb * 16 + r16, v);
+      epilogue<T, EPI, C>(a, tile + wave, g, col0 + nb * 16 + r16, v);
   }
 }
 

@@ -50,11 +50,11 @@ __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
 // Two or more sessions: fp64 MFMA 16x16x4 tiles
 // ---------------------------------------------------------------------------
 
-// 16 weight rows x 16 NB session columns per workgroup (see gemm_tile).
-template <typename T, int NB, int KW, int EPI, bool DB>
+// 16 RT weight rows x 16 NB session columns per workgroup (see gemm_tile).
+template <typename T, int NB, int KW, int EPI, bool DB, int RT = 1>
 __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
-  __shared__ f64x4 s_acc[KW * NB * 64];
-  gemm_tile<T, NB, KW, EPI, DB, false>(a, blockIdx.x, 0, s_acc);
+  __shared__ f64x4 s_acc[KW * RT * NB * 64];
+  gemm_tile<T, NB, KW, EPI, DB, false, RT>(a, blockIdx.x * RT, 0, s_acc);
 }
 
 // Input vectors for the MFMA path: xn[b][k] = round(x[b][k] * scale_b * g[k])
@@ -608,24 +608,24 @@ static hipError_t launch_gemv_kw(int pro, int epi, const GemmArgs& a, hipStream_
   return hipErrorInvalidValue;
 }
 
-template <typename T, int NB, int KW, bool DB>
+template <typename T, int NB, int KW, bool DB, int RT = 1>
 static hipError_t launch_gemm_db(int epi, const GemmArgs& a, hipStream_t st) {
-  dim3 grid(gemm_tiles(epi, a.N)), block(64 * KW);
+  dim3 grid((gemm_tiles(epi, a.N) + RT - 1) / RT), block(64 * KW);
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE, DB>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE, DB, RT>), grid, block, 0, st, a);
       break;
     case EPI_RESID:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_RESID, DB>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_RESID, DB, RT>), grid, block, 0, st, a);
       break;
     case EPI_QKV:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_QKV, DB>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_QKV, DB, RT>), grid, block, 0, st, a);
       break;
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_SWIGLU, DB>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_SWIGLU, DB, RT>), grid, block, 0, st, a);
       break;
     case EPI_ARGMAX:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_ARGMAX, DB>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_ARGMAX, DB, RT>), grid, block, 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -642,6 +642,14 @@ static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
   // measured slower)
   if constexpr (NB <= 2 && KW <= 8)
     if (a.K < 4096) return launch_gemm_db<T, NB, KW, true>(epi, a, st);
+  // wide inputs with four column blocks and many row tiles: two row tiles
+  // per workgroup share each input group's conversion (fewer VALU
+  // instructions per MFMA; measured faster for the 1408-tile gate/up and the
+  // 2000-tile text head at 64 sessions, slower wherever it halves the
+  // workgroups of a projection with fewer tiles or, with one column block,
+  // the workgroups per CU)
+  if constexpr (NB == 4 && KW <= 8)  // (LDS: KW x 2 x NB x 2 KB)
+    if (gemm_tiles(epi, a.N) >= 1024) return launch_gemm_db<T, NB, KW, false, 2>(epi, a, st);
   return launch_gemm_db<T, NB, KW, false>(epi, a, st);
 }
 
