@@ -111,6 +111,9 @@ CASES = {
                                                     dep_final_norm=True), 5, [3], 4, True, [4]),
     "ragged_bf16_b17": (spec.RAGGED, 17, [0, 16], 3, False, [5]),
     "ragged_bf16_b40": (spec.RAGGED, 40, [2, 33, 39], 3, True, [1]),
+    "ragged_bf16_b36_variants": (spec.RAGGED.replace(dep_q=8, dep_ref_ring=True,
+                                                     dep_final_norm=True), 36, [0, 20], 2, True,
+                                 [35]),
 }
 
 
