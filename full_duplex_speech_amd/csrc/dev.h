@@ -717,14 +717,48 @@ struct GemvShape {
   static constexpr int U = U_ > 0 ? U_ : ((R <= 2) ? 8 : 4);  // groups per lane and row per batch
 };
 
-// The first weight batch of workgroup `wg` for the projection `a`, requested
-// ahead of time (while the grid barrier that precedes it completes).
+// The row pairs a wave of workgroup wg (of nwg) takes in gemv_core: item j
+// (j < n) is pair `we` of tile tile0 + j * step. By default the workgroup
+// walks tiles wg, wg + nwg, ... and wave w takes pair w of each. A SwiGLU
+// projection with two rows per wave spreads its units evenly instead
+// (workgroup wg: units [wg P / nwg, (wg + 1) P / nwg), P = N; wave w every
+// 8th of them from the w-th; unit u is pair u % 8 of tile u / 8), so no
+// workgroup streams a whole tile more than another (the temporal gate/up's
+// 1408 tiles on 256 workgroups left half of them a sixth tile). Every row is
+// still summed by one wave in the same order, so the values do not depend
+// on the mapping.
+struct GemvItems {
+  int tile0, we, step, n;
+};
+template <int EPI, int R>
+__device__ __forceinline__ GemvItems gemv_items(const GemmArgs& a, int wg, int nwg, int wave) {
+  GemvItems it;
+  if constexpr (EPI == EPI_SWIGLU && R == 2) {
+    const int lo = (int)((int64_t)wg * a.N / nwg), hi = (int)((int64_t)(wg + 1) * a.N / nwg);
+    const int u0 = lo + wave;
+    it.tile0 = u0 / 8;
+    it.we = u0 % 8;
+    it.step = 1;
+    it.n = u0 < hi ? (hi - u0 + 7) / 8 : 0;
+  } else {
+    const int ntiles = n_tiles_of(EPI, a.N);
+    it.tile0 = wg;
+    it.we = wave;
+    it.step = nwg;
+    it.n = wg < ntiles ? (ntiles - wg + nwg - 1) / nwg : 0;
+  }
+  return it;
+}
+
+// The first weight batch of workgroup `wg` (of nwg) for the projection `a`,
+// requested ahead of time (while the grid barrier that precedes it completes).
 template <typename T, int KW, int EPI, int U_>
-__device__ __forceinline__ void gemv_prefetch(const GemmArgs& a, int wg,
+__device__ __forceinline__ void gemv_prefetch(const GemmArgs& a, int wg, int nwg,
                                               u32x4 (&w)[GemvShape<KW, U_>::U][GemvShape<KW, U_>::R]) {
   constexpr int R = GemvShape<KW, U_>::R, U = GemvShape<KW, U_>::U;
   const int t = tid();
-  load_wbatch<T, EPI, U, R>(a, wg, 0, t & 63, t >> 6, w, wg < n_tiles_of(EPI, a.N));
+  const GemvItems it = gemv_items<EPI, R>(a, wg, nwg, t >> 6);
+  load_wbatch<T, EPI, U, R>(a, it.tile0, 0, t & 63, it.we, w, it.n > 0);
 }
 
 // EPI_RESID: the residual values of wave `wave`'s rows of tile `tile`
@@ -803,11 +837,11 @@ __device__ __forceinline__ void gemv_core(
   __shared__ double s_red[2][16];
   __shared__ double s_tmp[KW];
 
-  const int ntiles = n_tiles_of(EPI, a.N);
   const int ngroups = a.K / VEC;  // K is a multiple of VEC
   const int nbatch = (ngroups + U * 64 - 1) / (U * 64);
+  const GemvItems it = gemv_items<EPI, R>(a, wg, nwg, wave);
 
-  int tile = wg;
+  int tile = it.tile0;
   u32x4 wa[U][R], wb[U][R];
   if (PRE) {
 #pragma unroll
@@ -816,12 +850,12 @@ __device__ __forceinline__ void gemv_core(
       for (int r = 0; r < R; ++r) wa[u][r] = pre[u][r];
   } else {
     // in flight while the input is built
-    load_wbatch<T, EPI, U, R>(a, tile, 0, lane, wave, wa, tile < ntiles);
+    load_wbatch<T, EPI, U, R>(a, tile, 0, lane, it.we, wa, it.n > 0);
   }
-  // residual rows of the first tile (one address per wave; clamped, so
+  // residual rows of the first item (one address per wave; clamped, so
   // every wave loads)
   double rpre[R];
-  load_rpre<EPI, C, R>(a, wg, wave, rpre);
+  load_rpre<EPI, C, R>(a, tile, it.we, rpre);
   QkvIn qin{};
   if constexpr (EPI == EPI_QKV) {
     __shared__ double s_rope[64][2];
@@ -836,11 +870,13 @@ __device__ __forceinline__ void gemv_core(
   else
     build_input<T, PRO, C, NTH, XP>(a, xs, s_tmp, wg == 0);
   __syncthreads();
-  if (tile < ntiles) {
+  // every wave of the workgroup has the same number of items unless they
+  // are SwiGLU units, whose epilogue needs no workgroup barrier
+  if (it.n > 0) {
     double acc[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) acc[r] = 0.0;
-    int bt = 0, parity = 0;
+    int bt = 0, parity = 0, j = 0;
 
     // consume batch (tile, bt) held in w; finish the tile after its last batch
     auto consume = [&](const u32x4 (&w)[U][R]) {
@@ -860,34 +896,36 @@ __device__ __forceinline__ void gemv_core(
         }
       }
       if (bt == nbatch - 1) {
-        finish_tile<T, EPI, C, R>(a, tile, wave, lane, acc, rpre, tile == wg, qin, s_red, parity);
+        finish_tile<T, EPI, C, R>(a, tile, it.we, lane, acc, rpre, j == 0, qin, s_red, parity);
 #pragma unroll
         for (int r = 0; r < R; ++r) acc[r] = 0.0;
       }
     };
-    // the batch after (tile, bt)
-    auto advance = [&](int& tt, int& b) {
+    // the batch after (item jj, batch b)
+    auto advance = [&](int& jj, int& b) {
       if (++b == nbatch) {
         b = 0;
-        tt += nwg;
+        ++jj;
       }
     };
 
     // the next batch is always requested (a placeholder past the last one)
     for (;;) {
-      int nt = tile, nb = bt;
-      advance(nt, nb);
-      load_wbatch<T, EPI, U, R>(a, nt, nb, lane, wave, wb, nt < ntiles);
+      int nj = j, nb = bt;
+      advance(nj, nb);
+      load_wbatch<T, EPI, U, R>(a, it.tile0 + nj * it.step, nb, lane, it.we, wb, nj < it.n);
       consume(wa);
-      if (nt >= ntiles) break;
-      tile = nt;
+      if (nj >= it.n) break;
+      j = nj;
       bt = nb;
-      advance(nt, nb);
-      load_wbatch<T, EPI, U, R>(a, nt, nb, lane, wave, wa, nt < ntiles);
+      tile = it.tile0 + j * it.step;
+      advance(nj, nb);
+      load_wbatch<T, EPI, U, R>(a, it.tile0 + nj * it.step, nb, lane, it.we, wa, nj < it.n);
       consume(wb);
-      if (nt >= ntiles) break;
-      tile = nt;
+      if (nj >= it.n) break;
+      j = nj;
       bt = nb;
+      tile = it.tile0 + j * it.step;
     }
   }
   __syncthreads();  // xs and s_red may be reused by the caller

@@ -1018,7 +1018,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
     drain_stores();                                        \
     __syncthreads();                                       \
     const unsigned old_ = grid_arrive(g);                  \
-    gemv_prefetch<T, KW, EPI_, GU_>(na_, wg, PF_);         \
+    gemv_prefetch<T, KW, EPI_, GU_>(na_, wg, nwg, PF_);         \
     if (grid_wait(g, old_)) return;                        \
   } while (0)
 #define PREFETCH_SYNC(EPI_, args_) PREFETCH_SYNC_G(EPI_, args_, GU, pf)
@@ -1163,7 +1163,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
         const int h = item / nspan, j = item % nspan;
         (void)ll_span_merge<T, HD>(c, M, l, h, nspan, j * HD / nspan, (j + 1) * HD / nspan);
       }
-    gemv_prefetch<T, KW, EPI_RESID, GU>(t_o(l), wg, pf);
+    gemv_prefetch<T, KW, EPI_RESID, GU>(t_o(l), wg, nwg, pf);
     {
       // output projection, its input polled from the flagged O[l] (no grid
       // barrier after the attention; a timed-out wait raises the abort flag,
