@@ -1637,9 +1637,32 @@ constexpr int GEMM_U = 4;  // k-steps per batch
 
 // A lane's weight groups of the U k-steps from st of tile `tile` (zero past
 // its wave's k-range or the matrix; rows past N may read anything).
+// The k-steps [first, first + count) of K segment kseg of a projection
+// (all of them when it is not split).
+__device__ __forceinline__ void gemm_segment(const GemmArgs& a, int nsteps, int kseg, int& first,
+                                             int& count) {
+  const int ks = a.ksplit > 1 ? a.ksplit : 1;
+  first = (kseg * nsteps) / ks;
+  count = ((kseg + 1) * nsteps) / ks - first;
+}
+
+// Item `item` of a projection's MFMA work: (row tile, first column, K
+// segment); the 16-column blocks of a tile are nt items apart and its K
+// segments nt * (column blocks) apart. Items: nt * ncb * ksplit.
+__device__ __forceinline__ int gemm_items(const GemmArgs& a, int epi) {
+  return n_tiles_of(epi, a.N) * ((a.B + 15) / 16) * (a.ksplit > 1 ? a.ksplit : 1);
+}
+__device__ __forceinline__ void gemm_item(const GemmArgs& a, int epi, int item, int& tile,
+                                          int& col0, int& kseg) {
+  const int nt = n_tiles_of(epi, a.N), ncb = (a.B + 15) / 16;
+  tile = item % nt;
+  col0 = ((item / nt) % ncb) * 16;
+  kseg = item / (nt * ncb);
+}
+
 template <typename T, int KW, int EPI>
 __device__ __forceinline__ void gemm_tile_weights(const GemmArgs& a, int tile, int st_off,
-                                                  u32x4 (&wv)[GEMM_U]) {
+                                                  u32x4 (&wv)[GEMM_U], int kseg = 0) {
   constexpr int VEC = VecOf<T>::N;
   constexpr int KSTEP = 4 * VEC;
   const int lane = tid() & 63, wave = tid() >> 6, r16 = lane & 15, g = lane >> 4;
@@ -1647,8 +1670,10 @@ __device__ __forceinline__ void gemm_tile_weights(const GemmArgs& a, int tile, i
   const int wrow = tile_row<EPI>(tile, 4 * (r16 & 3) + (r16 >> 2), a.N, rok);
   const T* wbase = (const T*)a.W + (size_t)(rok ? wrow : 0) * a.K + g * VEC;
   const int nsteps = (a.K + KSTEP - 1) / KSTEP;
-  const int s1 = ((wave + 1) * nsteps) / KW;
-  const int st = (wave * nsteps) / KW + st_off;
+  int g0, gn;
+  gemm_segment(a, nsteps, kseg, g0, gn);
+  const int s1 = g0 + ((wave + 1) * gn) / KW;
+  const int st = g0 + (wave * gn) / KW + st_off;
 #pragma unroll
   for (int u = 0; u < GEMM_U; ++u) {
     const int k0 = (st + u) * KSTEP + g * VEC;
@@ -1659,7 +1684,7 @@ __device__ __forceinline__ void gemm_tile_weights(const GemmArgs& a, int tile, i
 
 template <typename T, int NB, int KW, int EPI, bool DB, bool C, int RT = 1>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0, f64x4* s_acc,
-                                          const u32x4* wpre = nullptr) {
+                                          const u32x4* wpre = nullptr, int kseg = 0) {
   // RT row tiles (tile .. tile + RT - 1) share each input group's conversion;
   // each tile's sums are those of RT = 1 (same order), so RT changes no value
   constexpr int VEC = VecOf<T>::N;
@@ -1686,8 +1711,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
     wrow[r] = rok ? wrow[r] : 0;
   }
   const int nsteps = (a.K + KSTEP - 1) / KSTEP;
-  const int s0 = (wave * nsteps) / KW;
-  const int s1 = ((wave + 1) * nsteps) / KW;
+  int g0, gn;
+  gemm_segment(a, nsteps, kseg, g0, gn);
+  const int s0 = g0 + (wave * gn) / KW;
+  const int s1 = g0 + ((wave + 1) * gn) / KW;
   const bool ktail = (a.K % KSTEP) != 0;
 
   f64x4 acc[RT][NB];
@@ -1806,11 +1833,52 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0,
     for (int nb = 0; nb < NB; ++nb) s_acc[((wave * RT + r) * NB + nb) * 64 + lane] = acc[r][nb];
   __syncthreads();
   if (wave >= RT || tile + wave >= ntiles) return;
+  f64x4 sms[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     f64x4 sm = s_acc[(wave * NB + nb) * 64 + lane];
     for (int w = 1; w < KW; ++w) sm += s_acc[((w * RT + wave) * NB + nb) * 64 + lane];
-    const double v[4] = {sm[0], sm[1], sm[2], sm[3]};
+    sms[nb] = sm;
+  }
+  if (a.ksplit > 1) {
+    // K segments (RT == 1, wave 0): this segment's sums go out coherently;
+    // once they have landed, the segment counts itself in; the last one
+    // adds every segment's sums in segment order (its own from registers,
+    // the same values it stored) and runs the epilogue
+    const int ks = a.ksplit;
+    const int pc = tile * 4 + col0 / 16;  // (tile, first column block)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      double* p = a.kpart + ((((size_t)tile * 4 + col0 / 16 + nb) * ks + kseg) * 64 + lane) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_f64<true>(p + i, sms[nb][i]);
+    }
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    int old = 0;
+    if (lane == 0)
+      old = __hip_atomic_fetch_add((MOSHI_GLB int*)(a.kcnt + pc), 1, MOSHI_RLX, MOSHI_AGT);
+    old = __builtin_amdgcn_readfirstlane(old);
+    if (old != ks - 1) return;
+    if (lane == 0) __hip_atomic_store((MOSHI_GLB int*)(a.kcnt + pc), 0, MOSHI_RLX, MOSHI_AGT);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const double* p = a.kpart + (((size_t)tile * 4 + col0 / 16 + nb) * ks * 64 + lane) * 4;
+      f64x4 tot = {0.0, 0.0, 0.0, 0.0};
+      for (int s = 0; s < ks; ++s) {
+        f64x4 ps = sms[nb];
+        if (s != kseg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ps[i] = ld_f64<true>(p + (size_t)s * 256 + i);
+        tot = s == 0 ? ps : tot + ps;
+      }
+      sms[nb] = tot;
+    }
+  }
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const double v[4] = {sms[nb][0], sms[nb][1], sms[nb][2], sms[nb][3]};
     if constexpr (EPI == EPI_RESID)
       epilogue_resid<C>(a, tile + wave, g, col0 + nb * 16 + r16, v, rpre[nb]);
     else

@@ -108,6 +108,8 @@ struct moshi_ctx {
   int *tokens = nullptr, *codes = nullptr;
   ArgPart* apart = nullptr;  // per-tile argmax partials of the last head
   double* attn_part = nullptr;
+  double* kpart = nullptr;  // K-segment sums of split projections (GemmArgs::kpart)
+  int* kcnt = nullptr;      // their counters
   int *d_frames = nullptr, *d_live = nullptr;
   int64_t* d_pos = nullptr;
   int* d_err = nullptr;  // set by the embedding when a live code was out of range
@@ -394,6 +396,8 @@ GemmArgs d_dn_args(const moshi_ctx* c, int s, int l) {
   GemmArgs a = gemm_base(c);
   a.W = c->dep_down[s * c->Ld + l]; a.N = c->Dd; a.K = c->Fd; a.X = c->actd; a.ldx = c->Fd;
   a.resid = c->y; a.ldr = c->Dd; a.ssq_out = c->ssq_d;
+  a.ksplit = gemm_ksplit(c->B, a.K, gemm_tiles(EPI_RESID, a.N));
+  a.kpart = c->kpart; a.kcnt = c->kcnt;
   return a;
 }
 
@@ -1267,6 +1271,10 @@ int alloc_buffers(moshi_ctx* c) {
       {(void**)&c->d_samp, B * sizeof(SampleParams)},
       {(void**)&c->d_inv_freq, (size_t)(c->hd / 2) * 8},
       {&c->staging, (size_t)c->W * D * es},
+      // K-segment sums and counters of split MFMA projections (zeroed here;
+      // each counter is reset by the segment that completes it)
+      {(void**)&c->kpart, (size_t)(Dd + 15) / 16 * 4 * GEMM_KSPLIT_MAX * 64 * 4 * 8},
+      {(void**)&c->kcnt, (size_t)(Dd + 15) / 16 * 4 * 4},
   };
   for (auto& r : reqs) {
     hipError_t e = dalloc(c, r.p, r.bytes);

@@ -74,6 +74,14 @@ struct GemmArgs {
   void* ring_v;
   int64_t slot_stride, layer_off, head_stride;  // ring strides, elements
   int cap;                                      // ring capacity
+  // K split over workgroups (MFMA path; gemm_ksplit): ksplit > 1 segments of
+  // the k-steps, each summed by its own workgroup into kpart [tile][4][ksplit]
+  // [64 lanes] (f64x4); the last segment of a (tile, 16-column block group)
+  // to finish (counter kcnt [tile][4], back to 0 after) adds the segments in
+  // order and runs the epilogue
+  int ksplit;
+  double* kpart;
+  int* kcnt;
 };
 
 struct AttnArgs {
@@ -346,6 +354,9 @@ void set_gemv_grid(int n);
 // (33..64, at most / more than 512 tiles) for inputs of 4096 or wider, 8 / 4
 // for narrower ones (up to 32 / 33..64 sessions).
 int gemm_kw(int dtype, int B, int K, int tiles);
+// K segments of an MFMA projection (1: none); see GemmArgs::ksplit.
+int gemm_ksplit(int B, int K, int tiles);
+constexpr int GEMM_KSPLIT_MAX = 4;
 // kw from gemm_kw (B > 1: 16 or 8 up to 32 sessions, 12 or 4 above). With
 // B > 1 and PRO_NORM / PRO_CAST, xn_out must be a [B][K] buffer: the rounded
 // input vectors are written there first.

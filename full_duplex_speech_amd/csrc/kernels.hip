@@ -50,11 +50,12 @@ __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
 // Two or more sessions: fp64 MFMA 16x16x4 tiles
 // ---------------------------------------------------------------------------
 
-// 16 RT weight rows x 16 NB session columns per workgroup (see gemm_tile).
+// 16 RT weight rows x 16 NB session columns per workgroup (see gemm_tile);
+// K segment blockIdx.y of a.ksplit.
 template <typename T, int NB, int KW, int EPI, bool DB, int RT = 1>
 __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
   __shared__ f64x4 s_acc[KW * RT * NB * 64];
-  gemm_tile<T, NB, KW, EPI, DB, false, RT>(a, blockIdx.x * RT, 0, s_acc);
+  gemm_tile<T, NB, KW, EPI, DB, false, RT>(a, blockIdx.x * RT, 0, s_acc, nullptr, blockIdx.y);
 }
 
 // Input vectors for the MFMA path: xn[b][k] = round(x[b][k] * scale_b * g[k])
@@ -583,6 +584,20 @@ int gemm_kw(int dtype, int B, int K, int tiles) {
   return B <= 32 ? 8 : 4;
 }
 
+int gemm_ksplit(int B, int K, int tiles) {
+  // long inputs with few row tiles (the depformer's down projection: 64
+  // tiles, K = 2816) up to 32 sessions: a whole-K tile per workgroup left
+  // most CUs idle and each wave with ~44 dependent k-steps (16 sessions: the
+  // down phases 1.33 -> 0.86 ms per step, the step 15.02 -> 14.51 ms). At 33+
+  // sessions the multi-session depformer already spreads 4 column blocks
+  // per tile (2 or 4 segments: within noise of none); the temporal
+  // projections (256+ tiles) measured no faster split in a probe.
+  if (B < 2 || K < 2048 || tiles > 64) return 1;
+  const char* env = getenv("MOSHI_KSPLIT");  // segments override (measurement)
+  if (env && env[0] >= '1' && env[0] <= '4' && env[1] == 0) return env[0] - '0';
+  return B <= 32 ? 4 : 1;
+}
+
 // Workgroups of the one-session projection: at most one per CU (the kernel
 // loops over row tiles), never more than there are tiles.
 static int g_gemv_grid = 256;
@@ -610,7 +625,9 @@ static hipError_t launch_gemv_kw(int pro, int epi, const GemmArgs& a, hipStream_
 
 template <typename T, int NB, int KW, bool DB, int RT = 1>
 static hipError_t launch_gemm_db(int epi, const GemmArgs& a, hipStream_t st) {
-  dim3 grid((gemm_tiles(epi, a.N) + RT - 1) / RT), block(64 * KW);
+  if (a.ksplit > GEMM_KSPLIT_MAX || (a.ksplit > 1 && (RT != 1 || a.kpart == nullptr || a.kcnt == nullptr)))
+    return hipErrorInvalidValue;
+  dim3 grid((gemm_tiles(epi, a.N) + RT - 1) / RT, a.ksplit > 1 ? a.ksplit : 1), block(64 * KW);
   switch (epi) {
     case EPI_STORE:
       hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE, DB, RT>), grid, block, 0, st, a);
@@ -649,7 +666,8 @@ static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
   // workgroups of a projection with fewer tiles or, with one column block,
   // the workgroups per CU)
   if constexpr (NB == 4 && KW <= 8)  // (LDS: KW x 2 x NB x 2 KB)
-    if (gemm_tiles(epi, a.N) >= 1024) return launch_gemm_db<T, NB, KW, false, 2>(epi, a, st);
+    if (gemm_tiles(epi, a.N) >= 1024 && a.ksplit <= 1)
+      return launch_gemm_db<T, NB, KW, false, 2>(epi, a, st);
   return launch_gemm_db<T, NB, KW, false>(epi, a, st);
 }
 

@@ -1400,8 +1400,9 @@ __global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* 
   u32x4 wpf[GEMM_U];
   {
     const GemmArgs a = uni(A.d_in);
-    const int nt = n_tiles_of(EPI_STORE, a.N);
-    if (wg < nt * ((a.B + 15) / 16)) gemm_tile_weights<T, KW, EPI_STORE>(a, wg % nt, 0, wpf);
+    int tl, c0, ksg;
+    gemm_item(a, EPI_STORE, wg, tl, c0, ksg);
+    if (wg < gemm_items(a, EPI_STORE)) gemm_tile_weights<T, KW, EPI_STORE>(a, tl, 0, wpf, ksg);
   }
   Grid g;
   if (grid_init(g, uni(A.bar), parity, uni(A.abort), uni(A.spin_limit), trace)) return;
@@ -1410,16 +1411,18 @@ __global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* 
     if (grid_sync(g)) return;   \
   } while (0)
 
-  // projection tiles: (row tile, 16-column block); the blocks of one tile are
-  // nt items apart, so with nt a multiple of 8 they run on the same XCD and
-  // share its L2 copy of the tile's weights. The first item's first weight
-  // batch was requested during the barrier before the phase (sync_pf).
+  // projection items: (row tile, 16-column block, K segment) (gemm_item);
+  // the blocks of one tile are nt items apart, so with nt a multiple of 8
+  // they run on the same XCD and share its L2 copy of the tile's weights.
+  // The first item's first weight batch was requested during the barrier
+  // before the phase (sync_pf).
   auto gemm_phase = [&](auto epi_c, const GemmArgs& a) {
     constexpr int EPI = decltype(epi_c)::value;
-    const int nt = n_tiles_of(EPI, a.N), ncb = (a.B + 15) / 16;
-    for (int item = wg; item < nt * ncb; item += nwg) {
-      gemm_tile<T, 1, KW, EPI, true, true>(a, item % nt, (item / nt) * 16, s_acc,
-                                           item == wg ? wpf : nullptr);
+    const int n = gemm_items(a, EPI);
+    for (int item = wg; item < n; item += nwg) {
+      int tl, c0, ksg;
+      gemm_item(a, EPI, item, tl, c0, ksg);
+      gemm_tile<T, 1, KW, EPI, true, true>(a, tl, c0, s_acc, item == wg ? wpf : nullptr, ksg);
       __syncthreads();
     }
   };
@@ -1431,8 +1434,9 @@ __global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* 
     drain_stores();
     __syncthreads();
     const unsigned old = grid_arrive(g);
-    const int nt = n_tiles_of(EPI, next.N);
-    if (wg < nt * ((next.B + 15) / 16)) gemm_tile_weights<T, KW, EPI>(next, wg % nt, 0, wpf);
+    int tl, c0, ksg;
+    gemm_item(next, EPI, wg, tl, c0, ksg);
+    if (wg < gemm_items(next, EPI)) gemm_tile_weights<T, KW, EPI>(next, tl, 0, wpf, ksg);
     return grid_wait(g, old);
   };
   // rounded (normed) input vectors, one column per workgroup; the projection
