@@ -1682,15 +1682,16 @@ __device__ __forceinline__ void gemm_tile_weights(const GemmArgs& a, int tile, i
   }
 }
 
-template <typename T, int NB, int KW, int EPI, bool DB, bool C, int RT = 1>
+template <typename T, int NB, int KW, int EPI, bool DB, bool C, int RT = 1, int U = GEMM_U>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, int tile, int col0, f64x4* s_acc,
                                           const u32x4* wpre = nullptr, int kseg = 0) {
   // RT row tiles (tile .. tile + RT - 1) share each input group's conversion;
-  // each tile's sums are those of RT = 1 (same order), so RT changes no value
+  // each tile's sums are those of RT = 1 (same order), so RT changes no value;
+  // neither does U (k-steps per batch: a wave sums its k-steps in order)
   constexpr int VEC = VecOf<T>::N;
   constexpr int KSTEP = 4 * VEC;
-  constexpr int U = GEMM_U;
   static_assert(RT == 1 || !DB, "several row tiles: single batches");
+  static_assert(!DB || U == GEMM_U, "double-buffered batches take gemm_tile_weights' first batch");
   static_assert(RT <= KW, "one epilogue wave per row tile");
   const int lane = tid() & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid() >> 6);

@@ -52,10 +52,10 @@ __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
 
 // 16 RT weight rows x 16 NB session columns per workgroup (see gemm_tile);
 // K segment blockIdx.y of a.ksplit.
-template <typename T, int NB, int KW, int EPI, bool DB, int RT = 1>
+template <typename T, int NB, int KW, int EPI, bool DB, int RT = 1, int U = GEMM_U>
 __global__ __launch_bounds__(64 * KW) void gemm_kernel(GemmArgs a) {
   __shared__ f64x4 s_acc[KW * RT * NB * 64];
-  gemm_tile<T, NB, KW, EPI, DB, false, RT>(a, blockIdx.x * RT, 0, s_acc, nullptr, blockIdx.y);
+  gemm_tile<T, NB, KW, EPI, DB, false, RT, U>(a, blockIdx.x * RT, 0, s_acc, nullptr, blockIdx.y);
 }
 
 // Input vectors for the MFMA path: xn[b][k] = round(x[b][k] * scale_b * g[k])
@@ -623,26 +623,26 @@ static hipError_t launch_gemv_kw(int pro, int epi, const GemmArgs& a, hipStream_
   return hipErrorInvalidValue;
 }
 
-template <typename T, int NB, int KW, bool DB, int RT = 1>
+template <typename T, int NB, int KW, bool DB, int RT = 1, int U = GEMM_U>
 static hipError_t launch_gemm_db(int epi, const GemmArgs& a, hipStream_t st) {
   if (a.ksplit > GEMM_KSPLIT_MAX || (a.ksplit > 1 && (RT != 1 || a.kpart == nullptr || a.kcnt == nullptr)))
     return hipErrorInvalidValue;
   dim3 grid((gemm_tiles(epi, a.N) + RT - 1) / RT, a.ksplit > 1 ? a.ksplit : 1), block(64 * KW);
   switch (epi) {
     case EPI_STORE:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE, DB, RT>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_STORE, DB, RT, U>), grid, block, 0, st, a);
       break;
     case EPI_RESID:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_RESID, DB, RT>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_RESID, DB, RT, U>), grid, block, 0, st, a);
       break;
     case EPI_QKV:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_QKV, DB, RT>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_QKV, DB, RT, U>), grid, block, 0, st, a);
       break;
     case EPI_SWIGLU:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_SWIGLU, DB, RT>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_SWIGLU, DB, RT, U>), grid, block, 0, st, a);
       break;
     case EPI_ARGMAX:
-      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_ARGMAX, DB, RT>), grid, block, 0, st, a);
+      hipLaunchKernelGGL((gemm_kernel<T, NB, KW, EPI_ARGMAX, DB, RT, U>), grid, block, 0, st, a);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -668,6 +668,13 @@ static hipError_t launch_gemm_kw(int epi, const GemmArgs& a, hipStream_t st) {
   if constexpr (NB == 4 && KW <= 8)  // (LDS: KW x 2 x NB x 2 KB)
     if (gemm_tiles(epi, a.N) >= 1024 && a.ksplit <= 1)
       return launch_gemm_db<T, NB, KW, false, 2>(epi, a, st);
+  // up to 16 sessions, the 1408-tile gate/up: two row tiles per wave with
+  // two k-steps per batch (58 VGPRs: still two 16-wave workgroups per CU);
+  // 70.3 -> 65.2 us in a probe of its tiles, slower for the 256-tile
+  // projections (half the workgroups)
+  if constexpr (NB == 1 && KW == 16)
+    if (epi == EPI_SWIGLU && gemm_tiles(epi, a.N) >= 1024 && a.ksplit <= 1)
+      return launch_gemm_db<T, 1, 16, false, 2, 2>(epi, a, st);
   return launch_gemm_db<T, NB, KW, false>(epi, a, st);
 }
 
