@@ -1,8 +1,9 @@
 """The persistent multi-session depformer kernel (capacity 2..64) against the
 per-operation kernels (MOSHI_DEP_MULTI=0): every output a step returns is
 bit-identical, at capacities whose projection tiles take 8 waves (B <= 32)
-and 4 (B > 32), with free slots, teacher forcing and the depformer readings
-(dep_q, the ring reading, the final norm); a few session-frames are also
+and 4 (B > 32), with free slots, teacher forcing, the depformer readings
+(dep_q, the ring reading, the final norm) and a down projection split over
+K into segments; a few session-frames are also
 checked against the oracle; and its bounded-wait failure path (forced from
 the host by a tiny spin limit: every workgroup exits)."""
 import os
@@ -114,6 +115,10 @@ CASES = {
     "ragged_bf16_b36_variants": (spec.RAGGED.replace(dep_q=8, dep_ref_ring=True,
                                                      dep_final_norm=True), 36, [0, 20], 2, True,
                                  [35]),
+    # a down projection long enough to be split over K (4 segments up to 32
+    # sessions), its K (2104) not a multiple of the 32-element k-step
+    "ksplit_bf16_b5": (spec.RAGGED.replace(dep_ffn=2104), 5, [1], 3, True, [0]),
+    "ksplit_bf16_b17": (spec.RAGGED.replace(dep_ffn=2104), 17, [3, 16], 2, False, [2]),
 }
 
 
