@@ -1370,7 +1370,7 @@ __global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* 
   constexpr int NW = KW;
   extern __shared__ __align__(16) unsigned char s_dyn[];  // the weight pointer table
   __shared__ __align__(16) DepMultiArgs sA;
-  __shared__ f64x4 s_acc[KW * 64];
+  __shared__ f64x4 s_acc[KW * 2 * 64];  // two row tiles per wave: the gate/up
   __shared__ double s_red[NW];
   __shared__ double s_v[NW];
   __shared__ int s_i[NW];
@@ -1423,6 +1423,25 @@ __global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* 
       int tl, c0, ksg;
       gemm_item(a, EPI, item, tl, c0, ksg);
       gemm_tile<T, 1, KW, EPI, true, true>(a, tl, c0, s_acc, item == wg ? wpf : nullptr, ksg);
+      __syncthreads();
+    }
+  };
+  // A gate/up with more items than workgroups: items of two row tiles (each
+  // wave sums both over its k-steps, sharing every input group's conversion;
+  // the values are those of one tile per item), so no workgroup runs two
+  // items one after the other. Single batches: no prefetched first batch.
+  auto gu_pairs = [&](const GemmArgs& a) {
+    const int nt = n_tiles_of(EPI_SWIGLU, a.N), ncb = (a.B + 15) / 16;
+    return a.ksplit <= 1 && nt * ncb > nwg;
+  };
+  auto gemm_phase_gu = [&](const GemmArgs& a) {
+    if (!gu_pairs(a)) {
+      gemm_phase(IntC<EPI_SWIGLU>{}, a);
+      return;
+    }
+    const int nt = n_tiles_of(EPI_SWIGLU, a.N), nt2 = (nt + 1) / 2, ncb = (a.B + 15) / 16;
+    for (int item = wg; item < nt2 * ncb; item += nwg) {
+      gemm_tile<T, 1, KW, EPI_SWIGLU, false, true, 2>(a, (item % nt2) * 2, (item / nt2) * 16, s_acc);
       __syncthreads();
     }
   };
@@ -1525,8 +1544,8 @@ __global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* 
       gemm_phase(IntC<EPI_RESID>{}, d_o(s, l));
       DM_SYNC();
       norm_phase(IntC<PRO_NORM>{}, d_gu(s, l));
-      if (sync_pf(IntC<EPI_SWIGLU>{}, d_gu(s, l))) return;
-      gemm_phase(IntC<EPI_SWIGLU>{}, normed(d_gu(s, l)));
+      if (gu_pairs(d_gu(s, l)) ? grid_sync(g) : sync_pf(IntC<EPI_SWIGLU>{}, d_gu(s, l))) return;
+      gemm_phase_gu(normed(d_gu(s, l)));
       if (sync_pf(IntC<EPI_RESID>{}, d_dn(s, l))) return;
       gemm_phase(IntC<EPI_RESID>{}, d_dn(s, l));
       DM_SYNC();
