@@ -1932,7 +1932,7 @@ int moshi_time_kernels(moshi_ctx* c, const int32_t* frames, int32_t n_steps, dou
 int moshi_internal::ctx_device(const moshi_ctx* c) { return c ? c->device : -1; }
 
 int moshi_internal::enqueue_static(moshi_ctx* c, const int32_t* d_frames, int32_t* d_text_token,
-                                   int32_t* d_audio_codes, uint32_t seq) {
+                                   int32_t* d_audio_codes) {
   int rc = check_ctx(c);
   if (rc) return rc;
   if (!d_frames) return fail(c, MOSHI_E_INVALID, "frames is NULL");
@@ -1944,8 +1944,12 @@ int moshi_internal::enqueue_static(moshi_ctx* c, const int32_t* d_frames, int32_
   int* tok = d_text_token ? d_text_token : c->tokens;
   int* codes = d_audio_codes ? d_audio_codes : c->codes;
   if (live_count(c) > 0) {
-    CKD(c, launch_step(c->dtype, c->hd, c->hdd, c->d_step_static, d_frames, tok, codes,
-                       (int)(seq & 1u), seq, c->step_grid, c->step_lds, c->stream, nullptr));
+    uint32_t seq = 0;
+    int parity = 0;
+    moshi_internal::static_launch_ids(c->device, &seq, &parity);
+    CKD(c, launch_step(c->dtype, c->hd, c->hdd, c->d_step_static, d_frames, tok, codes, parity, seq,
+                       c->step_grid, c->step_lds, c->stream, nullptr));
+    moshi_internal::static_launch_done(c->device);
   } else {
     // no live session: every output reads -1 (a fill kernel, no memset)
     CKD(c, launch_finish_outputs(tok, codes, c->d_live, c->B, c->S, c->S_run, c->stream));

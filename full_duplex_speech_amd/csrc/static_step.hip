@@ -7,12 +7,14 @@
 //
 // Every call on one GPU shares that GPU's array and finds the last call's
 // contents there. Nothing has to be cleared per call: each launch clears the
-// barrier counter set the next launch uses (the array starts zeroed), and a
-// flagged word only counts when its flag equals the launch's sequence number,
-// which is unique per device (a host counter per device that skips 0), so a
-// word another context or an earlier call left behind is never taken as
-// current. Calls that overlap on one GPU (two streams, two threads) race and
-// are not supported.
+// barrier counter set the next launch on the device uses (the array starts
+// zeroed; the sets alternate per launch on the device, not per call, since a
+// call with no live session launches nothing), and a flagged word only
+// counts when its flag equals the launch's sequence number, which is unique
+// per device (a host counter per device that skips 0), so a word another
+// context or an earlier call left behind is never taken as current. Calls
+// that overlap on one GPU (two streams, two threads) race and are not
+// supported.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,6 +34,7 @@ constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 void* g_ptr[kMaxDevices];      // device address of `scratch`, per device
 uint32_t g_seq[kMaxDevices];   // last launch sequence number, per device
+int g_par[kMaxDevices];        // barrier counter set of the next launch, per device
 
 }  // namespace
 
@@ -49,15 +52,21 @@ void* moshi_internal::static_scratch_setup(int device, size_t* bytes) {
   return g_ptr[device];
 }
 
+void moshi_internal::static_launch_ids(int device, uint32_t* seq, int* parity) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (++g_seq[device] == 0) g_seq[device] = 1;  // 0 is the zeroed arena's flag
+  *seq = g_seq[device];
+  *parity = g_par[device];
+}
+
+void moshi_internal::static_launch_done(int device) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  g_par[device] ^= 1;
+}
+
 extern "C" int moshi_step_enqueue_noalloc(moshi_ctx* ctx, const int32_t* d_frames,
                                           int32_t* d_text_token, int32_t* d_audio_codes) {
   const int dev = moshi_internal::ctx_device(ctx);
   if (dev < 0 || dev >= kMaxDevices) return MOSHI_E_INVALID;
-  uint32_t seq;
-  {
-    std::lock_guard<std::mutex> lk(g_mu);
-    if (++g_seq[dev] == 0) g_seq[dev] = 1;  // 0 is the zeroed arena's flag
-    seq = g_seq[dev];
-  }
-  return moshi_internal::enqueue_static(ctx, d_frames, d_text_token, d_audio_codes, seq);
+  return moshi_internal::enqueue_static(ctx, d_frames, d_text_token, d_audio_codes);
 }

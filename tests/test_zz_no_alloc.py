@@ -74,3 +74,35 @@ def test_noalloc_rejects_what_does_not_fit():
         M.moshi_step_enqueue_noalloc(ctx, d.ptr)
     assert e.value.status == M.MOSHI_E_INVALID and "step kernel" in str(e.value)
     M.moshi_destroy(ctx)
+
+
+def test_noalloc_after_a_call_that_launches_nothing():
+    """A call with no live session launches no step kernel (its outputs read
+    -1); the barrier counter sets alternate per launch on the device, not per
+    call, so the launches after it still find a cleared set: several frames
+    then equal moshi_step_enqueue's bit for bit."""
+    shape = spec.TINY
+    weights = wl.make_weights(shape, 96, gains="random")
+    ref, na = new_engine(shape, weights, 1), new_engine(shape, weights, 1)
+    T = 5
+    fr = wl.frames(shape, 97, 0, 0, T)
+    empty_ref, empty_na = _bufs(shape, fr[:1]), _bufs(shape, fr[:1])
+    M.moshi_step_enqueue(ref, *(x.ptr for x in empty_ref[0]))
+    M.moshi_step_enqueue_noalloc(na, *(x.ptr for x in empty_na[0]))
+    M.moshi_sync(na)
+    assert empty_na[0][1].read()[0] == -1 and np.all(empty_na[0][2].read() == -1)
+    for ctx in (ref, na):
+        assert M.moshi_session_join(ctx) == 0
+    b_ref, b_na = _bufs(shape, fr), _bufs(shape, fr)
+    for t in range(T):
+        M.moshi_step_enqueue(ref, *(x.ptr for x in b_ref[t]))
+        M.moshi_step_enqueue_noalloc(na, *(x.ptr for x in b_na[t]))
+    for ctx in (ref, na):
+        M.moshi_sync(ctx)
+    for t in range(T):
+        assert np.array_equal(b_ref[t][1].read(), b_na[t][1].read()), f"t={t}: text token"
+        assert np.array_equal(b_ref[t][2].read(), b_na[t][2].read()), f"t={t}: codes"
+    assert M.moshi_session_info(ref, 0) == M.moshi_session_info(na, 0)
+    for ctx in (ref, na):
+        M.moshi_destroy(ctx)
+    log("no-alloc step after a call that launched nothing: bit-identical")
