@@ -43,15 +43,18 @@ static_assert(KW == GEMV_KW, "the step kernel's projections use the one-session 
 constexpr int GU = 4;
 
 // Barrier words of one set (32-bit words): one 4 KB page per XCD holding its
-// arrival counter, its registration count and its release word (each on a
-// 128-byte line of its own), then a page with the grid-wide counters. The
-// pages keep different XCDs' counters, and the release words every
-// workgroup polls, in different memory channels: 256 workgroups polling one
-// word would queue every other access to that word's channel behind them.
+// arrival counter, its registration count, its done words (one per XCD, on
+// one 128-byte line) and a copy of every workgroup's arrival word (each group
+// on lines of its own), then a page with the grid-wide start counter. Each
+// XCD's workgroups poll only their own page, so the polled lines of
+// different XCDs sit in different memory channels: 256 workgroups polling
+// one word would queue every other access to that word's channel behind
+// them.
 constexpr int MAX_XCC = 16;
 constexpr int BW_PAGE = 1024;
-constexpr int BW_LOCAL = 0, BW_REG = 32, BW_RELEASE = 64;  // within an XCD's page
-constexpr int BW_FLAT = MAX_XCC * BW_PAGE, BW_GLOBAL = BW_FLAT + 32;
+constexpr int BW_LOCAL = 0, BW_REG = 32, BW_DONE = 64, BW_ARRIVE = 256;  // within an XCD's page
+constexpr int BW_MAXWG = BW_PAGE - BW_ARRIVE;  // workgroups a grid barrier supports
+constexpr int BW_FLAT = MAX_XCC * BW_PAGE;
 static_assert(STEP_BAR_WORDS >= (MAX_XCC + 1) * BW_PAGE, "barrier words");
 
 __device__ __forceinline__ unsigned xcc_id() {
@@ -68,7 +71,8 @@ struct Grid {
   unsigned tshift; // trace entries written at flagged hand-offs (no barrier)
   unsigned xcc;    // this workgroup's XCD
   unsigned xcc_n;  // workgroups on it
-  unsigned n_xcc;  // XCDs with at least one workgroup
+  unsigned xmask;  // XCDs with at least one workgroup (bit x: XCD x)
+  bool words;      // barrier form: per-workgroup arrival words (else XCD counters)
 };
 
 // A value every lane holds equally (read from LDS), as a wave-uniform (scalar)
@@ -108,38 +112,91 @@ __device__ __forceinline__ int poll_until(unsigned* ctr, unsigned target, int* a
 }
 
 // Grid barrier in two halves, so that loads can be issued in between:
-// grid_arrive (after drain_stores() and a workgroup barrier) counts this
-// workgroup in; grid_wait completes the count and waits. Loads issued between
-// the two are younger than the arrival atomic, so reading its result does not
-// wait for them; the polls do, but those loads (a weight prefetch) land well
-// before the grid does. Every thread of every workgroup calls both; true =
-// abort.
+// grid_arrive (after drain_stores() and a workgroup barrier) posts this
+// workgroup's arrival; grid_wait waits for every other workgroup's. Loads
+// issued between the two do not delay the arrival; the polls wait for them,
+// but those loads (a weight prefetch) land well before the grid does. Every
+// thread of every workgroup calls both; true = abort. A workgroup's stores
+// landed before it arrived (drain_stores), its arrival before anything a
+// poll can see, so its stores are visible once the polls let a workgroup go.
+//
+// Two forms (chosen per kernel at grid_init, measured):
+// - arrival words: threads x < 16 store the barrier's number into this
+//   workgroup's arrival word in XCD x's page (one store per XCD with
+//   workgroups, issued together; no atomic round trip); wave 0 reads its own
+//   XCD's copy of all arrival words (16 bytes per lane per load) until every
+//   one has reached this barrier. Shortest path (one store, one poll), but
+//   every poll reads 4 bytes per workgroup: used by the one-session step
+//   kernel (256 workgroups, long phases).
+// - XCD counters: thread 0 counts the workgroup into its XCD's counter; the
+//   last arrival of an XCD (the returned count tells) writes the barrier's
+//   number into that XCD's done word of every XCD's page, and wave 0 polls
+//   the done words of its own page (one lane per XCD; one line). One atomic
+//   round trip more, but polls read one line: used by the multi-session
+//   depformer kernel (up to 512 workgroups, short phases).
+// Arrival words and done words only grow, so a workgroup already past this
+// barrier still counts as arrived.
 __device__ __forceinline__ unsigned grid_arrive(Grid& g) {
   g.idx += 1;
   unsigned old = 0;
-  if (threadIdx.x == 0)
+  if (g.words) {
+    if (threadIdx.x < MAX_XCC && ((g.xmask >> threadIdx.x) & 1u))
+      __hip_atomic_store((MOSHI_GLB unsigned*)g.set + threadIdx.x * BW_PAGE + BW_ARRIVE + blockIdx.x,
+                         g.idx, MOSHI_RLX, MOSHI_AGT);
+  } else if (threadIdx.x == 0) {
     old = __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + g.xcc * BW_PAGE + BW_LOCAL, 1u,
                                  MOSHI_RLX, MOSHI_AGT);
+  }
   return old;
 }
 
 __device__ __forceinline__ bool grid_wait(Grid& g, unsigned old) {
   __shared__ int s_leave;
-  if (threadIdx.x == 0) {
-    // the last arrival of the last XCD releases everyone through the release
-    // words, one per XCD (polling the counters themselves slows their
-    // increments)
-    if (old + 1 == g.idx * g.xcc_n) {
-      const unsigned og =
-          __hip_atomic_fetch_add((MOSHI_GLB unsigned*)g.set + BW_GLOBAL, 1u, MOSHI_RLX, MOSHI_AGT);
-      if (og + 1 == g.idx * g.n_xcc)
-        for (int x = 0; x < MAX_XCC; ++x)
-          __hip_atomic_store((MOSHI_GLB unsigned*)g.set + x * BW_PAGE + BW_RELEASE, g.idx, MOSHI_RLX,
-                             MOSHI_AGT);
+  if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const unsigned* page = g.set + g.xcc * BW_PAGE;
+    const int n = gridDim.x;
+    const bool mine = lane < MAX_XCC && ((g.xmask >> lane) & 1u);
+    if (!g.words) {
+      old = __builtin_amdgcn_readfirstlane(old);  // thread 0's arrival count
+      if (old + 1 == g.idx * g.xcc_n && mine)
+        __hip_atomic_store((MOSHI_GLB unsigned*)g.set + lane * BW_PAGE + BW_DONE + g.xcc, g.idx,
+                           MOSHI_RLX, MOSHI_AGT);
     }
-    s_leave = poll_until(g.set + g.xcc * BW_PAGE + BW_RELEASE, g.idx, g.abort, g.limit);
-    if (g.trace != nullptr && blockIdx.x == 0)
-      *(MOSHI_GLB uint64_t*)(g.trace + g.idx + g.tshift) = wall_clock64();
+    int spins = 0, leave = 0;
+    while (true) {
+      bool ok = true;
+      if (g.words) {
+        for (int base = 0; base < n; base += 256) {
+          const int w0 = base + lane * 4;
+          if (w0 < n) {
+            const u32x4 q = ld16_coh(page + BW_ARRIVE, (uint32_t)w0 * 4u);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ok = ok && (w0 + i >= n || (int)(q[i] - g.idx) >= 0);
+          }
+        }
+      } else if (mine) {
+        ok = (int)(__hip_atomic_load((MOSHI_GLB unsigned*)page + BW_DONE + lane, MOSHI_RLX,
+                                     MOSHI_AGT) - g.idx) >= 0;
+      }
+      if (__all(ok)) break;
+      if (++spins > g.limit) {
+        if (lane == 0) __hip_atomic_store((MOSHI_GLB int*)g.abort, 1, MOSHI_RLX, MOSHI_AGT);
+        leave = 1;
+        break;
+      }
+      if ((spins & 15) == 0 &&
+          __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load((MOSHI_GLB int*)g.abort, MOSHI_RLX, MOSHI_AGT))) {
+        leave = 1;
+        break;
+      }
+    }
+    if (lane == 0) {
+      s_leave = leave;
+      if (g.trace != nullptr && blockIdx.x == 0)
+        *(MOSHI_GLB uint64_t*)(g.trace + g.idx + g.tshift) = wall_clock64();
+    }
   }
   __syncthreads();
   return s_leave != 0;
@@ -156,7 +213,7 @@ __device__ __forceinline__ bool grid_sync(Grid& g) {
 // the previous launch, which used it, has finished), count the workgroups of
 // every XCD, and wait for all of them (flat barrier).
 __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, int parity, int* abort, int limit,
-                                          uint64_t* trace) {
+                                          uint64_t* trace, bool words) {
   __shared__ int s_leave;
   __shared__ unsigned s_cnt[MAX_XCC];
   g.set = bar + parity * STEP_BAR_WORDS;
@@ -166,16 +223,24 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, int parity, in
   g.idx = 0;
   g.tshift = 0;
   g.xcc = xcc_id();
+  g.words = words;
+  if (gridDim.x > (unsigned)BW_MAXWG) {  // the launchers never ask for more; leave, reported as an abort
+    if (threadIdx.x == 0) __hip_atomic_store((MOSHI_GLB int*)abort, 1, MOSHI_RLX, MOSHI_AGT);
+    return true;
+  }
   unsigned* other = bar + (parity ^ 1) * STEP_BAR_WORDS;
-  if (blockIdx.x == 0 && threadIdx.x < MAX_XCC) {
-    unsigned* page = other + threadIdx.x * BW_PAGE;
-    __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_LOCAL, 0u, MOSHI_RLX, MOSHI_AGT);
-    __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_REG, 0u, MOSHI_RLX, MOSHI_AGT);
-    __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_RELEASE, 0u, MOSHI_RLX, MOSHI_AGT);
-    if (threadIdx.x == 0) {
-      __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_FLAT, 0u, MOSHI_RLX, MOSHI_AGT);
-      __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_GLOBAL, 0u, MOSHI_RLX, MOSHI_AGT);
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i < MAX_XCC * BW_MAXWG; i += blockDim.x)
+      __hip_atomic_store((MOSHI_GLB unsigned*)other + (i / BW_MAXWG) * BW_PAGE + BW_ARRIVE + i % BW_MAXWG,
+                         0u, MOSHI_RLX, MOSHI_AGT);
+    if (threadIdx.x < MAX_XCC) {
+      unsigned* page = other + threadIdx.x * BW_PAGE;
+      __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_LOCAL, 0u, MOSHI_RLX, MOSHI_AGT);
+      __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_REG, 0u, MOSHI_RLX, MOSHI_AGT);
+      for (int x = 0; x < MAX_XCC; ++x)
+        __hip_atomic_store((MOSHI_GLB unsigned*)page + BW_DONE + x, 0u, MOSHI_RLX, MOSHI_AGT);
     }
+    if (threadIdx.x == 0) __hip_atomic_store((MOSHI_GLB unsigned*)other + BW_FLAT, 0u, MOSHI_RLX, MOSHI_AGT);
   }
   drain_stores();
   __syncthreads();
@@ -192,8 +257,8 @@ __device__ __forceinline__ bool grid_init(Grid& g, unsigned* bar, int parity, in
     s_cnt[threadIdx.x] = __hip_atomic_load((MOSHI_GLB unsigned*)g.set + threadIdx.x * BW_PAGE + BW_REG,
                                            MOSHI_RLX, MOSHI_AGT);
   __syncthreads();
-  g.n_xcc = 0;
-  for (int i = 0; i < MAX_XCC; ++i) g.n_xcc += s_cnt[i] ? 1u : 0u;
+  g.xmask = 0;
+  for (int i = 0; i < MAX_XCC; ++i) g.xmask |= s_cnt[i] ? (1u << i) : 0u;
   g.xcc_n = s_cnt[g.xcc];
   __syncthreads();
   return false;
@@ -1008,7 +1073,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const StepArgs* P,
             o_dh = uni(A.o_dh);
   const int64_t t_lel = uni(A.t_layer_elems), d_lel = uni(A.d_layer_elems);
   Grid g;
-  if (grid_init(g, uni(A.bar), parity, uni(A.abort), uni(A.spin_limit), trace)) return;
+  if (grid_init(g, uni(A.bar), parity, uni(A.abort), uni(A.spin_limit), trace, true)) return;
   // first weight batch of the next projection, requested before each barrier
   u32x4 pf[GU][16 / KW];
   unsigned char* const wbuf = s_dyn + uni(A.wbuf_lds);
@@ -1340,7 +1405,8 @@ int max_grid_t(size_t lds) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  return per_cu > 0 ? ncu : 0;  // one workgroup per CU
+  // one workgroup per CU (a grid barrier takes at most BW_MAXWG workgroups)
+  return per_cu > 0 ? (ncu < BW_MAXWG ? ncu : 0) : 0;
 }
 
 // ===========================================================================
@@ -1405,7 +1471,7 @@ __global__ __launch_bounds__(64 * KW) void dep_multi_kernel(const DepMultiArgs* 
     if (wg < gemm_items(a, EPI_STORE)) gemm_tile_weights<T, KW, EPI_STORE>(a, tl, 0, wpf, ksg);
   }
   Grid g;
-  if (grid_init(g, uni(A.bar), parity, uni(A.abort), uni(A.spin_limit), trace)) return;
+  if (grid_init(g, uni(A.bar), parity, uni(A.abort), uni(A.spin_limit), trace, false)) return;
 #define DM_SYNC()               \
   do {                          \
     if (grid_sync(g)) return;   \
@@ -1625,7 +1691,8 @@ int dep_multi_grid_t(size_t lds) {
     return 0;
   // one workgroup of 8 waves per CU; two of 4 waves where they fit
   const int want = KW == 4 ? 2 : 1;
-  return per_cu < 1 ? 0 : ncu * (per_cu < want ? per_cu : want);
+  const int n = per_cu < 1 ? 0 : ncu * (per_cu < want ? per_cu : want);
+  return n <= BW_MAXWG ? n : 0;  // a grid barrier takes at most BW_MAXWG workgroups
 }
 
 template <typename T, int HDD, int KW>
