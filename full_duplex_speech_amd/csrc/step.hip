@@ -14,10 +14,11 @@
 // workgroup runs per CU for the whole step and the operations are separated
 // by grid barriers instead of launches.
 //
-// Grid barrier: two levels, because 256 workgroups incrementing one counter
-// serialise at the memory side. Each workgroup counts into the counter of its
-// XCD; the last arrival of an XCD increments the global counter; the last of
-// those writes a release word that everyone polls. Cross-workgroup data use agent-scope relaxed
+// Grid barrier (grid_arrive / grid_wait below): no single counter that every
+// workgroup increments (those serialise at the memory side); each XCD's
+// workgroups poll words in a page of their own, written either by every
+// workgroup (arrival words) or by each XCD's last arrival (done words).
+// Cross-workgroup data use agent-scope relaxed
 // atomics (sc1 loads and stores, see dev.h), each thread waits for its own
 // stores (s_waitcnt 0) before the workgroup arrives, so no cache write-back
 // or invalidate is needed. Every wait is bounded: after SPIN_LIMIT polls a
@@ -320,7 +321,7 @@ __device__ __forceinline__ void embed_phase(const EmbedArgs& a, const int* frame
 //
 // The 16 substeps are ~400 dependent projections of a few MB each; a grid
 // barrier between them costs several memory round trips (store
-// acknowledgement, two counter atomics, the release word). Instead each
+// acknowledgement, the arrival, the polls). Instead each
 // vector a projection hands on is written as flagged 8-byte words
 // {payload, flag}, flag = the launch's sequence number, and its readers poll
 // the words themselves until every flag is current: one round trip after
