@@ -1,7 +1,8 @@
 """The persistent multi-session depformer kernel (capacity 2..64) against the
 per-operation kernels (MOSHI_DEP_MULTI=0): every output a step returns is
 bit-identical, at capacities whose projection tiles take 8 waves (B <= 32)
-and 4 (B > 32), with free slots, teacher forcing, the depformer readings
+and 4 (B > 32), from the smallest capacity (2) to the first with 4 waves
+(33) and beyond, with free slots, teacher forcing, the depformer readings
 (dep_q, the ring reading, the final norm) and a down projection split over
 K into segments; a few session-frames are also
 checked against the oracle; and its bounded-wait failure path (forced from
@@ -107,10 +108,12 @@ def _assert_same(a, b, tag):
 
 CASES = {
     # (shape, capacity, free slots, ticks, forcing, oracle-checked slots)
+    "tiny_fp32_b2": (spec.TINY.replace(window=9), 2, [], 4, True, [1]),  # the smallest capacity
     "tiny_fp32_b3": (spec.TINY.replace(window=9), 3, [1], 6, True, [0]),
     "ragged_bf16_b5_variants": (spec.RAGGED.replace(dep_q=8, dep_ref_ring=True,
                                                     dep_final_norm=True), 5, [3], 4, True, [4]),
     "ragged_bf16_b17": (spec.RAGGED, 17, [0, 16], 3, False, [5]),
+    "ragged_bf16_b33": (spec.RAGGED, 33, [32], 2, False, [31]),  # the first with 4 waves per tile
     "ragged_bf16_b40": (spec.RAGGED, 40, [2, 33, 39], 3, True, [1]),
     "ragged_bf16_b36_variants": (spec.RAGGED.replace(dep_q=8, dep_ref_ring=True,
                                                      dep_final_norm=True), 36, [0, 20], 2, True,
