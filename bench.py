@@ -488,6 +488,36 @@ def main():
         M.moshi_destroy(ctx)
         del ctx, d64
 
+    # ---------------- B = 4: every ring full (context) ----------------
+    # the pages' one multi-session figure is four concurrent sessions at
+    # ~70-74 ms per tick on an H20-class GPU (whole serving loop, other
+    # hardware): context only
+    if args.extra:
+        ctx = make_engine(M, shape, weights, 4, stream)
+        for sid in range(4):
+            s = M.moshi_session_join(ctx)
+            M.moshi_session_prefill_kv(ctx, s, k, v)
+        w5 = wl.WORKLOADS[5]
+        n4 = 40
+        fr4 = np.stack([wl.frames(shape, w5.seed("frames"), sid, 0, n4 + 3)
+                        for sid in range(4)], axis=1)
+        d4 = torch.from_numpy(np.ascontiguousarray(fr4)).to("cuda")
+        t4 = torch.zeros((n4, 4), dtype=torch.int32, device="cuda")
+        c4 = torch.zeros((n4, 4, shape.n_substeps), dtype=torch.int32, device="cuda")
+        ms4, _, ticks4 = timed_steps(M, torch, ctx, stream, d4, t4, c4, 3, n4)
+        kt4 = kernel_table(M, ctx, fr4[0], 1)
+        by4 = sum(x["bytes_per_step"] for x in kt4.values())
+        lines["b4_full_rings"] = {
+            "workload": "full step, B=4, every ring full at 3000 (the B=64 workload's "
+                        "first 4 sessions)",
+            "ms_per_step": round(ms4, 4), "frames_per_s": round(4 * 1000.0 / ms4, 1),
+            "rtf": round(ms4 / FRAME_MS, 5), "bytes_per_step": by4,
+            "hbm_frac": round(by4 / (ms4 * 1e6) / HBM_PEAK_GBS, 4),
+            "ticks_ms": ticks_stats(ticks4)}
+        log(f"B=4: {ms4:.3f} ms/step, {4 * 1000.0 / ms4:.1f} frames/s")
+        M.moshi_destroy(ctx)
+        del ctx, d4
+
     # ---------------- CPU oracle baseline ----------------
     cpu = None
     if not args.no_cpu and args.cpu_frames > 0:
