@@ -513,7 +513,7 @@ def main():
             "ms_per_step": round(ms4, 4), "frames_per_s": round(4 * 1000.0 / ms4, 1),
             "rtf": round(ms4 / FRAME_MS, 5), "bytes_per_step": by4,
             "hbm_frac": round(by4 / (ms4 * 1e6) / HBM_PEAK_GBS, 4),
-            "ticks_ms": ticks_stats(ticks4)}
+            "ticks_ms": ticks_stats(ticks4), "kernels": kt4}
         log(f"B=4: {ms4:.3f} ms/step, {4 * 1000.0 / ms4:.1f} frames/s")
         M.moshi_destroy(ctx)
         del ctx, d4

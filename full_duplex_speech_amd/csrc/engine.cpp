@@ -281,6 +281,7 @@ int64_t d_layer_elems(const moshi_ctx* c) { return (int64_t)c->Hd * c->S * c->hd
 // RMSNorm -> q|k|v -> RoPE -> ring write
 GemmArgs t_qkv_args(const moshi_ctx* c, int l) {
   GemmArgs a = gemm_base(c);
+  a.vec_cols = 1;  // two to four sessions: VALU tiles
   a.W = c->qkv[l]; a.N = 3 * c->D; a.K = c->D;
   a.X = c->x; a.ldx = c->D; a.ssq = c->ssq; a.n_ssq = n_ssq(c, c->D); a.gain = c->attn_norm[l];
   a.xn_out = c->B > 1 ? c->hn : nullptr;
@@ -307,6 +308,7 @@ AttnArgs t_attn_args(const moshi_ctx* c, int l) {
 // o-projection + residual
 GemmArgs t_o_args(const moshi_ctx* c, int l) {
   GemmArgs a = gemm_base(c);
+  a.vec_cols = 1;  // two to four sessions: VALU tiles
   a.W = c->wo[l]; a.N = c->D; a.K = c->D; a.X = c->o; a.ldx = c->D;
   a.resid = c->x; a.ldr = c->D; a.ssq_out = c->ssq;
   return a;
@@ -315,6 +317,7 @@ GemmArgs t_o_args(const moshi_ctx* c, int l) {
 // RMSNorm -> gate|up -> SiLU(gate)*up
 GemmArgs t_gu_args(const moshi_ctx* c, int l) {
   GemmArgs a = gemm_base(c);
+  a.vec_cols = 1;  // two to four sessions: VALU tiles
   a.W = c->gate_up[l]; a.N = c->F; a.K = c->D;
   a.X = c->x; a.ldx = c->D; a.ssq = c->ssq; a.n_ssq = n_ssq(c, c->D); a.gain = c->mlp_norm[l];
   a.xn_out = c->B > 1 ? c->hn : nullptr;
@@ -325,6 +328,7 @@ GemmArgs t_gu_args(const moshi_ctx* c, int l) {
 // down + residual
 GemmArgs t_dn_args(const moshi_ctx* c, int l) {
   GemmArgs a = gemm_base(c);
+  a.vec_cols = 1;  // two to four sessions: VALU tiles
   a.W = c->down[l]; a.N = c->D; a.K = c->F; a.X = c->act; a.ldx = c->F;
   a.resid = c->x; a.ldr = c->D; a.ssq_out = c->ssq;
   return a;
@@ -333,6 +337,7 @@ GemmArgs t_dn_args(const moshi_ctx* c, int l) {
 // final norm -> hidden (kept for the depformer) -> text head logits + argmax partials
 GemmArgs t_head_args(const moshi_ctx* c) {
   GemmArgs a = gemm_base(c);
+  a.vec_cols = 1;  // two to four sessions: VALU tiles
   a.W = c->text_head; a.N = c->Vt; a.K = c->D;
   a.X = c->x; a.ldx = c->D; a.ssq = c->ssq; a.n_ssq = n_ssq(c, c->D); a.gain = c->out_norm;
   a.xn_out = c->hid;

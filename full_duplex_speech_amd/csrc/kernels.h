@@ -74,6 +74,8 @@ struct GemmArgs {
   void* ring_v;
   int64_t slot_stride, layer_off, head_stride;  // ring strides, elements
   int cap;                                      // ring capacity
+  // two to four sessions: VALU tiles instead of MFMA (the temporal projections)
+  int vec_cols;
   // K split over workgroups (MFMA path; gemm_ksplit): ksplit > 1 segments of
   // the k-steps, each summed by its own workgroup into kpart [tile][4][ksplit]
   // [64 lanes] (f64x4); the last segment of a (tile, 16-column block group)
