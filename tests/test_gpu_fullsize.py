@@ -409,3 +409,34 @@ def test_dep_q8_full_step_b1(weights):
                       codes[0][:n], tl[0], al[0][:n], r2)
     M.moshi_destroy(ctx)
     log(f"dep_q=8 full step: {stats}")
+
+
+def test_b3_full_size_valu_tiles(weights, omodel):
+    """Three slots, so the temporal projections run on the fp64 VALU tiles of
+    two to four sessions (among them the 11264-wide down projection, whose
+    last batch is partial), with rings at 3000, 1000 and 7: the first frame
+    of every slot from its prefill, and the third frame of the full-ring slot
+    from the GPU's ring, against the oracle."""
+    w = wl.WORKLOADS[5]
+    bank = wl.prefill_bank(SHAPE, w.seed("prefill"), threads=16)
+    initial = [(0, SHAPE.window), (1, 1000), (2, 7)]
+    T = 3
+    outs, _, rings, _ = _elastic_run(weights, 3, w, bank, initial, {}, T, want_ring_at=T - 1,
+                                     sample_sid=[0])
+    log("B=3 GPU run done")
+    stats = Stats()
+    jobs, meta = [], []
+    for sid, fill in initial:
+        tok, codes, fr, tl, al = outs[sid][0]
+        kk, vv = wl.prefill_from_bank(bank, sid, fill)
+        jobs.append(lambda kk=kk, vv=vv, fr=fr, tok=tok, codes=codes:
+                    _oracle_from_prefill(omodel, kk, vv, fr, tok, codes))
+        meta.append((f"B=3 sid={sid} fill={fill} t=0", tok, codes, tl, al))
+    pos, rk, rv = rings[0]
+    tok, codes, fr, tl, al = outs[0][-1]
+    jobs.append(lambda: _oracle_from_ring(omodel, pos, rk, rv, fr, tok, codes))
+    meta.append((f"B=3 sid=0 t={T - 1} (from ring)", tok, codes, tl, al))
+    res = _parallel(jobs)
+    for (tag, tok, codes, tl, al), r in zip(meta, res):
+        compare_frame(SHAPE, stats, tag, tok, codes, tl, al, r)
+    log(f"B=3 oracle samples ok {stats}")
