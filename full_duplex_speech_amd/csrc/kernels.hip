@@ -53,20 +53,22 @@ __global__ __launch_bounds__(64 * KW) void gemv_kernel(GemmArgs a) {
 // A 16-column MFMA tile with two to four live columns spends most of its
 // matrix work on empty columns; here each weight group is read once and
 // multiplied into every session's rounded input (LDS, model dtype, columns
-// past B zero) on the VALU. One workgroup of 8 waves walks row tiles
-// blockIdx.x, + gridDim.x, ...; wave w takes tile rows 2w, 2w + 1 (the MFMA
-// path's row mapping, tile_row) over the whole of K in double-buffered
-// batches of 4 groups per lane; each row's sums are reduced over the 64
-// lanes and the tile's 16 x NC sums go through LDS to wave 0, which runs the
-// MFMA path's epilogue in its lane layout (lane 16 g + c: rows 4g..4g+3 of
-// column c), so every output, partial and ring write has that path's layout.
-// (Inputs kept as fp64 in LDS instead measured slower: LDS bound.)
-template <typename T, int NC, int EPI>
+// past B zero) on the VALU. One workgroup of 8 waves takes row tiles
+// blockIdx.x, + gridDim.x, ... (the MFMA path's row mapping, tile_row), up
+// to MT of them per pass over K: wave w holds tile rows 2w, 2w + 1 of each,
+// one group per lane and row per batch, double-buffered, and widens each
+// input group once for all of them. Each row's sums are reduced over the 64
+// lanes (a lane sums its groups in K order); the tiles' 16 x NC sums go
+// through LDS to wave 0, which runs the MFMA path's epilogue in its lane
+// layout (lane 16 g + c: rows 4g..4g+3 of column c), so every output,
+// partial and ring write has that path's layout. (Inputs kept as fp64 in
+// LDS instead measured slower: LDS bound.)
+template <typename T, int NC, int EPI, int MT>
 __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
-  constexpr int VEC = VecOf<T>::N, R = 2, U = 4;
+  constexpr int VEC = VecOf<T>::N, R = 2;
   extern __shared__ __align__(16) unsigned char s_dyn[];
   T* xs = (T*)s_dyn;  // [NC][K]
-  __shared__ double s_sum[16][NC];
+  __shared__ double s_sum[MT][16][NC];
   const int t = tid(), lane = t & 63, wave = t >> 6;
   const int ngroups = a.K / VEC;  // K is a multiple of VEC
   for (int i = t; i < NC * ngroups; i += 512) {
@@ -77,73 +79,86 @@ __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
   }
   __syncthreads();
   const int ntiles = n_tiles_of(EPI, a.N);
-  const int nbatch = (ngroups + U * 64 - 1) / (U * 64);
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const T* wr[R];
+  const int nb = (ngroups + 63) / 64;  // batches: group b * 64 + lane
+  for (int t0 = blockIdx.x; t0 < ntiles; t0 += MT * gridDim.x) {
+    // the pass's tiles t0 + m * gridDim.x, m < nm (wave-uniform)
+    const int nm = (ntiles - t0 + gridDim.x - 1) / gridDim.x < MT
+                       ? (ntiles - t0 + gridDim.x - 1) / gridDim.x
+                       : MT;
+    const T* wr[MT][R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      bool ok;
-      const int row = tile_row<EPI>(tile, 2 * wave + r, a.N, ok);
-      wr[r] = (const T*)a.W + (size_t)(ok ? row : 0) * a.K;
-    }
-    // batch bt: groups bt*U*64 + u*64 + lane (past K: the row's last group, unused)
-    auto load = [&](int bt, u32x4 (&w)[U][R]) {
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int gi = bt * U * 64 + u * 64 + lane;
-        const int gc = gi < ngroups ? gi : ngroups - 1;
+      for (int r = 0; r < R; ++r) {
+        bool ok;
+        const int row = tile_row<EPI>(t0 + m * (int)gridDim.x, 2 * wave + r, a.N, ok);
+        wr[m][r] = (const T*)a.W + (size_t)(ok ? row : 0) * a.K;
+      }
+    auto load = [&](int b, u32x4 (&w)[MT][R]) {
+      const int gi = b * 64 + lane;
+      const int gc = gi < ngroups ? gi : ngroups - 1;  // past K: the row's last group, unused
 #pragma unroll
-        for (int r = 0; r < R; ++r) w[u][r] = ld16_stream(wr[r] + (size_t)gc * VEC);
+      for (int m = 0; m < MT; ++m)
+        if (m < nm)
+#pragma unroll
+          for (int r = 0; r < R; ++r) w[m][r] = ld16_stream(wr[m][r] + (size_t)gc * VEC);
+    };
+    double acc[MT][R][NC];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[m][r][c] = 0.0;
+    auto consume = [&](int b, const u32x4 (&w)[MT][R]) {
+      const int gi = b * 64 + lane;
+      if (gi < ngroups) {
+        double xv[NC][VEC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+          widen<T>(*(const u32x4*)(xs + (size_t)c * a.K + (size_t)gi * VEC), xv[c]);
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+          if (m < nm)
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              double wd[VEC];
+              widen<T>(w[m][r], wd);
+#pragma unroll
+              for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[m][r][c] = fma(wd[e], xv[c][e], acc[m][r][c]);
+            }
       }
     };
-    double acc[R][NC];
+    u32x4 wa[MT][R], wb[MT][R];
+    load(0, wa);
+    for (int b = 0; b < nb; b += 2) {
+      if (b + 1 < nb) load(b + 1, wb);
+      consume(b, wa);
+      if (b + 1 >= nb) break;
+      if (b + 2 < nb) load(b + 2, wa);
+      consume(b + 1, wb);
+    }
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int m = 0; m < MT; ++m)
+      if (m < nm)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) acc[r][c] = 0.0;
-    auto consume = [&](int bt, const u32x4 (&w)[U][R]) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int gi = bt * U * 64 + u * 64 + lane;
-        if (gi < ngroups) {
-          double wd[R][VEC];
-#pragma unroll
-          for (int r = 0; r < R; ++r) widen<T>(w[u][r], wd[r]);
+        for (int r = 0; r < R; ++r)
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
-            double xv[VEC];
-            widen<T>(*(const u32x4*)(xs + (size_t)c * a.K + (size_t)gi * VEC), xv);
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-#pragma unroll
-              for (int e = 0; e < VEC; ++e) acc[r][c] = fma(wd[r][e], xv[e], acc[r][c]);
+            const double v = group_reduce<64>(acc[m][r][c]);
+            if (lane == 0) s_sum[m][2 * wave + r][c] = v;
           }
-        }
-      }
-    };
-    u32x4 wa[U][R], wb[U][R];
-    load(0, wa);
-    for (int bt = 0; bt < nbatch; bt += 2) {
-      if (bt + 1 < nbatch) load(bt + 1, wb);
-      consume(bt, wa);
-      if (bt + 1 >= nbatch) break;
-      if (bt + 2 < nbatch) load(bt + 2, wa);
-      consume(bt + 1, wb);
-    }
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const double v = group_reduce<64>(acc[r][c]);
-        if (lane == 0) s_sum[2 * wave + r][c] = v;
-      }
     __syncthreads();
     if (wave == 0) {
       const int g = lane >> 4, c = lane & 15;
-      double v[4];
+      for (int m = 0; m < nm; ++m) {
+        double v[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = c < NC ? s_sum[4 * g + i][c] : 0.0;
-      epilogue<T, EPI, false>(a, tile, g, c, v);  // columns past B store nothing
+        for (int i = 0; i < 4; ++i) v[i] = c < NC ? s_sum[m][4 * g + i][c] : 0.0;
+        epilogue<T, EPI, false>(a, t0 + m * (int)gridDim.x, g, c, v);  // columns past B store nothing
+      }
     }
     __syncthreads();
   }
@@ -808,9 +823,9 @@ static hipError_t launch_gemm_t(int kw, int pro, int epi, const GemmArgs& a, hip
     const int ntiles = gemm_tiles(epi, a.N);
     const int grid = ntiles < g_gemv_grid ? ntiles : g_gemv_grid;
     if ((size_t)4 * a.K * sizeof(T) > 160 * 1024 || a.K % VecOf<T>::N) return hipErrorInvalidValue;
-#define MOSHI_COLS(NC_, E_)                                                                \
-  hipLaunchKernelGGL((gemv_cols_kernel<T, NC_, E_>), dim3(grid), dim3(512), (NC_) * a.K * sizeof(T), \
-                     st, b)
+#define MOSHI_COLS(NC_, E_)                                                                    \
+  hipLaunchKernelGGL((gemv_cols_kernel<T, NC_, E_, 3>), dim3(grid), dim3(512),                 \
+                     (NC_) * a.K * sizeof(T), st, b)
     const bool two = a.B <= 2;
     switch (epi) {
       case EPI_STORE: if (two) MOSHI_COLS(2, EPI_STORE); else MOSHI_COLS(4, EPI_STORE); break;
