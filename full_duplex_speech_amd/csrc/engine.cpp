@@ -1235,10 +1235,12 @@ int alloc_buffers(moshi_ctx* c) {
     n = n < 1 ? 1 : n;
     c->max_spans = n < by_len ? n : by_len;
     if (c->max_spans > 8) c->max_spans = 8;  // the step kernel merges at most 8 span partials
-    // two or more sessions: (slot, head) pairs fill the CUs already; 4
+    // five or more sessions: (slot, head) pairs fill the CUs already; 4
     // longer spans per head measured faster than 8 (B=16: 3.42 -> 3.25 ms of
-    // attention and merge per step, B=64: 16.96 -> 16.60) and than 2 or ~23
-    if (c->B > 1 && c->max_spans > 4) c->max_spans = 4;
+    // attention and merge per step, B=64: 16.96 -> 16.60) and than 2 or ~23;
+    // up to four sessions 8 stay (full rings: B=3 10.23 -> 10.08 ms per step
+    // with 8, B=4 10.44 -> 10.35)
+    if (c->B > 4 && c->max_spans > 4) c->max_spans = 4;
   }
   const size_t hmax = c->H > c->Hd ? c->H : c->Hd;
   const size_t hdmax = c->hd > c->hdd ? c->hd : c->hdd;
