@@ -137,6 +137,24 @@ def test_isolation_and_recycle_bit_exact():
             assert np.array_equal(np.asarray(x), np.asarray(z)), f"recycle broken at t={t}"
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_steps_with_no_live_session(B):
+    """Ticks with no live session (before the first join, and after every
+    session has left) return -1 for every slot; sessions joining afterwards,
+    into the slots just vacated, match their oracles. At one session the step
+    kernel is not launched for such a tick; at three the temporal graph and
+    the depformer kernel run over free slots only."""
+    shape = spec.RAGGED
+    weights = wl.make_weights(shape, 29, gains="random")
+    more = B > 1
+    plan = {2: [("join", 0, 5)] + ([("join", 1, 0)] if more else []),
+            5: [("leave", 0)] + ([("leave", 1)] if more else []),
+            7: [("join", 2, 9)] + ([("join", 3, 0), ("join", 4, 2)] if more else [])}
+    outs, stats = _run_sessions(shape, weights, B, plan, 10)
+    assert len(outs[0]) == 3 and len(outs[2]) == 3
+    log(f"no live session, B={B}: {stats}")
+
+
 def test_run_twice_deterministic():
     shape = spec.RAGGED
     weights = wl.make_weights(shape, 17, gains="random")
