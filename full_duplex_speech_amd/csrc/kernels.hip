@@ -818,11 +818,13 @@ static hipError_t launch_gemm_t(int kw, int pro, int epi, const GemmArgs& a, hip
     b.X = a.xn_out;
     b.ldx = a.K;
   }
-  if (a.vec_cols && a.B <= 4) {
-    // temporal projections of two to four sessions: VALU tiles (gemv_cols_kernel)
+  // temporal projections of two to four sessions: VALU tiles (gemv_cols_kernel)
+  // where every session's input fits the workgroup's LDS beside the tiles'
+  // sums (wider inputs take the MFMA tiles below)
+  const size_t cols_lds = (size_t)(a.B <= 2 ? 2 : 4) * a.K * sizeof(T) + 3 * 16 * 4 * sizeof(double);
+  if (a.vec_cols && a.B <= 4 && cols_lds <= 160 * 1024 && a.K % VecOf<T>::N == 0) {
     const int ntiles = gemm_tiles(epi, a.N);
     const int grid = ntiles < g_gemv_grid ? ntiles : g_gemv_grid;
-    if ((size_t)4 * a.K * sizeof(T) > 160 * 1024 || a.K % VecOf<T>::N) return hipErrorInvalidValue;
 #define MOSHI_COLS(NC_, E_)                                                                    \
   hipLaunchKernelGGL((gemv_cols_kernel<T, NC_, E_, 3>), dim3(grid), dim3(512),                 \
                      (NC_) * a.K * sizeof(T), st, b)

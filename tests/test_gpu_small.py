@@ -115,6 +115,23 @@ def test_tiny_fp32_batched_ragged_capacity():
     log("tiny B=5:", stats)
 
 
+@pytest.mark.parametrize("case", ["bf16_ffn20488_b3", "fp32_ffn10240_b4", "fp32_ffn10240_b2"])
+def test_wide_ffn_few_sessions(case):
+    """Two to four sessions with a temporal FFN wider than four inputs of
+    the VALU tiles fit in LDS (bf16 20488, fp32 10240): at three and four
+    sessions the projections take the MFMA tiles, at two the VALU tiles
+    (two inputs fit); every session matches its oracle."""
+    if case.startswith("bf16"):
+        shape = spec.RAGGED.replace(ffn=20488, window=9)
+    else:
+        shape = spec.TINY.replace(ffn=10240, window=9)
+    B = int(case[-1])
+    weights = wl.make_weights(shape, 37, gains="random")
+    plan = {0: [("join", i, [0, 4, 9, 2][i]) for i in range(B)]}
+    _, stats = _run_sessions(shape, weights, B, plan, 4)
+    log(f"wide ffn {case}:", stats)
+
+
 def test_isolation_and_recycle_bit_exact():
     """A session's outputs are bit-identical alone in slot 0 of a fresh engine
     and batched in slot 2 among others; a recycled slot equals a fresh one."""
