@@ -132,6 +132,20 @@ def test_wide_ffn_few_sessions(case):
     log(f"wide ffn {case}:", stats)
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_largest_window(B):
+    """The largest window the config accepts (32768 keys): rings full, one
+    key short of full and nearly empty, stepped through the wrap-around;
+    every session matches its oracle (one session: the step kernel's 8 key
+    spans of 4096 keys per head)."""
+    shape = spec.RAGGED.replace(window=32768)
+    weights = wl.make_weights(shape, 41, gains="random")
+    fills = [32768, 32767, 5][:B] if B > 1 else [32767]
+    plan = {0: [("join", i, f) for i, f in enumerate(fills)]}
+    _, stats = _run_sessions(shape, weights, B, plan, 3)
+    log(f"window 32768, B={B}:", stats)
+
+
 def test_isolation_and_recycle_bit_exact():
     """A session's outputs are bit-identical alone in slot 0 of a fresh engine
     and batched in slot 2 among others; a recycled slot equals a fresh one."""
