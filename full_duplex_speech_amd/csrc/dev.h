@@ -1165,7 +1165,8 @@ __device__ __forceinline__ void gemv_staged(const GemmArgs& a, int wg, int nwg, 
 // ---------------------------------------------------------------------------
 
 // Keys of slot b visible at its current position: ring slots [0, nvalid),
-// minus `excl` (the oldest key, under the mask-oldest reading).
+// minus `excl` (the oldest key, under the mask-oldest reading). Without
+// positions (the depformer's entries): scalar_nvalid keys minus scalar_excl.
 __device__ __forceinline__ void window_of(const AttnArgs& a, int b, int& nvalid, int& excl) {
   excl = -1;
   if (a.pos != nullptr) {
@@ -1174,6 +1175,7 @@ __device__ __forceinline__ void window_of(const AttnArgs& a, int b, int& nvalid,
     if (a.mask_oldest && p >= (int64_t)a.cap - 1) excl = (int)((p + 1) % a.cap);
   } else {
     nvalid = a.scalar_nvalid;
+    excl = a.scalar_excl;
   }
 }
 

@@ -146,6 +146,29 @@ def test_largest_window(B):
     log(f"window 32768, B={B}:", stats)
 
 
+@pytest.mark.parametrize("case", ["ragged_bf16_s17_b1", "tiny_fp32_s17_ref_ring_b3",
+                                  "tiny_fp32_s64_b3"])
+def test_more_substeps_than_the_persistent_kernels_take(case):
+    """More than 16 depformer substeps (17, and the config's maximum of 64):
+    neither the one-session step kernel nor the multi-session depformer
+    kernel takes them, so the per-operation graph runs, its depformer
+    attention on the ring attention kernel; every session matches its
+    oracle. With the depformer ring reading (entry 0 masked at the last
+    substep) the fp32 oracle's last-substep logits move by ~3e-3, thirty
+    times the fp32 tolerance, so a mask left out fails the comparison."""
+    B = int(case[-1])
+    S = 64 if "s64" in case else 17
+    base = spec.RAGGED if case.startswith("ragged") else spec.TINY
+    shape = base.replace(n_substeps=S, window=9, dep_ref_ring="ref_ring" in case)
+    weights = wl.make_weights(shape, 43, gains="random")
+    ctx = new_engine(shape, weights, B)
+    assert not M.moshi_uses_step_kernel(ctx) and not M.moshi_uses_dep_kernel(ctx)
+    M.moshi_destroy(ctx)
+    plan = {0: [("join", i, [9, 0, 4][i]) for i in range(B)]}
+    _, stats = _run_sessions(shape, weights, B, plan, 3)
+    log(f"{case}:", stats)
+
+
 def test_isolation_and_recycle_bit_exact():
     """A session's outputs are bit-identical alone in slot 0 of a fresh engine
     and batched in slot 2 among others; a recycled slot equals a fresh one."""
