@@ -169,6 +169,29 @@ def test_more_substeps_than_the_persistent_kernels_take(case):
     log(f"{case}:", stats)
 
 
+@pytest.mark.parametrize("case", ["bf16_hd32_hdd128_b1", "bf16_hd32_hdd128_b3",
+                                  "fp32_hd128_hdd64_b1", "fp32_hd128_hdd64_b3"])
+def test_other_head_dims(case):
+    """Head dims the config accepts besides the two shapes the persistent
+    kernels are built for (bf16 128 / 64, fp32 64 / 32): a 32-wide temporal
+    and 128-wide depformer head in bf16, a 128-wide temporal and 64-wide
+    depformer head in fp32; the per-operation kernels at one and three
+    sessions match the oracle."""
+    B = int(case[-1])
+    if case.startswith("bf16"):
+        shape = spec.RAGGED.replace(dim=128, n_heads=4, ffn=352, dep_dim=256, dep_heads=2,
+                                    dep_ffn=520, window=11)
+    else:
+        shape = spec.TINY.replace(n_heads=2, dep_heads=2, window=11)
+    weights = wl.make_weights(shape, 47, gains="random")
+    ctx = new_engine(shape, weights, B)
+    assert not M.moshi_uses_step_kernel(ctx) and not M.moshi_uses_dep_kernel(ctx)
+    M.moshi_destroy(ctx)
+    plan = {0: [("join", i, [11, 0, 6][i]) for i in range(B)]}
+    _, stats = _run_sessions(shape, weights, B, plan, 14)
+    log(f"{case}:", stats)
+
+
 def test_isolation_and_recycle_bit_exact():
     """A session's outputs are bit-identical alone in slot 0 of a fresh engine
     and batched in slot 2 among others; a recycled slot equals a fresh one."""
