@@ -192,6 +192,26 @@ def test_other_head_dims(case):
     log(f"{case}:", stats)
 
 
+@pytest.mark.parametrize("case", ["fp32_b1", "fp32_b3", "bf16_b1", "bf16_b3"])
+def test_smallest_counts(case):
+    """The config's smallest counts at widths the persistent kernels are
+    built for: one temporal and one depformer layer, one substep, a window
+    of one key and vocabularies of two (a 16-row head tile with 14 rows past
+    the end); the step kernel at one session, the depformer kernel at three,
+    every session matching its oracle for 12 frames."""
+    B = int(case[-1])
+    base = spec.TINY if case.startswith("fp32") else spec.RAGGED
+    shape = base.replace(n_layers=1, dep_layers=1, n_substeps=1, text_vocab=2, audio_card=2,
+                         window=1)
+    weights = wl.make_weights(shape, 53, gains="random")
+    ctx = new_engine(shape, weights, B)
+    assert M.moshi_uses_step_kernel(ctx) == (B == 1) and M.moshi_uses_dep_kernel(ctx) == (B > 1)
+    M.moshi_destroy(ctx)
+    plan = {0: [("join", i, [1, 0, 1][i]) for i in range(B)]}
+    _, stats = _run_sessions(shape, weights, B, plan, 12)
+    log(f"smallest counts {case}:", stats)
+
+
 def test_isolation_and_recycle_bit_exact():
     """A session's outputs are bit-identical alone in slot 0 of a fresh engine
     and batched in slot 2 among others; a recycled slot equals a fresh one."""
