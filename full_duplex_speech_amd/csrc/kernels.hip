@@ -85,13 +85,20 @@ __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
     const int nm = (ntiles - t0 + gridDim.x - 1) / gridDim.x < MT
                        ? (ntiles - t0 + gridDim.x - 1) / gridDim.x
                        : MT;
+    // Every batch loads all MT x R rows with no branch around the loads (a
+    // tile past the end, m >= nm, re-reads tile t0's rows; a batch past K the
+    // row's last group; neither sum is used), so the compiler knows how many
+    // loads are younger than the batch being consumed and waits for that
+    // batch only: with branches around them (or a break between the two
+    // batches of a loop trip) it waited for all of them, the next batch
+    // included, and batches cost a full memory round trip each.
     const T* wr[MT][R];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         bool ok;
-        const int row = tile_row<EPI>(t0 + m * (int)gridDim.x, 2 * wave + r, a.N, ok);
+        const int row = tile_row<EPI>(m < nm ? t0 + m * (int)gridDim.x : t0, 2 * wave + r, a.N, ok);
         wr[m][r] = (const T*)a.W + (size_t)(ok ? row : 0) * a.K;
       }
     auto load = [&](int b, u32x4 (&w)[MT][R]) {
@@ -99,9 +106,8 @@ __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
       const int gc = gi < ngroups ? gi : ngroups - 1;  // past K: the row's last group, unused
 #pragma unroll
       for (int m = 0; m < MT; ++m)
-        if (m < nm)
 #pragma unroll
-          for (int r = 0; r < R; ++r) w[m][r] = ld16_stream(wr[m][r] + (size_t)gc * VEC);
+        for (int r = 0; r < R; ++r) w[m][r] = ld16_stream(wr[m][r] + (size_t)gc * VEC);
     };
     double acc[MT][R][NC];
 #pragma unroll
@@ -131,13 +137,14 @@ __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
             }
       }
     };
+    // whole pairs of batches, without a break between them (a batch past the
+    // last consumes nothing: every lane's group is past K)
     u32x4 wa[MT][R], wb[MT][R];
     load(0, wa);
     for (int b = 0; b < nb; b += 2) {
-      if (b + 1 < nb) load(b + 1, wb);
+      load(b + 1, wb);
       consume(b, wa);
-      if (b + 1 >= nb) break;
-      if (b + 2 < nb) load(b + 2, wa);
+      load(b + 2, wa);
       consume(b + 1, wb);
     }
 #pragma unroll
