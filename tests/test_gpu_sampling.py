@@ -102,12 +102,20 @@ def _run(shape, weights, B, plan, T, check=True, forcing=True):
     return outs, stats, n_drawn, n_excused
 
 
-@pytest.mark.parametrize("case", ["tiny_fp32_b1", "ragged_bf16_b4"])
+@pytest.mark.parametrize("case", ["tiny_fp32_b1", "ragged_bf16_b4", "ragged_bf16_b17"])
 def test_sampling_parity(case):
     if case == "tiny_fp32_b1":
         shape, B = spec.TINY.replace(window=16), 1
         plan = {0: [("join", 1, 0)]}
         T = 10
+    elif case == "ragged_bf16_b17":
+        # two 16-column MFMA blocks per projection tile, with churn
+        shape, B = spec.RAGGED, 17
+        plan = {0: [("join", i, (5 * i) % 38) for i in range(16)],
+                2: [("join", 16, 3)],
+                4: [("leave", 2)],
+                5: [("join", 17, 0)]}
+        T = 7
     else:
         shape, B = spec.RAGGED, 4
         plan = {0: [("join", 0, 0), ("join", 1, 12), ("join", 2, 37)],
