@@ -71,28 +71,22 @@ __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
   __shared__ double s_sum[MT][16][NC];
   const int t = tid(), lane = t & 63, wave = t >> 6;
   const int ngroups = a.K / VEC;  // K is a multiple of VEC
-  for (int i = t; i < NC * ngroups; i += 512) {
-    const int c = i / ngroups, gi = i - c * ngroups;
-    const u32x4 v = c < a.B ? ld16((const T*)a.X + (size_t)c * a.ldx + (size_t)gi * VEC)
-                            : u32x4{0u, 0u, 0u, 0u};
-    *(u32x4*)(xs + (size_t)c * a.K + (size_t)gi * VEC) = v;
-  }
-  __syncthreads();
   const int ntiles = n_tiles_of(EPI, a.N);
   const int nb = (ngroups + 63) / 64;  // batches: group b * 64 + lane
-  for (int t0 = blockIdx.x; t0 < ntiles; t0 += MT * gridDim.x) {
-    // the pass's tiles t0 + m * gridDim.x, m < nm (wave-uniform)
-    const int nm = (ntiles - t0 + gridDim.x - 1) / gridDim.x < MT
-                       ? (ntiles - t0 + gridDim.x - 1) / gridDim.x
-                       : MT;
-    // Every batch loads all MT x R rows with no branch around the loads (a
-    // tile past the end, m >= nm, re-reads tile t0's rows; a batch past K the
-    // row's last group; neither sum is used), so the compiler knows how many
-    // loads are younger than the batch being consumed and waits for that
-    // batch only: with branches around them (or a break between the two
-    // batches of a loop trip) it waited for all of them, the next batch
-    // included, and batches cost a full memory round trip each.
-    const T* wr[MT][R];
+  // the pass starting at tile t0 takes tiles t0 + m * gridDim.x, m < nm
+  auto n_in_pass = [&](int t0) {
+    const int n = (ntiles - t0 + (int)gridDim.x - 1) / (int)gridDim.x;
+    return n < MT ? n : MT;
+  };
+  // Every batch loads all MT x R rows with no branch around the loads (a
+  // tile past the end, m >= nm, re-reads tile t0's rows; a batch past K the
+  // row's last group; neither sum is used), so the compiler knows how many
+  // loads are younger than the batch being consumed and waits for that
+  // batch only: with branches around them (or a break between the two
+  // batches of a loop trip) it waited for all of them, the next batch
+  // included, and batches cost a full memory round trip each.
+  const T* wr[MT][R];
+  auto set_rows = [&](int t0, int nm) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
@@ -101,14 +95,54 @@ __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
         const int row = tile_row<EPI>(m < nm ? t0 + m * (int)gridDim.x : t0, 2 * wave + r, a.N, ok);
         wr[m][r] = (const T*)a.W + (size_t)(ok ? row : 0) * a.K;
       }
-    auto load = [&](int b, u32x4 (&w)[MT][R]) {
-      const int gi = b * 64 + lane;
-      const int gc = gi < ngroups ? gi : ngroups - 1;  // past K: the row's last group, unused
+  };
+  auto load = [&](int b, u32x4 (&w)[MT][R]) {
+    const int gi = b * 64 + lane;
+    const int gc = gi < ngroups ? gi : ngroups - 1;  // past K: the row's last group, unused
 #pragma unroll
-      for (int m = 0; m < MT; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int r = 0; r < R; ++r) w[m][r] = ld16_stream(wr[m][r] + (size_t)gc * VEC);
-    };
+      for (int r = 0; r < R; ++r) w[m][r] = ld16_stream(wr[m][r] + (size_t)gc * VEC);
+  };
+  // The first pass's first weight batch is requested before the inputs are
+  // staged (the grid is at most the tile count, so every workgroup has a
+  // tile), and the staging requests SU groups per thread before it stores
+  // any: one memory round trip before the products instead of one per
+  // staging round plus one for the weights.
+  u32x4 wa[MT][R], wb[MT][R];
+  int t0 = blockIdx.x;
+  int nm = n_in_pass(t0);
+  set_rows(t0, nm);
+  load(0, wa);
+  {
+    constexpr int SU = 4;
+    const int nx = NC * ngroups;
+    for (int i0 = t; i0 < nx; i0 += SU * 512) {
+      u32x4 v[SU];
+#pragma unroll
+      for (int u = 0; u < SU; ++u) {
+        const int i = i0 + u * 512 < nx ? i0 + u * 512 : nx - 1;
+        const int c = i / ngroups, gi = i - c * ngroups;
+        v[u] = c < a.B ? ld16((const T*)a.X + (size_t)c * a.ldx + (size_t)gi * VEC)
+                       : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < SU; ++u) {
+        const int i = i0 + u * 512;
+        if (i < nx) {
+          const int c = i / ngroups, gi = i - c * ngroups;
+          *(u32x4*)(xs + (size_t)c * a.K + (size_t)gi * VEC) = v[u];
+        }
+      }
+    }
+  }
+  __syncthreads();
+  for (; t0 < ntiles; t0 += MT * gridDim.x) {
+    if (t0 != (int)blockIdx.x) {
+      nm = n_in_pass(t0);
+      set_rows(t0, nm);
+      load(0, wa);
+    }
     double acc[MT][R][NC];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -139,8 +173,6 @@ __global__ __launch_bounds__(512) void gemv_cols_kernel(GemmArgs a) {
     };
     // whole pairs of batches, without a break between them (a batch past the
     // last consumes nothing: every lane's group is past K)
-    u32x4 wa[MT][R], wb[MT][R];
-    load(0, wa);
     for (int b = 0; b < nb; b += 2) {
       load(b + 1, wb);
       consume(b, wa);
